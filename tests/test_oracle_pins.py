@@ -1,0 +1,417 @@
+"""Pins of the CPU oracle to facts fixed outside itself: hand-computed values, closed forms, invariants, special cases
+that reduce to a library routine, and brute force on tiny inputs. CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax as sp_softmax
+
+import oracle as O
+from fixtures import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- number formats
+
+
+def test_bf16_hand_values():
+    # 1.0 = 0x3F80; 1 + 2^-8 is exactly halfway between 1.0 and 1 + 2^-7 -> ties to even -> 1.0
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 (0x3F81, odd) and 1 + 2^-6 (0x3F82, even) -> 0x3F82
+    vals = [1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.0, 0.0, 1.0 + 2.0 ** -7, 3.140625, -0.5]
+    want = [0x3F80, 0x3F80, 0x3F82, 0xC000, 0x0000, 0x3F81, 0x4049, 0xBF00]
+    assert list(O.bf16_bits(np.array(vals))) == want
+    assert np.array_equal(O.bf16_to_f64(np.array(want, dtype=np.uint16)),
+                          np.array([1.0, 1.0, 1.0 + 2.0 ** -6, -2.0, 0.0, 1.0 + 2.0 ** -7, 3.140625, -0.5]))
+
+
+def test_bf16_matches_torch_conversion():
+    # torch's own fp32 -> bf16 conversion (round to nearest even) is an independent implementation
+    x = rng(1).standard_normal(200000).astype(np.float32) * np.float32(3.0)
+    ours = O.bf16_bits(x.astype(np.float64))
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+    back = torch.from_numpy(theirs.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_to_f64(theirs), back)
+
+
+def test_mask_value_bits():
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    bits = int(g["mask_value_f32_bits"]["value"], 16)
+    assert int(np.array([O.NEG_FILL_F32], np.float32).view(np.uint32)[0]) == bits
+    assert float(O.NEG_FILL_F32) == pytest.approx(-1e30, rel=1e-7)
+
+
+# ---------------------------------------------------------------- elementary ops
+
+
+def test_rmsnorm_hand_and_closed_form():
+    out = O.rmsnorm(np.array([3.0, 4.0]), np.ones(2), 0.0)  # mean square 12.5
+    assert np.allclose(out, [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rtol=0, atol=1e-15)
+    v = rng(2).standard_normal((5, 256)) * 7.0
+    y = O.rmsnorm(v, np.ones(256), 1e-6)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, atol=1e-7)
+    w = rng(3).standard_normal(256)
+    assert np.allclose(O.rmsnorm(v, w, 1e-6), y * w)
+    assert np.array_equal(O.rmsnorm(np.zeros(8), np.ones(8), 1e-6), np.zeros(8))
+
+
+def test_gelu_tanh_against_exact_gelu():
+    a = np.linspace(-8, 8, 4001)
+    exact = np.array([0.5 * t * (1.0 + math.erf(t / math.sqrt(2.0))) for t in a])
+    g = O.gelu_tanh(a)
+    assert np.max(np.abs(g - exact)) < 1e-3       # the tanh form approximates the erf form to ~5e-4
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert abs(O.gelu_tanh(np.array([20.0]))[0] - 20.0) < 1e-12
+    assert abs(O.gelu_tanh(np.array([-20.0]))[0]) < 1e-12
+    # torch's tanh-approximate gelu (independent implementation)
+    tg = torch.nn.functional.gelu(torch.from_numpy(a), approximate="tanh").numpy()
+    assert np.allclose(g, tg, rtol=0, atol=1e-12)
+
+
+def test_rope_is_complex_rotation():
+    r = rng(4)
+    q = r.standard_normal(64)
+    ang = r.uniform(-10, 10, 32)
+    out = O.rope_rotate(q, np.cos(ang), np.sin(ang))
+    z = (q[:32] + 1j * q[32:]) * np.exp(1j * ang)
+    assert np.allclose(out[:32], z.real) and np.allclose(out[32:], z.imag)
+    assert np.allclose(O.rope_rotate(q, np.ones(32), np.zeros(32)), q)  # position 0 is the identity
+    pair_norm = lambda v: v[:32] ** 2 + v[32:] ** 2  # noqa: E731
+    assert np.allclose(pair_norm(out), pair_norm(q))
+
+
+def test_key_window_cases():
+    assert O.key_window(256, 512, False) == (0, 256)     # window wider than context: sliding == full
+    assert O.key_window(4096, 512, False) == (3584, 4096)
+    assert O.key_window(4096, 512, True) == (0, 4096)
+    assert O.key_window(10, 1, False) == (9, 10)
+
+
+def test_attention_closed_forms():
+    r = rng(5)
+    K = r.standard_normal((50, 16))
+    V = r.standard_normal((50, 16))
+    # q = 0: uniform weights -> mean of V
+    assert np.allclose(O.attend(np.zeros(16), K, V, 0.25), V.mean(axis=0))
+    # identical keys -> uniform weights
+    Kc = np.tile(K[:1], (50, 1))
+    assert np.allclose(O.attend(r.standard_normal(16), Kc, V, 0.25), V.mean(axis=0))
+    # one key: that value
+    assert np.allclose(O.attend(r.standard_normal(16), K[:1], V[:1], 0.25), V[0])
+    # against scipy's softmax
+    q = r.standard_normal(16)
+    p = sp_softmax(0.25 * (K @ q))
+    assert np.allclose(O.attend(q, K, V, 0.25), p @ V)
+    # permutation of the key/value rows does not change the result
+    perm = r.permutation(50)
+    assert np.allclose(O.attend(q, K[perm], V[perm], 0.25), O.attend(q, K, V, 0.25))
+    # a dominating key: the result tends to its value
+    Kd = K.copy()
+    Kd[17] = q * 100.0
+    assert np.allclose(O.attend(q, Kd, V, 1.0), V[17], atol=1e-9)
+
+
+def test_topk_matches_stable_sort_with_ties():
+    r = rng(6)
+    for trial in range(20):
+        s = r.standard_normal(2048).astype(np.float32)
+        # plant ties at the selection boundary and inside the selection
+        order = np.argsort(-s, kind="stable")
+        s[order[33]] = s[order[31]]
+        s[order[5]] = s[order[4]]
+        s = s.astype(np.float32)
+        want = np.argsort(-s.astype(np.float64), kind="stable")[:32]
+        assert np.array_equal(O.topk_desc(s, 32), want)
+
+
+# ---------------------------------------------------------------- head
+
+
+def _tiny_model(seed=0, **over):
+    shape = synth.TINY
+    if over:
+        import dataclasses
+        shape = dataclasses.replace(shape, **over)
+    w = synth.make_weights(shape, seed=seed)
+    return O.Model(O.config_from(shape), w), w, shape
+
+
+def test_masked_head_invariants_and_dense_equality():
+    m, w, shape = _tiny_model()
+    cfg = m.cfg
+    r = rng(7)
+    for t in range(10):
+        h = O.round_bf16(r.standard_normal(cfg.hidden))
+        out = O.masked_head_row(m, h, want_row=True)
+        row = out["row"]
+        finite = row != O.NEG_FILL_F32
+        assert finite.sum() == cfg.top_k * cfg.vsc
+        assert np.all(row.view(np.uint32)[~finite] == 0xF149F2CA)
+        blocks = np.asarray(w["token_ordering"]).reshape(cfg.n_centroids, cfg.vsc)[out["sel"]]
+        assert set(np.nonzero(finite)[0].tolist()) == set(blocks.reshape(-1).tolist())
+        assert len(set(out["ids"].tolist())) == len(out["ids"])
+        # sparse logits equal the brute-force dense product at the selected ids
+        dense = np.array([sum(float(a) * float(b) for a, b in zip(O.bf16_to_f64(m.head_bits[i]), h))
+                          for i in range(cfg.vocab)])
+        assert np.allclose(row[finite], dense[finite].astype(np.float32), rtol=1e-6, atol=1e-7)
+        assert out["next"] == int(np.argmax(np.where(finite, dense, -np.inf)))
+        # the selected clusters are the top-k by brute-force centroid scores
+        cs = np.array([np.dot(O.bf16_to_f64(np.asarray(w["centroids"]).view(np.uint16)[c]), h)
+                       for c in range(cfg.n_centroids)]).astype(np.float32)
+        assert set(out["sel"].tolist()) == set(np.argsort(-cs.astype(np.float64), kind="stable")[:cfg.top_k].tolist())
+
+
+def test_masked_head_all_clusters_equals_dense_argmax():
+    m, w, shape = _tiny_model(top_k=8)  # k == n_centroids: every token is scored
+    r = rng(8)
+    for t in range(10):
+        h = O.round_bf16(r.standard_normal(m.cfg.hidden))
+        out = O.masked_head_row(m, h, want_row=True)
+        dense = O.dense_head_row(m, h)
+        assert np.array_equal(out["row"], dense)
+        assert out["next"] == int(np.argmax(dense))
+
+
+def test_head_invariant_checks_reject_bad_inputs():
+    m, w, shape = _tiny_model()
+    cfg = m.cfg
+    bad = np.asarray(w["token_ordering"]).copy()
+    bad[3] = bad[4]
+    with pytest.raises(ValueError):
+        O.check_head_invariants(cfg, bad)
+    import dataclasses
+    with pytest.raises(ValueError):
+        O.check_head_invariants(dataclasses.replace(cfg, n_centroids=7), np.asarray(w["token_ordering"]))
+    with pytest.raises(ValueError):
+        O.check_head_invariants(dataclasses.replace(cfg, top_k=9), np.asarray(w["token_ordering"]))
+
+
+def test_argmax_tie_goes_to_lowest_token():
+    m, w, shape = _tiny_model()
+    cfg = m.cfg
+    # make every head row identical: all selected logits tie; the lowest selected token id must win
+    m.head_bits = np.tile(m.head_bits[:1], (cfg.vocab, 1))
+    h = O.round_bf16(rng(9).standard_normal(cfg.hidden))
+    out = O.masked_head_row(m, h)
+    assert out["next"] == int(np.min(out["ids"]))
+
+
+# ---------------------------------------------------------------- whole step
+
+
+def _tiny_inputs(shape, batch=3, context=40, ragged=True, seed=0):
+    wl = synth.Workload("tiny", shape, batch=batch, context=context, n_steps=3, ragged=ragged, seed=seed)
+    d = synth.make_inputs(wl)
+    kv = O.SharedKV(k=[d["k_sliding"].numpy().view(np.uint16), d["k_full"].numpy().view(np.uint16)],
+                    v=None, lens=[d["len_sliding"], d["len_full"]], rope=d["rope"].numpy())
+    kv.v = kv.k
+    return wl, d, kv
+
+
+def test_layer_scalar_zero_branch_closed_form():
+    """With attn_output = ffn_down = 0 every branch adds RMSNorm(0) = 0, so the residual stream leaving the last
+    layer is pre_projection(x0) times the product of the per-layer scalars."""
+    m, w, shape = _tiny_model()
+    for L in m.layers:
+        L["o"][:] = 0.0
+        L["down"][:] = 0.0
+    wl, d, kv = _tiny_inputs(shape)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    b = 1
+    x0 = np.concatenate([O.bf16_to_f64(th[b]), O.bf16_to_f64(emb[int(d["last_token"][b])])])
+    x = m.pre @ x0
+    want = x * np.prod([L["scale"] for L in m.layers])
+    for l in range(m.cfg.n_layer):
+        x = O.decoder_layer(m, l, x, b, kv)
+    assert np.allclose(x, want, rtol=1e-13, atol=0)
+
+
+def test_gqa_head_mapping():
+    """n_kv = 2, n_head = 4: heads 0-1 read kv head 0 and heads 2-3 kv head 1. Make kv head 1 a single repeated key:
+    every head reading it returns that key (K = V), heads reading kv head 0 do not."""
+    m, w, shape = _tiny_model(n_kv_head=2)
+    wl, d, kv = _tiny_inputs(shape)
+    const = kv.k[1][0, 1, 0].copy()
+    kv.k[1][:, 1] = const
+    kv.v = kv.k
+    cfg = m.cfg
+    b, l = 0, 3  # layer 3 is the full-attention layer
+    L = m.layers[l]
+    x = rng(10).standard_normal(cfg.hidden)
+    u = O.round_bf16(O.rmsnorm(x, L["attn_norm"], cfg.rms_eps))
+    q = (L["q"] @ u).reshape(cfg.n_head, cfg.head_dim)
+    a0, a1 = O.key_window(kv.lens[1][b], cfg.swa_window, True)
+    for h in range(cfg.n_head):
+        qh = O.round_bf16(O.rope_rotate(O.rmsnorm(q[h], L["q_norm"], cfg.rms_eps), kv.rope[b, 1, 0], kv.rope[b, 1, 1]))
+        g = h * cfg.n_kv_head // cfg.n_head
+        o = O.attend(qh, O.bf16_to_f64(kv.k[1][b, g, a0:a1]), O.bf16_to_f64(kv.k[1][b, g, a0:a1]), cfg.attn_scale)
+        if h >= 2:
+            assert np.allclose(o, O.bf16_to_f64(const))
+        else:
+            assert not np.allclose(o, O.bf16_to_f64(const))
+
+
+def test_window_one_returns_last_key():
+    m, w, shape = _tiny_model(swa_window=1)
+    wl, d, kv = _tiny_inputs(shape)
+    b = 2
+    a0, a1 = O.key_window(kv.lens[0][b], 1, False)
+    K = O.bf16_to_f64(kv.k[0][b, 0, a0:a1])
+    assert K.shape[0] == 1
+    o = O.attend(rng(11).standard_normal(shape.head_dim), K, K, 0.125)
+    assert np.array_equal(o, O.bf16_to_f64(kv.k[0][b, 0, kv.lens[0][b] - 1]))
+
+
+def test_concat_order_metamorphic():
+    """Swapping the two input halves together with the two column blocks of pre_projection leaves the step
+    unchanged: the hidden state is paired with the first backbone-wide block of pre_projection's input."""
+    m, w, shape = _tiny_model()
+    wl, d, kv = _tiny_inputs(shape, batch=2)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    tok = d["last_token"].numpy()
+    ref = O.drafter_step(m, th, tok, emb, kv)
+    Bb = shape.backbone
+    m2 = O.Model(m.cfg, w)
+    m2.pre = np.concatenate([m.pre[:, Bb:], m.pre[:, :Bb]], axis=1)
+    emb2 = emb.copy()
+    th2 = th.copy()
+    for b in range(2):  # token b's embedding row becomes the hidden input and vice versa
+        emb2[int(tok[b])] = th[b]
+        th2[b] = emb[int(tok[b])]
+    got = O.drafter_step(m2, th2, tok, emb2, kv)
+    assert np.array_equal(got["hidden_out"], ref["hidden_out"])
+    assert np.array_equal(got["next"], ref["next"])
+
+
+def test_draft_block_equals_chained_steps():
+    m, w, shape = _tiny_model()
+    wl, d, kv = _tiny_inputs(shape)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    tok = d["last_token"].numpy()
+    blk = O.draft_block(m, 3, th, tok, emb, kv)
+    cur_h, cur_t = th.copy(), tok.copy()
+    for i in range(3):
+        s = O.drafter_step(m, cur_h, cur_t, emb, kv)
+        assert np.array_equal(s["hidden_out"], blk[i]["hidden_out"])
+        assert np.array_equal(s["next"], blk[i]["next"])
+        cur_h, cur_t = s["hidden_out"], s["next"]
+
+
+def test_step_rows_are_independent():
+    m, w, shape = _tiny_model()
+    wl, d, kv = _tiny_inputs(shape)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    tok = d["last_token"].numpy()
+    full = O.drafter_step(m, th, tok, emb, kv)
+    one = O.drafter_step(m, th, tok, emb, kv, rows=[2])
+    assert np.array_equal(one["hidden_out"][0], full["hidden_out"][2])
+    assert one["next"][0] == full["next"][2]
+
+
+# ---------------------------------------------------------------- shapes named on the pages
+
+
+def _param_count(shape):
+    H, Bb, F, Q, hd = shape.hidden, shape.backbone, shape.ffn, shape.q_dim, shape.head_dim
+    per_layer = Q * H + hd + H * Q + 4 * H + 3 * F * H + 1
+    return 2 * Bb * H + H * Bb + H + shape.vocab * H + shape.n_centroids * H + shape.n_layer * per_layer
+
+
+def test_page_constants_against_workload_shapes():
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    for shape in (synth.E2B, synth.E4B):
+        assert shape.vocab == g["vocab"]["value"]
+        assert shape.n_centroids == g["n_centroids"]["value"]
+        assert shape.top_k == g["top_k"]["value"]
+        assert shape.hidden == g["hidden"]["value"]
+        assert shape.n_layer == g["n_layer"]["value"]
+        assert shape.top_k * shape.vsc == 4096  # finite logits per row
+        # the pages quote about 76-78 M parameters; our FFN width (1024) gives ~74-75 M
+        assert abs(_param_count(shape) - g["params_approx_e2b_e4b"]["value"]) < 0.06 * g["params_approx_e2b_e4b"]["value"]
+    assert synth.E2B.backbone == g["backbone_e2b"]["value"]
+    assert synth.E4B.backbone == g["backbone_e4b"]["value"]
+
+
+def test_full_size_ordering_and_head_row():
+    shape = synth.E4B
+    perm = synth.permutation(0, synth.TID["ordering"], shape.vocab).numpy()
+    cfg = O.config_from(shape)
+    O.check_head_invariants(cfg, perm)
+    assert perm.max() < (1 << 18)
+    assert np.array_equal(perm.astype(np.float32).astype(np.int64), perm)  # exact in F32
+
+
+# ---------------------------------------------------------------- the input generator (shared with the GPU side)
+
+
+def test_generator_rows_match_full_tensor_and_distribution():
+    full = synth.gen_bf16(0, 77, (64, 96), 1.0)
+    rows = torch.tensor([3, 0, 63, 17])
+    part = synth.gen_bf16(0, 77, (64, 96), 1.0, row_index=rows)
+    assert torch.equal(part, full[rows])
+    v = O.bf16_to_f64(synth.gen_bf16(0, 78, (1 << 18,), 2.0).numpy())
+    assert abs(v.mean()) < 0.02 and abs(v.std() - 2.0) < 0.02
+
+
+# ---------------------------------------------------------------- structure of the decoder layer
+
+
+def test_sandwich_norm_scale_invariance():
+    """The sandwich norms make a layer's output independent of the scale of q_proj (q_norm), o_proj
+    (post_attention_norm), ffn_down (post_ffw_norm) and, since GeGLU is linear in the up branch, of ffn_up. With
+    eps = 0 and a factor of 2 (exact in bf16) the invariance is exact. A dropped norm, or gelu applied to the up branch
+    instead of the gate branch, breaks it."""
+    m, w, shape = _tiny_model(rms_eps=0.0)
+    wl, d, kv = _tiny_inputs(shape)
+    x = rng(12).standard_normal(shape.hidden)
+    for l in range(shape.n_layer):
+        ref = O.decoder_layer(m, l, x, 1, kv)
+        for key in ("q", "o", "down", "up"):
+            saved = m.layers[l][key].copy()
+            m.layers[l][key] = saved * 2.0
+            got = O.decoder_layer(m, l, x, 1, kv)
+            m.layers[l][key] = saved
+            assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), (l, key)
+        # the gate branch is not scale invariant (gelu is not homogeneous): a check that the test can fail
+        saved = m.layers[l]["gate"].copy()
+        m.layers[l]["gate"] = saved * 2.0
+        assert not np.allclose(O.decoder_layer(m, l, x, 1, kv), ref, rtol=1e-6)
+        m.layers[l]["gate"] = saved
+
+
+def test_attention_branch_closed_form_with_identical_keys():
+    """If every key of a kv head equals k (K = V), each query head reading it returns k whatever its query. With the
+    FFN branch zeroed, a layer then maps x to (x + RMSNorm(W_o [o_0;..;o_{n-1}], post_attention_norm)) * s with
+    o_h the constant key of head h's kv head: this pins the head-to-kv mapping, the head concatenation order and the
+    post-attention norm weight."""
+    m, w, shape = _tiny_model(n_kv_head=2)
+    wl, d, kv = _tiny_inputs(shape)
+    cfg = m.cfg
+    for t in range(2):
+        kv.k[t][:, 0] = kv.k[t][:, 0, :1]
+        kv.k[t][:, 1] = kv.k[t][:, 1, :1]
+    kv.v = kv.k
+    x = rng(13).standard_normal(cfg.hidden)
+    for l in range(cfg.n_layer):
+        m.layers[l]["down"][:] = 0.0
+        t = 1 if cfg.is_full(l) else 0
+        b = 2
+        k0 = O.bf16_to_f64(kv.k[t][b, 0, 0])
+        k1 = O.bf16_to_f64(kv.k[t][b, 1, 0])
+        o = np.concatenate([k0, k0, k1, k1])  # heads 0,1 -> kv 0; heads 2,3 -> kv 1
+        L = m.layers[l]
+        want = (x + O.rmsnorm(L["o"] @ o, L["post_attn_norm"], cfg.rms_eps)) * L["scale"]
+        got = O.decoder_layer(m, l, x, b, kv)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), l
