@@ -1,0 +1,168 @@
+/*
+ * mtpd.h - C ABI of the MI355X (gfx950) drafter-step library: one draft step of the Gemma 4 assistant
+ * (multi-token-prediction drafter), a block of chained steps, and the centroid-clustered masked LM head.
+ *
+ * Pages cited (by title; sections as headed on each page):
+ *   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
+ *   [Inventory]  "Gemma 4 Assistant (MTP drafter) - tensor inventory (Stage 0)"
+ *   [Guide]      "Gemma 4 Assistant 使用指南：用 MTP 投机解码与 KV Sharing 加速 Gemma 4 推理" (gitcode blog)
+ *   [Explained]  "Gemma 4 drafter explained" (techtwitter)
+ *
+ * Conventions for every entry point:
+ *   - Tensors are DEVICE memory owned by the caller unless marked HOST. bf16 values are passed as their uint16_t
+ *     bit patterns. Matrices are row-major [out][in] (the PyTorch nn.Linear layout, which is the GGUF [in, out]
+ *     shape of the [MTP doc] "Tensor schema" read as ne0 = in). Device pointers must be 16-byte aligned.
+ *   - Weights are borrowed by mtpd_create and must outlive the handle.
+ *   - Calls enqueue work on the caller's HIP stream (passed as void*, a hipStream_t; NULL = the null stream) and
+ *     return without synchronising it. All argument validation happens on the host before anything is enqueued;
+ *     on a negative return nothing was enqueued and mtpd_last_error() describes the problem.
+ *   - The workspace (device, caller-owned, mtpd_workspace_bytes(h, batch) bytes, 256-byte aligned) holds every
+ *     intermediate. Calls that share a workspace must be ordered on one stream.
+ *   - Arithmetic: bf16 storage (weights, caches, embeddings, target hidden, hidden_out), fp32 activations and
+ *     accumulation; top-k and argmax are taken on fp32 values (descending, ties to the lower index).
+ */
+#ifndef MTPD_H
+#define MTPD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MTPD_API __attribute__((visibility("default")))
+#else
+#define MTPD_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MTPD_OK = 0,
+  MTPD_EINVAL = -1, /* null required pointer, misaligned pointer, bad argument value */
+  MTPD_ESHAPE = -2, /* configuration or per-call sizes violate a structural rule */
+  MTPD_ENOMEM = -3, /* host or device allocation failed inside mtpd_create */
+  MTPD_EHIP = -4,   /* a HIP runtime call or kernel launch failed */
+  MTPD_EUNSUP = -5  /* valid per the pages but not implemented by this library */
+};
+
+#define MTPD_MAX_BATCH 64 /* rows per call */
+
+typedef struct mtpd_handle_s *mtpd_handle;
+
+/* Drafter hyper-parameters. [MTP doc] "Conversion" (backbone_hidden_size, num_centroids,
+ * centroid_intermediate_top_k), "Variants supported" (4 layers, hidden 256, KV heads); [Inventory]
+ * "HF config highlights" (three sliding + one full layer, attention_k_eq_v, vocab 262144).
+ * Rules checked by mtpd_create: all sizes > 0; vocab % n_centroids == 0; top_k <= n_centroids;
+ * n_head % n_kv_head == 0; head_dim even and <= 256; hidden, backbone, ffn, head_dim multiples of 8;
+ * vocab / n_centroids <= 1024; n_centroids <= 8192; n_head <= 8; n_layer <= 32. */
+typedef struct {
+  int32_t backbone;          /* target model width (1536 E2B, 2560 E4B) */
+  int32_t hidden;            /* drafter width (256) */
+  int32_t n_layer;           /* decoder layers (4) */
+  int32_t n_head;            /* query heads per layer */
+  int32_t n_kv_head;         /* heads of the shared cache */
+  int32_t head_dim;
+  int32_t ffn;               /* GeGLU intermediate width */
+  int32_t vocab;
+  int32_t n_centroids;       /* clusters of the masked head (2048); 0 is rejected (dense head: MTPD_EUNSUP) */
+  int32_t top_k;             /* clusters kept (32) */
+  int32_t swa_window;        /* keys read by a sliding layer */
+  uint32_t full_attn_layers; /* bit l set: layer l reads the full-attention cache, else the sliding one */
+  float rms_eps;
+  float attn_scale;          /* softmax scale applied to q.k */
+  float embed_scale;         /* factor on the embedded token before pre_projection (1.0) */
+} mtpd_config;
+
+/* Per-layer weights, names as in [MTP doc] "Tensor schema" (blk.{i}.*). Shapes row-major:
+ * attn_q [n_head*head_dim][hidden], attn_q_norm [head_dim], attn_output [hidden][n_head*head_dim],
+ * attn_norm / post_attention_norm / ffn_norm / post_ffw_norm [hidden], ffn_gate / ffn_up [ffn][hidden],
+ * ffn_down [hidden][ffn]. layer_output_scale is the layer's scalar gate ([MTP doc] "What it is"), passed by value. */
+typedef struct {
+  const uint16_t *attn_q, *attn_q_norm, *attn_output, *attn_norm, *post_attention_norm;
+  const uint16_t *ffn_norm, *post_ffw_norm, *ffn_gate, *ffn_up, *ffn_down;
+  float layer_output_scale;
+} mtpd_layer;
+
+/* Global weights ([MTP doc] "Tensor schema"; [Inventory] "Expected safetensors names"):
+ * pre_proj [hidden][2*backbone] (input = [target hidden ; token embedding]), post_proj [backbone][hidden],
+ * output_norm [hidden], token_embd [vocab][hidden] (the head table), centroids [n_centroids][hidden],
+ * token_ordering [vocab] int32, a permutation of the vocabulary viewed as [n_centroids][vocab/n_centroids]
+ * ([Inventory] "Centroid / ordered embeddings LM head", step 3). layers is a HOST array [n_layer]. */
+typedef struct {
+  const uint16_t *pre_proj, *post_proj, *output_norm, *token_embd, *centroids;
+  const int32_t *token_ordering;
+  const mtpd_layer *layers;
+} mtpd_weights;
+
+/* One shared cache of the target ([MTP doc] "Runtime implementation", piece 1; [Guide] section 2(4),
+ * shared_kv_states): k, v [batch][n_kv_head][cap][head_dim] bf16; v may equal k (K = V, [Inventory]
+ * "Notes for llama.cpp port" 2), in which case it is read once. len is a HOST array [batch]: row b's valid keys
+ * are [0, len[b]), 1 <= len[b] <= cap. */
+typedef struct {
+  const uint16_t *k, *v;
+  int32_t cap;
+  const int32_t *len;
+} mtpd_kv;
+
+/* The two caches a drafter layer can read, plus the rotary tables for each row's constant position
+ * ([Guide] section 2(2)): rope [batch][2 (0 sliding, 1 full)][2 (cos, sin)][head_dim/2] fp32, device. */
+typedef struct {
+  mtpd_kv sliding, full;
+  const float *rope;
+} mtpd_shared_kv;
+
+/* Validate the configuration and weights and build a handle. Copies token_ordering to the host once (a blocking
+ * copy on the null stream) to check that it is a permutation ([Inventory] "GGUF / converter layout",
+ * verification script). max_batch <= MTPD_MAX_BATCH. Returns MTPD_OK and *out, or a negative code. */
+MTPD_API int mtpd_create(const mtpd_config *cfg, const mtpd_weights *w, int32_t max_batch, mtpd_handle *out);
+
+/* Release a handle (NULL is a no-op). Does not touch caller memory. */
+MTPD_API void mtpd_destroy(mtpd_handle h);
+
+/* Bytes of workspace needed for calls with `batch` rows (0 on a bad handle or batch). */
+MTPD_API size_t mtpd_workspace_bytes(mtpd_handle h, int32_t batch);
+
+/* One drafter step for `batch` independent rows ([MTP doc] "What it is"; [Guide] sections 2 and 6;
+ * [Explained] "Target Activations", "KV Cache Sharing", "The Efficient Embedder"):
+ *   x = pre_proj [target_hidden[b] ; embed_scale * target_embd[last_token[b]]]
+ *   4 Q-only layers over the shared caches (sliding layers: the last min(window, len) keys; full: all len keys)
+ *   h = output_norm(x); hidden_out = post_proj h (bf16)
+ *   masked head: top_k of centroids.h, their vocab/n_centroids token ids through token_ordering, sparse logits
+ *   token_embd[id].h, a -1e30 row with the sparse logits scattered in, next_token = argmax.
+ * target_hidden [batch][backbone] bf16; last_token [batch] int32 in [0, vocab) (out-of-range ids are clamped
+ * into range); target_embd [vocab][backbone] bf16 (the target's input embedding table).
+ * Outputs: next_token [batch] int32, hidden_out [batch][backbone] bf16 (required); logits [batch][vocab] fp32,
+ * sel_centroids [batch][top_k] int32 (descending score), sparse_ids / sparse_logits [batch][top_k*vsc]
+ * (optional, NULL to skip). */
+MTPD_API int mtpd_drafter_step(mtpd_handle h, void *stream, void *workspace, int32_t batch, const uint16_t *target_hidden,
+                      const int32_t *last_token, const uint16_t *target_embd, const mtpd_shared_kv *kv,
+                      float *logits, int32_t *next_token, uint16_t *hidden_out, int32_t *sel_centroids,
+                      int32_t *sparse_ids, float *sparse_logits);
+
+/* n >= 1 chained drafter steps at the constant position over the same caches ([Guide] section 2(3): within a
+ * draft round the last-seen token is the drafter's own; [Explained] "Target Activations": later rounds take the
+ * drafter's own post-projected activations). Step i+1 reads step i's hidden_out and next token on the device.
+ * tokens [batch][n] int32 (required); logits [n][batch][vocab] fp32 (optional); hidden_out [batch][backbone]
+ * bf16 of the last step (required). */
+MTPD_API int mtpd_draft_block(mtpd_handle h, void *stream, void *workspace, int32_t batch, int32_t n,
+                     const uint16_t *target_hidden, const int32_t *last_token, const uint16_t *target_embd,
+                     const mtpd_shared_kv *kv, int32_t *tokens, float *logits, uint16_t *hidden_out);
+
+/* The masked head alone on m rows of fp32 hidden states h [m][hidden] (normed, as the head receives them):
+ * [Inventory] "Centroid / ordered embeddings LM head" steps 1-5. argmax [m] int32 required; logits [m][vocab],
+ * sel_centroids [m][top_k], sparse_ids / sparse_logits [m][top_k*vsc] optional. m <= max_batch. */
+MTPD_API int mtpd_masked_head(mtpd_handle h, void *stream, void *workspace, int32_t m, const float *hidden,
+                     float *logits, int32_t *argmax, int32_t *sel_centroids, int32_t *sparse_ids,
+                     float *sparse_logits);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+MTPD_API const char *mtpd_last_error(void);
+
+/* ABI version: 1. */
+MTPD_API int32_t mtpd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTPD_H */

@@ -1,0 +1,502 @@
+// Host runtime of the drafter-step library: argument validation, workspace plan and kernel sequencing behind the
+// C ABI declared in include/mtpd.h.
+//
+// Pages cited (by title; sections as headed on each page):
+//   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
+//   [Inventory]  "Gemma 4 Assistant (MTP drafter) - tensor inventory (Stage 0)"
+//   [Guide]      "Gemma 4 Assistant 使用指南：用 MTP 投机解码与 KV Sharing 加速 Gemma 4 推理" (gitcode blog)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "mtpd.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+namespace {
+
+constexpr int kGraphCache = 8;
+
+// Everything a captured call depends on: the graph of one (call, arguments) pair is replayed only when every
+// pointer, size and per-row window is the same.
+struct CallKey {
+  int32_t kind, batch, n;
+  const void* ptrs[16];
+  mtpd::RowWindows win[2];
+  int32_t nsplit[2];
+  int32_t caps[2];
+  bool operator==(const CallKey& o) const { return std::memcmp(this, &o, sizeof(CallKey)) == 0; }
+};
+
+struct GraphEntry {
+  CallKey key;
+  hipGraphExec_t exec = nullptr;
+  uint64_t used = 0;
+};
+
+}  // namespace
+
+struct mtpd_handle_s {
+  mtpd_config cfg;
+  mtpd_weights w;
+  std::vector<mtpd_layer> layers;
+  int32_t max_batch;
+  int32_t vsc;
+  bool use_graphs = true;
+  hipStream_t cap_stream = nullptr;
+  GraphEntry graphs[kGraphCache];
+  uint64_t tick = 0;
+};
+
+namespace {
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Offsets of every intermediate in the caller's workspace for a given batch.
+struct Plan {
+  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, cnt, total;
+  int ncnt_attn, ncnt;
+};
+
+Plan make_plan(const mtpd_config& c, int B, int vsc) {
+  Plan p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t H = c.hidden, Bb = c.backbone, QD = (size_t)c.n_head * c.head_dim, F = c.ffn;
+  p.x[0] = take((size_t)B * H * 4);
+  p.x[1] = take((size_t)B * H * 4);
+  p.q = take((size_t)B * QD * 4);
+  p.pacc = take((size_t)B * c.n_head * mtpd::kMaxSplit * c.head_dim * 4);
+  p.pml = take((size_t)B * c.n_head * mtpd::kMaxSplit * 2 * 4);
+  p.o = take((size_t)B * QD * 4);
+  p.t = take((size_t)B * H * 4);
+  p.m = take((size_t)B * F * 4);
+  p.d = take((size_t)B * H * 4);
+  p.h = take((size_t)B * H * 4);
+  p.hid = take((size_t)2 * B * Bb * 2);
+  p.tok = take((size_t)2 * B * 4);
+  p.scores = take((size_t)B * c.n_centroids * 4);
+  p.sel = take((size_t)B * c.top_k * 4);
+  p.ids = take((size_t)B * c.top_k * vsc * 4);
+  p.z = take((size_t)B * c.top_k * vsc * 4);
+  p.keys = take((size_t)B * c.top_k * 8);
+  p.ncnt_attn = B * c.n_kv_head;
+  p.ncnt = p.ncnt_attn + B;
+  p.cnt = take((size_t)p.ncnt * 4);
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_config(const mtpd_config* c) {
+  if (!c) return fail(MTPD_EINVAL, "config is NULL");
+  if (c->n_centroids == 0) return fail(MTPD_EUNSUP, "n_centroids == 0 (dense tied head) is not implemented");
+  if (c->backbone <= 0 || c->hidden <= 0 || c->n_layer <= 0 || c->n_head <= 0 || c->n_kv_head <= 0 ||
+      c->head_dim <= 0 || c->ffn <= 0 || c->vocab <= 0 || c->n_centroids <= 0 || c->top_k <= 0 ||
+      c->swa_window <= 0)
+    return fail(MTPD_ESHAPE, "every size in the config must be positive");
+  if (c->vocab % c->n_centroids != 0) return fail(MTPD_ESHAPE, "vocab %% n_centroids != 0");
+  if (c->top_k > c->n_centroids) return fail(MTPD_ESHAPE, "top_k > n_centroids");
+  if (c->n_head % c->n_kv_head != 0) return fail(MTPD_ESHAPE, "n_head %% n_kv_head != 0");
+  const int G = c->n_head / c->n_kv_head;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(MTPD_ESHAPE, "query heads per kv head must be 1, 2, 4 or 8");
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(MTPD_ESHAPE, "head_dim must be 64, 128 or 256");
+  if (c->hidden % 8 != 0 || c->backbone % 16 != 0 || c->ffn % 8 != 0)
+    return fail(MTPD_ESHAPE, "hidden and ffn must be multiples of 8, backbone a multiple of 16");
+  if (c->hidden > 4096 || c->ffn > 4096 || c->n_head * c->head_dim > 4096)
+    return fail(MTPD_ESHAPE, "hidden, ffn and n_head*head_dim must be <= 4096");
+  if (c->n_centroids > 8192) return fail(MTPD_ESHAPE, "n_centroids > 8192");
+  if (c->vocab / c->n_centroids > 1024) return fail(MTPD_ESHAPE, "vocab / n_centroids > 1024");
+  if (c->top_k > 1024) return fail(MTPD_ESHAPE, "top_k > 1024");
+  if (c->n_layer > 32) return fail(MTPD_ESHAPE, "n_layer > 32");
+  if (!(c->rms_eps >= 0.f) || !(c->attn_scale > 0.f)) return fail(MTPD_EINVAL, "rms_eps < 0 or attn_scale <= 0");
+  return MTPD_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MTPD_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MTPD_EINVAL, "%s is not 16-byte aligned", name);
+  return MTPD_OK;
+}
+
+#define CHECK(expr)                 \
+  do {                              \
+    int rc_ = (expr);               \
+    if (rc_ != MTPD_OK) return rc_; \
+  } while (0)
+
+#define LAUNCH(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(MTPD_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+int check_kv(const mtpd_handle_s* h, const mtpd_kv& kv, int B, const char* name, mtpd::RowWindows* win, bool full) {
+  char nm[64];
+  snprintf(nm, sizeof(nm), "%s.k", name);
+  CHECK(check_ptr(kv.k, nm));
+  snprintf(nm, sizeof(nm), "%s.v", name);
+  CHECK(check_ptr(kv.v, nm));
+  if (!kv.len) return fail(MTPD_EINVAL, "%s.len is NULL", name);
+  if (kv.cap <= 0) return fail(MTPD_ESHAPE, "%s.cap must be positive", name);
+  std::memset(win, 0, sizeof(*win));
+  for (int b = 0; b < B; ++b) {
+    const int L = kv.len[b];
+    if (L < 1 || L > kv.cap) return fail(MTPD_ESHAPE, "%s.len[%d] = %d outside [1, cap=%d]", name, b, L, kv.cap);
+    const int n = full ? L : std::min(L, h->cfg.swa_window);
+    win->start[b] = L - n;
+    win->count[b] = n;
+  }
+  return MTPD_OK;
+}
+
+// Splits of each row's key window: about one block per 256 CUs' share of the batch's keys, at least 128 keys per
+// block, at most kMaxSplit blocks per (row, kv head).
+int nsplit_for(const mtpd::RowWindows& win, int B, int nkv) {
+  int mx = 1;
+  long total = 0;
+  for (int b = 0; b < B; ++b) {
+    mx = std::max(mx, win.count[b]);
+    total += win.count[b];
+  }
+  long per = (total * nkv + 255) / 256;
+  per = std::max<long>(128, (per + 63) / 64 * 64);
+  int ns = (int)((mx + per - 1) / per);
+  return std::max(1, std::min(ns, mtpd::kMaxSplit));
+}
+
+// The head on fp32 hidden states h [B][H] in the workspace: top-k of precomputed scores, gather + dot (+ scatter),
+// argmax.
+int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const float* hsrc,
+             float* logits, int32_t* next, int32_t* next2, int stride2, int32_t* sel_out, int32_t* ids_out,
+             float* z_out) {
+  const mtpd_config& c = h->cfg;
+  int32_t* sel = sel_out ? sel_out : at<int32_t>(ws, p.sel);
+  int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, p.ids);
+  float* z = z_out ? z_out : at<float>(ws, p.z);
+  // [Inventory] "Centroid / ordered embeddings LM head", step 2: top_k of the centroid logits
+  LAUNCH(mtpd::launch_topk(s, B, at<float>(ws, p.scores), c.n_centroids, c.top_k, sel));
+  // steps 3-5: candidate ids, sparse logits, scatter into the (already filled) row, argmax
+  LAUNCH(mtpd::launch_head(s, B, c.top_k, h->vsc, c.hidden, sel, h->w.token_ordering, h->w.token_embd, hsrc, ids, z,
+                           logits, (size_t)c.vocab, at<uint64_t>(ws, p.keys), at<uint32_t>(ws, p.cnt) + p.ncnt_attn,
+                           next, next2, stride2));
+  return MTPD_OK;
+}
+
+// One drafter step on workspace buffers; input hidden `th` [B][Bb] and tokens `tok` [B].
+int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const uint16_t* th,
+             const int32_t* tok, const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win,
+             const int* nsplit, float* logits, int32_t* next, int32_t* next2, int stride2, uint16_t* hidden_out,
+             int32_t* sel_out, int32_t* ids_out, float* z_out) {
+  const mtpd_config& c = h->cfg;
+  const int H = c.hidden, Bb = c.backbone, QD = c.n_head * c.head_dim, F = c.ffn, nL = c.n_layer;
+  float* x[2] = {at<float>(ws, p.x[0]), at<float>(ws, p.x[1])};
+  float* q = at<float>(ws, p.q);
+  float* o = at<float>(ws, p.o);
+  float* t = at<float>(ws, p.t);
+  float* m = at<float>(ws, p.m);
+  float* d = at<float>(ws, p.d);
+  uint32_t* cnt = at<uint32_t>(ws, p.cnt);
+  // input assembly + pre_projection ([MTP doc] "What it is"; [Guide] section 2(3))
+  LAUNCH(mtpd::launch_pre(s, B, Bb, H, c.vocab, th, tok, temb, c.embed_scale, h->w.pre_proj, x[0], cnt, p.ncnt));
+  int cur = 0;
+  const size_t BV = (size_t)B * c.vocab;
+  for (int l = 0; l < nL; ++l) {
+    const mtpd_layer& L = h->layers[l];
+    const int type = ((c.full_attn_layers >> l) & 1u) ? 1 : 0;
+    const mtpd_kv& cache = type ? kv->full : kv->sliding;
+    mtpd::Residual rq{x[cur], nullptr, nullptr, 1.0f, nullptr};
+    if (l > 0) {
+      const mtpd_layer& P = h->layers[l - 1];
+      rq = mtpd::Residual{x[cur], d, P.post_ffw_norm, P.layer_output_scale, x[cur ^ 1]};
+      cur ^= 1;
+    }
+    LAUNCH(mtpd::launch_qproj(s, B, H, QD, rq, L.attn_norm, c.rms_eps, L.attn_q, q));
+    LAUNCH(mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
+                             cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale,
+                             at<float>(ws, p.pacc), at<float>(ws, p.pml), cnt, o));
+    LAUNCH(mtpd::launch_dense(s, B, QD, H, o, L.attn_output, t));
+    mtpd::Residual rf{x[cur], t, L.post_attention_norm, 1.0f, x[cur ^ 1]};
+    cur ^= 1;
+    mtpd::FillRange fr{nullptr, 0, 0};
+    if (logits) fr = mtpd::FillRange{logits, (BV * l / nL) & ~size_t(3), l + 1 == nL ? BV : (BV * (l + 1) / nL) & ~size_t(3)};
+    LAUNCH(mtpd::launch_ffn(s, B, H, F, rf, L.ffn_norm, c.rms_eps, L.ffn_gate, L.ffn_up, m, fr));
+    LAUNCH(mtpd::launch_dense(s, B, F, H, m, L.ffn_down, d));
+  }
+  const mtpd_layer& Last = h->layers[nL - 1];
+  mtpd::Residual rp{x[cur], d, Last.post_ffw_norm, Last.layer_output_scale, nullptr};
+  // output norm, post_projection (the next step's hidden input, [Guide] section 6) and centroid scores
+  LAUNCH(mtpd::launch_post(s, B, H, Bb, c.n_centroids, rp, h->w.output_norm, c.rms_eps, h->w.post_proj,
+                           h->w.centroids, at<float>(ws, p.h), hidden_out, at<float>(ws, p.scores)));
+  return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, next, next2, stride2, sel_out, ids_out, z_out);
+}
+
+int check_call(const mtpd_handle_s* h, void* ws, int B) {
+  if (!h) return fail(MTPD_EINVAL, "handle is NULL");
+  if (B < 1 || B > h->max_batch) return fail(MTPD_ESHAPE, "batch %d outside [1, max_batch=%d]", B, h->max_batch);
+  if (!ws) return fail(MTPD_EINVAL, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MTPD_EINVAL, "workspace is not 256-byte aligned");
+  return MTPD_OK;
+}
+
+int check_step_inputs(const mtpd_handle_s* h, int B, const uint16_t* th, const int32_t* tok, const uint16_t* temb,
+                      const mtpd_shared_kv* kv, mtpd::RowWindows* win, int* nsplit) {
+  CHECK(check_ptr(th, "target_hidden"));
+  if (!tok) return fail(MTPD_EINVAL, "last_token is NULL");
+  CHECK(check_ptr(temb, "target_embd"));
+  if (!kv) return fail(MTPD_EINVAL, "shared kv is NULL");
+  if (!kv->rope) return fail(MTPD_EINVAL, "rope is NULL");
+  CHECK(check_kv(h, kv->sliding, B, "sliding", &win[0], false));
+  CHECK(check_kv(h, kv->full, B, "full", &win[1], true));
+  nsplit[0] = nsplit_for(win[0], B, h->cfg.n_kv_head);
+  nsplit[1] = nsplit_for(win[1], B, h->cfg.n_kv_head);
+  return MTPD_OK;
+}
+
+// Run `body(stream)` on the caller's stream: replay a cached graph of the same call when there is one, capture
+// one otherwise; when the caller's stream is itself being captured, or graphs are off, launch directly.
+template <typename Body>
+int run_graphed(mtpd_handle_s* h, hipStream_t s, const CallKey& key, Body body) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (!h->use_graphs || hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone)
+    return body(s);
+  GraphEntry* hit = nullptr;
+  for (auto& e : h->graphs)
+    if (e.exec && e.key == key) hit = &e;
+  if (!hit) {
+    if (!h->cap_stream) LAUNCH(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+    GraphEntry* slot = &h->graphs[0];
+    for (auto& e : h->graphs) {
+      if (!e.exec) { slot = &e; break; }
+      if (e.used < slot->used) slot = &e;
+    }
+    LAUNCH(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+    int rc = body(h->cap_stream);
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
+    if (rc != MTPD_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(MTPD_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(MTPD_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+    if (slot->exec) (void)hipGraphExecDestroy(slot->exec);
+    slot->key = key;
+    slot->exec = exec;
+    hit = slot;
+  }
+  hit->used = ++h->tick;
+  LAUNCH(hipGraphLaunch(hit->exec, s));
+  return MTPD_OK;
+}
+
+CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs, const mtpd::RowWindows* win,
+                 const int* nsplit, const mtpd_shared_kv* kv) {
+  CallKey k;
+  std::memset(&k, 0, sizeof(k));
+  k.kind = kind;
+  k.batch = B;
+  k.n = n;
+  int i = 0;
+  for (const void* p : ptrs) k.ptrs[i++] = p;
+  if (win) {
+    k.win[0] = win[0];
+    k.win[1] = win[1];
+    k.nsplit[0] = nsplit[0];
+    k.nsplit[1] = nsplit[1];
+  }
+  if (kv) {
+    k.caps[0] = kv->sliding.cap;
+    k.caps[1] = kv->full.cap;
+  }
+  return k;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mtpd_abi_version(void) { return 1; }
+
+const char* mtpd_last_error(void) { return g_last_error.c_str(); }
+
+int mtpd_create(const mtpd_config* cfg, const mtpd_weights* w, int32_t max_batch, mtpd_handle* out) {
+  g_last_error.clear();
+  if (!out) return fail(MTPD_EINVAL, "out is NULL");
+  *out = nullptr;
+  CHECK(check_config(cfg));
+  if (!w) return fail(MTPD_EINVAL, "weights are NULL");
+  if (max_batch < 1 || max_batch > MTPD_MAX_BATCH) return fail(MTPD_ESHAPE, "max_batch outside [1, %d]", MTPD_MAX_BATCH);
+  CHECK(check_ptr(w->pre_proj, "pre_proj"));
+  CHECK(check_ptr(w->post_proj, "post_proj"));
+  CHECK(check_ptr(w->output_norm, "output_norm"));
+  CHECK(check_ptr(w->token_embd, "token_embd"));
+  CHECK(check_ptr(w->centroids, "centroids"));
+  CHECK(check_ptr(w->token_ordering, "token_ordering"));
+  if (!w->layers) return fail(MTPD_EINVAL, "layers is NULL");
+  for (int l = 0; l < cfg->n_layer; ++l) {
+    const mtpd_layer& L = w->layers[l];
+    const void* ps[10] = {L.attn_q, L.attn_q_norm, L.attn_output, L.attn_norm, L.post_attention_norm,
+                          L.ffn_norm, L.post_ffw_norm, L.ffn_gate, L.ffn_up, L.ffn_down};
+    static const char* names[10] = {"attn_q", "attn_q_norm", "attn_output", "attn_norm", "post_attention_norm",
+                                    "ffn_norm", "post_ffw_norm", "ffn_gate", "ffn_up", "ffn_down"};
+    for (int i = 0; i < 10; ++i) {
+      char nm[64];
+      snprintf(nm, sizeof(nm), "layers[%d].%s", l, names[i]);
+      CHECK(check_ptr(ps[i], nm));
+    }
+  }
+  // token_ordering must list every token once ([Inventory] "GGUF / converter layout", verification)
+  std::vector<int32_t> ord((size_t)cfg->vocab);
+  hipError_t e = hipMemcpy(ord.data(), w->token_ordering, ord.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MTPD_EHIP, "copying token_ordering: %s", hipGetErrorString(e));
+  std::vector<uint8_t> seen((size_t)cfg->vocab, 0);
+  for (size_t i = 0; i < ord.size(); ++i) {
+    const int32_t v = ord[i];
+    if (v < 0 || v >= cfg->vocab || seen[(size_t)v])
+      return fail(MTPD_ESHAPE, "token_ordering is not a permutation (entry %zu = %d)", i, v);
+    seen[(size_t)v] = 1;
+  }
+  mtpd_handle_s* hh = new (std::nothrow) mtpd_handle_s();
+  if (!hh) return fail(MTPD_ENOMEM, "out of host memory");
+  hh->cfg = *cfg;
+  hh->w = *w;
+  hh->layers.assign(w->layers, w->layers + cfg->n_layer);
+  hh->w.layers = nullptr;
+  hh->max_batch = max_batch;
+  hh->vsc = cfg->vocab / cfg->n_centroids;
+  const char* g = getenv("MTPD_GRAPHS");
+  hh->use_graphs = !(g && g[0] == '0');
+  *out = hh;
+  return MTPD_OK;
+}
+
+void mtpd_destroy(mtpd_handle h) {
+  if (!h) return;
+  for (auto& e : h->graphs)
+    if (e.exec) (void)hipGraphExecDestroy(e.exec);
+  if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+  delete h;
+}
+
+size_t mtpd_workspace_bytes(mtpd_handle h, int32_t batch) {
+  if (!h || batch < 1 || batch > h->max_batch) return 0;
+  return make_plan(h->cfg, batch, h->vsc).total;
+}
+
+int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batch, const uint16_t* target_hidden,
+                      const int32_t* last_token, const uint16_t* target_embd, const mtpd_shared_kv* kv,
+                      float* logits, int32_t* next_token, uint16_t* hidden_out, int32_t* sel_centroids,
+                      int32_t* sparse_ids, float* sparse_logits) {
+  g_last_error.clear();
+  CHECK(check_call(h, workspace, batch));
+  mtpd::RowWindows win[2];
+  int nsplit[2];
+  CHECK(check_step_inputs(h, batch, target_hidden, last_token, target_embd, kv, win, nsplit));
+  if (!next_token) return fail(MTPD_EINVAL, "next_token is NULL");
+  CHECK(check_ptr(hidden_out, "hidden_out"));
+  if (logits) CHECK(check_ptr(logits, "logits"));
+  const Plan p = make_plan(h->cfg, batch, h->vsc);
+  const CallKey key = make_key(1, batch, 1,
+                               {workspace, target_hidden, last_token, target_embd, kv->sliding.k, kv->sliding.v,
+                                kv->full.k, kv->full.v, kv->rope, logits, next_token, hidden_out, sel_centroids,
+                                sparse_ids, sparse_logits},
+                               win, nsplit, kv);
+  return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
+    return run_step(h, s, workspace, p, batch, target_hidden, last_token, target_embd, kv, win, nsplit, logits,
+                    next_token, nullptr, 0, hidden_out, sel_centroids, sparse_ids, sparse_logits);
+  });
+}
+
+int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch, int32_t n,
+                     const uint16_t* target_hidden, const int32_t* last_token, const uint16_t* target_embd,
+                     const mtpd_shared_kv* kv, int32_t* tokens, float* logits, uint16_t* hidden_out) {
+  g_last_error.clear();
+  CHECK(check_call(h, workspace, batch));
+  if (n < 1 || n > 64) return fail(MTPD_ESHAPE, "n must be in [1, 64]");
+  mtpd::RowWindows win[2];
+  int nsplit[2];
+  CHECK(check_step_inputs(h, batch, target_hidden, last_token, target_embd, kv, win, nsplit));
+  if (!tokens) return fail(MTPD_EINVAL, "tokens is NULL");
+  CHECK(check_ptr(hidden_out, "hidden_out"));
+  if (logits) CHECK(check_ptr(logits, "logits"));
+  const Plan p = make_plan(h->cfg, batch, h->vsc);
+  const size_t BV = (size_t)batch * h->cfg.vocab;
+  const CallKey key = make_key(2, batch, n,
+                               {workspace, target_hidden, last_token, target_embd, kv->sliding.k, kv->sliding.v,
+                                kv->full.k, kv->full.v, kv->rope, logits, tokens, hidden_out},
+                               win, nsplit, kv);
+  return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
+    uint16_t* hid[2] = {at<uint16_t>(workspace, p.hid),
+                        at<uint16_t>(workspace, p.hid) + (size_t)batch * h->cfg.backbone};
+    int32_t* tk[2] = {at<int32_t>(workspace, p.tok), at<int32_t>(workspace, p.tok) + batch};
+    for (int i = 0; i < n; ++i) {
+      const uint16_t* th = (i == 0) ? target_hidden : hid[(i - 1) & 1];
+      const int32_t* tok = (i == 0) ? last_token : tk[(i - 1) & 1];
+      uint16_t* hout = (i == n - 1) ? hidden_out : hid[i & 1];
+      CHECK(run_step(h, s, workspace, p, batch, th, tok, target_embd, kv, win, nsplit,
+                     logits ? logits + (size_t)i * BV : nullptr, tk[i & 1], tokens + i, n, hout, nullptr, nullptr,
+                     nullptr));
+    }
+    return MTPD_OK;
+  });
+}
+
+int mtpd_masked_head(mtpd_handle h, void* stream, void* workspace, int32_t m, const float* hidden, float* logits,
+                     int32_t* argmax, int32_t* sel_centroids, int32_t* sparse_ids, float* sparse_logits) {
+  g_last_error.clear();
+  CHECK(check_call(h, workspace, m));
+  CHECK(check_ptr(hidden, "hidden"));
+  if (!argmax) return fail(MTPD_EINVAL, "argmax is NULL");
+  if (logits) CHECK(check_ptr(logits, "logits"));
+  const Plan p = make_plan(h->cfg, m, h->vsc);
+  const mtpd_config& c = h->cfg;
+  const CallKey key = make_key(3, m, 1, {workspace, hidden, logits, argmax, sel_centroids, sparse_ids, sparse_logits},
+                               nullptr, nullptr, nullptr);
+  return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
+    // [Inventory] "Centroid / ordered embeddings LM head", step 1: centroid logits
+    LAUNCH(mtpd::launch_zero_u32(s, at<uint32_t>(workspace, p.cnt), p.ncnt));
+    LAUNCH(mtpd::launch_dense(s, m, c.hidden, c.n_centroids, hidden, h->w.centroids, at<float>(workspace, p.scores)));
+    if (logits) LAUNCH(mtpd::launch_fill(s, logits, (size_t)m * c.vocab));
+    return run_head(h, s, workspace, p, m, hidden, logits, argmax, nullptr, 0, sel_centroids, sparse_ids,
+                    sparse_logits);
+  });
+}
+
+}  // extern "C"

@@ -4,14 +4,11 @@ TEST INFRASTRUCTURE ONLY. This module is the slow, plain, obviously-correct defi
 against. Only the test suite, the package smoke check and the benchmark's CPU-baseline leg may import it; the product
 path never calls it and shares no code with it (it uses NumPy only: no torch, no ctypes, nothing from the package).
 
-Arithmetic: IEEE fp64 everywhere, except at the rounding points that the step's precision contract fixes (they are
-taken identically by the GPU path):
-  R0  stored tensors are bf16 (weights, embeddings, K/V, target hidden); token ordering int32; rotary tables fp32;
-  R1  the input vector of every matrix product is rounded to bf16 (fp64 -> fp32 round-to-nearest -> bf16 RNE);
-  R2  each query head is rounded to bf16 after its q_norm and rotation;
-  R3  hidden_out is rounded to bf16;
-  and integer decisions (top-k of centroid scores, argmax of the logits row) are taken on fp32 values, the precision
-  the GPU takes them in.
+Arithmetic: IEEE fp64 everywhere. The only quantisation inside a step is the one the interface fixes: the
+post-projected hidden state handed back to the caller (and fed to the next drafted step) is bf16 like every other
+stored activation of the target (fp64 -> fp32 round-to-nearest -> bf16 round-to-nearest-even). Stored inputs are bf16
+(weights, embeddings, K/V, target hidden), the token ordering int32, the rotary tables fp32. Integer decisions
+(top-k of the centroid scores, argmax of the logits row) are taken on fp32 values, the precision the GPU takes them in.
 
 Pages cited (by title; sections as headed on each page):
   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
@@ -27,7 +24,9 @@ Readings where the pages are silent or disagree (each also listed in the design 
   * GeGLU = gelu_tanh(gate) * up; layer_scalar multiplies the residual stream after the FFN residual add;
   * rotary: half-split pairs (i, i + d/2) with per-row fp32 cos/sin tables for the constant position;
   * top-k order: descending fp32 score, ties to the lower centroid index; argmax ties to the lowest token id;
-  * mask value: fp32(-1e30) ([Inventory] "Centroid / ordered embeddings LM head", step 5).
+  * mask value: fp32(-1e30) ([Inventory] "Centroid / ordered embeddings LM head", step 5);
+  * precision: the configurations state bf16 weights with fp32 accumulation and nothing about rounding activations,
+    so activations stay unrounded (fp64 here, fp32 on the GPU) and only stored tensors are bf16.
 """
 from __future__ import annotations
 
@@ -40,7 +39,7 @@ NEG_FILL_F32 = np.float32(-1e30)  # [Inventory] "Centroid / ordered embeddings L
 
 
 # ----------------------------------------------------------------------------------------------------------------
-# number formats (R0-R3)
+# number formats
 
 
 def bf16_to_f64(bits) -> np.ndarray:
@@ -59,7 +58,7 @@ def bf16_bits(x) -> np.ndarray:
 
 
 def round_bf16(x) -> np.ndarray:
-    """Value of x after the R1 rounding (fp64 -> fp32 -> bf16), returned as fp64."""
+    """Value of x after rounding to bf16 (fp64 -> fp32 -> bf16), returned as fp64."""
     return bf16_to_f64(bf16_bits(x))
 
 
@@ -242,7 +241,7 @@ def decoder_layer(m: Model, l: int, x: np.ndarray, b: int, kv: SharedKV) -> np.n
     cfg, L = m.cfg, m.layers[l]
     t = 1 if cfg.is_full(l) else 0
     r = x
-    u = round_bf16(rmsnorm(x, L["attn_norm"], cfg.rms_eps))                                   # R1
+    u = rmsnorm(x, L["attn_norm"], cfg.rms_eps)
     q = (L["q"] @ u).reshape(cfg.n_head, cfg.head_dim)
     cos, sin = kv.rope[b, t, 0], kv.rope[b, t, 1]
     length = int(kv.lens[t][b])
@@ -250,21 +249,20 @@ def decoder_layer(m: Model, l: int, x: np.ndarray, b: int, kv: SharedKV) -> np.n
     o = np.empty((cfg.n_head, cfg.head_dim))
     for h in range(cfg.n_head):
         g = h * cfg.n_kv_head // cfg.n_head
-        qh = round_bf16(rope_rotate(rmsnorm(q[h], L["q_norm"], cfg.rms_eps), cos, sin))         # R2
+        qh = rope_rotate(rmsnorm(q[h], L["q_norm"], cfg.rms_eps), cos, sin)
         K = bf16_to_f64(kv.k[t][b, g, a0:a1])
         V = K if kv.v[t] is kv.k[t] else bf16_to_f64(kv.v[t][b, g, a0:a1])
         o[h] = attend(qh, K, V, cfg.attn_scale)
-    o = round_bf16(o.reshape(-1))                                                               # R1
-    x = r + rmsnorm(L["o"] @ o, L["post_attn_norm"], cfg.rms_eps)
+    x = r + rmsnorm(L["o"] @ o.reshape(-1), L["post_attn_norm"], cfg.rms_eps)
     r = x
-    u = round_bf16(rmsnorm(x, L["ffn_norm"], cfg.rms_eps))                                    # R1
-    mm = round_bf16(gelu_tanh(L["gate"] @ u) * (L["up"] @ u))                                  # R1
+    u = rmsnorm(x, L["ffn_norm"], cfg.rms_eps)
+    mm = gelu_tanh(L["gate"] @ u) * (L["up"] @ u)
     x = (r + rmsnorm(L["down"] @ mm, L["post_ffw_norm"], cfg.rms_eps)) * L["scale"]
     return x
 
 
 def masked_head_row(m: Model, h: np.ndarray, want_row: bool = False) -> Dict[str, object]:
-    """Centroid-clustered masked LM head for one bf16-valued h [hidden].
+    """Centroid-clustered masked LM head for one normed hidden state h [hidden].
 
     [Inventory] "Centroid / ordered embeddings LM head": centroid logits = centroids . h; top_k of them; the
     ordering viewed as [n_centroids][vsc] lists each centroid's vsc token ids; those rows of the token embedding
@@ -319,13 +317,13 @@ def drafter_step(m: Model, target_hidden, last_token, target_embd, kv: SharedKV,
     if want_rows:
         res["row"] = []
     for i, b in enumerate(rows):
-        e = round_bf16(cfg.embed_scale * bf16_to_f64(target_embd[int(tok[b])]))                 # R1 (exact at 1.0)
+        e = cfg.embed_scale * bf16_to_f64(target_embd[int(tok[b])])
         x0 = np.concatenate([bf16_to_f64(th[b]), e])
         x = m.pre @ x0
         for l in range(cfg.n_layer):
             x = decoder_layer(m, l, x, b, kv)
-        h = round_bf16(rmsnorm(x, m.out_norm, cfg.rms_eps))                                     # R1
-        res["hidden_out"][i] = bf16_bits(m.post @ h)                                           # R3
+        h = rmsnorm(x, m.out_norm, cfg.rms_eps)
+        res["hidden_out"][i] = bf16_bits(m.post @ h)  # handed back in bf16, the target's activation format
         hd = masked_head_row(m, h, want_row=want_rows)
         res["next"][i] = hd["next"]
         for k in ("sel", "ids", "z", "scores", "cgap", "margin"):

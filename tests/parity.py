@@ -1,0 +1,138 @@
+"""Shared helpers of the GPU parity tests: build one case's inputs for both sides from the seeded generators, and
+compare the HIP outputs with the oracle under the parity rules.
+
+Parity rules:
+  * selected-centroid sets identical on every row where the oracle's 32nd-33rd fp32 score gap exceeds 1e-3;
+  * drafted tokens identical where that holds and the oracle's top-1 minus top-2 logit margin exceeds 1e-3;
+  * floating outputs (sparse logits, hidden_out) within |gpu - ref| <= 2e-2 * max(|ref|, rms(ref row));
+  * every non-selected logit has exactly the bit pattern of fp32(-1e30).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle as O
+from fixtures import synth
+
+GAP = 1e-3
+RTOL = 2e-2
+NEG_BITS = 0xF149F2CA
+
+
+def to_dev(w, device="cuda"):
+    if isinstance(w, torch.Tensor):
+        return w.to(device)
+    if isinstance(w, dict):
+        return {k: to_dev(v, device) for k, v in w.items()}
+    if isinstance(w, list):
+        return [to_dev(v, device) for v in w]
+    return w
+
+
+class Case:
+    """Inputs of one parity case on both sides. Everything except the target's input embedding table is generated
+    on the CPU and copied to the GPU; that table is generated on the GPU and row-wise on the CPU by the same
+    counter-based generator (bit-identity of the two is itself tested)."""
+
+    def __init__(self, shape, batch: int, context: int, ragged: bool = False, seed: int = 0,
+                 distinct_v: bool = False, lens: Optional[Sequence[int]] = None, max_batch: Optional[int] = None):
+        from mtp_drafter_step_amd import Drafter, SharedKV
+        self.shape, self.batch = shape, batch
+        wl = synth.Workload("case", shape, batch=batch, context=context, n_steps=1, ragged=ragged, seed=seed)
+        self.w = synth.make_weights(shape, seed=seed)
+        inp = synth.make_inputs(wl, with_target_embd=False, distinct_v=distinct_v)
+        if lens is not None:
+            inp["len_sliding"] = list(lens)
+            inp["len_full"] = list(lens)
+            inp["positions"] = list(lens)
+            inp["rope"] = torch.from_numpy(synth.rope_tables(shape, list(lens)))
+        self.inp = inp
+        self.model = O.Model(O.config_from(shape), self.w)
+        ks = [inp["k_sliding"].numpy().view(np.uint16), inp["k_full"].numpy().view(np.uint16)]
+        vs = ks if not distinct_v else [inp["v_sliding"].numpy().view(np.uint16), inp["v_full"].numpy().view(np.uint16)]
+        self.kv_cpu = O.SharedKV(k=ks, v=vs, lens=[inp["len_sliding"], inp["len_full"]], rope=inp["rope"].numpy())
+        self.temb_cpu = synth.LazyRows(seed, shape)
+        # device side
+        self.wg = to_dev(self.w)
+        self.temb = synth.gen_bf16(seed, synth.TID["target_embd"], (shape.vocab, shape.backbone), 1.0, device="cuda")
+        self.th = inp["target_hidden"].cuda()
+        self.tok = inp["last_token"].cuda()
+        kd = [inp["k_sliding"].cuda(), inp["k_full"].cuda()]
+        vd = [None, None] if not distinct_v else [inp["v_sliding"].cuda(), inp["v_full"].cuda()]
+        self.kv = SharedKV(kd[0], kd[1], inp["len_sliding"], inp["len_full"], inp["rope"].cuda(), vd[0], vd[1])
+        self.drafter = Drafter(shape, self.wg, max_batch=max_batch or max(batch, 1))
+
+    def oracle_step(self, rows=None, want_rows=False, th=None, tok=None):
+        th = self.inp["target_hidden"].numpy().view(np.uint16) if th is None else th
+        tok = self.inp["last_token"].numpy() if tok is None else tok
+        return O.drafter_step(self.model, th, tok, self.temb_cpu, self.kv_cpu, want_rows=want_rows, rows=rows)
+
+
+def rel_ok(got: np.ndarray, ref: np.ndarray, rtol: float = RTOL) -> bool:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    floor = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    return bool(np.all(np.abs(got - ref) <= rtol * np.maximum(np.abs(ref), floor)))
+
+
+@dataclasses.dataclass
+class Tally:
+    rows: int = 0
+    sel_checked: int = 0
+    tok_checked: int = 0
+
+    def summary(self):
+        return f"rows={self.rows} sel_checked={self.sel_checked} tok_checked={self.tok_checked}"
+
+
+def compare_head_row(tally: Tally, cfg, ref: Dict, r: int, sel: np.ndarray, ids: Optional[np.ndarray],
+                     z: Optional[np.ndarray], nxt: int, row: Optional[np.ndarray] = None, where: str = ""):
+    """Compare one row's head outputs (GPU arrays) with oracle result `ref` (row index r in the oracle's lists)."""
+    tally.rows += 1
+    ref_sel = np.asarray(ref["sel"][r])
+    if ref["cgap"][r] > GAP:
+        tally.sel_checked += 1
+        assert set(sel.tolist()) == set(ref_sel.tolist()), f"{where} row {r}: selected centroids differ"
+        # order: descending, and equal to the oracle's where adjacent gaps are clear
+        if ids is not None:
+            ref_map = dict(zip(np.asarray(ref["ids"][r]).tolist(), np.asarray(ref["z"][r]).tolist()))
+            got_map = dict(zip(ids.tolist(), z.tolist()))
+            assert set(got_map) == set(ref_map), f"{where} row {r}: candidate ids differ"
+            keys = sorted(ref_map)
+            assert rel_ok([got_map[k] for k in keys], [ref_map[k] for k in keys]), f"{where} row {r}: sparse logits"
+        if ref["margin"][r] > GAP:
+            tally.tok_checked += 1
+            assert nxt == ref["next"][r], f"{where} row {r}: next token {nxt} != {ref['next'][r]}"
+    if row is not None:
+        finite = row.view(np.uint32) != NEG_BITS
+        assert int(finite.sum()) == cfg.top_k * cfg.vsc, f"{where} row {r}: finite count {int(finite.sum())}"
+        if ids is not None:
+            assert set(np.nonzero(finite)[0].tolist()) == set(ids.tolist())
+            assert np.array_equal(row[ids], z), f"{where} row {r}: scattered values differ from sparse logits"
+        assert nxt == int(np.argmax(row)), f"{where} row {r}: next is not the argmax of the row"
+    # the drafted token must always be one of the candidate ids and their maximum
+    if ids is not None:
+        assert nxt in set(ids.tolist())
+        zmax = z.max()
+        assert nxt == int(ids[z == zmax].min())
+
+
+def compare_step(case: Case, out: Dict[str, torch.Tensor], ref: Dict, rows: Sequence[int], where: str = "step") -> Tally:
+    cfg = case.model.cfg
+    tally = Tally()
+    nxt = out["next"].cpu().numpy()
+    hid = out["hidden_out"].cpu().numpy().view(np.uint16)
+    sel = out["sel"].cpu().numpy() if "sel" in out else None
+    ids = out["ids"].cpu().numpy() if "ids" in out else None
+    z = out["z"].cpu().numpy() if "z" in out else None
+    logits = out.get("logits")
+    for i, b in enumerate(rows):
+        row = logits[b].cpu().numpy() if logits is not None else None
+        if sel is not None:
+            compare_head_row(tally, cfg, ref, i, sel[b], ids[b], z[b], int(nxt[b]), row, where)
+        assert rel_ok(O.bf16_to_f64(hid[b]), O.bf16_to_f64(ref["hidden_out"][i])), f"{where} row {b}: hidden_out"
+    return tally

@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fixtures import synth
+from parity import Case, Tally, compare_head_row, compare_step, rel_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mtp_drafter_step_amd import abi
+    abi.lib()  # fails loudly if the library is missing
+
+
+def test_generator_identical_on_gpu_and_cpu():
+    shape = synth.E2B
+    rows = torch.tensor([0, 1, 77777, 262143], dtype=torch.int64)
+    full_gpu = synth.gen_bf16(0, synth.TID["target_embd"], (shape.vocab, shape.backbone), 1.0, device="cuda")
+    got = full_gpu[rows.cuda()].cpu()
+    want = synth.gen_bf16(0, synth.TID["target_embd"], (shape.vocab, shape.backbone), 1.0, row_index=rows)
+    assert torch.equal(got, want)
+    w_cpu = synth.gen_bf16(3, 5, (512, 256), 0.0625)
+    w_gpu = synth.gen_bf16(3, 5, (512, 256), 0.0625, device="cuda").cpu()
+    assert torch.equal(w_cpu, w_gpu)
+
+
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_masked_head_parity(m):
+    say(f"masked_head m={m}")
+    case = Case(synth.E4B, batch=1, context=16, max_batch=64)
+    g = torch.Generator().manual_seed(100 + m)
+    h = torch.randn(m, 256, generator=g, dtype=torch.float32)
+    out = case.drafter.masked_head(h.cuda(), want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    tally = Tally()
+    for r in range(m):
+        ref = O.masked_head_row(case.model, h[r].numpy().astype(np.float64))
+        refl = {k: [ref[k]] for k in ("sel", "ids", "z", "cgap", "margin", "next")}
+        compare_head_row(tally, case.model.cfg, refl, 0, out["sel"][r].cpu().numpy(), out["ids"][r].cpu().numpy(),
+                         out["z"][r].cpu().numpy(), int(out["argmax"][r]), out["logits"][r].cpu().numpy(),
+                         where=f"head m={m}")
+    say(tally.summary())
+    assert tally.sel_checked >= m // 2
+
+
+STEP_CASES = {
+    # E2B-shaped, batch 1, shared context 256 (shorter than the sliding window: sliding == full)
+    "e2b_b1_ctx256": dict(shape=synth.E2B, batch=1, context=256),
+    # E4B-shaped, batch 16, context 8192 per sequence
+    "e4b_b16_ctx8192": dict(shape=synth.E4B, batch=16, context=8192),
+    # ragged lengths 700 - 37 b: windows partly full, several key tiles and a ragged last tile per row
+    "e4b_b6_ragged700": dict(shape=synth.E4B, batch=6, context=700, ragged=True),
+    # E4B with two KV heads (the variant table's E4B), distinct V caches
+    "e4b_nkv2_distinct_v": dict(shape=dataclasses.replace(synth.E4B, n_kv_head=2), batch=3, context=1000,
+                                distinct_v=True),
+    # window 1 and a row with a single key
+    "e2b_window1_len1": dict(shape=dataclasses.replace(synth.E2B, swa_window=1), batch=3, context=64,
+                             lens=[64, 1, 33]),
+    # the largest batch the ABI takes
+    "e2b_b64_ctx300": dict(shape=synth.E2B, batch=64, context=300, ragged=True),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_drafter_step_parity(name):
+    say(f"drafter_step case={name}")
+    kw = STEP_CASES[name]
+    case = Case(**kw)
+    out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    B = kw["batch"]
+    rows = list(range(B)) if B <= 16 else list(range(0, B, 7)) + [B - 1]
+    ref = case.oracle_step(rows=rows)
+    tally = compare_step(case, out, ref, rows, where=name)
+    say(tally.summary())
+    assert tally.sel_checked >= len(rows) // 2
+
+
+def test_drafter_step_is_deterministic():
+    case = Case(synth.E4B, batch=4, context=2000, ragged=True)
+    a = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    a = {k: v.clone() for k, v in a.items()}
+    b = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+BLOCK_CASES = {
+    "e2b_b1_ctx4096_block4": dict(shape=synth.E2B, batch=1, context=4096, n=4),
+    "e4b_b16_ctx8192_block4": dict(shape=synth.E4B, batch=16, context=8192, n=4),
+}
+
+
+@pytest.mark.parametrize("name", list(BLOCK_CASES))
+def test_draft_block_parity_teacher_forced(name):
+    say(f"draft_block case={name}")
+    kw = dict(BLOCK_CASES[name])
+    n = kw.pop("n")
+    case = Case(**kw)
+    out = case.drafter.draft_block(n, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    torch.cuda.synchronize()
+    toks = out["tokens"].cpu().numpy()  # [B][n]
+    logits = out["logits"]  # [n][B][V]
+    B = kw["batch"]
+    forced = toks.T.copy()
+    refs = O.draft_block(case.model, n, case.inp["target_hidden"].numpy().view(np.uint16),
+                         case.inp["last_token"].numpy(), case.temb_cpu, case.kv_cpu, forced_tokens=forced)
+    tally = Tally()
+    for i in range(n):
+        for b in range(B):
+            row = logits[i, b].cpu().numpy()
+            finite = row.view(np.uint32) != 0xF149F2CA
+            ids = np.nonzero(finite)[0]
+            r = refs[i]
+            tally.rows += 1
+            assert int(finite.sum()) == case.model.cfg.top_k * case.model.cfg.vsc
+            if r["cgap"][b] > 1e-3:
+                tally.sel_checked += 1
+                ref_ids = np.asarray(r["ids"][b])
+                assert set(ids.tolist()) == set(ref_ids.tolist()), f"step {i} row {b}: candidate set differs"
+                ref_map = dict(zip(ref_ids.tolist(), np.asarray(r["z"][b]).tolist()))
+                assert rel_ok(row[ids], [ref_map[k] for k in ids.tolist()]), f"step {i} row {b}: logits"
+                if r["margin"][b] > 1e-3:
+                    tally.tok_checked += 1
+                    assert int(toks[b, i]) == r["next"][b], f"step {i} row {b}: token"
+            assert int(toks[b, i]) == int(np.argmax(row))
+    hid = out["hidden_out"].cpu().numpy().view(np.uint16)
+    for b in range(B):
+        assert rel_ok(O.bf16_to_f64(hid[b]), O.bf16_to_f64(refs[-1]["hidden_out"][b])), f"row {b}: hidden_out"
+    say(tally.summary())
+    assert tally.sel_checked >= (n * B) // 2
+
+
+def test_draft_block_equals_chained_steps():
+    case = Case(synth.E4B, batch=5, context=1500, ragged=True)
+    n = 3
+    blk = case.drafter.draft_block(n, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    blk = {k: v.clone() for k, v in blk.items()}
+    th, tok = case.th.clone(), case.tok.clone()
+    for i in range(n):
+        s = case.drafter.drafter_step(th, tok, case.temb, case.kv, want_logits=True)
+        assert torch.equal(s["next"], blk["tokens"][:, i].contiguous()), i
+        assert torch.equal(s["logits"], blk["logits"][i]), i
+        th, tok = s["hidden_out"].clone(), s["next"].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(th, blk["hidden_out"])
+
+
+def test_graph_replays_match_direct_launches():
+    """The same call replayed from a captured graph, interleaved with other work and synchronisations, gives
+    bit-identical results to direct launches (graphs disabled) every time."""
+    import os
+    from mtp_drafter_step_amd import Drafter
+    case = Case(synth.E4B, batch=4, context=1200, ragged=True)
+    os.environ["MTPD_GRAPHS"] = "0"
+    try:
+        direct = Drafter(case.shape, case.wg, max_batch=4)
+    finally:
+        del os.environ["MTPD_GRAPHS"]
+    ref = direct.draft_block(3, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    ref = {k: v.clone() for k, v in ref.items()}
+    for rep in range(4):
+        out = case.drafter.draft_block(3, case.th, case.tok, case.temb, case.kv, want_logits=True)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), (rep, k)
+        # unrelated eager work between replays
+        other = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_sparse=True)
+        torch.cuda.synchronize()
+        assert other["next"].shape[0] == 4
