@@ -53,9 +53,9 @@ typedef struct mtpd_handle_s *mtpd_handle;
 /* Drafter hyper-parameters. [MTP doc] "Conversion" (backbone_hidden_size, num_centroids,
  * centroid_intermediate_top_k), "Variants supported" (4 layers, hidden 256, KV heads); [Inventory]
  * "HF config highlights" (three sliding + one full layer, attention_k_eq_v, vocab 262144).
- * Rules checked by mtpd_create: all sizes > 0; vocab % n_centroids == 0; top_k <= n_centroids;
- * n_head % n_kv_head == 0; head_dim even and <= 256; hidden, backbone, ffn, head_dim multiples of 8;
- * vocab / n_centroids <= 1024; n_centroids <= 8192; n_head <= 8; n_layer <= 32. */
+ * Rules checked by mtpd_create: all sizes > 0; vocab % n_centroids == 0; top_k <= min(n_centroids, 64);
+ * n_head / n_kv_head in {1,2,4,8}; head_dim in {64,128,256}; hidden, backbone, ffn, n_head*head_dim multiples
+ * of 256 (hidden <= 1024); vocab / n_centroids a multiple of 16, <= 1024; n_centroids <= 4096; n_layer <= 32. */
 typedef struct {
   int32_t backbone;          /* target model width (1536 E2B, 2560 E4B) */
   int32_t hidden;            /* drafter width (256) */

@@ -2,6 +2,7 @@
 // stream; every launcher returns the hipError_t of its launch.
 //
 // Activations are fp32 throughout; stored tensors (weights, caches, embeddings, target hidden) are bf16.
+// Kernels never synchronise with each other inside a launch: every cross-block dependency is a kernel boundary.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -11,6 +12,8 @@ namespace mtpd {
 constexpr int kMaxBatch = 64;  // rows per call (matches MTPD_MAX_BATCH)
 constexpr int kMaxSplit = 32;  // key-range splits of one (row, kv head)
 constexpr int kRowGroup = 4;   // batch rows handled together by the dense kernels
+constexpr int kMaxTopK = 64;   // clusters kept per row
+constexpr int kMaxCentroids = 4096;
 
 // Per-row key window [start, start + count) of one cache, passed by value.
 struct RowWindows {
@@ -34,21 +37,34 @@ struct FillRange {
   size_t begin, end;
 };
 
-// x[b] = W_pre [target_hidden[b] ; escale * target_embd[tok[b]]] ; also zeroes `counters`.
-hipError_t launch_pre(hipStream_t s, int B, int Bb, int H, int V, const uint16_t* th, const int32_t* tok,
-                      const uint16_t* emb, float escale, const uint16_t* w_pre, float* x, uint32_t* counters,
-                      int ncounters);
+// Token input of a step: either ids (tok[b]) or the previous step's per-cluster argmax keys (keys[b][k]), whose
+// maximum decides the token; in that case block column 0 also records it to out[b*out_stride] and next[b].
+struct TokenSource {
+  const int32_t* tok;
+  const uint64_t* keys;
+  int k;
+  int32_t* out;
+  int out_stride;
+  int32_t* next;
+};
+
+// x[b] = W_pre [target_hidden[b] ; escale * target_embd[tok[b]]]
+hipError_t launch_pre(hipStream_t s, int B, int Bb, int H, int V, const uint16_t* th, TokenSource ts,
+                      const uint16_t* emb, float escale, const uint16_t* w_pre, float* x);
 
 // q[b] = W_q RMSNorm(x_new[b]; w_norm)   (raw q, before q_norm and rotation)
 hipError_t launch_qproj(hipStream_t s, int B, int H, int QD, Residual res, const uint16_t* w_norm, float eps,
                         const uint16_t* w_q, float* q);
 
-// Split-K single-query attention with q_norm + rotation in the prologue; the last block of each (row, kv head)
-// merges the splits into o[b][h*hd + d] (fp32).
+// Single-query attention with q_norm + rotation in the prologue. nsplit == 1: o[b][h*hd + d] directly (fp32);
+// nsplit > 1: unnormalised partials (pacc, pml) for launch_attn_merge.
 hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
                        float eps, const float* rope, int type, const uint16_t* K, const uint16_t* V, int cap,
-                       const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, uint32_t* cnt,
-                       float* o);
+                       const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, float* o);
+
+// Log-sum-exp merge of the split partials into o.
+hipError_t launch_attn_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
+                             float* o);
 
 // y[b] = W X[b] for fp32 X rows of width K (o_proj: K = n_head*head_dim, down: K = ffn), N outputs.
 hipError_t launch_dense(hipStream_t s, int B, int K, int N, const float* X, const uint16_t* w, float* y);
@@ -62,19 +78,20 @@ hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res,
                        const uint16_t* w_post, const uint16_t* w_cen, float* h_out, uint16_t* hidden_out,
                        float* scores);
 
-// Top-k of C fp32 scores per row, descending, ties to the lower index.
-hipError_t launch_topk(hipStream_t s, int B, const float* scores, int C, int k, int32_t* sel);
+// Masked head: per (row, selected slot j): top-k of the row's centroid scores (descending, ties to the lower
+// index), the cluster's token ids through the ordering, sparse logits token_embd[id] . h, optional scatter into
+// logits, and the slot's best (value, id) key (larger value, then lower id).
+hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,
+                       const int32_t* ordering, const uint16_t* E, const float* h, int32_t* sel, int32_t* ids,
+                       float* z, float* logits, size_t V, uint64_t* keys);
 
-// Sparse head: ids = ordering[sel*vsc + t], z = token_embd[id] . h, optional scatter into logits, and the argmax
-// (ties to the lowest id) written to next[b] and, if set, out2[b*stride2].
-hipError_t launch_head(hipStream_t s, int B, int k, int vsc, int H, const int32_t* sel, const int32_t* ordering,
-                       const uint16_t* E, const float* h, int32_t* ids, float* z, float* logits, size_t V,
-                       uint64_t* keys, uint32_t* cnt, int32_t* next, int32_t* out2, int stride2);
-
-// p[0, n) = 0
-hipError_t launch_zero_u32(hipStream_t s, uint32_t* p, int n);
+// next[b] = token of the largest key in keys[b][0, k); also out2[b*stride2] when set.
+hipError_t launch_final(hipStream_t s, int B, int k, const uint64_t* keys, int32_t* next, int32_t* out2, int stride2);
 
 // logits[0, n) = -1e30
 hipError_t launch_fill(hipStream_t s, float* logits, size_t n);
+
+// y[b][n] = centroids[n] . h[b] for the masked head on caller-provided states (K = H, N = C).
+hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, const uint16_t* w_cen, float* scores);
 
 }  // namespace mtpd

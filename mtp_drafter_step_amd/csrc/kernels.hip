@@ -8,18 +8,31 @@
 // Numerics: bf16 storage, fp32 activations and accumulation; integer decisions (top-k, argmax) on fp32 values
 // with ties to the lower index.
 //
+// Latency rules followed throughout (every stage of a drafter step is latency-bound except the long attention and
+// the head gather): loads are issued unconditionally from clamped addresses and masked afterwards, with trip counts
+// that the compiler can see are wave-uniform, so that a wave keeps all its loads in flight at once; weights that do
+// not depend on the previous stage are requested before the block waits on that stage's activations; no block
+// waits on another block inside a launch.
+//
 // Dense kernels: a block owns a tile of outputs for a group of 4 batch rows; each wave computes a few outputs for
-// the 4 rows with lanes striding the reduction dimension, then a butterfly transpose-reduction leaves one finished
-// (row, output) sum per lane group. Inputs that need a norm are normalised once per block into LDS.
+// the 4 rows with lanes striding the reduction dimension (4 elements per lane per 256-wide chunk), then a butterfly
+// transpose-reduction leaves one finished (row, output) sum per lane group.
 #include "kernels.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace mtpd {
 
 namespace {
 
 constexpr int kRG = kRowGroup;
+constexpr int kMaxPL = 16;   // fp32 row elements per lane in the norm prologue (H <= 1024)
+constexpr int kMaxIt = 16;   // 256-wide reduction chunks per dense product (K <= 4096)
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -44,27 +57,22 @@ __device__ __forceinline__ uint32_t f32_order(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-  return ((uint64_t)hi << 32) | lo;
+// (value, id) key: larger value first, then lower id
+__device__ __forceinline__ uint64_t vid_key(float v, uint32_t id) {
+  return ((uint64_t)f32_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - id);
 }
+__device__ __forceinline__ int32_t key_id(uint64_t k) { return (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)); }
+
+__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = u64_max(v, shfl_xor_u64(v, o));
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    v = u64_max(v, ((uint64_t)hi << 32) | lo);
+  }
   return v;
-}
-
-// max over a 256-thread block; every thread gets the result. `red` holds 4 entries.
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
-  v = wave_max_u64(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return u64_max(u64_max(red[0], red[1]), u64_max(red[2], red[3]));
 }
 
 __device__ __forceinline__ float gelu_tanh(float a) {
@@ -76,8 +84,9 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Butterfly transpose-reduction of V per-lane values over the 64 lanes. Afterwards v[0] of lane l holds the
-// wave-wide sum of value index (l >> (6 - log2 V)).
+// Butterfly transpose-reduction of V per-lane values over lanes differing in bits O, O/2, ..., 1. Afterwards v[0]
+// of lane l holds the sum over those lanes of the value whose index is given by the lane bits consumed by the
+// halving steps (the highest bit first).
 template <int V, int O>
 struct XR {
   static __device__ __forceinline__ void run(float* v, int lane) {
@@ -98,149 +107,184 @@ struct XR {
   }
 };
 
-template <int V>
-__device__ __forceinline__ constexpr int ilog2() {
-  return V <= 1 ? 0 : 1 + ilog2<V / 2>();
+__device__ __forceinline__ void unpack4(uint2 w, float* f) {
+  f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
 }
-
-// Load 8 consecutive bf16 as fp32.
-__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void unpack8(uint4 w, float* f) {
   f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
   f[4] = bf_lo(w.z); f[5] = bf_hi(w.z); f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
 }
 
-// Residual update + RMSNorm for the block's row group into LDS xs[kRG][H]; one wave per row.
-// Rows beyond B are zero. The block with blockIdx.x == 0 stores x_new when res.x_new is set.
-__device__ void prologue_norm(const Residual& res, const uint16_t* w_norm, float eps, int B, int H, float* xs) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.y * kRG + wave;
-  float* xr = xs + wave * H;
-  if (row >= B) {
-    for (int i = lane; i < H; i += 64) xr[i] = 0.f;
-    return;
-  }
-  const float* xo = res.x_old + (size_t)row * H;
-  float sd = 1.f;
-  if (res.delta) {
-    const float* dr = res.delta + (size_t)row * H;
-    float ss = 0.f;
-    for (int i = lane; i < H; i += 64) ss += dr[i] * dr[i];
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)H + eps);
-    float s2 = 0.f;
-    for (int i = lane; i < H; i += 64) {
-      const float v = (xo[i] + dr[i] * r * bf2f(res.w_delta[i])) * res.scale;
-      xr[i] = v;
-      s2 += v * v;
-    }
-    sd = wave_sum(s2);
-  } else {
-    float s2 = 0.f;
-    for (int i = lane; i < H; i += 64) {
-      const float v = xo[i];
-      xr[i] = v;
-      s2 += v * v;
-    }
-    sd = wave_sum(s2);
-  }
-  if (res.x_new && blockIdx.x == 0)
-    for (int i = lane; i < H; i += 64) res.x_new[(size_t)row * H + i] = xr[i];
-  const float r2 = 1.0f / sqrtf(sd / (float)H + eps);
-  for (int i = lane; i < H; i += 64) xr[i] = xr[i] * r2 * bf2f(w_norm[i]);
-}
+// ------------------------------------------------------------------------------------------------------------
+// dense building blocks
 
-// One wave: y[r][o] = sum_k xs[r][k] * W[n0 + o][k] for r < kRG, o < OPW (fp32 X in LDS, bf16 W in global).
-// acc receives the transpose-reduced sums: lane l holds value index (l >> (6 - log2(kRG*OPW))) = r*OPW + o.
+// Weights of OPW consecutive output rows for one wave, 4 bf16 per lane per 256-wide chunk of K (K % 256 == 0).
 template <int OPW>
-__device__ __forceinline__ void wave_dense(const float* xs, int ldx, const uint16_t* W, int K, int n0, int N,
-                                           float* acc) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < kRG * OPW; ++i) acc[i] = 0.f;
-  for (int k = lane * 8; k < K; k += 512) {
-    float wf[OPW][8];
+struct WaveW {
+  uint2 w[OPW][kMaxIt];
+  __device__ __forceinline__ void load(const uint16_t* W, int K, int n0, int N) {
+    const int lane = lane_id();
+    const int it = K >> 8;
 #pragma unroll
     for (int o = 0; o < OPW; ++o) {
-      if (n0 + o < N) {
-        load8(W + (size_t)(n0 + o) * K + k, wf[o]);
-      } else {
+      const int n = min(n0 + o, N - 1);
+      const uint16_t* row = W + (size_t)n * K + lane * 4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wf[o][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kRG; ++r) {
-      const float4 a = *reinterpret_cast<const float4*>(xs + r * ldx + k);
-      const float4 b = *reinterpret_cast<const float4*>(xs + r * ldx + k + 4);
-#pragma unroll
-      for (int o = 0; o < OPW; ++o) {
-        float s = acc[r * OPW + o];
-        s = fmaf(a.x, wf[o][0], s); s = fmaf(a.y, wf[o][1], s); s = fmaf(a.z, wf[o][2], s);
-        s = fmaf(a.w, wf[o][3], s); s = fmaf(b.x, wf[o][4], s); s = fmaf(b.y, wf[o][5], s);
-        s = fmaf(b.z, wf[o][6], s); s = fmaf(b.w, wf[o][7], s);
-        acc[r * OPW + o] = s;
-      }
+      for (int i = 0; i < kMaxIt; ++i)
+        if (i < it) w[o][i] = *reinterpret_cast<const uint2*>(row + i * 256);
     }
   }
-  XR<kRG * OPW, 32>::run(acc, lane);
+  // acc[r*OPW + o] = sum_k X(r, k) W[n0+o][k], X rows fp32 (global or LDS) at xrow[r]; transpose-reduced.
+  __device__ __forceinline__ void dot(const float* const* xrow, int K, float* acc) const {
+    const int lane = lane_id();
+    const int it = K >> 8;
+#pragma unroll
+    for (int i = 0; i < kRG * OPW; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxIt; ++i) {
+      if (i < it) {
+        float xr[kRG][4];
+#pragma unroll
+        for (int r = 0; r < kRG; ++r) {
+          const float4 a = *reinterpret_cast<const float4*>(xrow[r] + i * 256 + lane * 4);
+          xr[r][0] = a.x; xr[r][1] = a.y; xr[r][2] = a.z; xr[r][3] = a.w;
+        }
+#pragma unroll
+        for (int o = 0; o < OPW; ++o) {
+          float wf[4];
+          unpack4(w[o][i], wf);
+#pragma unroll
+          for (int r = 0; r < kRG; ++r) {
+            float s = acc[r * OPW + o];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s = fmaf(xr[r][e], wf[e], s);
+            acc[r * OPW + o] = s;
+          }
+        }
+      }
+    }
+    XR<kRG * OPW, 32>::run(acc, lane);
+  }
+};
+
+// Residual update + RMSNorm for the block's row group into LDS xs[kRG][H]; one wave per row (H % 64 == 0,
+// H <= 1024). Rows beyond B are zero. Block column 0 stores x_new when res.x_new is set.
+__device__ void prologue_norm(const Residual& res, const uint16_t* w_norm, float eps, int B, int H, float* xs) {
+  const int wave = wave_id(), lane = lane_id();
+  const int row = blockIdx.y * kRG + wave;
+  float* xr = xs + wave * H;
+  const int npl = H >> 6;
+  if (row >= B) {
+#pragma unroll
+    for (int j = 0; j < kMaxPL; ++j)
+      if (j < npl) xr[lane + 64 * j] = 0.f;
+    return;
+  }
+  float xv[kMaxPL], wv[kMaxPL];
+  const float* xo = res.x_old + (size_t)row * H;
+#pragma unroll
+  for (int j = 0; j < kMaxPL; ++j)
+    if (j < npl) {
+      xv[j] = xo[lane + 64 * j];
+      wv[j] = bf2f(w_norm[lane + 64 * j]);
+    }
+  if (res.delta) {
+    float dv[kMaxPL], wd[kMaxPL];
+    const float* dr = res.delta + (size_t)row * H;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPL; ++j)
+      if (j < npl) {
+        dv[j] = dr[lane + 64 * j];
+        wd[j] = bf2f(res.w_delta[lane + 64 * j]);
+        ss = fmaf(dv[j], dv[j], ss);
+      }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int j = 0; j < kMaxPL; ++j)
+      if (j < npl) xv[j] = (xv[j] + dv[j] * r * wd[j]) * res.scale;
+  }
+  float s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxPL; ++j)
+    if (j < npl) s2 = fmaf(xv[j], xv[j], s2);
+  s2 = wave_sum(s2);
+  const float r2 = 1.0f / sqrtf(s2 / (float)H + eps);
+  const bool store = res.x_new && blockIdx.x == 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPL; ++j)
+    if (j < npl) {
+      if (store) res.x_new[(size_t)row * H + lane + 64 * j] = xv[j];
+      xr[lane + 64 * j] = xv[j] * r2 * wv[j];
+    }
 }
 
 // ------------------------------------------------------------------------------------------------------------
 // pre_projection of [target hidden ; embedded token]  ([MTP doc] "What it is": 2x backbone input;
-// [Guide] section 2(3))
-// grid (H / 4, ceil(B / 4)); each wave one output for the 4 rows.
+// [Guide] section 2(3)). grid (H / 4, ceil(B / 4)); each wave one output for the 4 rows, 8 bf16 per lane per
+// 512-wide chunk of K = 2 Bb (Bb % 256 == 0).
 
 __global__ __launch_bounds__(256) void k_pre(int B, int Bb, int H, int V, const uint16_t* __restrict__ th,
-                                             const int32_t* __restrict__ tok, const uint16_t* __restrict__ emb,
-                                             float escale, const uint16_t* __restrict__ W, float* __restrict__ x,
-                                             uint32_t* __restrict__ counters, int ncounters) {
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < ncounters; i += 256) counters[i] = 0u;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + wave;
+                                             TokenSource ts, const uint16_t* __restrict__ emb, float escale,
+                                             const uint16_t* __restrict__ W, float* __restrict__ x) {
+  __shared__ int tok_s[kRG];
+  const int wave = wave_id(), lane = lane_id();
   const int r0 = blockIdx.y * kRG;
+  // token of this wave's row
+  {
+    const int b = min(r0 + wave, B - 1);
+    int t;
+    if (ts.keys) {
+      const uint64_t kv = (lane < ts.k) ? ts.keys[(size_t)b * ts.k + min(lane, ts.k - 1)] : 0ull;
+      t = key_id(wave_max_u64(kv));
+      if (blockIdx.x == 0 && lane == 0 && r0 + wave < B) {
+        if (ts.out) ts.out[(size_t)b * ts.out_stride] = t;
+        if (ts.next) ts.next[b] = t;
+      }
+    } else {
+      t = ts.tok[b];
+    }
+    t = t < 0 ? 0 : (t >= V ? V - 1 : t);  // out-of-range ids are clamped (documented in the ABI)
+    if (lane == 0) tok_s[wave] = t;
+  }
+  __syncthreads();
+  const int n = min((int)blockIdx.x * 4 + wave, H - 1);
   const int K = 2 * Bb;
   const uint16_t* hrow[kRG];
   const uint16_t* erow[kRG];
 #pragma unroll
   for (int r = 0; r < kRG; ++r) {
     const int b = min(r0 + r, B - 1);
-    int t = tok[b];
-    t = t < 0 ? 0 : (t >= V ? V - 1 : t);  // out-of-range ids are clamped (documented in the ABI)
     hrow[r] = th + (size_t)b * Bb;
-    erow[r] = emb + (size_t)t * Bb;
+    erow[r] = emb + (size_t)tok_s[r] * Bb;
   }
+  const uint16_t* w = W + (size_t)n * K;
   float acc[kRG];
 #pragma unroll
   for (int r = 0; r < kRG; ++r) acc[r] = 0.f;
-  if (n < H) {
-    const uint16_t* w = W + (size_t)n * K;
-    for (int k = lane * 8; k < K; k += 512) {
-      float wf[8];
-      load8(w + k, wf);
+  const int iters = K >> 9;
+#pragma unroll 4
+  for (int it = 0; it < iters; ++it) {
+    const int k = it * 512 + lane * 8;
+    float wf[8];
+    unpack8(*reinterpret_cast<const uint4*>(w + k), wf);
+    const bool hid = k < Bb;
+    const float sc = hid ? 1.0f : escale;
 #pragma unroll
-      for (int r = 0; r < kRG; ++r) {
-        float xf[8];
-        if (k < Bb) {
-          load8(hrow[r] + k, xf);
-        } else {
-          load8(erow[r] + (k - Bb), xf);
-          if (escale != 1.0f) {
+    for (int r = 0; r < kRG; ++r) {
+      const uint16_t* src = hid ? (hrow[r] + k) : (erow[r] + (k - Bb));
+      float xf[8];
+      unpack8(*reinterpret_cast<const uint4*>(src), xf);
+      float s = acc[r];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xf[e] *= escale;
-          }
-        }
-        float s = acc[r];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(xf[e], wf[e], s);
-        acc[r] = s;
-      }
+      for (int e = 0; e < 8; ++e) s = fmaf(xf[e] * sc, wf[e], s);
+      acc[r] = s;
     }
   }
   XR<kRG, 32>::run(acc, lane);
   const int idx = lane >> 4;  // row within the group
-  if ((lane & 15) == 0 && n < H && r0 + idx < B) x[(size_t)(r0 + idx) * H + n] = acc[0];
+  if ((lane & 15) == 0 && (int)blockIdx.x * 4 + wave < H && r0 + idx < B) x[(size_t)(r0 + idx) * H + n] = acc[0];
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -249,33 +293,36 @@ __global__ __launch_bounds__(256) void k_pre(int B, int Bb, int H, int V, const 
 __global__ __launch_bounds__(256) void k_qproj(int B, int H, int QD, Residual res, const uint16_t* __restrict__ w_norm,
                                                float eps, const uint16_t* __restrict__ W, float* __restrict__ q) {
   extern __shared__ float xs[];  // [kRG][H]
+  const int wave = wave_id(), lane = lane_id();
+  const int n0 = blockIdx.x * 16 + wave * 4;
+  WaveW<4> ww;
+  ww.load(W, H, n0, QD);
   prologue_norm(res, w_norm, eps, B, H, xs);
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 16 + wave * 4;
+  const float* xrow[kRG] = {xs, xs + H, xs + 2 * H, xs + 3 * H};
   float acc[kRG * 4];
-  wave_dense<4>(xs, H, W, H, n0, QD, acc);
+  ww.dot(xrow, H, acc);
   const int idx = lane >> 2;  // r * 4 + o
   const int r = blockIdx.y * kRG + (idx >> 2), n = n0 + (idx & 3);
   if ((lane & 3) == 0 && r < B && n < QD) q[(size_t)r * QD + n] = acc[0];
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// Dense product for o_proj / down: grid (N / 4, ceil(B / 4)); rows of X staged in LDS.
+// Dense product for o_proj / down / centroid scores: grid (N / 4, ceil(B / 4)); X rows read directly (rows beyond
+// B read row B-1, results discarded).
 
 __global__ __launch_bounds__(256) void k_dense(int B, int K, int N, const float* __restrict__ X,
                                                const uint16_t* __restrict__ W, float* __restrict__ y) {
-  extern __shared__ float xs[];  // [kRG][K]
-  const int r0 = blockIdx.y * kRG;
-  for (int i = threadIdx.x; i < kRG * K; i += 256) {
-    const int r = i / K, k = i % K;
-    xs[i] = (r0 + r < B) ? X[(size_t)(r0 + r) * K + k] : 0.f;
-  }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = lane_id();
   const int n = blockIdx.x * 4 + wave;
+  const int r0 = blockIdx.y * kRG;
+  WaveW<1> ww;
+  ww.load(W, K, n, N);
+  const float* xrow[kRG];
+#pragma unroll
+  for (int r = 0; r < kRG; ++r) xrow[r] = X + (size_t)min(r0 + r, B - 1) * K;
   float acc[kRG];
-  wave_dense<1>(xs, K, W, K, n, N, acc);
+  ww.dot(xrow, K, acc);
   const int idx = lane >> 4;
   if ((lane & 15) == 0 && r0 + idx < B && n < N) y[(size_t)(r0 + idx) * N + n] = acc[0];
 }
@@ -289,49 +336,21 @@ __global__ __launch_bounds__(256) void k_ffn(int B, int H, int F, Residual res, 
                                              const uint16_t* __restrict__ Wu, float* __restrict__ m,
                                              FillRange fill) {
   extern __shared__ float xs[];  // [kRG][H]
+  const int wave = wave_id(), lane = lane_id();
+  const int f0 = blockIdx.x * 16 + wave * 4;
+  WaveW<4> wg, wu;
+  wg.load(Wg, H, f0, F);
+  wu.load(Wu, H, f0, F);
   prologue_norm(res, w_norm, eps, B, H, xs);
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int f0 = blockIdx.x * 16 + wave * 4;
-  float acc[kRG * 8];
-#pragma unroll
-  for (int i = 0; i < kRG * 8; ++i) acc[i] = 0.f;
-  for (int k = lane * 8; k < H; k += 512) {
-    float wg[4][8], wu[4][8];
-#pragma unroll
-    for (int o = 0; o < 4; ++o) {
-      if (f0 + o < F) {
-        load8(Wg + (size_t)(f0 + o) * H + k, wg[o]);
-        load8(Wu + (size_t)(f0 + o) * H + k, wu[o]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wg[o][e] = wu[o][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kRG; ++r) {
-      const float4 a = *reinterpret_cast<const float4*>(xs + r * H + k);
-      const float4 b = *reinterpret_cast<const float4*>(xs + r * H + k + 4);
-      const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int o = 0; o < 4; ++o) {
-        float sg = acc[r * 8 + o * 2], su = acc[r * 8 + o * 2 + 1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sg = fmaf(xv[e], wg[o][e], sg);
-          su = fmaf(xv[e], wu[o][e], su);
-        }
-        acc[r * 8 + o * 2] = sg;
-        acc[r * 8 + o * 2 + 1] = su;
-      }
-    }
-  }
-  XR<kRG * 8, 32>::run(acc, lane);  // lane l holds index l >> 1 = r*8 + o*2 + {0 gate, 1 up}
-  const float other = __shfl_xor(acc[0], 2, 64);
-  const int idx = lane >> 1;
-  const int r = blockIdx.y * kRG + (idx >> 3), f = f0 + ((idx >> 1) & 3);
-  if ((lane & 3) == 0 && r < B && f < F) m[(size_t)r * F + f] = gelu_tanh(acc[0]) * other;
-  // logits fill share
+  const float* xrow[kRG] = {xs, xs + H, xs + 2 * H, xs + 3 * H};
+  float ag[kRG * 4], au[kRG * 4];
+  wg.dot(xrow, H, ag);
+  wu.dot(xrow, H, au);
+  const int idx = lane >> 2;
+  const int r = blockIdx.y * kRG + (idx >> 2), f = f0 + (idx & 3);
+  if ((lane & 3) == 0 && r < B && f < F) m[(size_t)r * F + f] = gelu_tanh(ag[0]) * au[0];
+  // logits fill share ([Inventory] "Centroid / ordered embeddings LM head", step 5: the -1e30 base row)
   if (fill.logits) {
     const size_t nblk = (size_t)gridDim.x * gridDim.y;
     const size_t bid = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
@@ -341,7 +360,6 @@ __global__ __launch_bounds__(256) void k_ffn(int B, int H, int F, Residual res, 
     const size_t e = a + per < fill.end ? a + per : fill.end;
     if (a < e) {
       const float4 v = make_float4(-1e30f, -1e30f, -1e30f, -1e30f);
-      // fill.begin and per are multiples of 4 floats except possibly the range end
       size_t i = a + threadIdx.x * 4;
       for (; i + 4 <= e; i += 1024) *reinterpret_cast<float4*>(fill.logits + i) = v;
       for (; i < e; ++i) fill.logits[i] = -1e30f;
@@ -360,6 +378,14 @@ __global__ __launch_bounds__(256) void k_post(int B, int H, int Bb, int C, Resid
                                               float* __restrict__ h_out, uint16_t* __restrict__ hidden_out,
                                               float* __restrict__ scores) {
   extern __shared__ float xs[];  // [kRG][H]
+  const int wave = wave_id(), lane = lane_id();
+  const int n0 = blockIdx.x * 16 + wave * 4;
+  const bool cen = n0 >= Bb;
+  WaveW<4> ww;
+  if (!cen)
+    ww.load(Wp, H, n0, Bb);
+  else
+    ww.load(Wc, H, n0 - Bb, C);
   prologue_norm(res, w_out, eps, B, H, xs);
   __syncthreads();
   if (blockIdx.x == 0) {
@@ -368,14 +394,9 @@ __global__ __launch_bounds__(256) void k_post(int B, int H, int Bb, int C, Resid
       if (r < B) h_out[(size_t)r * H + i % H] = xs[i];
     }
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 16 + wave * 4;
-  const bool cen = n0 >= Bb;
+  const float* xrow[kRG] = {xs, xs + H, xs + 2 * H, xs + 3 * H};
   float acc[kRG * 4];
-  if (!cen)
-    wave_dense<4>(xs, H, Wp, H, n0, Bb, acc);
-  else
-    wave_dense<4>(xs, H, Wc, H, n0 - Bb, C, acc);
+  ww.dot(xrow, H, acc);
   const int idx = lane >> 2;
   const int r = blockIdx.y * kRG + (idx >> 2), n = n0 + (idx & 3);
   if ((lane & 3) == 0 && r < B) {
@@ -390,55 +411,47 @@ __global__ __launch_bounds__(256) void k_post(int B, int H, int Bb, int C, Resid
 // ------------------------------------------------------------------------------------------------------------
 // single-query attention over the shared cache ([MTP doc] "What it is": Q-only attention on the target's
 // last-layer K/V; [Guide] section 2(4); [Inventory] "Notes for llama.cpp port" 2: V taken from K)
-// grid (nsplit, B * nkv). HD = head_dim, G = query heads per kv head, DPL = dims per lane, KB = keys per batch.
+// grid (nsplit, B * nkv), NW waves per block. HD = head_dim, G = query heads per kv head, DPL = dims per lane,
+// KB = keys per batch (KB * G = 64 scores, one per lane after the transpose-reduction).
 
-template <int HD, int G>
-__global__ __launch_bounds__(256) void k_attn(int B, int nh, int nkv, const float* __restrict__ q,
-                                              const uint16_t* __restrict__ qnorm, float eps,
-                                              const float* __restrict__ rope, int type, const uint16_t* __restrict__ K,
-                                              const uint16_t* __restrict__ Vc, int cap, RowWindows win, int nsplit,
-                                              float scale_log2, float* __restrict__ pacc, float* __restrict__ pml,
-                                              uint32_t* __restrict__ cnt, float* __restrict__ o) {
+template <int DPL>
+struct RawT;
+template <>
+struct RawT<4> { using T = uint2; };
+template <>
+struct RawT<2> { using T = uint32_t; };
+template <>
+struct RawT<1> { using T = uint16_t; };
+
+template <int DPL>
+__device__ __forceinline__ void unpack_raw(const typename RawT<DPL>::T& r, float* f) {
+  if constexpr (DPL == 4) {
+    f[0] = bf_lo(r.x); f[1] = bf_hi(r.x); f[2] = bf_lo(r.y); f[3] = bf_hi(r.y);
+  } else if constexpr (DPL == 2) {
+    f[0] = bf_lo(r); f[1] = bf_hi(r);
+  } else {
+    f[0] = bf2f(r);
+  }
+}
+
+template <int HD, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const float* __restrict__ q,
+                                                  const uint16_t* __restrict__ qnorm, float eps,
+                                                  const float* __restrict__ rope, int type,
+                                                  const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vc,
+                                                  int cap, RowWindows win, int nsplit, float scale_log2,
+                                                  float* __restrict__ pacc, float* __restrict__ pml,
+                                                  float* __restrict__ o) {
   constexpr int DPL = HD / 64;
   constexpr int KB = 64 / G;
+  using Raw = typename RawT<DPL>::T;
   __shared__ float qs[G][HD];
-  __shared__ float wml[4][G][2];
-  __shared__ float wacc[4][G][HD];
-  __shared__ int is_last;
+  __shared__ float wml[NW][G][2];
+  __shared__ float wacc[NW][G][HD];
   const int sp = blockIdx.x, bg = blockIdx.y;
   const int b = bg / nkv, g = bg % nkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int half = HD / 2;
-
-  // q_norm + rotation at the row's constant position ([Guide] section 2(2))
-  const float* tab = rope + ((size_t)b * 2 + type) * 2 * half;
-  for (int hh = wave; hh < G; hh += 4) {
-    const float* qr = q + ((size_t)b * nh + g * G + hh) * HD;
-    float v[DPL];
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      v[e] = qr[lane * DPL + e];
-      ss += v[e] * v[e];
-    }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)HD + eps);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) v[e] = v[e] * r * bf2f(qnorm[lane * DPL + e]);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const float partner = __shfl_xor(v[e], 32, 64);  // dim i <-> i + HD/2
-      const int i = (lane & 31) * DPL + e;
-      const float c = tab[i], s = tab[half + i];
-      qs[hh][lane * DPL + e] = (lane < 32) ? (v[e] * c - partner * s) : (v[e] * c + partner * s);
-    }
-  }
-  __syncthreads();
-  float qr[G][DPL];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) qr[hh][e] = qs[hh][lane * DPL + e];
+  const int wave = wave_id(), lane = lane_id();
+  constexpr int half = HD / 2;
 
   const int cntk = win.count[b];
   const int chunk = (cntk + nsplit - 1) / nsplit;
@@ -447,6 +460,46 @@ __global__ __launch_bounds__(256) void k_attn(int B, int nh, int nkv, const floa
   const bool same_v = (Vc == K);
   const uint16_t* Kb = K + ((size_t)b * nkv + g) * (size_t)cap * HD + lane * DPL;
   const uint16_t* Vb = Vc + ((size_t)b * nkv + g) * (size_t)cap * HD + lane * DPL;
+  // first batch of keys in flight before the q prologue
+  Raw kcur[KB], knext[KB];
+  int t0 = k0 + wave * KB;
+  if (t0 < k1) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) kcur[j] = *reinterpret_cast<const Raw*>(Kb + (size_t)min(t0 + j, k1 - 1) * HD);
+  }
+
+  // q_norm + rotation at the row's constant position ([Guide] section 2(2))
+  const float* tab = rope + ((size_t)b * 2 + type) * 2 * half;
+  for (int hh = wave; hh < G; hh += NW) {
+    const float* qr = q + ((size_t)b * nh + g * G + hh) * HD;
+    float v[DPL], wq[DPL], co[DPL], si[DPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const int d = lane * DPL + e;
+      const int i = d & (half - 1);
+      v[e] = qr[d];
+      wq[e] = bf2f(qnorm[d]);
+      co[e] = tab[i];
+      si[e] = tab[half + i];
+      ss = fmaf(v[e], v[e], ss);
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) v[e] = v[e] * r * wq[e];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float partner = __shfl_xor(v[e], 32, 64);  // dim i <-> i + HD/2
+      qs[hh][lane * DPL + e] = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
+    }
+  }
+  __syncthreads();
+  float qr[G][DPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qr[hh][e] = qs[hh][lane * DPL + e];
 
   float mrun[G], lrun[G], acc[G][DPL];
 #pragma unroll
@@ -458,39 +511,28 @@ __global__ __launch_bounds__(256) void k_attn(int B, int nh, int nkv, const floa
   }
   const int jl = lane / G, hl = lane % G;
 
-  for (int t0 = k0 + wave * KB; t0 < k1; t0 += 4 * KB) {
+  for (; t0 < k1; t0 += NW * KB) {
     const int nk = min(KB, k1 - t0);
-    float kf[KB][DPL];
+    const int tn = t0 + NW * KB;
+    if (tn < k1) {  // next batch in flight while this one is computed
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      if (j < nk) {
-        const uint16_t* p = Kb + (size_t)(t0 + j) * HD;
-        if constexpr (DPL == 4) {
-          const uint2 w = *reinterpret_cast<const uint2*>(p);
-          kf[j][0] = bf_lo(w.x); kf[j][1] = bf_hi(w.x); kf[j][2] = bf_lo(w.y); kf[j][3] = bf_hi(w.y);
-        } else if constexpr (DPL == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-          kf[j][0] = bf_lo(w); kf[j][1] = bf_hi(w);
-        } else {
-          kf[j][0] = bf2f(p[0]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) kf[j][e] = 0.f;
-      }
+      for (int j = 0; j < KB; ++j) knext[j] = *reinterpret_cast<const Raw*>(Kb + (size_t)min(tn + j, k1 - 1) * HD);
     }
     float sc[64];
 #pragma unroll
-    for (int j = 0; j < KB; ++j)
+    for (int j = 0; j < KB; ++j) {
+      float kf[DPL];
+      unpack_raw<DPL>(kcur[j], kf);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) s = fmaf(kf[j][e], qr[hh][e], s);
+        for (int e = 0; e < DPL; ++e) s = fmaf(kf[e], qr[hh][e], s);
         sc[j * G + hh] = s;
       }
+    }
     XR<64, 32>::run(sc, lane);  // lane l: score of key l / G, head l % G
-    float s = (jl < nk) ? sc[0] * scale_log2 : -INFINITY;
+    const float s = (jl < nk) ? sc[0] * scale_log2 : -INFINITY;
     float mx = s;
 #pragma unroll
     for (int of = G; of < 64; of <<= 1) mx = fmaxf(mx, __shfl_xor(mx, of, 64));
@@ -501,7 +543,7 @@ __global__ __launch_bounds__(256) void k_attn(int B, int nh, int nkv, const floa
       const float mn = fmaxf(mrun[hh], readlane_f(mx, hh));
       alpha[hh] = (mrun[hh] == -INFINITY) ? 0.f : exp2f(mrun[hh] - mn);
       mrun[hh] = mn;
-      if (hl == hh) mhl = mn;
+      mhl = (hl == hh) ? mn : mhl;
     }
     const float p = (jl < nk) ? exp2f(s - mhl) : 0.f;
     float ps = p;
@@ -513,29 +555,27 @@ __global__ __launch_bounds__(256) void k_attn(int B, int nh, int nkv, const floa
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[hh][e] *= alpha[hh];
     }
-    // P.V
+    // P.V (p of masked keys is 0)
+    Raw vraw[KB];
+    if (!same_v) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) vraw[j] = *reinterpret_cast<const Raw*>(Vb + (size_t)min(t0 + j, k1 - 1) * HD);
+    }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
-      if (j < nk) {
-        float vf[DPL];
-        if (same_v) {
+      float vf[DPL];
+      unpack_raw<DPL>(same_v ? kcur[j] : vraw[j], vf);
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) vf[e] = kf[j][e];
-        } else {
-          const uint16_t* pv = Vb + (size_t)(t0 + j) * HD;
+      for (int hh = 0; hh < G; ++hh) {
+        const float pj = readlane_f(p, j * G + hh);
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) vf[e] = bf2f(pv[e]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float pj = readlane_f(p, j * G + hh);
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
-        }
+        for (int e = 0; e < DPL; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) kcur[j] = knext[j];
   }
-  // combine the 4 waves of this block
+  // combine the waves of this block
   if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -548,135 +588,215 @@ __global__ __launch_bounds__(256) void k_attn(int B, int nh, int nkv, const floa
 #pragma unroll
     for (int e = 0; e < DPL; ++e) wacc[wave][hh][lane * DPL + e] = acc[hh][e];
   __syncthreads();
-  for (int i = threadIdx.x; i < G * HD; i += 256) {
+  for (int i = threadIdx.x; i < G * HD; i += NW * 64) {
     const int hh = i / HD, d = i % HD;
     float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wml[w][hh][0]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wml[w][hh][0]);
     float L = 0.f, A = 0.f;
     if (M != -INFINITY) {
-      for (int w = 0; w < 4; ++w) {
-        if (wml[w][hh][0] == -INFINITY) continue;
-        const float f = exp2f(wml[w][hh][0] - M);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = wml[w][hh][0];
+        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
         L = fmaf(wml[w][hh][1], f, L);
         A = fmaf(wacc[w][hh][d], f, A);
       }
     }
-    const size_t slot = ((size_t)b * nh + g * G + hh) * kMaxSplit + sp;
-    pacc[slot * HD + d] = A;
-    if (d == 0) {
-      pml[slot * 2 + 0] = M;
-      pml[slot * 2 + 1] = L;
-    }
-  }
-  // the last block of this (row, kv head) merges all splits
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(&cnt[bg], 1u) == (uint32_t)(nsplit - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < G * HD; i += 256) {
-    const int hh = i / HD, d = i % HD;
-    const size_t base = ((size_t)b * nh + g * G + hh) * kMaxSplit;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, pml[(base + s2) * 2]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int s2 = 0; s2 < nsplit; ++s2) {
-        const float m2 = pml[(base + s2) * 2];
-        if (m2 == -INFINITY) continue;
-        const float f = exp2f(m2 - M);
-        L = fmaf(pml[(base + s2) * 2 + 1], f, L);
-        A = fmaf(pacc[(base + s2) * HD + d], f, A);
+    const size_t hq = (size_t)b * nh + g * G + hh;
+    if (nsplit == 1) {
+      o[hq * HD + d] = (L > 0.f) ? A / L : 0.f;
+    } else {
+      const size_t slot = hq * kMaxSplit + sp;
+      pacc[slot * HD + d] = A;
+      if (d == 0) {
+        pml[slot * 2 + 0] = M;
+        pml[slot * 2 + 1] = L;
       }
     }
-    o[((size_t)b * nh + g * G + hh) * HD + d] = (L > 0.f) ? A / L : 0.f;
   }
-  if (threadIdx.x == 0) cnt[bg] = 0u;  // every other block of this (row, kv head) has already arrived
+}
+
+// grid (B * nh), 256 threads: thread d of head (b, h) merges the nsplit partials
+__global__ __launch_bounds__(256) void k_attn_merge(int hd, int nsplit, const float* __restrict__ pacc,
+                                                    const float* __restrict__ pml, float* __restrict__ o) {
+  const size_t base = (size_t)blockIdx.x * kMaxSplit;
+  const int d = min((int)threadIdx.x, hd - 1);
+  float m[kMaxSplit], l[kMaxSplit], a[kMaxSplit];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < nsplit) {
+      m[s] = pml[(base + s) * 2];
+      l[s] = pml[(base + s) * 2 + 1];
+      a[s] = pacc[(base + s) * hd + d];
+      M = fmaxf(M, m[s]);
+    }
+  }
+  float L = 0.f, A = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < nsplit) {
+      const float f = (m[s] == -INFINITY) ? 0.f : exp2f(m[s] - M);
+      L = fmaf(l[s], f, L);
+      A = fmaf(a[s], f, A);
+    }
+  }
+  if ((int)threadIdx.x < hd) o[(size_t)blockIdx.x * hd + d] = (L > 0.f) ? A / L : 0.f;
 }
 
 // ------------------------------------------------------------------------------------------------------------
 // masked head ([Inventory] "Centroid / ordered embeddings LM head" steps 2-5)
+// grid (k, B), 256 threads. Every block of a row recomputes the row's top-k (radix select over order-preserving
+// keys; exact, ties to the lower index) and keeps its slot j; 16 groups of 16 lanes then score the slot's cluster.
 
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, int C, int k,
-                                              int32_t* __restrict__ sel) {
-  constexpr int kPer = 32;  // C <= 256 * 32
+constexpr int kPerThr = kMaxCentroids / 256;
+
+__global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, int H, const float* __restrict__ scores,
+                                              const int32_t* __restrict__ ordering, const uint16_t* __restrict__ E,
+                                              const float* __restrict__ h, int32_t* __restrict__ sel,
+                                              int32_t* __restrict__ ids, float* __restrict__ z,
+                                              float* __restrict__ logits, size_t V, uint64_t* __restrict__ keys) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_digit, sh_before, sh_n;
+  __shared__ uint64_t cand[kMaxCentroids];
+  __shared__ int sh_c;
+  __shared__ float hs[1024];
   __shared__ uint64_t red[4];
-  const int b = blockIdx.x;
-  uint64_t key[kPer];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int npt = (C + 255) >> 8;
+
+  // scores -> order keys
+  uint32_t ok[kPerThr];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    key[i] = (c < C) ? (((uint64_t)f32_order(scores[(size_t)b * C + c]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c))
-                     : 0ull;
+  for (int i = 0; i < kPerThr; ++i)
+    if (i < npt) ok[i] = f32_order(scores[(size_t)b * C + min(tid + 256 * i, C - 1)]);
+  // the hidden row for the dot products
+  for (int i = tid; i < H; i += 256) hs[i] = h[(size_t)b * H + i];
+
+  // radix select of the k-th largest key value, 8 bits at a time from the top
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t need = (uint32_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPerThr; ++i)
+      if (i < npt && tid + 256 * i < C && (ok[i] & pmask) == prefix) atomicAdd(&hist[(ok[i] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      uint32_t cnt[4], sum = 0;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        cnt[q2] = hist[255 - 4 * lane - q2];
+        sum += cnt[q2];
+      }
+      uint32_t incl = sum;  // inclusive prefix over lanes (higher digits first)
+#pragma unroll
+      for (int of = 1; of < 64; of <<= 1) {
+        const uint32_t t = __shfl_up(incl, of, 64);
+        if (lane >= of) incl += t;
+      }
+      uint32_t before = incl - sum;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        if (before < need && before + cnt[q2] >= need) {
+          sh_digit = 255u - 4u * lane - q2;
+          sh_before = before;
+        }
+        before += cnt[q2];
+      }
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    pmask |= 255u << shift;
+    need -= sh_before;
+    __syncthreads();
   }
-  for (int j = 0; j < k; ++j) {
-    uint64_t mx = 0;
+  // prefix is now the exact key of the k-th largest score; every key >= prefix is a candidate
+  if (tid == 0) sh_n = 0u;
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) mx = u64_max(mx, key[i]);
-    mx = block_max_u64(mx, red);
-    const uint32_t c = 0xFFFFFFFFu - (uint32_t)(mx & 0xFFFFFFFFull);
-    if (threadIdx.x == 0) sel[(size_t)b * k + j] = (int32_t)c;
-    if ((int)(c % 256) == (int)threadIdx.x) {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (i == (int)(c / 256)) key[i] = 0ull;
+  for (int i = 0; i < kPerThr; ++i) {
+    const int c = tid + 256 * i;
+    if (i < npt && c < C && ok[i] >= prefix) {
+      const uint32_t pos = atomicAdd(&sh_n, 1u);
+      cand[pos] = ((uint64_t)ok[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
     }
   }
+  __syncthreads();
+  const uint32_t ncand = sh_n;
+  // rank among the candidates: descending score, then ascending index; slot j is the candidate of rank j
+  for (uint32_t e = tid; e < ncand; e += 256) {
+    const uint64_t me = cand[e];
+    uint32_t rank = 0;
+    for (uint32_t f = 0; f < ncand; ++f) rank += (cand[f] > me) ? 1u : 0u;
+    if (rank == (uint32_t)j) sh_c = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
+  }
+  __syncthreads();
+  const int c = sh_c;
+  if (tid == 0 && sel) sel[(size_t)b * k + j] = c;
+
+  // the cluster's candidate ids and their logits: group grp scores ids t = grp + 16 i, 8 ids per pass
+  const int grp = tid >> 4, l16 = tid & 15;
+  const int nper = vsc >> 4;  // ids per group (vsc % 16 == 0)
+  const int32_t* ord = ordering + (size_t)c * vsc;
+  const int hch = H >> 7;  // 128-wide chunks of h; lane l16 covers 8 elements of each
+  uint64_t best = 0;
+  for (int i0 = 0; i0 < nper; i0 += 8) {
+    int idv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) idv[u] = ord[min(grp + 16 * (i0 + u), vsc - 1)];
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    for (int ch = 0; ch < hch; ++ch) {
+      const int col = ch * 128 + l16 * 8;
+      uint4 raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = *reinterpret_cast<const uint4*>(E + (size_t)idv[u] * H + col);
+      float hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = hs[col + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float ef[8];
+        unpack8(raw[u], ef);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u] = fmaf(ef[e], hv[e], acc[u]);
+      }
+    }
+    XR<8, 8>::run(acc, l16);  // over the 16 lanes of the group: lane l16 holds id (l16 >> 1) of the 8
+    const int u = l16 >> 1;
+    int idu = idv[0];
+#pragma unroll
+    for (int w2 = 1; w2 < 8; ++w2) idu = (u == w2) ? idv[w2] : idu;
+    if ((l16 & 1) == 0 && i0 + u < nper) {
+      const int t = grp + 16 * (i0 + u);
+      const size_t slot = ((size_t)b * k + j) * vsc + t;
+      if (ids) ids[slot] = idu;
+      if (z) z[slot] = acc[0];
+      if (logits) logits[(size_t)b * V + idu] = acc[0];
+      best = u64_max(best, vid_key(acc[0], (uint32_t)idu));
+    }
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) red[wave] = best;
+  __syncthreads();
+  if (tid == 0) keys[(size_t)b * k + j] = u64_max(u64_max(red[0], red[1]), u64_max(red[2], red[3]));
 }
 
-// grid (k, B), 256 threads = 16 groups of 16 lanes; each group scores one candidate row at a time.
-__global__ __launch_bounds__(256) void k_head(int k, int vsc, int H, const int32_t* __restrict__ sel,
-                                              const int32_t* __restrict__ ordering, const uint16_t* __restrict__ E,
-                                              const float* __restrict__ h, int32_t* __restrict__ ids,
-                                              float* __restrict__ z, float* __restrict__ logits, size_t V,
-                                              uint64_t* __restrict__ keys, uint32_t* __restrict__ cnt,
-                                              int32_t* __restrict__ next, int32_t* __restrict__ out2, int stride2) {
-  extern __shared__ float hs[];  // [H]
-  __shared__ uint64_t red[4];
-  __shared__ int is_last;
-  const int j = blockIdx.x, b = blockIdx.y;
-  const int grp = threadIdx.x >> 4, l16 = threadIdx.x & 15;
-  for (int i = threadIdx.x; i < H; i += 256) hs[i] = h[(size_t)b * H + i];
-  __syncthreads();
-  const int c = sel[(size_t)b * k + j];
-  uint64_t best = 0;
-  for (int t = grp; t < vsc; t += 16) {
-    const int id = ordering[(size_t)c * vsc + t];
-    const uint16_t* e = E + (size_t)id * H;
-    float s = 0.f;
-    for (int col = l16 * 8; col < H; col += 128) {
-      float ef[8];
-      load8(e + col, ef);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) s = fmaf(ef[q], hs[col + q], s);
-    }
-#pragma unroll
-    for (int of = 8; of > 0; of >>= 1) s += __shfl_xor(s, of, 64);
-    if (l16 == 0) {
-      const size_t slot = ((size_t)b * k + j) * vsc + t;
-      ids[slot] = id;
-      z[slot] = s;
-      if (logits) logits[(size_t)b * V + id] = s;
-      best = u64_max(best, ((uint64_t)f32_order(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id));
-    }
-  }
-  best = block_max_u64(best, red);
-  if (threadIdx.x == 0) keys[(size_t)b * k + j] = best;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(&cnt[b], 1u) == (uint32_t)(k - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  uint64_t mx = 0;
-  for (int i = threadIdx.x; i < k; i += 256) mx = u64_max(mx, keys[(size_t)b * k + i]);
-  mx = block_max_u64(mx, red);
-  if (threadIdx.x == 0) {
-    const int32_t id = (int32_t)(0xFFFFFFFFu - (uint32_t)(mx & 0xFFFFFFFFull));
+// grid B, 64 threads
+__global__ void k_final(int k, const uint64_t* __restrict__ keys, int32_t* __restrict__ next,
+                        int32_t* __restrict__ out2, int stride2) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const uint64_t kv = (lane < k) ? keys[(size_t)b * k + min(lane, k - 1)] : 0ull;
+  const int32_t id = key_id(wave_max_u64(kv));
+  if (lane == 0) {
     next[b] = id;
     if (out2) out2[(size_t)b * stride2] = id;
-    cnt[b] = 0u;  // every other block of this row has already arrived
   }
 }
 
@@ -687,10 +807,6 @@ __global__ void k_fill(float4* __restrict__ p, size_t n4, float* __restrict__ ta
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = -1e30f;
 }
 
-__global__ void k_zero_u32(uint32_t* __restrict__ p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
-}
-
 int row_groups(int B) { return (B + kRG - 1) / kRG; }
 
 }  // namespace
@@ -698,11 +814,10 @@ int row_groups(int B) { return (B + kRG - 1) / kRG; }
 // ------------------------------------------------------------------------------------------------------------
 // launchers
 
-hipError_t launch_pre(hipStream_t s, int B, int Bb, int H, int V, const uint16_t* th, const int32_t* tok,
-                      const uint16_t* emb, float escale, const uint16_t* w_pre, float* x, uint32_t* counters,
-                      int ncounters) {
+hipError_t launch_pre(hipStream_t s, int B, int Bb, int H, int V, const uint16_t* th, TokenSource ts,
+                      const uint16_t* emb, float escale, const uint16_t* w_pre, float* x) {
   dim3 grid((H + 3) / 4, row_groups(B));
-  k_pre<<<grid, 256, 0, s>>>(B, Bb, H, V, th, tok, emb, escale, w_pre, x, counters, ncounters);
+  k_pre<<<grid, 256, 0, s>>>(B, Bb, H, V, th, ts, emb, escale, w_pre, x);
   return hipGetLastError();
 }
 
@@ -715,8 +830,12 @@ hipError_t launch_qproj(hipStream_t s, int B, int H, int QD, Residual res, const
 
 hipError_t launch_dense(hipStream_t s, int B, int K, int N, const float* X, const uint16_t* w, float* y) {
   dim3 grid((N + 3) / 4, row_groups(B));
-  k_dense<<<grid, 256, kRG * K * sizeof(float), s>>>(B, K, N, X, w, y);
+  k_dense<<<grid, 256, 0, s>>>(B, K, N, X, w, y);
   return hipGetLastError();
+}
+
+hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, const uint16_t* w_cen, float* scores) {
+  return launch_dense(s, B, H, C, h, w_cen, scores);
 }
 
 hipError_t launch_ffn(hipStream_t s, int B, int H, int F, Residual res, const uint16_t* w_norm, float eps,
@@ -737,40 +856,46 @@ hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res,
 
 hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
                        float eps, const float* rope, int type, const uint16_t* K, const uint16_t* V, int cap,
-                       const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, uint32_t* cnt,
-                       float* o) {
+                       const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, float* o) {
   dim3 grid(nsplit, B * nkv);
   const float sl2 = scale * 1.4426950408889634f;
   const int G = nh / nkv;
-#define MTPD_ATTN(HD_, G_)                                                                                     \
-  if (hd == HD_ && G == G_) {                                                                                  \
-    k_attn<HD_, G_><<<grid, 256, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, \
-                                         pacc, pml, cnt, o);                                                   \
-    return hipGetLastError();                                                                                  \
+#define MTPD_ATTN(HD_, G_, NW_)                                                                             \
+  if (hd == HD_ && G == G_) {                                                                               \
+    k_attn<HD_, G_, NW_><<<grid, NW_ * 64, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win,  \
+                                                    nsplit, sl2, pacc, pml, o);                             \
+    return hipGetLastError();                                                                               \
   }
-  MTPD_ATTN(256, 1) MTPD_ATTN(256, 2) MTPD_ATTN(256, 4) MTPD_ATTN(256, 8)
-  MTPD_ATTN(128, 1) MTPD_ATTN(128, 2) MTPD_ATTN(128, 4) MTPD_ATTN(128, 8)
-  MTPD_ATTN(64, 1) MTPD_ATTN(64, 2) MTPD_ATTN(64, 4) MTPD_ATTN(64, 8)
+  if (nsplit == 1) {
+    MTPD_ATTN(256, 1, 8) MTPD_ATTN(256, 2, 8) MTPD_ATTN(256, 4, 8) MTPD_ATTN(256, 8, 4)
+    MTPD_ATTN(128, 1, 8) MTPD_ATTN(128, 2, 8) MTPD_ATTN(128, 4, 8) MTPD_ATTN(128, 8, 8)
+    MTPD_ATTN(64, 1, 8) MTPD_ATTN(64, 2, 8) MTPD_ATTN(64, 4, 8) MTPD_ATTN(64, 8, 8)
+  } else {
+    MTPD_ATTN(256, 1, 4) MTPD_ATTN(256, 2, 4) MTPD_ATTN(256, 4, 4) MTPD_ATTN(256, 8, 4)
+    MTPD_ATTN(128, 1, 4) MTPD_ATTN(128, 2, 4) MTPD_ATTN(128, 4, 4) MTPD_ATTN(128, 8, 4)
+    MTPD_ATTN(64, 1, 4) MTPD_ATTN(64, 2, 4) MTPD_ATTN(64, 4, 4) MTPD_ATTN(64, 8, 4)
+  }
 #undef MTPD_ATTN
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_topk(hipStream_t s, int B, const float* scores, int C, int k, int32_t* sel) {
-  k_topk<<<B, 256, 0, s>>>(scores, C, k, sel);
+hipError_t launch_attn_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
+                             float* o) {
+  k_attn_merge<<<B * nh, 256, 0, s>>>(hd, nsplit, pacc, pml, o);
   return hipGetLastError();
 }
 
-hipError_t launch_head(hipStream_t s, int B, int k, int vsc, int H, const int32_t* sel, const int32_t* ordering,
-                       const uint16_t* E, const float* h, int32_t* ids, float* z, float* logits, size_t V,
-                       uint64_t* keys, uint32_t* cnt, int32_t* next, int32_t* out2, int stride2) {
+hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,
+                       const int32_t* ordering, const uint16_t* E, const float* h, int32_t* sel, int32_t* ids,
+                       float* z, float* logits, size_t V, uint64_t* keys) {
   dim3 grid(k, B);
-  k_head<<<grid, 256, H * sizeof(float), s>>>(k, vsc, H, sel, ordering, E, h, ids, z, logits, V, keys, cnt, next,
-                                              out2, stride2);
+  k_head<<<grid, 256, 0, s>>>(C, k, vsc, H, scores, ordering, E, h, sel, ids, z, logits, V, keys);
   return hipGetLastError();
 }
 
-hipError_t launch_zero_u32(hipStream_t s, uint32_t* p, int n) {
-  k_zero_u32<<<1, 256, 0, s>>>(p, n);
+hipError_t launch_final(hipStream_t s, int B, int k, const uint64_t* keys, int32_t* next, int32_t* out2,
+                        int stride2) {
+  k_final<<<B, 64, 0, s>>>(k, keys, next, out2, stride2);
   return hipGetLastError();
 }
 

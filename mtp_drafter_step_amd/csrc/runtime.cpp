@@ -78,8 +78,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Offsets of every intermediate in the caller's workspace for a given batch.
 struct Plan {
-  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, cnt, total;
-  int ncnt_attn, ncnt;
+  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, total;
 };
 
 Plan make_plan(const mtpd_config& c, int B, int vsc) {
@@ -108,9 +107,6 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.ids = take((size_t)B * c.top_k * vsc * 4);
   p.z = take((size_t)B * c.top_k * vsc * 4);
   p.keys = take((size_t)B * c.top_k * 8);
-  p.ncnt_attn = B * c.n_kv_head;
-  p.ncnt = p.ncnt_attn + B;
-  p.cnt = take((size_t)p.ncnt * 4);
   p.total = off;
   return p;
 }
@@ -134,13 +130,16 @@ int check_config(const mtpd_config* c) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(MTPD_ESHAPE, "query heads per kv head must be 1, 2, 4 or 8");
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
     return fail(MTPD_ESHAPE, "head_dim must be 64, 128 or 256");
-  if (c->hidden % 8 != 0 || c->backbone % 16 != 0 || c->ffn % 8 != 0)
-    return fail(MTPD_ESHAPE, "hidden and ffn must be multiples of 8, backbone a multiple of 16");
-  if (c->hidden > 4096 || c->ffn > 4096 || c->n_head * c->head_dim > 4096)
-    return fail(MTPD_ESHAPE, "hidden, ffn and n_head*head_dim must be <= 4096");
-  if (c->n_centroids > 8192) return fail(MTPD_ESHAPE, "n_centroids > 8192");
-  if (c->vocab / c->n_centroids > 1024) return fail(MTPD_ESHAPE, "vocab / n_centroids > 1024");
-  if (c->top_k > 1024) return fail(MTPD_ESHAPE, "top_k > 1024");
+  if (c->hidden % 256 != 0 || c->hidden > 1024) return fail(MTPD_ESHAPE, "hidden must be a multiple of 256, <= 1024");
+  if (c->backbone % 256 != 0 || c->backbone > 8192)
+    return fail(MTPD_ESHAPE, "backbone must be a multiple of 256, <= 8192");
+  if (c->ffn % 256 != 0 || c->ffn > 4096) return fail(MTPD_ESHAPE, "ffn must be a multiple of 256, <= 4096");
+  if ((c->n_head * c->head_dim) % 256 != 0 || c->n_head * c->head_dim > 4096)
+    return fail(MTPD_ESHAPE, "n_head*head_dim must be a multiple of 256, <= 4096");
+  if (c->n_centroids > mtpd::kMaxCentroids) return fail(MTPD_ESHAPE, "n_centroids > 4096");
+  if (c->top_k > mtpd::kMaxTopK) return fail(MTPD_ESHAPE, "top_k > 64");
+  const int vsc = c->vocab / c->n_centroids;
+  if (vsc % 16 != 0 || vsc > 1024) return fail(MTPD_ESHAPE, "vocab / n_centroids must be a multiple of 16, <= 1024");
   if (c->n_layer > 32) return fail(MTPD_ESHAPE, "n_layer > 32");
   if (!(c->rms_eps >= 0.f) || !(c->attn_scale > 0.f)) return fail(MTPD_EINVAL, "rms_eps < 0 or attn_scale <= 0");
   return MTPD_OK;
@@ -183,8 +182,9 @@ int check_kv(const mtpd_handle_s* h, const mtpd_kv& kv, int B, const char* name,
   return MTPD_OK;
 }
 
-// Splits of each row's key window: about one block per 256 CUs' share of the batch's keys, at least 128 keys per
-// block, at most kMaxSplit blocks per (row, kv head).
+// Splits of each row's key window: one block per row when the longest window is at most 1024 keys (the block's
+// waves merge in LDS); otherwise about one block per 256 CUs' share of the batch's keys, at least 128 keys per
+// block, at most kMaxSplit blocks per (row, kv head), merged by a second kernel.
 int nsplit_for(const mtpd::RowWindows& win, int B, int nkv) {
   int mx = 1;
   long total = 0;
@@ -192,35 +192,31 @@ int nsplit_for(const mtpd::RowWindows& win, int B, int nkv) {
     mx = std::max(mx, win.count[b]);
     total += win.count[b];
   }
+  if (mx <= 1024) return 1;
   long per = (total * nkv + 255) / 256;
   per = std::max<long>(128, (per + 63) / 64 * 64);
   int ns = (int)((mx + per - 1) / per);
-  return std::max(1, std::min(ns, mtpd::kMaxSplit));
+  return std::max(2, std::min(ns, mtpd::kMaxSplit));
 }
 
-// The head on fp32 hidden states h [B][H] in the workspace: top-k of precomputed scores, gather + dot (+ scatter),
-// argmax.
+// The masked head on fp32 hidden states h [B][H] and centroid scores already in the workspace: per (row, slot)
+// top-k + gather + dot (+ scatter) and the slot's best (value, id) key.
 int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const float* hsrc,
-             float* logits, int32_t* next, int32_t* next2, int stride2, int32_t* sel_out, int32_t* ids_out,
-             float* z_out) {
+             float* logits, int32_t* sel_out, int32_t* ids_out, float* z_out) {
   const mtpd_config& c = h->cfg;
-  int32_t* sel = sel_out ? sel_out : at<int32_t>(ws, p.sel);
-  int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, p.ids);
-  float* z = z_out ? z_out : at<float>(ws, p.z);
-  // [Inventory] "Centroid / ordered embeddings LM head", step 2: top_k of the centroid logits
-  LAUNCH(mtpd::launch_topk(s, B, at<float>(ws, p.scores), c.n_centroids, c.top_k, sel));
-  // steps 3-5: candidate ids, sparse logits, scatter into the (already filled) row, argmax
-  LAUNCH(mtpd::launch_head(s, B, c.top_k, h->vsc, c.hidden, sel, h->w.token_ordering, h->w.token_embd, hsrc, ids, z,
-                           logits, (size_t)c.vocab, at<uint64_t>(ws, p.keys), at<uint32_t>(ws, p.cnt) + p.ncnt_attn,
-                           next, next2, stride2));
+  // [Inventory] "Centroid / ordered embeddings LM head", steps 2-5
+  LAUNCH(mtpd::launch_head(s, B, c.n_centroids, c.top_k, h->vsc, c.hidden, at<float>(ws, p.scores),
+                           h->w.token_ordering, h->w.token_embd, hsrc, sel_out, ids_out, z_out, logits,
+                           (size_t)c.vocab, at<uint64_t>(ws, p.keys)));
   return MTPD_OK;
 }
 
-// One drafter step on workspace buffers; input hidden `th` [B][Bb] and tokens `tok` [B].
+// One drafter step on workspace buffers: input hidden `th` [B][Bb], token source `ts`; leaves the per-slot argmax
+// keys in the workspace (the step's token is their maximum).
 int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const uint16_t* th,
-             const int32_t* tok, const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win,
-             const int* nsplit, float* logits, int32_t* next, int32_t* next2, int stride2, uint16_t* hidden_out,
-             int32_t* sel_out, int32_t* ids_out, float* z_out) {
+             mtpd::TokenSource ts, const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win,
+             const int* nsplit, float* logits, uint16_t* hidden_out, int32_t* sel_out, int32_t* ids_out,
+             float* z_out) {
   const mtpd_config& c = h->cfg;
   const int H = c.hidden, Bb = c.backbone, QD = c.n_head * c.head_dim, F = c.ffn, nL = c.n_layer;
   float* x[2] = {at<float>(ws, p.x[0]), at<float>(ws, p.x[1])};
@@ -229,9 +225,8 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
   float* t = at<float>(ws, p.t);
   float* m = at<float>(ws, p.m);
   float* d = at<float>(ws, p.d);
-  uint32_t* cnt = at<uint32_t>(ws, p.cnt);
   // input assembly + pre_projection ([MTP doc] "What it is"; [Guide] section 2(3))
-  LAUNCH(mtpd::launch_pre(s, B, Bb, H, c.vocab, th, tok, temb, c.embed_scale, h->w.pre_proj, x[0], cnt, p.ncnt));
+  LAUNCH(mtpd::launch_pre(s, B, Bb, H, c.vocab, th, ts, temb, c.embed_scale, h->w.pre_proj, x[0]));
   int cur = 0;
   const size_t BV = (size_t)B * c.vocab;
   for (int l = 0; l < nL; ++l) {
@@ -247,12 +242,16 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
     LAUNCH(mtpd::launch_qproj(s, B, H, QD, rq, L.attn_norm, c.rms_eps, L.attn_q, q));
     LAUNCH(mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
                              cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale,
-                             at<float>(ws, p.pacc), at<float>(ws, p.pml), cnt, o));
+                             at<float>(ws, p.pacc), at<float>(ws, p.pml), o));
+    if (nsplit[type] > 1)
+      LAUNCH(mtpd::launch_attn_merge(s, B, c.n_head, c.head_dim, nsplit[type], at<float>(ws, p.pacc),
+                                     at<float>(ws, p.pml), o));
     LAUNCH(mtpd::launch_dense(s, B, QD, H, o, L.attn_output, t));
     mtpd::Residual rf{x[cur], t, L.post_attention_norm, 1.0f, x[cur ^ 1]};
     cur ^= 1;
     mtpd::FillRange fr{nullptr, 0, 0};
-    if (logits) fr = mtpd::FillRange{logits, (BV * l / nL) & ~size_t(3), l + 1 == nL ? BV : (BV * (l + 1) / nL) & ~size_t(3)};
+    if (logits)
+      fr = mtpd::FillRange{logits, (BV * l / nL) & ~size_t(3), l + 1 == nL ? BV : (BV * (l + 1) / nL) & ~size_t(3)};
     LAUNCH(mtpd::launch_ffn(s, B, H, F, rf, L.ffn_norm, c.rms_eps, L.ffn_gate, L.ffn_up, m, fr));
     LAUNCH(mtpd::launch_dense(s, B, F, H, m, L.ffn_down, d));
   }
@@ -261,7 +260,7 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
   // output norm, post_projection (the next step's hidden input, [Guide] section 6) and centroid scores
   LAUNCH(mtpd::launch_post(s, B, H, Bb, c.n_centroids, rp, h->w.output_norm, c.rms_eps, h->w.post_proj,
                            h->w.centroids, at<float>(ws, p.h), hidden_out, at<float>(ws, p.scores)));
-  return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, next, next2, stride2, sel_out, ids_out, z_out);
+  return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, sel_out, ids_out, z_out);
 }
 
 int check_call(const mtpd_handle_s* h, void* ws, int B) {
@@ -439,8 +438,11 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
                                 sparse_ids, sparse_logits},
                                win, nsplit, kv);
   return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
-    return run_step(h, s, workspace, p, batch, target_hidden, last_token, target_embd, kv, win, nsplit, logits,
-                    next_token, nullptr, 0, hidden_out, sel_centroids, sparse_ids, sparse_logits);
+    mtpd::TokenSource ts{last_token, nullptr, 0, nullptr, 0, nullptr};
+    CHECK(run_step(h, s, workspace, p, batch, target_hidden, ts, target_embd, kv, win, nsplit, logits, hidden_out,
+                   sel_centroids, sparse_ids, sparse_logits));
+    LAUNCH(mtpd::launch_final(s, batch, h->cfg.top_k, at<uint64_t>(workspace, p.keys), next_token, nullptr, 0));
+    return MTPD_OK;
   });
 }
 
@@ -465,15 +467,17 @@ int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch
   return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
     uint16_t* hid[2] = {at<uint16_t>(workspace, p.hid),
                         at<uint16_t>(workspace, p.hid) + (size_t)batch * h->cfg.backbone};
-    int32_t* tk[2] = {at<int32_t>(workspace, p.tok), at<int32_t>(workspace, p.tok) + batch};
+    const uint64_t* keys = at<uint64_t>(workspace, p.keys);
     for (int i = 0; i < n; ++i) {
       const uint16_t* th = (i == 0) ? target_hidden : hid[(i - 1) & 1];
-      const int32_t* tok = (i == 0) ? last_token : tk[(i - 1) & 1];
+      // step i's token: the caller's for i = 0, else the previous step's argmax (recorded as tokens[:, i-1])
+      mtpd::TokenSource ts{last_token, nullptr, 0, nullptr, 0, nullptr};
+      if (i > 0) ts = mtpd::TokenSource{nullptr, keys, h->cfg.top_k, tokens + (i - 1), n, nullptr};
       uint16_t* hout = (i == n - 1) ? hidden_out : hid[i & 1];
-      CHECK(run_step(h, s, workspace, p, batch, th, tok, target_embd, kv, win, nsplit,
-                     logits ? logits + (size_t)i * BV : nullptr, tk[i & 1], tokens + i, n, hout, nullptr, nullptr,
-                     nullptr));
+      CHECK(run_step(h, s, workspace, p, batch, th, ts, target_embd, kv, win, nsplit,
+                     logits ? logits + (size_t)i * BV : nullptr, hout, nullptr, nullptr, nullptr));
     }
+    LAUNCH(mtpd::launch_final(s, batch, h->cfg.top_k, keys, at<int32_t>(workspace, p.tok), tokens + (n - 1), n));
     return MTPD_OK;
   });
 }
@@ -491,11 +495,11 @@ int mtpd_masked_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
                                nullptr, nullptr, nullptr);
   return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
     // [Inventory] "Centroid / ordered embeddings LM head", step 1: centroid logits
-    LAUNCH(mtpd::launch_zero_u32(s, at<uint32_t>(workspace, p.cnt), p.ncnt));
-    LAUNCH(mtpd::launch_dense(s, m, c.hidden, c.n_centroids, hidden, h->w.centroids, at<float>(workspace, p.scores)));
+    LAUNCH(mtpd::launch_scores(s, m, c.hidden, c.n_centroids, hidden, h->w.centroids, at<float>(workspace, p.scores)));
     if (logits) LAUNCH(mtpd::launch_fill(s, logits, (size_t)m * c.vocab));
-    return run_head(h, s, workspace, p, m, hidden, logits, argmax, nullptr, 0, sel_centroids, sparse_ids,
-                    sparse_logits);
+    CHECK(run_head(h, s, workspace, p, m, hidden, logits, sel_centroids, sparse_ids, sparse_logits));
+    LAUNCH(mtpd::launch_final(s, m, c.top_k, at<uint64_t>(workspace, p.keys), argmax, nullptr, 0));
+    return MTPD_OK;
   });
 }
 

@@ -78,7 +78,8 @@ def create_rc(cfg, weights=None, max_batch=16):
     (dict(n_head=3, n_kv_head=2), abi.MTPD_ESHAPE, "n_kv_head"),
     (dict(n_centroids=0), abi.MTPD_EUNSUP, "dense"),
     (dict(head_dim=512), abi.MTPD_ESHAPE, "head_dim"),
-    (dict(hidden=250), abi.MTPD_ESHAPE, "multiples of 8"),
+    (dict(hidden=250), abi.MTPD_ESHAPE, "multiple of 256"),
+    (dict(top_k=65, n_centroids=2048), abi.MTPD_ESHAPE, "top_k > 64"),
     (dict(swa_window=0), abi.MTPD_ESHAPE, "positive"),
     (dict(attn_scale=0.0), abi.MTPD_EINVAL, "attn_scale"),
 ])
