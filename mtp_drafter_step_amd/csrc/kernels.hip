@@ -20,6 +20,7 @@
 #include "kernels.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -617,6 +618,216 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
   }
 }
 
+// Matrix-core variant for head_dim 256 and up to 4 query heads per kv head (heads padded to the 16 rows of an
+// MFMA tile). Per wave and batch of 16 keys:
+//   S[16 keys][16 heads] = K_tile . q^T with v_mfma_f32_16x16x32_bf16: the key rows load straight into the A
+//     operand (lane l: key l%16, 8 dims at 8*(l/16) of each 32-dim step); the fp32 query is split into two bf16
+//     terms q = q_hi + q_lo (relative error <= 2^-16) so the product keeps fp32-level accuracy;
+//   online softmax on the S layout (lane l holds keys 4*(l/16)+r of head l%16);
+//   O[16 heads][256] += P . V with v_mfma_f32_16x16x16_bf16: P (split into bf16 hi + lo) is already in the A layout,
+//     V comes from the wave's LDS copy of the key tile read column-wise (4 keys of one dim per lane).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv, const float* __restrict__ q,
+                                                          const uint16_t* __restrict__ qnorm, float eps,
+                                                          const float* __restrict__ rope, int type,
+                                                          const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ Vc, int cap, RowWindows win,
+                                                          int nsplit, float scale_log2, float* __restrict__ pacc,
+                                                          float* __restrict__ pml, float* __restrict__ o) {
+  constexpr int HD = 256, KSTEPS = HD / 32, TILES = HD / 16, LROW = HD + 8, S = NW * 16;
+  __shared__ float qs[G][HD];
+  __shared__ __attribute__((aligned(16))) uint16_t qop[KSTEPS][2][G][4][8];  // [step][hi/lo][head][kq][8 dims]
+  __shared__ __attribute__((aligned(16))) uint16_t vt[NW][16][LROW];
+  __shared__ float wml[NW][G][2];
+  __shared__ float wacc[NW][G][HD];
+  const int sp = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / nkv, g = bg % nkv;
+  const int wave = wave_id(), lane = lane_id();
+  const int hq = lane & 15, kq = lane >> 4;
+  constexpr int half = HD / 2;
+
+  const int cntk = win.count[b];
+  const int chunk = (cntk + nsplit - 1) / nsplit;
+  const int k0 = win.start[b] + sp * chunk;
+  const int k1 = min(win.start[b] + cntk, k0 + chunk);
+  const bool same_v = (Vc == K);
+  const uint16_t* Kb = K + ((size_t)b * nkv + g) * (size_t)cap * HD + 8 * kq;
+  const uint16_t* Vb = Vc + ((size_t)b * nkv + g) * (size_t)cap * HD + 8 * kq;
+
+  // key rows of batch t (lane: key t + hq, dims 32c + 8kq .. +8), clamped into the block's range; batch t + S is
+  // in flight while batch t is computed
+  uint4 ka[KSTEPS], kn[KSTEPS];
+  int t0 = k0 + wave * 16;
+  {
+    const uint16_t* r = Kb + (size_t)min(t0 + hq, k1 - 1) * HD;
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) ka[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
+  }
+
+  // q_norm + rotation at the row's constant position ([Guide] section 2(2))
+  const float* tab = rope + ((size_t)b * 2 + type) * 2 * half;
+  for (int hh = wave; hh < G; hh += NW) {
+    const float* qr = q + ((size_t)b * nh + g * G + hh) * HD;
+    float v[4], wq[4], co[4], si[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = lane * 4 + e;
+      const int i = d & (half - 1);
+      v[e] = qr[d];
+      wq[e] = bf2f(qnorm[d]);
+      co[e] = tab[i];
+      si[e] = tab[half + i];
+      ss = fmaf(v[e], v[e], ss);
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = v[e] * r * wq[e];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float partner = __shfl_xor(v[e], 32, 64);  // dim i <-> i + HD/2
+      qs[hh][lane * 4 + e] = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
+    }
+  }
+  __syncthreads();
+  // q = q_hi + q_lo in bf16, stored in the MFMA B-operand order
+  for (int i = threadIdx.x; i < KSTEPS * G * 4 * 8; i += NW * 64) {
+    const int e = i & 7, kk = (i >> 3) & 3, hh = (i >> 5) % G, c = i / (32 * G);
+    const float v = qs[hh][32 * c + 8 * kk + e];
+    const uint16_t hb = f2bf(v);
+    qop[c][0][hh][kk][e] = hb;
+    qop[c][1][hh][kk][e] = f2bf(v - bf2f(hb));
+  }
+  __syncthreads();
+
+  float mrun = -INFINITY, lrun = 0.f;  // softmax state of head hq (identical in the 4 lanes of that head)
+  f32x4 acc[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* tile = &vt[wave][0][0];
+  const int hsel = hq < G ? hq : 0;
+
+  for (; t0 < k1; t0 += S) {
+    const int tb = t0;
+    {
+      const uint16_t* r = Kb + (size_t)min(t0 + S + hq, k1 - 1) * HD;
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) kn[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
+    }
+    const int nk = min(16, k1 - tb);
+    // V tile into this wave's LDS (row = key hq, dims 32c + 8kq .. +8)
+    if (same_v) {
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = ka[c];
+    } else {
+      const uint16_t* r = Vb + (size_t)min(tb + hq, k1 - 1) * HD;
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c)
+        *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = *reinterpret_cast<const uint4*>(r + 32 * c);
+    }
+    // scores S[key 4kq + r][head hq]
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, ka[c]);
+      uint4 hi = *reinterpret_cast<const uint4*>(&qop[c][0][hsel][kq][0]);
+      uint4 lo = *reinterpret_cast<const uint4*>(&qop[c][1][hsel][kq][0]);
+      if (hq >= G) hi = lo = make_uint4(0u, 0u, 0u, 0u);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), sacc, 0, 0, 0);
+    }
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (4 * kq + r < nk && hq < G) ? sacc[r] * scale_log2 : -INFINITY;
+    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(mrun, mt);
+    const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
+    float pv[4], ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
+      ps += pv[r];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lrun = lrun * alpha + ps;
+    mrun = mn;
+    i16x4 phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint16_t hb = f2bf(pv[r]);
+      phi[r] = (short)hb;
+      plo[r] = (short)f2bf(pv[r] - bf2f(hb));
+    }
+    // rescale the accumulators: D rows are heads 4kq + r, whose alpha lives in lane 4kq + r
+    float al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * kq + r, 64);
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      i16x4 vb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vb[r] = (short)tile[(4 * kq + r) * LROW + 16 * t + hq];
+      f32x4 a = acc[t];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] *= al[r];
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
+      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);
+      acc[t] = a;
+    }
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) ka[c] = kn[c];
+  }
+  // combine the waves of this block: head h's state is in lane h; its output row in lanes 0-15 (kq = 0), slot h
+  if (lane < G) {
+    wml[wave][lane][0] = mrun;
+    wml[wave][lane][1] = lrun;
+  }
+  if (kq == 0) {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < G) wacc[wave][r][16 * t + hq] = acc[t][r];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * HD; i += NW * 64) {
+    const int hh = i / HD, d = i % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wml[w][hh][0]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = wml[w][hh][0];
+        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        L = fmaf(wml[w][hh][1], f, L);
+        A = fmaf(wacc[w][hh][d], f, A);
+      }
+    }
+    const size_t hqq = (size_t)b * nh + g * G + hh;
+    if (nsplit == 1) {
+      o[hqq * HD + d] = (L > 0.f) ? A / L : 0.f;
+    } else {
+      const size_t slot = hqq * kMaxSplit + sp;
+      pacc[slot * HD + d] = A;
+      if (d == 0) {
+        pml[slot * 2 + 0] = M;
+        pml[slot * 2 + 1] = L;
+      }
+    }
+  }
+}
+
 // grid (B * nh), 256 threads: thread d of head (b, h) merges the nsplit partials
 __global__ __launch_bounds__(256) void k_attn_merge(int hd, int nsplit, const float* __restrict__ pacc,
                                                     const float* __restrict__ pml, float* __restrict__ o) {
@@ -809,6 +1020,15 @@ __global__ void k_fill(float4* __restrict__ p, size_t n4, float* __restrict__ ta
 
 int row_groups(int B) { return (B + kRG - 1) / kRG; }
 
+// MTPD_ATTN_VALU=1 selects the vector-ALU attention for every shape (kept for comparison and as the general path).
+bool getenv_no_mfma() {
+  static const int v = [] {
+    const char* e = getenv("MTPD_ATTN_VALU");
+    return (e && e[0] == '1') ? 1 : 0;
+  }();
+  return v != 0;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------------------
@@ -860,6 +1080,12 @@ hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const floa
   dim3 grid(nsplit, B * nkv);
   const float sl2 = scale * 1.4426950408889634f;
   const int G = nh / nkv;
+  if (hd == 256 && G <= 4 && !getenv_no_mfma()) {
+    if (G == 4) k_attn_mfma<4, 4><<<grid, 256, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
+    else if (G == 2) k_attn_mfma<2, 4><<<grid, 256, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
+    else k_attn_mfma<1, 4><<<grid, 256, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
+    return hipGetLastError();
+  }
 #define MTPD_ATTN(HD_, G_, NW_)                                                                             \
   if (hd == HD_ && G == G_) {                                                                               \
     k_attn<HD_, G_, NW_><<<grid, NW_ * 64, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win,  \

@@ -39,12 +39,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 namespace {
 
-constexpr int kGraphCache = 8;
+constexpr int kGraphCache = 32;
+constexpr int kChains = 4;  // maximum sub-batches (make_chains currently uses one: graph replays on separate streams
+                            // were measured not to overlap)
 
 // Everything a captured call depends on: the graph of one (call, arguments) pair is replayed only when every
 // pointer, size and per-row window is the same.
 struct CallKey {
-  int32_t kind, batch, n;
+  int32_t kind, batch, n, chain;
   const void* ptrs[16];
   mtpd::RowWindows win[2];
   int32_t nsplit[2];
@@ -70,6 +72,10 @@ struct mtpd_handle_s {
   hipStream_t cap_stream = nullptr;
   GraphEntry graphs[kGraphCache];
   uint64_t tick = 0;
+  // independent row chains run on their own streams, forked from and joined back into the caller's stream
+  hipStream_t chain_stream[kChains] = {};
+  hipEvent_t fork_ev = nullptr;
+  hipEvent_t join_ev[kChains] = {};
 };
 
 namespace {
@@ -285,44 +291,135 @@ int check_step_inputs(const mtpd_handle_s* h, int B, const uint16_t* th, const i
   return MTPD_OK;
 }
 
-// Run `body(stream)` on the caller's stream: replay a cached graph of the same call when there is one, capture
-// one otherwise; when the caller's stream is itself being captured, or graphs are off, launch directly.
-template <typename Body>
-int run_graphed(mtpd_handle_s* h, hipStream_t s, const CallKey& key, Body body) {
-  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-  if (!h->use_graphs || hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone)
-    return body(s);
-  GraphEntry* hit = nullptr;
-  for (auto& e : h->graphs)
-    if (e.exec && e.key == key) hit = &e;
-  if (!hit) {
-    if (!h->cap_stream) LAUNCH(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
-    GraphEntry* slot = &h->graphs[0];
-    for (auto& e : h->graphs) {
-      if (!e.exec) { slot = &e; break; }
-      if (e.used < slot->used) slot = &e;
+// Rows are independent, so a batch is cut into up to kChains sub-batches (multiples of the 4-row group) whose
+// kernel chains run concurrently: every stage is latency-bound, and one chain's memory waits overlap the others'
+// work. Each chain has its own workspace region.
+struct Chains {
+  int n;
+  int rows[kChains + 1];
+  int bmax;
+};
+
+Chains make_chains(int B) {
+  Chains c{};
+  const int per = B;  // one chain: see kChains
+  c.n = (B + per - 1) / per;
+  for (int i = 0; i <= c.n; ++i) c.rows[i] = std::min(B, i * per);
+  c.bmax = std::min(per, B);
+  return c;
+}
+
+// The rows [b0, b0 + Bc) of the shared caches, rotary tables and key windows.
+struct ChainView {
+  mtpd_shared_kv kv;
+  mtpd::RowWindows win[2];
+  int nsplit[2];
+};
+
+ChainView chain_view(const mtpd_handle_s* h, const mtpd_shared_kv* kv, const mtpd::RowWindows* win, int b0, int Bc) {
+  ChainView v;
+  v.kv = *kv;
+  const size_t hd = (size_t)h->cfg.head_dim, nkv = (size_t)h->cfg.n_kv_head;
+  const size_t ss = nkv * (size_t)kv->sliding.cap * hd, fs = nkv * (size_t)kv->full.cap * hd;
+  v.kv.sliding.k = kv->sliding.k + (size_t)b0 * ss;
+  v.kv.sliding.v = kv->sliding.v + (size_t)b0 * ss;
+  v.kv.full.k = kv->full.k + (size_t)b0 * fs;
+  v.kv.full.v = kv->full.v + (size_t)b0 * fs;
+  v.kv.sliding.len = kv->sliding.len + b0;
+  v.kv.full.len = kv->full.len + b0;
+  v.kv.rope = kv->rope + (size_t)b0 * 2 * hd;
+  for (int t = 0; t < 2; ++t) {
+    std::memset(&v.win[t], 0, sizeof(v.win[t]));
+    for (int i = 0; i < Bc; ++i) {
+      v.win[t].start[i] = win[t].start[b0 + i];
+      v.win[t].count[i] = win[t].count[b0 + i];
     }
-    LAUNCH(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
-    int rc = body(h->cap_stream);
-    hipGraph_t graph = nullptr;
-    hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
-    if (rc != MTPD_OK) {
-      if (graph) (void)hipGraphDestroy(graph);
-      return rc;
-    }
-    if (e != hipSuccess) return fail(MTPD_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
-    hipGraphExec_t exec = nullptr;
-    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(graph);
-    if (e != hipSuccess) return fail(MTPD_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
-    if (slot->exec) (void)hipGraphExecDestroy(slot->exec);
-    slot->key = key;
-    slot->exec = exec;
-    hit = slot;
+    v.nsplit[t] = nsplit_for(v.win[t], Bc, h->cfg.n_kv_head);
   }
-  hit->used = ++h->tick;
-  LAUNCH(hipGraphLaunch(hit->exec, s));
+  return v;
+}
+
+// body(chain, stream) for every chain: forked from `s` by an event, joined back by events.
+template <typename Body>
+int run_chains(mtpd_handle_s* h, hipStream_t s, const Chains& ch, Body body) {
+  if (ch.n == 1) return body(0, s);
+  if (!h->fork_ev) {
+    LAUNCH(hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming));
+    for (int c = 0; c < kChains; ++c) {
+      LAUNCH(hipStreamCreateWithFlags(&h->chain_stream[c], hipStreamNonBlocking));
+      LAUNCH(hipEventCreateWithFlags(&h->join_ev[c], hipEventDisableTiming));
+    }
+  }
+  LAUNCH(hipEventRecord(h->fork_ev, s));
+  for (int c = 0; c < ch.n; ++c) {
+    LAUNCH(hipStreamWaitEvent(h->chain_stream[c], h->fork_ev, 0));
+    CHECK(body(c, h->chain_stream[c]));
+    LAUNCH(hipEventRecord(h->join_ev[c], h->chain_stream[c]));
+  }
+  for (int c = 0; c < ch.n; ++c) LAUNCH(hipStreamWaitEvent(s, h->join_ev[c], 0));
   return MTPD_OK;
+}
+
+// Find or capture the graph of one chain of a call.
+template <typename Body>
+int chain_graph(mtpd_handle_s* h, const CallKey& key, int chain, Body body, hipGraphExec_t* out) {
+  CallKey k = key;
+  k.chain = chain;
+  for (auto& e : h->graphs)
+    if (e.exec && e.key == k) {
+      e.used = ++h->tick;
+      *out = e.exec;
+      return MTPD_OK;
+    }
+  if (!h->cap_stream) LAUNCH(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+  GraphEntry* slot = &h->graphs[0];
+  for (auto& e : h->graphs) {
+    if (!e.exec) {
+      slot = &e;
+      break;
+    }
+    if (e.used < slot->used) slot = &e;
+  }
+  LAUNCH(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  int rc = body(chain, h->cap_stream);
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
+  if (rc != MTPD_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(MTPD_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return fail(MTPD_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  if (slot->exec) (void)hipGraphExecDestroy(slot->exec);
+  slot->key = k;
+  slot->exec = exec;
+  slot->used = ++h->tick;
+  *out = exec;
+  return MTPD_OK;
+}
+
+// Run a call made of independent row chains, body(chain, stream) launching one chain's kernels, on the caller's
+// stream `s`. Each chain is replayed from its own captured graph (captured on first use) on its own stream, forked
+// from and joined back into `s` by events, so that the chains' kernels overlap. When the caller's stream is being
+// captured, or graphs are off, the chains' kernels are launched directly on the forked streams.
+template <typename Body>
+int run_call(mtpd_handle_s* h, hipStream_t s, const CallKey& key, const Chains& ch, Body body) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) st = hipStreamCaptureStatusActive;
+  if (!h->use_graphs || st != hipStreamCaptureStatusNone) return run_chains(h, s, ch, body);
+  hipGraphExec_t exec[kChains];
+  for (int c = 0; c < ch.n; ++c) CHECK(chain_graph(h, key, c, body, &exec[c]));
+  if (ch.n == 1) {
+    LAUNCH(hipGraphLaunch(exec[0], s));
+    return MTPD_OK;
+  }
+  return run_chains(h, s, ch, [&](int c, hipStream_t cs) -> int {
+    LAUNCH(hipGraphLaunch(exec[c], cs));
+    return MTPD_OK;
+  });
 }
 
 CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs, const mtpd::RowWindows* win,
@@ -330,6 +427,7 @@ CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs
   CallKey k;
   std::memset(&k, 0, sizeof(k));
   k.kind = kind;
+  k.chain = -1;
   k.batch = B;
   k.n = n;
   int i = 0;
@@ -411,12 +509,18 @@ void mtpd_destroy(mtpd_handle h) {
   for (auto& e : h->graphs)
     if (e.exec) (void)hipGraphExecDestroy(e.exec);
   if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+  for (int c = 0; c < kChains; ++c) {
+    if (h->chain_stream[c]) (void)hipStreamDestroy(h->chain_stream[c]);
+    if (h->join_ev[c]) (void)hipEventDestroy(h->join_ev[c]);
+  }
+  if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
   delete h;
 }
 
 size_t mtpd_workspace_bytes(mtpd_handle h, int32_t batch) {
   if (!h || batch < 1 || batch > h->max_batch) return 0;
-  return make_plan(h->cfg, batch, h->vsc).total;
+  const Chains ch = make_chains(batch);
+  return (size_t)ch.n * make_plan(h->cfg, ch.bmax, h->vsc).total;
 }
 
 int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batch, const uint16_t* target_hidden,
@@ -431,18 +535,26 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
   if (!next_token) return fail(MTPD_EINVAL, "next_token is NULL");
   CHECK(check_ptr(hidden_out, "hidden_out"));
   if (logits) CHECK(check_ptr(logits, "logits"));
-  const Plan p = make_plan(h->cfg, batch, h->vsc);
+  const Chains ch = make_chains(batch);
+  const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
   const CallKey key = make_key(1, batch, 1,
                                {workspace, target_hidden, last_token, target_embd, kv->sliding.k, kv->sliding.v,
                                 kv->full.k, kv->full.v, kv->rope, logits, next_token, hidden_out, sel_centroids,
                                 sparse_ids, sparse_logits},
                                win, nsplit, kv);
-  return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
-    mtpd::TokenSource ts{last_token, nullptr, 0, nullptr, 0, nullptr};
-    CHECK(run_step(h, s, workspace, p, batch, target_hidden, ts, target_embd, kv, win, nsplit, logits, hidden_out,
-                   sel_centroids, sparse_ids, sparse_logits));
-    LAUNCH(mtpd::launch_final(s, batch, h->cfg.top_k, at<uint64_t>(workspace, p.keys), next_token, nullptr, 0));
-    return MTPD_OK;
+  const mtpd_config& c = h->cfg;
+  const size_t kv_n = (size_t)c.top_k * h->vsc;
+  return run_call(h, static_cast<hipStream_t>(stream), key, ch, [&](int ci, hipStream_t cs) -> int {
+      const int b0 = ch.rows[ci], Bc = ch.rows[ci + 1] - b0;
+      void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
+      const ChainView v = chain_view(h, kv, win, b0, Bc);
+      mtpd::TokenSource ts{last_token + b0, nullptr, 0, nullptr, 0, nullptr};
+      CHECK(run_step(h, cs, wsc, p, Bc, target_hidden + (size_t)b0 * c.backbone, ts, target_embd, &v.kv, v.win,
+                     v.nsplit, logits ? logits + (size_t)b0 * c.vocab : nullptr,
+                     hidden_out + (size_t)b0 * c.backbone, sel_centroids ? sel_centroids + (size_t)b0 * c.top_k : nullptr,
+                     sparse_ids ? sparse_ids + b0 * kv_n : nullptr, sparse_logits ? sparse_logits + b0 * kv_n : nullptr));
+      LAUNCH(mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), next_token + b0, nullptr, 0));
+      return MTPD_OK;
   });
 }
 
@@ -458,27 +570,33 @@ int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch
   if (!tokens) return fail(MTPD_EINVAL, "tokens is NULL");
   CHECK(check_ptr(hidden_out, "hidden_out"));
   if (logits) CHECK(check_ptr(logits, "logits"));
-  const Plan p = make_plan(h->cfg, batch, h->vsc);
-  const size_t BV = (size_t)batch * h->cfg.vocab;
+  const Chains ch = make_chains(batch);
+  const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
+  const mtpd_config& c = h->cfg;
+  const size_t BV = (size_t)batch * c.vocab;
   const CallKey key = make_key(2, batch, n,
                                {workspace, target_hidden, last_token, target_embd, kv->sliding.k, kv->sliding.v,
                                 kv->full.k, kv->full.v, kv->rope, logits, tokens, hidden_out},
                                win, nsplit, kv);
-  return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
-    uint16_t* hid[2] = {at<uint16_t>(workspace, p.hid),
-                        at<uint16_t>(workspace, p.hid) + (size_t)batch * h->cfg.backbone};
-    const uint64_t* keys = at<uint64_t>(workspace, p.keys);
-    for (int i = 0; i < n; ++i) {
-      const uint16_t* th = (i == 0) ? target_hidden : hid[(i - 1) & 1];
-      // step i's token: the caller's for i = 0, else the previous step's argmax (recorded as tokens[:, i-1])
-      mtpd::TokenSource ts{last_token, nullptr, 0, nullptr, 0, nullptr};
-      if (i > 0) ts = mtpd::TokenSource{nullptr, keys, h->cfg.top_k, tokens + (i - 1), n, nullptr};
-      uint16_t* hout = (i == n - 1) ? hidden_out : hid[i & 1];
-      CHECK(run_step(h, s, workspace, p, batch, th, ts, target_embd, kv, win, nsplit,
-                     logits ? logits + (size_t)i * BV : nullptr, hout, nullptr, nullptr, nullptr));
-    }
-    LAUNCH(mtpd::launch_final(s, batch, h->cfg.top_k, keys, at<int32_t>(workspace, p.tok), tokens + (n - 1), n));
-    return MTPD_OK;
+  return run_call(h, static_cast<hipStream_t>(stream), key, ch, [&](int ci, hipStream_t cs) -> int {
+      const int b0 = ch.rows[ci], Bc = ch.rows[ci + 1] - b0;
+      void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
+      const ChainView v = chain_view(h, kv, win, b0, Bc);
+      uint16_t* hid[2] = {at<uint16_t>(wsc, p.hid), at<uint16_t>(wsc, p.hid) + (size_t)Bc * c.backbone};
+      const uint64_t* keys = at<uint64_t>(wsc, p.keys);
+      int32_t* tok_c = tokens + (size_t)b0 * n;
+      for (int i = 0; i < n; ++i) {
+        const uint16_t* th = (i == 0) ? target_hidden + (size_t)b0 * c.backbone : hid[(i - 1) & 1];
+        // step i's token: the caller's for i = 0, else the previous step's argmax (recorded as tokens[:, i-1])
+        mtpd::TokenSource ts{last_token + b0, nullptr, 0, nullptr, 0, nullptr};
+        if (i > 0) ts = mtpd::TokenSource{nullptr, keys, c.top_k, tok_c + (i - 1), n, nullptr};
+        uint16_t* hout = (i == n - 1) ? hidden_out + (size_t)b0 * c.backbone : hid[i & 1];
+        CHECK(run_step(h, cs, wsc, p, Bc, th, ts, target_embd, &v.kv, v.win, v.nsplit,
+                       logits ? logits + (size_t)i * BV + (size_t)b0 * c.vocab : nullptr, hout, nullptr, nullptr,
+                       nullptr));
+      }
+      LAUNCH(mtpd::launch_final(cs, Bc, c.top_k, keys, at<int32_t>(wsc, p.tok), tok_c + (n - 1), n));
+      return MTPD_OK;
   });
 }
 
@@ -489,17 +607,24 @@ int mtpd_masked_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
   CHECK(check_ptr(hidden, "hidden"));
   if (!argmax) return fail(MTPD_EINVAL, "argmax is NULL");
   if (logits) CHECK(check_ptr(logits, "logits"));
-  const Plan p = make_plan(h->cfg, m, h->vsc);
+  const Chains ch = make_chains(m);
+  const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
   const mtpd_config& c = h->cfg;
+  const size_t kv_n = (size_t)c.top_k * h->vsc;
   const CallKey key = make_key(3, m, 1, {workspace, hidden, logits, argmax, sel_centroids, sparse_ids, sparse_logits},
                                nullptr, nullptr, nullptr);
-  return run_graphed(h, static_cast<hipStream_t>(stream), key, [&](hipStream_t s) -> int {
-    // [Inventory] "Centroid / ordered embeddings LM head", step 1: centroid logits
-    LAUNCH(mtpd::launch_scores(s, m, c.hidden, c.n_centroids, hidden, h->w.centroids, at<float>(workspace, p.scores)));
-    if (logits) LAUNCH(mtpd::launch_fill(s, logits, (size_t)m * c.vocab));
-    CHECK(run_head(h, s, workspace, p, m, hidden, logits, sel_centroids, sparse_ids, sparse_logits));
-    LAUNCH(mtpd::launch_final(s, m, c.top_k, at<uint64_t>(workspace, p.keys), argmax, nullptr, 0));
-    return MTPD_OK;
+  return run_call(h, static_cast<hipStream_t>(stream), key, ch, [&](int ci, hipStream_t cs) -> int {
+      const int b0 = ch.rows[ci], Bc = ch.rows[ci + 1] - b0;
+      void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
+      const float* hc = hidden + (size_t)b0 * c.hidden;
+      float* lc = logits ? logits + (size_t)b0 * c.vocab : nullptr;
+      // [Inventory] "Centroid / ordered embeddings LM head", step 1: centroid logits
+      LAUNCH(mtpd::launch_scores(cs, Bc, c.hidden, c.n_centroids, hc, h->w.centroids, at<float>(wsc, p.scores)));
+      if (lc) LAUNCH(mtpd::launch_fill(cs, lc, (size_t)Bc * c.vocab));
+      CHECK(run_head(h, cs, wsc, p, Bc, hc, lc, sel_centroids ? sel_centroids + (size_t)b0 * c.top_k : nullptr,
+                     sparse_ids ? sparse_ids + b0 * kv_n : nullptr, sparse_logits ? sparse_logits + b0 * kv_n : nullptr));
+      LAUNCH(mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), argmax + b0, nullptr, 0));
+      return MTPD_OK;
   });
 }
 
