@@ -6,14 +6,24 @@ layers over a shared K=V cache of 8192 keys per sequence, 3 sliding layers with 
 2048-centroid top-32 masked head over a 262144 vocabulary, the -1e30 logits row written every step). Inputs are
 synthetic (seeded counter-based generator) and resident in HBM before the timed region.
 
-Prints one JSON line: draft tokens/s (value), µs per drafter step, the roofline of the timed launch (algorithmic
-bytes / HIP-event duration against 8 TB/s), and the CPU oracle timed on a bounded sample on this host.
+Prints one JSON line: draft tokens/s (value), µs per drafter step, the roofline of the dominant kernel (its
+algorithmic bytes per launch over its HIP-event launch duration, against 8 TB/s), and the CPU oracle timed on a
+bounded sample on this host.
+
+Host-only helper modes (no GPU) turn rocprofv3 output of this script into the text summaries kept in profiles/:
+  --summarize-stats DIR   kernel-trace statistics of a bench run
+  --summarize-pmc FETCH_DIR WRITE_DIR   FETCH_SIZE / WRITE_SIZE per dispatch of the dominant kernel, scaled by what
+                          the same counters read for the calibration copy (--copy-probe) of known size
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -21,9 +31,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc", "kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_PROBE_BYTES = 512 << 20
+
+# launch-site label (as recorded by the library's timing records) -> kernel symbol stem
+SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma", "attn_full": "k_attn_mfma",
+               "attn_merge_sliding": "k_attn_merge", "attn_merge_full": "k_attn_merge", "o_proj": "k_dense",
+               "down": "k_dense", "ffn": "k_ffn", "post": "k_post", "head": "k_head", "final": "k_final",
+               "scores": "k_dense", "fill": "k_fill"}
 
 
-def algorithmic_bytes(shape, batch, lens, distinct_clusters, with_logits=True):
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def step_bytes(shape, batch, lens, distinct_clusters, with_logits=True):
     """Bytes one drafter step must move: weights once, each cache's K (= V) once over the keys it reads (the
     sliding window counted once for the three sliding layers), the selected clusters' head rows, their ordering
     ids, the logits row, and target hidden / embedding rows / hidden_out."""
@@ -39,9 +63,40 @@ def algorithmic_bytes(shape, batch, lens, distinct_clusters, with_logits=True):
                                                          io=io)
 
 
+def site_bytes(site, shape, batch, lens, distinct_clusters):
+    """Algorithmic bytes of one launch of a launch site: the weights and cache rows the step needs from it, its
+    activation inputs and outputs (fp32), and its share of the logits row. Intermediates that exist only because
+    the path is split into kernels (attention partials) count for the merge only."""
+    B, H, Bb, F, QD, hd = batch, shape.hidden, shape.backbone, shape.ffn, shape.q_dim, shape.head_dim
+    act = lambda n: 4 * B * n  # noqa: E731  fp32 activation rows
+    W = shape.swa_window
+    if site == "pre":
+        return 2 * H * 2 * Bb + 2 * 2 * B * Bb + act(H)
+    if site == "qproj":
+        return 2 * QD * H + 2 * H + 3 * act(H) + act(QD)
+    if site in ("attn_sliding", "attn_full"):
+        keys = sum(L if site == "attn_full" else min(W, L) for L in lens)
+        return shape.n_kv_head * hd * 2 * keys + 2 * hd + 2 * act(QD)
+    if site.startswith("attn_merge"):
+        return act(QD)
+    if site == "o_proj":
+        return 2 * H * QD + act(QD) + act(H)
+    if site == "ffn":
+        return 2 * 2 * F * H + 2 * H + 3 * act(H) + act(F) + 4 * shape.vocab * B // shape.n_layer
+    if site == "down":
+        return 2 * H * F + act(F) + act(H)
+    if site == "post":
+        return 2 * (Bb + shape.n_centroids) * H + 2 * H + 2 * act(H) + 2 * B * Bb + act(shape.n_centroids)
+    if site == "head":
+        n = shape.top_k * shape.vsc
+        return distinct_clusters * shape.vsc * H * 2 + 4 * n * B + act(shape.n_centroids) + act(H) + 4 * n * B
+    if site == "final":
+        return 8 * shape.top_k * B + 4 * B
+    raise KeyError(site)
+
+
 def cpu_baseline(wl, seconds):
     """The oracle as it stands, on single-row drafter steps of the same workload, for about `seconds`."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle as O
@@ -50,6 +105,7 @@ def cpu_baseline(wl, seconds):
     w = synth.make_weights(shape, seed=wl.seed)
     inp = synth.make_inputs(wl, with_target_embd=False)
     m = O.Model(O.config_from(shape), w)
+    import numpy as np
     ks = [inp["k_sliding"].numpy().view(np.uint16), inp["k_full"].numpy().view(np.uint16)]
     kv = O.SharedKV(k=ks, v=ks, lens=[inp["len_sliding"], inp["len_full"]], rope=inp["rope"].numpy())
     th = inp["target_hidden"].numpy().view(np.uint16)
@@ -71,19 +127,28 @@ def cpu_baseline(wl, seconds):
                       f" first step of the block), fp64 NumPy oracle, {dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="e4b_b16_ctx8192_block4")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus above 1 is not supported"}))
-        sys.exit(2)
+def traffic_file(kernel, workload):
+    return os.path.join(PROFILES, f"{kernel}__{workload}.traffic.md")
 
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when absent or taken on another source."""
+    p = traffic_file(kernel, workload)
+    if not os.path.exists(p):
+        return None
+    m = re.search(r"<!-- traffic-json: (\{.*\}) -->", open(p).read())
+    if not m:
+        return None
+    t = json.loads(m.group(1))
+    if t.get("source_sha256_16") != source_digest():
+        return None
+    return t
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# GPU run
+
+def run_bench(args):
     import numpy as np
     import torch
 
@@ -121,9 +186,10 @@ def main():
             clusters |= set((inv[np.nonzero(fin[b])[0]] // shape.vsc).tolist())
         U.append(len(clusters))
     u_mean = float(np.mean(U))
-    step_bytes, parts = algorithmic_bytes(shape, B, inp["len_full"], u_mean)
-    step_bytes_rows, _ = algorithmic_bytes(shape, B, inp["len_full"], B * shape.top_k)
+    lens = [int(x) for x in inp["len_full"]]
+    sbytes, parts = step_bytes(shape, B, lens, u_mean)
 
+    # timed region: graph-replayed draft_block calls on torch's current stream
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -134,12 +200,53 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = wall * 1e3 / args.steps
-    tokens = B * n * args.steps
-    value = tokens / wall
-    avg_launch_s = float(np.mean(launch_ms)) * 1e-3
-    achieved = n * step_bytes / avg_launch_s / 1e9
+    value = B * n * args.steps / wall
+    us_drafter_step = float(np.median(launch_ms)) * 1e3 / n
+
+    # per-kernel durations: the same calls with every launch bracketed by HIP events that the runtime records at
+    # the kernel's start and end (on the library's launch stream, which is torch's current stream)
+    d.timing(True)
+    for _ in range(args.timing_steps):
+        run()
+    torch.cuda.synchronize()
+    d.timing(False)
+    recs = d.timing_records()
+    per_site = {}
+    for name, ms in recs:
+        per_site.setdefault(name, []).append(ms)
+    per_kernel = {}
+    for site, v in per_site.items():
+        k = SITE_KERNEL[site]
+        e = per_kernel.setdefault(k, {"launches": 0, "total_ms": 0.0, "bytes": 0.0, "sites": []})
+        e["launches"] += len(v)
+        e["total_ms"] += float(np.sum(v))
+        e["bytes"] += len(v) * site_bytes(site, shape, B, lens, u_mean)
+        e["sites"].append(site)
+    calls = args.timing_steps
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["total_ms"])
+    dk = per_kernel[dom]
+    avg_launch_s = dk["total_ms"] / dk["launches"] * 1e-3
+    bytes_per_launch = dk["bytes"] / dk["launches"]
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    tr = load_traffic(dom, wl.name)
+    traffic = None if tr is None else tr["hbm_bytes_per_launch"]
+    kernels_table = {k: {"launches_per_drafter_step": v["launches"] / (calls * n),
+                         "avg_launch_us": v["total_ms"] / v["launches"] * 1e3,
+                         "us_per_drafter_step": v["total_ms"] * 1e3 / (calls * n),
+                         "algorithmic_GBs": v["bytes"] / (v["total_ms"] * 1e-3) / 1e9,
+                         "sites": sorted(set(v["sites"]))}
+                     for k, v in sorted(per_kernel.items(), key=lambda kv_: -kv_[1]["total_ms"])}
+
+    if args.copy_probe:
+        # calibration copy of known size for the HBM byte counters (a plain device-to-device copy)
+        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     res = {
         "metric": "draft tokens/sec and µs per drafter step; achieved HBM GB/s vs roofline",
@@ -149,20 +256,139 @@ def main():
         "config": {"workload": wl.name, "batch": B, "context": wl.context, "draft_block": n,
                    "backbone": shape.backbone, "hidden": shape.hidden, "vocab": shape.vocab,
                    "n_centroids": shape.n_centroids, "top_k": shape.top_k, "swa_window": shape.swa_window,
-                   "logits_row_written": True},
-        "us_per_drafter_step": float(np.mean(launch_ms)) * 1e3 / n,
+                   "logits_row_written": True, "graph_replay": True},
+        "us_per_drafter_step": us_drafter_step,
         "us_per_drafter_step_p10_p90": [float(np.percentile(launch_ms, 10)) * 1e3 / n,
                                         float(np.percentile(launch_ms, 90)) * 1e3 / n],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "draft_block launch (all kernels of 4 drafter steps)",
-                     "bytes_per_launch": n * step_bytes, "bytes_per_step_parts": parts,
-                     "distinct_clusters_per_step": U, "bytes_per_launch_per_row_clusters": n * step_bytes_rows,
-                     "avg_launch_us": avg_launch_s * 1e6},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": dom, "launch_sites": sorted(set(dk["sites"])),
+                     "launches_per_drafter_step": dk["launches"] / (calls * n),
+                     "avg_launch_us": avg_launch_s * 1e6, "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "traffic_source": None if tr is None else os.path.relpath(traffic_file(dom, wl.name), ROOT)},
+        "step_roofline": {"algorithmic_bytes_per_drafter_step": sbytes, "parts": parts,
+                          "distinct_clusters_per_step": U,
+                          "achieved_GBs": sbytes / (us_drafter_step * 1e-6) / 1e9,
+                          "frac": sbytes / (us_drafter_step * 1e-6) / 1e9 / HBM_PEAK_GBS},
+        "kernels": kernels_table,
+        "kernel_source_sha256_16": source_digest(),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# host-only summaries of rocprofv3 output
+
+def _find(dirname, suffix):
+    hits = sorted(glob.glob(os.path.join(dirname, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        sys.exit(f"no *{suffix} under {dirname}")
+    return hits[0]
+
+
+def _stem(name):
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("(anonymous namespace)::", "").replace("mtpd::", "")
+    return n.split("(")[0]
+
+
+def summarize_stats(args):
+    path = _find(args.summarize_stats, "kernel_stats.csv")
+    rows = list(csv.DictReader(open(path)))
+    mine = [r for r in rows if "mtpd::" in r["Name"]]
+    lines = [f"# Kernel-trace statistics: drafter kernels, {args.workload}", "",
+             f"Command: `{args.cmd}`", "",
+             f"Kernel source sha256[:16]: `{source_digest()}`", "",
+             "Only the library's kernels are listed (the run also holds the input generator's and torch's own "
+             "kernels, which are outside the timed calls).", "",
+             "| kernel | calls | avg µs | min µs | max µs | total µs | share of library time |", "|---|---|---|---|---|---|---|"]
+    tot = sum(float(r["TotalDurationNs"]) for r in mine)
+    for r in sorted(mine, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_stem(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / tot:.1f}% |")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"drafter_kernels__{args.workload}.stats.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_pmc(args):
+    fetch_dir, write_dir = args.summarize_pmc
+
+    def per_dispatch(dirname, counter):
+        path = _find(dirname, "counter_collection.csv")
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, dirname in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_dispatch(dirname, counter)
+        ker = [v for k, v in vals.items() if _stem(k).startswith(args.kernel)]
+        if not ker:
+            sys.exit(f"no dispatch of {args.kernel} with {counter} in {dirname}")
+        kv = [x for v in ker for x in v]
+        copies = sorted(x for k, v in vals.items() if "copyBuffer" in k or "copy" in _stem(k).lower() for x in v)
+        big = copies[-3:]
+        if not big:
+            sys.exit(f"no copy dispatch with {counter} in {dirname}")
+        copy_kib = sorted(big)[len(big) // 2]
+        factor = (COPY_PROBE_BYTES / 1024.0) / copy_kib  # known bytes over counted KiB of the copy
+        out[counter] = {"kernel_kib_per_dispatch": sum(kv) / len(kv), "dispatches": len(kv),
+                        "copy_kib": copy_kib, "copy_known_kib": COPY_PROBE_BYTES / 1024.0, "factor": factor,
+                        "bytes_per_launch": sum(kv) / len(kv) * 1024.0 * factor}
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    t = {"kernel": args.kernel, "workload": args.workload, "hbm_bytes_per_launch": total,
+         "fetch_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"],
+         "write_bytes_per_launch": out["WRITE_SIZE"]["bytes_per_launch"], "source_sha256_16": source_digest()}
+    lines = [f"# HBM traffic per launch: {args.kernel}, {args.workload}", "",
+             f"Commands: `{args.cmd}`", "",
+             f"Kernel source sha256[:16]: `{source_digest()}`", "",
+             "Each counter is read per dispatch in KiB, averaged over the kernel's dispatches, and scaled by the "
+             f"ratio of known bytes to counted KiB for the calibration copy ({COPY_PROBE_BYTES >> 20} MiB "
+             "device-to-device copy run by the same command).", "",
+             "| counter | kernel KiB / dispatch | dispatches | copy KiB counted | copy KiB known | factor | bytes / launch |",
+             "|---|---|---|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        o = out[c]
+        lines.append(f"| {c} | {o['kernel_kib_per_dispatch']:.1f} | {o['dispatches']} | {o['copy_kib']:.1f} | "
+                     f"{o['copy_known_kib']:.1f} | {o['factor']:.4f} | {o['bytes_per_launch']:.0f} |")
+    lines += ["", f"HBM bytes per launch (fetch + write): {total:.0f}", "", f"<!-- traffic-json: {json.dumps(t)} -->"]
+    os.makedirs(PROFILES, exist_ok=True)
+    p = traffic_file(args.kernel, args.workload)
+    open(p, "w").write("\n".join(lines) + "\n")
+    print(p)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--timing-steps", type=int, default=10, help="calls timed per kernel after the timed region")
+    ap.add_argument("--workload", default="e4b_b16_ctx8192_block4")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="run the counter calibration copy after timing")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--kernel", default="k_attn_mfma")
+    ap.add_argument("--cmd", default="", help="the command that produced the rocprofv3 output (recorded)")
+    args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus above 1 is not supported"}))
+        sys.exit(2)
+    run_bench(args)
 
 
 if __name__ == "__main__":

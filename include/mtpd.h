@@ -47,6 +47,7 @@ enum {
 };
 
 #define MTPD_MAX_BATCH 64 /* rows per call */
+#define MTPD_MAX_TIMED 4096 /* kernel timing records kept per handle */
 
 typedef struct mtpd_handle_s *mtpd_handle;
 
@@ -155,6 +156,20 @@ MTPD_API int mtpd_draft_block(mtpd_handle h, void *stream, void *workspace, int3
 MTPD_API int mtpd_masked_head(mtpd_handle h, void *stream, void *workspace, int32_t m, const float *hidden,
                      float *logits, int32_t *argmax, int32_t *sel_centroids, int32_t *sparse_ids,
                      float *sparse_logits);
+
+/* Kernel timing, a measurement aid outside the method. While enabled on a handle, drafter_step, draft_block and
+ * masked_head launch their kernels directly on the caller's stream (captured graphs are not replayed) and attach
+ * to each launch a pair of HIP events that the runtime records at the kernel's start and end. Enabling clears
+ * the records; disabling keeps them for reading; at most MTPD_MAX_TIMED launches are recorded, later ones are not.
+ * Not thread-safe per handle. Returns MTPD_OK or MTPD_EINVAL. */
+MTPD_API int mtpd_timing_enable(mtpd_handle h, int32_t enable);
+
+/* Waits for the recorded events and copies min(cap, count) records in launch order: names[i] is a static label of
+ * the launch site ("pre", "qproj", "attn_sliding", "attn_full", "attn_merge_sliding", "attn_merge_full",
+ * "o_proj", "ffn", "down", "post", "head", "final", "scores", "fill"), ms[i] its duration in milliseconds.
+ * names and ms are caller-owned host arrays of cap entries. Returns the number of records (which may exceed cap)
+ * or a negative error code. */
+MTPD_API int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char **names, float *ms);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 MTPD_API const char *mtpd_last_error(void);

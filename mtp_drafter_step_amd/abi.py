@@ -14,8 +14,9 @@ LIB_PATH = os.path.join(_HERE, "libmtpd.so")
 
 MTPD_OK, MTPD_EINVAL, MTPD_ESHAPE, MTPD_ENOMEM, MTPD_EHIP, MTPD_EUNSUP = 0, -1, -2, -3, -4, -5
 MTPD_MAX_BATCH = 64
+MTPD_MAX_TIMED = 4096
 SYMBOLS = ("mtpd_create", "mtpd_destroy", "mtpd_workspace_bytes", "mtpd_drafter_step", "mtpd_draft_block",
-           "mtpd_masked_head", "mtpd_last_error", "mtpd_abi_version")
+           "mtpd_masked_head", "mtpd_last_error", "mtpd_abi_version", "mtpd_timing_enable", "mtpd_timing_read")
 
 u16p = C.POINTER(C.c_uint16)
 i32p = C.POINTER(C.c_int32)
@@ -81,6 +82,10 @@ def lib() -> C.CDLL:
     L.mtpd_last_error.restype = C.c_char_p
     L.mtpd_abi_version.argtypes = []
     L.mtpd_abi_version.restype = C.c_int32
+    L.mtpd_timing_enable.argtypes = [vp, C.c_int32]
+    L.mtpd_timing_enable.restype = C.c_int
+    L.mtpd_timing_read.argtypes = [vp, C.c_int32, C.POINTER(C.c_char_p), f32p]
+    L.mtpd_timing_read.restype = C.c_int32
     _lib = L
     return L
 

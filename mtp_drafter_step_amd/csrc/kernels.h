@@ -48,6 +48,10 @@ struct TokenSource {
   int32_t* next;
 };
 
+// Attach a pair of timing events to the next kernel launched by this thread through one of the launchers below
+// (start recorded when the kernel begins, stop when it ends); the pair is consumed by that launch. Null clears.
+void set_next_launch_events(hipEvent_t start, hipEvent_t stop);
+
 // x[b] = W_pre [target_hidden[b] ; escale * target_embd[tok[b]]]
 hipError_t launch_pre(hipStream_t s, int B, int Bb, int H, int V, const uint16_t* th, TokenSource ts,
                       const uint16_t* emb, float escale, const uint16_t* w_pre, float* x);

@@ -19,6 +19,8 @@
 // transpose-reduction leaves one finished (row, output) sum per lane group.
 #include "kernels.h"
 
+#include <hip/hip_ext.h>
+
 #include <math.h>
 #include <stdlib.h>
 
@@ -1029,29 +1031,49 @@ bool getenv_no_mfma() {
   return v != 0;
 }
 
+// Timing events for the next launch only (see set_next_launch_events).
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+// Launch `k` on `s`; when timing events are pending they are attached to this launch (recorded by the runtime at
+// the kernel's start and end) and consumed.
+template <typename... P, typename... A>
+hipError_t go(void (*k)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t s, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  if (t_ev_start || t_ev_stop) {
+    hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    hipExtLaunchKernelGGL(k, grid, block, (uint32_t)shmem, s, e0, e1, 0u, static_cast<P>(a)...);
+  } else {
+    k<<<grid, block, shmem, s>>>(static_cast<P>(a)...);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------------------
 // launchers
 
+void set_next_launch_events(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
+}
+
 hipError_t launch_pre(hipStream_t s, int B, int Bb, int H, int V, const uint16_t* th, TokenSource ts,
                       const uint16_t* emb, float escale, const uint16_t* w_pre, float* x) {
   dim3 grid((H + 3) / 4, row_groups(B));
-  k_pre<<<grid, 256, 0, s>>>(B, Bb, H, V, th, ts, emb, escale, w_pre, x);
-  return hipGetLastError();
+  return go(k_pre, grid, 256, 0, s, B, Bb, H, V, th, ts, emb, escale, w_pre, x);
 }
 
 hipError_t launch_qproj(hipStream_t s, int B, int H, int QD, Residual res, const uint16_t* w_norm, float eps,
                         const uint16_t* w_q, float* q) {
   dim3 grid((QD + 15) / 16, row_groups(B));
-  k_qproj<<<grid, 256, kRG * H * sizeof(float), s>>>(B, H, QD, res, w_norm, eps, w_q, q);
-  return hipGetLastError();
+  return go(k_qproj, grid, 256, kRG * H * sizeof(float), s, B, H, QD, res, w_norm, eps, w_q, q);
 }
 
 hipError_t launch_dense(hipStream_t s, int B, int K, int N, const float* X, const uint16_t* w, float* y) {
   dim3 grid((N + 3) / 4, row_groups(B));
-  k_dense<<<grid, 256, 0, s>>>(B, K, N, X, w, y);
-  return hipGetLastError();
+  return go(k_dense, grid, 256, 0, s, B, K, N, X, w, y);
 }
 
 hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, const uint16_t* w_cen, float* scores) {
@@ -1061,17 +1083,15 @@ hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, con
 hipError_t launch_ffn(hipStream_t s, int B, int H, int F, Residual res, const uint16_t* w_norm, float eps,
                       const uint16_t* w_gate, const uint16_t* w_up, float* m, FillRange fill) {
   dim3 grid((F + 15) / 16, row_groups(B));
-  k_ffn<<<grid, 256, kRG * H * sizeof(float), s>>>(B, H, F, res, w_norm, eps, w_gate, w_up, m, fill);
-  return hipGetLastError();
+  return go(k_ffn, grid, 256, kRG * H * sizeof(float), s, B, H, F, res, w_norm, eps, w_gate, w_up, m, fill);
 }
 
 hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res, const uint16_t* w_out, float eps,
                        const uint16_t* w_post, const uint16_t* w_cen, float* h_out, uint16_t* hidden_out,
                        float* scores) {
   dim3 grid((Bb + C + 15) / 16, row_groups(B));
-  k_post<<<grid, 256, kRG * H * sizeof(float), s>>>(B, H, Bb, C, res, w_out, eps, w_post, w_cen, h_out, hidden_out,
+  return go(k_post, grid, 256, kRG * H * sizeof(float), s, B, H, Bb, C, res, w_out, eps, w_post, w_cen, h_out, hidden_out,
                                                      scores);
-  return hipGetLastError();
 }
 
 hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
@@ -1081,16 +1101,14 @@ hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const floa
   const float sl2 = scale * 1.4426950408889634f;
   const int G = nh / nkv;
   if (hd == 256 && G <= 4 && !getenv_no_mfma()) {
-    if (G == 4) k_attn_mfma<4, 4><<<grid, 256, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
-    else if (G == 2) k_attn_mfma<2, 4><<<grid, 256, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
-    else k_attn_mfma<1, 4><<<grid, 256, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
-    return hipGetLastError();
+    if (G == 4) return go(k_attn_mfma<4, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
+    if (G == 2) return go(k_attn_mfma<2, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
+    return go(k_attn_mfma<1, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
   }
 #define MTPD_ATTN(HD_, G_, NW_)                                                                             \
   if (hd == HD_ && G == G_) {                                                                               \
-    k_attn<HD_, G_, NW_><<<grid, NW_ * 64, 0, s>>>(B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win,  \
-                                                    nsplit, sl2, pacc, pml, o);                             \
-    return hipGetLastError();                                                                               \
+    return go(k_attn<HD_, G_, NW_>, grid, NW_ * 64, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, \
+              win, nsplit, sl2, pacc, pml, o);                                                              \
   }
   if (nsplit == 1) {
     MTPD_ATTN(256, 1, 8) MTPD_ATTN(256, 2, 8) MTPD_ATTN(256, 4, 8) MTPD_ATTN(256, 8, 4)
@@ -1107,22 +1125,19 @@ hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const floa
 
 hipError_t launch_attn_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
                              float* o) {
-  k_attn_merge<<<B * nh, 256, 0, s>>>(hd, nsplit, pacc, pml, o);
-  return hipGetLastError();
+  return go(k_attn_merge, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
 }
 
 hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,
                        const int32_t* ordering, const uint16_t* E, const float* h, int32_t* sel, int32_t* ids,
                        float* z, float* logits, size_t V, uint64_t* keys) {
   dim3 grid(k, B);
-  k_head<<<grid, 256, 0, s>>>(C, k, vsc, H, scores, ordering, E, h, sel, ids, z, logits, V, keys);
-  return hipGetLastError();
+  return go(k_head, grid, 256, 0, s, C, k, vsc, H, scores, ordering, E, h, sel, ids, z, logits, V, keys);
 }
 
 hipError_t launch_final(hipStream_t s, int B, int k, const uint64_t* keys, int32_t* next, int32_t* out2,
                         int stride2) {
-  k_final<<<B, 64, 0, s>>>(k, keys, next, out2, stride2);
-  return hipGetLastError();
+  return go(k_final, B, 64, 0, s, k, keys, next, out2, stride2);
 }
 
 hipError_t launch_fill(hipStream_t s, float* logits, size_t n) {
@@ -1131,8 +1146,7 @@ hipError_t launch_fill(hipStream_t s, float* logits, size_t n) {
   size_t grid = (n4 + 255) / 256;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
-  k_fill<<<(unsigned)grid, 256, 0, s>>>(reinterpret_cast<float4*>(logits), n4, logits + n4 * 4, ntail);
-  return hipGetLastError();
+  return go(k_fill, (unsigned)grid, 256, 0, s, reinterpret_cast<float4*>(logits), n4, logits + n4 * 4, ntail);
 }
 
 }  // namespace mtpd

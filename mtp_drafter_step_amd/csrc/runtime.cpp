@@ -76,6 +76,11 @@ struct mtpd_handle_s {
   hipStream_t chain_stream[kChains] = {};
   hipEvent_t fork_ev = nullptr;
   hipEvent_t join_ev[kChains] = {};
+  // kernel timing: while `timing` is set every launch takes the next event pair and records its site label
+  mutable bool timing = false;
+  mutable int32_t n_timed = 0;
+  mutable std::vector<hipEvent_t> timing_ev;  // 2 per record, created on first use
+  mutable std::vector<const char*> timing_name;
 };
 
 namespace {
@@ -169,6 +174,34 @@ int check_ptr(const void* p, const char* name) {
     if (e_ != hipSuccess) return fail(MTPD_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
+// Take the next timing record for a launch labelled `name` (no-op unless timing is on; launches beyond
+// MTPD_MAX_TIMED records are not recorded).
+int timing_mark(const mtpd_handle_s* h, const char* name) {
+  if (!h->timing || h->n_timed >= MTPD_MAX_TIMED) return MTPD_OK;
+  const size_t i = (size_t)h->n_timed;
+  if (h->timing_ev.size() < 2 * (i + 1)) {
+    for (int j = 0; j < 2; ++j) {
+      hipEvent_t e = nullptr;
+      LAUNCH(hipEventCreate(&e));
+      h->timing_ev.push_back(e);
+    }
+    h->timing_name.push_back(nullptr);
+  }
+  h->timing_name[i] = name;
+  mtpd::set_next_launch_events(h->timing_ev[2 * i], h->timing_ev[2 * i + 1]);
+  ++h->n_timed;
+  return MTPD_OK;
+}
+
+// A kernel launch labelled for the timing records.
+#define KLAUNCH(h, name, expr)                                                                \
+  do {                                                                                        \
+    CHECK(timing_mark((h), (name)));                                                          \
+    hipError_t e_ = (expr);                                                                   \
+    mtpd::set_next_launch_events(nullptr, nullptr);                                           \
+    if (e_ != hipSuccess) return fail(MTPD_EHIP, "%s: %s", #expr, hipGetErrorString(e_));   \
+  } while (0)
+
 int check_kv(const mtpd_handle_s* h, const mtpd_kv& kv, int B, const char* name, mtpd::RowWindows* win, bool full) {
   char nm[64];
   snprintf(nm, sizeof(nm), "%s.k", name);
@@ -211,7 +244,7 @@ int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
              float* logits, int32_t* sel_out, int32_t* ids_out, float* z_out) {
   const mtpd_config& c = h->cfg;
   // [Inventory] "Centroid / ordered embeddings LM head", steps 2-5
-  LAUNCH(mtpd::launch_head(s, B, c.n_centroids, c.top_k, h->vsc, c.hidden, at<float>(ws, p.scores),
+  KLAUNCH(h, "head", mtpd::launch_head(s, B, c.n_centroids, c.top_k, h->vsc, c.hidden, at<float>(ws, p.scores),
                            h->w.token_ordering, h->w.token_embd, hsrc, sel_out, ids_out, z_out, logits,
                            (size_t)c.vocab, at<uint64_t>(ws, p.keys)));
   return MTPD_OK;
@@ -232,7 +265,7 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
   float* m = at<float>(ws, p.m);
   float* d = at<float>(ws, p.d);
   // input assembly + pre_projection ([MTP doc] "What it is"; [Guide] section 2(3))
-  LAUNCH(mtpd::launch_pre(s, B, Bb, H, c.vocab, th, ts, temb, c.embed_scale, h->w.pre_proj, x[0]));
+  KLAUNCH(h, "pre", mtpd::launch_pre(s, B, Bb, H, c.vocab, th, ts, temb, c.embed_scale, h->w.pre_proj, x[0]));
   int cur = 0;
   const size_t BV = (size_t)B * c.vocab;
   for (int l = 0; l < nL; ++l) {
@@ -245,26 +278,26 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
       rq = mtpd::Residual{x[cur], d, P.post_ffw_norm, P.layer_output_scale, x[cur ^ 1]};
       cur ^= 1;
     }
-    LAUNCH(mtpd::launch_qproj(s, B, H, QD, rq, L.attn_norm, c.rms_eps, L.attn_q, q));
-    LAUNCH(mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
+    KLAUNCH(h, "qproj", mtpd::launch_qproj(s, B, H, QD, rq, L.attn_norm, c.rms_eps, L.attn_q, q));
+    KLAUNCH(h, type ? "attn_full" : "attn_sliding", mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
                              cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale,
                              at<float>(ws, p.pacc), at<float>(ws, p.pml), o));
     if (nsplit[type] > 1)
-      LAUNCH(mtpd::launch_attn_merge(s, B, c.n_head, c.head_dim, nsplit[type], at<float>(ws, p.pacc),
+      KLAUNCH(h, type ? "attn_merge_full" : "attn_merge_sliding", mtpd::launch_attn_merge(s, B, c.n_head, c.head_dim, nsplit[type], at<float>(ws, p.pacc),
                                      at<float>(ws, p.pml), o));
-    LAUNCH(mtpd::launch_dense(s, B, QD, H, o, L.attn_output, t));
+    KLAUNCH(h, "o_proj", mtpd::launch_dense(s, B, QD, H, o, L.attn_output, t));
     mtpd::Residual rf{x[cur], t, L.post_attention_norm, 1.0f, x[cur ^ 1]};
     cur ^= 1;
     mtpd::FillRange fr{nullptr, 0, 0};
     if (logits)
       fr = mtpd::FillRange{logits, (BV * l / nL) & ~size_t(3), l + 1 == nL ? BV : (BV * (l + 1) / nL) & ~size_t(3)};
-    LAUNCH(mtpd::launch_ffn(s, B, H, F, rf, L.ffn_norm, c.rms_eps, L.ffn_gate, L.ffn_up, m, fr));
-    LAUNCH(mtpd::launch_dense(s, B, F, H, m, L.ffn_down, d));
+    KLAUNCH(h, "ffn", mtpd::launch_ffn(s, B, H, F, rf, L.ffn_norm, c.rms_eps, L.ffn_gate, L.ffn_up, m, fr));
+    KLAUNCH(h, "down", mtpd::launch_dense(s, B, F, H, m, L.ffn_down, d));
   }
   const mtpd_layer& Last = h->layers[nL - 1];
   mtpd::Residual rp{x[cur], d, Last.post_ffw_norm, Last.layer_output_scale, nullptr};
   // output norm, post_projection (the next step's hidden input, [Guide] section 6) and centroid scores
-  LAUNCH(mtpd::launch_post(s, B, H, Bb, c.n_centroids, rp, h->w.output_norm, c.rms_eps, h->w.post_proj,
+  KLAUNCH(h, "post", mtpd::launch_post(s, B, H, Bb, c.n_centroids, rp, h->w.output_norm, c.rms_eps, h->w.post_proj,
                            h->w.centroids, at<float>(ws, p.h), hidden_out, at<float>(ws, p.scores)));
   return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, sel_out, ids_out, z_out);
 }
@@ -409,7 +442,7 @@ template <typename Body>
 int run_call(mtpd_handle_s* h, hipStream_t s, const CallKey& key, const Chains& ch, Body body) {
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &st) != hipSuccess) st = hipStreamCaptureStatusActive;
-  if (!h->use_graphs || st != hipStreamCaptureStatusNone) return run_chains(h, s, ch, body);
+  if (!h->use_graphs || h->timing || st != hipStreamCaptureStatusNone) return run_chains(h, s, ch, body);
   hipGraphExec_t exec[kChains];
   for (int c = 0; c < ch.n; ++c) CHECK(chain_graph(h, key, c, body, &exec[c]));
   if (ch.n == 1) {
@@ -514,6 +547,7 @@ void mtpd_destroy(mtpd_handle h) {
     if (h->join_ev[c]) (void)hipEventDestroy(h->join_ev[c]);
   }
   if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
+  for (hipEvent_t e : h->timing_ev) (void)hipEventDestroy(e);
   delete h;
 }
 
@@ -553,7 +587,7 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
                      v.nsplit, logits ? logits + (size_t)b0 * c.vocab : nullptr,
                      hidden_out + (size_t)b0 * c.backbone, sel_centroids ? sel_centroids + (size_t)b0 * c.top_k : nullptr,
                      sparse_ids ? sparse_ids + b0 * kv_n : nullptr, sparse_logits ? sparse_logits + b0 * kv_n : nullptr));
-      LAUNCH(mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), next_token + b0, nullptr, 0));
+      KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), next_token + b0, nullptr, 0));
       return MTPD_OK;
   });
 }
@@ -595,7 +629,7 @@ int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch
                        logits ? logits + (size_t)i * BV + (size_t)b0 * c.vocab : nullptr, hout, nullptr, nullptr,
                        nullptr));
       }
-      LAUNCH(mtpd::launch_final(cs, Bc, c.top_k, keys, at<int32_t>(wsc, p.tok), tok_c + (n - 1), n));
+      KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, c.top_k, keys, at<int32_t>(wsc, p.tok), tok_c + (n - 1), n));
       return MTPD_OK;
   });
 }
@@ -619,13 +653,36 @@ int mtpd_masked_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
       const float* hc = hidden + (size_t)b0 * c.hidden;
       float* lc = logits ? logits + (size_t)b0 * c.vocab : nullptr;
       // [Inventory] "Centroid / ordered embeddings LM head", step 1: centroid logits
-      LAUNCH(mtpd::launch_scores(cs, Bc, c.hidden, c.n_centroids, hc, h->w.centroids, at<float>(wsc, p.scores)));
-      if (lc) LAUNCH(mtpd::launch_fill(cs, lc, (size_t)Bc * c.vocab));
+      KLAUNCH(h, "scores", mtpd::launch_scores(cs, Bc, c.hidden, c.n_centroids, hc, h->w.centroids, at<float>(wsc, p.scores)));
+      if (lc) KLAUNCH(h, "fill", mtpd::launch_fill(cs, lc, (size_t)Bc * c.vocab));
       CHECK(run_head(h, cs, wsc, p, Bc, hc, lc, sel_centroids ? sel_centroids + (size_t)b0 * c.top_k : nullptr,
                      sparse_ids ? sparse_ids + b0 * kv_n : nullptr, sparse_logits ? sparse_logits + b0 * kv_n : nullptr));
-      LAUNCH(mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), argmax + b0, nullptr, 0));
+      KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), argmax + b0, nullptr, 0));
       return MTPD_OK;
   });
+}
+
+int mtpd_timing_enable(mtpd_handle h, int32_t enable) {
+  g_last_error.clear();
+  if (!h) return fail(MTPD_EINVAL, "handle is NULL");
+  if (enable) h->n_timed = 0;
+  h->timing = enable != 0;
+  return MTPD_OK;
+}
+
+int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char** names, float* ms) {
+  g_last_error.clear();
+  if (!h) return fail(MTPD_EINVAL, "handle is NULL");
+  if (cap < 0 || (cap > 0 && (!names || !ms))) return fail(MTPD_EINVAL, "names/ms are NULL or cap < 0");
+  const int32_t n = std::min(cap, h->n_timed);
+  for (int32_t i = 0; i < n; ++i) {
+    LAUNCH(hipEventSynchronize(h->timing_ev[2 * (size_t)i + 1]));
+    float t = 0.f;
+    LAUNCH(hipEventElapsedTime(&t, h->timing_ev[2 * (size_t)i], h->timing_ev[2 * (size_t)i + 1]));
+    names[i] = h->timing_name[(size_t)i];
+    ms[i] = t;
+  }
+  return h->n_timed;
 }
 
 }  // extern "C"

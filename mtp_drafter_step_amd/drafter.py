@@ -6,7 +6,7 @@ torch is used for device memory and streams only; all arithmetic runs in libmtpd
 from __future__ import annotations
 
 import ctypes as C
-from typing import Dict, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
@@ -87,6 +87,21 @@ class Drafter:
             self.close()
         except Exception:
             pass
+
+    def timing(self, enable: bool) -> None:
+        """Switch per-kernel timing records on (clearing them) or off (keeping them for timing_records)."""
+        abi.check(abi.lib().mtpd_timing_enable(self.handle, 1 if enable else 0))
+
+    def timing_records(self) -> List[Tuple[str, float]]:
+        """(launch-site label, duration in ms) of every launch recorded since timing was switched on."""
+        L = abi.lib()
+        cap = abi.MTPD_MAX_TIMED
+        names = (C.c_char_p * cap)()
+        ms = (C.c_float * cap)()
+        n = int(L.mtpd_timing_read(self.handle, cap, names, ms))
+        if n < 0:
+            abi.check(n)
+        return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
 
     def workspace_bytes(self, batch: int) -> int:
         return int(abi.lib().mtpd_workspace_bytes(self.handle, int(batch)))

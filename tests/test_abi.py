@@ -115,3 +115,12 @@ def test_calls_reject_null_handle():
     rc = L.mtpd_masked_head(None, None, None, 1, None, None, None, None, None, None)
     assert rc == abi.MTPD_EINVAL
     L.mtpd_destroy(None)
+
+
+def test_timing_calls_reject_null_handle():
+    import ctypes as C
+    L = abi.lib()
+    assert L.mtpd_timing_enable(None, 1) == abi.MTPD_EINVAL
+    names = (C.c_char_p * 4)()
+    ms = (C.c_float * 4)()
+    assert L.mtpd_timing_read(None, 4, names, ms) == abi.MTPD_EINVAL

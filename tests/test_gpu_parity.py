@@ -183,3 +183,29 @@ def test_graph_replays_match_direct_launches():
         other = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_sparse=True)
         torch.cuda.synchronize()
         assert other["next"].shape[0] == 4
+
+
+def test_kernel_timing_records_every_launch_and_keeps_results():
+    """Timing records: one per kernel launch of the call, in launch order, with positive durations; the results
+    equal those of the graph-replayed call."""
+    case = Case(synth.E4B, batch=4, context=1200, ragged=True)
+    d = case.drafter
+    ref = d.draft_block(2, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    ref = {k: v.clone() for k, v in ref.items()}
+    d.timing(True)
+    out = d.draft_block(2, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    torch.cuda.synchronize()
+    d.timing(False)
+    recs = d.timing_records()
+    for k in ref:
+        assert torch.equal(out[k], ref[k]), k
+    names = [r[0] for r in recs]
+    L = case.shape.n_layer
+    per_step = ["pre"] + ["qproj", "attn", "o_proj", "ffn", "down"] * L + ["post", "head"]
+    got = [("attn" if n.startswith("attn_") and "merge" not in n else n) for n in names if "merge" not in n]
+    assert got == per_step * 2 + ["final"], names
+    assert all(ms > 0.0 for _, ms in recs)
+    # after switching off, calls replay graphs again and add no records
+    d.draft_block(2, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    torch.cuda.synchronize()
+    assert len(d.timing_records()) == len(recs)
