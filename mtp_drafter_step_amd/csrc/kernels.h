@@ -37,11 +37,13 @@ struct FillRange {
   size_t begin, end;
 };
 
-// Token input of a step: either ids (tok[b]) or the previous step's per-cluster argmax keys (keys[b][k]), whose
-// maximum decides the token; in that case block column 0 also records it to out[b*out_stride] and next[b].
+// Token input of a step: either ids (tok[b]) or, when use_keys is set, the previous step's per-cluster argmax keys
+// (keys[b][k]), whose maximum decides the token; in that case block column 0 also records it to out[b*out_stride]
+// and next[b]. tok and keys must both be valid device pointers ([B] and [B][k]) whichever is used: both are read.
 struct TokenSource {
   const int32_t* tok;
   const uint64_t* keys;
+  int use_keys;
   int k;
   int32_t* out;
   int out_stride;

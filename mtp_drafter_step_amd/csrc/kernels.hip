@@ -31,8 +31,6 @@ namespace mtpd {
 namespace {
 
 constexpr int kRG = kRowGroup;
-constexpr int kMaxPL = 16;   // fp32 row elements per lane in the norm prologue (H <= 1024)
-constexpr int kMaxIt = 16;   // 256-wide reduction chunks per dense product (K <= 4096)
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -120,212 +118,235 @@ __device__ __forceinline__ void unpack8(uint4 w, float* f) {
 
 // ------------------------------------------------------------------------------------------------------------
 // dense building blocks
+//
+// Every trip count below is a template parameter, and every load a wave needs is issued before any loaded value is
+// used: a load inside a data-dependent branch, or inside a loop whose bound the compiler cannot see, is followed by
+// its own wait, which turns one memory round trip into one per element.
 
-// Weights of OPW consecutive output rows for one wave, 4 bf16 per lane per 256-wide chunk of K (K % 256 == 0).
-template <int OPW>
+// Weights of OPW consecutive output rows for one wave: IT chunks of 256 along K, 4 bf16 per lane per chunk.
+template <int OPW, int IT>
 struct WaveW {
-  uint2 w[OPW][kMaxIt];
+  uint2 w[OPW][IT];
   __device__ __forceinline__ void load(const uint16_t* W, int K, int n0, int N) {
     const int lane = lane_id();
-    const int it = K >> 8;
 #pragma unroll
     for (int o = 0; o < OPW; ++o) {
-      const int n = min(n0 + o, N - 1);
-      const uint16_t* row = W + (size_t)n * K + lane * 4;
+      const uint16_t* row = W + (size_t)min(n0 + o, N - 1) * K + lane * 4;
 #pragma unroll
-      for (int i = 0; i < kMaxIt; ++i)
-        if (i < it) w[o][i] = *reinterpret_cast<const uint2*>(row + i * 256);
+      for (int i = 0; i < IT; ++i) w[o][i] = *reinterpret_cast<const uint2*>(row + i * 256);
     }
   }
-  // acc[r*OPW + o] = sum_k X(r, k) W[n0+o][k], X rows fp32 (global or LDS) at xrow[r]; transpose-reduced.
-  __device__ __forceinline__ void dot(const float* const* xrow, int K, float* acc) const {
+  // acc[r*OPW + o] = sum_k X(r, k) W[n0+o][k] for the kRG rows at xrow[r] (fp32, LDS or global); afterwards lane l
+  // holds the finished sum of (row, output) index l >> (6 - log2(kRG*OPW)) in acc[0] (transpose-reduction).
+  __device__ __forceinline__ void dot(const float* const* xrow, float* acc) const {
     const int lane = lane_id();
-    const int it = K >> 8;
+    float4 xr[kRG][IT];
+#pragma unroll
+    for (int r = 0; r < kRG; ++r)
+#pragma unroll
+      for (int i = 0; i < IT; ++i) xr[r][i] = *reinterpret_cast<const float4*>(xrow[r] + i * 256 + lane * 4);
 #pragma unroll
     for (int i = 0; i < kRG * OPW; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxIt; ++i) {
-      if (i < it) {
-        float xr[kRG][4];
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+      for (int o = 0; o < OPW; ++o) {
+        float wf[4];
+        unpack4(w[o][i], wf);
 #pragma unroll
         for (int r = 0; r < kRG; ++r) {
-          const float4 a = *reinterpret_cast<const float4*>(xrow[r] + i * 256 + lane * 4);
-          xr[r][0] = a.x; xr[r][1] = a.y; xr[r][2] = a.z; xr[r][3] = a.w;
-        }
-#pragma unroll
-        for (int o = 0; o < OPW; ++o) {
-          float wf[4];
-          unpack4(w[o][i], wf);
-#pragma unroll
-          for (int r = 0; r < kRG; ++r) {
-            float s = acc[r * OPW + o];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s = fmaf(xr[r][e], wf[e], s);
-            acc[r * OPW + o] = s;
-          }
+          float s = acc[r * OPW + o];
+          s = fmaf(xr[r][i].x, wf[0], s);
+          s = fmaf(xr[r][i].y, wf[1], s);
+          s = fmaf(xr[r][i].z, wf[2], s);
+          s = fmaf(xr[r][i].w, wf[3], s);
+          acc[r * OPW + o] = s;
         }
       }
-    }
     XR<kRG * OPW, 32>::run(acc, lane);
   }
 };
 
-// Residual update + RMSNorm for the block's row group into LDS xs[kRG][H]; one wave per row (H % 64 == 0,
-// H <= 1024). Rows beyond B are zero. Block column 0 stores x_new when res.x_new is set.
-__device__ void prologue_norm(const Residual& res, const uint16_t* w_norm, float eps, int B, int H, float* xs) {
+// Residual update + RMSNorm for the block's row group into LDS xs[kRG][H] (H = 64 NPL); one wave per row. Rows
+// beyond B are zero. Block column 0 stores x_new when res.x_new is set. Branch-free: the delta loads are always
+// issued (from x_old when there is no delta) and their effect selected afterwards.
+template <int NPL>
+__device__ __forceinline__ void prologue_norm(const Residual& res, const uint16_t* w_norm, float eps, int B,
+                                              float* xs) {
+  constexpr int H = NPL * 64;
   const int wave = wave_id(), lane = lane_id();
   const int row = blockIdx.y * kRG + wave;
-  float* xr = xs + wave * H;
-  const int npl = H >> 6;
-  if (row >= B) {
+  const int rr = min(row, B - 1);
+  const bool hasd = res.delta != nullptr;
+  const float* xo = res.x_old + (size_t)rr * H;
+  const float* dr = hasd ? res.delta + (size_t)rr * H : xo;
+  const uint16_t* wdp = hasd ? res.w_delta : w_norm;
+  float xv[NPL], dv[NPL];
+  uint16_t wv[NPL], wd[NPL];
 #pragma unroll
-    for (int j = 0; j < kMaxPL; ++j)
-      if (j < npl) xr[lane + 64 * j] = 0.f;
-    return;
+  for (int j = 0; j < NPL; ++j) {
+    xv[j] = xo[lane + 64 * j];
+    dv[j] = dr[lane + 64 * j];
+    wv[j] = w_norm[lane + 64 * j];
+    wd[j] = wdp[lane + 64 * j];
   }
-  float xv[kMaxPL], wv[kMaxPL];
-  const float* xo = res.x_old + (size_t)row * H;
+  float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxPL; ++j)
-    if (j < npl) {
-      xv[j] = xo[lane + 64 * j];
-      wv[j] = bf2f(w_norm[lane + 64 * j]);
-    }
-  if (res.delta) {
-    float dv[kMaxPL], wd[kMaxPL];
-    const float* dr = res.delta + (size_t)row * H;
-    float ss = 0.f;
+  for (int j = 0; j < NPL; ++j) ss = fmaf(dv[j], dv[j], ss);
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
-    for (int j = 0; j < kMaxPL; ++j)
-      if (j < npl) {
-        dv[j] = dr[lane + 64 * j];
-        wd[j] = bf2f(res.w_delta[lane + 64 * j]);
-        ss = fmaf(dv[j], dv[j], ss);
-      }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)H + eps);
-#pragma unroll
-    for (int j = 0; j < kMaxPL; ++j)
-      if (j < npl) xv[j] = (xv[j] + dv[j] * r * wd[j]) * res.scale;
-  }
+  for (int j = 0; j < NPL; ++j) xv[j] = hasd ? (xv[j] + dv[j] * r * bf2f(wd[j])) * res.scale : xv[j];
   float s2 = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxPL; ++j)
-    if (j < npl) s2 = fmaf(xv[j], xv[j], s2);
+  for (int j = 0; j < NPL; ++j) s2 = fmaf(xv[j], xv[j], s2);
   s2 = wave_sum(s2);
   const float r2 = 1.0f / sqrtf(s2 / (float)H + eps);
-  const bool store = res.x_new && blockIdx.x == 0;
+  const bool valid = row < B;
+  if (res.x_new && blockIdx.x == 0 && valid) {
 #pragma unroll
-  for (int j = 0; j < kMaxPL; ++j)
-    if (j < npl) {
-      if (store) res.x_new[(size_t)row * H + lane + 64 * j] = xv[j];
-      xr[lane + 64 * j] = xv[j] * r2 * wv[j];
-    }
+    for (int j = 0; j < NPL; ++j) res.x_new[(size_t)row * H + lane + 64 * j] = xv[j];
+  }
+  float* xr = xs + wave * H;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) xr[lane + 64 * j] = valid ? xv[j] * r2 * bf2f(wv[j]) : 0.f;
 }
 
 // ------------------------------------------------------------------------------------------------------------
 // pre_projection of [target hidden ; embedded token]  ([MTP doc] "What it is": 2x backbone input;
-// [Guide] section 2(3)). grid (H / 4, ceil(B / 4)); each wave one output for the 4 rows, 8 bf16 per lane per
-// 512-wide chunk of K = 2 Bb (Bb % 256 == 0).
+// [Guide] section 2(3)). grid (ceil(H / 4), ceil(B / 4)), NWV waves. A block computes 4 outputs for 4 rows; its waves
+// split K = 2 Bb into 256-wide chunks (CPW per wave; a chunk lies wholly in the hidden half or the embedding half,
+// since Bb % 256 == 0), and the partial sums meet in LDS. Weight and hidden loads are issued before the token is
+// known; the embedding rows right after.
 
-__global__ __launch_bounds__(256) void k_pre(int B, int Bb, int H, int V, const uint16_t* __restrict__ th,
-                                             TokenSource ts, const uint16_t* __restrict__ emb, float escale,
-                                             const uint16_t* __restrict__ W, float* __restrict__ x) {
+template <int NWV, int CPW>
+__global__ __launch_bounds__(NWV * 64) void k_pre(int B, int Bb, int H, int V, const uint16_t* __restrict__ th,
+                                                  TokenSource ts, const uint16_t* __restrict__ emb, float escale,
+                                                  const uint16_t* __restrict__ W, float* __restrict__ x) {
   __shared__ int tok_s[kRG];
+  __shared__ float red[NWV][16];
   const int wave = wave_id(), lane = lane_id();
   const int r0 = blockIdx.y * kRG;
-  // token of this wave's row
-  {
-    const int b = min(r0 + wave, B - 1);
-    int t;
-    if (ts.keys) {
-      const uint64_t kv = (lane < ts.k) ? ts.keys[(size_t)b * ts.k + min(lane, ts.k - 1)] : 0ull;
-      t = key_id(wave_max_u64(kv));
+  const int n0 = blockIdx.x * 4;
+  const int K = 2 * Bb;
+  const int nch = K >> 8, hch = Bb >> 8;  // chunks in total / in the hidden half
+  // the token source of row r0 + wave is requested first (waves beyond kRG repeat row r0), then the weights and
+  // hidden-half activations, which do not depend on it
+  const int bt = min(r0 + min(wave, kRG - 1), B - 1);
+  const uint64_t kraw = ts.keys[(size_t)bt * ts.k + min(lane, ts.k - 1)];
+  const int traw = ts.tok[bt];
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight loads (waits count in issue order)
+  uint2 wr[CPW][4], xr[CPW][kRG];
+  int cidx[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    cidx[c] = min(wave * CPW + c, nch - 1);
+    const int k = cidx[c] * 256 + lane * 4;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) wr[c][o] = *reinterpret_cast<const uint2*>(W + (size_t)min(n0 + o, H - 1) * K + k);
+#pragma unroll
+    for (int r = 0; r < kRG; ++r)
+      xr[c][r] = *reinterpret_cast<const uint2*>(th + (size_t)min(r0 + r, B - 1) * Bb + min(k, Bb - 4));
+  }
+  if (wave < kRG) {
+    int t = traw;
+    if (ts.use_keys) {
+      t = key_id(wave_max_u64(lane < ts.k ? kraw : 0ull));
       if (blockIdx.x == 0 && lane == 0 && r0 + wave < B) {
-        if (ts.out) ts.out[(size_t)b * ts.out_stride] = t;
-        if (ts.next) ts.next[b] = t;
+        if (ts.out) ts.out[(size_t)bt * ts.out_stride] = t;
+        if (ts.next) ts.next[bt] = t;
       }
-    } else {
-      t = ts.tok[b];
     }
     t = t < 0 ? 0 : (t >= V ? V - 1 : t);  // out-of-range ids are clamped (documented in the ABI)
     if (lane == 0) tok_s[wave] = t;
   }
   __syncthreads();
-  const int n = min((int)blockIdx.x * 4 + wave, H - 1);
-  const int K = 2 * Bb;
-  const uint16_t* hrow[kRG];
-  const uint16_t* erow[kRG];
+  // embedding-half activations (chunks of the hidden half keep their hidden values)
 #pragma unroll
-  for (int r = 0; r < kRG; ++r) {
-    const int b = min(r0 + r, B - 1);
-    hrow[r] = th + (size_t)b * Bb;
-    erow[r] = emb + (size_t)tok_s[r] * Bb;
-  }
-  const uint16_t* w = W + (size_t)n * K;
-  float acc[kRG];
-#pragma unroll
-  for (int r = 0; r < kRG; ++r) acc[r] = 0.f;
-  const int iters = K >> 9;
-#pragma unroll 4
-  for (int it = 0; it < iters; ++it) {
-    const int k = it * 512 + lane * 8;
-    float wf[8];
-    unpack8(*reinterpret_cast<const uint4*>(w + k), wf);
-    const bool hid = k < Bb;
-    const float sc = hid ? 1.0f : escale;
+  for (int c = 0; c < CPW; ++c) {
+    const int k = cidx[c] * 256 + lane * 4;
 #pragma unroll
     for (int r = 0; r < kRG; ++r) {
-      const uint16_t* src = hid ? (hrow[r] + k) : (erow[r] + (k - Bb));
-      float xf[8];
-      unpack8(*reinterpret_cast<const uint4*>(src), xf);
-      float s = acc[r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(xf[e] * sc, wf[e], s);
-      acc[r] = s;
+      const uint2 e = *reinterpret_cast<const uint2*>(emb + (size_t)tok_s[r] * Bb + max(k - Bb, 0));
+      xr[c][r] = (cidx[c] >= hch) ? e : xr[c][r];
     }
   }
-  XR<kRG, 32>::run(acc, lane);
-  const int idx = lane >> 4;  // row within the group
-  if ((lane & 15) == 0 && (int)blockIdx.x * 4 + wave < H && r0 + idx < B) x[(size_t)(r0 + idx) * H + n] = acc[0];
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const bool live = wave * CPW + c < nch;
+    const float sc = live ? (cidx[c] >= hch ? escale : 1.0f) : 0.0f;
+#pragma unroll
+    for (int r = 0; r < kRG; ++r) {
+      float xf[4];
+      unpack4(xr[c][r], xf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xf[e] *= sc;
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        float wf[4];
+        unpack4(wr[c][o], wf);
+        float s = acc[r * 4 + o];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(xf[e], wf[e], s);
+        acc[r * 4 + o] = s;
+      }
+    }
+  }
+  XR<16, 32>::run(acc, lane);  // lanes 4i .. 4i+3 hold the wave's partial of (row, output) index i
+  if ((lane & 3) == 0) red[wave][lane >> 2] = acc[0];
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) s += red[w][threadIdx.x];
+    const int r = r0 + (threadIdx.x >> 2), n = n0 + (threadIdx.x & 3);
+    if (r < B && n < H) x[(size_t)r * H + n] = s;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// q projection ([MTP doc] "Tensor schema": attn_norm, attn_q); grid (QD / 16, ceil(B / 4))
+// q projection ([MTP doc] "Tensor schema": attn_norm, attn_q); grid (QD / 16, ceil(B / 4)), H = 64 NPL
 
-__global__ __launch_bounds__(256) void k_qproj(int B, int H, int QD, Residual res, const uint16_t* __restrict__ w_norm,
+template <int NPL>
+__global__ __launch_bounds__(256) void k_qproj(int B, int QD, Residual res, const uint16_t* __restrict__ w_norm,
                                                float eps, const uint16_t* __restrict__ W, float* __restrict__ q) {
-  extern __shared__ float xs[];  // [kRG][H]
+  constexpr int H = NPL * 64;
+  __shared__ __attribute__((aligned(16))) float xs[kRG][H];
   const int wave = wave_id(), lane = lane_id();
   const int n0 = blockIdx.x * 16 + wave * 4;
-  WaveW<4> ww;
+  WaveW<4, H / 256> ww;
   ww.load(W, H, n0, QD);
-  prologue_norm(res, w_norm, eps, B, H, xs);
+  prologue_norm<NPL>(res, w_norm, eps, B, &xs[0][0]);
   __syncthreads();
-  const float* xrow[kRG] = {xs, xs + H, xs + 2 * H, xs + 3 * H};
+  const float* xrow[kRG] = {xs[0], xs[1], xs[2], xs[3]};
   float acc[kRG * 4];
-  ww.dot(xrow, H, acc);
+  ww.dot(xrow, acc);
   const int idx = lane >> 2;  // r * 4 + o
   const int r = blockIdx.y * kRG + (idx >> 2), n = n0 + (idx & 3);
   if ((lane & 3) == 0 && r < B && n < QD) q[(size_t)r * QD + n] = acc[0];
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// Dense product for o_proj / down / centroid scores: grid (N / 4, ceil(B / 4)); X rows read directly (rows beyond
-// B read row B-1, results discarded).
+// Dense product for o_proj / down / centroid scores: grid (N / 4, ceil(B / 4)), K = 256 IT; X rows read directly
+// (rows beyond B read row B-1, results discarded).
 
-__global__ __launch_bounds__(256) void k_dense(int B, int K, int N, const float* __restrict__ X,
+template <int IT>
+__global__ __launch_bounds__(256) void k_dense(int B, int N, const float* __restrict__ X,
                                                const uint16_t* __restrict__ W, float* __restrict__ y) {
+  constexpr int K = IT * 256;
   const int wave = wave_id(), lane = lane_id();
   const int n = blockIdx.x * 4 + wave;
   const int r0 = blockIdx.y * kRG;
-  WaveW<1> ww;
+  WaveW<1, IT> ww;
   ww.load(W, K, n, N);
   const float* xrow[kRG];
 #pragma unroll
   for (int r = 0; r < kRG; ++r) xrow[r] = X + (size_t)min(r0 + r, B - 1) * K;
   float acc[kRG];
-  ww.dot(xrow, K, acc);
+  ww.dot(xrow, acc);
   const int idx = lane >> 4;
   if ((lane & 15) == 0 && r0 + idx < B && n < N) y[(size_t)(r0 + idx) * N + n] = acc[0];
 }
@@ -334,22 +355,24 @@ __global__ __launch_bounds__(256) void k_dense(int B, int K, int N, const float*
 // GeGLU FFN input half ([MTP doc] "Tensor schema": ffn_norm, ffn_gate, ffn_up): grid (F / 16, ceil(B / 4)).
 // Each wave: 4 ffn indices x {gate, up} for the 4 rows. Blocks also fill their share of the logits row.
 
-__global__ __launch_bounds__(256) void k_ffn(int B, int H, int F, Residual res, const uint16_t* __restrict__ w_norm,
+template <int NPL>
+__global__ __launch_bounds__(256) void k_ffn(int B, int F, Residual res, const uint16_t* __restrict__ w_norm,
                                              float eps, const uint16_t* __restrict__ Wg,
                                              const uint16_t* __restrict__ Wu, float* __restrict__ m,
                                              FillRange fill) {
-  extern __shared__ float xs[];  // [kRG][H]
+  constexpr int H = NPL * 64;
+  __shared__ __attribute__((aligned(16))) float xs[kRG][H];
   const int wave = wave_id(), lane = lane_id();
   const int f0 = blockIdx.x * 16 + wave * 4;
-  WaveW<4> wg, wu;
+  WaveW<4, H / 256> wg, wu;
   wg.load(Wg, H, f0, F);
   wu.load(Wu, H, f0, F);
-  prologue_norm(res, w_norm, eps, B, H, xs);
+  prologue_norm<NPL>(res, w_norm, eps, B, &xs[0][0]);
   __syncthreads();
-  const float* xrow[kRG] = {xs, xs + H, xs + 2 * H, xs + 3 * H};
+  const float* xrow[kRG] = {xs[0], xs[1], xs[2], xs[3]};
   float ag[kRG * 4], au[kRG * 4];
-  wg.dot(xrow, H, ag);
-  wu.dot(xrow, H, au);
+  wg.dot(xrow, ag);
+  wu.dot(xrow, au);
   const int idx = lane >> 2;
   const int r = blockIdx.y * kRG + (idx >> 2), f = f0 + (idx & 3);
   if ((lane & 3) == 0 && r < B && f < F) m[(size_t)r * F + f] = gelu_tanh(ag[0]) * au[0];
@@ -375,31 +398,29 @@ __global__ __launch_bounds__(256) void k_ffn(int B, int H, int F, Residual res, 
 // assist_embed_centroids; [Inventory] "Centroid / ordered embeddings LM head", step 1)
 // grid ((Bb + C) / 16, ceil(B / 4))
 
-__global__ __launch_bounds__(256) void k_post(int B, int H, int Bb, int C, Residual res,
-                                              const uint16_t* __restrict__ w_out, float eps,
-                                              const uint16_t* __restrict__ Wp, const uint16_t* __restrict__ Wc,
-                                              float* __restrict__ h_out, uint16_t* __restrict__ hidden_out,
-                                              float* __restrict__ scores) {
-  extern __shared__ float xs[];  // [kRG][H]
+template <int NPL>
+__global__ __launch_bounds__(256) void k_post(int B, int Bb, int C, Residual res, const uint16_t* __restrict__ w_out,
+                                              float eps, const uint16_t* __restrict__ Wp,
+                                              const uint16_t* __restrict__ Wc, float* __restrict__ h_out,
+                                              uint16_t* __restrict__ hidden_out, float* __restrict__ scores) {
+  constexpr int H = NPL * 64;
+  __shared__ __attribute__((aligned(16))) float xs[kRG][H];
   const int wave = wave_id(), lane = lane_id();
   const int n0 = blockIdx.x * 16 + wave * 4;
-  const bool cen = n0 >= Bb;
-  WaveW<4> ww;
-  if (!cen)
-    ww.load(Wp, H, n0, Bb);
-  else
-    ww.load(Wc, H, n0 - Bb, C);
-  prologue_norm(res, w_out, eps, B, H, xs);
+  const bool cen = n0 >= Bb;  // Bb % 16 == 0: a block is wholly post_proj or wholly centroids
+  WaveW<4, H / 256> ww;
+  ww.load(cen ? Wc : Wp, H, cen ? n0 - Bb : n0, cen ? C : Bb);
+  prologue_norm<NPL>(res, w_out, eps, B, &xs[0][0]);
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < kRG * H; i += 256) {
       const int r = blockIdx.y * kRG + i / H;
-      if (r < B) h_out[(size_t)r * H + i % H] = xs[i];
+      if (r < B) h_out[(size_t)r * H + i % H] = xs[0][i];
     }
   }
-  const float* xrow[kRG] = {xs, xs + H, xs + 2 * H, xs + 3 * H};
+  const float* xrow[kRG] = {xs[0], xs[1], xs[2], xs[3]};
   float acc[kRG * 4];
-  ww.dot(xrow, H, acc);
+  ww.dot(xrow, acc);
   const int idx = lane >> 2;
   const int r = blockIdx.y * kRG + (idx >> 2), n = n0 + (idx & 3);
   if ((lane & 3) == 0 && r < B) {
@@ -1061,19 +1082,61 @@ void set_next_launch_events(hipEvent_t start, hipEvent_t stop) {
 
 hipError_t launch_pre(hipStream_t s, int B, int Bb, int H, int V, const uint16_t* th, TokenSource ts,
                       const uint16_t* emb, float escale, const uint16_t* w_pre, float* x) {
-  dim3 grid((H + 3) / 4, row_groups(B));
-  return go(k_pre, grid, 256, 0, s, B, Bb, H, V, th, ts, emb, escale, w_pre, x);
+  const dim3 grid((H + 3) / 4, row_groups(B));
+  const int nch = Bb / 128;  // 256-wide chunks of K = 2 Bb
+#define MTPD_PRE(NWV_, CPW_) \
+  return go(k_pre<NWV_, CPW_>, grid, NWV_ * 64, 0, s, B, Bb, H, V, th, ts, emb, escale, w_pre, x)
+  if (nch <= 32) {
+    switch ((nch + 3) / 4) {
+      case 1: MTPD_PRE(4, 1);
+      case 2: MTPD_PRE(4, 2);
+      case 3: MTPD_PRE(4, 3);
+      case 4: MTPD_PRE(4, 4);
+      case 5: MTPD_PRE(4, 5);
+      case 6: MTPD_PRE(4, 6);
+      case 7: MTPD_PRE(4, 7);
+      case 8: MTPD_PRE(4, 8);
+    }
+  } else {
+    switch ((nch + 7) / 8) {
+      case 5: MTPD_PRE(8, 5);
+      case 6: MTPD_PRE(8, 6);
+      case 7: MTPD_PRE(8, 7);
+      case 8: MTPD_PRE(8, 8);
+    }
+  }
+#undef MTPD_PRE
+  return hipErrorInvalidValue;
 }
+
+// H = 64 NPL for the kernels with a norm prologue (hidden in {256, 512, 768, 1024})
+#define MTPD_BY_NPL(H_, CALL)        \
+  switch ((H_) / 64) {               \
+    case 4: { constexpr int NPL = 4; CALL; }   \
+    case 8: { constexpr int NPL = 8; CALL; }   \
+    case 12: { constexpr int NPL = 12; CALL; } \
+    case 16: { constexpr int NPL = 16; CALL; } \
+  }                                  \
+  return hipErrorInvalidValue;
 
 hipError_t launch_qproj(hipStream_t s, int B, int H, int QD, Residual res, const uint16_t* w_norm, float eps,
                         const uint16_t* w_q, float* q) {
-  dim3 grid((QD + 15) / 16, row_groups(B));
-  return go(k_qproj, grid, 256, kRG * H * sizeof(float), s, B, H, QD, res, w_norm, eps, w_q, q);
+  const dim3 grid((QD + 15) / 16, row_groups(B));
+  MTPD_BY_NPL(H, return go(k_qproj<NPL>, grid, 256, 0, s, B, QD, res, w_norm, eps, w_q, q))
 }
 
 hipError_t launch_dense(hipStream_t s, int B, int K, int N, const float* X, const uint16_t* w, float* y) {
-  dim3 grid((N + 3) / 4, row_groups(B));
-  return go(k_dense, grid, 256, 0, s, B, K, N, X, w, y);
+  const dim3 grid((N + 3) / 4, row_groups(B));
+  switch (K / 256) {
+#define MTPD_DENSE(IT_) \
+  case IT_:             \
+    return go(k_dense<IT_>, grid, 256, 0, s, B, N, X, w, y);
+    MTPD_DENSE(1) MTPD_DENSE(2) MTPD_DENSE(3) MTPD_DENSE(4) MTPD_DENSE(5) MTPD_DENSE(6) MTPD_DENSE(7) MTPD_DENSE(8)
+    MTPD_DENSE(9) MTPD_DENSE(10) MTPD_DENSE(11) MTPD_DENSE(12) MTPD_DENSE(13) MTPD_DENSE(14) MTPD_DENSE(15)
+    MTPD_DENSE(16)
+#undef MTPD_DENSE
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, const uint16_t* w_cen, float* scores) {
@@ -1082,17 +1145,18 @@ hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, con
 
 hipError_t launch_ffn(hipStream_t s, int B, int H, int F, Residual res, const uint16_t* w_norm, float eps,
                       const uint16_t* w_gate, const uint16_t* w_up, float* m, FillRange fill) {
-  dim3 grid((F + 15) / 16, row_groups(B));
-  return go(k_ffn, grid, 256, kRG * H * sizeof(float), s, B, H, F, res, w_norm, eps, w_gate, w_up, m, fill);
+  const dim3 grid((F + 15) / 16, row_groups(B));
+  MTPD_BY_NPL(H, return go(k_ffn<NPL>, grid, 256, 0, s, B, F, res, w_norm, eps, w_gate, w_up, m, fill))
 }
 
 hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res, const uint16_t* w_out, float eps,
                        const uint16_t* w_post, const uint16_t* w_cen, float* h_out, uint16_t* hidden_out,
                        float* scores) {
-  dim3 grid((Bb + C + 15) / 16, row_groups(B));
-  return go(k_post, grid, 256, kRG * H * sizeof(float), s, B, H, Bb, C, res, w_out, eps, w_post, w_cen, h_out, hidden_out,
-                                                     scores);
+  const dim3 grid((Bb + C + 15) / 16, row_groups(B));
+  MTPD_BY_NPL(H, return go(k_post<NPL>, grid, 256, 0, s, B, Bb, C, res, w_out, eps, w_post, w_cen, h_out,
+                           hidden_out, scores))
 }
+#undef MTPD_BY_NPL
 
 hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
                        float eps, const float* rope, int type, const uint16_t* K, const uint16_t* V, int cap,

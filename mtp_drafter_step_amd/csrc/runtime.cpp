@@ -582,7 +582,7 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
       const int b0 = ch.rows[ci], Bc = ch.rows[ci + 1] - b0;
       void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
       const ChainView v = chain_view(h, kv, win, b0, Bc);
-      mtpd::TokenSource ts{last_token + b0, nullptr, 0, nullptr, 0, nullptr};
+      mtpd::TokenSource ts{last_token + b0, at<uint64_t>(wsc, p.keys), 0, c.top_k, nullptr, 0, nullptr};
       CHECK(run_step(h, cs, wsc, p, Bc, target_hidden + (size_t)b0 * c.backbone, ts, target_embd, &v.kv, v.win,
                      v.nsplit, logits ? logits + (size_t)b0 * c.vocab : nullptr,
                      hidden_out + (size_t)b0 * c.backbone, sel_centroids ? sel_centroids + (size_t)b0 * c.top_k : nullptr,
@@ -622,8 +622,8 @@ int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch
       for (int i = 0; i < n; ++i) {
         const uint16_t* th = (i == 0) ? target_hidden + (size_t)b0 * c.backbone : hid[(i - 1) & 1];
         // step i's token: the caller's for i = 0, else the previous step's argmax (recorded as tokens[:, i-1])
-        mtpd::TokenSource ts{last_token + b0, nullptr, 0, nullptr, 0, nullptr};
-        if (i > 0) ts = mtpd::TokenSource{nullptr, keys, c.top_k, tok_c + (i - 1), n, nullptr};
+        mtpd::TokenSource ts{last_token + b0, keys, 0, c.top_k, nullptr, 0, nullptr};
+        if (i > 0) ts = mtpd::TokenSource{last_token + b0, keys, 1, c.top_k, tok_c + (i - 1), n, nullptr};
         uint16_t* hout = (i == n - 1) ? hidden_out + (size_t)b0 * c.backbone : hid[i & 1];
         CHECK(run_step(h, cs, wsc, p, Bc, th, ts, target_embd, &v.kv, v.win, v.nsplit,
                        logits ? logits + (size_t)i * BV + (size_t)b0 * c.vocab : nullptr, hout, nullptr, nullptr,
