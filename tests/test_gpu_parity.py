@@ -107,43 +107,38 @@ BLOCK_CASES = {
 
 
 @pytest.mark.parametrize("name", list(BLOCK_CASES))
-def test_draft_block_parity_teacher_forced(name):
+def test_draft_block_parity_stepwise(name):
+    """draft_block(n) against the oracle one step at a time on identical inputs.
+
+    The block is replayed as chained drafter_step calls, which must reproduce its tokens and logits bit for bit;
+    the oracle is then given each step's exact inputs (the GPU's bf16 hidden_out and token of the previous step).
+    Chaining the oracle on its own hidden states is not a parity test: one-ulp bf16 differences in hidden_out
+    grow through the steps (a few flips move centroid scores by about 1e-2 three steps later), so agreement
+    after the first step would depend on rounding luck rather than on the arithmetic."""
     say(f"draft_block case={name}")
     kw = dict(BLOCK_CASES[name])
     n = kw.pop("n")
     case = Case(**kw)
-    out = case.drafter.draft_block(n, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    blk = case.drafter.draft_block(n, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    blk = {k: v.clone() for k, v in blk.items()}
     torch.cuda.synchronize()
-    toks = out["tokens"].cpu().numpy()  # [B][n]
-    logits = out["logits"]  # [n][B][V]
     B = kw["batch"]
-    forced = toks.T.copy()
-    refs = O.draft_block(case.model, n, case.inp["target_hidden"].numpy().view(np.uint16),
-                         case.inp["last_token"].numpy(), case.temb_cpu, case.kv_cpu, forced_tokens=forced)
-    tally = Tally()
+    th, tok = case.th.clone(), case.tok.clone()
+    rows = list(range(B))
+    tallies = []
     for i in range(n):
-        for b in range(B):
-            row = logits[i, b].cpu().numpy()
-            finite = row.view(np.uint32) != 0xF149F2CA
-            ids = np.nonzero(finite)[0]
-            r = refs[i]
-            tally.rows += 1
-            assert int(finite.sum()) == case.model.cfg.top_k * case.model.cfg.vsc
-            if r["cgap"][b] > 1e-3:
-                tally.sel_checked += 1
-                ref_ids = np.asarray(r["ids"][b])
-                assert set(ids.tolist()) == set(ref_ids.tolist()), f"step {i} row {b}: candidate set differs"
-                ref_map = dict(zip(ref_ids.tolist(), np.asarray(r["z"][b]).tolist()))
-                assert rel_ok(row[ids], [ref_map[k] for k in ids.tolist()]), f"step {i} row {b}: logits"
-                if r["margin"][b] > 1e-3:
-                    tally.tok_checked += 1
-                    assert int(toks[b, i]) == r["next"][b], f"step {i} row {b}: token"
-            assert int(toks[b, i]) == int(np.argmax(row))
-    hid = out["hidden_out"].cpu().numpy().view(np.uint16)
-    for b in range(B):
-        assert rel_ok(O.bf16_to_f64(hid[b]), O.bf16_to_f64(refs[-1]["hidden_out"][b])), f"row {b}: hidden_out"
-    say(tally.summary())
-    assert tally.sel_checked >= (n * B) // 2
+        st = case.drafter.drafter_step(th, tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+        st = {k: v.clone() for k, v in st.items()}
+        torch.cuda.synchronize()
+        assert torch.equal(st["next"], blk["tokens"][:, i].contiguous()), f"step {i}: block tokens"
+        assert torch.equal(st["logits"], blk["logits"][i]), f"step {i}: block logits"
+        ref = case.oracle_step(rows=rows, th=th.cpu().numpy().view(np.uint16), tok=tok.cpu().numpy())
+        tallies.append(compare_step(case, st, ref, rows, where=f"step {i}"))
+        th, tok = st["hidden_out"], st["next"]
+    torch.cuda.synchronize()
+    assert torch.equal(th, blk["hidden_out"])
+    say(" | ".join(t.summary() for t in tallies))
+    assert sum(t.sel_checked for t in tallies) >= (n * B) // 2
 
 
 def test_draft_block_equals_chained_steps():
