@@ -682,6 +682,16 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   const uint16_t* Kb = K + ((size_t)b * nkv + g) * (size_t)cap * HD + 8 * kq;
   const uint16_t* Vb = Vc + ((size_t)b * nkv + g) * (size_t)cap * HD + 8 * kq;
 
+  // inputs of q_norm + rotation first (waits count loads in issue order, so these must precede the key batch)
+  const float* tab = rope + ((size_t)b * 2 + type) * 2 * half;
+  const int hh = min(wave, G - 1);  // the wave's head (waves beyond G repeat the last head and store nothing)
+  const float4 qv = *reinterpret_cast<const float4*>(q + ((size_t)b * nh + g * G + hh) * HD + lane * 4);
+  const uint2 qw = *reinterpret_cast<const uint2*>(qnorm + lane * 4);
+  const int i0 = (lane * 4) & (half - 1);
+  const float4 co4 = *reinterpret_cast<const float4*>(tab + i0);
+  const float4 si4 = *reinterpret_cast<const float4*>(tab + half + i0);
+  __builtin_amdgcn_sched_barrier(0);
+
   // key rows of batch t (lane: key t + hq, dims 32c + 8kq .. +8), clamped into the block's range; batch t + S is
   // in flight while batch t is computed
   uint4 ka[KSTEPS], kn[KSTEPS];
@@ -691,31 +701,26 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) ka[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
   }
+  __builtin_amdgcn_sched_barrier(0);  // the q arithmetic below must not be hoisted above the key loads
 
-  // q_norm + rotation at the row's constant position ([Guide] section 2(2))
-  const float* tab = rope + ((size_t)b * 2 + type) * 2 * half;
-  for (int hh = wave; hh < G; hh += NW) {
-    const float* qr = q + ((size_t)b * nh + g * G + hh) * HD;
-    float v[4], wq[4], co[4], si[4];
+  // q_norm + rotation at the row's constant position ([Guide] section 2(2)); lane l holds dims 4l .. 4l+3, whose
+  // rotation partners (dim i <-> i + HD/2) sit in lane l ^ 32
+  {
+    float v[4] = {qv.x, qv.y, qv.z, qv.w}, wq[4];
+    const float co[4] = {co4.x, co4.y, co4.z, co4.w}, si[4] = {si4.x, si4.y, si4.z, si4.w};
+    unpack4(qw, wq);
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = lane * 4 + e;
-      const int i = d & (half - 1);
-      v[e] = qr[d];
-      wq[e] = bf2f(qnorm[d]);
-      co[e] = tab[i];
-      si[e] = tab[half + i];
-      ss = fmaf(v[e], v[e], ss);
-    }
+    for (int e = 0; e < 4; ++e) ss = fmaf(v[e], v[e], ss);
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / (float)HD + eps);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = v[e] * r * wq[e];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float partner = __shfl_xor(v[e], 32, 64);  // dim i <-> i + HD/2
-      qs[hh][lane * 4 + e] = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
+      const float partner = __shfl_xor(v[e], 32, 64);
+      const float rot = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
+      if (wave < G) qs[hh][lane * 4 + e] = rot;
     }
   }
   __syncthreads();
@@ -851,31 +856,32 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   }
 }
 
-// grid (B * nh), 256 threads: thread d of head (b, h) merges the nsplit partials
-__global__ __launch_bounds__(256) void k_attn_merge(int hd, int nsplit, const float* __restrict__ pacc,
-                                                    const float* __restrict__ pml, float* __restrict__ o) {
+// grid (B * nh), 256 threads: thread d of head (b, h) merges the nsplit partials (nsplit <= NS <= 64). Each wave
+// reads the (max, sum) pairs with one load per lane (lane s: split s) and forms the merge weights there; the NS
+// partial values of a thread are loaded unconditionally from clamped slots and the surplus weighted by zero.
+template <int NS>
+__global__ __launch_bounds__(256) void k_attn_merge(int hd, int nsplit, const float* pacc, const float* pml,
+                                                    float* __restrict__ o) {  // (no restrict on the inputs: it
+                                                                             // would let the loads sink below the
+                                                                             // issue barrier)
   const size_t base = (size_t)blockIdx.x * kMaxSplit;
+  const int lane = lane_id();
   const int d = min((int)threadIdx.x, hd - 1);
-  float m[kMaxSplit], l[kMaxSplit], a[kMaxSplit];
-  float M = -INFINITY;
+  float a[NS];
 #pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    if (s < nsplit) {
-      m[s] = pml[(base + s) * 2];
-      l[s] = pml[(base + s) * 2 + 1];
-      a[s] = pacc[(base + s) * hd + d];
-      M = fmaxf(M, m[s]);
-    }
-  }
-  float L = 0.f, A = 0.f;
+  for (int s = 0; s < NS; ++s) a[s] = pacc[(base + (size_t)min(s, nsplit - 1)) * hd + d];
+  const float2 ml = *reinterpret_cast<const float2*>(pml + (base + (size_t)min(lane, nsplit - 1)) * 2);
+  asm volatile("" ::: "memory");  // every load above is issued before the first wait
+  __builtin_amdgcn_sched_barrier(0);
+  const float mv = lane < nsplit ? ml.x : -INFINITY;
+  float M = mv;
 #pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    if (s < nsplit) {
-      const float f = (m[s] == -INFINITY) ? 0.f : exp2f(m[s] - M);
-      L = fmaf(l[s], f, L);
-      A = fmaf(a[s], f, A);
-    }
-  }
+  for (int of = 32; of > 0; of >>= 1) M = fmaxf(M, __shfl_xor(M, of, 64));
+  const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
+  const float L = wave_sum(ml.y * f);
+  float A = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) A = fmaf(a[s], readlane_f(f, s), A);
   if ((int)threadIdx.x < hd) o[(size_t)blockIdx.x * hd + d] = (L > 0.f) ? A / L : 0.f;
 }
 
@@ -1189,7 +1195,11 @@ hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const floa
 
 hipError_t launch_attn_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
                              float* o) {
-  return go(k_attn_merge, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
+  if (nsplit <= 2) return go(k_attn_merge<2>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
+  if (nsplit <= 4) return go(k_attn_merge<4>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
+  if (nsplit <= 8) return go(k_attn_merge<8>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
+  if (nsplit <= 16) return go(k_attn_merge<16>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
+  return go(k_attn_merge<32>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
 }
 
 hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,

@@ -221,9 +221,11 @@ int check_kv(const mtpd_handle_s* h, const mtpd_kv& kv, int B, const char* name,
   return MTPD_OK;
 }
 
-// Splits of each row's key window: one block per row when the longest window is at most 1024 keys (the block's
-// waves merge in LDS); otherwise about one block per 256 CUs' share of the batch's keys, at least 128 keys per
-// block, at most kMaxSplit blocks per (row, kv head), merged by a second kernel.
+// Splits of each row's key window. A block of the attention kernel runs 4 waves that take 16-key batches in turn,
+// and each batch costs about one memory round trip, so a block should see few batches; but every block pays the
+// same prologue, and the split partials are merged by a second kernel. Blocks cover at least 64 keys (one batch
+// per wave) and at least the batch's keys / 256 (about one block per CU), up to kMaxSplit blocks per
+// (row, kv head).
 int nsplit_for(const mtpd::RowWindows& win, int B, int nkv) {
   int mx = 1;
   long total = 0;
@@ -231,11 +233,9 @@ int nsplit_for(const mtpd::RowWindows& win, int B, int nkv) {
     mx = std::max(mx, win.count[b]);
     total += win.count[b];
   }
-  if (mx <= 1024) return 1;
-  long per = (total * nkv + 255) / 256;
-  per = std::max<long>(128, (per + 63) / 64 * 64);
-  int ns = (int)((mx + per - 1) / per);
-  return std::max(2, std::min(ns, mtpd::kMaxSplit));
+  const long per = std::max<long>(64, (total * nkv + 255) / 256);
+  const long ns = (mx + per - 1) / per;
+  return (int)std::max<long>(1, std::min<long>(ns, mtpd::kMaxSplit));
 }
 
 // The masked head on fp32 hidden states h [B][H] and centroid scores already in the workspace: per (row, slot)
