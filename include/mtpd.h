@@ -12,7 +12,9 @@
  *   - Tensors are DEVICE memory owned by the caller unless marked HOST. bf16 values are passed as their uint16_t
  *     bit patterns. Matrices are row-major [out][in] (the PyTorch nn.Linear layout, which is the GGUF [in, out]
  *     shape of the [MTP doc] "Tensor schema" read as ne0 = in). Device pointers must be 16-byte aligned.
- *   - Weights are borrowed by mtpd_create and must outlive the handle.
+ *   - Weights are borrowed by mtpd_create and must outlive the handle. The exception is the head table:
+ *     mtpd_create copies token_embd into cluster order (row r = token_embd[token_ordering[r]], vocab*hidden bf16
+ *     of device memory owned by the handle), so later changes to token_embd or token_ordering are not seen.
  *   - Calls enqueue work on the caller's HIP stream (passed as void*, a hipStream_t; NULL = the null stream) and
  *     return without synchronising it. All argument validation happens on the host before anything is enqueued;
  *     on a negative return nothing was enqueued and mtpd_last_error() describes the problem.
@@ -115,7 +117,8 @@ typedef struct {
 
 /* Validate the configuration and weights and build a handle. Copies token_ordering to the host once (a blocking
  * copy on the null stream) to check that it is a permutation ([Inventory] "GGUF / converter layout",
- * verification script). max_batch <= MTPD_MAX_BATCH. Returns MTPD_OK and *out, or a negative code. */
+ * verification script), then builds the cluster-ordered head table on the null stream and waits for it
+ * (MTPD_ENOMEM if it does not fit). max_batch <= MTPD_MAX_BATCH. Returns MTPD_OK and *out, or a negative code. */
 MTPD_API int mtpd_create(const mtpd_config *cfg, const mtpd_weights *w, int32_t max_batch, mtpd_handle *out);
 
 /* Release a handle (NULL is a no-op). Does not touch caller memory. */

@@ -85,11 +85,15 @@ hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res,
                        float* scores);
 
 // Masked head: per (row, selected slot j): top-k of the row's centroid scores (descending, ties to the lower
-// index), the cluster's token ids through the ordering, sparse logits token_embd[id] . h, optional scatter into
-// logits, and the slot's best (value, id) key (larger value, then lower id).
+// index), the cluster's token ids through the ordering, sparse logits token_embd[id] . h (rows read from Es, the
+// head table in cluster order), optional scatter into logits, and the slot's best (value, id) key (larger value,
+// then lower id).
 hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,
-                       const int32_t* ordering, const uint16_t* E, const float* h, int32_t* sel, int32_t* ids,
+                       const int32_t* ordering, const uint16_t* Es, const float* h, int32_t* sel, int32_t* ids,
                        float* z, float* logits, size_t V, uint64_t* keys);
+
+// out[r] = E[ordering[r]] for r < V (rows of H bf16): the head table in cluster order.
+hipError_t launch_gather_rows(hipStream_t s, const uint16_t* E, const int32_t* ordering, uint16_t* out, int V, int H);
 
 // next[b] = token of the largest key in keys[b][0, k); also out2[b*stride2] when set.
 hipError_t launch_final(hipStream_t s, int B, int k, const uint64_t* keys, int32_t* next, int32_t* out2, int stride2);

@@ -396,7 +396,7 @@ __global__ __launch_bounds__(256) void k_ffn(int B, int F, Residual res, const u
 // ------------------------------------------------------------------------------------------------------------
 // output norm + post_projection + centroid scores ([MTP doc] "Tensor schema": output_norm, assist_post_proj,
 // assist_embed_centroids; [Inventory] "Centroid / ordered embeddings LM head", step 1)
-// grid ((Bb + C) / 16, ceil(B / 4))
+// grid ((Bb + C) / 32, ceil(B / 4)); each wave computes 8 outputs for the 4 rows
 
 template <int NPL>
 __global__ __launch_bounds__(256) void k_post(int B, int Bb, int C, Residual res, const uint16_t* __restrict__ w_out,
@@ -406,9 +406,9 @@ __global__ __launch_bounds__(256) void k_post(int B, int Bb, int C, Residual res
   constexpr int H = NPL * 64;
   __shared__ __attribute__((aligned(16))) float xs[kRG][H];
   const int wave = wave_id(), lane = lane_id();
-  const int n0 = blockIdx.x * 16 + wave * 4;
-  const bool cen = n0 >= Bb;  // Bb % 16 == 0: a block is wholly post_proj or wholly centroids
-  WaveW<4, H / 256> ww;
+  const int n0 = blockIdx.x * 32 + wave * 8;
+  const bool cen = n0 >= Bb;  // Bb % 32 == 0: a block is wholly post_proj or wholly centroids
+  WaveW<8, H / 256> ww;
   ww.load(cen ? Wc : Wp, H, cen ? n0 - Bb : n0, cen ? C : Bb);
   prologue_norm<NPL>(res, w_out, eps, B, &xs[0][0]);
   __syncthreads();
@@ -419,11 +419,11 @@ __global__ __launch_bounds__(256) void k_post(int B, int Bb, int C, Residual res
     }
   }
   const float* xrow[kRG] = {xs[0], xs[1], xs[2], xs[3]};
-  float acc[kRG * 4];
+  float acc[kRG * 8];
   ww.dot(xrow, acc);
-  const int idx = lane >> 2;
-  const int r = blockIdx.y * kRG + (idx >> 2), n = n0 + (idx & 3);
-  if ((lane & 3) == 0 && r < B) {
+  const int idx = lane >> 1;  // r * 8 + o
+  const int r = blockIdx.y * kRG + (idx >> 3), n = n0 + (idx & 7);
+  if ((lane & 1) == 0 && r < B) {
     if (!cen) {
       if (n < Bb) hidden_out[(size_t)r * Bb + n] = f2bf(acc[0]);
     } else if (n - Bb < C) {
@@ -890,47 +890,64 @@ __global__ __launch_bounds__(256) void k_attn_merge(int hd, int nsplit, const fl
 // grid (k, B), 256 threads. Every block of a row recomputes the row's top-k (radix select over order-preserving
 // keys; exact, ties to the lower index) and keeps its slot j; 16 groups of 16 lanes then score the slot's cluster.
 
-constexpr int kPerThr = kMaxCentroids / 256;
-
-__global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, int H, const float* __restrict__ scores,
-                                              const int32_t* __restrict__ ordering, const uint16_t* __restrict__ E,
-                                              const float* __restrict__ h, int32_t* __restrict__ sel,
+// NPT scores per thread (C <= 256 NPT), H = 128 HCH. Every score and hidden-state load is issued before the first
+// wait. Es is the head table in cluster order (row r = token_embd[ordering[r]]), so the selected cluster's rows are
+// contiguous and load together with their token ids. (No restrict on the loaded arrays: it would let the loads
+// sink below the issue barriers.)
+template <int NPT, int HCH>
+__global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float* scores, const int32_t* ordering,
+                                              const uint16_t* Es, const float* h, int32_t* __restrict__ sel,
                                               int32_t* __restrict__ ids, float* __restrict__ z,
                                               float* __restrict__ logits, size_t V, uint64_t* __restrict__ keys) {
-  __shared__ uint32_t hist[256];
+  constexpr int H = HCH * 128;
+  constexpr int HPT = (H + 255) / 256;  // hidden elements per thread
+  __shared__ uint32_t hist[4][256];  // one histogram per wave (fewer same-address atomics), summed by the scan
   __shared__ uint32_t sh_digit, sh_before, sh_n;
   __shared__ uint64_t cand[kMaxCentroids];
   __shared__ int sh_c;
-  __shared__ float hs[1024];
+  __shared__ float hs[H];
   __shared__ uint64_t red[4];
   const int j = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int npt = (C + 255) >> 8;
 
-  // scores -> order keys
-  uint32_t ok[kPerThr];
+  float sv[NPT], hv[HPT];
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i)
-    if (i < npt) ok[i] = f32_order(scores[(size_t)b * C + min(tid + 256 * i, C - 1)]);
-  // the hidden row for the dot products
-  for (int i = tid; i < H; i += 256) hs[i] = h[(size_t)b * H + i];
+  for (int i = 0; i < NPT; ++i) sv[i] = scores[(size_t)b * C + min(tid + 256 * i, C - 1)];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) hv[i] = h[(size_t)b * H + min(tid + 256 * i, H - 1)];
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < HPT; ++i)
+    if (tid + 256 * i < H) hs[tid + 256 * i] = hv[i];
+  // scores -> order keys; entries beyond C never take part
+  uint32_t ok[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) ok[i] = f32_order(sv[i]);
 
-  // radix select of the k-th largest key value, 8 bits at a time from the top
+  // Slot j holds the (j+1)-th element in descending (score, then ascending index) order. Radix select on the order
+  // keys, 8 bits at a time from the top, narrows the search to the digit bin that holds that rank; as soon as the
+  // bin has at most 64 members they are sorted by one wave (key, then index) and the rank read off. After all four
+  // passes the bin is the set of elements tied with the exact key, ordered by index the same way.
   uint32_t prefix = 0, pmask = 0;
-  uint32_t need = (uint32_t)k;
+  uint32_t need = (uint32_t)j + 1u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0u;
+    hist[0][tid] = 0u;
+    hist[1][tid] = 0u;
+    hist[2][tid] = 0u;
+    hist[3][tid] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kPerThr; ++i)
-      if (i < npt && tid + 256 * i < C && (ok[i] & pmask) == prefix) atomicAdd(&hist[(ok[i] >> shift) & 255u], 1u);
+    for (int i = 0; i < NPT; ++i)
+      if (tid + 256 * i < C && (ok[i] & pmask) == prefix) atomicAdd(&hist[wave][(ok[i] >> shift) & 255u], 1u);
     __syncthreads();
     if (wave == 0) {
       // lane l owns digits 255-4l .. 252-4l (descending)
       uint32_t cnt[4], sum = 0;
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
-        cnt[q2] = hist[255 - 4 * lane - q2];
+        const int dg = 255 - 4 * lane - q2;
+        cnt[q2] = hist[0][dg] + hist[1][dg] + hist[2][dg] + hist[3][dg];
         sum += cnt[q2];
       }
       uint32_t incl = sum;  // inclusive prefix over lanes (higher digits first)
@@ -945,6 +962,7 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, int H, cons
         if (before < need && before + cnt[q2] >= need) {
           sh_digit = 255u - 4u * lane - q2;
           sh_before = before;
+          sh_n = cnt[q2];
         }
         before += cnt[q2];
       }
@@ -953,27 +971,46 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, int H, cons
     prefix |= sh_digit << shift;
     pmask |= 255u << shift;
     need -= sh_before;
+    const uint32_t inbin = sh_n;
     __syncthreads();
+    if (inbin <= 64u || shift == 0) break;
   }
-  // prefix is now the exact key of the k-th largest score; every key >= prefix is a candidate
+  // the bin's members as (key, ~index) composites: descending composite order is the slot order
   if (tid == 0) sh_n = 0u;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i) {
+  for (int i = 0; i < NPT; ++i) {
     const int c = tid + 256 * i;
-    if (i < npt && c < C && ok[i] >= prefix) {
+    if (c < C && (ok[i] & pmask) == prefix) {
       const uint32_t pos = atomicAdd(&sh_n, 1u);
       cand[pos] = ((uint64_t)ok[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
     }
   }
   __syncthreads();
   const uint32_t ncand = sh_n;
-  // rank among the candidates: descending score, then ascending index; slot j is the candidate of rank j
-  for (uint32_t e = tid; e < ncand; e += 256) {
-    const uint64_t me = cand[e];
-    uint32_t rank = 0;
-    for (uint32_t f = 0; f < ncand; ++f) rank += (cand[f] > me) ? 1u : 0u;
-    if (rank == (uint32_t)j) sh_c = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
+  if (ncand <= 64u) {
+    if (wave == 0) {
+      // lane e holds member e; its rank is the number of larger members, compared through scalar reads
+      // (fully unrolled over the 64 lanes: empty lanes hold 0, which is never larger than a member)
+      const uint64_t v = (uint32_t)lane < ncand ? cand[lane] : 0ull;
+      const int vhi = (int)(v >> 32), vlo = (int)(uint32_t)v;
+      uint32_t rank = 0;
+#pragma unroll
+      for (int f = 0; f < 64; ++f) {
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(vhi, f) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane(vlo, f);
+        rank += (o > v) ? 1u : 0u;
+      }
+      if ((uint32_t)lane < ncand && rank == need - 1u) sh_c = (int)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
+    }
+  } else {
+    // more than 64 elements share the exact key: their order is by index alone
+    for (uint32_t e = tid; e < ncand; e += 256) {
+      const uint64_t me = cand[e];
+      uint32_t rank = 0;
+      for (uint32_t f = 0; f < ncand; ++f) rank += (cand[f] > me) ? 1u : 0u;
+      if (rank == need - 1u) sh_c = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
+    }
   }
   __syncthreads();
   const int c = sh_c;
@@ -983,29 +1020,36 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, int H, cons
   const int grp = tid >> 4, l16 = tid & 15;
   const int nper = vsc >> 4;  // ids per group (vsc % 16 == 0)
   const int32_t* ord = ordering + (size_t)c * vsc;
-  const int hch = H >> 7;  // 128-wide chunks of h; lane l16 covers 8 elements of each
+  const uint16_t* crow = Es + (size_t)c * vsc * H;
   uint64_t best = 0;
   for (int i0 = 0; i0 < nper; i0 += 8) {
     int idv[8];
+    uint4 raw[8][HCH];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) idv[u] = ord[min(grp + 16 * (i0 + u), vsc - 1)];
+    for (int u = 0; u < 8; ++u) {
+      const int t = min(grp + 16 * (i0 + u), vsc - 1);
+      idv[u] = ord[t];
+#pragma unroll
+      for (int ch = 0; ch < HCH; ++ch)
+        raw[u][ch] = *reinterpret_cast<const uint4*>(crow + (size_t)t * H + ch * 128 + l16 * 8);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     float acc[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-    for (int ch = 0; ch < hch; ++ch) {
+#pragma unroll
+    for (int ch = 0; ch < HCH; ++ch) {
       const int col = ch * 128 + l16 * 8;
-      uint4 raw[8];
+      float hf[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) raw[u] = *reinterpret_cast<const uint4*>(E + (size_t)idv[u] * H + col);
-      float hv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = hs[col + e];
+      for (int e = 0; e < 8; ++e) hf[e] = hs[col + e];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float ef[8];
-        unpack8(raw[u], ef);
+        unpack8(raw[u][ch], ef);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[u] = fmaf(ef[e], hv[e], acc[u]);
+        for (int e = 0; e < 8; ++e) acc[u] = fmaf(ef[e], hf[e], acc[u]);
       }
     }
     XR<8, 8>::run(acc, l16);  // over the 16 lanes of the group: lane l16 holds id (l16 >> 1) of the 8
@@ -1026,6 +1070,17 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, int H, cons
   if (lane == 0) red[wave] = best;
   __syncthreads();
   if (tid == 0) keys[(size_t)b * k + j] = u64_max(u64_max(red[0], red[1]), u64_max(red[2], red[3]));
+}
+
+// Head table in cluster order: out[r] = E[ordering[r]], rows of H bf16 (H % 8 == 0); grid ceil(V / 8), 256 threads,
+// 32 threads per row.
+__global__ __launch_bounds__(256) void k_gather_rows(const uint16_t* __restrict__ E, const int32_t* __restrict__ ordering,
+                                                     uint16_t* __restrict__ out, int V, int H) {
+  const int r = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (r >= V) return;
+  const uint4* src = reinterpret_cast<const uint4*>(E + (size_t)ordering[r] * H);
+  uint4* dst = reinterpret_cast<uint4*>(out + (size_t)r * H);
+  for (int i = threadIdx.x & 31; i < H / 8; i += 32) dst[i] = src[i];
 }
 
 // grid B, 64 threads
@@ -1158,7 +1213,7 @@ hipError_t launch_ffn(hipStream_t s, int B, int H, int F, Residual res, const ui
 hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res, const uint16_t* w_out, float eps,
                        const uint16_t* w_post, const uint16_t* w_cen, float* h_out, uint16_t* hidden_out,
                        float* scores) {
-  const dim3 grid((Bb + C + 15) / 16, row_groups(B));
+  const dim3 grid((Bb + C + 31) / 32, row_groups(B));
   MTPD_BY_NPL(H, return go(k_post<NPL>, grid, 256, 0, s, B, Bb, C, res, w_out, eps, w_post, w_cen, h_out,
                            hidden_out, scores))
 }
@@ -1203,10 +1258,25 @@ hipError_t launch_attn_merge(hipStream_t s, int B, int nh, int hd, int nsplit, c
 }
 
 hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,
-                       const int32_t* ordering, const uint16_t* E, const float* h, int32_t* sel, int32_t* ids,
+                       const int32_t* ordering, const uint16_t* Es, const float* h, int32_t* sel, int32_t* ids,
                        float* z, float* logits, size_t V, uint64_t* keys) {
-  dim3 grid(k, B);
-  return go(k_head, grid, 256, 0, s, C, k, vsc, H, scores, ordering, E, h, sel, ids, z, logits, V, keys);
+  const dim3 grid(k, B);
+  const int npt = C <= 256 ? 1 : C <= 512 ? 2 : C <= 1024 ? 4 : C <= 2048 ? 8 : 16;
+#define MTPD_HEAD(NPT_, HCH_)                                                                                 \
+  if (npt == NPT_ && H == HCH_ * 128)                                                                         \
+    return go(k_head<NPT_, HCH_>, grid, 256, 0, s, C, k, vsc, scores, ordering, Es, h, sel, ids, z, logits, V, \
+              keys);
+  MTPD_HEAD(1, 2) MTPD_HEAD(2, 2) MTPD_HEAD(4, 2) MTPD_HEAD(8, 2) MTPD_HEAD(16, 2)
+  MTPD_HEAD(1, 4) MTPD_HEAD(2, 4) MTPD_HEAD(4, 4) MTPD_HEAD(8, 4) MTPD_HEAD(16, 4)
+  MTPD_HEAD(1, 6) MTPD_HEAD(2, 6) MTPD_HEAD(4, 6) MTPD_HEAD(8, 6) MTPD_HEAD(16, 6)
+  MTPD_HEAD(1, 8) MTPD_HEAD(2, 8) MTPD_HEAD(4, 8) MTPD_HEAD(8, 8) MTPD_HEAD(16, 8)
+#undef MTPD_HEAD
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_rows(hipStream_t s, const uint16_t* E, const int32_t* ordering, uint16_t* out, int V,
+                              int H) {
+  return go(k_gather_rows, (V + 7) / 8, 256, 0, s, E, ordering, out, V, H);
 }
 
 hipError_t launch_final(hipStream_t s, int B, int k, const uint64_t* keys, int32_t* next, int32_t* out2,

@@ -68,6 +68,7 @@ struct mtpd_handle_s {
   std::vector<mtpd_layer> layers;
   int32_t max_batch;
   int32_t vsc;
+  uint16_t* head_sorted = nullptr;  // token_embd rows in cluster order (owned; built by mtpd_create)
   bool use_graphs = true;
   hipStream_t cap_stream = nullptr;
   GraphEntry graphs[kGraphCache];
@@ -245,7 +246,7 @@ int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
   const mtpd_config& c = h->cfg;
   // [Inventory] "Centroid / ordered embeddings LM head", steps 2-5
   KLAUNCH(h, "head", mtpd::launch_head(s, B, c.n_centroids, c.top_k, h->vsc, c.hidden, at<float>(ws, p.scores),
-                           h->w.token_ordering, h->w.token_embd, hsrc, sel_out, ids_out, z_out, logits,
+                           h->w.token_ordering, h->head_sorted, hsrc, sel_out, ids_out, z_out, logits,
                            (size_t)c.vocab, at<uint64_t>(ws, p.keys)));
   return MTPD_OK;
 }
@@ -525,6 +526,20 @@ int mtpd_create(const mtpd_config* cfg, const mtpd_weights* w, int32_t max_batch
   }
   mtpd_handle_s* hh = new (std::nothrow) mtpd_handle_s();
   if (!hh) return fail(MTPD_ENOMEM, "out of host memory");
+  // the head table in cluster order ([Inventory] "Centroid / ordered embeddings LM head", step 3: a cluster's ids
+  // are a contiguous slice of the ordering), so that a selected cluster's rows are one contiguous read
+  const size_t head_bytes = (size_t)cfg->vocab * cfg->hidden * sizeof(uint16_t);
+  if (hipMalloc(&hh->head_sorted, head_bytes) != hipSuccess) {
+    delete hh;
+    return fail(MTPD_ENOMEM, "no device memory for the cluster-ordered head table (%zu bytes)", head_bytes);
+  }
+  e = mtpd::launch_gather_rows(nullptr, w->token_embd, w->token_ordering, hh->head_sorted, cfg->vocab, cfg->hidden);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) {
+    (void)hipFree(hh->head_sorted);
+    delete hh;
+    return fail(MTPD_EHIP, "building the cluster-ordered head table: %s", hipGetErrorString(e));
+  }
   hh->cfg = *cfg;
   hh->w = *w;
   hh->layers.assign(w->layers, w->layers + cfg->n_layer);
@@ -548,6 +563,7 @@ void mtpd_destroy(mtpd_handle h) {
   }
   if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
   for (hipEvent_t e : h->timing_ev) (void)hipEventDestroy(e);
+  if (h->head_sorted) (void)hipFree(h->head_sorted);
   delete h;
 }
 

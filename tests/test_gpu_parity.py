@@ -38,12 +38,15 @@ def test_generator_identical_on_gpu_and_cpu():
     assert torch.equal(w_cpu, w_gpu)
 
 
-@pytest.mark.parametrize("m", [1, 16, 64])
-def test_masked_head_parity(m):
-    say(f"masked_head m={m}")
+@pytest.mark.parametrize("m,scale", [(1, 1.0), (16, 1.0), (64, 1.0), (64, 0.1)])
+def test_masked_head_parity(m, scale):
+    """Centroid scores ~ N(0, scale^2). At scale 1 the top-ranked scores share their leading key byte with a few
+    dozen others; at scale 0.1 a couple of hundred scores share it, so the selection takes more than one radix
+    pass."""
+    say(f"masked_head m={m} scale={scale}")
     case = Case(synth.E4B, batch=1, context=16, max_batch=64)
     g = torch.Generator().manual_seed(100 + m)
-    h = torch.randn(m, 256, generator=g, dtype=torch.float32)
+    h = torch.randn(m, 256, generator=g, dtype=torch.float32) * scale
     out = case.drafter.masked_head(h.cuda(), want_logits=True, want_sparse=True)
     torch.cuda.synchronize()
     tally = Tally()
@@ -55,6 +58,37 @@ def test_masked_head_parity(m):
                          where=f"head m={m}")
     say(tally.summary())
     assert tally.sel_checked >= m // 2
+
+
+@pytest.mark.parametrize("ntie", [40, 100])
+def test_masked_head_exact_ties(ntie):
+    """Centroid rows 0 .. ntie-1 are copies of row ntie and h points along that row, so those ntie scores tie
+    exactly (identical terms in the same order) and lie far above every other score. Ties go to the lower index, so
+    the slots must be centroids 0 .. top_k-1 in order: 40 tied members are ordered by the small in-wave sort, 100
+    by the rank-by-index path."""
+    from mtp_drafter_step_amd import Drafter
+    say(f"masked_head ties={ntie}")
+    case = Case(synth.E4B, batch=1, context=16, max_batch=4)
+    w = dict(case.w)
+    cen = case.w["centroids"].clone()
+    cen[:ntie] = cen[ntie]
+    w["centroids"] = cen
+    model = O.Model(O.config_from(case.shape), w)
+    wg = dict(case.wg)
+    wg["centroids"] = cen.cuda()
+    d = Drafter(case.shape, wg, max_batch=4)
+    u = O.bf16_to_f64(cen[ntie].numpy().view(np.uint16))
+    h = torch.from_numpy((50.0 * u).astype(np.float32)).reshape(1, -1)
+    out = d.masked_head(h.cuda(), want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    k = case.shape.top_k
+    assert out["sel"][0].cpu().tolist() == list(range(k))
+    ref = O.masked_head_row(model, h[0].numpy().astype(np.float64))
+    assert list(ref["sel"]) == list(range(k))
+    assert out["ids"][0].cpu().tolist() == list(np.asarray(ref["ids"]))
+    assert rel_ok(out["z"][0].cpu().numpy(), ref["z"])
+    row = out["logits"][0].cpu().numpy()
+    assert int(out["argmax"][0]) == int(np.argmax(row))
 
 
 STEP_CASES = {
