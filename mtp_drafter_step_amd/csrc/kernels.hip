@@ -32,6 +32,10 @@ namespace {
 
 constexpr int kRG = kRowGroup;
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -384,11 +388,11 @@ __global__ __launch_bounds__(256) void k_ffn(int B, int F, Residual res, const u
     const size_t per = ((total + nblk - 1) / nblk + 3) & ~(size_t)3;
     const size_t a = fill.begin + bid * per;
     const size_t e = a + per < fill.end ? a + per : fill.end;
-    if (a < e) {
-      const float4 v = make_float4(-1e30f, -1e30f, -1e30f, -1e30f);
+    if (a < e) {  // streaming stores: the row is not read again in this kernel or the next
+      const f32x4 v = f32x4{-1e30f, -1e30f, -1e30f, -1e30f};
       size_t i = a + threadIdx.x * 4;
-      for (; i + 4 <= e; i += 1024) *reinterpret_cast<float4*>(fill.logits + i) = v;
-      for (; i < e; ++i) fill.logits[i] = -1e30f;
+      for (; i + 4 <= e; i += 1024) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(fill.logits + i));
+      for (; i < e; ++i) __builtin_nontemporal_store(-1e30f, fill.logits + i);
     }
   }
 }
@@ -649,9 +653,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
 //   online softmax on the S layout (lane l holds keys 4*(l/16)+r of head l%16);
 //   O[16 heads][256] += P . V with v_mfma_f32_16x16x16_bf16: P (split into bf16 hi + lo) is already in the A layout,
 //     V comes from the wave's LDS copy of the key tile read column-wise (4 keys of one dim per lane).
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 
 template <int G, int NW>
