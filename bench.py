@@ -37,7 +37,7 @@ COPY_PROBE_BYTES = 512 << 20
 
 # launch-site label (as recorded by the library's timing records) -> kernel symbol stem
 SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma", "attn_full": "k_attn_mfma",
-               "attn_merge_sliding": "k_attn_merge", "attn_merge_full": "k_attn_merge", "o_proj": "k_dense",
+               "o_proj": "k_oproj",
                "down": "k_dense", "ffn": "k_ffn", "post": "k_post", "head": "k_head", "final": "k_final",
                "scores": "k_dense", "fill": "k_fill"}
 
@@ -77,10 +77,8 @@ def site_bytes(site, shape, batch, lens, distinct_clusters):
     if site in ("attn_sliding", "attn_full"):
         keys = sum(L if site == "attn_full" else min(W, L) for L in lens)
         return shape.n_kv_head * hd * 2 * keys + 2 * hd + 2 * act(QD)
-    if site.startswith("attn_merge"):
-        return act(QD)
     if site == "o_proj":
-        return 2 * H * QD + act(QD) + act(H)
+        return 2 * H * QD + act(QD) + act(H) * (QD // 256)
     if site == "ffn":
         return 2 * 2 * F * H + 2 * H + 3 * act(H) + act(F) + 4 * shape.vocab * B // shape.n_layer
     if site == "down":

@@ -23,12 +23,15 @@ struct RowWindows {
 
 // Residual update applied in a dense kernel's prologue before its input norm:
 //   x_new = (x_old + RMSNorm(delta; w_delta)) * scale       (delta == nullptr: x_new = x_old)
+// where delta is the sum of nd partial vectors delta[p * dstride + b * H + i] (p < nd).
 struct Residual {
   const float* x_old;       // [B][H]
-  const float* delta;       // [B][H] or nullptr
+  const float* delta;       // [nd][B][H] or nullptr
   const uint16_t* w_delta;  // [H]
   float scale;
   float* x_new;             // [B][H], written by one block per row group (nullptr: not stored)
+  int nd;                   // partials in delta (1 .. 16)
+  size_t dstride;           // elements between consecutive partials
 };
 
 // Fill logits[begin, end) with -1e30 (spread over a kernel's blocks; no-op when logits is null).
@@ -68,11 +71,13 @@ hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const floa
                        float eps, const float* rope, int type, const uint16_t* K, const uint16_t* V, int cap,
                        const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, float* o);
 
-// Log-sum-exp merge of the split partials into o.
-hipError_t launch_attn_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
-                             float* o);
+// o_proj in QD / 256 partial sums: t[c][b][n] = sum over k in [256c, 256c + 256) of W[n][k] o[b][k], where o is
+// read directly (nsplit == 1) or merged from the attention's split partials (log-sum-exp over the splits of each
+// head). W [N][QD]; t [QD / 256][B][N]. The next kernel adds the partials up (Residual::nd).
+hipError_t launch_oproj(hipStream_t s, int B, int N, int QD, int hd, int nh, int nsplit, const float* o,
+                        const float* pacc, const float* pml, const uint16_t* W, float* t);
 
-// y[b] = W X[b] for fp32 X rows of width K (o_proj: K = n_head*head_dim, down: K = ffn), N outputs.
+// y[b] = W X[b] for fp32 X rows of width K (down: K = ffn; centroid scores: K = hidden), N outputs.
 hipError_t launch_dense(hipStream_t s, int B, int K, int N, const float* X, const uint16_t* w, float* y);
 
 // m[b] = gelu_tanh(W_g u) * (W_u u), u = RMSNorm(x_new; w_norm); also fills a slice of the logits.

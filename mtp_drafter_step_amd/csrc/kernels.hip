@@ -172,9 +172,11 @@ struct WaveW {
 };
 
 // Residual update + RMSNorm for the block's row group into LDS xs[kRG][H] (H = 64 NPL); one wave per row. Rows
-// beyond B are zero. Block column 0 stores x_new when res.x_new is set. Branch-free: the delta loads are always
-// issued (from x_old when there is no delta) and their effect selected afterwards.
-template <int NPL>
+// beyond B are zero. Block column 0 stores x_new when res.x_new is set. The delta is the sum of res.nd <= ND
+// partials (ND a power of two; the surplus loads are clamped to the last partial and weighted by zero).
+// Branch-free: the delta loads are always issued (from x_old when there is no delta) and their effect selected
+// afterwards.
+template <int NPL, int ND>
 __device__ __forceinline__ void prologue_norm(const Residual& res, const uint16_t* w_norm, float eps, int B,
                                               float* xs) {
   constexpr int H = NPL * 64;
@@ -184,15 +186,28 @@ __device__ __forceinline__ void prologue_norm(const Residual& res, const uint16_
   const bool hasd = res.delta != nullptr;
   const float* xo = res.x_old + (size_t)rr * H;
   const float* dr = hasd ? res.delta + (size_t)rr * H : xo;
+  const size_t dst = hasd ? res.dstride : 0;
+  const int nd = hasd ? res.nd : 1;
   const uint16_t* wdp = hasd ? res.w_delta : w_norm;
-  float xv[NPL], dv[NPL];
+  float xv[NPL], dp[ND][NPL];
   uint16_t wv[NPL], wd[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     xv[j] = xo[lane + 64 * j];
-    dv[j] = dr[lane + 64 * j];
     wv[j] = w_norm[lane + 64 * j];
     wd[j] = wdp[lane + 64 * j];
+  }
+#pragma unroll
+  for (int p = 0; p < ND; ++p)
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) dp[p][j] = dr[(size_t)min(p, nd - 1) * dst + lane + 64 * j];
+  float dv[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    float a = dp[0][j];
+#pragma unroll
+    for (int p = 1; p < ND; ++p) a += (p < nd) ? dp[p][j] : 0.f;
+    dv[j] = a;
   }
   float ss = 0.f;
 #pragma unroll
@@ -323,7 +338,7 @@ __global__ __launch_bounds__(256) void k_qproj(int B, int QD, Residual res, cons
   const int n0 = blockIdx.x * 16 + wave * 4;
   WaveW<4, H / 256> ww;
   ww.load(W, H, n0, QD);
-  prologue_norm<NPL>(res, w_norm, eps, B, &xs[0][0]);
+  prologue_norm<NPL, 1>(res, w_norm, eps, B, &xs[0][0]);
   __syncthreads();
   const float* xrow[kRG] = {xs[0], xs[1], xs[2], xs[3]};
   float acc[kRG * 4];
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(256) void k_dense(int B, int N, const float* __rest
 // GeGLU FFN input half ([MTP doc] "Tensor schema": ffn_norm, ffn_gate, ffn_up): grid (F / 16, ceil(B / 4)).
 // Each wave: 4 ffn indices x {gate, up} for the 4 rows. Blocks also fill their share of the logits row.
 
-template <int NPL>
+template <int NPL, int ND>
 __global__ __launch_bounds__(256) void k_ffn(int B, int F, Residual res, const uint16_t* __restrict__ w_norm,
                                              float eps, const uint16_t* __restrict__ Wg,
                                              const uint16_t* __restrict__ Wu, float* __restrict__ m,
@@ -371,7 +386,7 @@ __global__ __launch_bounds__(256) void k_ffn(int B, int F, Residual res, const u
   WaveW<4, H / 256> wg, wu;
   wg.load(Wg, H, f0, F);
   wu.load(Wu, H, f0, F);
-  prologue_norm<NPL>(res, w_norm, eps, B, &xs[0][0]);
+  prologue_norm<NPL, ND>(res, w_norm, eps, B, &xs[0][0]);
   __syncthreads();
   const float* xrow[kRG] = {xs[0], xs[1], xs[2], xs[3]};
   float ag[kRG * 4], au[kRG * 4];
@@ -414,7 +429,7 @@ __global__ __launch_bounds__(256) void k_post(int B, int Bb, int C, Residual res
   const bool cen = n0 >= Bb;  // Bb % 32 == 0: a block is wholly post_proj or wholly centroids
   WaveW<8, H / 256> ww;
   ww.load(cen ? Wc : Wp, H, cen ? n0 - Bb : n0, cen ? C : Bb);
-  prologue_norm<NPL>(res, w_out, eps, B, &xs[0][0]);
+  prologue_norm<NPL, 1>(res, w_out, eps, B, &xs[0][0]);
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < kRG * H; i += 256) {
@@ -857,33 +872,66 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   }
 }
 
-// grid (B * nh), 256 threads: thread d of head (b, h) merges the nsplit partials (nsplit <= NS <= 64). Each wave
-// reads the (max, sum) pairs with one load per lane (lane s: split s) and forms the merge weights there; the NS
-// partial values of a thread are loaded unconditionally from clamped slots and the surplus weighted by zero.
+// o_proj partial of chunk c = blockIdx.y of the attention output (dims [256c, 256c + 256)) for row b = blockIdx.z:
+// thread i first forms o[b][256c + i], either read directly (NS == 1: the attention wrote o) or merged from the
+// nsplit <= NS key-range partials of its head (log-sum-exp weights; the NS loads are issued unconditionally from
+// clamped slots and the surplus weighted by zero); then wave w computes outputs 64 bx + 16 w .. +16 over the chunk
+// ([MTP doc] "Tensor schema": attn_output). grid (ceil(N / 64), QD / 256, B), 256 threads. (No restrict on the
+// loaded arrays: it would let their loads sink below the issue barrier.)
 template <int NS>
-__global__ __launch_bounds__(256) void k_attn_merge(int hd, int nsplit, const float* pacc, const float* pml,
-                                                    float* __restrict__ o) {  // (no restrict on the inputs: it
-                                                                             // would let the loads sink below the
-                                                                             // issue barrier)
-  const size_t base = (size_t)blockIdx.x * kMaxSplit;
-  const int lane = lane_id();
-  const int d = min((int)threadIdx.x, hd - 1);
-  float a[NS];
+__global__ __launch_bounds__(256) void k_oproj(int N, int QD, int hd, int nh, int nsplit, const float* o,
+                                               const float* pacc, const float* pml, const uint16_t* W,
+                                               float* __restrict__ t) {
+  __shared__ __attribute__((aligned(16))) float os[256];
+  const int wave = wave_id(), lane = lane_id();
+  const int c = blockIdx.y, b = blockIdx.z;
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int k0 = c * 256;
+  uint2 w[16];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) a[s] = pacc[(base + (size_t)min(s, nsplit - 1)) * hd + d];
-  const float2 ml = *reinterpret_cast<const float2*>(pml + (base + (size_t)min(lane, nsplit - 1)) * 2);
-  asm volatile("" ::: "memory");  // every load above is issued before the first wait
-  __builtin_amdgcn_sched_barrier(0);
-  const float mv = lane < nsplit ? ml.x : -INFINITY;
-  float M = mv;
+  for (int q = 0; q < 16; ++q) w[q] = *reinterpret_cast<const uint2*>(W + (size_t)min(n0 + q, N - 1) * QD + k0 + lane * 4);
+  const int d = k0 + (int)threadIdx.x;
+  const int h = d / hd, dh = d - h * hd;
+  float val;
+  if constexpr (NS == 1) {
+    val = o[(size_t)b * QD + d];
+  } else {
+    const size_t base = ((size_t)b * nh + h) * kMaxSplit;
+    float a[NS];
+    float2 ml[NS];
 #pragma unroll
-  for (int of = 32; of > 0; of >>= 1) M = fmaxf(M, __shfl_xor(M, of, 64));
-  const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
-  const float L = wave_sum(ml.y * f);
-  float A = 0.f;
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const size_t sc = base + (size_t)min(s2, nsplit - 1);
+      a[s2] = pacc[sc * hd + dh];
+      ml[s2] = *reinterpret_cast<const float2*>(pml + sc * 2);
+    }
+    asm volatile("" ::: "memory");  // every load above issued before the first wait
+    __builtin_amdgcn_sched_barrier(0);
+    float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) A = fmaf(a[s], readlane_f(f, s), A);
-  if ((int)threadIdx.x < hd) o[(size_t)blockIdx.x * hd + d] = (L > 0.f) ? A / L : 0.f;
+    for (int s2 = 0; s2 < NS; ++s2) M = fmaxf(M, s2 < nsplit ? ml[s2].x : -INFINITY);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const float f = (s2 >= nsplit || ml[s2].x == -INFINITY) ? 0.f : exp2f(ml[s2].x - M);
+      L = fmaf(ml[s2].y, f, L);
+      A = fmaf(a[s2], f, A);
+    }
+    val = (L > 0.f) ? A / L : 0.f;
+  }
+  os[threadIdx.x] = val;
+  __syncthreads();
+  const float4 xv = *reinterpret_cast<const float4*>(os + lane * 4);
+  float acc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    float wf[4];
+    unpack4(w[q], wf);
+    acc[q] = fmaf(xv.x, wf[0], fmaf(xv.y, wf[1], fmaf(xv.z, wf[2], xv.w * wf[3])));
+  }
+  XR<16, 32>::run(acc, lane);  // lane l holds output l >> 2 of the wave's 16
+  const int n = n0 + (lane >> 2);
+  if ((lane & 3) == 0 && n < N) t[((size_t)c * gridDim.z + b) * N + n] = acc[0];
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1208,7 +1256,21 @@ hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, con
 hipError_t launch_ffn(hipStream_t s, int B, int H, int F, Residual res, const uint16_t* w_norm, float eps,
                       const uint16_t* w_gate, const uint16_t* w_up, float* m, FillRange fill) {
   const dim3 grid((F + 15) / 16, row_groups(B));
-  MTPD_BY_NPL(H, return go(k_ffn<NPL>, grid, 256, 0, s, B, F, res, w_norm, eps, w_gate, w_up, m, fill))
+  const int nd = res.delta ? res.nd : 1;
+#define MTPD_FFN(ND_) \
+  MTPD_BY_NPL(H, return go(k_ffn<NPL, ND_>, grid, 256, 0, s, B, F, res, w_norm, eps, w_gate, w_up, m, fill))
+  if (nd <= 1) {
+    MTPD_FFN(1)
+  } else if (nd <= 2) {
+    MTPD_FFN(2)
+  } else if (nd <= 4) {
+    MTPD_FFN(4)
+  } else if (nd <= 8) {
+    MTPD_FFN(8)
+  } else {
+    MTPD_FFN(16)
+  }
+#undef MTPD_FFN
 }
 
 hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res, const uint16_t* w_out, float eps,
@@ -1249,13 +1311,17 @@ hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const floa
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
-                             float* o) {
-  if (nsplit <= 2) return go(k_attn_merge<2>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
-  if (nsplit <= 4) return go(k_attn_merge<4>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
-  if (nsplit <= 8) return go(k_attn_merge<8>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
-  if (nsplit <= 16) return go(k_attn_merge<16>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
-  return go(k_attn_merge<32>, B * nh, 256, 0, s, hd, nsplit, pacc, pml, o);
+hipError_t launch_oproj(hipStream_t s, int B, int N, int QD, int hd, int nh, int nsplit, const float* o,
+                        const float* pacc, const float* pml, const uint16_t* W, float* t) {
+  const dim3 grid((N + 63) / 64, QD / 256, B);
+#define MTPD_OPROJ(NS_) return go(k_oproj<NS_>, grid, 256, 0, s, N, QD, hd, nh, nsplit, o, pacc, pml, W, t)
+  if (nsplit <= 1) MTPD_OPROJ(1);
+  if (nsplit <= 2) MTPD_OPROJ(2);
+  if (nsplit <= 4) MTPD_OPROJ(4);
+  if (nsplit <= 8) MTPD_OPROJ(8);
+  if (nsplit <= 16) MTPD_OPROJ(16);
+  MTPD_OPROJ(32);
+#undef MTPD_OPROJ
 }
 
 hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,

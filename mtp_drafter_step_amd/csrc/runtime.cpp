@@ -108,7 +108,7 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.pacc = take((size_t)B * c.n_head * mtpd::kMaxSplit * c.head_dim * 4);
   p.pml = take((size_t)B * c.n_head * mtpd::kMaxSplit * 2 * 4);
   p.o = take((size_t)B * QD * 4);
-  p.t = take((size_t)B * H * 4);
+  p.t = take((size_t)(QD / 256) * B * H * 4);  // o_proj partials [QD / 256][B][H]
   p.m = take((size_t)B * F * 4);
   p.d = take((size_t)B * H * 4);
   p.h = take((size_t)B * H * 4);
@@ -273,21 +273,20 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
     const mtpd_layer& L = h->layers[l];
     const int type = ((c.full_attn_layers >> l) & 1u) ? 1 : 0;
     const mtpd_kv& cache = type ? kv->full : kv->sliding;
-    mtpd::Residual rq{x[cur], nullptr, nullptr, 1.0f, nullptr};
+    mtpd::Residual rq{x[cur], nullptr, nullptr, 1.0f, nullptr, 1, 0};
     if (l > 0) {
       const mtpd_layer& P = h->layers[l - 1];
-      rq = mtpd::Residual{x[cur], d, P.post_ffw_norm, P.layer_output_scale, x[cur ^ 1]};
+      rq = mtpd::Residual{x[cur], d, P.post_ffw_norm, P.layer_output_scale, x[cur ^ 1], 1, 0};
       cur ^= 1;
     }
     KLAUNCH(h, "qproj", mtpd::launch_qproj(s, B, H, QD, rq, L.attn_norm, c.rms_eps, L.attn_q, q));
     KLAUNCH(h, type ? "attn_full" : "attn_sliding", mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
                              cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale,
                              at<float>(ws, p.pacc), at<float>(ws, p.pml), o));
-    if (nsplit[type] > 1)
-      KLAUNCH(h, type ? "attn_merge_full" : "attn_merge_sliding", mtpd::launch_attn_merge(s, B, c.n_head, c.head_dim, nsplit[type], at<float>(ws, p.pacc),
-                                     at<float>(ws, p.pml), o));
-    KLAUNCH(h, "o_proj", mtpd::launch_dense(s, B, QD, H, o, L.attn_output, t));
-    mtpd::Residual rf{x[cur], t, L.post_attention_norm, 1.0f, x[cur ^ 1]};
+    // o_proj in QD / 256 partials, merging the split attention partials on the way in
+    KLAUNCH(h, "o_proj", mtpd::launch_oproj(s, B, H, QD, c.head_dim, c.n_head, nsplit[type], o, at<float>(ws, p.pacc),
+                                            at<float>(ws, p.pml), L.attn_output, t));
+    mtpd::Residual rf{x[cur], t, L.post_attention_norm, 1.0f, x[cur ^ 1], QD / 256, (size_t)B * H};
     cur ^= 1;
     mtpd::FillRange fr{nullptr, 0, 0};
     if (logits)
@@ -296,7 +295,7 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
     KLAUNCH(h, "down", mtpd::launch_dense(s, B, F, H, m, L.ffn_down, d));
   }
   const mtpd_layer& Last = h->layers[nL - 1];
-  mtpd::Residual rp{x[cur], d, Last.post_ffw_norm, Last.layer_output_scale, nullptr};
+  mtpd::Residual rp{x[cur], d, Last.post_ffw_norm, Last.layer_output_scale, nullptr, 1, 0};
   // output norm, post_projection (the next step's hidden input, [Guide] section 6) and centroid scores
   KLAUNCH(h, "post", mtpd::launch_post(s, B, H, Bb, c.n_centroids, rp, h->w.output_norm, c.rms_eps, h->w.post_proj,
                            h->w.centroids, at<float>(ws, p.h), hidden_out, at<float>(ws, p.scores)));
