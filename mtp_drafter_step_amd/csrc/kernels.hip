@@ -950,7 +950,7 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
                                               float* __restrict__ logits, size_t V, uint64_t* __restrict__ keys) {
   constexpr int H = HCH * 128;
   constexpr int HPT = (H + 255) / 256;  // hidden elements per thread
-  __shared__ uint32_t hist[4][256];  // one histogram per wave (fewer same-address atomics), summed by the scan
+  __shared__ uint32_t hist[2][4][256];  // per wave (fewer same-address atomics), double-buffered
   __shared__ uint32_t sh_digit, sh_before, sh_n;
   __shared__ uint64_t cand[kMaxCentroids];
   __shared__ int sh_c;
@@ -975,20 +975,21 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
   for (int i = 0; i < NPT; ++i) ok[i] = f32_order(sv[i]);
 
   // Slot j holds the (j+1)-th element in descending (score, then ascending index) order. Radix select on the order
-  // keys, 8 bits at a time from the top, narrows the search to the digit bin that holds that rank; as soon as the
-  // bin has at most 64 members they are sorted by one wave (key, then index) and the rank read off. After all four
-  // passes the bin is the set of elements tied with the exact key, ordered by index the same way.
+  // keys, 8 bits at a time from the top, narrows the search to the digit bin that holds that rank; once the bin
+  // holds a single element, that element is the answer. Only elements tied with the exact key (bin still larger
+  // than one after all four passes) need ordering by index, below. Histograms are double-buffered so that a pass
+  // takes two barriers: the scan wave reads one buffer while the others clear the next.
   uint32_t prefix = 0, pmask = 0;
   uint32_t need = (uint32_t)j + 1u;
+  uint32_t inbin = 0;
+  hist[0][0][tid] = hist[0][1][tid] = hist[0][2][tid] = hist[0][3][tid] = 0u;
+  __syncthreads();
+  int buf = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[0][tid] = 0u;
-    hist[1][tid] = 0u;
-    hist[2][tid] = 0u;
-    hist[3][tid] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
-      if (tid + 256 * i < C && (ok[i] & pmask) == prefix) atomicAdd(&hist[wave][(ok[i] >> shift) & 255u], 1u);
+      if (tid + 256 * i < C && (ok[i] & pmask) == prefix)
+        atomicAdd(&hist[buf][wave][(ok[i] >> shift) & 255u], 1u);
     __syncthreads();
     if (wave == 0) {
       // lane l owns digits 255-4l .. 252-4l (descending)
@@ -996,7 +997,7 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
         const int dg = 255 - 4 * lane - q2;
-        cnt[q2] = hist[0][dg] + hist[1][dg] + hist[2][dg] + hist[3][dg];
+        cnt[q2] = hist[buf][0][dg] + hist[buf][1][dg] + hist[buf][2][dg] + hist[buf][3][dg];
         sum += cnt[q2];
       }
       uint32_t incl = sum;  // inclusive prefix over lanes (higher digits first)
@@ -1015,16 +1016,26 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
         }
         before += cnt[q2];
       }
+    } else {
+      const int ow = wave - 1;  // waves 1-3 clear the other buffer (all four wave histograms)
+      for (int i = ow * 64 + lane; i < 4 * 256; i += 3 * 64) (&hist[buf ^ 1][0][0])[i] = 0u;
     }
     __syncthreads();
     prefix |= sh_digit << shift;
     pmask |= 255u << shift;
     need -= sh_before;
-    const uint32_t inbin = sh_n;
-    __syncthreads();
-    if (inbin <= 64u || shift == 0) break;
+    inbin = sh_n;
+    buf ^= 1;
+    if (inbin == 1u) break;
   }
+  if (inbin == 1u) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (tid + 256 * i < C && (ok[i] & pmask) == prefix) sh_c = tid + 256 * i;
+    __syncthreads();
+  } else {
   // the bin's members as (key, ~index) composites: descending composite order is the slot order
+  __syncthreads();  // every wave has read the last bin count
   if (tid == 0) sh_n = 0u;
   __syncthreads();
 #pragma unroll
@@ -1062,6 +1073,7 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
     }
   }
   __syncthreads();
+  }
   const int c = sh_c;
   if (tid == 0 && sel) sel[(size_t)b * k + j] = c;
 
