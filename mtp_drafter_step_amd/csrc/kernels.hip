@@ -50,11 +50,6 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // order-preserving map of fp32 onto uint32 (larger float -> larger integer)
 __device__ __forceinline__ uint32_t f32_order(float f) {
@@ -92,25 +87,80 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 // Butterfly transpose-reduction of V per-lane values over lanes differing in bits O, O/2, ..., 1. Afterwards v[0]
 // of lane l holds the sum over those lanes of the value whose index is given by the lane bits consumed by the
 // halving steps (the highest bit first).
+//
+// The exchanges stay in the vector ALU: lanes 32 apart and 16 apart swap through v_permlane32_swap /
+// v_permlane16_swap applied to the value pair itself (the swap leaves each lane its own kept value and its
+// partner's, so one add finishes the step); within rows of 16 lanes DPP moves supply the partner: a rotation by 8
+// (the partner 8 away), the half-row mirror (lane i <-> 7 - i: opposite bit 2, and the two later steps over bits 1
+// and 0 still cover all eight lanes), and quad permutations for bits 1 and 0.
+template <int O>
+__device__ __forceinline__ float xr_partner(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (O == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  if constexpr (O == 4) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false));  // half mirror
+  if constexpr (O == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false));   // [2,3,0,1]
+  if constexpr (O == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false));   // [1,0,3,2]
+  if constexpr (O == 32 || O == 16) {
+    // swapping a value with itself leaves each lane its own value and its partner's, in the slot set by the lane
+    // bit O
+    const unsigned u = __float_as_uint(v);
+    if constexpr (O == 32) {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+    } else {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+    }
+  }
+  return v;
+}
+
+// (lo, hi) pair step over lanes O apart for O = 32 / 16: returns, per lane, the kept value plus the partner's
+template <int O>
+__device__ __forceinline__ float xr_swap_sum(float lo, float hi) {
+  const unsigned a = __float_as_uint(lo), c = __float_as_uint(hi);
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, c, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, c, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 template <int V, int O>
 struct XR {
   static __device__ __forceinline__ void run(float* v, int lane) {
     if constexpr (V > 1) {
       constexpr int H = V / 2;
-      const bool up = (lane & O) != 0;
+      if constexpr (O == 32 || O == 16) {
 #pragma unroll
-      for (int i = 0; i < H; ++i) {
-        const float send = up ? v[i] : v[i + H];
-        const float keep = up ? v[i + H] : v[i];
-        v[i] = keep + __shfl_xor(send, O, 64);
+        for (int i = 0; i < H; ++i) v[i] = xr_swap_sum<O>(v[i], v[i + H]);
+      } else {
+        const bool up = (lane & O) != 0;
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          const float send = up ? v[i] : v[i + H];
+          const float keep = up ? v[i + H] : v[i];
+          v[i] = keep + xr_partner<O>(send);
+        }
       }
       if constexpr (O > 1) XR<H, O / 2>::run(v, lane);
     } else {
-      v[0] += __shfl_xor(v[0], O, 64);
+      if constexpr (O == 32 || O == 16)
+        v[0] = xr_swap_sum<O>(v[0], v[0]);
+      else
+        v[0] += xr_partner<O>(v[0]);
       if constexpr (O > 1) XR<1, O / 2>::run(v, lane);
     }
   }
 };
+
+// Sum over the wave, left in every lane (the exchanges of XR, with nothing to transpose).
+__device__ __forceinline__ float wave_sum(float v) {
+  XR<1, 32>::run(&v, 0);
+  return v;
+}
 
 __device__ __forceinline__ void unpack4(uint2 w, float* f) {
   f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
@@ -679,6 +729,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
                                                           int nsplit, float scale_log2, float* __restrict__ pacc,
                                                           float* __restrict__ pml, float* __restrict__ o) {
   constexpr int HD = 256, KSTEPS = HD / 32, TILES = HD / 16, LROW = HD + 8, S = NW * 16;
+  static_assert(G >= 1 && G <= 4, "the heads of a kv group sit in lanes 0..G-1 of the score tile");
   __shared__ float qs[G][HD];
   __shared__ __attribute__((aligned(16))) uint16_t qop[KSTEPS][2][G][4][8];  // [step][hi/lo][head][kq][8 dims]
   __shared__ __attribute__((aligned(16))) uint16_t vt[NW][16][LROW];
@@ -734,7 +785,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
     for (int e = 0; e < 4; ++e) v[e] = v[e] * r * wq[e];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float partner = __shfl_xor(v[e], 32, 64);
+      const float partner = xr_partner<32>(v[e]);
       const float rot = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
       if (wave < G) qs[hh][lane * 4 + e] = rot;
     }
@@ -790,8 +841,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = (4 * kq + r < nk && hq < G) ? sacc[r] * scale_log2 : -INFINITY;
     float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = fmaxf(mt, xr_partner<16>(mt));
+    mt = fmaxf(mt, xr_partner<32>(mt));
     const float mn = fmaxf(mrun, mt);
     const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
     float pv[4], ps = 0.f;
@@ -800,8 +851,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
       pv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
       ps += pv[r];
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps += xr_partner<16>(ps);
+    ps += xr_partner<32>(ps);
     lrun = lrun * alpha + ps;
     mrun = mn;
     i16x4 phi, plo;
@@ -814,7 +865,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
     // rescale the accumulators: D rows are heads 4kq + r, whose alpha lives in lane 4kq + r
     float al[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * kq + r, 64);
+    for (int r = 0; r < 4; ++r) al[r] = readlane_f(alpha, r);  // heads 0-3 (G <= 4): lanes 0-3; other D rows are padding
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       i16x4 vb;
