@@ -933,6 +933,7 @@ template <int NS>
 __global__ __launch_bounds__(256) void k_oproj(int N, int QD, int hd, int nh, int nsplit, const float* o,
                                                const float* pacc, const float* pml, const uint16_t* W,
                                                float* __restrict__ t) {
+  static_assert(NS >= 1 && NS <= 64, "one (max, sum) pair per lane");
   __shared__ __attribute__((aligned(16))) float os[256];
   const int wave = wave_id(), lane = lane_id();
   const int c = blockIdx.y, b = blockIdx.z;
@@ -947,27 +948,28 @@ __global__ __launch_bounds__(256) void k_oproj(int N, int QD, int hd, int nh, in
   if constexpr (NS == 1) {
     val = o[(size_t)b * QD + d];
   } else {
+    // a wave's 64 dims lie in one head (head_dim is a multiple of 64): lane s reads split s's (max, sum) pair,
+    // the wave forms the merge weights, and each thread takes them by lane index
     const size_t base = ((size_t)b * nh + h) * kMaxSplit;
     float a[NS];
-    float2 ml[NS];
 #pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) {
-      const size_t sc = base + (size_t)min(s2, nsplit - 1);
-      a[s2] = pacc[sc * hd + dh];
-      ml[s2] = *reinterpret_cast<const float2*>(pml + sc * 2);
-    }
+    for (int s2 = 0; s2 < NS; ++s2) a[s2] = pacc[(base + (size_t)min(s2, nsplit - 1)) * hd + dh];
+    const float2 ml = *reinterpret_cast<const float2*>(pml + (base + (size_t)min(lane, nsplit - 1)) * 2);
     asm volatile("" ::: "memory");  // every load above issued before the first wait
     __builtin_amdgcn_sched_barrier(0);
-    float M = -INFINITY;
+    const float mv = lane < nsplit ? ml.x : -INFINITY;
+    float M = mv;
+    M = fmaxf(M, xr_partner<32>(M));
+    M = fmaxf(M, xr_partner<16>(M));
+    M = fmaxf(M, xr_partner<8>(M));
+    M = fmaxf(M, xr_partner<4>(M));
+    M = fmaxf(M, xr_partner<2>(M));
+    M = fmaxf(M, xr_partner<1>(M));
+    const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
+    const float L = wave_sum(ml.y * f);
+    float A = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) M = fmaxf(M, s2 < nsplit ? ml[s2].x : -INFINITY);
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) {
-      const float f = (s2 >= nsplit || ml[s2].x == -INFINITY) ? 0.f : exp2f(ml[s2].x - M);
-      L = fmaf(ml[s2].y, f, L);
-      A = fmaf(a[s2], f, A);
-    }
+    for (int s2 = 0; s2 < NS; ++s2) A = fmaf(a[s2], readlane_f(f, s2), A);
     val = (L > 0.f) ? A / L : 0.f;
   }
   os[threadIdx.x] = val;
