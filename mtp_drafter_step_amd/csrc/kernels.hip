@@ -733,8 +733,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   __shared__ float qs[G][HD];
   __shared__ __attribute__((aligned(16))) uint16_t qop[KSTEPS][2][G][4][8];  // [step][hi/lo][head][kq][8 dims]
   __shared__ __attribute__((aligned(16))) uint16_t vt[NW][16][LROW];
-  __shared__ float wml[NW][G][2];
-  __shared__ float wacc[NW][G][HD];
+  __shared__ __attribute__((aligned(16))) float wml[NW][G][2];
+  __shared__ __attribute__((aligned(16))) float wacc[NW][HD][4];  // [wave][dim][head]
+  static_assert(NW * 64 == HD, "one thread per dim in the combine");
   const int sp = blockIdx.x, bg = blockIdx.y;
   const int b = bg / nkv, g = bg % nkv;
   const int wave = wave_id(), lane = lane_id();
@@ -881,43 +882,53 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) ka[c] = kn[c];
   }
-  // combine the waves of this block: head h's state is in lane h; its output row in lanes 0-15 (kq = 0), slot h
+  // combine the waves of this block: head h's softmax state is in lane h; the output rows sit in lanes 0-15
+  // (kq = 0): dim 16t + lane, heads in the four registers of acc[t], stored as one float4 per dim
   if (lane < G) {
     wml[wave][lane][0] = mrun;
     wml[wave][lane][1] = lrun;
   }
   if (kq == 0) {
 #pragma unroll
-    for (int t = 0; t < TILES; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r < G) wacc[wave][r][16 * t + hq] = acc[t][r];
+    for (int t = 0; t < TILES; ++t) *reinterpret_cast<f32x4*>(&wacc[wave][16 * t + hq][0]) = acc[t];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < G * HD; i += NW * 64) {
-    const int hh = i / HD, d = i % HD;
-    float M = -INFINITY;
+  {
+    // thread d: dim d of the G heads over the NW waves
+    const int d = threadIdx.x;
+    f32x4 av[NW];
+    float2 ml[NW][G];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, wml[w][hh][0]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
+    for (int w = 0; w < NW; ++w) {
+      av[w] = *reinterpret_cast<const f32x4*>(&wacc[w][d][0]);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) ml[w][hh] = *reinterpret_cast<const float2*>(&wml[w][hh][0]);
+    }
+    asm volatile("" ::: "memory");  // all LDS reads issued before the arithmetic
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[w][hh].x);
+      float L = 0.f, A = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = wml[w][hh][0];
+        const float mw = ml[w][hh].x;
         const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        L = fmaf(wml[w][hh][1], f, L);
-        A = fmaf(wacc[w][hh][d], f, A);
+        L = fmaf(ml[w][hh].y, f, L);
+        A = fmaf(av[w][hh], f, A);
       }
-    }
-    const size_t hqq = (size_t)b * nh + g * G + hh;
-    if (nsplit == 1) {
-      o[hqq * HD + d] = (L > 0.f) ? A / L : 0.f;
-    } else {
-      const size_t slot = hqq * kMaxSplit + sp;
-      pacc[slot * HD + d] = A;
-      if (d == 0) {
-        pml[slot * 2 + 0] = M;
-        pml[slot * 2 + 1] = L;
+      const size_t hqq = (size_t)b * nh + g * G + hh;
+      if (nsplit == 1) {
+        o[hqq * HD + d] = (L > 0.f) ? A / L : 0.f;
+      } else {
+        const size_t slot = hqq * kMaxSplit + sp;
+        pacc[slot * HD + d] = A;
+        if (d == 0) {
+          pml[slot * 2 + 0] = M;
+          pml[slot * 2 + 1] = L;
+        }
       }
     }
   }
