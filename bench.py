@@ -237,6 +237,21 @@ def run_bench(args):
                          "sites": sorted(set(v["sites"]))}
                      for k, v in sorted(per_kernel.items(), key=lambda kv_: -kv_[1]["total_ms"])}
 
+    # cold regime: before each timed call a 1 GiB read sweep evicts L2 and the memory-side cache (the first drafter
+    # step of the block starts cold; the next three run on what it brought in)
+    sweep = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    cold_ms = []
+    for _ in range(args.cold_steps):
+        sweep.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(e0.elapsed_time(e1))
+    del sweep
+    us_cold = float(np.median(cold_ms)) * 1e3 / n
+
     if args.copy_probe:
         # calibration copy of known size for the HBM byte counters (a plain device-to-device copy)
         src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
@@ -267,7 +282,9 @@ def run_bench(args):
         "step_roofline": {"algorithmic_bytes_per_drafter_step": sbytes, "parts": parts,
                           "distinct_clusters_per_step": U,
                           "achieved_GBs": sbytes / (us_drafter_step * 1e-6) / 1e9,
-                          "frac": sbytes / (us_drafter_step * 1e-6) / 1e9 / HBM_PEAK_GBS},
+                          "frac": sbytes / (us_drafter_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "cold_us_per_drafter_step": us_cold,
+                          "cold_achieved_GBs": sbytes / (us_cold * 1e-6) / 1e9},
         "kernels": kernels_table,
         "kernel_source_sha256_16": source_digest(),
     }
@@ -370,6 +387,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--timing-steps", type=int, default=10, help="calls timed per kernel after the timed region")
+    ap.add_argument("--cold-steps", type=int, default=10, help="calls timed after a cache-evicting sweep each")
     ap.add_argument("--workload", default="e4b_b16_ctx8192_block4")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
