@@ -51,7 +51,12 @@ class DrafterShape:
 
     @property
     def vsc(self) -> int:
-        return self.vocab // self.n_centroids
+        """Tokens per cluster of the masked head (0 for the dense tied head, n_centroids == 0)."""
+        return self.vocab // self.n_centroids if self.n_centroids else 0
+
+    @property
+    def dense_head(self) -> bool:
+        return self.n_centroids == 0
 
     @property
     def q_dim(self) -> int:
@@ -79,6 +84,10 @@ class Workload:
 
 E2B = DrafterShape(backbone=1536)
 E4B = DrafterShape(backbone=2560)
+# 26B-A4B-shaped drafter with the dense tied head (no centroids): backbone 2816, hidden 1024, 8 query heads of 256
+# over one shared K=V head, FFN 4096, sliding window 1024
+E26B = DrafterShape(backbone=2816, hidden=1024, n_head=8, n_kv_head=1, head_dim=256, ffn=4096, n_centroids=0, top_k=1,
+                    swa_window=1024)
 
 WORKLOADS: Dict[str, Workload] = {
     # E2B-shaped drafter, one step, batch 1, shared KV context 256
@@ -87,11 +96,14 @@ WORKLOADS: Dict[str, Workload] = {
     "e2b_b1_ctx4096_block4": Workload("e2b_b1_ctx4096_block4", E2B, batch=1, context=4096, n_steps=4),
     # E4B-shaped drafter, batch 16 independent sequences, context 8192 each, draft_block 4
     "e4b_b16_ctx8192_block4": Workload("e4b_b16_ctx8192_block4", E4B, batch=16, context=8192, n_steps=4),
+    # 26B-A4B-shaped drafter with the dense head, batch 32, context 32768 each, draft_block 4
+    "e26b_b32_ctx32768_block4": Workload("e26b_b32_ctx32768_block4", E26B, batch=32, context=32768, n_steps=4),
 }
 
 # small shapes for fast CPU checks and multi-tile / ragged GPU parity cases
 TINY = DrafterShape(backbone=64, hidden=32, n_layer=4, n_head=4, n_kv_head=1, head_dim=64, ffn=64, vocab=1024,
                     n_centroids=8, top_k=2, swa_window=16)
+TINY_DENSE = dataclasses.replace(TINY, n_centroids=0, top_k=1)
 
 # ----------------------------------------------------------------------------------------------------------------
 # counter-based generator
@@ -228,9 +240,10 @@ def make_weights(shape: DrafterShape, seed: int = 0, device="cpu") -> Dict[str, 
         "post_proj": gen_bf16(seed, TID["post_proj"], (Bb, H), 1.0 / math.sqrt(H), device=device),
         "output_norm": gen_bf16(seed, TID["output_norm"], (H,), 0.1, 1.0, device=device),
         "token_embd": gen_bf16(seed, TID["token_embd"], (shape.vocab, H), 0.02, device=device),
-        "centroids": gen_bf16(seed, TID["centroids"], (shape.n_centroids, H), 1.0 / math.sqrt(H), device=device),
-        "token_ordering": permutation(seed, TID["ordering"], shape.vocab).to(device),
     }
+    if not shape.dense_head:
+        w["centroids"] = gen_bf16(seed, TID["centroids"], (shape.n_centroids, H), 1.0 / math.sqrt(H), device=device)
+        w["token_ordering"] = permutation(seed, TID["ordering"], shape.vocab).to(device)
     layers = []
     for l in range(shape.n_layer):
         t = lambda n: layer_tid(l, n)  # noqa: E731

@@ -144,7 +144,12 @@ class Config:
 
     @property
     def vsc(self) -> int:
-        return self.vocab // self.n_centroids
+        """Tokens per cluster of the masked head; 0 for the dense tied head (n_centroids == 0)."""
+        return self.vocab // self.n_centroids if self.n_centroids else 0
+
+    @property
+    def dense(self) -> bool:
+        return self.n_centroids == 0
 
     def is_full(self, l: int) -> bool:
         return bool((self.full_attn_layers >> l) & 1)
@@ -179,10 +184,14 @@ class Model:
         self.pre = d(w["pre_proj"]).reshape(cfg.hidden, 2 * cfg.backbone)
         self.post = d(w["post_proj"]).reshape(cfg.backbone, cfg.hidden)
         self.out_norm = d(w["output_norm"])
-        self.cen = d(w["centroids"]).reshape(cfg.n_centroids, cfg.hidden)
         self.head_bits = _np16(w["token_embd"]).reshape(cfg.vocab, cfg.hidden)
-        self.ordering = np.asarray(_np32(w["token_ordering"]), dtype=np.int64)
-        check_head_invariants(cfg, self.ordering)
+        if cfg.dense:  # dense tied head: every token scored, no centroids or ordering
+            self.cen = None
+            self.ordering = None
+        else:
+            self.cen = d(w["centroids"]).reshape(cfg.n_centroids, cfg.hidden)
+            self.ordering = np.asarray(_np32(w["token_ordering"]), dtype=np.int64)
+            check_head_invariants(cfg, self.ordering)
         self.layers = []
         for lw in w["layers"]:
             self.layers.append({
@@ -292,9 +301,24 @@ def masked_head_row(m: Model, h: np.ndarray, want_row: bool = False) -> Dict[str
     return out
 
 
-def dense_head_row(m: Model, h: np.ndarray) -> np.ndarray:
-    """Dense tied head: logits over the whole vocabulary (the use_ordered_embeddings=false form)."""
-    return (bf16_to_f64(m.head_bits) @ h).astype(np.float32)
+def dense_head_row(m: Model, h: np.ndarray, chunk: int = 16384) -> np.ndarray:
+    """Dense tied head: logits over the whole vocabulary, token_embd . h for every token (the
+    use_ordered_embeddings=false form: [Guide] section 5; [MTP doc] "Variants supported": the large drafters tie
+    the full embedding as their head). Decoded in row chunks to bound host memory."""
+    out = np.empty(m.cfg.vocab, dtype=np.float32)
+    for a in range(0, m.cfg.vocab, chunk):
+        out[a:a + chunk] = (bf16_to_f64(m.head_bits[a:a + chunk]) @ h).astype(np.float32)
+    return out
+
+
+def dense_head_result(m: Model, h: np.ndarray) -> Dict[str, object]:
+    """The dense head's outputs in the form of masked_head_row's: the full fp32 row, its argmax (first occurrence:
+    lowest token id on ties) and the top-1 minus top-2 margin."""
+    row = dense_head_row(m, h)
+    nxt = int(np.argmax(row))
+    top2 = np.partition(row.astype(np.float64), -2)[-2:]
+    return {"scores": None, "sel": [], "ids": [], "z": [], "next": nxt, "cgap": np.inf,
+            "margin": float(top2[1] - top2[0]), "row": row}
 
 
 def drafter_step(m: Model, target_hidden, last_token, target_embd, kv: SharedKV, want_rows: bool = False,
@@ -324,7 +348,7 @@ def drafter_step(m: Model, target_hidden, last_token, target_embd, kv: SharedKV,
             x = decoder_layer(m, l, x, b, kv)
         h = rmsnorm(x, m.out_norm, cfg.rms_eps)
         res["hidden_out"][i] = bf16_bits(m.post @ h)  # handed back in bf16, the target's activation format
-        hd = masked_head_row(m, h, want_row=want_rows)
+        hd = dense_head_result(m, h) if cfg.dense else masked_head_row(m, h, want_row=want_rows)
         res["next"][i] = hd["next"]
         for k in ("sel", "ids", "z", "scores", "cgap", "margin"):
             res[k].append(hd[k])

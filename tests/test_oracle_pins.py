@@ -320,6 +320,48 @@ def test_step_rows_are_independent():
     assert one["next"][0] == full["next"][2]
 
 
+def test_dense_step_equals_masked_step_with_every_cluster():
+    """The dense tied head scores every token; the masked head with top_k = n_centroids also scores every token
+    (no -1e30 entries), so on the same weights the two steps must agree in hidden state, token and whole row."""
+    shape_m = __import__("dataclasses").replace(synth.TINY, top_k=synth.TINY.n_centroids)
+    wm = synth.make_weights(shape_m, seed=3)
+    wd = synth.make_weights(synth.TINY_DENSE, seed=3)
+    assert "centroids" not in wd and "token_ordering" not in wd
+    for k in wd:
+        if k != "layers":
+            assert torch.equal(wd[k], wm[k]), k
+    mm, md = O.Model(O.config_from(shape_m), wm), O.Model(O.config_from(synth.TINY_DENSE), wd)
+    wl, d, kv = _tiny_inputs(synth.TINY_DENSE, batch=4)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    tok = d["last_token"].numpy()
+    a = O.drafter_step(mm, th, tok, emb, kv, want_rows=True)
+    b = O.drafter_step(md, th, tok, emb, kv, want_rows=True)
+    assert np.array_equal(a["hidden_out"], b["hidden_out"])
+    assert np.array_equal(a["next"], b["next"])
+    for ra, rb, mg in zip(a["row"], b["row"], b["margin"]):
+        assert np.array_equal(ra, rb)
+        srt = np.sort(rb.astype(np.float64))
+        assert mg == srt[-1] - srt[-2]
+    assert all(len(x) == 0 for x in b["sel"]) and all(len(x) == 0 for x in b["ids"])
+
+
+def test_dense_head_one_hot_table_closed_form():
+    """Head row i = unit vector e_(i mod H): the logit of token i is h[i mod H]. The argmax is the first index of
+    max(h) (it recurs every H tokens; the lowest token id wins) and the top-1 minus top-2 margin is 0."""
+    m, w, shape = _tiny_model(n_centroids=0, top_k=1)
+    H, V = m.cfg.hidden, m.cfg.vocab
+    bits = np.zeros((V, H), np.uint16)
+    bits[np.arange(V), np.arange(V) % H] = 0x3F80  # bf16 1.0
+    m.head_bits = bits
+    for t in range(5):
+        h = O.round_bf16(rng(20 + t).standard_normal(H))
+        out = O.dense_head_result(m, h)
+        assert np.array_equal(out["row"], h[np.arange(V) % H].astype(np.float32))
+        assert out["next"] == int(np.argmax(h)) and out["next"] < H
+        assert out["margin"] == 0.0
+
+
 # ---------------------------------------------------------------- shapes named on the pages
 
 
@@ -340,6 +382,9 @@ def test_page_constants_against_workload_shapes():
         assert shape.top_k * shape.vsc == 4096  # finite logits per row
         # the pages quote about 76-78 M parameters; our FFN width (1024) gives ~74-75 M
         assert abs(_param_count(shape) - g["params_approx_e2b_e4b"]["value"]) < 0.06 * g["params_approx_e2b_e4b"]["value"]
+    assert synth.E26B.backbone == g["backbone_26b"]["value"]
+    assert synth.E26B.vocab == g["vocab"]["value"] and synth.E26B.n_layer == g["n_layer"]["value"]
+    assert synth.E26B.dense_head and synth.E26B.q_dim == 8 * 256
     assert synth.E2B.backbone == g["backbone_e2b"]["value"]
     assert synth.E4B.backbone == g["backbone_e4b"]["value"]
 
