@@ -1,6 +1,7 @@
 /*
  * mtpd.h - C ABI of the MI355X (gfx950) drafter-step library: one draft step of the Gemma 4 assistant
- * (multi-token-prediction drafter), a block of chained steps, and the centroid-clustered masked LM head.
+ * (multi-token-prediction drafter), a block of chained steps, and the LM head: centroid-clustered (masked) or
+ * dense (tied to the full embedding table).
  *
  * Pages cited (by title; sections as headed on each page):
  *   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
@@ -12,7 +13,7 @@
  *   - Tensors are DEVICE memory owned by the caller unless marked HOST. bf16 values are passed as their uint16_t
  *     bit patterns. Matrices are row-major [out][in] (the PyTorch nn.Linear layout, which is the GGUF [in, out]
  *     shape of the [MTP doc] "Tensor schema" read as ne0 = in). Device pointers must be 16-byte aligned.
- *   - Weights are borrowed by mtpd_create and must outlive the handle. The exception is the head table:
+ *   - Weights are borrowed by mtpd_create and must outlive the handle. The exception is the masked head's table:
  *     mtpd_create copies token_embd into cluster order (row r = token_embd[token_ordering[r]], vocab*hidden bf16
  *     of device memory owned by the handle), so later changes to token_embd or token_ordering are not seen.
  *   - Calls enqueue work on the caller's HIP stream (passed as void*, a hipStream_t; NULL = the null stream) and
@@ -56,9 +57,12 @@ typedef struct mtpd_handle_s *mtpd_handle;
 /* Drafter hyper-parameters. [MTP doc] "Conversion" (backbone_hidden_size, num_centroids,
  * centroid_intermediate_top_k), "Variants supported" (4 layers, hidden 256, KV heads); [Inventory]
  * "HF config highlights" (three sliding + one full layer, attention_k_eq_v, vocab 262144).
- * Rules checked by mtpd_create: all sizes > 0; vocab % n_centroids == 0; top_k <= min(n_centroids, 64);
- * n_head / n_kv_head in {1,2,4,8}; head_dim in {64,128,256}; hidden, backbone, ffn, n_head*head_dim multiples
- * of 256 (hidden <= 1024); vocab / n_centroids a multiple of 16, <= 1024; n_centroids <= 4096; n_layer <= 32. */
+ * Rules checked by mtpd_create: all sizes > 0 except n_centroids; n_head / n_kv_head in {1,2,4,8}; head_dim in
+ * {64,128,256}; hidden, backbone, ffn, n_head*head_dim multiples of 256 (hidden <= 1024); n_layer <= 32.
+ * Masked head (n_centroids > 0): vocab % n_centroids == 0; top_k <= min(n_centroids, 64); vocab / n_centroids a
+ * multiple of 16, <= 1024; n_centroids <= 4096.
+ * Dense tied head (n_centroids == 0: the use_ordered_embeddings=false form, [Guide] section 5; [MTP doc]
+ * "Variants supported" for the large drafters): top_k 0 or 1 (unused); vocab a multiple of 16. */
 typedef struct {
   int32_t backbone;          /* target model width (1536 E2B, 2560 E4B) */
   int32_t hidden;            /* drafter width (256) */
@@ -68,7 +72,7 @@ typedef struct {
   int32_t head_dim;
   int32_t ffn;               /* GeGLU intermediate width */
   int32_t vocab;
-  int32_t n_centroids;       /* clusters of the masked head (2048); 0 is rejected (dense head: MTPD_EUNSUP) */
+  int32_t n_centroids;       /* clusters of the masked head (2048); 0 selects the dense tied head */
   int32_t top_k;             /* clusters kept (32) */
   int32_t swa_window;        /* keys read by a sliding layer */
   uint32_t full_attn_layers; /* bit l set: layer l reads the full-attention cache, else the sliding one */
@@ -91,7 +95,8 @@ typedef struct {
  * pre_proj [hidden][2*backbone] (input = [target hidden ; token embedding]), post_proj [backbone][hidden],
  * output_norm [hidden], token_embd [vocab][hidden] (the head table), centroids [n_centroids][hidden],
  * token_ordering [vocab] int32, a permutation of the vocabulary viewed as [n_centroids][vocab/n_centroids]
- * ([Inventory] "Centroid / ordered embeddings LM head", step 3). layers is a HOST array [n_layer]. */
+ * ([Inventory] "Centroid / ordered embeddings LM head", step 3). centroids and token_ordering are not read (may
+ * be NULL) with the dense head. layers is a HOST array [n_layer]. */
 typedef struct {
   const uint16_t *pre_proj, *post_proj, *output_norm, *token_embd, *centroids;
   const int32_t *token_ordering;
@@ -115,10 +120,11 @@ typedef struct {
   const float *rope;
 } mtpd_shared_kv;
 
-/* Validate the configuration and weights and build a handle. Copies token_ordering to the host once (a blocking
- * copy on the null stream) to check that it is a permutation ([Inventory] "GGUF / converter layout",
- * verification script), then builds the cluster-ordered head table on the null stream and waits for it
- * (MTPD_ENOMEM if it does not fit). max_batch <= MTPD_MAX_BATCH. Returns MTPD_OK and *out, or a negative code. */
+/* Validate the configuration and weights and build a handle. With the masked head, copies token_ordering to the
+ * host once (a blocking copy on the null stream) to check that it is a permutation ([Inventory] "GGUF /
+ * converter layout", verification script), then builds the cluster-ordered head table on the null stream and
+ * waits for it (MTPD_ENOMEM if it does not fit); the dense head reads token_embd as given and allocates nothing.
+ * max_batch <= MTPD_MAX_BATCH. Returns MTPD_OK and *out, or a negative code. */
 MTPD_API int mtpd_create(const mtpd_config *cfg, const mtpd_weights *w, int32_t max_batch, mtpd_handle *out);
 
 /* Release a handle (NULL is a no-op). Does not touch caller memory. */
@@ -133,12 +139,13 @@ MTPD_API size_t mtpd_workspace_bytes(mtpd_handle h, int32_t batch);
  *   4 Q-only layers over the shared caches (sliding layers: the last min(window, len) keys; full: all len keys)
  *   h = output_norm(x); hidden_out = post_proj h (bf16)
  *   masked head: top_k of centroids.h, their vocab/n_centroids token ids through token_ordering, sparse logits
- *   token_embd[id].h, a -1e30 row with the sparse logits scattered in, next_token = argmax.
+ *   token_embd[id].h, a -1e30 row with the sparse logits scattered in, next_token = argmax;
+ *   dense head: the row is token_embd[v].h for every v, next_token = argmax (ties to the lowest id).
  * target_hidden [batch][backbone] bf16; last_token [batch] int32 in [0, vocab) (out-of-range ids are clamped
  * into range); target_embd [vocab][backbone] bf16 (the target's input embedding table).
  * Outputs: next_token [batch] int32, hidden_out [batch][backbone] bf16 (required); logits [batch][vocab] fp32,
  * sel_centroids [batch][top_k] int32 (descending score), sparse_ids / sparse_logits [batch][top_k*vsc]
- * (optional, NULL to skip). */
+ * (optional, NULL to skip; the last three must be NULL with the dense head: MTPD_EINVAL otherwise). */
 MTPD_API int mtpd_drafter_step(mtpd_handle h, void *stream, void *workspace, int32_t batch, const uint16_t *target_hidden,
                       const int32_t *last_token, const uint16_t *target_embd, const mtpd_shared_kv *kv,
                       float *logits, int32_t *next_token, uint16_t *hidden_out, int32_t *sel_centroids,
@@ -155,7 +162,9 @@ MTPD_API int mtpd_draft_block(mtpd_handle h, void *stream, void *workspace, int3
 
 /* The masked head alone on m rows of fp32 hidden states h [m][hidden] (normed, as the head receives them):
  * [Inventory] "Centroid / ordered embeddings LM head" steps 1-5. argmax [m] int32 required; logits [m][vocab],
- * sel_centroids [m][top_k], sparse_ids / sparse_logits [m][top_k*vsc] optional. m <= max_batch. */
+ * sel_centroids [m][top_k], sparse_ids / sparse_logits [m][top_k*vsc] optional. m <= max_batch.
+ * With n_centroids == 0 this is the dense tied head: logits [m][vocab] = token_embd . h (optional), argmax; the
+ * per-cluster outputs must be NULL. */
 MTPD_API int mtpd_masked_head(mtpd_handle h, void *stream, void *workspace, int32_t m, const float *hidden,
                      float *logits, int32_t *argmax, int32_t *sel_centroids, int32_t *sparse_ids,
                      float *sparse_logits);
@@ -169,7 +178,8 @@ MTPD_API int mtpd_timing_enable(mtpd_handle h, int32_t enable);
 
 /* Waits for the recorded events and copies min(cap, count) records in launch order: names[i] is a static label of
  * the launch site ("pre", "qproj", "attn_sliding", "attn_full", "attn_merge_sliding", "attn_merge_full",
- * "o_proj", "ffn", "down", "post", "head", "final", "scores", "fill"), ms[i] its duration in milliseconds.
+ * "o_proj", "ffn", "down", "post", "head", "head_dense", "zero_keys", "final", "scores", "fill"), ms[i] its
+ * duration in milliseconds.
  * names and ms are caller-owned host arrays of cap entries. Returns the number of records (which may exceed cap)
  * or a negative error code. */
 MTPD_API int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char **names, float *ms);

@@ -84,10 +84,19 @@ hipError_t launch_dense(hipStream_t s, int B, int K, int N, const float* X, cons
 hipError_t launch_ffn(hipStream_t s, int B, int H, int F, Residual res, const uint16_t* w_norm, float eps,
                       const uint16_t* w_gate, const uint16_t* w_up, float* m, FillRange fill);
 
-// h = RMSNorm(x_new; w_out) (stored to h_out); hidden_out = bf16(W_post h); scores = centroids h.
+// h = RMSNorm(x_new; w_out) (stored to h_out); hidden_out = bf16(W_post h); scores = centroids h (C may be 0);
+// keys_zero[0, B) = 0 when set (the dense head's atomic-max keys).
 hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res, const uint16_t* w_out, float eps,
                        const uint16_t* w_post, const uint16_t* w_cen, float* h_out, uint16_t* hidden_out,
-                       float* scores);
+                       float* scores, uint64_t* keys_zero);
+
+// Dense tied head: logits[b][v] = E[v] . h[b] for every v < V (when logits is set) and keys[b] = max(keys[b],
+// (value, id) key of the row's best token); keys must be zero beforehand. V % 16 == 0, H in {256, 512, 768, 1024}.
+hipError_t launch_head_dense(hipStream_t s, int B, int V, int H, const uint16_t* E, const float* h, float* logits,
+                             uint64_t* keys);
+
+// keys[0, n) = 0
+hipError_t launch_zero_keys(hipStream_t s, uint64_t* keys, int n);
 
 // Masked head: per (row, selected slot j): top-k of the row's centroid scores (descending, ties to the lower
 // index), the cluster's token ids through the ordering, sparse logits token_embd[id] . h (rows read from Es, the

@@ -65,6 +65,13 @@ __device__ __forceinline__ int32_t key_id(uint64_t k) { return (int32_t)(0xFFFFF
 
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// 16-byte load through the global address space: a generic (flat) load would also count against the LDS wait
+// counter, so a wait for LDS reads would drain the outstanding memory loads too
+__device__ __forceinline__ uint4 ld_global16(const void* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(p));
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -471,7 +478,8 @@ template <int NPL>
 __global__ __launch_bounds__(256) void k_post(int B, int Bb, int C, Residual res, const uint16_t* __restrict__ w_out,
                                               float eps, const uint16_t* __restrict__ Wp,
                                               const uint16_t* __restrict__ Wc, float* __restrict__ h_out,
-                                              uint16_t* __restrict__ hidden_out, float* __restrict__ scores) {
+                                              uint16_t* __restrict__ hidden_out, float* __restrict__ scores,
+                                              uint64_t* __restrict__ keys_zero) {
   constexpr int H = NPL * 64;
   __shared__ __attribute__((aligned(16))) float xs[kRG][H];
   const int wave = wave_id(), lane = lane_id();
@@ -486,6 +494,8 @@ __global__ __launch_bounds__(256) void k_post(int B, int Bb, int C, Residual res
       const int r = blockIdx.y * kRG + i / H;
       if (r < B) h_out[(size_t)r * H + i % H] = xs[0][i];
     }
+    // the dense head accumulates its argmax keys by atomic max from zero
+    if (keys_zero && threadIdx.x < kRG && blockIdx.y * kRG + threadIdx.x < B) keys_zero[blockIdx.y * kRG + threadIdx.x] = 0ull;
   }
   const float* xrow[kRG] = {xs[0], xs[1], xs[2], xs[3]};
   float acc[kRG * 8];
@@ -1197,6 +1207,195 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
   if (tid == 0) keys[(size_t)b * k + j] = u64_max(u64_max(red[0], red[1]), u64_max(red[2], red[3]));
 }
 
+// ------------------------------------------------------------------------------------------------------------
+// dense tied head: logits[b][v] = E[v] . h[b] for every token ([Guide] section 5: with use_ordered_embeddings off
+// the head is the plain tied embedding; [MTP doc] "Variants supported": the large drafters use it), and the row's
+// argmax folded into one (value, id) key per row by atomic max (keys must hold 0 beforehand).
+//
+// The table is streamed once per pass of up to 32 batch rows, as a GEMM on v_mfma_f32_16x16x32_bf16:
+//   A = 16 table rows x 32 dims, loaded straight from HBM (lane l: row l%16, 8 dims at 8*(l/16) of each 32-dim
+//       step, so each row's 64 contiguous bytes per step come from 4 lanes and two steps cover a 128-byte line);
+//   B = the pass's hidden states from LDS, each fp32 value split into bf16 hi + lo (h = hi + lo within 2^-16
+//       relative), two products per step, so the logits keep fp32-level accuracy;
+//   D = 16 rows x 16 batch columns: lane l holds rows 4*(l/16) .. +3 of column l%16.
+// A wave owns 32-row groups (two 16-row tiles) over the whole hidden dimension: no cross-wave reduction. Its loads
+// run in chunks of P steps, double-buffered, and the next group's first chunk is requested during the current
+// group's last chunk (from a clamped group index, so the issue count never depends on data).
+// grid (blocks, ceil(B / 32)), 1024 threads; NC = batch columns per pass (16 or 32), H = 256 * NPL.
+
+template <int NC, int NPL>
+__global__ __launch_bounds__(1024) void k_head_dense(int B, int V, const uint16_t* E, const float* h,
+                                                     float* __restrict__ logits, uint64_t* __restrict__ keys) {
+  constexpr int H = NPL * 256, KSTEPS = H / 32, LROW = H + 8, NBT = NC / 16;
+  // tiles per group, steps per chunk (fewer with 32 columns, whose operands take more registers), chunks per group
+  constexpr int RT = 2, P = NC == 32 ? 2 : 4, NCH = KSTEPS / P;
+  static_assert(NCH % 2 == 0, "chunks alternate between the two buffers");
+  constexpr int NW = 16;
+  __shared__ __attribute__((aligned(16))) uint16_t hs[2][NC][LROW];  // [hi / lo][column][dim], rows padded by 16 B
+  __shared__ uint64_t red[NW][NC];
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int c0 = blockIdx.y * NC;
+  const int ngroups = (V + 31) / 32;
+  const int gstride = gridDim.x * NW;
+  int grp = blockIdx.x * NW + wave;
+
+  // lane's pieces of row 32 gq + 16 r + n (clamped to V - 1) start at element 8 g4 of the row; step s adds 32 s.
+  // Offsets, not pointers, are carried between groups: pointers carried through the loop lose their global
+  // address space and become flat loads.
+  auto rows_of = [&](int gq, size_t (&ro)[RT]) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) ro[r] = (size_t)min(gq * 32 + r * 16 + n, V - 1) * H + 8 * g4;
+  };
+  auto load = [&](uint4 (&a)[P][RT], const size_t (&ro)[RT], int c) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) a[p][r] = ld_global16(E + ro[r] + (c * P + p) * 32);
+  };
+  uint4 a0[P][RT], a1[P][RT];
+  size_t rp[RT];
+  rows_of(min(grp, ngroups - 1), rp);
+  load(a0, rp, 0);
+
+  // stage the pass's hidden states as bf16 hi + lo (columns past B are zero)
+  constexpr int NV4 = NC * H / 4 / 1024;  // float4 per thread
+  static_assert(NV4 >= 1 && NC * H % 4096 == 0, "staging covers the columns exactly");
+  float4 hv[NV4];
+#pragma unroll
+  for (int i = 0; i < NV4; ++i) {
+    const int e = (tid + i * 1024) * 4, col = e / H, k = e % H;
+    const int b = min(c0 + col, B - 1);
+    hv[i] = *reinterpret_cast<const float4*>(h + (size_t)b * H + k);
+  }
+#pragma unroll
+  for (int i = 0; i < NV4; ++i) {
+    const int e = (tid + i * 1024) * 4, col = e / H, k = e % H;
+    const bool live = c0 + col < B;
+    const float f[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = live ? f[j] : 0.f;
+      hi[j] = f2bf(v);
+      lo[j] = f2bf(v - bf2f(hi[j]));
+    }
+    *reinterpret_cast<uint2*>(&hs[0][col][k]) =
+        make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2*>(&hs[1][col][k]) =
+        make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+  }
+  __syncthreads();
+
+  float best[NBT];
+  int bid[NBT];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    best[t] = -INFINITY;
+    bid[t] = -1;
+  }
+
+  auto compute = [&](const uint4 (&a)[P][RT], int c, f32x4 (&acc)[RT][NBT]) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int k = (c * P + p) * 32 + 8 * g4;
+      uint4 bh[NBT], bl[NBT];
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) {
+        bh[t] = *reinterpret_cast<const uint4*>(&hs[0][t * 16 + n][k]);
+        bl[t] = *reinterpret_cast<const uint4*>(&hs[1][t * 16 + n][k]);
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < NBT; ++t)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[p][r]),
+                                                              __builtin_bit_cast(bf16x8, bh[t]), acc[r][t], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < NBT; ++t)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[p][r]),
+                                                              __builtin_bit_cast(bf16x8, bl[t]), acc[r][t], 0, 0, 0);
+    }
+  };
+
+  while (grp < ngroups) {  // wave-uniform
+    size_t rn[RT];
+    rows_of(min(grp + gstride, ngroups - 1), rn);
+    f32x4 acc[RT][NBT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; c += 2) {
+      // the order as written (each buffer refilled right after its last use) is what bounds the live registers:
+      // the scheduler must not hoist later loads above the products
+      load(a1, rp, c + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(a0, c, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 2 < NCH)
+        load(a0, rp, c + 2);
+      else
+        load(a0, rn, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(a1, c + 1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // epilogue: full logits and the running (value, id) best per column; rows visited in increasing order, so a
+    // strict comparison keeps the lowest id among equal values
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row0 = grp * 32 + r * 16 + 4 * g4;
+      if (grp * 32 + r * 16 < V) {  // V % 16 == 0: a tile is wholly inside or outside the table
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) {
+          const int col = c0 + t * 16 + n;
+          const f32x4 v = acc[r][t];
+          if (logits && col < B)
+            *reinterpret_cast<float4*>(logits + (size_t)col * V + row0) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v[i] > best[t]) {
+              best[t] = v[i];
+              bid[t] = row0 + i;
+            }
+        }
+      }
+    }
+    grp += gstride;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) rp[r] = rn[r];
+  }
+
+  // block-wide best per column, then one atomic max per (block, column)
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    uint64_t kk = bid[t] >= 0 ? vid_key(best[t], (uint32_t)bid[t]) : 0ull;
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)kk, o, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(kk >> 32), o, 64);
+      kk = u64_max(kk, ((uint64_t)hi << 32) | lo);
+    }
+    if (g4 == 0) red[wave][t * 16 + n] = kk;
+  }
+  __syncthreads();
+  if (tid < NC && c0 + tid < B) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = u64_max(m, red[w][tid]);
+    if (m) atomicMax(reinterpret_cast<unsigned long long*>(keys + c0 + tid), (unsigned long long)m);
+  }
+}
+
+__global__ void k_zero_u64(uint64_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
 // Head table in cluster order: out[r] = E[ordering[r]], rows of H bf16 (H % 8 == 0); grid ceil(V / 8), 256 threads,
 // 32 threads per row.
 __global__ __launch_bounds__(256) void k_gather_rows(const uint16_t* __restrict__ E, const int32_t* __restrict__ ordering,
@@ -1351,10 +1550,10 @@ hipError_t launch_ffn(hipStream_t s, int B, int H, int F, Residual res, const ui
 
 hipError_t launch_post(hipStream_t s, int B, int H, int Bb, int C, Residual res, const uint16_t* w_out, float eps,
                        const uint16_t* w_post, const uint16_t* w_cen, float* h_out, uint16_t* hidden_out,
-                       float* scores) {
+                       float* scores, uint64_t* keys_zero) {
   const dim3 grid((Bb + C + 31) / 32, row_groups(B));
   MTPD_BY_NPL(H, return go(k_post<NPL>, grid, 256, 0, s, B, Bb, C, res, w_out, eps, w_post, w_cen, h_out,
-                           hidden_out, scores))
+                           hidden_out, scores, keys_zero))
 }
 #undef MTPD_BY_NPL
 
@@ -1415,6 +1614,24 @@ hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const
   MTPD_HEAD(1, 8) MTPD_HEAD(2, 8) MTPD_HEAD(4, 8) MTPD_HEAD(8, 8) MTPD_HEAD(16, 8)
 #undef MTPD_HEAD
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_head_dense(hipStream_t s, int B, int V, int H, const uint16_t* E, const float* h, float* logits,
+                             uint64_t* keys) {
+  const int ngroups = (V + 31) / 32;
+  const int nc = B <= 16 ? 16 : 32;
+  const int nblk = (ngroups + 15) / 16;
+  const dim3 grid(nblk < 256 ? nblk : 256, (B + nc - 1) / nc);
+#define MTPD_HD(NC_, NPL_) \
+  if (nc == NC_ && H == NPL_ * 256) return go(k_head_dense<NC_, NPL_>, grid, 1024, 0, s, B, V, E, h, logits, keys);
+  MTPD_HD(16, 1) MTPD_HD(16, 2) MTPD_HD(16, 3) MTPD_HD(16, 4)
+  MTPD_HD(32, 1) MTPD_HD(32, 2) MTPD_HD(32, 3) MTPD_HD(32, 4)
+#undef MTPD_HD
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_keys(hipStream_t s, uint64_t* keys, int n) {
+  return go(k_zero_u64, (n + 255) / 256, 256, 0, s, keys, n);
 }
 
 hipError_t launch_gather_rows(hipStream_t s, const uint16_t* E, const int32_t* ordering, uint16_t* out, int V,

@@ -93,6 +93,9 @@ struct Plan {
   size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, total;
 };
 
+// Argmax keys per row: one per selected cluster for the masked head, one for the dense head.
+int key_slots(const mtpd_config& c) { return c.n_centroids == 0 ? 1 : c.top_k; }
+
 Plan make_plan(const mtpd_config& c, int B, int vsc) {
   Plan p{};
   size_t off = 0;
@@ -118,7 +121,7 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.sel = take((size_t)B * c.top_k * 4);
   p.ids = take((size_t)B * c.top_k * vsc * 4);
   p.z = take((size_t)B * c.top_k * vsc * 4);
-  p.keys = take((size_t)B * c.top_k * 8);
+  p.keys = take((size_t)B * key_slots(c) * 8);
   p.total = off;
   return p;
 }
@@ -130,13 +133,18 @@ T* at(void* ws, size_t off) {
 
 int check_config(const mtpd_config* c) {
   if (!c) return fail(MTPD_EINVAL, "config is NULL");
-  if (c->n_centroids == 0) return fail(MTPD_EUNSUP, "n_centroids == 0 (dense tied head) is not implemented");
+  const bool dense = c->n_centroids == 0;  // dense tied head
   if (c->backbone <= 0 || c->hidden <= 0 || c->n_layer <= 0 || c->n_head <= 0 || c->n_kv_head <= 0 ||
-      c->head_dim <= 0 || c->ffn <= 0 || c->vocab <= 0 || c->n_centroids <= 0 || c->top_k <= 0 ||
-      c->swa_window <= 0)
-    return fail(MTPD_ESHAPE, "every size in the config must be positive");
-  if (c->vocab % c->n_centroids != 0) return fail(MTPD_ESHAPE, "vocab %% n_centroids != 0");
-  if (c->top_k > c->n_centroids) return fail(MTPD_ESHAPE, "top_k > n_centroids");
+      c->head_dim <= 0 || c->ffn <= 0 || c->vocab <= 0 || c->n_centroids < 0 || c->swa_window <= 0 ||
+      (!dense && c->top_k <= 0))
+    return fail(MTPD_ESHAPE, "every size in the config must be positive (n_centroids may be 0: dense head)");
+  if (dense) {
+    if (c->top_k != 0 && c->top_k != 1) return fail(MTPD_ESHAPE, "top_k must be 0 or 1 with the dense head");
+    if (c->vocab % 16 != 0) return fail(MTPD_ESHAPE, "vocab must be a multiple of 16 with the dense head");
+  } else {
+    if (c->vocab % c->n_centroids != 0) return fail(MTPD_ESHAPE, "vocab %% n_centroids != 0");
+    if (c->top_k > c->n_centroids) return fail(MTPD_ESHAPE, "top_k > n_centroids");
+  }
   if (c->n_head % c->n_kv_head != 0) return fail(MTPD_ESHAPE, "n_head %% n_kv_head != 0");
   const int G = c->n_head / c->n_kv_head;
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(MTPD_ESHAPE, "query heads per kv head must be 1, 2, 4 or 8");
@@ -148,10 +156,13 @@ int check_config(const mtpd_config* c) {
   if (c->ffn % 256 != 0 || c->ffn > 4096) return fail(MTPD_ESHAPE, "ffn must be a multiple of 256, <= 4096");
   if ((c->n_head * c->head_dim) % 256 != 0 || c->n_head * c->head_dim > 4096)
     return fail(MTPD_ESHAPE, "n_head*head_dim must be a multiple of 256, <= 4096");
-  if (c->n_centroids > mtpd::kMaxCentroids) return fail(MTPD_ESHAPE, "n_centroids > 4096");
-  if (c->top_k > mtpd::kMaxTopK) return fail(MTPD_ESHAPE, "top_k > 64");
-  const int vsc = c->vocab / c->n_centroids;
-  if (vsc % 16 != 0 || vsc > 1024) return fail(MTPD_ESHAPE, "vocab / n_centroids must be a multiple of 16, <= 1024");
+  if (!dense) {
+    if (c->n_centroids > mtpd::kMaxCentroids) return fail(MTPD_ESHAPE, "n_centroids > 4096");
+    if (c->top_k > mtpd::kMaxTopK) return fail(MTPD_ESHAPE, "top_k > 64");
+    const int vsc = c->vocab / c->n_centroids;
+    if (vsc % 16 != 0 || vsc > 1024)
+      return fail(MTPD_ESHAPE, "vocab / n_centroids must be a multiple of 16, <= 1024");
+  }
   if (c->n_layer > 32) return fail(MTPD_ESHAPE, "n_layer > 32");
   if (!(c->rms_eps >= 0.f) || !(c->attn_scale > 0.f)) return fail(MTPD_EINVAL, "rms_eps < 0 or attn_scale <= 0");
   return MTPD_OK;
@@ -244,6 +255,11 @@ int nsplit_for(const mtpd::RowWindows& win, int B, int nkv) {
 int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const float* hsrc,
              float* logits, int32_t* sel_out, int32_t* ids_out, float* z_out) {
   const mtpd_config& c = h->cfg;
+  if (c.n_centroids == 0) {  // dense tied head ([Guide] section 5, use_ordered_embeddings off); keys zeroed before
+    KLAUNCH(h, "head_dense", mtpd::launch_head_dense(s, B, c.vocab, c.hidden, h->w.token_embd, hsrc, logits,
+                                                     at<uint64_t>(ws, p.keys)));
+    return MTPD_OK;
+  }
   // [Inventory] "Centroid / ordered embeddings LM head", steps 2-5
   KLAUNCH(h, "head", mtpd::launch_head(s, B, c.n_centroids, c.top_k, h->vsc, c.hidden, at<float>(ws, p.scores),
                            h->w.token_ordering, h->head_sorted, hsrc, sel_out, ids_out, z_out, logits,
@@ -289,7 +305,7 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
     mtpd::Residual rf{x[cur], t, L.post_attention_norm, 1.0f, x[cur ^ 1], QD / 256, (size_t)B * H};
     cur ^= 1;
     mtpd::FillRange fr{nullptr, 0, 0};
-    if (logits)
+    if (logits && c.n_centroids > 0)  // the dense head writes every logit itself
       fr = mtpd::FillRange{logits, (BV * l / nL) & ~size_t(3), l + 1 == nL ? BV : (BV * (l + 1) / nL) & ~size_t(3)};
     KLAUNCH(h, "ffn", mtpd::launch_ffn(s, B, H, F, rf, L.ffn_norm, c.rms_eps, L.ffn_gate, L.ffn_up, m, fr));
     KLAUNCH(h, "down", mtpd::launch_dense(s, B, F, H, m, L.ffn_down, d));
@@ -298,7 +314,8 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
   mtpd::Residual rp{x[cur], d, Last.post_ffw_norm, Last.layer_output_scale, nullptr, 1, 0};
   // output norm, post_projection (the next step's hidden input, [Guide] section 6) and centroid scores
   KLAUNCH(h, "post", mtpd::launch_post(s, B, H, Bb, c.n_centroids, rp, h->w.output_norm, c.rms_eps, h->w.post_proj,
-                           h->w.centroids, at<float>(ws, p.h), hidden_out, at<float>(ws, p.scores)));
+                           h->w.centroids, at<float>(ws, p.h), hidden_out, at<float>(ws, p.scores),
+                           c.n_centroids == 0 ? at<uint64_t>(ws, p.keys) : nullptr));
   return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, sel_out, ids_out, z_out);
 }
 
@@ -307,6 +324,13 @@ int check_call(const mtpd_handle_s* h, void* ws, int B) {
   if (B < 1 || B > h->max_batch) return fail(MTPD_ESHAPE, "batch %d outside [1, max_batch=%d]", B, h->max_batch);
   if (!ws) return fail(MTPD_EINVAL, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MTPD_EINVAL, "workspace is not 256-byte aligned");
+  return MTPD_OK;
+}
+
+// The per-cluster outputs exist only for the masked head.
+int check_head_outputs(const mtpd_handle_s* h, const void* sel, const void* ids, const void* z) {
+  if (h->cfg.n_centroids == 0 && (sel || ids || z))
+    return fail(MTPD_EINVAL, "sel_centroids / sparse_ids / sparse_logits must be NULL with the dense head");
   return MTPD_OK;
 }
 
@@ -497,8 +521,11 @@ int mtpd_create(const mtpd_config* cfg, const mtpd_weights* w, int32_t max_batch
   CHECK(check_ptr(w->post_proj, "post_proj"));
   CHECK(check_ptr(w->output_norm, "output_norm"));
   CHECK(check_ptr(w->token_embd, "token_embd"));
-  CHECK(check_ptr(w->centroids, "centroids"));
-  CHECK(check_ptr(w->token_ordering, "token_ordering"));
+  const bool dense = cfg->n_centroids == 0;  // centroids and token_ordering are not read by the dense head
+  if (!dense) {
+    CHECK(check_ptr(w->centroids, "centroids"));
+    CHECK(check_ptr(w->token_ordering, "token_ordering"));
+  }
   if (!w->layers) return fail(MTPD_EINVAL, "layers is NULL");
   for (int l = 0; l < cfg->n_layer; ++l) {
     const mtpd_layer& L = w->layers[l];
@@ -512,39 +539,44 @@ int mtpd_create(const mtpd_config* cfg, const mtpd_weights* w, int32_t max_batch
       CHECK(check_ptr(ps[i], nm));
     }
   }
-  // token_ordering must list every token once ([Inventory] "GGUF / converter layout", verification)
-  std::vector<int32_t> ord((size_t)cfg->vocab);
-  hipError_t e = hipMemcpy(ord.data(), w->token_ordering, ord.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail(MTPD_EHIP, "copying token_ordering: %s", hipGetErrorString(e));
-  std::vector<uint8_t> seen((size_t)cfg->vocab, 0);
-  for (size_t i = 0; i < ord.size(); ++i) {
-    const int32_t v = ord[i];
-    if (v < 0 || v >= cfg->vocab || seen[(size_t)v])
-      return fail(MTPD_ESHAPE, "token_ordering is not a permutation (entry %zu = %d)", i, v);
-    seen[(size_t)v] = 1;
+  if (!dense) {
+    // token_ordering must list every token once ([Inventory] "GGUF / converter layout", verification)
+    std::vector<int32_t> ord((size_t)cfg->vocab);
+    hipError_t e = hipMemcpy(ord.data(), w->token_ordering, ord.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(MTPD_EHIP, "copying token_ordering: %s", hipGetErrorString(e));
+    std::vector<uint8_t> seen((size_t)cfg->vocab, 0);
+    for (size_t i = 0; i < ord.size(); ++i) {
+      const int32_t v = ord[i];
+      if (v < 0 || v >= cfg->vocab || seen[(size_t)v])
+        return fail(MTPD_ESHAPE, "token_ordering is not a permutation (entry %zu = %d)", i, v);
+      seen[(size_t)v] = 1;
+    }
   }
   mtpd_handle_s* hh = new (std::nothrow) mtpd_handle_s();
   if (!hh) return fail(MTPD_ENOMEM, "out of host memory");
-  // the head table in cluster order ([Inventory] "Centroid / ordered embeddings LM head", step 3: a cluster's ids
-  // are a contiguous slice of the ordering), so that a selected cluster's rows are one contiguous read
-  const size_t head_bytes = (size_t)cfg->vocab * cfg->hidden * sizeof(uint16_t);
-  if (hipMalloc(&hh->head_sorted, head_bytes) != hipSuccess) {
-    delete hh;
-    return fail(MTPD_ENOMEM, "no device memory for the cluster-ordered head table (%zu bytes)", head_bytes);
-  }
-  e = mtpd::launch_gather_rows(nullptr, w->token_embd, w->token_ordering, hh->head_sorted, cfg->vocab, cfg->hidden);
-  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
-  if (e != hipSuccess) {
-    (void)hipFree(hh->head_sorted);
-    delete hh;
-    return fail(MTPD_EHIP, "building the cluster-ordered head table: %s", hipGetErrorString(e));
+  if (!dense) {
+    // the head table in cluster order ([Inventory] "Centroid / ordered embeddings LM head", step 3: a cluster's
+    // ids are a contiguous slice of the ordering), so that a selected cluster's rows are one contiguous read
+    const size_t head_bytes = (size_t)cfg->vocab * cfg->hidden * sizeof(uint16_t);
+    if (hipMalloc(&hh->head_sorted, head_bytes) != hipSuccess) {
+      delete hh;
+      return fail(MTPD_ENOMEM, "no device memory for the cluster-ordered head table (%zu bytes)", head_bytes);
+    }
+    hipError_t e =
+        mtpd::launch_gather_rows(nullptr, w->token_embd, w->token_ordering, hh->head_sorted, cfg->vocab, cfg->hidden);
+    if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess) {
+      (void)hipFree(hh->head_sorted);
+      delete hh;
+      return fail(MTPD_EHIP, "building the cluster-ordered head table: %s", hipGetErrorString(e));
+    }
   }
   hh->cfg = *cfg;
   hh->w = *w;
   hh->layers.assign(w->layers, w->layers + cfg->n_layer);
   hh->w.layers = nullptr;
   hh->max_batch = max_batch;
-  hh->vsc = cfg->vocab / cfg->n_centroids;
+  hh->vsc = dense ? 0 : cfg->vocab / cfg->n_centroids;
   const char* g = getenv("MTPD_GRAPHS");
   hh->use_graphs = !(g && g[0] == '0');
   *out = hh;
@@ -584,6 +616,7 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
   if (!next_token) return fail(MTPD_EINVAL, "next_token is NULL");
   CHECK(check_ptr(hidden_out, "hidden_out"));
   if (logits) CHECK(check_ptr(logits, "logits"));
+  CHECK(check_head_outputs(h, sel_centroids, sparse_ids, sparse_logits));
   const Chains ch = make_chains(batch);
   const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
   const CallKey key = make_key(1, batch, 1,
@@ -597,12 +630,12 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
       const int b0 = ch.rows[ci], Bc = ch.rows[ci + 1] - b0;
       void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
       const ChainView v = chain_view(h, kv, win, b0, Bc);
-      mtpd::TokenSource ts{last_token + b0, at<uint64_t>(wsc, p.keys), 0, c.top_k, nullptr, 0, nullptr};
+      mtpd::TokenSource ts{last_token + b0, at<uint64_t>(wsc, p.keys), 0, key_slots(c), nullptr, 0, nullptr};
       CHECK(run_step(h, cs, wsc, p, Bc, target_hidden + (size_t)b0 * c.backbone, ts, target_embd, &v.kv, v.win,
                      v.nsplit, logits ? logits + (size_t)b0 * c.vocab : nullptr,
                      hidden_out + (size_t)b0 * c.backbone, sel_centroids ? sel_centroids + (size_t)b0 * c.top_k : nullptr,
                      sparse_ids ? sparse_ids + b0 * kv_n : nullptr, sparse_logits ? sparse_logits + b0 * kv_n : nullptr));
-      KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), next_token + b0, nullptr, 0));
+      KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, key_slots(c), at<uint64_t>(wsc, p.keys), next_token + b0, nullptr, 0));
       return MTPD_OK;
   });
 }
@@ -637,14 +670,14 @@ int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch
       for (int i = 0; i < n; ++i) {
         const uint16_t* th = (i == 0) ? target_hidden + (size_t)b0 * c.backbone : hid[(i - 1) & 1];
         // step i's token: the caller's for i = 0, else the previous step's argmax (recorded as tokens[:, i-1])
-        mtpd::TokenSource ts{last_token + b0, keys, 0, c.top_k, nullptr, 0, nullptr};
-        if (i > 0) ts = mtpd::TokenSource{last_token + b0, keys, 1, c.top_k, tok_c + (i - 1), n, nullptr};
+        mtpd::TokenSource ts{last_token + b0, keys, 0, key_slots(c), nullptr, 0, nullptr};
+        if (i > 0) ts = mtpd::TokenSource{last_token + b0, keys, 1, key_slots(c), tok_c + (i - 1), n, nullptr};
         uint16_t* hout = (i == n - 1) ? hidden_out + (size_t)b0 * c.backbone : hid[i & 1];
         CHECK(run_step(h, cs, wsc, p, Bc, th, ts, target_embd, &v.kv, v.win, v.nsplit,
                        logits ? logits + (size_t)i * BV + (size_t)b0 * c.vocab : nullptr, hout, nullptr, nullptr,
                        nullptr));
       }
-      KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, c.top_k, keys, at<int32_t>(wsc, p.tok), tok_c + (n - 1), n));
+      KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, key_slots(c), keys, at<int32_t>(wsc, p.tok), tok_c + (n - 1), n));
       return MTPD_OK;
   });
 }
@@ -656,6 +689,7 @@ int mtpd_masked_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
   CHECK(check_ptr(hidden, "hidden"));
   if (!argmax) return fail(MTPD_EINVAL, "argmax is NULL");
   if (logits) CHECK(check_ptr(logits, "logits"));
+  CHECK(check_head_outputs(h, sel_centroids, sparse_ids, sparse_logits));
   const Chains ch = make_chains(m);
   const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
   const mtpd_config& c = h->cfg;
@@ -667,6 +701,12 @@ int mtpd_masked_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
       void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
       const float* hc = hidden + (size_t)b0 * c.hidden;
       float* lc = logits ? logits + (size_t)b0 * c.vocab : nullptr;
+      if (c.n_centroids == 0) {  // dense tied head
+        KLAUNCH(h, "zero_keys", mtpd::launch_zero_keys(cs, at<uint64_t>(wsc, p.keys), Bc));
+        CHECK(run_head(h, cs, wsc, p, Bc, hc, lc, nullptr, nullptr, nullptr));
+        KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, 1, at<uint64_t>(wsc, p.keys), argmax + b0, nullptr, 0));
+        return MTPD_OK;
+      }
       // [Inventory] "Centroid / ordered embeddings LM head", step 1: centroid logits
       KLAUNCH(h, "scores", mtpd::launch_scores(cs, Bc, c.hidden, c.n_centroids, hc, h->w.centroids, at<float>(wsc, p.scores)));
       if (lc) KLAUNCH(h, "fill", mtpd::launch_fill(cs, lc, (size_t)Bc * c.vocab));

@@ -68,7 +68,8 @@ class Drafter:
             layers[i].layer_output_scale = float(lw["layer_output_scale"])
         w = abi.mtpd_weights(pre_proj=_ptr(weights["pre_proj"]), post_proj=_ptr(weights["post_proj"]),
                              output_norm=_ptr(weights["output_norm"]), token_embd=_ptr(weights["token_embd"]),
-                             centroids=_ptr(weights["centroids"]), token_ordering=_ptr(weights["token_ordering"]),
+                             centroids=_ptr(weights.get("centroids")),  # absent with the dense head
+                             token_ordering=_ptr(weights.get("token_ordering")),
                              layers=layers)
         self._cfg, self._layers, self._w = cfg, layers, w
         h = C.c_void_p()
@@ -129,6 +130,8 @@ class Drafter:
             if want_logits:
                 o["logits"] = torch.empty(B, sh.vocab, dtype=torch.float32, device=dev)
             if want_sparse:
+                if sh.n_centroids == 0:
+                    raise ValueError("the dense head has no per-cluster outputs")
                 kv_n = sh.top_k * sh.vocab // sh.n_centroids
                 o["sel"] = torch.empty(B, sh.top_k, dtype=torch.int32, device=dev)
                 o["ids"] = torch.empty(B, kv_n, dtype=torch.int32, device=dev)
@@ -160,8 +163,14 @@ class Drafter:
             C.byref(s), _ptr(o["tokens"]), _ptr(o.get("logits")), _ptr(o["hidden_out"])))
         return o
 
-    def masked_head(self, h, want_logits: bool = False, want_sparse: bool = True) -> Dict[str, torch.Tensor]:
+    def masked_head(self, h, want_logits: bool = False, want_sparse: Optional[bool] = None) -> Dict[str, torch.Tensor]:
+        """The LM head alone on fp32 normed states h [m][hidden]; with n_centroids == 0 the dense tied head (no
+        per-cluster outputs; want_sparse defaults to True for the masked head only)."""
         sh = self.shape
+        if want_sparse is None:
+            want_sparse = sh.n_centroids > 0
+        if want_sparse and sh.n_centroids == 0:
+            raise ValueError("the dense head has no per-cluster outputs")
         m = int(h.shape[0])
         dev = h.device
         o = {"argmax": torch.empty(m, dtype=torch.int32, device=dev)}

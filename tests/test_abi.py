@@ -76,7 +76,9 @@ def create_rc(cfg, weights=None, max_batch=16):
     (dict(vocab=262143), abi.MTPD_ESHAPE, "n_centroids"),
     (dict(top_k=4096), abi.MTPD_ESHAPE, "top_k"),
     (dict(n_head=3, n_kv_head=2), abi.MTPD_ESHAPE, "n_kv_head"),
-    (dict(n_centroids=0), abi.MTPD_EUNSUP, "dense"),
+    (dict(n_centroids=0, top_k=5), abi.MTPD_ESHAPE, "top_k must be 0 or 1"),
+    (dict(n_centroids=0, top_k=1, vocab=262150), abi.MTPD_ESHAPE, "multiple of 16 with the dense head"),
+    (dict(n_centroids=-1), abi.MTPD_ESHAPE, "positive"),
     (dict(head_dim=512), abi.MTPD_ESHAPE, "head_dim"),
     (dict(hidden=250), abi.MTPD_ESHAPE, "multiple of 256"),
     (dict(top_k=65, n_centroids=2048), abi.MTPD_ESHAPE, "top_k > 64"),
@@ -103,6 +105,20 @@ def test_create_rejects_null_and_misaligned_weights():
     assert rc == abi.MTPD_EINVAL and "layers[0].attn_q" in err
     rc, err = create_rc(good_config(), w, max_batch=65)
     assert rc == abi.MTPD_ESHAPE and "max_batch" in err
+
+
+def test_dense_head_config_needs_no_centroids_or_ordering():
+    """With n_centroids == 0 the centroid table and the ordering are not read: NULL passes their checks and the
+    first rejected pointer is a layer weight."""
+    layers = (abi.mtpd_layer * 4)()
+    w = abi.mtpd_weights(pre_proj=0x1000, post_proj=0x1000, output_norm=0x1000, token_embd=0x1000, centroids=None,
+                         token_ordering=None, layers=layers)
+    for top_k in (0, 1):
+        rc, err = create_rc(good_config(n_centroids=0, top_k=top_k, hidden=1024, backbone=2816, n_head=8,
+                                        ffn=4096), w)
+        assert rc == abi.MTPD_EINVAL and "layers[0].attn_q" in err, err
+    rc, err = create_rc(good_config(), w)  # the masked head does need them
+    assert rc == abi.MTPD_EINVAL and "centroids" in err
 
 
 def test_calls_reject_null_handle():
