@@ -5,6 +5,8 @@ One bench step = one draft_block(4) call over the E4B-shaped batch-16 workload (
 layers over a shared K=V cache of 8192 keys per sequence, 3 sliding layers with window 512 and one full layer,
 2048-centroid top-32 masked head over a 262144 vocabulary, the -1e30 logits row written every step). Inputs are
 synthetic (seeded counter-based generator) and resident in HBM before the timed region.
+--workload e26b_b32_ctx32768_block4 times the 26B-A4B-shaped drafter instead (backbone 2816, hidden 1024, 8 query
+heads over one kv head, batch 32, context 32768, window 1024) with the dense tied head over the full table.
 
 Prints one JSON line: draft tokens/s (value), µs per drafter step, the roofline of the dominant kernel (its
 algorithmic bytes per launch over its HIP-event launch duration, against 8 TB/s), and the CPU oracle timed on a
@@ -39,7 +41,15 @@ COPY_PROBE_BYTES = 512 << 20
 SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma", "attn_full": "k_attn_mfma",
                "o_proj": "k_oproj",
                "down": "k_dense", "ffn": "k_ffn", "post": "k_post", "head": "k_head", "final": "k_final",
-               "scores": "k_dense", "fill": "k_fill"}
+               "scores": "k_dense", "fill": "k_fill", "head_dense": "k_head_dense", "zero_keys": "k_zero_u64"}
+
+
+def site_kernel(site, shape):
+    """Kernel behind a launch site for this shape (the matrix-core attention covers head_dim 256 with up to eight
+    query heads per kv head; other shapes run the vector-ALU attention)."""
+    if site.startswith("attn_") and not (shape.head_dim == 256 and shape.n_head // shape.n_kv_head <= 8):
+        return "k_attn"
+    return SITE_KERNEL[site]
 
 
 def source_digest() -> str:
@@ -49,14 +59,15 @@ def source_digest() -> str:
 
 def step_bytes(shape, batch, lens, distinct_clusters, with_logits=True):
     """Bytes one drafter step must move: weights once, each cache's K (= V) once over the keys it reads (the
-    sliding window counted once for the three sliding layers), the selected clusters' head rows, their ordering
-    ids, the logits row, and target hidden / embedding rows / hidden_out."""
+    sliding window counted once for the three sliding layers), the selected clusters' head rows and their ordering
+    ids (the dense head: the whole table), the logits row, and target hidden / embedding rows / hidden_out."""
     H, Bb, F, Q, hd = shape.hidden, shape.backbone, shape.ffn, shape.q_dim, shape.head_dim
     per_layer = (Q * H + H * Q + 3 * F * H) * 2 + (hd + 4 * H) * 2
     weights = (2 * Bb * H + Bb * H + shape.n_centroids * H + H) * 2 + shape.n_layer * per_layer
     kv = sum(shape.n_kv_head * hd * 2 * (L + min(shape.swa_window, L)) for L in lens)
-    head = distinct_clusters * shape.vsc * H * 2
-    ids = 4 * shape.top_k * shape.vsc * batch
+    dense = shape.n_centroids == 0
+    head = shape.vocab * H * 2 if dense else distinct_clusters * shape.vsc * H * 2
+    ids = 0 if dense else 4 * shape.top_k * shape.vsc * batch
     logits = 4 * shape.vocab * batch if with_logits else 0
     io = 2 * Bb * batch * 3
     return weights + kv + head + ids + logits + io, dict(weights=weights, kv=kv, head=head, ids=ids, logits=logits,
@@ -79,8 +90,9 @@ def site_bytes(site, shape, batch, lens, distinct_clusters):
         return shape.n_kv_head * hd * 2 * keys + 2 * hd + 2 * act(QD)
     if site == "o_proj":
         return 2 * H * QD + act(QD) + act(H) * (QD // 256)
-    if site == "ffn":
-        return 2 * 2 * F * H + 2 * H + 3 * act(H) + act(F) + 4 * shape.vocab * B // shape.n_layer
+    if site == "ffn":  # with the masked head, a quarter of the -1e30 logits fill
+        fill = 0 if shape.n_centroids == 0 else 4 * shape.vocab * B // shape.n_layer
+        return 2 * 2 * F * H + 2 * H + 3 * act(H) + act(F) + fill
     if site == "down":
         return 2 * H * F + act(F) + act(H)
     if site == "post":
@@ -88,20 +100,41 @@ def site_bytes(site, shape, batch, lens, distinct_clusters):
     if site == "head":
         n = shape.top_k * shape.vsc
         return distinct_clusters * shape.vsc * H * 2 + 4 * n * B + act(shape.n_centroids) + act(H) + 4 * n * B
+    if site == "head_dense":  # the whole table once, h in, the full logits rows out
+        return shape.vocab * H * 2 + act(H) + 4 * shape.vocab * B + 8 * B
     if site == "final":
-        return 8 * shape.top_k * B + 4 * B
+        return 8 * max(shape.top_k, 1) * B + 4 * B
+    if site == "zero_keys":
+        return 8 * B
     raise KeyError(site)
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle as it stands, on single-row drafter steps of the same workload, for about `seconds`."""
+def cpu_baseline(wl, seconds, w_dev=None, inp_dev=None):
+    """The oracle as it stands, on single-row drafter steps of the same workload, for about `seconds`. The weights
+    and inputs are the GPU-generated ones copied to the host when given (the generator is bit-identical on both
+    devices), else generated on the host."""
     from threadpoolctl import threadpool_info
+
+    import torch
 
     import oracle as O
     from fixtures import synth
+
+    def host(x):
+        if isinstance(x, torch.Tensor):
+            return x.cpu()
+        if isinstance(x, dict):
+            return {k: host(v) for k, v in x.items()}
+        if isinstance(x, list):
+            return [host(v) for v in x]
+        return x
+
     shape = wl.shape
-    w = synth.make_weights(shape, seed=wl.seed)
-    inp = synth.make_inputs(wl, with_target_embd=False)
+    w = host(w_dev) if w_dev is not None else synth.make_weights(shape, seed=wl.seed)
+    if inp_dev is not None:
+        inp = {k: host(v) for k, v in inp_dev.items() if k != "target_embd"}
+    else:
+        inp = synth.make_inputs(wl, with_target_embd=False)
     m = O.Model(O.config_from(shape), w)
     import numpy as np
     ks = [inp["k_sliding"].numpy().view(np.uint16), inp["k_full"].numpy().view(np.uint16)]
@@ -172,18 +205,19 @@ def run_bench(args):
     torch.cuda.synchronize()
 
     # distinct clusters selected per step (for the head-row bytes), from this run's own logits rows
-    ordering = w["token_ordering"].cpu().numpy()
-    inv = np.empty_like(ordering)
-    inv[ordering] = np.arange(ordering.size, dtype=ordering.dtype)
-    lg = out["logits"].view(torch.int32).cpu().numpy()
     U = []
-    for i in range(n):
-        fin = lg[i] != np.int32(np.uint32(0xF149F2CA).view(np.int32))
-        clusters = set()
-        for b in range(B):
-            clusters |= set((inv[np.nonzero(fin[b])[0]] // shape.vsc).tolist())
-        U.append(len(clusters))
-    u_mean = float(np.mean(U))
+    if shape.n_centroids > 0:
+        ordering = w["token_ordering"].cpu().numpy()
+        inv = np.empty_like(ordering)
+        inv[ordering] = np.arange(ordering.size, dtype=ordering.dtype)
+        lg = out["logits"].view(torch.int32).cpu().numpy()
+        for i in range(n):
+            fin = lg[i] != np.int32(np.uint32(0xF149F2CA).view(np.int32))
+            clusters = set()
+            for b in range(B):
+                clusters |= set((inv[np.nonzero(fin[b])[0]] // shape.vsc).tolist())
+            U.append(len(clusters))
+    u_mean = float(np.mean(U)) if U else 0.0
     lens = [int(x) for x in inp["len_full"]]
     sbytes, parts = step_bytes(shape, B, lens, u_mean)
 
@@ -216,7 +250,7 @@ def run_bench(args):
         per_site.setdefault(name, []).append(ms)
     per_kernel = {}
     for site, v in per_site.items():
-        k = SITE_KERNEL[site]
+        k = site_kernel(site, shape)
         e = per_kernel.setdefault(k, {"launches": 0, "total_ms": 0.0, "bytes": 0.0, "sites": []})
         e["launches"] += len(v)
         e["total_ms"] += float(np.sum(v))
@@ -269,6 +303,7 @@ def run_bench(args):
         "config": {"workload": wl.name, "batch": B, "context": wl.context, "draft_block": n,
                    "backbone": shape.backbone, "hidden": shape.hidden, "vocab": shape.vocab,
                    "n_centroids": shape.n_centroids, "top_k": shape.top_k, "swa_window": shape.swa_window,
+                   "head": "dense" if shape.n_centroids == 0 else "masked",
                    "logits_row_written": True, "graph_replay": True},
         "us_per_drafter_step": us_drafter_step,
         "us_per_drafter_step_p10_p90": [float(np.percentile(launch_ms, 10)) * 1e3 / n,
@@ -289,7 +324,7 @@ def run_bench(args):
         "kernel_source_sha256_16": source_digest(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, w, inp)
     print(json.dumps(res), flush=True)
 
 

@@ -720,7 +720,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
   }
 }
 
-// Matrix-core variant for head_dim 256 and up to 4 query heads per kv head (heads padded to the 16 rows of an
+// Matrix-core variant for head_dim 256 and up to 8 query heads per kv head (heads padded to the 16 rows of an
 // MFMA tile). Per wave and batch of 16 keys:
 //   S[16 keys][16 heads] = K_tile . q^T with v_mfma_f32_16x16x32_bf16: the key rows load straight into the A
 //     operand (lane l: key l%16, 8 dims at 8*(l/16) of each 32-dim step); the fp32 query is split into two bf16
@@ -739,12 +739,17 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
                                                           int nsplit, float scale_log2, float* __restrict__ pacc,
                                                           float* __restrict__ pml, float* __restrict__ o) {
   constexpr int HD = 256, KSTEPS = HD / 32, TILES = HD / 16, LROW = HD + 8, S = NW * 16;
-  static_assert(G >= 1 && G <= 4, "the heads of a kv group sit in lanes 0..G-1 of the score tile");
-  __shared__ float qs[G][HD];
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "the heads of a kv group sit in lanes 0..G-1 of the score tile");
+  constexpr int GQ = (G + 3) / 4;      // 4-head row groups of the output tile that hold real heads
+  constexpr int HPW = (G + NW - 1) / NW;  // heads whose q a wave normalises and rotates
+  // the q staging buffer is dead once the B operands are built (a barrier later), so the combine reuses it
+  constexpr int QS_FLOATS = G * HD, WACC_FLOATS = NW * HD * 4 * GQ;
+  __shared__ __attribute__((aligned(16))) float qs_wacc[QS_FLOATS > WACC_FLOATS ? QS_FLOATS : WACC_FLOATS];
+  float (*qs)[HD] = reinterpret_cast<float (*)[HD]>(qs_wacc);                  // [head][dim]
+  float (*wacc)[HD][4 * GQ] = reinterpret_cast<float (*)[HD][4 * GQ]>(qs_wacc);  // [wave][dim][head]
   __shared__ __attribute__((aligned(16))) uint16_t qop[KSTEPS][2][G][4][8];  // [step][hi/lo][head][kq][8 dims]
   __shared__ __attribute__((aligned(16))) uint16_t vt[NW][16][LROW];
   __shared__ __attribute__((aligned(16))) float wml[NW][G][2];
-  __shared__ __attribute__((aligned(16))) float wacc[NW][HD][4];  // [wave][dim][head]
   static_assert(NW * 64 == HD, "one thread per dim in the combine");
   const int sp = blockIdx.x, bg = blockIdx.y;
   const int b = bg / nkv, g = bg % nkv;
@@ -762,8 +767,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 
   // inputs of q_norm + rotation first (waits count loads in issue order, so these must precede the key batch)
   const float* tab = rope + ((size_t)b * 2 + type) * 2 * half;
-  const int hh = min(wave, G - 1);  // the wave's head (waves beyond G repeat the last head and store nothing)
-  const float4 qv = *reinterpret_cast<const float4*>(q + ((size_t)b * nh + g * G + hh) * HD + lane * 4);
+  // the wave's heads wave + NW j (waves beyond G repeat the last head and store nothing)
+  float4 qv[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j)
+    qv[j] = *reinterpret_cast<const float4*>(q + ((size_t)b * nh + g * G + min(wave + NW * j, G - 1)) * HD + lane * 4);
   const uint2 qw = *reinterpret_cast<const uint2*>(qnorm + lane * 4);
   const int i0 = (lane * 4) & (half - 1);
   const float4 co4 = *reinterpret_cast<const float4*>(tab + i0);
@@ -783,8 +791,10 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 
   // q_norm + rotation at the row's constant position ([Guide] section 2(2)); lane l holds dims 4l .. 4l+3, whose
   // rotation partners (dim i <-> i + HD/2) sit in lane l ^ 32
-  {
-    float v[4] = {qv.x, qv.y, qv.z, qv.w}, wq[4];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const int hh = wave + NW * j;
+    float v[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w}, wq[4];
     const float co[4] = {co4.x, co4.y, co4.z, co4.w}, si[4] = {si4.x, si4.y, si4.z, si4.w};
     unpack4(qw, wq);
     float ss = 0.f;
@@ -798,7 +808,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
     for (int e = 0; e < 4; ++e) {
       const float partner = xr_partner<32>(v[e]);
       const float rot = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
-      if (wave < G) qs[hh][lane * 4 + e] = rot;
+      if (hh < G) qs[hh][lane * 4 + e] = rot;
     }
   }
   __syncthreads();
@@ -873,10 +883,14 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
       phi[r] = (short)hb;
       plo[r] = (short)f2bf(pv[r] - bf2f(hb));
     }
-    // rescale the accumulators: D rows are heads 4kq + r, whose alpha lives in lane 4kq + r
+    // rescale the accumulators: D rows are heads 4kq + r, whose alpha lives in lane 4kq + r (rows of heads >= G
+    // are padding)
     float al[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = readlane_f(alpha, r);  // heads 0-3 (G <= 4): lanes 0-3; other D rows are padding
+    for (int r = 0; r < 4; ++r) {
+      al[r] = readlane_f(alpha, r);
+      if constexpr (GQ > 1) al[r] = (kq == 1) ? readlane_f(alpha, 4 + r) : al[r];
+    }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       i16x4 vb;
@@ -892,25 +906,27 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) ka[c] = kn[c];
   }
-  // combine the waves of this block: head h's softmax state is in lane h; the output rows sit in lanes 0-15
-  // (kq = 0): dim 16t + lane, heads in the four registers of acc[t], stored as one float4 per dim
+  // combine the waves of this block: head h's softmax state is in lane h; output row group kq (heads 4kq .. +3)
+  // sits in lanes 16kq .. +15: dim 16t + hq, heads in the four registers of acc[t], stored as one float4 per dim
   if (lane < G) {
     wml[wave][lane][0] = mrun;
     wml[wave][lane][1] = lrun;
   }
-  if (kq == 0) {
+  // (the combine buffer overlays the q staging buffer, whose last reads precede the barrier before the key loop)
+  if (kq < GQ) {
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) *reinterpret_cast<f32x4*>(&wacc[wave][16 * t + hq][0]) = acc[t];
+    for (int t = 0; t < TILES; ++t) *reinterpret_cast<f32x4*>(&wacc[wave][16 * t + hq][4 * kq]) = acc[t];
   }
   __syncthreads();
   {
     // thread d: dim d of the G heads over the NW waves
     const int d = threadIdx.x;
-    f32x4 av[NW];
+    f32x4 av[NW][GQ];
     float2 ml[NW][G];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      av[w] = *reinterpret_cast<const f32x4*>(&wacc[w][d][0]);
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) av[w][j] = *reinterpret_cast<const f32x4*>(&wacc[w][d][4 * j]);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) ml[w][hh] = *reinterpret_cast<const float2*>(&wml[w][hh][0]);
     }
@@ -927,7 +943,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
         const float mw = ml[w][hh].x;
         const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
         L = fmaf(ml[w][hh].y, f, L);
-        A = fmaf(av[w][hh], f, A);
+        A = fmaf(av[w][hh >> 2][hh & 3], f, A);
       }
       const size_t hqq = (size_t)b * nh + g * G + hh;
       if (nsplit == 1) {
@@ -1429,12 +1445,10 @@ __global__ void k_fill(float4* __restrict__ p, size_t n4, float* __restrict__ ta
 int row_groups(int B) { return (B + kRG - 1) / kRG; }
 
 // MTPD_ATTN_VALU=1 selects the vector-ALU attention for every shape (kept for comparison and as the general path).
+// Read at each launch (a captured graph keeps the kernel it was captured with).
 bool getenv_no_mfma() {
-  static const int v = [] {
-    const char* e = getenv("MTPD_ATTN_VALU");
-    return (e && e[0] == '1') ? 1 : 0;
-  }();
-  return v != 0;
+  const char* e = getenv("MTPD_ATTN_VALU");
+  return e && e[0] == '1';
 }
 
 // Timing events for the next launch only (see set_next_launch_events).
@@ -1563,7 +1577,8 @@ hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const floa
   dim3 grid(nsplit, B * nkv);
   const float sl2 = scale * 1.4426950408889634f;
   const int G = nh / nkv;
-  if (hd == 256 && G <= 4 && !getenv_no_mfma()) {
+  if (hd == 256 && G <= 8 && !getenv_no_mfma()) {
+    if (G == 8) return go(k_attn_mfma<8, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
     if (G == 4) return go(k_attn_mfma<4, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
     if (G == 2) return go(k_attn_mfma<2, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
     return go(k_attn_mfma<1, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);

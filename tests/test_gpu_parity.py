@@ -106,6 +106,11 @@ STEP_CASES = {
                              lens=[64, 1, 33]),
     # the largest batch the ABI takes
     "e2b_b64_ctx300": dict(shape=synth.E2B, batch=64, context=300, ragged=True),
+    # head_dim 128 and 64 (the vector-ALU attention): 2 and 8 query heads per kv head
+    "e2b_hd128_g2": dict(shape=dataclasses.replace(synth.E2B, head_dim=128, n_head=8, n_kv_head=4), batch=3,
+                         context=700, ragged=True),
+    "e2b_hd64_g8": dict(shape=dataclasses.replace(synth.E2B, head_dim=64, n_head=16, n_kv_head=2), batch=2,
+                        context=600, ragged=True),
 }
 
 
@@ -122,6 +127,29 @@ def test_drafter_step_parity(name):
     tally = compare_step(case, out, ref, rows, where=name)
     say(tally.summary())
     assert tally.sel_checked >= len(rows) // 2
+
+
+def test_vector_alu_attention_at_head_dim_256():
+    """The vector-ALU attention (selected per launch by MTPD_ATTN_VALU=1, else used only for head_dim 64 / 128)
+    on head_dim 256 with 4 and 8 query heads per kv head, split over several key ranges."""
+    import os
+    from mtp_drafter_step_amd import Drafter
+    for shape in (synth.E4B, synth.E26B):
+        say(f"valu attention {shape.n_head}/{shape.n_kv_head} heads")
+        case = Case(shape, batch=3, context=2500, ragged=True, gen_device="cuda")
+        os.environ["MTPD_ATTN_VALU"] = "1"
+        try:
+            d = Drafter(shape, case.wg, max_batch=3)
+            want_sparse = shape.n_centroids > 0
+            out = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=want_sparse)
+            torch.cuda.synchronize()
+        finally:
+            del os.environ["MTPD_ATTN_VALU"]
+        rows = [0, 1, 2]
+        ref = case.oracle_step(rows=rows, want_rows=not want_sparse)
+        tally = compare_step(case, out, ref, rows, where=f"valu {shape.n_head}")
+        say(tally.summary())
+        assert tally.tok_checked >= 1
 
 
 def test_drafter_step_is_deterministic():
