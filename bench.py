@@ -33,7 +33,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc")
+# the source file of each kernel; a kernel's digest covers that file and the shared headers
+KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_head": "k_head.hip",
+               "k_head_dense": "k_head.hip", "k_final": "k_head.hip", "k_fill": "k_head.hip",
+               "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 512 << 20
 
@@ -52,9 +56,13 @@ def site_kernel(site, shape):
     return SITE_KERNEL[site]
 
 
-def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(kernel: str) -> str:
+    """sha256[:16] of the sources that define `kernel` (its file plus device.h and kernels.h)."""
+    h = hashlib.sha256()
+    for name in ("device.h", "kernels.h", KERNEL_FILE.get(kernel, "k_layers.hip")):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def step_bytes(shape, batch, lens, distinct_clusters, with_logits=True):
@@ -171,7 +179,7 @@ def load_traffic(kernel, workload):
     if not m:
         return None
     t = json.loads(m.group(1))
-    if t.get("source_sha256_16") != source_digest():
+    if t.get("source_sha256_16") != source_digest(kernel):
         return None
     return t
 
@@ -284,7 +292,7 @@ def run_bench(args):
         torch.cuda.synchronize()
         cold_ms.append(e0.elapsed_time(e1))
     del sweep
-    us_cold = float(np.median(cold_ms)) * 1e3 / n
+    us_cold = float(np.median(cold_ms)) * 1e3 / n if cold_ms else None
 
     if args.copy_probe:
         # calibration copy of known size for the HBM byte counters (a plain device-to-device copy)
@@ -319,9 +327,9 @@ def run_bench(args):
                           "achieved_GBs": sbytes / (us_drafter_step * 1e-6) / 1e9,
                           "frac": sbytes / (us_drafter_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
                           "cold_us_per_drafter_step": us_cold,
-                          "cold_achieved_GBs": sbytes / (us_cold * 1e-6) / 1e9},
+                          "cold_achieved_GBs": sbytes / (us_cold * 1e-6) / 1e9 if us_cold else None},
         "kernels": kernels_table,
-        "kernel_source_sha256_16": source_digest(),
+        "kernel_source_sha256_16": source_digest(dom),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, w, inp)
@@ -350,7 +358,9 @@ def summarize_stats(args):
     mine = [r for r in rows if "mtpd::" in r["Name"]]
     lines = [f"# Kernel-trace statistics: drafter kernels, {args.workload}", "",
              f"Command: `{args.cmd}`", "",
-             f"Kernel source sha256[:16]: `{source_digest()}`", "",
+             "Kernel source sha256[:16]: " + ", ".join(
+                 f"{f} `{source_digest(k)}`" for f, k in (("k_layers.hip", "k_ffn"), ("k_attention.hip", "k_attn_mfma"),
+                                                          ("k_head.hip", "k_head"))), "",
              "Only the library's kernels are listed (the run also holds the input generator's and torch's own "
              "kernels, which are outside the timed calls).", "",
              "| kernel | calls | avg µs | min µs | max µs | total µs | share of library time |", "|---|---|---|---|---|---|---|"]
@@ -396,10 +406,11 @@ def summarize_pmc(args):
     total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
     t = {"kernel": args.kernel, "workload": args.workload, "hbm_bytes_per_launch": total,
          "fetch_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"],
-         "write_bytes_per_launch": out["WRITE_SIZE"]["bytes_per_launch"], "source_sha256_16": source_digest()}
+         "write_bytes_per_launch": out["WRITE_SIZE"]["bytes_per_launch"], "source_sha256_16": source_digest(args.kernel)}
     lines = [f"# HBM traffic per launch: {args.kernel}, {args.workload}", "",
              f"Commands: `{args.cmd}`", "",
-             f"Kernel source sha256[:16]: `{source_digest()}`", "",
+             f"Kernel source sha256[:16] ({KERNEL_FILE.get(args.kernel, 'k_layers.hip')} with the shared headers): "
+             f"`{source_digest(args.kernel)}`", "",
              "Each counter is read per dispatch in KiB, averaged over the kernel's dispatches, and scaled by the "
              f"ratio of known bytes to counted KiB for the calibration copy ({COPY_PROBE_BYTES >> 20} MiB "
              "device-to-device copy run by the same command).", "",

@@ -1,0 +1,490 @@
+// LM heads: the centroid-masked head (top-k of centroid scores, gathered cluster rows, sparse logits, scatter and
+// argmax keys), the dense tied head, the cluster-order table build, the final argmax and the -1e30 fill.
+//
+// Pages cited (by title; sections as headed on each page):
+//   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
+//   [Inventory]  "Gemma 4 Assistant (MTP drafter) - tensor inventory (Stage 0)"
+//   [Guide]      "Gemma 4 Assistant 使用指南：用 MTP 投机解码与 KV Sharing 加速 Gemma 4 推理" (gitcode blog)
+#include "device.h"
+
+namespace mtpd {
+namespace {
+
+// ------------------------------------------------------------------------------------------------------------
+// masked head ([Inventory] "Centroid / ordered embeddings LM head" steps 2-5)
+// grid (k, B), 256 threads. Every block of a row recomputes the row's top-k (radix select over order-preserving
+// keys; exact, ties to the lower index) and keeps its slot j; 16 groups of 16 lanes then score the slot's cluster.
+
+// NPT scores per thread (C <= 256 NPT), H = 128 HCH. Every score and hidden-state load is issued before the first
+// wait. Es is the head table in cluster order (row r = token_embd[ordering[r]]), so the selected cluster's rows are
+// contiguous and load together with their token ids. (No restrict on the loaded arrays: it would let the loads
+// sink below the issue barriers.)
+template <int NPT, int HCH>
+__global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float* scores, const int32_t* ordering,
+                                              const uint16_t* Es, const float* h, int32_t* __restrict__ sel,
+                                              int32_t* __restrict__ ids, float* __restrict__ z,
+                                              float* __restrict__ logits, size_t V, uint64_t* __restrict__ keys) {
+  constexpr int H = HCH * 128;
+  constexpr int HPT = (H + 255) / 256;  // hidden elements per thread
+  __shared__ uint32_t hist[2][4][256];  // per wave (fewer same-address atomics), double-buffered
+  __shared__ uint32_t sh_digit, sh_before, sh_n;
+  __shared__ uint64_t cand[kMaxCentroids];
+  __shared__ int sh_c;
+  __shared__ float hs[H];
+  __shared__ uint64_t red[4];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+
+  float sv[NPT], hv[HPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) sv[i] = scores[(size_t)b * C + min(tid + 256 * i, C - 1)];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) hv[i] = h[(size_t)b * H + min(tid + 256 * i, H - 1)];
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < HPT; ++i)
+    if (tid + 256 * i < H) hs[tid + 256 * i] = hv[i];
+  // scores -> order keys; entries beyond C never take part
+  uint32_t ok[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) ok[i] = f32_order(sv[i]);
+
+  // Slot j holds the (j+1)-th element in descending (score, then ascending index) order. Radix select on the order
+  // keys, 8 bits at a time from the top, narrows the search to the digit bin that holds that rank; once the bin
+  // holds a single element, that element is the answer. Only elements tied with the exact key (bin still larger
+  // than one after all four passes) need ordering by index, below. Histograms are double-buffered so that a pass
+  // takes two barriers: the scan wave reads one buffer while the others clear the next.
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t need = (uint32_t)j + 1u;
+  uint32_t inbin = 0;
+  hist[0][0][tid] = hist[0][1][tid] = hist[0][2][tid] = hist[0][3][tid] = 0u;
+  __syncthreads();
+  int buf = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (tid + 256 * i < C && (ok[i] & pmask) == prefix)
+        atomicAdd(&hist[buf][wave][(ok[i] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      uint32_t cnt[4], sum = 0;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const int dg = 255 - 4 * lane - q2;
+        cnt[q2] = hist[buf][0][dg] + hist[buf][1][dg] + hist[buf][2][dg] + hist[buf][3][dg];
+        sum += cnt[q2];
+      }
+      uint32_t incl = sum;  // inclusive prefix over lanes (higher digits first)
+#pragma unroll
+      for (int of = 1; of < 64; of <<= 1) {
+        const uint32_t t = __shfl_up(incl, of, 64);
+        if (lane >= of) incl += t;
+      }
+      uint32_t before = incl - sum;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        if (before < need && before + cnt[q2] >= need) {
+          sh_digit = 255u - 4u * lane - q2;
+          sh_before = before;
+          sh_n = cnt[q2];
+        }
+        before += cnt[q2];
+      }
+    } else {
+      const int ow = wave - 1;  // waves 1-3 clear the other buffer (all four wave histograms)
+      for (int i = ow * 64 + lane; i < 4 * 256; i += 3 * 64) (&hist[buf ^ 1][0][0])[i] = 0u;
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    pmask |= 255u << shift;
+    need -= sh_before;
+    inbin = sh_n;
+    buf ^= 1;
+    if (inbin == 1u) break;
+  }
+  if (inbin == 1u) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (tid + 256 * i < C && (ok[i] & pmask) == prefix) sh_c = tid + 256 * i;
+    __syncthreads();
+  } else {
+  // the bin's members as (key, ~index) composites: descending composite order is the slot order
+  __syncthreads();  // every wave has read the last bin count
+  if (tid == 0) sh_n = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int c = tid + 256 * i;
+    if (c < C && (ok[i] & pmask) == prefix) {
+      const uint32_t pos = atomicAdd(&sh_n, 1u);
+      cand[pos] = ((uint64_t)ok[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
+    }
+  }
+  __syncthreads();
+  const uint32_t ncand = sh_n;
+  if (ncand <= 64u) {
+    if (wave == 0) {
+      // lane e holds member e; its rank is the number of larger members, compared through scalar reads
+      // (fully unrolled over the 64 lanes: empty lanes hold 0, which is never larger than a member)
+      const uint64_t v = (uint32_t)lane < ncand ? cand[lane] : 0ull;
+      const int vhi = (int)(v >> 32), vlo = (int)(uint32_t)v;
+      uint32_t rank = 0;
+#pragma unroll
+      for (int f = 0; f < 64; ++f) {
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(vhi, f) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane(vlo, f);
+        rank += (o > v) ? 1u : 0u;
+      }
+      if ((uint32_t)lane < ncand && rank == need - 1u) sh_c = (int)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
+    }
+  } else {
+    // more than 64 elements share the exact key: their order is by index alone
+    for (uint32_t e = tid; e < ncand; e += 256) {
+      const uint64_t me = cand[e];
+      uint32_t rank = 0;
+      for (uint32_t f = 0; f < ncand; ++f) rank += (cand[f] > me) ? 1u : 0u;
+      if (rank == need - 1u) sh_c = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
+    }
+  }
+  __syncthreads();
+  }
+  const int c = sh_c;
+  if (tid == 0 && sel) sel[(size_t)b * k + j] = c;
+
+  // the cluster's candidate ids and their logits: group grp scores ids t = grp + 16 i, 8 ids per pass
+  const int grp = tid >> 4, l16 = tid & 15;
+  const int nper = vsc >> 4;  // ids per group (vsc % 16 == 0)
+  const int32_t* ord = ordering + (size_t)c * vsc;
+  const uint16_t* crow = Es + (size_t)c * vsc * H;
+  uint64_t best = 0;
+  for (int i0 = 0; i0 < nper; i0 += 8) {
+    int idv[8];
+    uint4 raw[8][HCH];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = min(grp + 16 * (i0 + u), vsc - 1);
+      idv[u] = ord[t];
+#pragma unroll
+      for (int ch = 0; ch < HCH; ++ch)
+        raw[u][ch] = *reinterpret_cast<const uint4*>(crow + (size_t)t * H + ch * 128 + l16 * 8);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < HCH; ++ch) {
+      const int col = ch * 128 + l16 * 8;
+      float hf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hf[e] = hs[col + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float ef[8];
+        unpack8(raw[u][ch], ef);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u] = fmaf(ef[e], hf[e], acc[u]);
+      }
+    }
+    XR<8, 8>::run(acc, l16);  // over the 16 lanes of the group: lane l16 holds id (l16 >> 1) of the 8
+    const int u = l16 >> 1;
+    int idu = idv[0];
+#pragma unroll
+    for (int w2 = 1; w2 < 8; ++w2) idu = (u == w2) ? idv[w2] : idu;
+    if ((l16 & 1) == 0 && i0 + u < nper) {
+      const int t = grp + 16 * (i0 + u);
+      const size_t slot = ((size_t)b * k + j) * vsc + t;
+      if (ids) ids[slot] = idu;
+      if (z) z[slot] = acc[0];
+      if (logits) logits[(size_t)b * V + idu] = acc[0];
+      best = u64_max(best, vid_key(acc[0], (uint32_t)idu));
+    }
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) red[wave] = best;
+  __syncthreads();
+  if (tid == 0) keys[(size_t)b * k + j] = u64_max(u64_max(red[0], red[1]), u64_max(red[2], red[3]));
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// dense tied head: logits[b][v] = E[v] . h[b] for every token ([Guide] section 5: with use_ordered_embeddings off
+// the head is the plain tied embedding; [MTP doc] "Variants supported": the large drafters use it), and the row's
+// argmax folded into one (value, id) key per row by atomic max (keys must hold 0 beforehand).
+//
+// The table is streamed once per pass of up to 32 batch rows, as a GEMM on v_mfma_f32_16x16x32_bf16:
+//   A = 16 table rows x 32 dims, loaded straight from HBM (lane l: row l%16, 8 dims at 8*(l/16) of each 32-dim
+//       step, so each row's 64 contiguous bytes per step come from 4 lanes and two steps cover a 128-byte line);
+//   B = the pass's hidden states from LDS, each fp32 value split into bf16 hi + lo (h = hi + lo within 2^-16
+//       relative), two products per step, so the logits keep fp32-level accuracy;
+//   D = 16 rows x 16 batch columns: lane l holds rows 4*(l/16) .. +3 of column l%16.
+// A wave owns 32-row groups (two 16-row tiles) over the whole hidden dimension: no cross-wave reduction. Its loads
+// run in chunks of P steps, double-buffered, and the next group's first chunk is requested during the current
+// group's last chunk (from a clamped group index, so the issue count never depends on data).
+// grid (blocks, ceil(B / 32)), 1024 threads; NC = batch columns per pass (16 or 32), H = 256 * NPL.
+
+template <int NC, int NPL>
+__global__ __launch_bounds__(1024) void k_head_dense(int B, int V, const uint16_t* E, const float* h,
+                                                     float* __restrict__ logits, uint64_t* __restrict__ keys) {
+  constexpr int H = NPL * 256, KSTEPS = H / 32, LROW = H + 8, NBT = NC / 16;
+  // tiles per group, steps per chunk (fewer with 32 columns, whose operands take more registers), chunks per group
+  constexpr int RT = 2, P = NC == 32 ? 2 : 4, NCH = KSTEPS / P;
+  static_assert(NCH % 2 == 0, "chunks alternate between the two buffers");
+  constexpr int NW = 16;
+  __shared__ __attribute__((aligned(16))) uint16_t hs[2][NC][LROW];  // [hi / lo][column][dim], rows padded by 16 B
+  __shared__ uint64_t red[NW][NC];
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int c0 = blockIdx.y * NC;
+  const int ngroups = (V + 31) / 32;
+  const int gstride = gridDim.x * NW;
+  int grp = blockIdx.x * NW + wave;
+
+  // lane's pieces of row 32 gq + 16 r + n (clamped to V - 1) start at element 8 g4 of the row; step s adds 32 s.
+  // Offsets, not pointers, are carried between groups: pointers carried through the loop lose their global
+  // address space and become flat loads.
+  auto rows_of = [&](int gq, size_t (&ro)[RT]) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) ro[r] = (size_t)min(gq * 32 + r * 16 + n, V - 1) * H + 8 * g4;
+  };
+  auto load = [&](uint4 (&a)[P][RT], const size_t (&ro)[RT], int c) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) a[p][r] = ld_global16(E + ro[r] + (c * P + p) * 32);
+  };
+  uint4 a0[P][RT], a1[P][RT];
+  size_t rp[RT];
+  rows_of(min(grp, ngroups - 1), rp);
+  load(a0, rp, 0);
+
+  // stage the pass's hidden states as bf16 hi + lo (columns past B are zero)
+  constexpr int NV4 = NC * H / 4 / 1024;  // float4 per thread
+  static_assert(NV4 >= 1 && NC * H % 4096 == 0, "staging covers the columns exactly");
+  float4 hv[NV4];
+#pragma unroll
+  for (int i = 0; i < NV4; ++i) {
+    const int e = (tid + i * 1024) * 4, col = e / H, k = e % H;
+    const int b = min(c0 + col, B - 1);
+    hv[i] = *reinterpret_cast<const float4*>(h + (size_t)b * H + k);
+  }
+#pragma unroll
+  for (int i = 0; i < NV4; ++i) {
+    const int e = (tid + i * 1024) * 4, col = e / H, k = e % H;
+    const bool live = c0 + col < B;
+    const float f[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = live ? f[j] : 0.f;
+      hi[j] = f2bf(v);
+      lo[j] = f2bf(v - bf2f(hi[j]));
+    }
+    *reinterpret_cast<uint2*>(&hs[0][col][k]) =
+        make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2*>(&hs[1][col][k]) =
+        make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+  }
+  __syncthreads();
+
+  float best[NBT];
+  int bid[NBT];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    best[t] = -INFINITY;
+    bid[t] = -1;
+  }
+
+  auto compute = [&](const uint4 (&a)[P][RT], int c, f32x4 (&acc)[RT][NBT]) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int k = (c * P + p) * 32 + 8 * g4;
+      uint4 bh[NBT], bl[NBT];
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) {
+        bh[t] = *reinterpret_cast<const uint4*>(&hs[0][t * 16 + n][k]);
+        bl[t] = *reinterpret_cast<const uint4*>(&hs[1][t * 16 + n][k]);
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < NBT; ++t)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[p][r]),
+                                                              __builtin_bit_cast(bf16x8, bh[t]), acc[r][t], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < NBT; ++t)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[p][r]),
+                                                              __builtin_bit_cast(bf16x8, bl[t]), acc[r][t], 0, 0, 0);
+    }
+  };
+
+  while (grp < ngroups) {  // wave-uniform
+    size_t rn[RT];
+    rows_of(min(grp + gstride, ngroups - 1), rn);
+    f32x4 acc[RT][NBT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; c += 2) {
+      // the order as written (each buffer refilled right after its last use) is what bounds the live registers:
+      // the scheduler must not hoist later loads above the products
+      load(a1, rp, c + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(a0, c, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 2 < NCH)
+        load(a0, rp, c + 2);
+      else
+        load(a0, rn, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(a1, c + 1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // epilogue: full logits and the running (value, id) best per column; rows visited in increasing order, so a
+    // strict comparison keeps the lowest id among equal values
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row0 = grp * 32 + r * 16 + 4 * g4;
+      if (grp * 32 + r * 16 < V) {  // V % 16 == 0: a tile is wholly inside or outside the table
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) {
+          const int col = c0 + t * 16 + n;
+          const f32x4 v = acc[r][t];
+          if (logits && col < B)
+            *reinterpret_cast<float4*>(logits + (size_t)col * V + row0) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v[i] > best[t]) {
+              best[t] = v[i];
+              bid[t] = row0 + i;
+            }
+        }
+      }
+    }
+    grp += gstride;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) rp[r] = rn[r];
+  }
+
+  // block-wide best per column, then one atomic max per (block, column)
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    uint64_t kk = bid[t] >= 0 ? vid_key(best[t], (uint32_t)bid[t]) : 0ull;
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)kk, o, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(kk >> 32), o, 64);
+      kk = u64_max(kk, ((uint64_t)hi << 32) | lo);
+    }
+    if (g4 == 0) red[wave][t * 16 + n] = kk;
+  }
+  __syncthreads();
+  if (tid < NC && c0 + tid < B) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = u64_max(m, red[w][tid]);
+    if (m) atomicMax(reinterpret_cast<unsigned long long*>(keys + c0 + tid), (unsigned long long)m);
+  }
+}
+
+__global__ void k_zero_u64(uint64_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+// Head table in cluster order: out[r] = E[ordering[r]], rows of H bf16 (H % 8 == 0); grid ceil(V / 8), 256 threads,
+// 32 threads per row.
+__global__ __launch_bounds__(256) void k_gather_rows(const uint16_t* __restrict__ E, const int32_t* __restrict__ ordering,
+                                                     uint16_t* __restrict__ out, int V, int H) {
+  const int r = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (r >= V) return;
+  const uint4* src = reinterpret_cast<const uint4*>(E + (size_t)ordering[r] * H);
+  uint4* dst = reinterpret_cast<uint4*>(out + (size_t)r * H);
+  for (int i = threadIdx.x & 31; i < H / 8; i += 32) dst[i] = src[i];
+}
+
+// grid B, 64 threads
+__global__ void k_final(int k, const uint64_t* __restrict__ keys, int32_t* __restrict__ next,
+                        int32_t* __restrict__ out2, int stride2) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const uint64_t kv = (lane < k) ? keys[(size_t)b * k + min(lane, k - 1)] : 0ull;
+  const int32_t id = key_id(wave_max_u64(kv));
+  if (lane == 0) {
+    next[b] = id;
+    if (out2) out2[(size_t)b * stride2] = id;
+  }
+}
+
+__global__ void k_fill(float4* __restrict__ p, size_t n4, float* __restrict__ tail, int ntail) {
+  const float4 v = make_float4(-1e30f, -1e30f, -1e30f, -1e30f);
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) p[i] = v;
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = -1e30f;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,
+                       const int32_t* ordering, const uint16_t* Es, const float* h, int32_t* sel, int32_t* ids,
+                       float* z, float* logits, size_t V, uint64_t* keys) {
+  const dim3 grid(k, B);
+  const int npt = C <= 256 ? 1 : C <= 512 ? 2 : C <= 1024 ? 4 : C <= 2048 ? 8 : 16;
+#define MTPD_HEAD(NPT_, HCH_)                                                                                 \
+  if (npt == NPT_ && H == HCH_ * 128)                                                                         \
+    return go(k_head<NPT_, HCH_>, grid, 256, 0, s, C, k, vsc, scores, ordering, Es, h, sel, ids, z, logits, V, \
+              keys);
+  MTPD_HEAD(1, 2) MTPD_HEAD(2, 2) MTPD_HEAD(4, 2) MTPD_HEAD(8, 2) MTPD_HEAD(16, 2)
+  MTPD_HEAD(1, 4) MTPD_HEAD(2, 4) MTPD_HEAD(4, 4) MTPD_HEAD(8, 4) MTPD_HEAD(16, 4)
+  MTPD_HEAD(1, 6) MTPD_HEAD(2, 6) MTPD_HEAD(4, 6) MTPD_HEAD(8, 6) MTPD_HEAD(16, 6)
+  MTPD_HEAD(1, 8) MTPD_HEAD(2, 8) MTPD_HEAD(4, 8) MTPD_HEAD(8, 8) MTPD_HEAD(16, 8)
+#undef MTPD_HEAD
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_head_dense(hipStream_t s, int B, int V, int H, const uint16_t* E, const float* h, float* logits,
+                             uint64_t* keys) {
+  const int ngroups = (V + 31) / 32;
+  const int nc = B <= 16 ? 16 : 32;
+  const int nblk = (ngroups + 15) / 16;
+  const dim3 grid(nblk < 256 ? nblk : 256, (B + nc - 1) / nc);
+#define MTPD_HD(NC_, NPL_) \
+  if (nc == NC_ && H == NPL_ * 256) return go(k_head_dense<NC_, NPL_>, grid, 1024, 0, s, B, V, E, h, logits, keys);
+  MTPD_HD(16, 1) MTPD_HD(16, 2) MTPD_HD(16, 3) MTPD_HD(16, 4)
+  MTPD_HD(32, 1) MTPD_HD(32, 2) MTPD_HD(32, 3) MTPD_HD(32, 4)
+#undef MTPD_HD
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_keys(hipStream_t s, uint64_t* keys, int n) {
+  return go(k_zero_u64, (n + 255) / 256, 256, 0, s, keys, n);
+}
+
+hipError_t launch_gather_rows(hipStream_t s, const uint16_t* E, const int32_t* ordering, uint16_t* out, int V,
+                              int H) {
+  return go(k_gather_rows, (V + 7) / 8, 256, 0, s, E, ordering, out, V, H);
+}
+
+hipError_t launch_final(hipStream_t s, int B, int k, const uint64_t* keys, int32_t* next, int32_t* out2,
+                        int stride2) {
+  return go(k_final, B, 64, 0, s, k, keys, next, out2, stride2);
+}
+
+hipError_t launch_fill(hipStream_t s, float* logits, size_t n) {
+  const size_t n4 = n / 4;
+  const int ntail = (int)(n - n4 * 4);
+  size_t grid = (n4 + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  return go(k_fill, (unsigned)grid, 256, 0, s, reinterpret_cast<float4*>(logits), n4, logits + n4 * 4, ntail);
+}
+
+}  // namespace mtpd
