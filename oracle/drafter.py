@@ -227,13 +227,24 @@ class SharedKV:
     [Guide] section 2(4): shared_kv_states {full_attention, sliding_attention} -> (key, value)).
 
     k[t], v[t]: [B][n_kv][cap][head_dim] bf16 bits (v may be the same array as k: K = V);
-    lens[t]: valid keys per row, keys [0, len) ; rope: [B][2 types][2 (cos, sin)][head_dim/2] fp32.
-    Type index 0 = sliding, 1 = full.
+    lens[t]: valid keys per row; rope: [B][2 types][2 (cos, sin)][head_dim/2] fp32. Type index 0 = sliding, 1 = full.
+    first[t] (optional, default 0): slot of each row's oldest valid key. Row b's valid keys, oldest first, are slots
+    (first + i) mod cap for i < len: a left-padded batch ([Guide] section 2 "create_attention_masks" and
+    padding_side="left") starts at its padding width, a ring-buffer cache at its oldest slot.
     """
     k: Sequence[np.ndarray]
     v: Sequence[np.ndarray]
     lens: Sequence[Sequence[int]]
     rope: np.ndarray
+    first: Optional[Sequence[Sequence[int]]] = None
+
+    def slots(self, t: int, b: int, a0: int, a1: int) -> np.ndarray:
+        """Cache slots of the row's valid keys a0 .. a1 - 1 (oldest first)."""
+        cap = self.k[t].shape[2]
+        f = 0 if self.first is None else int(self.first[t][b])
+        if not (0 <= f < cap and 0 <= a0 <= a1 <= int(self.lens[t][b]) <= cap):
+            raise ValueError("cache window outside the cache")
+        return (f + np.arange(a0, a1)) % cap
 
 
 # ----------------------------------------------------------------------------------------------------------------
@@ -259,8 +270,9 @@ def decoder_layer(m: Model, l: int, x: np.ndarray, b: int, kv: SharedKV) -> np.n
     for h in range(cfg.n_head):
         g = h * cfg.n_kv_head // cfg.n_head
         qh = rope_rotate(rmsnorm(q[h], L["q_norm"], cfg.rms_eps), cos, sin)
-        K = bf16_to_f64(kv.k[t][b, g, a0:a1])
-        V = K if kv.v[t] is kv.k[t] else bf16_to_f64(kv.v[t][b, g, a0:a1])
+        sl = kv.slots(t, b, a0, a1)
+        K = bf16_to_f64(kv.k[t][b, g, sl])
+        V = K if kv.v[t] is kv.k[t] else bf16_to_f64(kv.v[t][b, g, sl])
         o[h] = attend(qh, K, V, cfg.attn_scale)
     x = r + rmsnorm(L["o"] @ o.reshape(-1), L["post_attn_norm"], cfg.rms_eps)
     r = x

@@ -308,6 +308,51 @@ def test_draft_block_equals_chained_steps():
         cur_h, cur_t = s["hidden_out"], s["next"]
 
 
+def test_left_padded_and_ring_caches_equal_the_linear_cache():
+    """The same keys stored left-padded (row b's keys after pad_b junk slots) or in a ring-buffer sliding cache
+    (capacity 24 >= window, position p in slot p mod 24, oldest slot first) give bit-identical steps: only the slot
+    of each key changes, and the keys are gathered oldest first."""
+    m, w, shape = _tiny_model()
+    wl, d, kv = _tiny_inputs(shape, batch=3, context=40, ragged=True)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    tok = d["last_token"].numpy()
+    ref = O.drafter_step(m, th, tok, emb, kv)
+    r = rng(30)
+    B, nkv, cap, hd = kv.k[0].shape
+    # left padding: pad_b junk slots, then the row's keys; both caches
+    pads = [5, 0, 11]
+    padded, firsts = [], []
+    for t in range(2):
+        big = r.integers(0, 1 << 16, size=(B, nkv, cap + 11, hd), dtype=np.uint16)
+        for b in range(B):
+            L = int(kv.lens[t][b])
+            big[b, :, pads[b]:pads[b] + L] = kv.k[t][b, :, :L]
+        padded.append(big)
+        firsts.append(pads)
+    kvp = O.SharedKV(k=padded, v=padded, lens=kv.lens, rope=kv.rope, first=firsts)
+    got = O.drafter_step(m, th, tok, emb, kvp)
+    assert np.array_equal(got["hidden_out"], ref["hidden_out"]) and np.array_equal(got["next"], ref["next"])
+    # ring-buffer sliding cache of 24 slots holding the last 24 positions of each row
+    C = 24
+    ring = r.integers(0, 1 << 16, size=(B, nkv, C, hd), dtype=np.uint16)
+    rlen, rfirst = [], []
+    for b in range(B):
+        L = int(kv.lens[0][b])
+        n = min(L, C)
+        for p in range(L - n, L):
+            ring[b, :, p % C] = kv.k[0][b, :, p]
+        rlen.append(n)
+        rfirst.append((L - n) % C)
+    kvr = O.SharedKV(k=[ring, kv.k[1]], v=[ring, kv.k[1]], lens=[rlen, kv.lens[1]], rope=kv.rope,
+                     first=[rfirst, [0] * B])
+    got = O.drafter_step(m, th, tok, emb, kvr)
+    assert any(f + n > C for f, n in zip(rfirst, rlen))  # at least one row wraps around the end
+    assert np.array_equal(got["hidden_out"], ref["hidden_out"]) and np.array_equal(got["next"], ref["next"])
+    with pytest.raises(ValueError):
+        O.SharedKV(k=[ring, kv.k[1]], v=[ring, kv.k[1]], lens=[[C + 1] * B, kv.lens[1]], rope=kv.rope).slots(0, 0, 0, 3)
+
+
 def test_step_rows_are_independent():
     m, w, shape = _tiny_model()
     wl, d, kv = _tiny_inputs(shape)
