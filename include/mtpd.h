@@ -105,12 +105,16 @@ typedef struct {
 
 /* One shared cache of the target ([MTP doc] "Runtime implementation", piece 1; [Guide] section 2(4),
  * shared_kv_states): k, v [batch][n_kv_head][cap][head_dim] bf16; v may equal k (K = V, [Inventory]
- * "Notes for llama.cpp port" 2), in which case it is read once. len is a HOST array [batch]: row b's valid keys
- * are [0, len[b]), 1 <= len[b] <= cap. */
+ * "Notes for llama.cpp port" 2), in which case it is read once. len is a HOST array [batch], 1 <= len[b] <= cap.
+ * first is an optional HOST array [batch] (NULL = all zero), 0 <= first[b] < cap: row b's valid keys, oldest
+ * first, are the slots (first[b] + i) mod cap for i < len[b]. A left-padded batch ([Guide] section 2,
+ * "create_attention_masks" and padding_side="left") passes its padding widths; a ring-buffer cache passes the
+ * slot of its oldest key. */
 typedef struct {
   const uint16_t *k, *v;
   int32_t cap;
   const int32_t *len;
+  const int32_t *first;
 } mtpd_kv;
 
 /* The two caches a drafter layer can read, plus the rotary tables for each row's constant position
@@ -187,7 +191,7 @@ MTPD_API int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char **names
 /* Message for the last non-OK return on the calling thread ("" if none). */
 MTPD_API const char *mtpd_last_error(void);
 
-/* ABI version: 1. */
+/* ABI version: 2 (mtpd_kv gained `first`). */
 MTPD_API int32_t mtpd_abi_version(void);
 
 #ifdef __cplusplus

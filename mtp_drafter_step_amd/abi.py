@@ -45,7 +45,7 @@ class mtpd_weights(C.Structure):
 
 
 class mtpd_kv(C.Structure):
-    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("cap", C.c_int32), ("len", i32p)]
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("cap", C.c_int32), ("len", i32p), ("first", i32p)]
 
 
 class mtpd_shared_kv(C.Structure):

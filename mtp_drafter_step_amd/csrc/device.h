@@ -181,6 +181,10 @@ __device__ __forceinline__ void unpack8(uint4 w, float* f) {
   f[4] = bf_lo(w.z); f[5] = bf_hi(w.z); f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
 }
 
+// Cache slot of key index t of a row's window: windows are given as [start, start + count) with start < cap and
+// count <= cap, and indices past the end of the cache wrap to its beginning (ring-buffer caches)
+__device__ __forceinline__ int slot_of(int t, int cap) { return t >= cap ? t - cap : t; }
+
 inline int row_groups(int B) { return (B + kRG - 1) / kRG; }
 
 // Launch `k` on `s`; when timing events are pending they are attached to this launch (recorded by the runtime at

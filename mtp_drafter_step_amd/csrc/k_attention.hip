@@ -67,7 +67,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
   int t0 = k0 + wave * KB;
   if (t0 < k1) {
 #pragma unroll
-    for (int j = 0; j < KB; ++j) kcur[j] = *reinterpret_cast<const Raw*>(Kb + (size_t)min(t0 + j, k1 - 1) * HD);
+    for (int j = 0; j < KB; ++j) kcur[j] = *reinterpret_cast<const Raw*>(Kb + (size_t)slot_of(min(t0 + j, k1 - 1), cap) * HD);
   }
 
   // q_norm + rotation at the row's constant position ([Guide] section 2(2))
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
     const int tn = t0 + NW * KB;
     if (tn < k1) {  // next batch in flight while this one is computed
 #pragma unroll
-      for (int j = 0; j < KB; ++j) knext[j] = *reinterpret_cast<const Raw*>(Kb + (size_t)min(tn + j, k1 - 1) * HD);
+      for (int j = 0; j < KB; ++j) knext[j] = *reinterpret_cast<const Raw*>(Kb + (size_t)slot_of(min(tn + j, k1 - 1), cap) * HD);
     }
     float sc[64];
 #pragma unroll
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
     Raw vraw[KB];
     if (!same_v) {
 #pragma unroll
-      for (int j = 0; j < KB; ++j) vraw[j] = *reinterpret_cast<const Raw*>(Vb + (size_t)min(t0 + j, k1 - 1) * HD);
+      for (int j = 0; j < KB; ++j) vraw[j] = *reinterpret_cast<const Raw*>(Vb + (size_t)slot_of(min(t0 + j, k1 - 1), cap) * HD);
     }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   uint4 ka[KSTEPS], kn[KSTEPS];
   int t0 = k0 + wave * 16;
   {
-    const uint16_t* r = Kb + (size_t)min(t0 + hq, k1 - 1) * HD;
+    const uint16_t* r = Kb + (size_t)slot_of(min(t0 + hq, k1 - 1), cap) * HD;
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) ka[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
   }
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   for (; t0 < k1; t0 += S) {
     const int tb = t0;
     {
-      const uint16_t* r = Kb + (size_t)min(t0 + S + hq, k1 - 1) * HD;
+      const uint16_t* r = Kb + (size_t)slot_of(min(t0 + S + hq, k1 - 1), cap) * HD;
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) kn[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
     }
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = ka[c];
     } else {
-      const uint16_t* r = Vb + (size_t)min(tb + hq, k1 - 1) * HD;
+      const uint16_t* r = Vb + (size_t)slot_of(min(tb + hq, k1 - 1), cap) * HD;
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c)
         *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = *reinterpret_cast<const uint4*>(r + 32 * c);

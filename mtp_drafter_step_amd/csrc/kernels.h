@@ -15,7 +15,8 @@ constexpr int kRowGroup = 4;   // batch rows handled together by the dense kerne
 constexpr int kMaxTopK = 64;   // clusters kept per row
 constexpr int kMaxCentroids = 4096;
 
-// Per-row key window [start, start + count) of one cache, passed by value.
+// Per-row key window [start, start + count) of one cache, passed by value; start < cap, count <= cap, and indices
+// from cap on wrap to slot index - cap.
 struct RowWindows {
   int32_t start[kMaxBatch];
   int32_t count[kMaxBatch];

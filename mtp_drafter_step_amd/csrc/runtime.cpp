@@ -226,8 +226,12 @@ int check_kv(const mtpd_handle_s* h, const mtpd_kv& kv, int B, const char* name,
   for (int b = 0; b < B; ++b) {
     const int L = kv.len[b];
     if (L < 1 || L > kv.cap) return fail(MTPD_ESHAPE, "%s.len[%d] = %d outside [1, cap=%d]", name, b, L, kv.cap);
+    const int f = kv.first ? kv.first[b] : 0;
+    if (f < 0 || f >= kv.cap) return fail(MTPD_ESHAPE, "%s.first[%d] = %d outside [0, cap=%d)", name, b, f, kv.cap);
+    // the last n valid keys; window indices from cap on wrap to the start of the cache
     const int n = full ? L : std::min(L, h->cfg.swa_window);
-    win->start[b] = L - n;
+    const int s0 = f + (L - n);
+    win->start[b] = s0 >= kv.cap ? s0 - kv.cap : s0;
     win->count[b] = n;
   }
   return MTPD_OK;
@@ -384,6 +388,8 @@ ChainView chain_view(const mtpd_handle_s* h, const mtpd_shared_kv* kv, const mtp
   v.kv.full.v = kv->full.v + (size_t)b0 * fs;
   v.kv.sliding.len = kv->sliding.len + b0;
   v.kv.full.len = kv->full.len + b0;
+  if (kv->sliding.first) v.kv.sliding.first = kv->sliding.first + b0;
+  if (kv->full.first) v.kv.full.first = kv->full.first + b0;
   v.kv.rope = kv->rope + (size_t)b0 * 2 * hd;
   for (int t = 0; t < 2; ++t) {
     std::memset(&v.win[t], 0, sizeof(v.win[t]));
@@ -506,7 +512,7 @@ CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs
 
 extern "C" {
 
-int32_t mtpd_abi_version(void) { return 1; }
+int32_t mtpd_abi_version(void) { return 2; }
 
 const char* mtpd_last_error(void) { return g_last_error.c_str(); }
 

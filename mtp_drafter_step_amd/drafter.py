@@ -29,23 +29,28 @@ def _stream() -> int:
 
 class SharedKV:
     """The two target caches ([batch][n_kv][cap][head_dim] bf16 device tensors, v may be k), HOST per-row lengths,
-    and the rotary table [batch][2][2][head_dim/2] fp32 on the device."""
+    optional HOST per-row first slots (left padding, ring buffers), and the rotary table [batch][2][2][head_dim/2]
+    fp32 on the device."""
 
     def __init__(self, k_sliding, k_full, len_sliding: Sequence[int], len_full: Sequence[int], rope,
-                 v_sliding=None, v_full=None):
+                 v_sliding=None, v_full=None, first_sliding: Optional[Sequence[int]] = None,
+                 first_full: Optional[Sequence[int]] = None):
         self.k = (k_sliding, k_full)
         self.v = (k_sliding if v_sliding is None else v_sliding, k_full if v_full is None else v_full)
         self.lens = ([int(x) for x in len_sliding], [int(x) for x in len_full])
+        self.first = tuple(None if f is None else [int(x) for x in f] for f in (first_sliding, first_full))
         self.rope = rope
 
     def struct(self):
         arrs = [(C.c_int32 * len(l))(*l) for l in self.lens]
+        firsts = [None if f is None else (C.c_int32 * len(f))(*f) for f in self.first]
         kvs = []
         for t in range(2):
             kvs.append(abi.mtpd_kv(k=_ptr(self.k[t]), v=_ptr(self.v[t]), cap=int(self.k[t].shape[2]),
-                                   len=C.cast(arrs[t], abi.i32p)))
+                                   len=C.cast(arrs[t], abi.i32p),
+                                   first=None if firsts[t] is None else C.cast(firsts[t], abi.i32p)))
         s = abi.mtpd_shared_kv(sliding=kvs[0], full=kvs[1], rope=_ptr(self.rope))
-        return s, arrs  # keep the length arrays alive for the call
+        return s, (arrs, firsts)  # keep the host arrays alive for the call
 
 
 class Drafter:

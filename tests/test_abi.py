@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mtpd_\w+)", out))
     assert exported == set(declared_functions())
-    assert L.mtpd_abi_version() == 1
+    assert L.mtpd_abi_version() == 2
 
 
 def test_struct_layout_matches_c(tmp_path):
@@ -42,7 +42,7 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu\\n", sizeof(mtpd_config), sizeof(mtpd_layer), sizeof(mtpd_weights), sizeof(mtpd_kv),
          sizeof(mtpd_shared_kv));
   printf("%zu %zu %zu %zu %zu\\n", offsetof(mtpd_config, embed_scale), offsetof(mtpd_layer, layer_output_scale),
-         offsetof(mtpd_weights, layers), offsetof(mtpd_kv, len), offsetof(mtpd_shared_kv, rope));
+         offsetof(mtpd_weights, layers), offsetof(mtpd_kv, first), offsetof(mtpd_shared_kv, rope));
   return 0;
 }
 """)
@@ -54,7 +54,7 @@ int main(void) {
     assert sizes == [C.sizeof(abi.mtpd_config), C.sizeof(abi.mtpd_layer), C.sizeof(abi.mtpd_weights),
                      C.sizeof(abi.mtpd_kv), C.sizeof(abi.mtpd_shared_kv)]
     assert offs == [abi.mtpd_config.embed_scale.offset, abi.mtpd_layer.layer_output_scale.offset,
-                    abi.mtpd_weights.layers.offset, abi.mtpd_kv.len.offset, abi.mtpd_shared_kv.rope.offset]
+                    abi.mtpd_weights.layers.offset, abi.mtpd_kv.first.offset, abi.mtpd_shared_kv.rope.offset]
 
 
 def good_config(**over):

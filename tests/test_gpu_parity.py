@@ -152,6 +152,68 @@ def test_vector_alu_attention_at_head_dim_256():
         assert tally.tok_checked >= 1
 
 
+def test_left_padded_and_ring_buffer_caches():
+    """The same keys in a left-padded batch (both caches, junk before each row's keys) and in a ring-buffer
+    sliding cache (capacity 700 >= window 512, position p in slot p mod 700, rows wrapping past the end) give
+    outputs bit-identical to the linear caches (same keys in the same order and splits), and match the oracle."""
+    from mtp_drafter_step_amd import SharedKV, abi
+    case = Case(synth.E4B, batch=4, context=1500, ragged=True)
+    B = 4
+    ref = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    ref = {k: v.clone() for k, v in ref.items()}
+    lens = case.kv.lens
+    g = torch.Generator(device="cuda").manual_seed(5)
+    # left padding
+    pads = [0, 17, 64, 3]
+    padded = []
+    for t in range(2):
+        k = case.kv.k[t]
+        big = torch.randint(-32768, 32767, (B, k.shape[1], k.shape[2] + 64, k.shape[3]), generator=g, device="cuda",
+                            dtype=torch.int32).to(torch.int16)
+        for b in range(B):
+            big[b, :, pads[b]:pads[b] + lens[t][b]] = k[b, :, :lens[t][b]]
+        padded.append(big)
+    kvp = SharedKV(padded[0], padded[1], lens[0], lens[1], case.kv.rope, first_sliding=pads, first_full=pads)
+    say("left-padded caches")
+    got = case.drafter.drafter_step(case.th, case.tok, case.temb, kvp, want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), f"left padding: {k}"
+    # ring-buffer sliding cache
+    C = 700
+    ks = case.kv.k[0]
+    ring = torch.randint(-32768, 32767, (B, ks.shape[1], C, ks.shape[3]), generator=g, device="cuda",
+                         dtype=torch.int32).to(torch.int16)
+    rlen, rfirst = [], []
+    for b in range(B):
+        L = lens[0][b]
+        n = min(L, C)
+        pos = torch.arange(L - n, L, device="cuda")
+        ring[b, :, pos % C] = ks[b, :, L - n:L]
+        rlen.append(n)
+        rfirst.append((L - n) % C)
+    assert any(f + n > C for f, n in zip(rfirst, rlen))
+    kvr = SharedKV(ring, case.kv.k[1], rlen, lens[1], case.kv.rope, first_sliding=rfirst)
+    say("ring-buffer sliding cache")
+    got = case.drafter.drafter_step(case.th, case.tok, case.temb, kvr, want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), f"ring buffer: {k}"
+    # the oracle on the ring layout
+    ring_np = ring.cpu().numpy().view(np.uint16)
+    okv = O.SharedKV(k=[ring_np, case.kv_cpu.k[1]], v=[ring_np, case.kv_cpu.k[1]], lens=[rlen, lens[1]],
+                     rope=case.kv_cpu.rope, first=[rfirst, [0] * B])
+    oref = O.drafter_step(case.model, case.inp["target_hidden"].numpy().view(np.uint16), case.inp["last_token"].numpy(),
+                          case.temb_cpu, okv)
+    tally = compare_step(case, got, oref, list(range(B)), where="ring")
+    say(tally.summary())
+    # a first slot outside the cache is rejected before anything runs
+    bad = SharedKV(ring, case.kv.k[1], rlen, lens[1], case.kv.rope, first_sliding=[C, 0, 0, 0])
+    with pytest.raises(abi.MtpdError) as ei:
+        case.drafter.drafter_step(case.th, case.tok, case.temb, bad)
+    assert "first" in str(ei.value)
+
+
 def test_drafter_step_is_deterministic():
     case = Case(synth.E4B, batch=4, context=2000, ragged=True)
     a = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
