@@ -26,7 +26,11 @@ Readings where the pages are silent or disagree (each also listed in the design 
   * top-k order: descending fp32 score, ties to the lower centroid index; argmax ties to the lowest token id;
   * mask value: fp32(-1e30) ([Inventory] "Centroid / ordered embeddings LM head", step 5);
   * precision: the configurations state bf16 weights with fp32 accumulation and nothing about rounding activations,
-    so activations stay unrounded (fp64 here, fp32 on the GPU) and only stored tensors are bf16.
+    so activations stay unrounded (fp64 here, fp32 on the GPU) and only stored tensors are bf16;
+  * sampling at temperature T > 0: p = softmax(row / T) over the scored tokens (the -1e30 entries have p = 0),
+    drawn by inverse CDF with a caller-supplied uniform u in [0, 1), the CDF running in the head table's row order
+    (masked head: selected clusters by ascending index, each cluster's ids in ordering order; dense head: token
+    order), so that the draw does not depend on how near-equal centroid scores are ranked.
 """
 from __future__ import annotations
 
@@ -333,9 +337,39 @@ def dense_head_result(m: Model, h: np.ndarray) -> Dict[str, object]:
             "margin": float(top2[1] - top2[0]), "row": row}
 
 
+def head_order(m: Model, sel: Optional[np.ndarray]) -> np.ndarray:
+    """The scored tokens in the head table's row order: for the masked head the selected clusters by ascending
+    cluster index, each cluster's vsc ids as the ordering lists them ([Inventory] "Centroid / ordered embeddings LM
+    head", step 3); for the dense head every token in id order."""
+    if m.cfg.dense:
+        return np.arange(m.cfg.vocab, dtype=np.int64)
+    return m.ordering.reshape(m.cfg.n_centroids, m.cfg.vsc)[np.sort(np.asarray(sel))].reshape(-1)
+
+
+def sample_row(values: np.ndarray, order: np.ndarray, temperature: float, u: float) -> Dict[str, object]:
+    """Draw one token from p = softmax(values / temperature) by inverse CDF at u in [0, 1).
+
+    `values` are the fp32 logits of the tokens in `order` (the head table's row order). The token is the first one
+    whose cumulative probability exceeds u (the last token with p > 0 if rounding leaves the total below u).
+    Returns the token, its probability, and the distance from u to the nearer end of the token's CDF interval (how
+    far u is from selecting a neighbour)."""
+    z = np.asarray(values, dtype=np.float32).astype(np.float64)
+    e = np.exp((z - np.max(z)) / temperature)
+    p = e / np.sum(e)
+    c = np.cumsum(p)
+    above = np.nonzero(c > u)[0]
+    j = int(above[0]) if above.size else int(np.nonzero(p > 0)[0][-1])
+    lo = c[j] - p[j]
+    return {"token": int(order[j]), "prob": float(p[j]), "cdf_margin": float(min(u - lo, c[j] - u))}
+
+
 def drafter_step(m: Model, target_hidden, last_token, target_embd, kv: SharedKV, want_rows: bool = False,
-                 rows: Optional[Sequence[int]] = None) -> Dict[str, object]:
+                 rows: Optional[Sequence[int]] = None, temperature: Optional[float] = None,
+                 uniforms: Optional[Sequence[float]] = None) -> Dict[str, object]:
     """One drafter forward for every batch row (or the listed `rows`).
+
+    With a temperature > 0 the token is drawn by `sample_row` at uniforms[b] over the row's scored tokens instead of
+    taken by argmax, and its draft probability is returned ("prob"), as stochastic acceptance needs.
 
     Input: [target_last_hidden ; embed(last_token)] with the token embedded by the target's input table
     ([MTP doc] "What it is": 2x backbone input; [Explained] "Target Activations": the input embedding table is
@@ -360,7 +394,13 @@ def drafter_step(m: Model, target_hidden, last_token, target_embd, kv: SharedKV,
             x = decoder_layer(m, l, x, b, kv)
         h = rmsnorm(x, m.out_norm, cfg.rms_eps)
         res["hidden_out"][i] = bf16_bits(m.post @ h)  # handed back in bf16, the target's activation format
-        hd = dense_head_result(m, h) if cfg.dense else masked_head_row(m, h, want_row=want_rows)
+        hd = dense_head_result(m, h) if cfg.dense else masked_head_row(m, h, want_row=want_rows or bool(temperature))
+        if temperature:
+            order = head_order(m, hd["sel"])
+            smp = sample_row(hd["row"][order], order, temperature, float(uniforms[b]))
+            hd["next"] = smp["token"]
+            res.setdefault("prob", []).append(smp["prob"])
+            res.setdefault("cdf_margin", []).append(smp["cdf_margin"])
         res["next"][i] = hd["next"]
         for k in ("sel", "ids", "z", "scores", "cgap", "margin"):
             res[k].append(hd[k])
@@ -371,7 +411,8 @@ def drafter_step(m: Model, target_hidden, last_token, target_embd, kv: SharedKV,
 
 
 def draft_block(m: Model, n: int, target_hidden, last_token, target_embd, kv: SharedKV,
-                forced_tokens: Optional[np.ndarray] = None, rows: Optional[Sequence[int]] = None) -> List[Dict]:
+                forced_tokens: Optional[np.ndarray] = None, rows: Optional[Sequence[int]] = None,
+                temperature: Optional[float] = None, uniforms: Optional[np.ndarray] = None) -> List[Dict]:
     """n chained drafter steps at the constant position over the same shared cache.
 
     Step i+1 takes step i's post-projected hidden state and drafted token ([Explained] "Target Activations": the
@@ -386,7 +427,8 @@ def draft_block(m: Model, n: int, target_hidden, last_token, target_embd, kv: Sh
     rows = list(range(B)) if rows is None else list(rows)
     out = []
     for i in range(n):
-        r = drafter_step(m, th, tok, target_embd, kv, rows=rows)
+        r = drafter_step(m, th, tok, target_embd, kv, rows=rows, temperature=temperature,
+                         uniforms=None if uniforms is None else uniforms[i])
         out.append(r)
         for j, b in enumerate(rows):
             th[b] = r["hidden_out"][j]

@@ -204,6 +204,82 @@ def test_argmax_tie_goes_to_lowest_token():
     assert out["next"] == int(np.min(out["ids"]))
 
 
+# ---------------------------------------------------------------- sampling
+
+
+def test_sample_row_closed_form_weights():
+    """Logits T*log(w) at temperature T give p = w / sum(w) exactly in the limit of exact arithmetic (softmax of
+    log-weights): with w = 1, 2, 3, 4 the CDF steps are at 0.1, 0.3, 0.6, 1.0, so u picks the token whose interval
+    holds it, in the given order."""
+    order = np.array([907, 3, 55, 12])
+    for T in (0.5, 1.0, 3.0):
+        vals = (T * np.log([1.0, 2.0, 3.0, 4.0])).astype(np.float32)
+        for u, want, pw in ((0.0, 907, 0.1), (0.05, 907, 0.1), (0.15, 3, 0.2), (0.35, 55, 0.3), (0.65, 12, 0.4),
+                            (0.999999, 12, 0.4)):
+            r = O.sample_row(vals, order, T, u)
+            assert r["token"] == want and abs(r["prob"] - pw) < 1e-6
+        r = O.sample_row(vals, order, T, 0.3 + 1e-3)
+        assert r["token"] == 55 and abs(r["cdf_margin"] - 1e-3) < 1e-6
+
+
+def test_sample_row_uniform_and_peaked_limits():
+    order = np.arange(100, 140)
+    flat = np.full(40, 0.37, np.float32)
+    for u in (0.0, 0.013, 0.51, 0.987, 0.99999):  # off the CDF steps at multiples of 1/40
+        r = O.sample_row(flat, order, 0.8, u)
+        assert r["token"] == order[int(u * 40)] and abs(r["prob"] - 1 / 40) < 1e-12
+    # a tiny temperature puts all mass on the maximum (lowest position on ties) for any u
+    vals = rng(40).standard_normal(40).astype(np.float32)
+    for u in (0.0, 0.5, 0.999999):
+        r = O.sample_row(vals, order, 1e-6, u)
+        assert r["token"] == order[int(np.argmax(vals))] and r["prob"] == 1.0
+    # masked entries (-1e30) are never drawn, whatever u
+    vals2 = vals.copy()
+    vals2[::2] = O.NEG_FILL_F32
+    for u in np.linspace(0, 0.999999, 50):
+        assert (O.sample_row(vals2, order, 1.0, u)["token"] - 100) % 2 == 1
+
+
+def test_sample_frequencies_match_probabilities_on_a_grid():
+    """Inverse-CDF sampling over a fine grid of u reproduces each token's probability to within the grid step."""
+    vals = rng(41).standard_normal(12).astype(np.float32)
+    order = np.arange(12)
+    N = 20000
+    counts = np.zeros(12)
+    probs = {}
+    for k in range(N):
+        r = O.sample_row(vals, order, 0.9, (k + 0.5) / N)
+        counts[r["token"]] += 1
+        probs[r["token"]] = r["prob"]
+    for t, pr in probs.items():
+        assert abs(counts[t] / N - pr) <= 1.0 / N + 1e-12
+    assert abs(sum(probs.values()) - 1.0) < 1e-12 and len(probs) == 12
+
+
+def test_head_order_masked_and_dense():
+    m, w, shape = _tiny_model()
+    sel = np.array([5, 1, 6])
+    order = O.head_order(m, sel)
+    blocks = np.asarray(w["token_ordering"]).reshape(shape.n_centroids, shape.vsc)
+    assert np.array_equal(order, np.concatenate([blocks[1], blocks[5], blocks[6]]))
+    md, _, _ = _tiny_model(n_centroids=0, top_k=1)
+    assert np.array_equal(O.head_order(md, None), np.arange(shape.vocab))
+
+
+def test_sampled_step_at_tiny_temperature_is_the_argmax_step():
+    m, w, shape = _tiny_model()
+    wl, d, kv = _tiny_inputs(shape, batch=3)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    tok = d["last_token"].numpy()
+    ref = O.drafter_step(m, th, tok, emb, kv)
+    got = O.drafter_step(m, th, tok, emb, kv, temperature=1e-6, uniforms=[0.3, 0.9, 0.0])
+    for b in range(3):
+        if ref["margin"][b] > 1e-3:
+            assert got["next"][b] == ref["next"][b] and got["prob"][b] == 1.0
+    assert np.array_equal(got["hidden_out"], ref["hidden_out"])
+
+
 # ---------------------------------------------------------------- whole step
 
 
