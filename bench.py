@@ -37,7 +37,8 @@ CSRC = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc")
 # the source file of each kernel; a kernel's digest covers that file and the shared headers
 KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_head": "k_head.hip",
                "k_head_dense": "k_head.hip", "k_final": "k_head.hip", "k_fill": "k_head.hip",
-               "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip"}
+               "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip",
+               "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 512 << 20
 
@@ -45,7 +46,8 @@ COPY_PROBE_BYTES = 512 << 20
 SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma", "attn_full": "k_attn_mfma",
                "o_proj": "k_oproj",
                "down": "k_dense", "ffn": "k_ffn", "post": "k_post", "head": "k_head", "final": "k_final",
-               "scores": "k_dense", "fill": "k_fill", "head_dense": "k_head_dense", "zero_keys": "k_zero_u64"}
+               "scores": "k_dense", "fill": "k_fill", "head_dense": "k_head_dense", "zero_keys": "k_zero_u64",
+               "sample_tiles": "k_sample_tiles", "sample_pick": "k_sample_pick"}
 
 
 def site_kernel(site, shape):
@@ -114,6 +116,10 @@ def site_bytes(site, shape, batch, lens, distinct_clusters):
         return 8 * max(shape.top_k, 1) * B + 4 * B
     if site == "zero_keys":
         return 8 * B
+    if site == "sample_tiles":  # every scored logit once
+        return 4 * (shape.vocab if shape.n_centroids == 0 else shape.top_k * shape.vsc) * B
+    if site == "sample_pick":  # one 4096-wide tile per row, its ids, the tile sums, the drawn token and probability
+        return 4 * 4096 * B * (1 if shape.n_centroids == 0 else 2) + 4 * 256 * B + 8 * B
     raise KeyError(site)
 
 
@@ -205,7 +211,15 @@ def run_bench(args):
     ws = d.workspace(B)
     th, tok, temb = inp["target_hidden"], inp["last_token"], inp["target_embd"]
 
+    uni = None
+    if args.temperature:
+        g = torch.Generator(device=dev).manual_seed(wl.seed + 17)
+        uni = torch.rand(n, B, generator=g, device=dev, dtype=torch.float32)
+
     def run():
+        if args.temperature:
+            return d.draft_block_sampled(n, th, tok, temb, kv, args.temperature, uni, want_logits=True, out=out,
+                                         workspace=ws)
         return d.draft_block(n, th, tok, temb, kv, want_logits=True, out=out, workspace=ws)
 
     for _ in range(args.warmup):
@@ -312,7 +326,8 @@ def run_bench(args):
                    "backbone": shape.backbone, "hidden": shape.hidden, "vocab": shape.vocab,
                    "n_centroids": shape.n_centroids, "top_k": shape.top_k, "swa_window": shape.swa_window,
                    "head": "dense" if shape.n_centroids == 0 else "masked",
-                   "logits_row_written": True, "graph_replay": True},
+                   "logits_row_written": True, "graph_replay": True,
+                   "token_choice": f"sampled, temperature {args.temperature}" if args.temperature else "argmax"},
         "us_per_drafter_step": us_drafter_step,
         "us_per_drafter_step_p10_p90": [float(np.percentile(launch_ms, 10)) * 1e3 / n,
                                         float(np.percentile(launch_ms, 90)) * 1e3 / n],
@@ -435,6 +450,8 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=10, help="calls timed per kernel after the timed region")
     ap.add_argument("--cold-steps", type=int, default=10, help="calls timed after a cache-evicting sweep each")
     ap.add_argument("--workload", default="e4b_b16_ctx8192_block4")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="time draft_block_sampled at this temperature instead of the argmax draft_block")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter calibration copy after timing")

@@ -173,6 +173,27 @@ MTPD_API int mtpd_masked_head(mtpd_handle h, void *stream, void *workspace, int3
                      float *logits, int32_t *argmax, int32_t *sel_centroids, int32_t *sparse_ids,
                      float *sparse_logits);
 
+/* draft_block(n) with sampled tokens instead of the argmax, for stochastic acceptance ([MTP doc] "Runtime
+ * implementation (shipped)": the accept rate varies with temperature; [Inventory] "Centroid / ordered embeddings LM
+ * head", step 5: the full logits row exists for sampling). Step i draws its token from p = softmax(row / temperature)
+ * over the row's scored tokens (the masked head's top_k * vsc candidates, or the whole vocabulary with the dense
+ * head; masked entries have p = 0) by inverse CDF at uniforms[i][b], the CDF running in the head table's row order:
+ * the selected clusters by ascending cluster index, each cluster's ids in token_ordering order (dense head: token
+ * order). Step i+1 reads that token. temperature > 0 and finite; uniforms [n][batch] fp32 device, in [0, 1) (u >= 1
+ * draws the last token with p > 0). tokens [batch][n] int32 (required); probs [batch][n] fp32, the draft
+ * probability of each drawn token (optional); logits [n][batch][vocab] (optional); hidden_out as draft_block.
+ * With the dense head, vocab <= 1048576 (MTPD_EUNSUP otherwise). */
+MTPD_API int mtpd_draft_block_sampled(mtpd_handle h, void *stream, void *workspace, int32_t batch, int32_t n,
+                     const uint16_t *target_hidden, const int32_t *last_token, const uint16_t *target_embd,
+                     const mtpd_shared_kv *kv, float temperature, const float *uniforms, int32_t *tokens,
+                     float *probs, float *logits, uint16_t *hidden_out);
+
+/* The head alone with a sampled token: m rows of fp32 normed states h [m][hidden], one token per row drawn as in
+ * mtpd_draft_block_sampled at uniforms[b] ([m] device). token [m] int32 (required); prob [m] (optional); logits
+ * [m][vocab] (optional: the masked head's -1e30 row, or the dense row). */
+MTPD_API int mtpd_sample_head(mtpd_handle h, void *stream, void *workspace, int32_t m, const float *hidden,
+                     float temperature, const float *uniforms, int32_t *token, float *prob, float *logits);
+
 /* Kernel timing, a measurement aid outside the method. While enabled on a handle, drafter_step, draft_block and
  * masked_head launch their kernels directly on the caller's stream (captured graphs are not replayed) and attach
  * to each launch a pair of HIP events that the runtime records at the kernel's start and end. Enabling clears
@@ -182,7 +203,7 @@ MTPD_API int mtpd_timing_enable(mtpd_handle h, int32_t enable);
 
 /* Waits for the recorded events and copies min(cap, count) records in launch order: names[i] is a static label of
  * the launch site ("pre", "qproj", "attn_sliding", "attn_full", "attn_merge_sliding", "attn_merge_full",
- * "o_proj", "ffn", "down", "post", "head", "head_dense", "zero_keys", "final", "scores", "fill"), ms[i] its
+ * "o_proj", "ffn", "down", "post", "head", "head_dense", "zero_keys", "final", "scores", "fill", "sample_tiles", "sample_pick"), ms[i] its
  * duration in milliseconds.
  * names and ms are caller-owned host arrays of cap entries. Returns the number of records (which may exceed cap)
  * or a negative error code. */

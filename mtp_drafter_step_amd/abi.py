@@ -16,7 +16,8 @@ MTPD_OK, MTPD_EINVAL, MTPD_ESHAPE, MTPD_ENOMEM, MTPD_EHIP, MTPD_EUNSUP = 0, -1, 
 MTPD_MAX_BATCH = 64
 MTPD_MAX_TIMED = 4096
 SYMBOLS = ("mtpd_create", "mtpd_destroy", "mtpd_workspace_bytes", "mtpd_drafter_step", "mtpd_draft_block",
-           "mtpd_masked_head", "mtpd_last_error", "mtpd_abi_version", "mtpd_timing_enable", "mtpd_timing_read")
+           "mtpd_masked_head", "mtpd_last_error", "mtpd_abi_version", "mtpd_timing_enable", "mtpd_timing_read",
+           "mtpd_draft_block_sampled", "mtpd_sample_head")
 
 u16p = C.POINTER(C.c_uint16)
 i32p = C.POINTER(C.c_int32)
@@ -78,6 +79,11 @@ def lib() -> C.CDLL:
     L.mtpd_draft_block.restype = C.c_int
     L.mtpd_masked_head.argtypes = [vp, vp, vp, C.c_int32, vp, vp, vp, vp, vp, vp]
     L.mtpd_masked_head.restype = C.c_int
+    L.mtpd_draft_block_sampled.argtypes = [vp, vp, vp, C.c_int32, C.c_int32, vp, vp, vp, vp, C.c_float, vp, vp, vp,
+                                           vp, vp]
+    L.mtpd_draft_block_sampled.restype = C.c_int
+    L.mtpd_sample_head.argtypes = [vp, vp, vp, C.c_int32, vp, C.c_float, vp, vp, vp, vp]
+    L.mtpd_sample_head.restype = C.c_int
     L.mtpd_last_error.argtypes = []
     L.mtpd_last_error.restype = C.c_char_p
     L.mtpd_abi_version.argtypes = []

@@ -65,6 +65,11 @@ __device__ __forceinline__ uint32_t f32_order(float f) {
 __device__ __forceinline__ uint64_t vid_key(float v, uint32_t id) {
   return ((uint64_t)f32_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - id);
 }
+// the value of a (value, id) key (inverse of f32_order)
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
 __device__ __forceinline__ int32_t key_id(uint64_t k) { return (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)); }
 
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }

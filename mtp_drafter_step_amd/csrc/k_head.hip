@@ -428,6 +428,193 @@ __global__ void k_fill(float4* __restrict__ p, size_t n4, float* __restrict__ ta
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = -1e30f;
 }
 
+// ------------------------------------------------------------------------------------------------------------
+// temperature sampling: p = softmax(row / T) over the scored tokens, one token per row drawn by inverse CDF at the
+// caller's uniform u, the CDF running in the head table's row order (masked head: the selected clusters by ascending
+// cluster index, each cluster's ids in ordering order; dense head: token order). e = 2^((v - M) * log2(e) / T) with
+// M the row maximum, read from the argmax keys. The ordered elements are cut into tiles of 4096:
+//   k_sample_tiles: one block per (tile, row) sums its tile's e (fixed reduction order);
+//   k_sample_pick:  one block per row walks the tile sums to the tile holding u * S (S = their total), scans that
+//                   tile's e in order and takes the first element whose running sum exceeds u * S.
+// Both recompute e with the same instructions, so the walk and the scan see the same values.
+
+constexpr int kSampleThreads = 1024, kSampleTile = 4 * kSampleThreads;
+
+// Per-row setup shared by both kernels: the row maximum (into sh_M) and, for the masked head, the slot holding each
+// rank of the selected clusters' ascending order (into rank2slot).
+template <bool SPARSE>
+__device__ __forceinline__ void sample_setup(int b, int k, const int32_t* sel, const uint64_t* keys, int nk,
+                                             float* sh_M, int* rank2slot) {
+  __shared__ int sel_s[kMaxTopK];
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  // both loads of wave 0 go out before either is waited on
+  const uint64_t kraw = keys[(size_t)b * nk + min(lane, nk - 1)];
+  const int sraw = SPARSE ? sel[(size_t)b * k + min(lane, k - 1)] : 0;
+  if (wave == 0) {
+    const uint64_t kv = wave_max_u64(lane < nk ? kraw : 0ull);
+    if (lane == 0) *sh_M = key_value(kv);
+    if (SPARSE && lane < k) sel_s[lane] = sraw;
+  }
+  if (SPARSE) {  // each slot's rank among the selected clusters (ascending cluster index)
+    __syncthreads();
+    if (tid < k) {
+      const int sj = sel_s[tid];
+      int r = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) r += (j < k && sel_s[j] < sj) ? 1 : 0;
+      rank2slot[r] = tid;
+    }
+  }
+  __syncthreads();
+}
+
+// e of ordered elements r .. r + 3 (n % 4 == 0; zero past n) and their offset in the value array
+template <bool SPARSE>
+__device__ __forceinline__ size_t sample_load4(const float* vals, size_t rowbase, int n, int vsc, const int* rank2slot,
+                                               int r, float M, float c, float* e) {
+  const int rc = min(r, n - 4);
+  size_t off = rowbase + rc;
+  if (SPARSE) {
+    const int seg = rc / vsc;  // vsc % 4 == 0: the 4 elements share a cluster
+    off = rowbase + (size_t)rank2slot[seg] * vsc + (rc - seg * vsc);
+  }
+  const float4 v = *reinterpret_cast<const float4*>(vals + off);
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = (r < n) ? exp2f((vv[i] - M) * c) : 0.f;
+  return off;
+}
+
+// grid (tiles, B), kSampleThreads threads. vals: dense logits [B][n] or sparse logits [B][k][vsc] (n = k vsc).
+template <bool SPARSE>
+__global__ __launch_bounds__(kSampleThreads) void k_sample_tiles(int n, int vsc, int k, const float* vals,
+                                                                 const int32_t* sel, const uint64_t* keys, int nk,
+                                                                 float c, float* __restrict__ tsum) {
+  __shared__ float sh_M;
+  __shared__ int rank2slot[kMaxTopK];
+  __shared__ float wpart[kSampleThreads / 64];
+  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  sample_setup<SPARSE>(b, k, sel, keys, nk, &sh_M, rank2slot);
+  float e[4];
+  sample_load4<SPARSE>(vals, (size_t)b * n, n, vsc, rank2slot, t * kSampleTile + tid * 4, sh_M, c, e);
+  const float s = wave_sum((e[0] + e[1]) + (e[2] + e[3]));
+  if (lane_id() == 0) wpart[wave_id()] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSampleThreads / 64; ++w) a += wpart[w];
+    tsum[(size_t)b * kMaxSampleTiles + t] = a;
+  }
+}
+
+// grid B, kSampleThreads threads. Writes the token and its probability to tok_out / prob_out[b * out_stride] and the
+// token to tok_next[b] (each when set). ONE: the row's scored tokens fit one tile (the masked head); the total is
+// then the block sum of the same e values and no tile sums are read.
+template <bool SPARSE, bool ONE>
+__global__ __launch_bounds__(kSampleThreads) void k_sample_pick(int n, int vsc, int k, const float* vals,
+                                                                const int32_t* ids, const int32_t* sel,
+                                                                const uint64_t* keys, int nk, float c,
+                                                                const float* tsum, const float* u,
+                                                                int32_t* tok_out, float* prob_out, int out_stride,
+                                                                int32_t* tok_next) {
+  __shared__ float sh_M, sh_P, sh_S, sh_target;
+  __shared__ int sh_tile, sh_pick, sh_last;
+  __shared__ int rank2slot[kMaxTopK];
+  __shared__ float ts[kMaxSampleTiles];
+  __shared__ float wtot[kSampleThreads / 64];
+  const int b = blockIdx.x, tid = threadIdx.x, wave = wave_id(), lane = lane_id();
+  const int ntiles = (n + kSampleTile - 1) / kSampleTile;
+  const float ub = u[b];
+  if (!ONE && tid < ntiles) ts[tid] = tsum[(size_t)b * kMaxSampleTiles + tid];
+  if (tid == 0) {
+    sh_pick = 0x7FFFFFFF;
+    sh_last = -1;
+  }
+  sample_setup<SPARSE>(b, k, sel, keys, nk, &sh_M, rank2slot);
+  if (ONE) {
+    if (tid == 0) {
+      sh_tile = 0;
+      sh_P = 0.f;
+    }
+  } else if (tid == 0) {  // total, target, and the tile whose running sum first exceeds the target (in order)
+    float S = 0.f;
+    for (int t = 0; t < ntiles; ++t) S += ts[t];
+    const float target = ub * S;
+    float P = 0.f, Plast = 0.f;
+    int tile = -1, last = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      if (P + ts[t] > target) {
+        tile = t;
+        break;
+      }
+      if (ts[t] > 0.f) {
+        last = t;
+        Plast = P;
+      }
+      P += ts[t];
+    }
+    if (tile < 0) {  // rounding left the total at or below u * S: the last tile with mass (the row maximum has e = 1)
+      tile = last;
+      P = Plast;
+    }
+    sh_S = S;
+    sh_P = P;
+    sh_target = target;
+    sh_tile = tile;
+  }
+  __syncthreads();
+  const int r0 = sh_tile * kSampleTile + tid * 4;
+  float e[4];
+  const size_t off = sample_load4<SPARSE>(vals, (size_t)b * n, n, vsc, rank2slot, r0, sh_M, c, e);
+  int4 idv = make_int4(0, 0, 0, 0);  // the four elements' token ids, fetched with their logits
+  if (SPARSE) idv = *reinterpret_cast<const int4*>(ids + off);
+  const float s = (e[0] + e[1]) + (e[2] + e[3]);
+  // exclusive prefix of s over the block in thread order: wave inclusive scan, then the earlier waves' totals
+  float incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  float woff = 0.f;
+  for (int w = 0; w < wave; ++w) woff += wtot[w];
+  if (ONE) {  // every thread forms the same total from the wave totals
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSampleThreads / 64; ++w) S += wtot[w];
+    if (tid == 0) {
+      sh_S = S;
+      sh_target = ub * S;
+    }
+    __syncthreads();
+  }
+  float run = sh_P + woff + (incl - s);
+  const float target = sh_target;
+  int found = -1, lastpos = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    run += e[i];
+    if (found < 0 && run > target) found = i;
+    if (e[i] > 0.f) lastpos = i;
+  }
+  if (found >= 0) atomicMin(&sh_pick, r0 + found);
+  if (lastpos >= 0) atomicMax(&sh_last, r0 + lastpos);
+  __syncthreads();
+  const int pick = sh_pick != 0x7FFFFFFF ? sh_pick : sh_last;  // no crossing: rounding, take the last token with p > 0
+  if (r0 <= pick && pick < r0 + 4) {
+    const int i = pick - r0;
+    const int iv[4] = {idv.x, idv.y, idv.z, idv.w};
+    const int32_t token = SPARSE ? iv[i] : pick;
+    const float prob = e[i] / sh_S;
+    if (tok_out) tok_out[(size_t)b * out_stride] = token;
+    if (prob_out) prob_out[(size_t)b * out_stride] = prob;
+    if (tok_next) tok_next[b] = token;
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------------------
@@ -485,6 +672,30 @@ hipError_t launch_fill(hipStream_t s, float* logits, size_t n) {
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
   return go(k_fill, (unsigned)grid, 256, 0, s, reinterpret_cast<float4*>(logits), n4, logits + n4 * 4, ntail);
+}
+
+hipError_t launch_sample(hipStream_t s, int phase, int B, int n, int vsc, int k, const float* vals,
+                         const int32_t* ids, const int32_t* sel, const uint64_t* keys, int nk, float temperature,
+                         float* tsum, const float* u, int32_t* tok_out, float* prob_out, int out_stride,
+                         int32_t* tok_next) {
+  const int ntiles = (n + kSampleTile - 1) / kSampleTile;
+  if (ntiles > kMaxSampleTiles || n % 4 != 0 || (k > 0 && vsc % 4 != 0)) return hipErrorInvalidValue;
+  const float c = 1.4426950408889634f / temperature;
+  if (phase == 0) {  // a single tile needs no tile sums: nothing to launch
+    if (ntiles == 1) return hipSuccess;
+    if (k > 0) return go(k_sample_tiles<true>, dim3(ntiles, B), kSampleThreads, 0, s, n, vsc, k, vals, sel, keys, nk, c, tsum);
+    return go(k_sample_tiles<false>, dim3(ntiles, B), kSampleThreads, 0, s, n, vsc, k, vals, sel, keys, nk, c, tsum);
+  }
+#define MTPD_PICK(SP_, ONE_)                                                                                    \
+  return go(k_sample_pick<SP_, ONE_>, B, kSampleThreads, 0, s, n, vsc, k, vals, ids, sel, keys, nk, c, tsum, u, \
+            tok_out, prob_out, out_stride, tok_next)
+  if (k > 0) {
+    if (ntiles == 1) MTPD_PICK(true, true);
+    MTPD_PICK(true, false);
+  }
+  if (ntiles == 1) MTPD_PICK(false, true);
+  MTPD_PICK(false, false);
+#undef MTPD_PICK
 }
 
 }  // namespace mtpd

@@ -14,6 +14,7 @@ constexpr int kMaxSplit = 32;  // key-range splits of one (row, kv head)
 constexpr int kRowGroup = 4;   // batch rows handled together by the dense kernels
 constexpr int kMaxTopK = 64;   // clusters kept per row
 constexpr int kMaxCentroids = 4096;
+constexpr int kMaxSampleTiles = 256;  // sampled rows hold at most 256 * 4096 scored tokens
 
 // Per-row key window [start, start + count) of one cache, passed by value; start < cap, count <= cap, and indices
 // from cap on wrap to slot index - cap.
@@ -98,6 +99,17 @@ hipError_t launch_head_dense(hipStream_t s, int B, int V, int H, const uint16_t*
 
 // keys[0, n) = 0
 hipError_t launch_zero_keys(hipStream_t s, uint64_t* keys, int n);
+
+// Temperature sampling of one token per row: p = softmax(row / temperature) over the row's scored tokens, drawn
+// by inverse CDF at u[b] in the head table's order (k > 0: the masked head's sparse logits vals [B][k][vsc] with
+// their ids and the selected clusters sel [B][k], visited by ascending cluster index; k == 0: dense logits vals
+// [B][n]). The row maximum comes from keys [B][nk]. tsum: workspace [B][kMaxSampleTiles]. Phase 0 sums the tiles,
+// phase 1 draws: it writes the token and its probability at [b * out_stride] of tok_out / prob_out and the token to
+// tok_next[b] (each when set).
+hipError_t launch_sample(hipStream_t s, int phase, int B, int n, int vsc, int k, const float* vals,
+                         const int32_t* ids, const int32_t* sel, const uint64_t* keys, int nk, float temperature,
+                         float* tsum, const float* u, int32_t* tok_out, float* prob_out, int out_stride,
+                         int32_t* tok_next);
 
 // Masked head: per (row, selected slot j): top-k of the row's centroid scores (descending, ties to the lower
 // index), the cluster's token ids through the ordering, sparse logits token_embd[id] . h (rows read from Es, the

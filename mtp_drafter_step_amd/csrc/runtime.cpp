@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -51,6 +52,7 @@ struct CallKey {
   mtpd::RowWindows win[2];
   int32_t nsplit[2];
   int32_t caps[2];
+  uint32_t fbits;  // bits of a float argument baked into the kernels (the sampling temperature), else 0
   bool operator==(const CallKey& o) const { return std::memcmp(this, &o, sizeof(CallKey)) == 0; }
 };
 
@@ -90,7 +92,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Offsets of every intermediate in the caller's workspace for a given batch.
 struct Plan {
-  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, total;
+  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, stok, tsum, row, total;
 };
 
 // Argmax keys per row: one per selected cluster for the masked head, one for the dense head.
@@ -122,6 +124,9 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.ids = take((size_t)B * c.top_k * vsc * 4);
   p.z = take((size_t)B * c.top_k * vsc * 4);
   p.keys = take((size_t)B * key_slots(c) * 8);
+  p.stok = take((size_t)B * 4);                                  // sampled tokens (next step's input)
+  p.tsum = take((size_t)B * mtpd::kMaxSampleTiles * 4);          // sampling tile sums
+  p.row = take(c.n_centroids == 0 ? (size_t)B * c.vocab * 4 : 0);  // dense logits rows for sampling
   p.total = off;
   return p;
 }
@@ -486,9 +491,10 @@ int run_call(mtpd_handle_s* h, hipStream_t s, const CallKey& key, const Chains& 
 }
 
 CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs, const mtpd::RowWindows* win,
-                 const int* nsplit, const mtpd_shared_kv* kv) {
+                 const int* nsplit, const mtpd_shared_kv* kv, float farg = 0.f) {
   CallKey k;
   std::memset(&k, 0, sizeof(k));
+  std::memcpy(&k.fbits, &farg, sizeof(farg));
   k.kind = kind;
   k.chain = -1;
   k.batch = B;
@@ -720,6 +726,121 @@ int mtpd_masked_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
                      sparse_ids ? sparse_ids + b0 * kv_n : nullptr, sparse_logits ? sparse_logits + b0 * kv_n : nullptr));
       KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, c.top_k, at<uint64_t>(wsc, p.keys), argmax + b0, nullptr, 0));
       return MTPD_OK;
+  });
+}
+
+}  // extern "C"
+
+namespace {
+
+// Sampling of the row's token from the head outputs already in the workspace (sparse logits, ids and selected
+// clusters for the masked head; the logits row `dense_row` for the dense head).
+int run_sample(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const float* dense_row,
+               float temperature, const float* u, int32_t* tok_out, float* prob_out, int out_stride) {
+  const mtpd_config& c = h->cfg;
+  const bool dense = c.n_centroids == 0;
+  const int n = dense ? c.vocab : c.top_k * h->vsc;
+  const float* vals = dense ? dense_row : at<float>(ws, p.z);
+  const int k = dense ? 0 : c.top_k;
+  if (n > 4096)  // several tiles: their sums first (a single tile is summed by the draw itself)
+    KLAUNCH(h, "sample_tiles", mtpd::launch_sample(s, 0, B, n, h->vsc, k, vals, at<int32_t>(ws, p.ids), at<int32_t>(ws, p.sel),
+                                                 at<uint64_t>(ws, p.keys), key_slots(c), temperature,
+                                                 at<float>(ws, p.tsum), u, tok_out, prob_out, out_stride,
+                                                 at<int32_t>(ws, p.stok)));
+  KLAUNCH(h, "sample_pick", mtpd::launch_sample(s, 1, B, n, h->vsc, k, vals, at<int32_t>(ws, p.ids), at<int32_t>(ws, p.sel),
+                                                at<uint64_t>(ws, p.keys), key_slots(c), temperature,
+                                                at<float>(ws, p.tsum), u, tok_out, prob_out, out_stride,
+                                                at<int32_t>(ws, p.stok)));
+  return MTPD_OK;
+}
+
+int check_sampling(const mtpd_handle_s* h, float temperature, const float* u) {
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(MTPD_EINVAL, "temperature must be > 0 and finite");
+  if (!u) return fail(MTPD_EINVAL, "uniforms is NULL");
+  if (h->cfg.n_centroids == 0 && h->cfg.vocab > mtpd::kMaxSampleTiles * 4096)
+    return fail(MTPD_EUNSUP, "sampling the dense head needs vocab <= %d", mtpd::kMaxSampleTiles * 4096);
+  return MTPD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtpd_draft_block_sampled(mtpd_handle h, void* stream, void* workspace, int32_t batch, int32_t n,
+                             const uint16_t* target_hidden, const int32_t* last_token, const uint16_t* target_embd,
+                             const mtpd_shared_kv* kv, float temperature, const float* uniforms, int32_t* tokens,
+                             float* probs, float* logits, uint16_t* hidden_out) {
+  g_last_error.clear();
+  CHECK(check_call(h, workspace, batch));
+  if (n < 1 || n > 64) return fail(MTPD_ESHAPE, "n must be in [1, 64]");
+  CHECK(check_sampling(h, temperature, uniforms));
+  mtpd::RowWindows win[2];
+  int nsplit[2];
+  CHECK(check_step_inputs(h, batch, target_hidden, last_token, target_embd, kv, win, nsplit));
+  if (!tokens) return fail(MTPD_EINVAL, "tokens is NULL");
+  CHECK(check_ptr(hidden_out, "hidden_out"));
+  if (logits) CHECK(check_ptr(logits, "logits"));
+  const Chains ch = make_chains(batch);
+  const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
+  const mtpd_config& c = h->cfg;
+  const bool dense = c.n_centroids == 0;
+  const size_t BV = (size_t)batch * c.vocab;
+  const CallKey key = make_key(4, batch, n,
+                               {workspace, target_hidden, last_token, target_embd, kv->sliding.k, kv->sliding.v,
+                                kv->full.k, kv->full.v, kv->rope, uniforms, tokens, probs, logits, hidden_out},
+                               win, nsplit, kv, temperature);
+  return run_call(h, static_cast<hipStream_t>(stream), key, ch, [&](int ci, hipStream_t cs) -> int {
+      const int b0 = ch.rows[ci], Bc = ch.rows[ci + 1] - b0;
+      void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
+      const ChainView v = chain_view(h, kv, win, b0, Bc);
+      uint16_t* hid[2] = {at<uint16_t>(wsc, p.hid), at<uint16_t>(wsc, p.hid) + (size_t)Bc * c.backbone};
+      const uint64_t* keys = at<uint64_t>(wsc, p.keys);
+      for (int i = 0; i < n; ++i) {
+        const uint16_t* th = (i == 0) ? target_hidden + (size_t)b0 * c.backbone : hid[(i - 1) & 1];
+        // step i's token: the caller's for i = 0, else the token the previous step drew
+        const mtpd::TokenSource ts{i == 0 ? last_token + b0 : at<int32_t>(wsc, p.stok), keys, 0, key_slots(c),
+                                   nullptr, 0, nullptr};
+        uint16_t* hout = (i == n - 1) ? hidden_out + (size_t)b0 * c.backbone : hid[i & 1];
+        float* lrow = logits ? logits + (size_t)i * BV + (size_t)b0 * c.vocab : (dense ? at<float>(wsc, p.row) : nullptr);
+        // the masked head keeps its selected clusters, ids and sparse logits in the workspace for the sampler
+        CHECK(run_step(h, cs, wsc, p, Bc, th, ts, target_embd, &v.kv, v.win, v.nsplit, lrow, hout,
+                       dense ? nullptr : at<int32_t>(wsc, p.sel), dense ? nullptr : at<int32_t>(wsc, p.ids),
+                       dense ? nullptr : at<float>(wsc, p.z)));
+        CHECK(run_sample(h, cs, wsc, p, Bc, lrow, temperature, uniforms + (size_t)i * batch + b0,
+                         tokens + (size_t)b0 * n + i, probs ? probs + (size_t)b0 * n + i : nullptr, n));
+      }
+      return MTPD_OK;
+  });
+}
+
+int mtpd_sample_head(mtpd_handle h, void* stream, void* workspace, int32_t m, const float* hidden,
+                     float temperature, const float* uniforms, int32_t* token, float* prob, float* logits) {
+  g_last_error.clear();
+  CHECK(check_call(h, workspace, m));
+  CHECK(check_ptr(hidden, "hidden"));
+  CHECK(check_sampling(h, temperature, uniforms));
+  if (!token) return fail(MTPD_EINVAL, "token is NULL");
+  if (logits) CHECK(check_ptr(logits, "logits"));
+  const Chains ch = make_chains(m);
+  const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
+  const mtpd_config& c = h->cfg;
+  const bool dense = c.n_centroids == 0;
+  const CallKey key = make_key(5, m, 1, {workspace, hidden, uniforms, token, prob, logits}, nullptr, nullptr, nullptr,
+                               temperature);
+  return run_call(h, static_cast<hipStream_t>(stream), key, ch, [&](int ci, hipStream_t cs) -> int {
+      const int b0 = ch.rows[ci], Bc = ch.rows[ci + 1] - b0;
+      void* wsc = static_cast<char*>(workspace) + (size_t)ci * p.total;
+      const float* hc = hidden + (size_t)b0 * c.hidden;
+      float* lc = logits ? logits + (size_t)b0 * c.vocab : (dense ? at<float>(wsc, p.row) : nullptr);
+      if (dense) {
+        KLAUNCH(h, "zero_keys", mtpd::launch_zero_keys(cs, at<uint64_t>(wsc, p.keys), Bc));
+        CHECK(run_head(h, cs, wsc, p, Bc, hc, lc, nullptr, nullptr, nullptr));
+      } else {
+        KLAUNCH(h, "scores", mtpd::launch_scores(cs, Bc, c.hidden, c.n_centroids, hc, h->w.centroids, at<float>(wsc, p.scores)));
+        if (lc) KLAUNCH(h, "fill", mtpd::launch_fill(cs, lc, (size_t)Bc * c.vocab));
+        CHECK(run_head(h, cs, wsc, p, Bc, hc, lc, at<int32_t>(wsc, p.sel), at<int32_t>(wsc, p.ids), at<float>(wsc, p.z)));
+      }
+      return run_sample(h, cs, wsc, p, Bc, lc, temperature, uniforms + b0, token + b0, prob ? prob + b0 : nullptr, 1);
   });
 }
 

@@ -168,6 +168,43 @@ class Drafter:
             C.byref(s), _ptr(o["tokens"]), _ptr(o.get("logits")), _ptr(o["hidden_out"])))
         return o
 
+    def draft_block_sampled(self, n: int, target_hidden, last_token, target_embd, kv: SharedKV, temperature: float,
+                            uniforms, want_logits: bool = False, out: Optional[Dict[str, torch.Tensor]] = None,
+                            workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+        """draft_block(n) drawing each step's token at `temperature` with uniforms [n][B] (fp32 device, in [0, 1));
+        returns tokens [B][n], their draft probabilities probs [B][n], hidden_out and optionally logits."""
+        sh = self.shape
+        B = int(target_hidden.shape[0])
+        dev = target_hidden.device
+        o = out if out is not None else {}
+        if "tokens" not in o:
+            o["tokens"] = torch.empty(B, n, dtype=torch.int32, device=dev)
+            o["probs"] = torch.empty(B, n, dtype=torch.float32, device=dev)
+            o["hidden_out"] = torch.empty(B, sh.backbone, dtype=torch.int16, device=dev)
+            if want_logits:
+                o["logits"] = torch.empty(n, B, sh.vocab, dtype=torch.float32, device=dev)
+        ws = workspace if workspace is not None else self.workspace(B)
+        s, keep = kv.struct()
+        abi.check(abi.lib().mtpd_draft_block_sampled(
+            self.handle, _stream(), _ptr(ws), B, int(n), _ptr(target_hidden), _ptr(last_token), _ptr(target_embd),
+            C.byref(s), float(temperature), _ptr(uniforms), _ptr(o["tokens"]), _ptr(o["probs"]), _ptr(o.get("logits")),
+            _ptr(o["hidden_out"])))
+        return o
+
+    def sample_head(self, h, temperature: float, uniforms, want_logits: bool = False) -> Dict[str, torch.Tensor]:
+        """The head alone on fp32 normed states h [m][hidden] with a token drawn per row at uniforms [m]."""
+        sh = self.shape
+        m = int(h.shape[0])
+        dev = h.device
+        o = {"token": torch.empty(m, dtype=torch.int32, device=dev), "prob": torch.empty(m, dtype=torch.float32,
+                                                                                          device=dev)}
+        if want_logits:
+            o["logits"] = torch.empty(m, sh.vocab, dtype=torch.float32, device=dev)
+        ws = self.workspace(m)
+        abi.check(abi.lib().mtpd_sample_head(self.handle, _stream(), _ptr(ws), m, _ptr(h), float(temperature),
+                                             _ptr(uniforms), _ptr(o["token"]), _ptr(o["prob"]), _ptr(o.get("logits"))))
+        return o
+
     def masked_head(self, h, want_logits: bool = False, want_sparse: Optional[bool] = None) -> Dict[str, torch.Tensor]:
         """The LM head alone on fp32 normed states h [m][hidden]; with n_centroids == 0 the dense tied head (no
         per-cluster outputs; want_sparse defaults to True for the masked head only)."""

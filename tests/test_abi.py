@@ -130,6 +130,10 @@ def test_calls_reject_null_handle():
     assert rc == abi.MTPD_EINVAL
     rc = L.mtpd_masked_head(None, None, None, 1, None, None, None, None, None, None)
     assert rc == abi.MTPD_EINVAL
+    rc = L.mtpd_draft_block_sampled(None, None, None, 1, 4, None, None, None, None, 1.0, None, None, None, None, None)
+    assert rc == abi.MTPD_EINVAL
+    rc = L.mtpd_sample_head(None, None, None, 1, None, 1.0, None, None, None, None)
+    assert rc == abi.MTPD_EINVAL
     L.mtpd_destroy(None)
 
 
