@@ -75,6 +75,7 @@ class Workload:
     n_steps: int  # draft_block length
     ragged: bool = False  # per-row lengths context - 37*b instead of all equal
     seed: int = 0
+    shared_kv: bool = False  # one cache per type read by every row (rows of one sequence), else one per row
 
     def lens(self) -> List[int]:
         if self.ragged:
@@ -98,6 +99,9 @@ WORKLOADS: Dict[str, Workload] = {
     "e4b_b16_ctx8192_block4": Workload("e4b_b16_ctx8192_block4", E4B, batch=16, context=8192, n_steps=4),
     # 26B-A4B-shaped drafter with the dense head, batch 32, context 32768 each, draft_block 4
     "e26b_b32_ctx32768_block4": Workload("e26b_b32_ctx32768_block4", E26B, batch=32, context=32768, n_steps=4),
+    # verify width: 256 query rows of one sequence sharing one cache of 131072 keys (window 1024), one drafter step
+    "e4b_verify256_ctx131072": Workload("e4b_verify256_ctx131072", dataclasses.replace(E4B, swa_window=1024),
+                                        batch=256, context=131072, n_steps=1, shared_kv=True),
 }
 
 # small shapes for fast CPU checks and multi-tile / ragged GPU parity cases
@@ -270,21 +274,22 @@ def make_inputs(wl: Workload, device="cpu", with_target_embd: bool = True, disti
     """Per-call inputs: target hidden [B][Bb], last token [B], shared K(=V) caches [B][n_kv][cap][hd] per type,
     lengths, rope tables, and (optionally, full size) the target's input embedding table [V][Bb]."""
     sh, B = wl.shape, wl.batch
+    KB = 1 if wl.shared_kv else B  # cache rows
     cap = wl.context
     lens = wl.lens()
     d: Dict[str, object] = {
         "target_hidden": gen_bf16(wl.seed, TID["target_hidden"], (B, sh.backbone), 1.0, device=device),
         "last_token": (uniform_u32(wl.seed, TID["last_token"], torch.arange(B, dtype=torch.int64)) % sh.vocab)
         .to(torch.int32).to(device),
-        "k_sliding": gen_bf16(wl.seed, TID["kv_sliding"], (B, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device),
-        "k_full": gen_bf16(wl.seed, TID["kv_full"], (B, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device),
+        "k_sliding": gen_bf16(wl.seed, TID["kv_sliding"], (KB, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device),
+        "k_full": gen_bf16(wl.seed, TID["kv_full"], (KB, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device),
         "len_sliding": list(lens),
         "len_full": list(lens),
         "positions": list(lens),
     }
     if distinct_v:
-        d["v_sliding"] = gen_bf16(wl.seed, TID["v_sliding"], (B, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device)
-        d["v_full"] = gen_bf16(wl.seed, TID["v_full"], (B, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device)
+        d["v_sliding"] = gen_bf16(wl.seed, TID["v_sliding"], (KB, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device)
+        d["v_full"] = gen_bf16(wl.seed, TID["v_full"], (KB, sh.n_kv_head, cap, sh.head_dim), 1.0, device=device)
     d["rope"] = torch.from_numpy(rope_tables(sh, d["positions"])).to(device)
     if with_target_embd:
         d["target_embd"] = gen_bf16(wl.seed, TID["target_embd"], (sh.vocab, sh.backbone), 1.0, device=device)

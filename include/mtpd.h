@@ -49,7 +49,7 @@ enum {
   MTPD_EUNSUP = -5  /* valid per the pages but not implemented by this library */
 };
 
-#define MTPD_MAX_BATCH 64 /* rows per call */
+#define MTPD_MAX_BATCH 256 /* rows per call */
 #define MTPD_MAX_TIMED 4096 /* kernel timing records kept per handle */
 
 typedef struct mtpd_handle_s *mtpd_handle;
@@ -105,7 +105,9 @@ typedef struct {
 
 /* One shared cache of the target ([MTP doc] "Runtime implementation", piece 1; [Guide] section 2(4),
  * shared_kv_states): k, v [batch][n_kv_head][cap][head_dim] bf16; v may equal k (K = V, [Inventory]
- * "Notes for llama.cpp port" 2), in which case it is read once. len is a HOST array [batch], 1 <= len[b] <= cap.
+ * "Notes for llama.cpp port" 2), in which case it is read once. shared != 0: k, v are one cache
+ * [1][n_kv_head][cap][head_dim] read by every row (rows of one sequence scored together, each with its own length,
+ * token and position). len is a HOST array [batch], 1 <= len[b] <= cap.
  * first is an optional HOST array [batch] (NULL = all zero), 0 <= first[b] < cap: row b's valid keys, oldest
  * first, are the slots (first[b] + i) mod cap for i < len[b]. A left-padded batch ([Guide] section 2,
  * "create_attention_masks" and padding_side="left") passes its padding widths; a ring-buffer cache passes the
@@ -113,6 +115,7 @@ typedef struct {
 typedef struct {
   const uint16_t *k, *v;
   int32_t cap;
+  int32_t shared;
   const int32_t *len;
   const int32_t *first;
 } mtpd_kv;
@@ -212,7 +215,7 @@ MTPD_API int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char **names
 /* Message for the last non-OK return on the calling thread ("" if none). */
 MTPD_API const char *mtpd_last_error(void);
 
-/* ABI version: 2 (mtpd_kv gained `first`). */
+/* ABI version: 3 (mtpd_kv gained `first` in 2 and `shared` in 3). */
 MTPD_API int32_t mtpd_abi_version(void);
 
 #ifdef __cplusplus

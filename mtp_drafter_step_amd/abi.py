@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmtpd.so")
 
 MTPD_OK, MTPD_EINVAL, MTPD_ESHAPE, MTPD_ENOMEM, MTPD_EHIP, MTPD_EUNSUP = 0, -1, -2, -3, -4, -5
-MTPD_MAX_BATCH = 64
+MTPD_MAX_BATCH = 256
 MTPD_MAX_TIMED = 4096
 SYMBOLS = ("mtpd_create", "mtpd_destroy", "mtpd_workspace_bytes", "mtpd_drafter_step", "mtpd_draft_block",
            "mtpd_masked_head", "mtpd_last_error", "mtpd_abi_version", "mtpd_timing_enable", "mtpd_timing_read",
@@ -46,7 +46,8 @@ class mtpd_weights(C.Structure):
 
 
 class mtpd_kv(C.Structure):
-    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("cap", C.c_int32), ("len", i32p), ("first", i32p)]
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("cap", C.c_int32), ("shared", C.c_int32), ("len", i32p),
+                ("first", i32p)]
 
 
 class mtpd_shared_kv(C.Structure):

@@ -60,8 +60,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
   const int k0 = win.start[b] + sp * chunk;
   const int k1 = min(win.start[b] + cntk, k0 + chunk);
   const bool same_v = (Vc == K);
-  const uint16_t* Kb = K + ((size_t)b * nkv + g) * (size_t)cap * HD + lane * DPL;
-  const uint16_t* Vb = Vc + ((size_t)b * nkv + g) * (size_t)cap * HD + lane * DPL;
+  const size_t crow = win.shared ? 0 : (size_t)b;  // cache row (shared caches: row 0 for every batch row)
+  const uint16_t* Kb = K + (crow * nkv + g) * (size_t)cap * HD + lane * DPL;
+  const uint16_t* Vb = Vc + (crow * nkv + g) * (size_t)cap * HD + lane * DPL;
   // first batch of keys in flight before the q prologue
   Raw kcur[KB], knext[KB];
   int t0 = k0 + wave * KB;
@@ -261,8 +262,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   const int k0 = win.start[b] + sp * chunk;
   const int k1 = min(win.start[b] + cntk, k0 + chunk);
   const bool same_v = (Vc == K);
-  const uint16_t* Kb = K + ((size_t)b * nkv + g) * (size_t)cap * HD + 8 * kq;
-  const uint16_t* Vb = Vc + ((size_t)b * nkv + g) * (size_t)cap * HD + 8 * kq;
+  const size_t crow = win.shared ? 0 : (size_t)b;  // cache row (shared caches: row 0 for every batch row)
+  const uint16_t* Kb = K + (crow * nkv + g) * (size_t)cap * HD + 8 * kq;
+  const uint16_t* Vb = Vc + (crow * nkv + g) * (size_t)cap * HD + 8 * kq;
 
   // inputs of q_norm + rotation first (waits count loads in issue order, so these must precede the key batch)
   const float* tab = rope + ((size_t)b * 2 + type) * 2 * half;

@@ -9,7 +9,7 @@
 
 namespace mtpd {
 
-constexpr int kMaxBatch = 64;  // rows per call (matches MTPD_MAX_BATCH)
+constexpr int kMaxBatch = 256;  // rows per call (matches MTPD_MAX_BATCH)
 constexpr int kMaxSplit = 32;  // key-range splits of one (row, kv head)
 constexpr int kRowGroup = 4;   // batch rows handled together by the dense kernels
 constexpr int kMaxTopK = 64;   // clusters kept per row
@@ -21,6 +21,7 @@ constexpr int kMaxSampleTiles = 256;  // sampled rows hold at most 256 * 4096 sc
 struct RowWindows {
   int32_t start[kMaxBatch];
   int32_t count[kMaxBatch];
+  int32_t shared;  // 1: every row reads cache row 0
 };
 
 // Residual update applied in a dense kernel's prologue before its input norm:

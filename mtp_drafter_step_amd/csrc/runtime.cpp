@@ -228,6 +228,7 @@ int check_kv(const mtpd_handle_s* h, const mtpd_kv& kv, int B, const char* name,
   if (!kv.len) return fail(MTPD_EINVAL, "%s.len is NULL", name);
   if (kv.cap <= 0) return fail(MTPD_ESHAPE, "%s.cap must be positive", name);
   std::memset(win, 0, sizeof(*win));
+  win->shared = kv.shared ? 1 : 0;
   for (int b = 0; b < B; ++b) {
     const int L = kv.len[b];
     if (L < 1 || L > kv.cap) return fail(MTPD_ESHAPE, "%s.len[%d] = %d outside [1, cap=%d]", name, b, L, kv.cap);
@@ -387,10 +388,11 @@ ChainView chain_view(const mtpd_handle_s* h, const mtpd_shared_kv* kv, const mtp
   v.kv = *kv;
   const size_t hd = (size_t)h->cfg.head_dim, nkv = (size_t)h->cfg.n_kv_head;
   const size_t ss = nkv * (size_t)kv->sliding.cap * hd, fs = nkv * (size_t)kv->full.cap * hd;
-  v.kv.sliding.k = kv->sliding.k + (size_t)b0 * ss;
-  v.kv.sliding.v = kv->sliding.v + (size_t)b0 * ss;
-  v.kv.full.k = kv->full.k + (size_t)b0 * fs;
-  v.kv.full.v = kv->full.v + (size_t)b0 * fs;
+  const size_t bs = kv->sliding.shared ? 0 : b0, bf = kv->full.shared ? 0 : b0;  // shared caches: one row
+  v.kv.sliding.k = kv->sliding.k + bs * ss;
+  v.kv.sliding.v = kv->sliding.v + bs * ss;
+  v.kv.full.k = kv->full.k + bf * fs;
+  v.kv.full.v = kv->full.v + bf * fs;
   v.kv.sliding.len = kv->sliding.len + b0;
   v.kv.full.len = kv->full.len + b0;
   if (kv->sliding.first) v.kv.sliding.first = kv->sliding.first + b0;
@@ -398,6 +400,7 @@ ChainView chain_view(const mtpd_handle_s* h, const mtpd_shared_kv* kv, const mtp
   v.kv.rope = kv->rope + (size_t)b0 * 2 * hd;
   for (int t = 0; t < 2; ++t) {
     std::memset(&v.win[t], 0, sizeof(v.win[t]));
+    v.win[t].shared = win[t].shared;
     for (int i = 0; i < Bc; ++i) {
       v.win[t].start[i] = win[t].start[b0 + i];
       v.win[t].count[i] = win[t].count[b0 + i];
@@ -518,7 +521,7 @@ CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs
 
 extern "C" {
 
-int32_t mtpd_abi_version(void) { return 2; }
+int32_t mtpd_abi_version(void) { return 3; }
 
 const char* mtpd_last_error(void) { return g_last_error.c_str(); }
 

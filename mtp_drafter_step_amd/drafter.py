@@ -34,11 +34,12 @@ class SharedKV:
 
     def __init__(self, k_sliding, k_full, len_sliding: Sequence[int], len_full: Sequence[int], rope,
                  v_sliding=None, v_full=None, first_sliding: Optional[Sequence[int]] = None,
-                 first_full: Optional[Sequence[int]] = None):
+                 first_full: Optional[Sequence[int]] = None, shared: bool = False):
         self.k = (k_sliding, k_full)
         self.v = (k_sliding if v_sliding is None else v_sliding, k_full if v_full is None else v_full)
         self.lens = ([int(x) for x in len_sliding], [int(x) for x in len_full])
         self.first = tuple(None if f is None else [int(x) for x in f] for f in (first_sliding, first_full))
+        self.shared = bool(shared)  # both caches are one [1][n_kv][cap][head_dim] cache read by every row
         self.rope = rope
 
     def struct(self):
@@ -47,7 +48,7 @@ class SharedKV:
         kvs = []
         for t in range(2):
             kvs.append(abi.mtpd_kv(k=_ptr(self.k[t]), v=_ptr(self.v[t]), cap=int(self.k[t].shape[2]),
-                                   len=C.cast(arrs[t], abi.i32p),
+                                   shared=1 if self.shared else 0, len=C.cast(arrs[t], abi.i32p),
                                    first=None if firsts[t] is None else C.cast(firsts[t], abi.i32p)))
         s = abi.mtpd_shared_kv(sliding=kvs[0], full=kvs[1], rope=_ptr(self.rope))
         return s, (arrs, firsts)  # keep the host arrays alive for the call

@@ -232,6 +232,8 @@ class SharedKV:
 
     k[t], v[t]: [B][n_kv][cap][head_dim] bf16 bits (v may be the same array as k: K = V);
     lens[t]: valid keys per row; rope: [B][2 types][2 (cos, sin)][head_dim/2] fp32. Type index 0 = sliding, 1 = full.
+    shared[t] (optional, default False): one cache [1][n_kv][cap][head_dim] read by every row (rows of one sequence
+    scored together, each with its own length and position).
     first[t] (optional, default 0): slot of each row's oldest valid key. Row b's valid keys, oldest first, are slots
     (first + i) mod cap for i < len: a left-padded batch ([Guide] section 2 "create_attention_masks" and
     padding_side="left") starts at its padding width, a ring-buffer cache at its oldest slot.
@@ -241,6 +243,11 @@ class SharedKV:
     lens: Sequence[Sequence[int]]
     rope: np.ndarray
     first: Optional[Sequence[Sequence[int]]] = None
+    shared: Optional[Sequence[bool]] = None
+
+    def row(self, t: int, b: int) -> int:
+        """Cache row that batch row b reads."""
+        return 0 if (self.shared is not None and self.shared[t]) else b
 
     def slots(self, t: int, b: int, a0: int, a1: int) -> np.ndarray:
         """Cache slots of the row's valid keys a0 .. a1 - 1 (oldest first)."""
@@ -275,8 +282,9 @@ def decoder_layer(m: Model, l: int, x: np.ndarray, b: int, kv: SharedKV) -> np.n
         g = h * cfg.n_kv_head // cfg.n_head
         qh = rope_rotate(rmsnorm(q[h], L["q_norm"], cfg.rms_eps), cos, sin)
         sl = kv.slots(t, b, a0, a1)
-        K = bf16_to_f64(kv.k[t][b, g, sl])
-        V = K if kv.v[t] is kv.k[t] else bf16_to_f64(kv.v[t][b, g, sl])
+        cb = kv.row(t, b)
+        K = bf16_to_f64(kv.k[t][cb, g, sl])
+        V = K if kv.v[t] is kv.k[t] else bf16_to_f64(kv.v[t][cb, g, sl])
         o[h] = attend(qh, K, V, cfg.attn_scale)
     x = r + rmsnorm(L["o"] @ o.reshape(-1), L["post_attn_norm"], cfg.rms_eps)
     r = x

@@ -40,12 +40,16 @@ class Case:
 
     def __init__(self, shape, batch: int, context: int, ragged: bool = False, seed: int = 0,
                  distinct_v: bool = False, lens: Optional[Sequence[int]] = None, max_batch: Optional[int] = None,
-                 gen_device: str = "cpu"):
+                 gen_device: str = "cpu", shared_kv: bool = False, swa_window: Optional[int] = None):
         """gen_device "cuda" runs the (bit-identical) generators on the GPU and copies the results to the host, for
         shapes whose tables take the CPU generator too long."""
         from mtp_drafter_step_amd import Drafter, SharedKV
         self.shape, self.batch = shape, batch
-        wl = synth.Workload("case", shape, batch=batch, context=context, n_steps=1, ragged=ragged, seed=seed)
+        if swa_window is not None:
+            shape = dataclasses.replace(shape, swa_window=swa_window)
+            self.shape = shape
+        wl = synth.Workload("case", shape, batch=batch, context=context, n_steps=1, ragged=ragged, seed=seed,
+                            shared_kv=shared_kv)
         self.w = to_dev(synth.make_weights(shape, seed=seed, device=gen_device), "cpu")
         inp = synth.make_inputs(wl, device=gen_device, with_target_embd=False, distinct_v=distinct_v)
         inp = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
@@ -58,7 +62,8 @@ class Case:
         self.model = O.Model(O.config_from(shape), self.w)
         ks = [inp["k_sliding"].numpy().view(np.uint16), inp["k_full"].numpy().view(np.uint16)]
         vs = ks if not distinct_v else [inp["v_sliding"].numpy().view(np.uint16), inp["v_full"].numpy().view(np.uint16)]
-        self.kv_cpu = O.SharedKV(k=ks, v=vs, lens=[inp["len_sliding"], inp["len_full"]], rope=inp["rope"].numpy())
+        self.kv_cpu = O.SharedKV(k=ks, v=vs, lens=[inp["len_sliding"], inp["len_full"]], rope=inp["rope"].numpy(),
+                                 shared=[shared_kv, shared_kv])
         self.temb_cpu = synth.LazyRows(seed, shape)
         # device side
         self.wg = to_dev(self.w)
@@ -67,7 +72,8 @@ class Case:
         self.tok = inp["last_token"].cuda()
         kd = [inp["k_sliding"].cuda(), inp["k_full"].cuda()]
         vd = [None, None] if not distinct_v else [inp["v_sliding"].cuda(), inp["v_full"].cuda()]
-        self.kv = SharedKV(kd[0], kd[1], inp["len_sliding"], inp["len_full"], inp["rope"].cuda(), vd[0], vd[1])
+        self.kv = SharedKV(kd[0], kd[1], inp["len_sliding"], inp["len_full"], inp["rope"].cuda(), vd[0], vd[1],
+                           shared=shared_kv)
         self.drafter = Drafter(shape, self.wg, max_batch=max_batch or max(batch, 1))
 
     def oracle_step(self, rows=None, want_rows=False, th=None, tok=None):

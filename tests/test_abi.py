@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mtpd_\w+)", out))
     assert exported == set(declared_functions())
-    assert L.mtpd_abi_version() == 2
+    assert L.mtpd_abi_version() == 3
 
 
 def test_struct_layout_matches_c(tmp_path):
@@ -103,7 +103,7 @@ def test_create_rejects_null_and_misaligned_weights():
     w.token_ordering = 0x1000
     rc, err = create_rc(good_config(), w)  # layer pointers are NULL
     assert rc == abi.MTPD_EINVAL and "layers[0].attn_q" in err
-    rc, err = create_rc(good_config(), w, max_batch=65)
+    rc, err = create_rc(good_config(), w, max_batch=257)
     assert rc == abi.MTPD_ESHAPE and "max_batch" in err
 
 

@@ -104,8 +104,10 @@ STEP_CASES = {
     # window 1 and a row with a single key
     "e2b_window1_len1": dict(shape=dataclasses.replace(synth.E2B, swa_window=1), batch=3, context=64,
                              lens=[64, 1, 33]),
-    # the largest batch the ABI takes
+    # more than one 64-row group of blocks
     "e2b_b64_ctx300": dict(shape=synth.E2B, batch=64, context=300, ragged=True),
+    # the largest batch the ABI takes, per-row caches
+    "e2b_b256_ctx200": dict(shape=synth.E2B, batch=256, context=200, ragged=True),
     # head_dim 128 and 64 (the vector-ALU attention): 2 and 8 query heads per kv head
     "e2b_hd128_g2": dict(shape=dataclasses.replace(synth.E2B, head_dim=128, n_head=8, n_kv_head=4), batch=3,
                          context=700, ragged=True),
@@ -212,6 +214,39 @@ def test_left_padded_and_ring_buffer_caches():
     with pytest.raises(abi.MtpdError) as ei:
         case.drafter.drafter_step(case.th, case.tok, case.temb, bad)
     assert "first" in str(ei.value)
+
+
+def test_shared_cache_rows():
+    """Rows of one sequence reading one shared cache (own lengths, tokens and positions): bit-identical to the same
+    call with per-row copies of that cache, and equal to the oracle."""
+    from mtp_drafter_step_amd import SharedKV
+    say("shared cache, batch 8")
+    case = Case(synth.E4B, batch=8, context=3000, ragged=True, shared_kv=True)
+    out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    out = {k: v.clone() for k, v in out.items()}
+    copies = [t.expand(8, -1, -1, -1).contiguous() for t in case.kv.k]
+    kvc = SharedKV(copies[0], copies[1], case.kv.lens[0], case.kv.lens[1], case.kv.rope)
+    got = case.drafter.drafter_step(case.th, case.tok, case.temb, kvc, want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    for k in out:
+        assert torch.equal(got[k], out[k]), k
+    rows = list(range(8))
+    tally = compare_step(case, out, case.oracle_step(rows=rows), rows, where="shared")
+    say(tally.summary())
+    assert tally.sel_checked >= 4
+
+
+def test_verify_width_step():
+    """The verify-width workload: 256 rows of one sequence sharing one cache of 131072 keys (window 1024), the
+    largest batch the ABI takes; sampled rows against the oracle."""
+    say("verify width: 256 rows, shared 131072-key cache")
+    case = Case(synth.E4B, batch=256, context=131072, gen_device="cuda", shared_kv=True, swa_window=1024)
+    out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    rows = [0, 97, 255]
+    tally = compare_step(case, out, case.oracle_step(rows=rows), rows, where="verify")
+    say(tally.summary())
+    assert tally.sel_checked >= 2
 
 
 def test_drafter_step_is_deterministic():

@@ -429,6 +429,24 @@ def test_left_padded_and_ring_caches_equal_the_linear_cache():
         O.SharedKV(k=[ring, kv.k[1]], v=[ring, kv.k[1]], lens=[[C + 1] * B, kv.lens[1]], rope=kv.rope).slots(0, 0, 0, 3)
 
 
+def test_shared_cache_equals_per_row_copies():
+    """One cache read by every row (each row with its own length, token and position) gives exactly the step of
+    per-row caches that are all copies of that cache."""
+    m, w, shape = _tiny_model()
+    wl, d, kv = _tiny_inputs(shape, batch=3, context=40, ragged=True)
+    th = d["target_hidden"].numpy().view(np.uint16)
+    emb = d["target_embd"].numpy().view(np.uint16)
+    tok = d["last_token"].numpy()
+    one = [kv.k[t][:1].copy() for t in range(2)]
+    copies = [np.repeat(one[t], 3, axis=0) for t in range(2)]
+    ref = O.drafter_step(m, th, tok, emb, O.SharedKV(k=copies, v=copies, lens=kv.lens, rope=kv.rope))
+    got = O.drafter_step(m, th, tok, emb, O.SharedKV(k=one, v=one, lens=kv.lens, rope=kv.rope, shared=[True, True]))
+    assert np.array_equal(got["hidden_out"], ref["hidden_out"]) and np.array_equal(got["next"], ref["next"])
+    # and it differs from the rows' own caches (rows 1, 2 read row 0's keys)
+    own = O.drafter_step(m, th, tok, emb, kv)
+    assert not np.array_equal(own["hidden_out"][1:], got["hidden_out"][1:])
+
+
 def test_step_rows_are_independent():
     m, w, shape = _tiny_model()
     wl, d, kv = _tiny_inputs(shape)
