@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc")
 # the source file of each kernel; a kernel's digest covers that file and the shared headers
-KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_head": "k_head.hip",
+KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_attn_mq": "k_attention_shared.hip", "k_head": "k_head.hip",
                "k_head_dense": "k_head.hip", "k_final": "k_head.hip", "k_fill": "k_head.hip",
                "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip",
                "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip"}
@@ -50,9 +50,12 @@ SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma"
                "sample_tiles": "k_sample_tiles", "sample_pick": "k_sample_pick"}
 
 
-def site_kernel(site, shape):
+def site_kernel(site, shape, shared=False):
     """Kernel behind a launch site for this shape (the matrix-core attention covers head_dim 256 with up to eight
-    query heads per kv head; other shapes run the vector-ALU attention)."""
+    query heads per kv head; other shapes run the vector-ALU attention; caches shared by the rows run the
+    multi-query attention)."""
+    if site.startswith("attn_") and shared and shape.head_dim == 256:
+        return "k_attn_mq"
     if site.startswith("attn_") and not (shape.head_dim == 256 and shape.n_head // shape.n_kv_head <= 8):
         return "k_attn"
     return SITE_KERNEL[site]
@@ -67,14 +70,16 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def step_bytes(shape, batch, lens, distinct_clusters, with_logits=True):
+def step_bytes(shape, batch, lens, distinct_clusters, with_logits=True, shared=False):
     """Bytes one drafter step must move: weights once, each cache's K (= V) once over the keys it reads (the
     sliding window counted once for the three sliding layers), the selected clusters' head rows and their ordering
     ids (the dense head: the whole table), the logits row, and target hidden / embedding rows / hidden_out."""
     H, Bb, F, Q, hd = shape.hidden, shape.backbone, shape.ffn, shape.q_dim, shape.head_dim
     per_layer = (Q * H + H * Q + 3 * F * H) * 2 + (hd + 4 * H) * 2
     weights = (2 * Bb * H + Bb * H + shape.n_centroids * H + H) * 2 + shape.n_layer * per_layer
-    kv = sum(shape.n_kv_head * hd * 2 * (L + min(shape.swa_window, L)) for L in lens)
+    # a shared cache (rows of one sequence) is needed once: its longest row's keys
+    kv_lens = [max(lens)] if shared else lens
+    kv = sum(shape.n_kv_head * hd * 2 * (L + min(shape.swa_window, L)) for L in kv_lens)
     dense = shape.n_centroids == 0
     head = shape.vocab * H * 2 if dense else distinct_clusters * shape.vsc * H * 2
     ids = 0 if dense else 4 * shape.top_k * shape.vsc * batch
@@ -84,7 +89,7 @@ def step_bytes(shape, batch, lens, distinct_clusters, with_logits=True):
                                                          io=io)
 
 
-def site_bytes(site, shape, batch, lens, distinct_clusters):
+def site_bytes(site, shape, batch, lens, distinct_clusters, shared=False):
     """Algorithmic bytes of one launch of a launch site: the weights and cache rows the step needs from it, its
     activation inputs and outputs (fp32), and its share of the logits row. Intermediates that exist only because
     the path is split into kernels (attention partials) count for the merge only."""
@@ -96,7 +101,7 @@ def site_bytes(site, shape, batch, lens, distinct_clusters):
     if site == "qproj":
         return 2 * QD * H + 2 * H + 3 * act(H) + act(QD)
     if site in ("attn_sliding", "attn_full"):
-        keys = sum(L if site == "attn_full" else min(W, L) for L in lens)
+        keys = sum(L if site == "attn_full" else min(W, L) for L in ([max(lens)] if shared else lens))
         return shape.n_kv_head * hd * 2 * keys + 2 * hd + 2 * act(QD)
     if site == "o_proj":
         return 2 * H * QD + act(QD) + act(H) * (QD // 256)
@@ -152,7 +157,8 @@ def cpu_baseline(wl, seconds, w_dev=None, inp_dev=None):
     m = O.Model(O.config_from(shape), w)
     import numpy as np
     ks = [inp["k_sliding"].numpy().view(np.uint16), inp["k_full"].numpy().view(np.uint16)]
-    kv = O.SharedKV(k=ks, v=ks, lens=[inp["len_sliding"], inp["len_full"]], rope=inp["rope"].numpy())
+    kv = O.SharedKV(k=ks, v=ks, lens=[inp["len_sliding"], inp["len_full"]], rope=inp["rope"].numpy(),
+                    shared=[wl.shared_kv, wl.shared_kv])
     th = inp["target_hidden"].numpy().view(np.uint16)
     tok = inp["last_token"].numpy()
     rows_emb = synth.LazyRows(wl.seed, shape)
@@ -205,7 +211,8 @@ def run_bench(args):
     dev = "cuda"
     w = synth.make_weights(shape, seed=wl.seed, device=dev)
     inp = synth.make_inputs(wl, device=dev, with_target_embd=True)
-    kv = SharedKV(inp["k_sliding"], inp["k_full"], inp["len_sliding"], inp["len_full"], inp["rope"])
+    kv = SharedKV(inp["k_sliding"], inp["k_full"], inp["len_sliding"], inp["len_full"], inp["rope"],
+                  shared=wl.shared_kv)
     d = Drafter(shape, w, max_batch=B)
     out = {}
     ws = d.workspace(B)
@@ -241,7 +248,7 @@ def run_bench(args):
             U.append(len(clusters))
     u_mean = float(np.mean(U)) if U else 0.0
     lens = [int(x) for x in inp["len_full"]]
-    sbytes, parts = step_bytes(shape, B, lens, u_mean)
+    sbytes, parts = step_bytes(shape, B, lens, u_mean, shared=wl.shared_kv)
 
     # timed region: graph-replayed draft_block calls on torch's current stream
     stream = torch.cuda.current_stream()
@@ -272,11 +279,11 @@ def run_bench(args):
         per_site.setdefault(name, []).append(ms)
     per_kernel = {}
     for site, v in per_site.items():
-        k = site_kernel(site, shape)
+        k = site_kernel(site, shape, wl.shared_kv)
         e = per_kernel.setdefault(k, {"launches": 0, "total_ms": 0.0, "bytes": 0.0, "sites": []})
         e["launches"] += len(v)
         e["total_ms"] += float(np.sum(v))
-        e["bytes"] += len(v) * site_bytes(site, shape, B, lens, u_mean)
+        e["bytes"] += len(v) * site_bytes(site, shape, B, lens, u_mean, shared=wl.shared_kv)
         e["sites"].append(site)
     calls = args.timing_steps
     dom = max(per_kernel, key=lambda k: per_kernel[k]["total_ms"])

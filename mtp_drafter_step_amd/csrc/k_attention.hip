@@ -1,5 +1,6 @@
 // Single-query attention over the shared caches: the vector-ALU kernel (any head_dim in {64, 128, 256}) and the
-// matrix-core kernel (head_dim 256, up to 8 query heads per kv head).
+// matrix-core kernel (head_dim 256, up to 8 query heads per kv head); caches shared by all rows go to the
+// multi-query kernel of k_attention_shared.hip.
 //
 // Pages cited (by title; sections as headed on each page):
 //   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
@@ -473,12 +474,16 @@ bool getenv_no_mfma() {
 // ------------------------------------------------------------------------------------------------------------
 // launcher
 
+bool attn_uses_multi_query(bool shared, int hd, bool same_v) { return shared && hd == 256 && same_v && !getenv_no_mfma(); }
+
 hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
                        float eps, const float* rope, int type, const uint16_t* K, const uint16_t* V, int cap,
                        const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, float* o) {
   dim3 grid(nsplit, B * nkv);
   const float sl2 = scale * 1.4426950408889634f;
   const int G = nh / nkv;
+  if (attn_uses_multi_query(win.shared != 0, hd, V == K))
+    return launch_attn_shared(s, B, nh, nkv, q, qnorm, eps, rope, type, K, cap, win, nsplit, sl2, pacc, pml, o);
   if (hd == 256 && G <= 8 && !getenv_no_mfma()) {
     if (G == 8) return go(k_attn_mfma<8, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);
     if (G == 4) return go(k_attn_mfma<4, 4>, grid, 256, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, V, cap, win, nsplit, sl2, pacc, pml, o);

@@ -1,0 +1,295 @@
+// Multi-query attention over one cache shared by every row of the batch (rows of one sequence scored together).
+//
+// Pages cited (by title; sections as headed on each page):
+//   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
+//   [Guide]      "Gemma 4 Assistant 使用指南：用 MTP 投机解码与 KV Sharing 加速 Gemma 4 推理" (gitcode blog)
+//   [Inventory]  "Gemma 4 Assistant (MTP drafter) - tensor inventory (Stage 0)"
+//
+// The attention itself is the per-row one ([MTP doc] "What it is": Q-only attention on the target's last-layer
+// K/V; [Guide] section 2(4); [Inventory] "Notes for llama.cpp port" 2: V taken from K): each row's queries over its
+// own key window. Only the schedule differs: the rows meet each key once.
+#include "device.h"
+
+namespace mtpd {
+namespace {
+
+// ------------------------------------------------------------------------------------------------------------
+// Multi-query matrix-core attention over a cache shared by the batch's rows (rows of one sequence scored together):
+// every row reads the same keys, so the query rows meet each key tile once. A block holds 128 queries (8 waves x 16
+// queries: 16 / G rows x the G query heads of kv head blockIdx.z) and one key range: split blockIdx.x of the union
+// [u0, u1) of the rows' windows. Key tiles of 64 rows are staged in LDS for all waves (double-buffered, one barrier
+// per tile), twice: row-major (K rows for the scores) and transposed (each dim's keys contiguous, so a lane's four
+// keys of one dim, the P.V operand, are one 8-byte read). Each thread loads 4 x 4 (key x dim) blocks so that it can
+// write both layouts with 8-byte stores. Per wave and 16-key batch:
+//   S^T[16 keys][16 queries] = K_tile . Q^T with v_mfma_f32_16x16x32_bf16, the keys as A rows from LDS and the
+//     queries as B columns held in registers as bf16 hi + lo (q after q_norm and rotation, fp32-level accuracy);
+//   online softmax per query (lane column), each key masked by the query row's own window;
+//   O[16 queries][256] += P . V with v_mfma_f32_16x16x16_bf16, P split hi + lo, V read from the LDS tile.
+// Each wave's queries are its own, so the outputs need no combine: (max, sum) and the unnormalised sums go to the
+// split partials that the o_proj kernel merges (or, with one split, straight to o).
+// grid (nsplit, ceil(B / (128 / G)), n_kv), 512 threads.
+template <int G>
+__global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, const float* __restrict__ q,
+                                                    const uint16_t* __restrict__ qnorm, float eps,
+                                                    const float* __restrict__ rope, int type,
+                                                    const uint16_t* __restrict__ K, int cap, RowWindows win,
+                                                    int nsplit, int u0, int u1, float scale_log2,
+                                                    float* __restrict__ pacc, float* __restrict__ pml,
+                                                    float* __restrict__ o) {
+  constexpr int HD = 256, KSTEPS = HD / 32, TILES = HD / 16, NW = 8, KT = 64, LROW = HD + 8, half = HD / 2;
+  constexpr int VROW = KT + 4;  // transposed rows: 136 B, so 16 dims at one key offset fall in distinct banks
+  constexpr int RPW = 16 / G, RPB = NW * RPW;  // rows per wave, per block
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "16 queries per wave are whole rows");
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][KT][LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][HD][VROW];
+  const int sp = blockIdx.x, g = blockIdx.z;
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const int hq = lane & 15, kq = lane >> 4;
+  const int rbase = blockIdx.y * RPB + wave * RPW;  // the wave's first row
+  // the lane's query: row rbase + hq / G, head g G + hq % G; rows past B repeat the last row and store nothing
+  const int rq = min(rbase + hq / G, B - 1);
+  const bool qlive = rbase + hq / G < B;
+  const int head = g * G + hq % G;
+  int wst = 0, wen = 0;  // the query row's window (virtual indices), from wave-uniform reads of the row table
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int r = min(rbase + j, B - 1);
+    const int st = win.start[r], en = st + win.count[r];
+    if (hq / G == j) {
+      wst = st;
+      wen = en;
+    }
+  }
+  const int chunk = (u1 - u0 + nsplit - 1) / nsplit;
+  const int k0 = u0 + sp * chunk, k1 = min(u1, k0 + chunk);
+  const uint16_t* Kb = K + (size_t)g * cap * HD;  // the shared cache (row 0)
+
+  // first key tile in flight before the q prologue: thread t loads the 4 x 4 blocks (keys 4 kg .. +4, dims 4 dg ..
+  // +4) with kg = i / 64, dg = i % 64 for i = t and t + 512 (a wave reads 512 contiguous bytes of one key per load)
+  uint2 st[2][4];
+  auto gload = [&](int tb) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        st[x][j] = *reinterpret_cast<const uint2*>(Kb + (size_t)slot_of(min(tb + 4 * kg + j, k1 - 1), cap) * HD + 4 * dg);
+    }
+  };
+  auto lstore = [&](int bf) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(&kt[bf][4 * kg + j][4 * dg]) = st[x][j];
+      // dim 4 dg + e of the 4 keys
+      const uint32_t w[4][2] = {{st[x][0].x, st[x][0].y}, {st[x][1].x, st[x][1].y}, {st[x][2].x, st[x][2].y},
+                                {st[x][3].x, st[x][3].y}};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int wi = e >> 1, sh = (e & 1) * 16;
+        const uint32_t k0v = (w[0][wi] >> sh) & 0xFFFFu, k1v = (w[1][wi] >> sh) & 0xFFFFu;
+        const uint32_t k2v = (w[2][wi] >> sh) & 0xFFFFu, k3v = (w[3][wi] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(&vt[bf][4 * dg + e][4 * kg]) = make_uint2(k0v | (k1v << 16), k2v | (k3v << 16));
+      }
+    }
+  };
+  const bool any = k0 < k1;
+  if (any) gload(k0);
+
+  // q_norm + rotation of the lane's query: the lane holds dims 32 s + 8 kq + e (s < 8, e < 8); the rotation partner
+  // of dim d < 128 is d + 128, the same lane's step s + 4; the norm's sum spans the four lanes of the query (kq)
+  uint4 qhi[KSTEPS], qlo[KSTEPS];
+  {
+    const float* qr = q + ((size_t)rq * nh + head) * HD + 8 * kq;
+    const float* tab = rope + ((size_t)rq * 2 + type) * 2 * half + 8 * kq;
+    float4 qv[KSTEPS][2], co[4][2], si[4][2];
+    uint4 qw[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      qv[s][0] = *reinterpret_cast<const float4*>(qr + 32 * s);
+      qv[s][1] = *reinterpret_cast<const float4*>(qr + 32 * s + 4);
+      qw[s] = *reinterpret_cast<const uint4*>(qnorm + 32 * s + 8 * kq);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      co[s][0] = *reinterpret_cast<const float4*>(tab + 32 * s);
+      co[s][1] = *reinterpret_cast<const float4*>(tab + 32 * s + 4);
+      si[s][0] = *reinterpret_cast<const float4*>(tab + half + 32 * s);
+      si[s][1] = *reinterpret_cast<const float4*>(tab + half + 32 * s + 4);
+    }
+    float v[KSTEPS][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const float f[8] = {qv[s][0].x, qv[s][0].y, qv[s][0].z, qv[s][0].w,
+                          qv[s][1].x, qv[s][1].y, qv[s][1].z, qv[s][1].w};
+      float w8[8];
+      unpack8(qw[s], w8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[s][e] = f[e] * w8[e];
+        ss = fmaf(f[e], f[e], ss);
+      }
+    }
+    ss += xr_partner<16>(ss);
+    ss += xr_partner<32>(ss);
+    const float rn = 1.0f / sqrtf(ss / (float)HD + eps);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float c8[8] = {co[s][0].x, co[s][0].y, co[s][0].z, co[s][0].w, co[s][1].x, co[s][1].y, co[s][1].z, co[s][1].w};
+      const float s8[8] = {si[s][0].x, si[s][0].y, si[s][0].z, si[s][0].w, si[s][1].x, si[s][1].y, si[s][1].z, si[s][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float lo = v[s][e] * rn, hi = v[s + 4][e] * rn;
+        v[s][e] = lo * c8[e] - hi * s8[e];
+        v[s + 4][e] = hi * c8[e] + lo * s8[e];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      uint32_t h32[4], l32[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h0 = f2bf(v[s][2 * e]), h1 = f2bf(v[s][2 * e + 1]);
+        const uint16_t l0 = f2bf(v[s][2 * e] - bf2f(h0)), l1 = f2bf(v[s][2 * e + 1] - bf2f(h1));
+        h32[e] = h0 | ((uint32_t)h1 << 16);
+        l32[e] = l0 | ((uint32_t)l1 << 16);
+      }
+      qhi[s] = make_uint4(h32[0], h32[1], h32[2], h32[3]);
+      qlo[s] = make_uint4(l32[0], l32[1], l32[2], l32[3]);
+    }
+  }
+
+  float mrun = -INFINITY, lrun = 0.f;  // softmax state of query hq (identical in its four lanes)
+  f32x4 acc[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (any) lstore(0);
+  __syncthreads();
+  int buf = 0;
+  for (int tb = k0; tb < k1; tb += KT) {  // block-uniform
+    const bool more = tb + KT < k1;
+    if (more) gload(tb + KT);
+#pragma unroll
+    for (int j = 0; j < KT / 16; ++j) {
+      const int kb = tb + 16 * j;
+      if (kb >= k1) break;  // block-uniform
+      uint4 ka[KSTEPS];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) ka[s] = *reinterpret_cast<const uint4*>(&kt[buf][16 * j + hq][32 * s + 8 * kq]);
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ka[s]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qhi[s]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qlo[s]), sacc, 0, 0, 0);
+      }
+      // scores S[query hq][key kb + 4 kq + r], masked to the query row's window
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = kb + 4 * kq + r;
+        sv[r] = (t < k1 && t >= wst && t < wen) ? sacc[r] * scale_log2 : -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mt = fmaxf(mt, xr_partner<16>(mt));
+      mt = fmaxf(mt, xr_partner<32>(mt));
+      const float mn = fmaxf(mrun, mt);
+      const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
+      float pv[4], ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
+        ps += pv[r];
+      }
+      ps += xr_partner<16>(ps);
+      ps += xr_partner<32>(ps);
+      lrun = lrun * alpha + ps;
+      mrun = mn;
+      i16x4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint16_t hb = f2bf(pv[r]);
+        phi[r] = (short)hb;
+        plo[r] = (short)f2bf(pv[r] - bf2f(hb));
+      }
+      // output rows are queries 4 kq + r; their alphas live in lanes 4 kq + r
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a0 = readlane_f(alpha, r), a1 = readlane_f(alpha, 4 + r);
+        const float a2 = readlane_f(alpha, 8 + r), a3 = readlane_f(alpha, 12 + r);
+        al[r] = kq == 0 ? a0 : (kq == 1 ? a1 : (kq == 2 ? a2 : a3));
+      }
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        const i16x4 vb = __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2*>(&vt[buf][16 * t + hq][16 * j + 4 * kq]));
+        f32x4 a = acc[t];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] *= al[r];
+        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);
+        acc[t] = a;
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // outputs: query 4 kq + r of the wave holds dims 16 t + hq in acc[t][r]; its (max, sum) is in lane 4 kq + r
+  float Lq[4];
+  bool live[4];
+  size_t obase[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qq = 4 * kq + r;
+    const float l0 = readlane_f(lrun, r), l1 = readlane_f(lrun, 4 + r), l2 = readlane_f(lrun, 8 + r),
+                l3 = readlane_f(lrun, 12 + r);
+    Lq[r] = kq == 0 ? l0 : (kq == 1 ? l1 : (kq == 2 ? l2 : l3));
+    const int row = rbase + qq / G;
+    live[r] = row < B;
+    obase[r] = (size_t)min(row, B - 1) * nh + g * G + qq % G;  // (row, head) index
+  }
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (!live[r]) continue;
+      const int d = 16 * t + hq;
+      if (nsplit == 1) {
+        o[obase[r] * HD + d] = (Lq[r] > 0.f) ? acc[t][r] / Lq[r] : 0.f;
+      } else {
+        pacc[(obase[r] * kMaxSplit + sp) * HD + d] = acc[t][r];
+      }
+    }
+  if (nsplit > 1 && kq == 0 && qlive) {
+    const size_t slot = ((size_t)rq * nh + head) * kMaxSplit + sp;
+    pml[slot * 2 + 0] = mrun;
+    pml[slot * 2 + 1] = lrun;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_shared(hipStream_t s, int B, int nh, int nkv, const float* q, const uint16_t* qnorm, float eps,
+                              const float* rope, int type, const uint16_t* K, int cap, const RowWindows& win,
+                              int nsplit, float scale_log2, float* pacc, float* pml, float* o) {
+  const int G = nh / nkv;
+  // the union of the rows' windows
+  int u0 = win.start[0], u1 = win.start[0] + win.count[0];
+  for (int b = 1; b < B; ++b) {
+    u0 = win.start[b] < u0 ? win.start[b] : u0;
+    u1 = win.start[b] + win.count[b] > u1 ? win.start[b] + win.count[b] : u1;
+  }
+  const dim3 grid(nsplit, (B + 8 * (16 / G) - 1) / (8 * (16 / G)), nkv);
+#define MTPD_MQ(G_)                                                                                              \
+  if (G == G_)                                                                                                   \
+    return go(k_attn_mq<G_>, grid, 512, 0, s, B, nh, nkv, q, qnorm, eps, rope, type, K, cap, win, nsplit, u0, u1, \
+              scale_log2, pacc, pml, o);
+  MTPD_MQ(1) MTPD_MQ(2) MTPD_MQ(4) MTPD_MQ(8)
+#undef MTPD_MQ
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mtpd

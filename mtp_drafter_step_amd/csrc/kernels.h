@@ -70,6 +70,16 @@ hipError_t launch_qproj(hipStream_t s, int B, int H, int QD, Residual res, const
 
 // Single-query attention with q_norm + rotation in the prologue. nsplit == 1: o[b][h*hd + d] directly (fp32);
 // nsplit > 1: unnormalised partials (pacc, pml) for launch_attn_merge.
+// Whether launch_attn takes the multi-query kernel (a cache shared by the rows, head_dim 256, V = K): its key
+// splits then cover the union of the rows' windows.
+bool attn_uses_multi_query(bool shared, int hd, bool same_v);
+
+// Multi-query attention of rows sharing one cache (head_dim 256, V = K): same inputs and outputs as launch_attn
+// with scale_log2 = scale * log2(e).
+hipError_t launch_attn_shared(hipStream_t s, int B, int nh, int nkv, const float* q, const uint16_t* qnorm, float eps,
+                              const float* rope, int type, const uint16_t* K, int cap, const RowWindows& win,
+                              int nsplit, float scale_log2, float* pacc, float* pml, float* o);
+
 hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
                        float eps, const float* rope, int type, const uint16_t* K, const uint16_t* V, int cap,
                        const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, float* o);

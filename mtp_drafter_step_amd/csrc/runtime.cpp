@@ -344,6 +344,26 @@ int check_head_outputs(const mtpd_handle_s* h, const void* sel, const void* ids,
   return MTPD_OK;
 }
 
+// Splits of the union of the rows' windows for the multi-query attention (rows sharing one cache): about 256 blocks
+// over the (split, 128-query group, kv head) grid, at least 64 keys per split.
+int nsplit_multi_query(const mtpd::RowWindows& win, int B, int G, int nkv) {
+  int u0 = win.start[0], u1 = win.start[0] + win.count[0];
+  for (int b = 1; b < B; ++b) {
+    u0 = std::min(u0, win.start[b]);
+    u1 = std::max(u1, win.start[b] + win.count[b]);
+  }
+  const int groups = (B + 8 * (16 / G) - 1) / (8 * (16 / G)) * nkv;
+  const int ns = std::max(1, std::min((256 + groups - 1) / groups, (u1 - u0 + 63) / 64));
+  return std::min(ns, mtpd::kMaxSplit);
+}
+
+int split_count(const mtpd_handle_s* h, const mtpd_kv& kv, const mtpd::RowWindows& win, int B) {
+  const mtpd_config& c = h->cfg;
+  if (mtpd::attn_uses_multi_query(kv.shared != 0, c.head_dim, kv.v == kv.k))
+    return nsplit_multi_query(win, B, c.n_head / c.n_kv_head, c.n_kv_head);
+  return nsplit_for(win, B, c.n_kv_head);
+}
+
 int check_step_inputs(const mtpd_handle_s* h, int B, const uint16_t* th, const int32_t* tok, const uint16_t* temb,
                       const mtpd_shared_kv* kv, mtpd::RowWindows* win, int* nsplit) {
   CHECK(check_ptr(th, "target_hidden"));
@@ -353,8 +373,8 @@ int check_step_inputs(const mtpd_handle_s* h, int B, const uint16_t* th, const i
   if (!kv->rope) return fail(MTPD_EINVAL, "rope is NULL");
   CHECK(check_kv(h, kv->sliding, B, "sliding", &win[0], false));
   CHECK(check_kv(h, kv->full, B, "full", &win[1], true));
-  nsplit[0] = nsplit_for(win[0], B, h->cfg.n_kv_head);
-  nsplit[1] = nsplit_for(win[1], B, h->cfg.n_kv_head);
+  nsplit[0] = split_count(h, kv->sliding, win[0], B);
+  nsplit[1] = split_count(h, kv->full, win[1], B);
   return MTPD_OK;
 }
 
@@ -405,7 +425,7 @@ ChainView chain_view(const mtpd_handle_s* h, const mtpd_shared_kv* kv, const mtp
       v.win[t].start[i] = win[t].start[b0 + i];
       v.win[t].count[i] = win[t].count[b0 + i];
     }
-    v.nsplit[t] = nsplit_for(v.win[t], Bc, h->cfg.n_kv_head);
+    v.nsplit[t] = split_count(h, t ? kv->full : kv->sliding, v.win[t], Bc);
   }
   return v;
 }

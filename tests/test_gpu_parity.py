@@ -216,24 +216,39 @@ def test_left_padded_and_ring_buffer_caches():
     assert "first" in str(ei.value)
 
 
-def test_shared_cache_rows():
-    """Rows of one sequence reading one shared cache (own lengths, tokens and positions): bit-identical to the same
-    call with per-row copies of that cache, and equal to the oracle."""
+SHARED_CASES = {
+    # 4 query heads per kv head: 32 rows per block of the multi-query kernel, 8 live; ragged windows
+    "e4b_b8_ragged3000": dict(shape=synth.E4B, batch=8, context=3000, ragged=True),
+    # two kv heads (2 query heads each), two 64-row blocks
+    "e4b_nkv2_b80": dict(shape=dataclasses.replace(synth.E4B, n_kv_head=2), batch=80, context=1200, ragged=True),
+    # 8 query heads per kv head (16 rows per block), dense head
+    "e26b_b5_ragged1500": dict(shape=synth.E26B, batch=5, context=1500, ragged=True, gen_device="cuda"),
+}
+
+
+@pytest.mark.parametrize("name", list(SHARED_CASES))
+def test_shared_cache_rows(name):
+    """Rows of one sequence reading one shared cache (own lengths, tokens and positions; the multi-query attention)
+    against the oracle; the same call with per-row copies of the cache (the per-row attention) too."""
     from mtp_drafter_step_amd import SharedKV
-    say("shared cache, batch 8")
-    case = Case(synth.E4B, batch=8, context=3000, ragged=True, shared_kv=True)
-    out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    kw = SHARED_CASES[name]
+    say(f"shared cache {name}")
+    case = Case(**kw, shared_kv=True)
+    dense = case.shape.n_centroids == 0
+    B = kw["batch"]
+    out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=not dense)
     out = {k: v.clone() for k, v in out.items()}
-    copies = [t.expand(8, -1, -1, -1).contiguous() for t in case.kv.k]
-    kvc = SharedKV(copies[0], copies[1], case.kv.lens[0], case.kv.lens[1], case.kv.rope)
-    got = case.drafter.drafter_step(case.th, case.tok, case.temb, kvc, want_logits=True, want_sparse=True)
-    torch.cuda.synchronize()
-    for k in out:
-        assert torch.equal(got[k], out[k]), k
-    rows = list(range(8))
-    tally = compare_step(case, out, case.oracle_step(rows=rows), rows, where="shared")
+    rows = list(range(B)) if B <= 8 else list(range(0, B, 9)) + [B - 1]
+    ref = case.oracle_step(rows=rows, want_rows=dense)
+    tally = compare_step(case, out, ref, rows, where=f"shared {name}")
     say(tally.summary())
-    assert tally.sel_checked >= 4
+    assert tally.tok_checked >= len(rows) // 2
+    copies = [t.expand(B, -1, -1, -1).contiguous() for t in case.kv.k]
+    kvc = SharedKV(copies[0], copies[1], case.kv.lens[0], case.kv.lens[1], case.kv.rope)
+    got = case.drafter.drafter_step(case.th, case.tok, case.temb, kvc, want_logits=True, want_sparse=not dense)
+    torch.cuda.synchronize()
+    tally = compare_step(case, got, ref, rows, where=f"copies {name}")
+    assert tally.tok_checked >= len(rows) // 2
 
 
 def test_verify_width_step():
