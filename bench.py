@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 CSRC = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc")
 # the source file of each kernel; a kernel's digest covers that file and the shared headers
 KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_attn_mq": "k_attention_shared.hip", "k_head": "k_head.hip",
@@ -126,6 +127,15 @@ def site_bytes(site, shape, batch, lens, distinct_clusters, shared=False):
     if site == "sample_pick":  # one 4096-wide tile per row, its ids, the tile sums, the drawn token and probability
         return 4 * 4096 * B * (1 if shape.n_centroids == 0 else 2) + 4 * 256 * B + 8 * B
     raise KeyError(site)
+
+
+def site_flops(site, shape, lens, shared):
+    """Algorithmic flops of one attention launch over a cache shared by the rows (a dense contraction): for every
+    query (row, head), 2 * keys * head_dim for the scores and as many for P.V; None for the other sites."""
+    if not (shared and site.startswith("attn_")):
+        return None
+    keys = sum(L if site == "attn_full" else min(shape.swa_window, L) for L in lens)
+    return 4.0 * shape.n_head * keys * shape.head_dim
 
 
 def cpu_baseline(wl, seconds, w_dev=None, inp_dev=None):
@@ -284,6 +294,9 @@ def run_bench(args):
         e["launches"] += len(v)
         e["total_ms"] += float(np.sum(v))
         e["bytes"] += len(v) * site_bytes(site, shape, B, lens, u_mean, shared=wl.shared_kv)
+        fl = site_flops(site, shape, lens, wl.shared_kv)
+        if fl is not None:
+            e["flops"] = e.get("flops", 0.0) + len(v) * fl
         e["sites"].append(site)
     calls = args.timing_steps
     dom = max(per_kernel, key=lambda k: per_kernel[k]["total_ms"])
@@ -293,10 +306,23 @@ def run_bench(args):
     achieved = bytes_per_launch / avg_launch_s / 1e9
     tr = load_traffic(dom, wl.name)
     traffic = None if tr is None else tr["hbm_bytes_per_launch"]
+    if "flops" in dk:  # a dense contraction (attention over a cache shared by the rows): priced on the matrix cores
+        tfl = dk["flops"] / dk["launches"] / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": tfl, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tfl / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                "algorithmic_flops_per_launch": dk["flops"] / dk["launches"], "algorithmic_GBs": achieved}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    roof.update({"kernel": dom, "launch_sites": sorted(set(dk["sites"])),
+                 "launches_per_drafter_step": dk["launches"] / (calls * n),
+                 "avg_launch_us": avg_launch_s * 1e6, "algorithmic_bytes_per_launch": bytes_per_launch,
+                 "traffic_source": None if tr is None else os.path.relpath(traffic_file(dom, wl.name), ROOT)})
     kernels_table = {k: {"launches_per_drafter_step": v["launches"] / (calls * n),
                          "avg_launch_us": v["total_ms"] / v["launches"] * 1e3,
                          "us_per_drafter_step": v["total_ms"] * 1e3 / (calls * n),
                          "algorithmic_GBs": v["bytes"] / (v["total_ms"] * 1e-3) / 1e9,
+                         "algorithmic_TFLOPs": (v["flops"] / (v["total_ms"] * 1e-3) / 1e12) if "flops" in v else None,
                          "sites": sorted(set(v["sites"]))}
                      for k, v in sorted(per_kernel.items(), key=lambda kv_: -kv_[1]["total_ms"])}
 
@@ -338,12 +364,7 @@ def run_bench(args):
         "us_per_drafter_step": us_drafter_step,
         "us_per_drafter_step_p10_p90": [float(np.percentile(launch_ms, 10)) * 1e3 / n,
                                         float(np.percentile(launch_ms, 90)) * 1e3 / n],
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": dom, "launch_sites": sorted(set(dk["sites"])),
-                     "launches_per_drafter_step": dk["launches"] / (calls * n),
-                     "avg_launch_us": avg_launch_s * 1e6, "algorithmic_bytes_per_launch": bytes_per_launch,
-                     "traffic_source": None if tr is None else os.path.relpath(traffic_file(dom, wl.name), ROOT)},
+        "roofline": roof,
         "step_roofline": {"algorithmic_bytes_per_drafter_step": sbytes, "parts": parts,
                           "distinct_clusters_per_step": U,
                           "achieved_GBs": sbytes / (us_drafter_step * 1e-6) / 1e9,
