@@ -39,7 +39,8 @@ CSRC = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc")
 KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_attn_mq": "k_attention_shared.hip", "k_head": "k_head.hip",
                "k_head_dense": "k_head.hip", "k_final": "k_head.hip", "k_fill": "k_head.hip",
                "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip",
-               "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip"}
+               "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip", "k_gemm": "k_gemm.hip",
+               "k_rownorm": "k_gemm.hip", "k_merge": "k_gemm.hip", "k_token": "k_gemm.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 512 << 20
 
@@ -48,7 +49,11 @@ SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma"
                "o_proj": "k_oproj",
                "down": "k_dense", "ffn": "k_ffn", "post": "k_post", "head": "k_head", "final": "k_final",
                "scores": "k_dense", "fill": "k_fill", "head_dense": "k_head_dense", "zero_keys": "k_zero_u64",
-               "sample_tiles": "k_sample_tiles", "sample_pick": "k_sample_pick"}
+               "sample_tiles": "k_sample_tiles", "sample_pick": "k_sample_pick",
+               # the large-batch path
+               "token": "k_token", "rownorm": "k_rownorm", "post_norm": "k_rownorm", "attn_merge": "k_merge",
+               "pre_gemm": "k_gemm", "qproj_gemm": "k_gemm", "o_proj_gemm": "k_gemm", "ffn_gemm": "k_gemm",
+               "down_gemm": "k_gemm", "post_gemm": "k_gemm", "scores_gemm": "k_gemm"}
 
 
 def site_kernel(site, shape, shared=False):
@@ -96,6 +101,24 @@ def site_bytes(site, shape, batch, lens, distinct_clusters, shared=False):
     the path is split into kernels (attention partials) count for the merge only."""
     B, H, Bb, F, QD, hd = batch, shape.hidden, shape.backbone, shape.ffn, shape.q_dim, shape.head_dim
     act = lambda n: 4 * B * n  # noqa: E731  fp32 activation rows
+    if site.endswith("_gemm"):  # the large-batch path: the same weights and activations as the fused stages
+        base = {"pre_gemm": "pre", "qproj_gemm": "qproj", "o_proj_gemm": "o_proj", "ffn_gemm": "ffn",
+                "down_gemm": "down"}.get(site)
+        if site == "post_gemm":
+            return 2 * Bb * H + act(H) + 2 * B * Bb
+        if site == "scores_gemm":
+            return 2 * shape.n_centroids * H + act(H) + act(shape.n_centroids)
+        if site == "ffn_gemm":
+            return 2 * 2 * F * H + act(H) + act(F)
+        return site_bytes(base, shape, batch, lens, distinct_clusters, shared)
+    if site in ("rownorm", "post_norm"):  # residual stream, partials, norm weights, normed output
+        return 4 * act(H) + 4 * H
+    if site == "attn_merge":
+        return act(QD) * 2
+    if site == "fill":  # the -1e30 logits rows
+        return 4 * shape.vocab * B
+    if site == "token":
+        return 8 * max(shape.top_k, 1) * B + 8 * B
     W = shape.swa_window
     if site == "pre":
         return 2 * H * 2 * Bb + 2 * 2 * B * Bb + act(H)
@@ -372,6 +395,8 @@ def run_bench(args):
                           "cold_us_per_drafter_step": us_cold,
                           "cold_achieved_GBs": sbytes / (us_cold * 1e-6) / 1e9 if us_cold else None},
         "kernels": kernels_table,
+        "sites": {site: {"launches_per_drafter_step": len(v) / (calls * n), "avg_launch_us": float(np.mean(v)) * 1e3}
+                  for site, v in sorted(per_site.items(), key=lambda kv_: -sum(kv_[1]))},
         "kernel_source_sha256_16": source_digest(dom),
     }
     if not args.no_cpu_baseline:

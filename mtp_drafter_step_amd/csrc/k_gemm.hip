@@ -1,0 +1,326 @@
+// Dense stages for large batches (32 rows and more): the drafter's projections there are dense contractions
+// (M = batch), so they run as streaming matrix-core GEMMs that read each weight matrix once per 16 batch rows,
+// after one residual + norm kernel per stage (instead of every block repeating the stage's prologue).
+//
+// Pages cited (by title; sections as headed on each page):
+//   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
+//   [Inventory]  "Gemma 4 Assistant (MTP drafter) - tensor inventory (Stage 0)"
+//   [Guide]      "Gemma 4 Assistant 使用指南：用 MTP 投机解码与 KV Sharing 加速 Gemma 4 推理" (gitcode blog)
+//
+// The arithmetic is the same as the small-batch kernels' ([MTP doc] "What it is", "Tensor schema": pre_projection,
+// q / o projections, GeGLU FFN, sandwich norms, layer scalar, post_projection; [Inventory] "Centroid / ordered
+// embeddings LM head" step 1: centroid scores): bf16 weights, fp32 activations and accumulation. On the matrix cores
+// each fp32 activation enters as bf16 hi + lo (h = hi + lo within 2^-16 relative), two products per step.
+#include "device.h"
+
+namespace mtpd {
+namespace {
+
+// ------------------------------------------------------------------------------------------------------------
+// Y = W X^T over a K chunk: grid (ceil(N / 64), K / KC, ceil(B / 16)), 256 threads. Block: 64 output rows (one
+// 16-row tile per wave) x 16 batch rows x the K chunk blockIdx.y. The chunk of X (16 rows) is staged in LDS as bf16
+// hi + lo; each wave streams its 16 weight rows (A operand of v_mfma_f32_16x16x32_bf16: lane l reads row l%16,
+// 8 dims at 8 (l/16) of each 32-dim step) in double-buffered chunks of P steps.
+// Sources of X: SRC_F32 fp32 rows [B][K]; SRC_PRE the pre_projection input [target hidden ; escale * embedding of
+// the row's token] from bf16 tables (tokens already resolved). Epilogues: EPI_F32 partial [kc][B][N] fp32;
+// EPI_BF16 bf16 [B][N] (K in one chunk); EPI_GEGLU gelu_tanh(W x) * (W2 x) fp32 [B][N] (K in one chunk).
+
+enum { SRC_F32 = 0, SRC_PRE = 1 };
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_GEGLU = 2 };
+
+struct GemmSrc {
+  const float* x;          // SRC_F32: [B][K]
+  const uint16_t* th;      // SRC_PRE: target hidden [B][Bb]
+  const uint16_t* emb;     // SRC_PRE: embedding table [V][Bb]
+  const int32_t* tok;      // SRC_PRE: resolved tokens [B]
+  int Bb;                  // SRC_PRE: backbone width (K = 2 Bb)
+  float escale;            // SRC_PRE: factor on the embedding half
+};
+
+template <int KC, int SRC, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, const uint16_t* W, const uint16_t* W2,
+                                              float* Y, uint16_t* Yb) {
+  constexpr int NC = 16, KSTEPS = KC / 32, LROW = KC + 8;
+  constexpr int NW2 = EPI == EPI_GEGLU ? 2 : 1;
+  constexpr int P = EPI == EPI_GEGLU ? 4 : 8;  // steps per load chunk
+  static_assert(KC % 256 == 0 && KSTEPS % P == 0, "whole load chunks");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][NC][LROW];  // [hi / lo][batch row][dim]
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const int hq = lane & 15, kq = lane >> 4;
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int kc = blockIdx.y, kbase = kc * KC;
+  const int c0 = blockIdx.z * NC;
+  const uint16_t* wrow[2];
+  wrow[0] = W + (size_t)min(n0 + hq, N - 1) * K + kbase + 8 * kq;
+  wrow[1] = (EPI == EPI_GEGLU ? W2 : W) + (size_t)min(n0 + hq, N - 1) * K + kbase + 8 * kq;
+
+  uint4 a[2][NW2][P];  // [buffer][matrix][step]
+  auto load = [&](int bf, int ch) {
+#pragma unroll
+    for (int m = 0; m < NW2; ++m)
+#pragma unroll
+      for (int p = 0; p < P; ++p) a[bf][m][p] = ld_global16(wrow[m] + (ch * P + p) * 32);
+  };
+  load(0, 0);
+
+  // stage the X chunk: 16 rows x KC, rows past B are zero
+  constexpr int NV4 = NC * KC / 4 / 256;  // float4 (or 4 bf16) per thread
+#pragma unroll
+  for (int i = 0; i < NV4; ++i) {
+    const int e = (tid + i * 256) * 4, r = e / KC, k = e % KC;
+    const int b = min(c0 + r, B - 1);
+    float f[4];
+    if constexpr (SRC == SRC_F32) {
+      const float4 v = *reinterpret_cast<const float4*>(src.x + (size_t)b * K + kbase + k);
+      f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    } else {
+      const int kk = kbase + k;  // Bb % 256 == 0: 4 dims lie in one half
+      const bool hid = kk < src.Bb;
+      const uint16_t* p = hid ? src.th + (size_t)b * src.Bb + kk : src.emb + (size_t)src.tok[b] * src.Bb + (kk - src.Bb);
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      unpack4(w, f);
+      if (!hid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] *= src.escale;
+      }
+    }
+    const bool live = c0 + r < B;
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = live ? f[j] : 0.f;
+      hi[j] = f2bf(v);
+      lo[j] = f2bf(v - bf2f(hi[j]));
+    }
+    *reinterpret_cast<uint2*>(&xs[0][r][k]) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2*>(&xs[1][r][k]) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+  }
+  __syncthreads();
+
+  f32x4 acc[NW2];
+#pragma unroll
+  for (int m = 0; m < NW2; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int bf, int ch) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int k = (ch * P + p) * 32 + 8 * kq;
+      const uint4 bh = *reinterpret_cast<const uint4*>(&xs[0][hq][k]);
+      const uint4 bl = *reinterpret_cast<const uint4*>(&xs[1][hq][k]);
+#pragma unroll
+      for (int m = 0; m < NW2; ++m) {
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[bf][m][p]),
+                                                         __builtin_bit_cast(bf16x8, bh), acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[bf][m][p]),
+                                                         __builtin_bit_cast(bf16x8, bl), acc[m], 0, 0, 0);
+      }
+    }
+  };
+  constexpr int NCH = KSTEPS / P;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ch += 2) {
+    if (ch + 1 < NCH) load(1, ch + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0, ch);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch + 2 < NCH) load(0, ch + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch + 1 < NCH) compute(1, ch + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // D: rows n0 + 4 kq + i, batch column c0 + hq
+  const int c = c0 + hq, n = n0 + 4 * kq;
+  if (c < B && n0 < N) {  // N % 16 == 0: a wave's 16 rows are wholly inside or outside
+    if constexpr (EPI == EPI_F32) {
+      *reinterpret_cast<float4*>(Y + ((size_t)kc * B + c) * N + n) = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+    } else if constexpr (EPI == EPI_BF16) {
+      *reinterpret_cast<uint2*>(Yb + (size_t)c * N + n) =
+          make_uint2(f2bf(acc[0][0]) | ((uint32_t)f2bf(acc[0][1]) << 16), f2bf(acc[0][2]) | ((uint32_t)f2bf(acc[0][3]) << 16));
+    } else {
+      float mv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mv[i] = gelu_tanh(acc[0][i]) * acc[NW2 - 1][i];
+      *reinterpret_cast<float4*>(Y + (size_t)c * N + n) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Residual + norms of one row per block (256 threads, H = 256 HPT): x = sum of the nx partials of xp (stride xs);
+// with a delta, x = (x + RMSNorm(sum of the nd partials of the delta; w_delta)) * scale; x_new = x (when set);
+// u = RMSNorm(x; w_norm). Partial counts are template maxima NX / ND (loads clamped, surplus weighted by zero).
+
+template <int HPT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return s;
+}
+
+template <int HPT, int NX, int ND>
+__global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx, size_t xs, const float* delta,
+                                                 int nd, size_t ds, const uint16_t* w_delta, float scale,
+                                                 const uint16_t* w_norm, float eps, float* x_new, float* u,
+                                                 uint64_t* keys_zero) {
+  constexpr int H = HPT * 256;
+  __shared__ float red[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  float xv[NX][HPT], dv[ND][HPT];
+#pragma unroll
+  for (int p = 0; p < NX; ++p)
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) xv[p][i] = xp[(size_t)min(p, nx - 1) * xs + (size_t)b * H + tid + 256 * i];
+#pragma unroll
+  for (int p = 0; p < ND; ++p)
+#pragma unroll
+    for (int i = 0; i < HPT; ++i)
+      dv[p][i] = delta ? delta[(size_t)min(p, nd - 1) * ds + (size_t)b * H + tid + 256 * i] : 0.f;
+  float x[HPT];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < NX; ++p) s += p < nx ? xv[p][i] : 0.f;
+    x[i] = s;
+  }
+  if (delta) {
+    float d[HPT], ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int p = 0; p < ND; ++p) s += p < nd ? dv[p][i] : 0.f;
+      d[i] = s;
+      ss = fmaf(s, s, ss);
+    }
+    const float r = 1.0f / sqrtf(block_sum<HPT>(ss, red) / (float)H + eps);
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) x[i] = (x[i] + d[i] * r * bf2f(w_delta[tid + 256 * i])) * scale;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    if (x_new) x_new[(size_t)b * H + tid + 256 * i] = x[i];
+    ss = fmaf(x[i], x[i], ss);
+  }
+  const float r = 1.0f / sqrtf(block_sum<HPT>(ss, red) / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) u[(size_t)b * H + tid + 256 * i] = x[i] * r * bf2f(w_norm[tid + 256 * i]);
+  if (keys_zero && tid == 0) keys_zero[b] = 0ull;
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Merge of the key-range split partials of the attention: o[b][h][d] = sum_s f_s A_s[d] / sum_s f_s L_s with
+// f_s = 2^(M_s - max M). grid B * nh, hd threads.
+__global__ __launch_bounds__(256) void k_merge(int nsplit, int hd, const float* pacc, const float* pml, float* o) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const size_t base = (size_t)bh * kMaxSplit;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml[(base + s) * 2]);
+  float L = 0.f, A = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float mw = pml[(base + s) * 2];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      L = fmaf(pml[(base + s) * 2 + 1], f, L);
+      A = fmaf(pacc[(base + s) * hd + d], f, A);
+    }
+  }
+  o[(size_t)bh * hd + d] = (L > 0.f) ? A / L : 0.f;
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// The step's input token of each row (the caller's, or the previous step's argmax from its keys), clamped into
+// [0, V), recorded where the token source asks. grid B, 64 threads.
+__global__ void k_token(int V, TokenSource ts, int32_t* tok_out) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const uint64_t kraw = ts.keys[(size_t)b * ts.k + min(lane, ts.k - 1)];
+  int t = ts.tok[b];
+  if (ts.use_keys) {
+    t = key_id(wave_max_u64(lane < ts.k ? kraw : 0ull));
+    if (lane == 0) {
+      if (ts.out) ts.out[(size_t)b * ts.out_stride] = t;
+      if (ts.next) ts.next[b] = t;
+    }
+  }
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+  if (lane == 0) tok_out[b] = t;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------------------
+// launchers
+
+int gemm_chunks(int B, int N, int K, bool one_chunk) {
+  // K chunk of 256 d (d | K / 256, d <= 4): the largest that still gives about 256 blocks
+  const int q = K / 256;
+  if (one_chunk) return 1;
+  const int nb = ((N + 63) / 64) * ((B + 15) / 16);
+  int best = q;  // chunks
+  for (int d = 4; d >= 1; --d) {
+    if (q % d) continue;
+    best = q / d;
+    if (nb * (q / d) >= 256) break;
+  }
+  return best;
+}
+
+hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float* X, const uint16_t* th,
+                       const uint16_t* emb, const int32_t* tok, int Bb, float escale, const uint16_t* W,
+                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks) {
+  if (K % 256 || N % 16 || K > 4096 * 2 || (K / 256) % nchunks) return hipErrorInvalidValue;
+  const int KC = K / nchunks;
+  const dim3 grid((N + 63) / 64, nchunks, (B + 15) / 16);
+  GemmSrc src{X, th, emb, tok, Bb, escale};
+#define MTPD_GEMM(KC_, SRC_, EPI_) \
+  if (KC == KC_) return go(k_gemm<KC_, SRC_, EPI_>, grid, 256, 0, s, B, N, K, src, W, W2, Y, Yb);
+  if (kind == 0) {  // fp32 partials from fp32 rows
+    MTPD_GEMM(256, SRC_F32, EPI_F32) MTPD_GEMM(512, SRC_F32, EPI_F32) MTPD_GEMM(768, SRC_F32, EPI_F32)
+    MTPD_GEMM(1024, SRC_F32, EPI_F32)
+  } else if (kind == 1) {  // bf16 out
+    MTPD_GEMM(256, SRC_F32, EPI_BF16) MTPD_GEMM(512, SRC_F32, EPI_BF16) MTPD_GEMM(768, SRC_F32, EPI_BF16)
+    MTPD_GEMM(1024, SRC_F32, EPI_BF16)
+  } else if (kind == 2) {  // GeGLU
+    MTPD_GEMM(256, SRC_F32, EPI_GEGLU) MTPD_GEMM(512, SRC_F32, EPI_GEGLU) MTPD_GEMM(768, SRC_F32, EPI_GEGLU)
+    MTPD_GEMM(1024, SRC_F32, EPI_GEGLU)
+  } else {  // pre_projection partials
+    MTPD_GEMM(256, SRC_PRE, EPI_F32) MTPD_GEMM(512, SRC_PRE, EPI_F32) MTPD_GEMM(768, SRC_PRE, EPI_F32)
+    MTPD_GEMM(1024, SRC_PRE, EPI_F32)
+  }
+#undef MTPD_GEMM
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_rownorm(hipStream_t s, int B, int H, const float* xp, int nx, size_t xs, const float* delta, int nd,
+                          size_t ds, const uint16_t* w_delta, float scale, const uint16_t* w_norm, float eps,
+                          float* x_new, float* u, uint64_t* keys_zero) {
+  const int hpt = H / 256;
+  const int NXc = nx <= 1 ? 1 : nx <= 4 ? 4 : nx <= 8 ? 8 : nx <= 16 ? 16 : 32;
+  const int NDc = nd <= 1 ? 1 : nd <= 4 ? 4 : 16;
+  if (H % 256 || hpt > 4 || nx > 32 || nd > 16) return hipErrorInvalidValue;
+#define MTPD_RN(HPT_, NX_, ND_)                                                                                    \
+  if (hpt == HPT_ && NXc == NX_ && NDc == ND_)                                                                     \
+    return go(k_rownorm<HPT_, NX_, ND_>, B, 256, 0, s, B, xp, nx, xs, delta, nd, ds, w_delta, scale, w_norm, eps, \
+              x_new, u, keys_zero);
+#define MTPD_RN_H(NX_, ND_) MTPD_RN(1, NX_, ND_) MTPD_RN(2, NX_, ND_) MTPD_RN(3, NX_, ND_) MTPD_RN(4, NX_, ND_)
+  MTPD_RN_H(1, 1) MTPD_RN_H(1, 4) MTPD_RN_H(1, 16)
+  MTPD_RN_H(4, 1) MTPD_RN_H(8, 1) MTPD_RN_H(16, 1) MTPD_RN_H(32, 1)
+#undef MTPD_RN_H
+#undef MTPD_RN
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
+                        float* o) {
+  return go(k_merge, B * nh, hd, 0, s, nsplit, hd, pacc, pml, o);
+}
+
+hipError_t launch_token(hipStream_t s, int B, int V, TokenSource ts, int32_t* tok_out) {
+  return go(k_token, B, 64, 0, s, V, ts, tok_out);
+}
+
+}  // namespace mtpd

@@ -142,4 +142,28 @@ hipError_t launch_fill(hipStream_t s, float* logits, size_t n);
 // y[b][n] = centroids[n] . h[b] for the masked head on caller-provided states (K = H, N = C).
 hipError_t launch_scores(hipStream_t s, int B, int H, int C, const float* h, const uint16_t* w_cen, float* scores);
 
+// ---- dense stages for large batches (k_gemm.hip)
+
+// K chunks for a streaming GEMM of B rows, N outputs and reduction K (1 when the epilogue needs the whole sum).
+int gemm_chunks(int B, int N, int K, bool one_chunk);
+
+// Matrix-core GEMM Y = W X^T, W bf16 [N][K], over nchunks K chunks (K % 256 == 0, N % 16 == 0). kind 0: X fp32
+// [B][K] -> fp32 partials Y [nchunks][B][N]; 1: -> bf16 Yb [B][N]; 2: GeGLU gelu_tanh(W X) * (W2 X) -> fp32 Y [B][N];
+// 3: X = [th ; escale * emb[tok]] (bf16 tables, K = 2 Bb) -> fp32 partials. Kinds 1 and 2 need nchunks == 1.
+hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float* X, const uint16_t* th,
+                       const uint16_t* emb, const int32_t* tok, int Bb, float escale, const uint16_t* W,
+                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks);
+
+// Per row: x = sum of nx partials of xp (stride xs); with delta (nd partials, stride ds) x = (x + RMSNorm(delta;
+// w_delta)) * scale; x_new = x (when set); u = RMSNorm(x; w_norm); keys_zero[b] = 0 (when set). H % 256 == 0.
+hipError_t launch_rownorm(hipStream_t s, int B, int H, const float* xp, int nx, size_t xs, const float* delta, int nd,
+                          size_t ds, const uint16_t* w_delta, float scale, const uint16_t* w_norm, float eps,
+                          float* x_new, float* u, uint64_t* keys_zero);
+
+// o[b][h] = merge of the nsplit key-range partials (pacc, pml) of the attention.
+hipError_t launch_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml, float* o);
+
+// tok_out[b] = the step's input token of row b from the token source (recorded where it asks), clamped to [0, V).
+hipError_t launch_token(hipStream_t s, int B, int V, TokenSource ts, int32_t* tok_out);
+
 }  // namespace mtpd

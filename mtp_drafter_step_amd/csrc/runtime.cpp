@@ -92,7 +92,8 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Offsets of every intermediate in the caller's workspace for a given batch.
 struct Plan {
-  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, stok, tsum, row, total;
+  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, stok, tsum, row, u, xp, dp, rtok,
+      total;
 };
 
 // Argmax keys per row: one per selected cluster for the masked head, one for the dense head.
@@ -127,6 +128,11 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.stok = take((size_t)B * 4);                                  // sampled tokens (next step's input)
   p.tsum = take((size_t)B * mtpd::kMaxSampleTiles * 4);          // sampling tile sums
   p.row = take(c.n_centroids == 0 ? (size_t)B * c.vocab * 4 : 0);  // dense logits rows for sampling
+  // the large-batch path: normed stage inputs, K-split partials of pre_projection and down, resolved tokens
+  p.u = take((size_t)B * H * 4);
+  p.xp = take((size_t)(2 * Bb / 256) * B * H * 4);
+  p.dp = take((size_t)(F / 256) * B * H * 4);
+  p.rtok = take((size_t)B * 4);
   p.total = off;
   return p;
 }
@@ -278,8 +284,9 @@ int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
 }
 
 // One drafter step on workspace buffers: input hidden `th` [B][Bb], token source `ts`; leaves the per-slot argmax
-// keys in the workspace (the step's token is their maximum).
-int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const uint16_t* th,
+// keys in the workspace (the step's token is their maximum). Small batches: kernels that fold each stage's residual
+// and norm into their prologue.
+int run_step_small(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const uint16_t* th,
              mtpd::TokenSource ts, const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win,
              const int* nsplit, float* logits, uint16_t* hidden_out, int32_t* sel_out, int32_t* ids_out,
              float* z_out) {
@@ -327,6 +334,104 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
                            h->w.centroids, at<float>(ws, p.h), hidden_out, at<float>(ws, p.scores),
                            c.n_centroids == 0 ? at<uint64_t>(ws, p.keys) : nullptr));
   return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, sel_out, ids_out, z_out);
+}
+
+// Batches of at least this many rows take the matrix-core path for the dense stages (MTPD_GEMM_PATH=1 / 0 forces
+// it on / off, read at each call).
+constexpr int kGemmRows = 32;
+
+bool use_gemm_path(int B) {
+  const char* e = getenv("MTPD_GEMM_PATH");
+  if (e && e[0] == '1') return true;
+  if (e && e[0] == '0') return false;
+  return B >= kGemmRows;
+}
+
+// One drafter step with the dense stages as streaming matrix-core GEMMs (large batches): a residual + norm kernel
+// per stage feeds each GEMM its normed input once; K-split partials are summed by the next norm kernel.
+int run_step_gemm(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const uint16_t* th,
+                  mtpd::TokenSource ts, const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win,
+                  const int* nsplit, float* logits, uint16_t* hidden_out, int32_t* sel_out, int32_t* ids_out,
+                  float* z_out) {
+  const mtpd_config& c = h->cfg;
+  const int H = c.hidden, Bb = c.backbone, QD = c.n_head * c.head_dim, F = c.ffn, nL = c.n_layer;
+  const bool dense = c.n_centroids == 0;
+  const size_t BH = (size_t)B * H;
+  float* x = at<float>(ws, p.x[0]);
+  float* u = at<float>(ws, p.u);
+  float* q = at<float>(ws, p.q);
+  float* o = at<float>(ws, p.o);
+  float* t = at<float>(ws, p.t);
+  float* m = at<float>(ws, p.m);
+  float* xp = at<float>(ws, p.xp);
+  float* dp = at<float>(ws, p.dp);
+  int32_t* rtok = at<int32_t>(ws, p.rtok);
+  // input assembly + pre_projection ([MTP doc] "What it is"; [Guide] section 2(3))
+  KLAUNCH(h, "token", mtpd::launch_token(s, B, c.vocab, ts, rtok));
+  const int npre = mtpd::gemm_chunks(B, H, 2 * Bb, false);
+  KLAUNCH(h, "pre_gemm", mtpd::launch_gemm(s, 3, B, H, 2 * Bb, nullptr, th, temb, rtok, Bb, c.embed_scale, h->w.pre_proj,
+                                           nullptr, xp, nullptr, npre));
+  const float* xin = xp;  // the residual stream entering the next norm, as partials
+  int nx = npre;
+  const float* din = nullptr;
+  int nd = 1;
+  const uint16_t* wd = nullptr;
+  float sc = 1.0f;
+  const int no = mtpd::gemm_chunks(B, H, QD, false), nf = mtpd::gemm_chunks(B, H, F, false);
+  for (int l = 0; l < nL; ++l) {
+    const mtpd_layer& L = h->layers[l];
+    const int type = ((c.full_attn_layers >> l) & 1u) ? 1 : 0;
+    const mtpd_kv& cache = type ? kv->full : kv->sliding;
+    KLAUNCH(h, "rownorm", mtpd::launch_rownorm(s, B, H, xin, nx, BH, din, nd, BH, wd, sc, L.attn_norm, c.rms_eps, x, u,
+                                               nullptr));
+    KLAUNCH(h, "qproj_gemm", mtpd::launch_gemm(s, 0, B, QD, H, u, nullptr, nullptr, nullptr, 0, 0.f, L.attn_q, nullptr,
+                                               q, nullptr, 1));
+    KLAUNCH(h, type ? "attn_full" : "attn_sliding",
+            mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
+                              cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale, at<float>(ws, p.pacc),
+                              at<float>(ws, p.pml), o));
+    if (nsplit[type] > 1)
+      KLAUNCH(h, "attn_merge", mtpd::launch_merge(s, B, c.n_head, c.head_dim, nsplit[type], at<float>(ws, p.pacc),
+                                                  at<float>(ws, p.pml), o));
+    KLAUNCH(h, "o_proj_gemm", mtpd::launch_gemm(s, 0, B, H, QD, o, nullptr, nullptr, nullptr, 0, 0.f, L.attn_output,
+                                                nullptr, t, nullptr, no));
+    KLAUNCH(h, "rownorm", mtpd::launch_rownorm(s, B, H, x, 1, 0, t, no, BH, L.post_attention_norm, 1.0f, L.ffn_norm,
+                                               c.rms_eps, x, u, nullptr));
+    KLAUNCH(h, "ffn_gemm", mtpd::launch_gemm(s, 2, B, F, H, u, nullptr, nullptr, nullptr, 0, 0.f, L.ffn_gate, L.ffn_up,
+                                             m, nullptr, 1));
+    KLAUNCH(h, "down_gemm", mtpd::launch_gemm(s, 0, B, H, F, m, nullptr, nullptr, nullptr, 0, 0.f, L.ffn_down, nullptr,
+                                              dp, nullptr, nf));
+    xin = x;
+    nx = 1;
+    din = dp;
+    nd = nf;
+    wd = L.post_ffw_norm;
+    sc = L.layer_output_scale;
+  }
+  // output norm, post_projection (the next step's hidden input, [Guide] section 6) and centroid scores
+  KLAUNCH(h, "post_norm", mtpd::launch_rownorm(s, B, H, xin, nx, BH, din, nd, BH, wd, sc, h->w.output_norm, c.rms_eps,
+                                               nullptr, at<float>(ws, p.h), dense ? at<uint64_t>(ws, p.keys) : nullptr));
+  KLAUNCH(h, "post_gemm", mtpd::launch_gemm(s, 1, B, Bb, H, at<float>(ws, p.h), nullptr, nullptr, nullptr, 0, 0.f,
+                                            h->w.post_proj, nullptr, nullptr, hidden_out, 1));
+  if (!dense && c.n_centroids % 16 != 0) {
+    KLAUNCH(h, "scores", mtpd::launch_scores(s, B, H, c.n_centroids, at<float>(ws, p.h), h->w.centroids,
+                                             at<float>(ws, p.scores)));
+    if (logits) KLAUNCH(h, "fill", mtpd::launch_fill(s, logits, (size_t)B * c.vocab));
+  } else if (!dense) {
+    KLAUNCH(h, "scores_gemm", mtpd::launch_gemm(s, 0, B, c.n_centroids, H, at<float>(ws, p.h), nullptr, nullptr, nullptr,
+                                                0, 0.f, h->w.centroids, nullptr, at<float>(ws, p.scores), nullptr, 1));
+    if (logits) KLAUNCH(h, "fill", mtpd::launch_fill(s, logits, (size_t)B * c.vocab));
+  }
+  return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, sel_out, ids_out, z_out);
+}
+
+int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const uint16_t* th,
+             mtpd::TokenSource ts, const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win,
+             const int* nsplit, float* logits, uint16_t* hidden_out, int32_t* sel_out, int32_t* ids_out,
+             float* z_out) {
+  if (use_gemm_path(B))
+    return run_step_gemm(h, s, ws, p, B, th, ts, temb, kv, win, nsplit, logits, hidden_out, sel_out, ids_out, z_out);
+  return run_step_small(h, s, ws, p, B, th, ts, temb, kv, win, nsplit, logits, hidden_out, sel_out, ids_out, z_out);
 }
 
 int check_call(const mtpd_handle_s* h, void* ws, int B) {

@@ -264,6 +264,41 @@ def test_verify_width_step():
     assert tally.sel_checked >= 2
 
 
+GEMM_PATH_CASES = {
+    # 32+ rows take the matrix-core dense stages by default: run both paths on the same inputs
+    "e4b_b40_ragged2000": dict(shape=synth.E4B, batch=40, context=2000, ragged=True),
+    "e26b_b32_ctx4000": dict(shape=synth.E26B, batch=32, context=4000, ragged=True, gen_device="cuda"),
+    # and the matrix-core path forced on a small batch (one 16-row pass with ragged columns)
+    "e4b_b5_forced": dict(shape=synth.E4B, batch=5, context=900, ragged=True),
+}
+
+
+@pytest.mark.parametrize("name", list(GEMM_PATH_CASES))
+def test_dense_stage_paths(name):
+    """The large-batch path (residual + norm kernels, matrix-core GEMMs with K-split partials, separate attention
+    merge) and the small-batch path (fused prologues), each forced on a fresh handle, both against the oracle."""
+    import os
+    from mtp_drafter_step_amd import Drafter
+    kw = GEMM_PATH_CASES[name]
+    case = Case(**kw)
+    dense = case.shape.n_centroids == 0
+    B = kw["batch"]
+    rows = list(range(B)) if B <= 8 else list(range(0, B, 6)) + [B - 1]
+    ref = case.oracle_step(rows=rows, want_rows=dense)
+    for flag in ("1", "0"):
+        say(f"dense stages {name} MTPD_GEMM_PATH={flag}")
+        os.environ["MTPD_GEMM_PATH"] = flag
+        try:
+            d = Drafter(case.shape, case.wg, max_batch=B)
+            out = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=not dense)
+            torch.cuda.synchronize()
+        finally:
+            del os.environ["MTPD_GEMM_PATH"]
+        tally = compare_step(case, out, ref, rows, where=f"{name} path {flag}")
+        say(tally.summary())
+        assert tally.tok_checked >= len(rows) // 2
+
+
 def test_drafter_step_is_deterministic():
     case = Case(synth.E4B, batch=4, context=2000, ragged=True)
     a = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
