@@ -17,10 +17,11 @@ namespace mtpd {
 namespace {
 
 // ------------------------------------------------------------------------------------------------------------
-// Y = W X^T over a K chunk: grid (ceil(N / 64), K / KC, ceil(B / 16)), 256 threads. Block: 64 output rows (one
-// 16-row tile per wave) x 16 batch rows x the K chunk blockIdx.y. The chunk of X (16 rows) is staged in LDS as bf16
-// hi + lo; each wave streams its 16 weight rows (A operand of v_mfma_f32_16x16x32_bf16: lane l reads row l%16,
-// 8 dims at 8 (l/16) of each 32-dim step) in double-buffered chunks of P steps.
+// Y = W X^T over a K chunk: grid (ceil(N / (64 / WPT)), K / KC, ceil(B / 16)), 256 threads. Block: 64 / WPT output
+// rows x 16 batch rows x the K chunk blockIdx.y. The chunk of X (16 rows) is staged in LDS as bf16 hi + lo. WPT
+// waves share each 16-row tile, each streaming its tile's weight rows over its own KC / WPT of the chunk (A operand
+// of v_mfma_f32_16x16x32_bf16: lane l reads row l%16, 8 dims at 8 (l/16) of each 32-dim step) in double-buffered
+// chunks of P steps, so that a wave's loads take few round trips; the WPT partial sums meet in LDS in a fixed order.
 // Sources of X: SRC_F32 fp32 rows [B][K]; SRC_PRE the pre_projection input [target hidden ; escale * embedding of
 // the row's token] from bf16 tables (tokens already resolved). Epilogues: EPI_F32 partial [kc][B][N] fp32;
 // EPI_BF16 bf16 [B][N] (K in one chunk); EPI_GEGLU gelu_tanh(W x) * (W2 x) fp32 [B][N] (K in one chunk).
@@ -37,22 +38,27 @@ struct GemmSrc {
   float escale;            // SRC_PRE: factor on the embedding half
 };
 
-template <int KC, int SRC, int EPI>
+template <int KC, int WPT, int SRC, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, const uint16_t* W, const uint16_t* W2,
                                               float* Y, uint16_t* Yb) {
   constexpr int NC = 16, KSTEPS = KC / 32, LROW = KC + 8;
+  constexpr int WSTEPS = KSTEPS / WPT;  // steps per wave (WPT waves per 16-row tile)
   constexpr int NW2 = EPI == EPI_GEGLU ? 2 : 1;
-  constexpr int P = EPI == EPI_GEGLU ? 4 : 8;  // steps per load chunk
-  static_assert(KC % 256 == 0 && KSTEPS % P == 0, "whole load chunks");
+  // steps per load chunk: 8 (4 with the two GeGLU matrices), fewer when the wave's steps do not divide
+  constexpr int PMAX = EPI == EPI_GEGLU ? 4 : 8;
+  constexpr int P = WSTEPS % PMAX == 0 ? PMAX : (WSTEPS % 4 == 0 ? 4 : (WSTEPS % 2 == 0 ? 2 : 1));
+  static_assert(KC % 256 == 0 && WSTEPS % P == 0, "whole load chunks");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][NC][LROW];  // [hi / lo][batch row][dim]
+  __shared__ __attribute__((aligned(16))) f32x4 part[4][NW2][64];     // partial sums of the waves of a tile
   const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
   const int hq = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int n0 = blockIdx.x * (64 / WPT) + (wave / WPT) * 16;
+  const int kw = (wave % WPT) * (KC / WPT);  // the wave's part of the chunk
   const int kc = blockIdx.y, kbase = kc * KC;
   const int c0 = blockIdx.z * NC;
   const uint16_t* wrow[2];
-  wrow[0] = W + (size_t)min(n0 + hq, N - 1) * K + kbase + 8 * kq;
-  wrow[1] = (EPI == EPI_GEGLU ? W2 : W) + (size_t)min(n0 + hq, N - 1) * K + kbase + 8 * kq;
+  wrow[0] = W + (size_t)min(n0 + hq, N - 1) * K + kbase + kw + 8 * kq;
+  wrow[1] = (EPI == EPI_GEGLU ? W2 : W) + (size_t)min(n0 + hq, N - 1) * K + kbase + kw + 8 * kq;
 
   uint4 a[2][NW2][P];  // [buffer][matrix][step]
   auto load = [&](int bf, int ch) {
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
   auto compute = [&](int bf, int ch) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int k = (ch * P + p) * 32 + 8 * kq;
+      const int k = kw + (ch * P + p) * 32 + 8 * kq;
       const uint4 bh = *reinterpret_cast<const uint4*>(&xs[0][hq][k]);
       const uint4 bl = *reinterpret_cast<const uint4*>(&xs[1][hq][k]);
 #pragma unroll
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
       }
     }
   };
-  constexpr int NCH = KSTEPS / P;
+  constexpr int NCH = WSTEPS / P;
 #pragma unroll
   for (int ch = 0; ch < NCH; ch += 2) {
     if (ch + 1 < NCH) load(1, ch + 1);
@@ -128,6 +134,23 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // the tile's WPT partial sums, added in wave order by the tile's first wave
+  if constexpr (WPT > 1) {
+#pragma unroll
+    for (int m = 0; m < NW2; ++m) part[wave][m][lane] = acc[m];
+    __syncthreads();
+    if (wave % WPT != 0) return;
+#pragma unroll
+    for (int m = 0; m < NW2; ++m) {
+      f32x4 sum = part[wave][m][lane];
+#pragma unroll
+      for (int w = 1; w < WPT; ++w) {
+        const f32x4 v = part[wave + w][m][lane];
+        sum = f32x4{sum[0] + v[0], sum[1] + v[1], sum[2] + v[2], sum[3] + v[3]};
+      }
+      acc[m] = sum;
+    }
+  }
   // D: rows n0 + 4 kq + i, batch column c0 + hq
   const int c = c0 + hq, n = n0 + 4 * kq;
   if (c < B && n0 < N) {  // N % 16 == 0: a wave's 16 rows are wholly inside or outside
@@ -274,10 +297,16 @@ hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float
                        const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks) {
   if (K % 256 || N % 16 || K > 4096 * 2 || (K / 256) % nchunks) return hipErrorInvalidValue;
   const int KC = K / nchunks;
-  const dim3 grid((N + 63) / 64, nchunks, (B + 15) / 16);
+  // waves per 16-row tile: more only while the grid is below about 256 blocks (each block stages its X chunk, so
+  // more blocks cost L2 reads), and at most KC / 256
+  int wpt = 1;
+  auto blocks = [&](int w) { return ((N + 64 / w - 1) / (64 / w)) * nchunks * ((B + 15) / 16); };
+  while (wpt < 4 && wpt * 2 <= KC / 256 && blocks(wpt) < 256) wpt *= 2;
+  const dim3 grid((N + 64 / wpt - 1) / (64 / wpt), nchunks, (B + 15) / 16);
   GemmSrc src{X, th, emb, tok, Bb, escale};
-#define MTPD_GEMM(KC_, SRC_, EPI_) \
-  if (KC == KC_) return go(k_gemm<KC_, SRC_, EPI_>, grid, 256, 0, s, B, N, K, src, W, W2, Y, Yb);
+#define MTPD_GEMM_W(KC_, WPT_, SRC_, EPI_) \
+  if (KC == KC_ && wpt == WPT_) return go(k_gemm<KC_, WPT_, SRC_, EPI_>, grid, 256, 0, s, B, N, K, src, W, W2, Y, Yb);
+#define MTPD_GEMM(KC_, SRC_, EPI_) MTPD_GEMM_W(KC_, 1, SRC_, EPI_) MTPD_GEMM_W(KC_, 2, SRC_, EPI_) MTPD_GEMM_W(KC_, 4, SRC_, EPI_)
   if (kind == 0) {  // fp32 partials from fp32 rows
     MTPD_GEMM(256, SRC_F32, EPI_F32) MTPD_GEMM(512, SRC_F32, EPI_F32) MTPD_GEMM(768, SRC_F32, EPI_F32)
     MTPD_GEMM(1024, SRC_F32, EPI_F32)
@@ -292,6 +321,7 @@ hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float
     MTPD_GEMM(1024, SRC_PRE, EPI_F32)
   }
 #undef MTPD_GEMM
+#undef MTPD_GEMM_W
   return hipErrorInvalidValue;
 }
 
