@@ -18,9 +18,9 @@ namespace {
 // every row reads the same keys, so the query rows meet each key tile once. A block holds 128 queries (8 waves x 16
 // queries: 16 / G rows x the G query heads of kv head blockIdx.z) and one key range: split blockIdx.x of the union
 // [u0, u1) of the rows' windows. Key tiles of 64 rows are staged in LDS for all waves (double-buffered, one barrier
-// per tile), twice: row-major (K rows for the scores) and transposed (each dim's keys contiguous, so a lane's four
-// keys of one dim, the P.V operand, are one 8-byte read). Each thread loads 4 x 4 (key x dim) blocks so that it can
-// write both layouts with 8-byte stores. Per wave and 16-key batch:
+// per tile), twice: row-major (K rows for the scores) and transposed (each dim's keys contiguous, so a lane's keys
+// of one dim, the P.V operand, are 8-byte reads). Each thread loads 4 x 4 (key x dim) blocks so that it can
+// write both layouts with 8-byte stores. Per wave and 32-key batch (two 16-key score tiles):
 //   S^T[16 keys][16 queries] = K_tile . Q^T with v_mfma_f32_16x16x32_bf16, the keys as A rows from LDS and the
 //     queries as B columns held in registers as bf16 hi + lo (q after q_norm and rotation, fp32-level accuracy);
 //   online softmax per query (lane column), each key masked by the query row's own window;
@@ -67,18 +67,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
   // first key tile in flight before the q prologue: thread t loads the 4 x 4 blocks (keys 4 kg .. +4, dims 4 dg ..
   // +4) with kg = i / 64, dg = i % 64 for i = t and t + 512 (a wave reads 512 contiguous bytes of one key per load)
   uint2 st[2][4];
-  auto gload = [&](int tb) {
+  // half x of a tile (keys 32 x .. +32): loads into st[x], stores into LDS buffer bf
+  auto gload = [&](int tb, int x) {
+    const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        st[x][j] = *reinterpret_cast<const uint2*>(Kb + (size_t)slot_of(min(tb + 4 * kg + j, k1 - 1), cap) * HD + 4 * dg);
-    }
+    for (int j = 0; j < 4; ++j)
+      st[x][j] = *reinterpret_cast<const uint2*>(Kb + (size_t)slot_of(min(tb + 4 * kg + j, k1 - 1), cap) * HD + 4 * dg);
   };
-  auto lstore = [&](int bf) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
+  auto lstore = [&](int bf, int x) {
+    {
       const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(&kt[bf][4 * kg + j][4 * dg]) = st[x][j];
@@ -95,7 +92,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
     }
   };
   const bool any = k0 < k1;
-  if (any) gload(k0);
+  if (any) {
+    gload(k0, 0);
+    gload(k0, 1);
+  }
 
   // q_norm + rotation of the lane's query: the lane holds dims 32 s + 8 kq + e (s < 8, e < 8); the rotation partner
   // of dim d < 128 is d + 128, the same lane's step s + 4; the norm's sum spans the four lanes of the query (kq)
@@ -165,75 +165,108 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
   f32x4 acc[TILES];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (any) lstore(0);
+  if (any) {
+    lstore(0, 0);
+    lstore(0, 1);
+  }
   __syncthreads();
   int buf = 0;
   for (int tb = k0; tb < k1; tb += KT) {  // block-uniform
     const bool more = tb + KT < k1;
-    if (more) gload(tb + KT);
+    // the next tile, in halves, into the other buffer (free since the last barrier): each half's loads are in
+    // flight during one 32-key batch, and only one half's registers are live at a time
+    if (more) gload(tb + KT, 0);
 #pragma unroll
-    for (int j = 0; j < KT / 16; ++j) {
-      const int kb = tb + 16 * j;
-      if (kb >= k1) break;  // block-uniform
-      uint4 ka[KSTEPS];
+    for (int j = 0; j < KT / 32; ++j) {  // 32-key batches: two score tiles, one softmax update
+      const int kb = tb + 32 * j;
+      if (kb < k1) {  // block-uniform
+      f32x4 sacc[2];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) ka[s] = *reinterpret_cast<const uint4*>(&kt[buf][16 * j + hq][32 * s + 8 * kq]);
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h2 = 0; h2 < 2; ++h2) {
+        // K operands read one step ahead of the products (few registers live: the wave is at its register limit)
+        const uint16_t* krow = &kt[buf][32 * j + 16 * h2 + hq][8 * kq];
+        uint4 kcur = *reinterpret_cast<const uint4*>(krow);
+        sacc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, ka[s]);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qhi[s]), sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qlo[s]), sacc, 0, 0, 0);
+        for (int s = 0; s < KSTEPS; ++s) {
+          const uint4 knext = *reinterpret_cast<const uint4*>(krow + 32 * min(s + 1, KSTEPS - 1));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, kcur);
+          sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qhi[s]), sacc[h2], 0, 0, 0);
+          sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qlo[s]), sacc[h2], 0, 0, 0);
+          kcur = knext;
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      // scores S[query hq][key kb + 4 kq + r], masked to the query row's window
-      float sv[4];
+      // scores S[query hq][key kb + 16 h2 + 4 kq + r], masked to the query row's window
+      float sv[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = kb + 4 * kq + r;
-        sv[r] = (t < k1 && t >= wst && t < wen) ? sacc[r] * scale_log2 : -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = kb + 16 * h2 + 4 * kq + r;
+          sv[4 * h2 + r] = (t < k1 && t >= wst && t < wen) ? sacc[h2][r] * scale_log2 : -INFINITY;
+        }
+      float mt = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
       mt = fmaxf(mt, xr_partner<16>(mt));
       mt = fmaxf(mt, xr_partner<32>(mt));
       const float mn = fmaxf(mrun, mt);
       const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
-      float pv[4], ps = 0.f;
+      float pv[8], ps = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
-        ps += pv[r];
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = (sv[i] == -INFINITY) ? 0.f : exp2f(sv[i] - mn);
+        ps += pv[i];
       }
       ps += xr_partner<16>(ps);
       ps += xr_partner<32>(ps);
       lrun = lrun * alpha + ps;
       mrun = mn;
-      i16x4 phi, plo;
+      // P as the A operand of v_mfma_f32_16x16x32_bf16 over the 32 keys: lane l supplies k = 8 kq + i, which stands
+      // for key 4 kq + i (i < 4) and key 16 + 4 kq + (i - 4); the V operand below follows the same order
+      uint16_t ph[8], pl[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint16_t hb = f2bf(pv[r]);
-        phi[r] = (short)hb;
-        plo[r] = (short)f2bf(pv[r] - bf2f(hb));
+      for (int i = 0; i < 8; ++i) {
+        ph[i] = f2bf(pv[i]);
+        pl[i] = f2bf(pv[i] - bf2f(ph[i]));
       }
-      // output rows are queries 4 kq + r; their alphas live in lanes 4 kq + r
-      float al[4];
+      const uint4 phi = make_uint4(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16),
+                                   ph[4] | ((uint32_t)ph[5] << 16), ph[6] | ((uint32_t)ph[7] << 16));
+      const uint4 plo = make_uint4(pl[0] | ((uint32_t)pl[1] << 16), pl[2] | ((uint32_t)pl[3] << 16),
+                                   pl[4] | ((uint32_t)pl[5] << 16), pl[6] | ((uint32_t)pl[7] << 16));
+      // rescale only when some query's maximum moved (alpha is exactly 1 otherwise); output rows are queries
+      // 4 kq + r, whose alphas live in lanes 4 kq + r
+      if (__any(alpha != 1.0f)) {
+        float al[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a0 = readlane_f(alpha, r), a1 = readlane_f(alpha, 4 + r);
-        const float a2 = readlane_f(alpha, 8 + r), a3 = readlane_f(alpha, 12 + r);
-        al[r] = kq == 0 ? a0 : (kq == 1 ? a1 : (kq == 2 ? a2 : a3));
+        for (int r = 0; r < 4; ++r) {
+          const float a0 = readlane_f(alpha, r), a1 = readlane_f(alpha, 4 + r);
+          const float a2 = readlane_f(alpha, 8 + r), a3 = readlane_f(alpha, 12 + r);
+          al[r] = kq == 0 ? a0 : (kq == 1 ? a1 : (kq == 2 ? a2 : a3));
+        }
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][r] *= al[r];
       }
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
-        const i16x4 vb = __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2*>(&vt[buf][16 * t + hq][16 * j + 4 * kq]));
+        const uint2 v0 = *reinterpret_cast<const uint2*>(&vt[buf][16 * t + hq][32 * j + 4 * kq]);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(&vt[buf][16 * t + hq][32 * j + 16 + 4 * kq]);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
         f32x4 a = acc[t];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] *= al[r];
-        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi), vb, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo), vb, a, 0, 0, 0);
         acc[t] = a;
+        if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // V operands of at most four tiles in flight
+      }
+      }
+      if (more) {
+        lstore(buf ^ 1, j);
+        if (j == 0) gload(tb + KT, 1);
       }
     }
-    if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
