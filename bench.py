@@ -40,6 +40,7 @@ KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k
                "k_head_dense": "k_head.hip", "k_final": "k_head.hip", "k_fill": "k_head.hip",
                "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip",
                "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip", "k_gemm": "k_gemm.hip",
+               "k_group": "k_head.hip", "k_head_grouped": "k_head.hip", "k_topk_rows": "k_head.hip",
                "k_rownorm": "k_gemm.hip", "k_merge": "k_gemm.hip", "k_token": "k_gemm.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 512 << 20
@@ -53,7 +54,8 @@ SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma"
                # the large-batch path
                "token": "k_token", "rownorm": "k_rownorm", "post_norm": "k_rownorm", "attn_merge": "k_merge",
                "pre_gemm": "k_gemm", "qproj_gemm": "k_gemm", "o_proj_gemm": "k_gemm", "ffn_gemm": "k_gemm",
-               "down_gemm": "k_gemm", "post_gemm": "k_gemm", "scores_gemm": "k_gemm"}
+               "down_gemm": "k_gemm", "post_gemm": "k_gemm", "scores_gemm": "k_gemm",
+               "head_select": "k_topk_rows", "head_group": "k_group", "head_grouped": "k_head_grouped"}
 
 
 def site_kernel(site, shape, shared=False):
@@ -139,6 +141,13 @@ def site_bytes(site, shape, batch, lens, distinct_clusters, shared=False):
     if site == "head":
         n = shape.top_k * shape.vsc
         return distinct_clusters * shape.vsc * H * 2 + 4 * n * B + act(shape.n_centroids) + act(H) + 4 * n * B
+    if site == "head_select":  # centroid scores in, selections out
+        return act(shape.n_centroids) + 4 * shape.top_k * B
+    if site == "head_group":
+        return 4 * shape.top_k * B * 2 + 8 * shape.n_centroids
+    if site == "head_grouped":  # each selected cluster once (at most the whole table), ids, scatter
+        n = shape.top_k * shape.vsc
+        return min(distinct_clusters, shape.n_centroids) * shape.vsc * H * 2 + act(H) + 3 * 4 * n * B
     if site == "head_dense":  # the whole table once, h in, the full logits rows out
         return shape.vocab * H * 2 + act(H) + 4 * shape.vocab * B + 8 * B
     if site == "final":

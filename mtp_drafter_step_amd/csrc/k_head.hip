@@ -152,6 +152,7 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
   }
   const int c = sh_c;
   if (tid == 0 && sel) sel[(size_t)b * k + j] = c;
+  if (!Es) return;  // selection only: the cluster-grouped head scores the candidates
 
   // the cluster's candidate ids and their logits: group grp scores ids t = grp + 16 i, 8 ids per pass
   const int grp = tid >> 4, l16 = tid & 15;
@@ -396,6 +397,260 @@ __global__ __launch_bounds__(1024) void k_head_dense(int B, int V, const uint16_
 __global__ void k_zero_u64(uint64_t* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0ull;
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Cluster-grouped scoring for many rows ([Inventory] "Centroid / ordered embeddings LM head", steps 3-5, the same
+// outputs as k_head): when the batch's rows select many clusters in common, each selected cluster's rows are read
+// once and scored for every (row, slot) that selected it.
+//
+// k_topk_rows (one block of 256 threads per row): the row's top k centroids in slot order (descending score, ties
+// to the lower index); sel[b][j] = slot j's centroid. A radix select on the order keys, 8 bits at a time from the
+// top, finds the bin that holds the k-th element. Elements in higher bins (fewer than k) take the first slots by
+// their rank among themselves; the bin's members, all tied at the resolved bits (or the bin's only member when the
+// search stopped early), take the remaining slots in ascending index order.
+template <int NPT>
+__global__ __launch_bounds__(256) void k_topk_rows(int C, int k, const float* scores, int32_t* sel) {
+  __shared__ uint32_t hist[2][4][256];
+  __shared__ uint32_t sh_digit, sh_before, sh_n, sh_above;
+  __shared__ uint64_t above[kMaxTopK];
+  __shared__ uint32_t bcount[NPT][4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  uint32_t ok[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) ok[i] = f32_order(scores[(size_t)b * C + min(tid + 256 * i, C - 1)]);
+  uint32_t prefix = 0, pmask = 0, need = (uint32_t)k, inbin = 0;
+  hist[0][0][tid] = hist[0][1][tid] = hist[0][2][tid] = hist[0][3][tid] = 0u;
+  if (tid == 0) sh_above = 0u;
+  __syncthreads();
+  int buf = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (tid + 256 * i < C && (ok[i] & pmask) == prefix) atomicAdd(&hist[buf][wave][(ok[i] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t cnt[4], sum = 0;  // lane l owns digits 255-4l .. 252-4l (descending)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dg = 255 - 4 * lane - q;
+        cnt[q] = hist[buf][0][dg] + hist[buf][1][dg] + hist[buf][2][dg] + hist[buf][3][dg];
+        sum += cnt[q];
+      }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int of = 1; of < 64; of <<= 1) {
+        const uint32_t t = __shfl_up(incl, of, 64);
+        if (lane >= of) incl += t;
+      }
+      uint32_t before = incl - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (before < need && before + cnt[q] >= need) {
+          sh_digit = 255u - 4u * lane - q;
+          sh_before = before;
+          sh_n = cnt[q];
+        }
+        before += cnt[q];
+      }
+    } else {
+      for (int i = (wave - 1) * 64 + lane; i < 4 * 256; i += 3 * 64) (&hist[buf ^ 1][0][0])[i] = 0u;
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    pmask |= 255u << shift;
+    need -= sh_before;
+    inbin = sh_n;
+    buf ^= 1;
+    if (inbin == 1u) break;
+  }
+  const uint32_t nabove = (uint32_t)k - need;  // elements in higher bins: fewer than k <= 64
+  // bin members: their rank in index order (index tid + 256 i runs i-major, then wave, then lane)
+  uint64_t inb[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const bool mem = tid + 256 * i < C && (ok[i] & pmask) == prefix;
+    inb[i] = __ballot(mem);
+    if (lane == 0) bcount[i][wave] = (uint32_t)__popcll(inb[i]);
+    if (tid + 256 * i < C && (ok[i] & pmask) > prefix) {
+      const uint32_t pos = atomicAdd(&sh_above, 1u);
+      above[pos] = ((uint64_t)ok[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(tid + 256 * i));
+    }
+  }
+  __syncthreads();
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    uint32_t r = base;
+    for (int w = 0; w < wave; ++w) r += bcount[i][w];
+    r += (uint32_t)__popcll(inb[i] & ((1ull << lane) - 1ull));
+    if (((inb[i] >> lane) & 1ull) && r < need) sel[(size_t)b * k + nabove + r] = tid + 256 * i;
+    base += bcount[i][0] + bcount[i][1] + bcount[i][2] + bcount[i][3];
+  }
+  if (wave == 0) {
+    // lane e holds element e of the higher bins; its slot is the number of larger ones (distinct composites)
+    const uint64_t v = (uint32_t)lane < nabove ? above[lane] : 0ull;
+    const int vhi = (int)(v >> 32), vlo = (int)(uint32_t)v;
+    uint32_t rank = 0;
+#pragma unroll
+    for (int f = 0; f < 64; ++f) {
+      const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(vhi, f) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane(vlo, f);
+      rank += (o > v) ? 1u : 0u;
+    }
+    if ((uint32_t)lane < nabove) sel[(size_t)b * k + rank] = key_id(v);
+  }
+}
+
+// k_group (one block of 1024 threads): the n = B k selections sel[] grouped by cluster with a counting sort in LDS:
+// a cluster's count and a "selected" flag packed in one word go through one prefix scan, giving each cluster its
+// first entry and each selected cluster its place in the compacted list. Outputs: nuniq, clist[nuniq] (clusters),
+// cstart[nuniq + 1], entries[n] (flat (row, slot) indices grouped by cluster; the order inside a group does not
+// matter, every entry's outputs are its own).
+__global__ __launch_bounds__(1024) void k_group(int n, int C, const int32_t* sel, int32_t* nuniq, int32_t* clist,
+                                                int32_t* cstart, int32_t* entries) {
+  constexpr int EPT = kMaxBatch * kMaxTopK / 1024;  // entries per thread at most
+  constexpr int CPT = kMaxCentroids / 1024;         // clusters per thread
+  __shared__ uint32_t cnt[kMaxCentroids];
+  __shared__ uint32_t wtot[16];
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  for (int c = tid; c < kMaxCentroids; c += 1024) cnt[c] = 0u;
+  __syncthreads();
+  int cv[EPT];
+  uint32_t pos[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + 1024 * i;
+    cv[i] = e < n ? sel[e] : -1;
+    pos[i] = cv[i] >= 0 ? atomicAdd(&cnt[cv[i]], 1u) : 0u;
+  }
+  __syncthreads();
+  // packed (flag << 16 | count) per cluster, thread-local prefix over CPT consecutive clusters
+  uint32_t loc[CPT], run = 0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid * CPT + i;
+    const uint32_t v = c < C ? cnt[c] : 0u;
+    loc[i] = run;
+    run += (v ? 0x10000u : 0u) | v;
+  }
+  uint32_t incl = run;
+#pragma unroll
+  for (int of = 1; of < 64; of <<= 1) {
+    const uint32_t t = __shfl_up(incl, of, 64);
+    if (lane >= of) incl += t;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  base += incl - run;
+  if (tid == 1023) {
+    const uint32_t tot = base + run;
+    *nuniq = (int32_t)(tot >> 16);
+    cstart[tot >> 16] = (int32_t)(tot & 0xFFFFu);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid * CPT + i;
+    const uint32_t pre = base + loc[i];
+    if (c < C && cnt[c]) {
+      clist[pre >> 16] = c;
+      cstart[pre >> 16] = (int32_t)(pre & 0xFFFFu);
+    }
+    cnt[c] = pre & 0xFFFFu;  // first entry of cluster c (reused as the offset table)
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < EPT; ++i)
+    if (cv[i] >= 0) entries[cnt[cv[i]] + pos[i]] = tid + 1024 * i;
+}
+
+// One block per selected cluster (grid = the most clusters there can be; blocks past nuniq exit): the cluster's
+// rows and ids are loaded once per pass of 8 ids per 16-thread group and scored against the h of every entry;
+// writes each entry's ids, sparse logits, scatter and slot key as k_head does. 256 threads, H = 128 HCH.
+template <int HCH>
+__global__ __launch_bounds__(256) void k_head_grouped(int k, int vsc, const int32_t* ordering, const uint16_t* Es,
+                                                      const float* h, const int32_t* nuniq, const int32_t* clist,
+                                                      const int32_t* cstart, const int32_t* entries,
+                                                      int32_t* __restrict__ ids, float* __restrict__ z,
+                                                      float* __restrict__ logits, size_t V,
+                                                      uint64_t* __restrict__ keys) {
+  constexpr int H = HCH * 128;
+  __shared__ unsigned long long best[kMaxBatch];  // per entry of this cluster (a row selects a cluster once)
+  __shared__ __attribute__((aligned(16))) float hs8[8][H];  // h rows of 8 entries
+  const int u = blockIdx.x;
+  if (u >= *nuniq) return;  // block-uniform
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int c = clist[u], e0 = cstart[u], ne = cstart[u + 1] - e0;
+  for (int i = tid; i < ne; i += 256) best[i] = 0ull;
+  const int grp = tid >> 4, l16 = tid & 15;
+  const int nper = vsc >> 4;  // ids per group (vsc % 16 == 0)
+  const int32_t* ord = ordering + (size_t)c * vsc;
+  const uint16_t* crow = Es + (size_t)c * vsc * H;
+  __syncthreads();
+  for (int i0 = 0; i0 < nper; i0 += 8) {
+    int idv[8];
+    uint4 raw[8][HCH];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int t = min(grp + 16 * (i0 + q), vsc - 1);
+      idv[q] = ord[t];
+#pragma unroll
+      for (int ch = 0; ch < HCH; ++ch)
+        raw[q][ch] = *reinterpret_cast<const uint4*>(crow + (size_t)t * H + ch * 128 + l16 * 8);
+    }
+    const int q = l16 >> 1;
+    int idq = idv[0];
+#pragma unroll
+    for (int w2 = 1; w2 < 8; ++w2) idq = (q == w2) ? idv[w2] : idq;
+    const bool mine = (l16 & 1) == 0 && i0 + q < nper;
+    const int t = grp + 16 * (i0 + q);
+    for (int e8 = 0; e8 < ne; e8 += 8) {  // block-uniform: 8 entries' h rows staged in LDS, then scored
+      __syncthreads();  // the previous chunk's h reads are done
+      for (int i = tid; i < 8 * H / 4; i += 256) {
+        const int ee = e8 + i / (H / 4);
+        const int b = entries[e0 + min(ee, ne - 1)] / k;
+        reinterpret_cast<float4*>(&hs8[0][0])[i] = *reinterpret_cast<const float4*>(h + (size_t)b * H + (i % (H / 4)) * 4);
+      }
+      __syncthreads();
+      const int nchunk = min(8, ne - e8);
+      for (int e = 0; e < nchunk; ++e) {  // block-uniform
+        const int flat = entries[e0 + e8 + e];
+        const int b = flat / k;
+        float acc[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) acc[w] = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < HCH; ++ch) {
+          const float4 h0 = *reinterpret_cast<const float4*>(&hs8[e][ch * 128 + l16 * 8]);
+          const float4 h1 = *reinterpret_cast<const float4*>(&hs8[e][ch * 128 + l16 * 8 + 4]);
+          const float hf[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            float ef[8];
+            unpack8(raw[w][ch], ef);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[w] = fmaf(ef[d], hf[d], acc[w]);
+          }
+        }
+        XR<8, 8>::run(acc, l16);  // lane l16 of the group holds id (l16 >> 1) of the 8
+        uint64_t kv = 0ull;
+        if (mine) {
+          const size_t slot = (size_t)flat * vsc + t;
+          if (ids) ids[slot] = idq;
+          if (z) z[slot] = acc[0];
+          if (logits) logits[(size_t)b * V + idq] = acc[0];
+          kv = vid_key(acc[0], (uint32_t)idq);
+        }
+        kv = wave_max_u64(kv);
+        if (lane == 0) atomicMax(&best[e8 + e], (unsigned long long)kv);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < ne; e += 256) keys[entries[e0 + e]] = best[e];
 }
 
 // Head table in cluster order: out[r] = E[ordering[r]], rows of H bf16 (H % 8 == 0); grid ceil(V / 8), 256 threads,
@@ -653,6 +908,39 @@ hipError_t launch_head_dense(hipStream_t s, int B, int V, int H, const uint16_t*
 
 hipError_t launch_zero_keys(hipStream_t s, uint64_t* keys, int n) {
   return go(k_zero_u64, (n + 255) / 256, 256, 0, s, keys, n);
+}
+
+hipError_t launch_topk_rows(hipStream_t s, int B, int C, int k, const float* scores, int32_t* sel) {
+  if (k < 1 || k > kMaxTopK || k > C || C > kMaxCentroids) return hipErrorInvalidValue;
+  const int npt = (C + 255) / 256;
+  if (npt <= 2) return go(k_topk_rows<2>, B, 256, 0, s, C, k, scores, sel);
+  if (npt <= 4) return go(k_topk_rows<4>, B, 256, 0, s, C, k, scores, sel);
+  if (npt <= 8) return go(k_topk_rows<8>, B, 256, 0, s, C, k, scores, sel);
+  return go(k_topk_rows<16>, B, 256, 0, s, C, k, scores, sel);
+}
+
+hipError_t launch_group(hipStream_t s, int B, int C, int k, const int32_t* sel, int32_t* work) {
+  const int n = B * k;
+  if (n > kMaxBatch * kMaxTopK || C > kMaxCentroids) return hipErrorInvalidValue;
+  return go(k_group, 1, 1024, 0, s, n, C, sel, work, work + 1, work + 1 + C, work + 2 + 2 * C);
+}
+
+hipError_t launch_head_grouped(hipStream_t s, int B, int C, int k, int vsc, int H, const int32_t* ordering,
+                               const uint16_t* Es, const float* h, const int32_t* work, int32_t* ids, float* z,
+                               float* logits, size_t V, uint64_t* keys) {
+  const int n = B * k;
+  if (n > kMaxBatch * kMaxTopK || C > kMaxCentroids) return hipErrorInvalidValue;
+  const int32_t* nuniq = work;
+  const int32_t* clist = work + 1;
+  const int32_t* cstart = clist + C;
+  const int32_t* entries = cstart + C + 1;
+  const int grid = C < n ? C : n;
+#define MTPD_HG(HCH_) \
+  if (H == HCH_ * 128) \
+    return go(k_head_grouped<HCH_>, grid, 256, 0, s, k, vsc, ordering, Es, h, nuniq, clist, cstart, entries, ids, z, logits, V, keys);
+  MTPD_HG(2) MTPD_HG(4) MTPD_HG(6) MTPD_HG(8)
+#undef MTPD_HG
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gather_rows(hipStream_t s, const uint16_t* E, const int32_t* ordering, uint16_t* out, int V,

@@ -122,13 +122,24 @@ hipError_t launch_sample(hipStream_t s, int phase, int B, int n, int vsc, int k,
                          float* tsum, const float* u, int32_t* tok_out, float* prob_out, int out_stride,
                          int32_t* tok_next);
 
-// Masked head: per (row, selected slot j): top-k of the row's centroid scores (descending, ties to the lower
+// Masked head: per (row, selected slot j): top-k of the row's centroid scores (only the selection, into sel, when
+// Es is null) (descending, ties to the lower
 // index), the cluster's token ids through the ordering, sparse logits token_embd[id] . h (rows read from Es, the
 // head table in cluster order), optional scatter into logits, and the slot's best (value, id) key (larger value,
 // then lower id).
 hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const float* scores,
                        const int32_t* ordering, const uint16_t* Es, const float* h, int32_t* sel, int32_t* ids,
                        float* z, float* logits, size_t V, uint64_t* keys);
+
+// The masked head's scoring grouped by cluster (for batches whose rows select many clusters in common): launch_group
+// groups the selections sel [B][k] (launch_head with Es == nullptr writes them) by cluster into work (int32, 2 + 2 C
+// + B k), then launch_head_grouped scores them, with the same outputs as launch_head.
+hipError_t launch_group(hipStream_t s, int B, int C, int k, const int32_t* sel, int32_t* work);
+// sel [B][k] = each row's top k of scores [B][C] in slot order (descending score, ties to the lower index).
+hipError_t launch_topk_rows(hipStream_t s, int B, int C, int k, const float* scores, int32_t* sel);
+hipError_t launch_head_grouped(hipStream_t s, int B, int C, int k, int vsc, int H, const int32_t* ordering,
+                               const uint16_t* Es, const float* h, const int32_t* work, int32_t* ids, float* z,
+                               float* logits, size_t V, uint64_t* keys);
 
 // out[r] = E[ordering[r]] for r < V (rows of H bf16): the head table in cluster order.
 hipError_t launch_gather_rows(hipStream_t s, const uint16_t* E, const int32_t* ordering, uint16_t* out, int V, int H);

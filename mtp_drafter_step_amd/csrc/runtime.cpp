@@ -93,7 +93,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 // Offsets of every intermediate in the caller's workspace for a given batch.
 struct Plan {
   size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, stok, tsum, row, u, xp, dp, rtok,
-      total;
+      grp, total;
 };
 
 // Argmax keys per row: one per selected cluster for the masked head, one for the dense head.
@@ -133,6 +133,7 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.xp = take((size_t)(2 * Bb / 256) * B * H * 4);
   p.dp = take((size_t)(F / 256) * B * H * 4);
   p.rtok = take((size_t)B * 4);
+  p.grp = take((size_t)(2 + 2 * c.n_centroids + B * std::max(c.top_k, 1)) * 4);  // cluster grouping of the head
   p.total = off;
   return p;
 }
@@ -277,6 +278,16 @@ int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
     return MTPD_OK;
   }
   // [Inventory] "Centroid / ordered embeddings LM head", steps 2-5
+  if (B * c.top_k >= c.n_centroids) {  // many rows: the selected clusters read once, scored for every row
+    int32_t* selw = sel_out ? sel_out : at<int32_t>(ws, p.sel);
+    KLAUNCH(h, "head_select", mtpd::launch_topk_rows(s, B, c.n_centroids, c.top_k, at<float>(ws, p.scores), selw));
+    KLAUNCH(h, "head_group", mtpd::launch_group(s, B, c.n_centroids, c.top_k, selw, at<int32_t>(ws, p.grp)));
+    KLAUNCH(h, "head_grouped", mtpd::launch_head_grouped(s, B, c.n_centroids, c.top_k, h->vsc, c.hidden,
+                                                         h->w.token_ordering, h->head_sorted, hsrc,
+                                                         at<int32_t>(ws, p.grp), ids_out, z_out, logits,
+                                                         (size_t)c.vocab, at<uint64_t>(ws, p.keys)));
+    return MTPD_OK;
+  }
   KLAUNCH(h, "head", mtpd::launch_head(s, B, c.n_centroids, c.top_k, h->vsc, c.hidden, at<float>(ws, p.scores),
                            h->w.token_ordering, h->head_sorted, hsrc, sel_out, ids_out, z_out, logits,
                            (size_t)c.vocab, at<uint64_t>(ws, p.keys)));

@@ -60,15 +60,18 @@ def test_masked_head_parity(m, scale):
     assert tally.sel_checked >= m // 2
 
 
-@pytest.mark.parametrize("ntie", [40, 100])
-def test_masked_head_exact_ties(ntie):
-    """Centroid rows 0 .. ntie-1 are copies of row ntie and h points along that row, so those ntie scores tie
+@pytest.mark.parametrize("batch", [1, 64])
+@pytest.mark.parametrize("ntie", [20, 40, 100])
+def test_masked_head_exact_ties(ntie, batch):
+    """Centroid rows 0 .. ntie-1 are copies of row ntie and h points along that row, so those ntie + 1 scores tie
     exactly (identical terms in the same order) and lie far above every other score. Ties go to the lower index, so
-    the slots must be centroids 0 .. top_k-1 in order: 40 tied members are ordered by the small in-wave sort, 100
-    by the rank-by-index path."""
+    the first slots must be centroids 0, 1, 2, ... in order. With 20 ties the rest of the slots come from the
+    untied scores; 40 tied members are ordered by the small in-wave sort of the one-row-per-block head, 100 by its
+    rank-by-index path. At batch 64 every row is the same and the head takes its per-row selection and per-cluster
+    scoring, each cluster then serving all 64 rows."""
     from mtp_drafter_step_amd import Drafter
-    say(f"masked_head ties={ntie}")
-    case = Case(synth.E4B, batch=1, context=16, max_batch=4)
+    say(f"masked_head ties={ntie} batch={batch}")
+    case = Case(synth.E4B, batch=1, context=16, max_batch=batch)
     w = dict(case.w)
     cen = case.w["centroids"].clone()
     cen[:ntie] = cen[ntie]
@@ -76,19 +79,26 @@ def test_masked_head_exact_ties(ntie):
     model = O.Model(O.config_from(case.shape), w)
     wg = dict(case.wg)
     wg["centroids"] = cen.cuda()
-    d = Drafter(case.shape, wg, max_batch=4)
+    d = Drafter(case.shape, wg, max_batch=batch)
     u = O.bf16_to_f64(cen[ntie].numpy().view(np.uint16))
-    h = torch.from_numpy((50.0 * u).astype(np.float32)).reshape(1, -1)
+    h = torch.from_numpy((50.0 * u).astype(np.float32)).reshape(1, -1).repeat(batch, 1).contiguous()
     out = d.masked_head(h.cuda(), want_logits=True, want_sparse=True)
     torch.cuda.synchronize()
     k = case.shape.top_k
-    assert out["sel"][0].cpu().tolist() == list(range(k))
     ref = O.masked_head_row(model, h[0].numpy().astype(np.float64))
-    assert list(ref["sel"]) == list(range(k))
-    assert out["ids"][0].cpu().tolist() == list(np.asarray(ref["ids"]))
-    assert rel_ok(out["z"][0].cpu().numpy(), ref["z"])
-    row = out["logits"][0].cpu().numpy()
-    assert int(out["argmax"][0]) == int(np.argmax(row))
+    lead = min(ntie + 1, k)
+    assert list(ref["sel"])[:lead] == list(range(lead))
+    tally = Tally()
+    refl = {key: [ref[key]] for key in ("sel", "ids", "z", "cgap", "margin", "next")}
+    for r in range(batch):
+        sel = out["sel"][r].cpu().numpy()
+        assert sel[:lead].tolist() == list(range(lead)), f"row {r}"
+        if lead == k:  # every slot tied: the order is fixed by index alone
+            assert sel.tolist() == list(ref["sel"]), f"row {r}"
+            assert out["ids"][r].cpu().tolist() == list(np.asarray(ref["ids"])), f"row {r}"
+            assert rel_ok(out["z"][r].cpu().numpy(), ref["z"])
+        compare_head_row(tally, case.model.cfg, refl, 0, sel, out["ids"][r].cpu().numpy(), out["z"][r].cpu().numpy(),
+                         int(out["argmax"][r]), out["logits"][r].cpu().numpy(), where=f"ties row {r}")
 
 
 STEP_CASES = {
