@@ -231,6 +231,101 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
 //     V comes from the wave's LDS copy of the key tile read column-wise (4 keys of one dim per lane).
 
 
+// One batch of 16 keys for one wave of k_attn_mfma: scores of the keys in ka against the G heads, online softmax
+// update, and P V into acc. PF: the next batch's key loads (into kn) are issued first, to arrive during this batch's
+// arithmetic, and become ka at the end; the last batch of a wave issues none, since copying them into ka would wait
+// for loads nobody uses. The two forms are separate instances, so that the loads of the first are unconditional
+// (loads under a run-time branch make every later wait count assume the branch was not taken).
+template <int G, bool PF>
+__device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, const uint16_t* Vb, int cap,
+                                           bool same_v, float scale_log2, uint16_t* tile,
+                                           const uint16_t (*qop)[2][G][4][8], uint4 (&ka)[8], uint4 (&kn)[8],
+                                           f32x4 (&acc)[16], float& mrun, float& lrun) {
+  constexpr int HD = 256, KSTEPS = 8, TILES = 16, LROW = HD + 8, S = 64;
+  constexpr int GQ = (G + 3) / 4;
+  const int lane = lane_id(), hq = lane & 15, kq = lane >> 4;
+  const int hsel = hq < G ? hq : 0;
+  const int tb = t0;
+  if constexpr (PF) {
+    const uint16_t* r = Kb + (size_t)slot_of(min(t0 + S + hq, k1 - 1), cap) * HD;
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) kn[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
+  }
+  const int nk = min(16, k1 - tb);
+  // V tile into this wave's LDS (row = key hq, dims 32c + 8kq .. +8)
+  if (same_v) {
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = ka[c];
+  } else {
+    const uint16_t* r = Vb + (size_t)slot_of(min(tb + hq, k1 - 1), cap) * HD;
+    uint4 vv[KSTEPS];
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) vv[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = vv[c];
+  }
+  // scores S[key 4kq + r][head hq]
+  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < KSTEPS; ++c) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ka[c]);
+    uint4 hi = *reinterpret_cast<const uint4*>(&qop[c][0][hsel][kq][0]);
+    uint4 lo = *reinterpret_cast<const uint4*>(&qop[c][1][hsel][kq][0]);
+    if (hq >= G) hi = lo = make_uint4(0u, 0u, 0u, 0u);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), sacc, 0, 0, 0);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), sacc, 0, 0, 0);
+  }
+  float sv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sv[r] = (4 * kq + r < nk && hq < G) ? sacc[r] * scale_log2 : -INFINITY;
+  float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mt = fmaxf(mt, xr_partner<16>(mt));
+  mt = fmaxf(mt, xr_partner<32>(mt));
+  const float mn = fmaxf(mrun, mt);
+  const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
+  float pv[4], ps = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
+    ps += pv[r];
+  }
+  ps += xr_partner<16>(ps);
+  ps += xr_partner<32>(ps);
+  lrun = lrun * alpha + ps;
+  mrun = mn;
+  i16x4 phi, plo;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint16_t hb = f2bf(pv[r]);
+    phi[r] = (short)hb;
+    plo[r] = (short)f2bf(pv[r] - bf2f(hb));
+  }
+  // rescale the accumulators: D rows are heads 4kq + r, whose alpha lives in lane 4kq + r (rows of heads >= G
+  // are padding)
+  float al[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    al[r] = readlane_f(alpha, r);
+    if constexpr (GQ > 1) al[r] = (kq == 1) ? readlane_f(alpha, 4 + r) : al[r];
+  }
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) {
+    i16x4 vb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vb[r] = (short)tile[(4 * kq + r) * LROW + 16 * t + hq];
+    f32x4 a = acc[t];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] *= al[r];
+    a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
+    a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);
+    acc[t] = a;
+  }
+  if constexpr (PF) {
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) ka[c] = kn[c];
+  }
+}
+
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv, const float* __restrict__ q,
                                                           const uint16_t* __restrict__ qnorm, float eps,
@@ -329,85 +424,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* tile = &vt[wave][0][0];
-  const int hsel = hq < G ? hq : 0;
+  static_assert(S == 64, "mfma_batch takes 16 keys per wave and 4 waves");
 
-  for (; t0 < k1; t0 += S) {
-    const int tb = t0;
-    {
-      const uint16_t* r = Kb + (size_t)slot_of(min(t0 + S + hq, k1 - 1), cap) * HD;
-#pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) kn[c] = *reinterpret_cast<const uint4*>(r + 32 * c);
-    }
-    const int nk = min(16, k1 - tb);
-    // V tile into this wave's LDS (row = key hq, dims 32c + 8kq .. +8)
-    if (same_v) {
-#pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = ka[c];
-    } else {
-      const uint16_t* r = Vb + (size_t)slot_of(min(tb + hq, k1 - 1), cap) * HD;
-#pragma unroll
-      for (int c = 0; c < KSTEPS; ++c)
-        *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = *reinterpret_cast<const uint4*>(r + 32 * c);
-    }
-    // scores S[key 4kq + r][head hq]
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, ka[c]);
-      uint4 hi = *reinterpret_cast<const uint4*>(&qop[c][0][hsel][kq][0]);
-      uint4 lo = *reinterpret_cast<const uint4*>(&qop[c][1][hsel][kq][0]);
-      if (hq >= G) hi = lo = make_uint4(0u, 0u, 0u, 0u);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), sacc, 0, 0, 0);
-    }
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (4 * kq + r < nk && hq < G) ? sacc[r] * scale_log2 : -INFINITY;
-    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mt = fmaxf(mt, xr_partner<16>(mt));
-    mt = fmaxf(mt, xr_partner<32>(mt));
-    const float mn = fmaxf(mrun, mt);
-    const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
-    float pv[4], ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
-      ps += pv[r];
-    }
-    ps += xr_partner<16>(ps);
-    ps += xr_partner<32>(ps);
-    lrun = lrun * alpha + ps;
-    mrun = mn;
-    i16x4 phi, plo;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint16_t hb = f2bf(pv[r]);
-      phi[r] = (short)hb;
-      plo[r] = (short)f2bf(pv[r] - bf2f(hb));
-    }
-    // rescale the accumulators: D rows are heads 4kq + r, whose alpha lives in lane 4kq + r (rows of heads >= G
-    // are padding)
-    float al[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      al[r] = readlane_f(alpha, r);
-      if constexpr (GQ > 1) al[r] = (kq == 1) ? readlane_f(alpha, 4 + r) : al[r];
-    }
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      i16x4 vb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vb[r] = (short)tile[(4 * kq + r) * LROW + 16 * t + hq];
-      f32x4 a = acc[t];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] *= al[r];
-      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
-      a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);
-      acc[t] = a;
-    }
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) ka[c] = kn[c];
-  }
+  for (; t0 + S < k1; t0 += S)
+    mfma_batch<G, true>(t0, k1, Kb, Vb, cap, same_v, scale_log2, tile, qop, ka, kn, acc, mrun, lrun);
+  if (t0 < k1) mfma_batch<G, false>(t0, k1, Kb, Vb, cap, same_v, scale_log2, tile, qop, ka, kn, acc, mrun, lrun);
   // combine the waves of this block: head h's softmax state is in lane h; output row group kq (heads 4kq .. +3)
   // sits in lanes 16kq .. +15: dim 16t + hq, heads in the four registers of acc[t], stored as one float4 per dim
   if (lane < G) {
