@@ -437,7 +437,8 @@ def summarize_stats(args):
              f"Command: `{args.cmd}`", "",
              "Kernel source sha256[:16]: " + ", ".join(
                  f"{f} `{source_digest(k)}`" for f, k in (("k_layers.hip", "k_ffn"), ("k_attention.hip", "k_attn_mfma"),
-                                                          ("k_head.hip", "k_head"))), "",
+                                                          ("k_attention_shared.hip", "k_attn_mq"),
+                                                          ("k_head.hip", "k_head"), ("k_gemm.hip", "k_gemm"))), "",
              "Only the library's kernels are listed (the run also holds the input generator's and torch's own "
              "kernels, which are outside the timed calls).", "",
              "| kernel | calls | avg µs | min µs | max µs | total µs | share of library time |", "|---|---|---|---|---|---|---|"]
