@@ -60,6 +60,45 @@ def test_masked_head_parity(m, scale):
     assert tally.sel_checked >= m // 2
 
 
+HEAD_SHAPES = {
+    # 40 clusters of 48 ids, top 7: a cluster count that is no power of two, an odd top_k
+    "c40_v48_k7": dataclasses.replace(synth.E4B, vocab=1920, n_centroids=40, top_k=7),
+    # 16 clusters of 1024 ids (the largest cluster the ABI takes), top 3
+    "c16_v1024_k3": dataclasses.replace(synth.E4B, vocab=16384, n_centroids=16, top_k=3),
+    # 4096 clusters of 16 ids, top 64 (the largest cluster count and top_k)
+    "c4096_v16_k64": dataclasses.replace(synth.E4B, vocab=65536, n_centroids=4096, top_k=64),
+}
+
+
+@pytest.mark.parametrize("m", [3, 64])
+@pytest.mark.parametrize("name", list(HEAD_SHAPES))
+def test_masked_head_shapes(name, m):
+    """The masked head at the edges of its shape limits. At 3 rows the head runs one block per (row, slot); at 64
+    rows (64 top_k at least the cluster count) it runs the per-row top-k, the grouping by cluster and one block per
+    selected cluster."""
+    shape = HEAD_SHAPES[name]
+    say(f"masked_head {name} m={m}")
+    case = Case(shape, batch=1, context=16, max_batch=64)
+    g = torch.Generator().manual_seed(300 + m)
+    h = torch.randn(m, shape.hidden, generator=g, dtype=torch.float32)
+    out = case.drafter.masked_head(h.cuda(), want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    tally = Tally()
+    for r in range(m):
+        ref = O.masked_head_row(case.model, h[r].numpy().astype(np.float64))
+        refl = {k: [ref[k]] for k in ("sel", "ids", "z", "cgap", "margin", "next")}
+        compare_head_row(tally, case.model.cfg, refl, 0, out["sel"][r].cpu().numpy(), out["ids"][r].cpu().numpy(),
+                         out["z"][r].cpu().numpy(), int(out["argmax"][r]), out["logits"][r].cpu().numpy(),
+                         where=f"head {name} m={m}")
+        # the slots are in descending score order
+        sc = np.asarray(ref["scores"]) if ref.get("scores") is not None else None
+        if sc is not None and ref["cgap"] > 1e-3:
+            got = sc[out["sel"][r].cpu().numpy()]
+            assert np.all(np.diff(got) <= 1e-3), f"{name} row {r}: slots out of order"
+    say(tally.summary())
+    assert tally.sel_checked >= m // 2
+
+
 @pytest.mark.parametrize("batch", [1, 64])
 @pytest.mark.parametrize("ntie", [20, 40, 100])
 def test_masked_head_exact_ties(ntie, batch):
