@@ -361,6 +361,20 @@ def run_bench(args):
     # cold regime: before each timed call a 1 GiB read sweep evicts L2 and the memory-side cache (the first drafter
     # step of the block starts cold; the next three run on what it brought in)
     sweep = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    # the measured streaming-read rate of this device: the best of a few row-wise reductions over the resident
+    # 1 GiB tensor (rows of 4096 floats, and 4096 rows), whose output is negligible next to the bytes read
+    read_ms = []
+    for shape in ((-1, 4096), (4096, -1)):
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sweep.view(*shape).sum(dim=1)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            read_ms.append(e0.elapsed_time(e1))
+    read_gbs = sweep.numel() * 4 / (min(read_ms) * 1e-3) / 1e9
+    if roof["bound"] == "hbm":
+        roof["frac_of_measured_read_peak"] = roof["achieved"] / read_gbs
     cold_ms = []
     for _ in range(args.cold_steps):
         sweep.sum()
@@ -402,7 +416,11 @@ def run_bench(args):
                           "achieved_GBs": sbytes / (us_drafter_step * 1e-6) / 1e9,
                           "frac": sbytes / (us_drafter_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
                           "cold_us_per_drafter_step": us_cold,
-                          "cold_achieved_GBs": sbytes / (us_cold * 1e-6) / 1e9 if us_cold else None},
+                          "cold_achieved_GBs": sbytes / (us_cold * 1e-6) / 1e9 if us_cold else None,
+                          "measured_read_peak_GBs": read_gbs,
+                          "frac_of_measured_read_peak": sbytes / (us_drafter_step * 1e-6) / 1e9 / read_gbs},
+        "measured_read_peak": {"GBs": read_gbs, "how": "best of 8 row-wise torch sums over a resident 1 GiB fp32 "
+                                                       "tensor (4096-wide rows and 4096 rows), timed with HIP events"},
         "kernels": kernels_table,
         "sites": {site: {"launches_per_drafter_step": len(v) / (calls * n), "avg_launch_us": float(np.mean(v)) * 1e3}
                   for site, v in sorted(per_site.items(), key=lambda kv_: -sum(kv_[1]))},

@@ -97,6 +97,9 @@ WORKLOADS: Dict[str, Workload] = {
     "e2b_b1_ctx4096_block4": Workload("e2b_b1_ctx4096_block4", E2B, batch=1, context=4096, n_steps=4),
     # E4B-shaped drafter, batch 16 independent sequences, context 8192 each, draft_block 4
     "e4b_b16_ctx8192_block4": Workload("e4b_b16_ctx8192_block4", E4B, batch=16, context=8192, n_steps=4),
+    # the same with two KV heads (two query heads per kv head): twice the cache bytes
+    "e4b_nkv2_b16_ctx8192_block4": Workload("e4b_nkv2_b16_ctx8192_block4", dataclasses.replace(E4B, n_kv_head=2),
+                                            batch=16, context=8192, n_steps=4),
     # 26B-A4B-shaped drafter with the dense head, batch 32, context 32768 each, draft_block 4
     "e26b_b32_ctx32768_block4": Workload("e26b_b32_ctx32768_block4", E26B, batch=32, context=32768, n_steps=4),
     # verify width: 256 query rows of one sequence sharing one cache of 131072 keys (window 1024), one drafter step

@@ -147,6 +147,9 @@ STEP_CASES = {
     "e4b_b16_ctx8192": dict(shape=synth.E4B, batch=16, context=8192),
     # ragged lengths 700 - 37 b: windows partly full, several key tiles and a ragged last tile per row
     "e4b_b6_ragged700": dict(shape=synth.E4B, batch=6, context=700, ragged=True),
+    # E4B with two KV heads, batch 16, K = V: the two-kv-head workload's shapes at a shorter, ragged context
+    "e4b_nkv2_b16_ragged1500": dict(shape=dataclasses.replace(synth.E4B, n_kv_head=2), batch=16, context=1500,
+                                    ragged=True),
     # E4B with two KV heads (the variant table's E4B), distinct V caches
     "e4b_nkv2_distinct_v": dict(shape=dataclasses.replace(synth.E4B, n_kv_head=2), batch=3, context=1000,
                                 distinct_v=True),
