@@ -502,17 +502,20 @@ __global__ __launch_bounds__(256) void k_topk_rows(int C, int k, const float* sc
   }
 }
 
+// entries of one cluster scored by one block of k_head_grouped (four 16-row matrix-core tiles)
+constexpr int kGroupTile = 64;
+
 // k_group (one block of 1024 threads): the n = B k selections sel[] grouped by cluster with a counting sort in LDS:
-// a cluster's count and a "selected" flag packed in one word go through one prefix scan, giving each cluster its
-// first entry and each selected cluster its place in the compacted list. Outputs: nuniq, clist[nuniq] (clusters),
-// cstart[nuniq + 1], entries[n] (flat (row, slot) indices grouped by cluster; the order inside a group does not
-// matter, every entry's outputs are its own).
-__global__ __launch_bounds__(1024) void k_group(int n, int C, const int32_t* sel, int32_t* nuniq, int32_t* clist,
-                                                int32_t* cstart, int32_t* entries) {
+// a cluster's count, a "selected" flag and its number of kGroupTile-entry tiles packed in one 64-bit word go through one
+// prefix scan, giving each cluster its first entry and each selected cluster its place in the compacted list and
+// its first tile. Outputs: trec[T] (per tile: cluster, first entry, entry count; count 0 past the last tile, T = the
+// most tiles there can be), entries[n] (flat (row, slot) indices grouped by cluster; the order inside a group does
+// not matter, every entry's outputs are its own).
+__global__ __launch_bounds__(1024) void k_group(int n, int C, int T, const int32_t* sel, int4* trec, int32_t* entries) {
   constexpr int EPT = kMaxBatch * kMaxTopK / 1024;  // entries per thread at most
   constexpr int CPT = kMaxCentroids / 1024;         // clusters per thread
   __shared__ uint32_t cnt[kMaxCentroids];
-  __shared__ uint32_t wtot[16];
+  __shared__ uint64_t wtot[16];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   for (int c = tid; c < kMaxCentroids; c += 1024) cnt[c] = 0u;
   __syncthreads();
@@ -525,41 +528,41 @@ __global__ __launch_bounds__(1024) void k_group(int n, int C, const int32_t* sel
     pos[i] = cv[i] >= 0 ? atomicAdd(&cnt[cv[i]], 1u) : 0u;
   }
   __syncthreads();
-  // packed (flag << 16 | count) per cluster, thread-local prefix over CPT consecutive clusters
-  uint32_t loc[CPT], run = 0;
+  // packed (tiles << 32 | flag << 16 | count) per cluster (count <= 16384, flags <= 4096, tiles <= 4352), thread-local
+  // prefix over CPT consecutive clusters
+  uint64_t loc[CPT], run = 0;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid * CPT + i;
     const uint32_t v = c < C ? cnt[c] : 0u;
     loc[i] = run;
-    run += (v ? 0x10000u : 0u) | v;
+    run += ((uint64_t)((v + kGroupTile - 1) / kGroupTile) << 32) | (v ? 0x10000u : 0u) | v;
   }
-  uint32_t incl = run;
+  uint64_t incl = run;
 #pragma unroll
   for (int of = 1; of < 64; of <<= 1) {
-    const uint32_t t = __shfl_up(incl, of, 64);
-    if (lane >= of) incl += t;
+    const uint32_t tlo = __shfl_up((uint32_t)incl, of, 64), thi = __shfl_up((uint32_t)(incl >> 32), of, 64);
+    if (lane >= of) incl += ((uint64_t)thi << 32) | tlo;
   }
   if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  uint32_t base = 0;
+  uint64_t base = 0;
   for (int w = 0; w < wave; ++w) base += wtot[w];
   base += incl - run;
-  if (tid == 1023) {
-    const uint32_t tot = base + run;
-    *nuniq = (int32_t)(tot >> 16);
-    cstart[tot >> 16] = (int32_t)(tot & 0xFFFFu);
-  }
+  __shared__ int ntiles;
+  if (tid == 1023) ntiles = (int)((base + run) >> 32);
   __syncthreads();
+  for (int t = ntiles + tid; t < T; t += 1024) trec[t] = make_int4(0, 0, 0, 0);  // no tile
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid * CPT + i;
-    const uint32_t pre = base + loc[i];
+    const uint64_t pre = base + loc[i];
     if (c < C && cnt[c]) {
-      clist[pre >> 16] = c;
-      cstart[pre >> 16] = (int32_t)(pre & 0xFFFFu);
+      const int first = (int)(pre & 0xFFFFu), t0 = (int)(pre >> 32), v = (int)cnt[c];
+      for (int t = 0; t * kGroupTile < v; ++t)
+        trec[t0 + t] = make_int4(c, first + t * kGroupTile, min(kGroupTile, v - t * kGroupTile), 0);
     }
-    cnt[c] = pre & 0xFFFFu;  // first entry of cluster c (reused as the offset table)
+    cnt[c] = (uint32_t)(pre & 0xFFFFu);  // first entry of cluster c (reused as the offset table)
   }
   __syncthreads();
 #pragma unroll
@@ -567,90 +570,121 @@ __global__ __launch_bounds__(1024) void k_group(int n, int C, const int32_t* sel
     if (cv[i] >= 0) entries[cnt[cv[i]] + pos[i]] = tid + 1024 * i;
 }
 
-// One block per selected cluster (grid = the most clusters there can be; blocks past nuniq exit): the cluster's
-// rows and ids are loaded once per pass of 8 ids per 16-thread group and scored against the h of every entry;
-// writes each entry's ids, sparse logits, scatter and slot key as k_head does. 256 threads, H = 128 HCH.
+// One block per (selected cluster, tile of up to kGroupTile of the entries that selected it) (grid = the most tiles
+// there can be; blocks past the last tile exit): the cluster's vsc rows are scored against the h of the tile's
+// entries (row, slot) as a matrix-core product Z[entries][ids] = H[entries][dims] . E_c[ids][dims]^T with
+// v_mfma_f32_16x16x32_bf16, 16 entries at a time. A cluster chosen by many rows is thus spread over a few blocks,
+// so no block carries a long tail, while most clusters are read once.
+//   B operand (ids as columns): the cluster's rows, 16 ids per tile, each wave holding CTW tiles in registers
+//     (lane: id 16 tile + l % 16, dims 32 s + 8 (l / 16) .. +8), loaded straight from the cluster-ordered table;
+//   A operand (entries as rows): 16 entries' h, staged in LDS as bf16 hi + lo (fp32-level products);
+//   D: lane l holds entries 4 (l / 16) + i, id 16 tile + l % 16.
+// The epilogue writes each entry's ids, sparse logits and logits-row scatter as k_head does, and the entry's best
+// (value, id) key: a 16-lane reduction, then a maximum over id tiles and waves in LDS. 256 threads, H = 128 HCH.
 template <int HCH>
 __global__ __launch_bounds__(256) void k_head_grouped(int k, int vsc, const int32_t* ordering, const uint16_t* Es,
-                                                      const float* h, const int32_t* nuniq, const int32_t* clist,
-                                                      const int32_t* cstart, const int32_t* entries,
+                                                      const float* h, const int4* trec, const int32_t* entries,
                                                       int32_t* __restrict__ ids, float* __restrict__ z,
                                                       float* __restrict__ logits, size_t V,
                                                       uint64_t* __restrict__ keys) {
-  constexpr int H = HCH * 128;
-  __shared__ unsigned long long best[kMaxBatch];  // per entry of this cluster (a row selects a cluster once)
-  __shared__ __attribute__((aligned(16))) float hs8[8][H];  // h rows of 8 entries
-  const int u = blockIdx.x;
-  if (u >= *nuniq) return;  // block-uniform
+  constexpr int H = HCH * 128, KSTEPS = H / 32, LROW = H + 8;
+  constexpr int CTW = HCH <= 4 ? 2 : 1;  // id tiles per wave held at once
+  __shared__ unsigned long long best[kGroupTile];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[2][16][LROW];  // [hi / lo][entry][dim]
+  const int4 rec = trec[blockIdx.x];
+  const int c = rec.x, e0 = rec.y, ne = rec.z;
+  if (ne == 0) return;  // block-uniform: no tile
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int c = clist[u], e0 = cstart[u], ne = cstart[u + 1] - e0;
-  for (int i = tid; i < ne; i += 256) best[i] = 0ull;
-  const int grp = tid >> 4, l16 = tid & 15;
-  const int nper = vsc >> 4;  // ids per group (vsc % 16 == 0)
+  const int n = lane & 15, kq = lane >> 4;
+  const int ct = vsc / 16;  // id tiles of the cluster
+  const bool one_group = ct <= 4 * CTW;  // every id tile in registers at once
   const int32_t* ord = ordering + (size_t)c * vsc;
   const uint16_t* crow = Es + (size_t)c * vsc * H;
-  __syncthreads();
-  for (int i0 = 0; i0 < nper; i0 += 8) {
-    int idv[8];
-    uint4 raw[8][HCH];
+  if (tid < kGroupTile) best[tid] = 0ull;
+  uint4 eb[CTW][KSTEPS];
+  int idv[CTW];
+  auto load_rows = [&](int g0) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int t = min(grp + 16 * (i0 + q), vsc - 1);
-      idv[q] = ord[t];
+    for (int j = 0; j < CTW; ++j) {
+      const int t = min((g0 + wave * CTW + j) * 16 + n, vsc - 1);  // the lane's id position (clamped)
 #pragma unroll
-      for (int ch = 0; ch < HCH; ++ch)
-        raw[q][ch] = *reinterpret_cast<const uint4*>(crow + (size_t)t * H + ch * 128 + l16 * 8);
+      for (int s2 = 0; s2 < KSTEPS; ++s2) eb[j][s2] = ld_global16(crow + (size_t)t * H + 32 * s2 + 8 * kq);
+      idv[j] = ord[t];
     }
-    const int q = l16 >> 1;
-    int idq = idv[0];
+  };
+  load_rows(0);  // in flight while the first entries' h is staged
+
+  for (int et = 0; et < ne; et += 16) {  // block-uniform: 16 entries at a time
+    // every load of the tile is issued before any is used (clamped indices, no branches around the loads): the
+    // entries of the thread's staged rows and of its output rows, then the staged rows of h
+    constexpr int NLD = 16 * H / 4 / 256;  // float4 of h per thread
+    int fl[NLD], fo[4];
 #pragma unroll
-    for (int w2 = 1; w2 < 8; ++w2) idq = (q == w2) ? idv[w2] : idq;
-    const bool mine = (l16 & 1) == 0 && i0 + q < nper;
-    const int t = grp + 16 * (i0 + q);
-    for (int e8 = 0; e8 < ne; e8 += 8) {  // block-uniform: 8 entries' h rows staged in LDS, then scored
-      __syncthreads();  // the previous chunk's h reads are done
-      for (int i = tid; i < 8 * H / 4; i += 256) {
-        const int ee = e8 + i / (H / 4);
-        const int b = entries[e0 + min(ee, ne - 1)] / k;
-        reinterpret_cast<float4*>(&hs8[0][0])[i] = *reinterpret_cast<const float4*>(h + (size_t)b * H + (i % (H / 4)) * 4);
+    for (int q = 0; q < NLD; ++q) fl[q] = entries[e0 + min(et + (tid + 256 * q) / (H / 4), ne - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fo[i] = entries[e0 + min(et + 4 * kq + i, ne - 1)];
+    float4 xv[NLD];
+#pragma unroll
+    for (int q = 0; q < NLD; ++q)
+      xv[q] = *reinterpret_cast<const float4*>(h + (size_t)(fl[q] / k) * H + ((tid + 256 * q) % (H / 4)) * 4);
+    __syncthreads();  // the previous tile's reads of hs (and best's initialisation) are done
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int i = tid + 256 * q, r = i / (H / 4), d = (i % (H / 4)) * 4;
+      const bool live = et + r < ne;
+      const float f[4] = {live ? xv[q].x : 0.f, live ? xv[q].y : 0.f, live ? xv[q].z : 0.f, live ? xv[q].w : 0.f};
+      uint16_t hi2[4], lo2[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        hi2[q2] = f2bf(f[q2]);
+        lo2[q2] = f2bf(f[q2] - bf2f(hi2[q2]));
       }
-      __syncthreads();
-      const int nchunk = min(8, ne - e8);
-      for (int e = 0; e < nchunk; ++e) {  // block-uniform
-        const int flat = entries[e0 + e8 + e];
-        const int b = flat / k;
-        float acc[8];
+      *reinterpret_cast<uint2*>(&hs[0][r][d]) = make_uint2(hi2[0] | ((uint32_t)hi2[1] << 16), hi2[2] | ((uint32_t)hi2[3] << 16));
+      *reinterpret_cast<uint2*>(&hs[1][r][d]) = make_uint2(lo2[0] | ((uint32_t)lo2[1] << 16), lo2[2] | ((uint32_t)lo2[3] << 16));
+    }
+    __syncthreads();
+
+    for (int g0 = 0; g0 < ct; g0 += 4 * CTW) {  // block-uniform: groups of id tiles
+      if (!one_group) load_rows(g0);
 #pragma unroll
-        for (int w = 0; w < 8; ++w) acc[w] = 0.f;
+      for (int j = 0; j < CTW; ++j) {
+        const int tile = g0 + wave * CTW + j;
+        if (tile >= ct) break;  // wave-uniform
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ch = 0; ch < HCH; ++ch) {
-          const float4 h0 = *reinterpret_cast<const float4*>(&hs8[e][ch * 128 + l16 * 8]);
-          const float4 h1 = *reinterpret_cast<const float4*>(&hs8[e][ch * 128 + l16 * 8 + 4]);
-          const float hf[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        for (int s2 = 0; s2 < KSTEPS; ++s2) {
+          const uint4 ah = *reinterpret_cast<const uint4*>(&hs[0][n][32 * s2 + 8 * kq]);
+          const uint4 al = *reinterpret_cast<const uint4*>(&hs[1][n][32 * s2 + 8 * kq]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, eb[j][s2]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, eb[j][s2]), acc, 0, 0, 0);
+        }
+        const int t = tile * 16 + n;  // id position in the cluster (< vsc: vsc is a multiple of 16)
+        const uint32_t id = (uint32_t)idv[j];
 #pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            float ef[8];
-            unpack8(raw[w][ch], ef);
-#pragma unroll
-            for (int d = 0; d < 8; ++d) acc[w] = fmaf(ef[d], hf[d], acc[w]);
+        for (int i = 0; i < 4; ++i) {
+          const int e = et + 4 * kq + i;
+          uint64_t kv = 0ull;
+          if (e < ne) {
+            const int flat = fo[i];
+            const size_t slot = (size_t)flat * vsc + t;
+            if (ids) ids[slot] = (int32_t)id;
+            if (z) z[slot] = acc[i];
+            if (logits) logits[(size_t)(flat / k) * V + id] = acc[i];
+            kv = vid_key(acc[i], id);
           }
+          // maximum over the 16 ids of this tile (lanes of equal kq)
+#pragma unroll
+          for (int o = 8; o > 0; o >>= 1) {
+            const uint32_t klo = __shfl_xor((uint32_t)kv, o, 64), khi = __shfl_xor((uint32_t)(kv >> 32), o, 64);
+            kv = u64_max(kv, ((uint64_t)khi << 32) | klo);
+          }
+          if (n == 0 && e < ne) atomicMax(&best[e], (unsigned long long)kv);
         }
-        XR<8, 8>::run(acc, l16);  // lane l16 of the group holds id (l16 >> 1) of the 8
-        uint64_t kv = 0ull;
-        if (mine) {
-          const size_t slot = (size_t)flat * vsc + t;
-          if (ids) ids[slot] = idq;
-          if (z) z[slot] = acc[0];
-          if (logits) logits[(size_t)b * V + idq] = acc[0];
-          kv = vid_key(acc[0], (uint32_t)idq);
-        }
-        kv = wave_max_u64(kv);
-        if (lane == 0) atomicMax(&best[e8 + e], (unsigned long long)kv);
       }
     }
   }
   __syncthreads();
-  for (int e = tid; e < ne; e += 256) keys[entries[e0 + e]] = best[e];
+  if (tid < ne) keys[entries[e0 + tid]] = best[tid];
 }
 
 // Head table in cluster order: out[r] = E[ordering[r]], rows of H bf16 (H % 8 == 0); grid ceil(V / 8), 256 threads,
@@ -919,10 +953,14 @@ hipError_t launch_topk_rows(hipStream_t s, int B, int C, int k, const float* sco
   return go(k_topk_rows<16>, B, 256, 0, s, C, k, scores, sel);
 }
 
+// the most (cluster, entry tile) pairs n selections of C clusters make: at most one partial tile per cluster
+int group_tiles(int n, int C) { return (C < n ? C : n) + (n + kGroupTile - 1) / kGroupTile; }
+
 hipError_t launch_group(hipStream_t s, int B, int C, int k, const int32_t* sel, int32_t* work) {
   const int n = B * k;
   if (n > kMaxBatch * kMaxTopK || C > kMaxCentroids) return hipErrorInvalidValue;
-  return go(k_group, 1, 1024, 0, s, n, C, sel, work, work + 1, work + 1 + C, work + 2 + 2 * C);
+  const int T = group_tiles(n, C);
+  return go(k_group, 1, 1024, 0, s, n, C, T, sel, reinterpret_cast<int4*>(work), work + 4 * T);
 }
 
 hipError_t launch_head_grouped(hipStream_t s, int B, int C, int k, int vsc, int H, const int32_t* ordering,
@@ -930,14 +968,12 @@ hipError_t launch_head_grouped(hipStream_t s, int B, int C, int k, int vsc, int 
                                float* logits, size_t V, uint64_t* keys) {
   const int n = B * k;
   if (n > kMaxBatch * kMaxTopK || C > kMaxCentroids) return hipErrorInvalidValue;
-  const int32_t* nuniq = work;
-  const int32_t* clist = work + 1;
-  const int32_t* cstart = clist + C;
-  const int32_t* entries = cstart + C + 1;
-  const int grid = C < n ? C : n;
+  const int T = group_tiles(n, C);
+  const int4* trec = reinterpret_cast<const int4*>(work);
+  const int32_t* entries = work + 4 * T;
 #define MTPD_HG(HCH_) \
   if (H == HCH_ * 128) \
-    return go(k_head_grouped<HCH_>, grid, 256, 0, s, k, vsc, ordering, Es, h, nuniq, clist, cstart, entries, ids, z, logits, V, keys);
+    return go(k_head_grouped<HCH_>, T, 256, 0, s, k, vsc, ordering, Es, h, trec, entries, ids, z, logits, V, keys);
   MTPD_HG(2) MTPD_HG(4) MTPD_HG(6) MTPD_HG(8)
 #undef MTPD_HG
   return hipErrorInvalidValue;

@@ -131,9 +131,10 @@ hipError_t launch_head(hipStream_t s, int B, int C, int k, int vsc, int H, const
                        const int32_t* ordering, const uint16_t* Es, const float* h, int32_t* sel, int32_t* ids,
                        float* z, float* logits, size_t V, uint64_t* keys);
 
-// The masked head's scoring grouped by cluster (for batches whose rows select many clusters in common): launch_group
-// groups the selections sel [B][k] (launch_head with Es == nullptr writes them) by cluster into work (int32, 2 + 2 C
-// + B k), then launch_head_grouped scores them, with the same outputs as launch_head.
+// The masked head's scoring grouped by cluster (for batches whose rows select many clusters in common):
+// launch_topk_rows writes the selections sel [B][k], launch_group groups them by cluster into work (int32, at most
+// 4 (C + B k) + B k: a (cluster, first entry, count) record per tile of up to 64 entries of one cluster, then the
+// grouped entries), then launch_head_grouped scores them one tile per block, with the same outputs as launch_head.
 hipError_t launch_group(hipStream_t s, int B, int C, int k, const int32_t* sel, int32_t* work);
 // sel [B][k] = each row's top k of scores [B][C] in slot order (descending score, ties to the lower index).
 hipError_t launch_topk_rows(hipStream_t s, int B, int C, int k, const float* scores, int32_t* sel);

@@ -133,7 +133,8 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.xp = take((size_t)(2 * Bb / 256) * B * H * 4);
   p.dp = take((size_t)(F / 256) * B * H * 4);
   p.rtok = take((size_t)B * 4);
-  p.grp = take((size_t)(2 + 2 * c.n_centroids + B * std::max(c.top_k, 1)) * 4);  // cluster grouping of the head
+  // cluster grouping of the head: a 16-byte record per (cluster, entry tile), then the grouped entries
+  p.grp = take((size_t)(4 * (c.n_centroids + B * std::max(c.top_k, 1)) + B * std::max(c.top_k, 1)) * 4);
   p.total = off;
   return p;
 }
