@@ -67,6 +67,10 @@ HEAD_SHAPES = {
     "c16_v1024_k3": dataclasses.replace(synth.E4B, vocab=16384, n_centroids=16, top_k=3),
     # 4096 clusters of 16 ids, top 64 (the largest cluster count and top_k)
     "c4096_v16_k64": dataclasses.replace(synth.E4B, vocab=65536, n_centroids=4096, top_k=64),
+    # hidden 512: 64 clusters of 32 ids, top 5
+    "h512_c64_v32_k5": dataclasses.replace(synth.E4B, hidden=512, vocab=2048, n_centroids=64, top_k=5),
+    # hidden 1024 (one id tile per wave at a time, the rows reloaded per group of tiles): 32 clusters of 128, top 4
+    "h1024_c32_v128_k4": dataclasses.replace(synth.E4B, hidden=1024, vocab=4096, n_centroids=32, top_k=4),
 }
 
 
