@@ -55,23 +55,24 @@ def check_draw(row, order, T, u, tok, prob, where):
     return checked
 
 
-HEAD_CASES = {
-    "e4b_masked": (synth.E4B, 1.0),
-    "e4b_masked_cold": (synth.E4B, 0.05),
-    "dense_h256": (None, 0.3),  # E2B-shaped with a dense 8208-token head (two tiles, a ragged second)
-    "e26b_dense": (synth.E26B, 0.05),
+HEAD_CASES = {  # (shape, temperature, rows)
+    "e4b_masked": (synth.E4B, 1.0, 32),
+    "e4b_masked_cold": (synth.E4B, 0.05, 32),
+    # 64 rows x top 32 = every cluster's worth: the head runs grouped by cluster
+    "e4b_masked_grouped": (synth.E4B, 0.7, 64),
+    "dense_h256": (None, 0.3, 32),  # E2B-shaped with a dense 8208-token head (two tiles, a ragged second)
+    "e26b_dense": (synth.E26B, 0.05, 32),
 }
 
 
 @pytest.mark.parametrize("name", list(HEAD_CASES))
 def test_sample_head_draws_match_the_oracle_sampler(name):
     import dataclasses
-    shape, T = HEAD_CASES[name]
+    shape, T, m = HEAD_CASES[name]
     if shape is None:
         shape = dataclasses.replace(synth.E2B, n_centroids=0, top_k=1, vocab=8208)
     say(f"sample_head {name} T={T}")
-    case = Case(shape, batch=1, context=16, max_batch=32, gen_device="cuda")
-    m = 32
+    case = Case(shape, batch=1, context=16, max_batch=m, gen_device="cuda")
     g = torch.Generator().manual_seed(300)
     h = torch.randn(m, shape.hidden, generator=g, dtype=torch.float32)
     u = torch.rand(m, generator=g, dtype=torch.float32)
@@ -86,7 +87,7 @@ def test_sample_head_draws_match_the_oracle_sampler(name):
     say(f"checked {checked}/{m}")
     assert checked >= m // 2
     # the whole pipeline from h: where u is far from any interval end, the oracle's own logits give the same draw
-    for r in (0, 7, 31):
+    for r in (0, 7, m - 1):
         hr = h[r].numpy().astype(np.float64)
         ref = O.dense_head_result(case.model, hr) if shape.n_centroids == 0 else \
             O.masked_head_row(case.model, hr, want_row=True)
