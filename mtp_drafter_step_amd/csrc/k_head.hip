@@ -152,7 +152,6 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
   }
   const int c = sh_c;
   if (tid == 0 && sel) sel[(size_t)b * k + j] = c;
-  if (!Es) return;  // selection only: the cluster-grouped head scores the candidates
 
   // the cluster's candidate ids and their logits: group grp scores ids t = grp + 16 i, 8 ids per pass
   const int grp = tid >> 4, l16 = tid & 15;

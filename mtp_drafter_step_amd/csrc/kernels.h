@@ -122,8 +122,7 @@ hipError_t launch_sample(hipStream_t s, int phase, int B, int n, int vsc, int k,
                          float* tsum, const float* u, int32_t* tok_out, float* prob_out, int out_stride,
                          int32_t* tok_next);
 
-// Masked head: per (row, selected slot j): top-k of the row's centroid scores (only the selection, into sel, when
-// Es is null) (descending, ties to the lower
+// Masked head: per (row, selected slot j): top-k of the row's centroid scores (descending, ties to the lower
 // index), the cluster's token ids through the ordering, sparse logits token_embd[id] . h (rows read from Es, the
 // head table in cluster order), optional scatter into logits, and the slot's best (value, id) key (larger value,
 // then lower id).

@@ -269,7 +269,9 @@ int nsplit_for(const mtpd::RowWindows& win, int B, int nkv) {
 }
 
 // The masked head on fp32 hidden states h [B][H] and centroid scores already in the workspace: per (row, slot)
-// top-k + gather + dot (+ scatter) and the slot's best (value, id) key.
+// top-k + gather + dot (+ scatter) and the slot's best (value, id) key. With few rows one kernel does it all per
+// (row, slot); with many (B k at least the cluster count) the selection runs once per row, the selections are
+// grouped by cluster, and each cluster's rows are read once for all the rows that chose it.
 int run_head(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int B, const float* hsrc,
              float* logits, int32_t* sel_out, int32_t* ids_out, float* z_out) {
   const mtpd_config& c = h->cfg;
