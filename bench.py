@@ -364,11 +364,11 @@ def run_bench(args):
     # the measured streaming-read rate of this device: the best of a few row-wise reductions over the resident
     # 1 GiB tensor (rows of 4096 floats, and 4096 rows), whose output is negligible next to the bytes read
     read_ms = []
-    for shape in ((-1, 4096), (4096, -1)):
+    for rows in ((-1, 4096), (4096, -1)):
         for _ in range(4):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            sweep.view(*shape).sum(dim=1)
+            sweep.view(*rows).sum(dim=1)
             e1.record(stream)
             torch.cuda.synchronize()
             read_ms.append(e0.elapsed_time(e1))
