@@ -445,6 +445,42 @@ def test_graph_replays_match_direct_launches():
         assert other["next"].shape[0] == 4
 
 
+@pytest.mark.parametrize("name,shape,batch", [("e4b_b4_small_path", synth.E4B, 4), ("e2b_b48_gemm_path", synth.E2B, 48)])
+def test_caller_graph_capture_replays(name, shape, batch):
+    """A caller captures draft_block into its own graph (the library then launches straight into the caller's
+    capture instead of replaying its own graphs): every replay, with eager work and synchronisations between them,
+    reproduces the eager call bit for bit. At 48 rows the step takes the matrix-core dense stages and the grouped
+    head."""
+    say(f"caller capture {name}")
+    case = Case(shape, batch=batch, context=900, ragged=True, max_batch=batch)
+    d = case.drafter
+    ws = d.workspace(batch)
+    ref = d.draft_block(2, case.th, case.tok, case.temb, case.kv, want_logits=True, workspace=ws)
+    ref = {k: v.clone() for k, v in ref.items()}
+    out = {"tokens": torch.empty_like(ref["tokens"]), "hidden_out": torch.empty_like(ref["hidden_out"]),
+           "logits": torch.empty_like(ref["logits"])}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture's stream kind, outside the capture
+        d.draft_block(2, case.th, case.tok, case.temb, case.kv, want_logits=True, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.draft_block(2, case.th, case.tok, case.temb, case.kv, want_logits=True, out=out, workspace=ws)
+    for rep in range(3):
+        for v in out.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), (name, rep, k)
+        other = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_sparse=False)  # eager work between
+        torch.cuda.synchronize()
+        assert other["next"].shape[0] == batch
+
+
 def test_kernel_timing_records_every_launch_and_keeps_results():
     """Timing records: one per kernel launch of the call, in launch order, with positive durations; the results
     equal those of the graph-replayed call."""
