@@ -164,6 +164,9 @@ STEP_CASES = {
     "e2b_b64_ctx300": dict(shape=synth.E2B, batch=64, context=300, ragged=True),
     # the largest batch the ABI takes, per-row caches
     "e2b_b256_ctx200": dict(shape=synth.E2B, batch=256, context=200, ragged=True),
+    # hidden 512 and 768 (the small-batch kernels' wider prologues)
+    "e2b_h512_b3_ragged600": dict(shape=dataclasses.replace(synth.E2B, hidden=512), batch=3, context=600, ragged=True),
+    "e2b_h768_b5_ragged600": dict(shape=dataclasses.replace(synth.E2B, hidden=768), batch=5, context=600, ragged=True),
     # head_dim 128 and 64 (the vector-ALU attention): 2 and 8 query heads per kv head
     "e2b_hd128_g2": dict(shape=dataclasses.replace(synth.E2B, head_dim=128, n_head=8, n_kv_head=4), batch=3,
                          context=700, ragged=True),
@@ -324,6 +327,8 @@ GEMM_PATH_CASES = {
     # 32+ rows take the matrix-core dense stages by default: run both paths on the same inputs
     "e4b_b40_ragged2000": dict(shape=synth.E4B, batch=40, context=2000, ragged=True),
     "e26b_b32_ctx4000": dict(shape=synth.E26B, batch=32, context=4000, ragged=True, gen_device="cuda"),
+    # hidden 768 at 33 rows: three 16-row tiles, the last with one row
+    "e2b_h768_b33_ragged900": dict(shape=dataclasses.replace(synth.E2B, hidden=768), batch=33, context=900, ragged=True),
     # and the matrix-core path forced on a small batch (one 16-row pass with ragged columns)
     "e4b_b5_forced": dict(shape=synth.E4B, batch=5, context=900, ragged=True),
 }
