@@ -183,18 +183,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       f32x4 sacc[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        // K operands read one step ahead of the products (few registers live: the wave is at its register limit)
+        // K operands read two steps ahead of the products
         const uint16_t* krow = &kt[buf][32 * j + 16 * h2 + hq][8 * kq];
         uint4 kcur = *reinterpret_cast<const uint4*>(krow);
+        uint4 knx = *reinterpret_cast<const uint4*>(krow + 32);
         sacc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const uint4 knext = *reinterpret_cast<const uint4*>(krow + 32 * min(s + 1, KSTEPS - 1));
+          const uint4 knext = knx;
+          knx = *reinterpret_cast<const uint4*>(krow + 32 * min(s + 2, KSTEPS - 1));
           const bf16x8 a = __builtin_bit_cast(bf16x8, kcur);
           sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qhi[s]), sacc[h2], 0, 0, 0);
           sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qlo[s]), sacc[h2], 0, 0, 0);
           kcur = knext;
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // scores S[query hq][key kb + 16 h2 + 4 kq + r], masked to the query row's window
@@ -259,7 +260,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi), vb, a, 0, 0, 0);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo), vb, a, 0, 0, 0);
         acc[t] = a;
-        if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // V operands of at most four tiles in flight
       }
       }
       if (more) {
