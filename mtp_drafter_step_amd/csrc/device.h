@@ -48,10 +48,18 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // fp32 -> bf16, round to nearest even (finite inputs)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two fp32 -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+// the pair (a, b) as bf16 hi + lo parts (a + b within 2^-16 relative of hi + lo), each packed as by f2bf2
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = f2bf2(a, b);
+  lo = f2bf2(a - bf_lo(hi), b - bf_hi(hi));
 }
 
 

@@ -293,20 +293,24 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
   ps += xr_partner<32>(ps);
   lrun = lrun * alpha + ps;
   mrun = mn;
-  i16x4 phi, plo;
+  uint32_t ph2[2], pl2[2];
+  split_bf16x2(pv[0], pv[1], ph2[0], pl2[0]);
+  split_bf16x2(pv[2], pv[3], ph2[1], pl2[1]);
+  const i16x4 phi = __builtin_bit_cast(i16x4, make_uint2(ph2[0], ph2[1]));
+  const i16x4 plo = __builtin_bit_cast(i16x4, make_uint2(pl2[0], pl2[1]));
+  // rescale the accumulators only when some head's maximum moved (alpha is exactly 1 otherwise): D rows are heads
+  // 4kq + r, whose alpha lives in lane 4kq + r (rows of heads >= G are padding)
+  if (__any(alpha != 1.0f)) {
+    float al[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint16_t hb = f2bf(pv[r]);
-    phi[r] = (short)hb;
-    plo[r] = (short)f2bf(pv[r] - bf2f(hb));
-  }
-  // rescale the accumulators: D rows are heads 4kq + r, whose alpha lives in lane 4kq + r (rows of heads >= G
-  // are padding)
-  float al[4];
+    for (int r = 0; r < 4; ++r) {
+      al[r] = readlane_f(alpha, r);
+      if constexpr (GQ > 1) al[r] = (kq == 1) ? readlane_f(alpha, 4 + r) : al[r];
+    }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    al[r] = readlane_f(alpha, r);
-    if constexpr (GQ > 1) al[r] = (kq == 1) ? readlane_f(alpha, 4 + r) : al[r];
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] *= al[r];
   }
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
@@ -314,8 +318,6 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
 #pragma unroll
     for (int r = 0; r < 4; ++r) vb[r] = (short)tile[(4 * kq + r) * LROW + 16 * t + hq];
     f32x4 a = acc[t];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] *= al[r];
     a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
     a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);
     acc[t] = a;

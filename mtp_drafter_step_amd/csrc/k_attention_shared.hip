@@ -150,12 +150,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
     for (int s = 0; s < KSTEPS; ++s) {
       uint32_t h32[4], l32[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h0 = f2bf(v[s][2 * e]), h1 = f2bf(v[s][2 * e + 1]);
-        const uint16_t l0 = f2bf(v[s][2 * e] - bf2f(h0)), l1 = f2bf(v[s][2 * e + 1] - bf2f(h1));
-        h32[e] = h0 | ((uint32_t)h1 << 16);
-        l32[e] = l0 | ((uint32_t)l1 << 16);
-      }
+      for (int e = 0; e < 4; ++e) split_bf16x2(v[s][2 * e], v[s][2 * e + 1], h32[e], l32[e]);
       qhi[s] = make_uint4(h32[0], h32[1], h32[2], h32[3]);
       qlo[s] = make_uint4(l32[0], l32[1], l32[2], l32[3]);
     }
@@ -226,16 +221,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       mrun = mn;
       // P as the A operand of v_mfma_f32_16x16x32_bf16 over the 32 keys: lane l supplies k = 8 kq + i, which stands
       // for key 4 kq + i (i < 4) and key 16 + 4 kq + (i - 4); the V operand below follows the same order
-      uint16_t ph[8], pl[8];
+      uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ph[i] = f2bf(pv[i]);
-        pl[i] = f2bf(pv[i] - bf2f(ph[i]));
-      }
-      const uint4 phi = make_uint4(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16),
-                                   ph[4] | ((uint32_t)ph[5] << 16), ph[6] | ((uint32_t)ph[7] << 16));
-      const uint4 plo = make_uint4(pl[0] | ((uint32_t)pl[1] << 16), pl[2] | ((uint32_t)pl[3] << 16),
-                                   pl[4] | ((uint32_t)pl[5] << 16), pl[6] | ((uint32_t)pl[7] << 16));
+      for (int i = 0; i < 4; ++i) split_bf16x2(pv[2 * i], pv[2 * i + 1], ph[i], pl[i]);
+      const uint4 phi = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+      const uint4 plo = make_uint4(pl[0], pl[1], pl[2], pl[3]);
       // rescale only when some query's maximum moved (alpha is exactly 1 otherwise); output rows are queries
       // 4 kq + r, whose alphas live in lanes 4 kq + r
       if (__any(alpha != 1.0f)) {

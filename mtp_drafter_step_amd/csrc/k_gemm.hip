@@ -91,15 +91,11 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
       }
     }
     const bool live = c0 + r < B;
-    uint16_t hi[4], lo[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v = live ? f[j] : 0.f;
-      hi[j] = f2bf(v);
-      lo[j] = f2bf(v - bf2f(hi[j]));
-    }
-    *reinterpret_cast<uint2*>(&xs[0][r][k]) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-    *reinterpret_cast<uint2*>(&xs[1][r][k]) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    uint32_t hi[2], lo[2];
+    split_bf16x2(live ? f[0] : 0.f, live ? f[1] : 0.f, hi[0], lo[0]);
+    split_bf16x2(live ? f[2] : 0.f, live ? f[3] : 0.f, hi[1], lo[1]);
+    *reinterpret_cast<uint2*>(&xs[0][r][k]) = make_uint2(hi[0], hi[1]);
+    *reinterpret_cast<uint2*>(&xs[1][r][k]) = make_uint2(lo[0], lo[1]);
   }
   __syncthreads();
 
@@ -158,7 +154,7 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
       *reinterpret_cast<float4*>(Y + ((size_t)kc * B + c) * N + n) = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
     } else if constexpr (EPI == EPI_BF16) {
       *reinterpret_cast<uint2*>(Yb + (size_t)c * N + n) =
-          make_uint2(f2bf(acc[0][0]) | ((uint32_t)f2bf(acc[0][1]) << 16), f2bf(acc[0][2]) | ((uint32_t)f2bf(acc[0][3]) << 16));
+          make_uint2(f2bf2(acc[0][0], acc[0][1]), f2bf2(acc[0][2], acc[0][3]));
     } else {
       float mv[4];
 #pragma unroll

@@ -275,17 +275,11 @@ __global__ __launch_bounds__(1024) void k_head_dense(int B, int V, const uint16_
     const int e = (tid + i * 1024) * 4, col = e / H, k = e % H;
     const bool live = c0 + col < B;
     const float f[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
-    uint16_t hi[4], lo[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v = live ? f[j] : 0.f;
-      hi[j] = f2bf(v);
-      lo[j] = f2bf(v - bf2f(hi[j]));
-    }
-    *reinterpret_cast<uint2*>(&hs[0][col][k]) =
-        make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-    *reinterpret_cast<uint2*>(&hs[1][col][k]) =
-        make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    uint32_t hi[2], lo[2];
+    split_bf16x2(live ? f[0] : 0.f, live ? f[1] : 0.f, hi[0], lo[0]);
+    split_bf16x2(live ? f[2] : 0.f, live ? f[3] : 0.f, hi[1], lo[1]);
+    *reinterpret_cast<uint2*>(&hs[0][col][k]) = make_uint2(hi[0], hi[1]);
+    *reinterpret_cast<uint2*>(&hs[1][col][k]) = make_uint2(lo[0], lo[1]);
   }
   __syncthreads();
 
@@ -632,14 +626,11 @@ __global__ __launch_bounds__(256) void k_head_grouped(int k, int vsc, const int3
       const int i = tid + 256 * q, r = i / (H / 4), d = (i % (H / 4)) * 4;
       const bool live = et + r < ne;
       const float f[4] = {live ? xv[q].x : 0.f, live ? xv[q].y : 0.f, live ? xv[q].z : 0.f, live ? xv[q].w : 0.f};
-      uint16_t hi2[4], lo2[4];
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        hi2[q2] = f2bf(f[q2]);
-        lo2[q2] = f2bf(f[q2] - bf2f(hi2[q2]));
-      }
-      *reinterpret_cast<uint2*>(&hs[0][r][d]) = make_uint2(hi2[0] | ((uint32_t)hi2[1] << 16), hi2[2] | ((uint32_t)hi2[3] << 16));
-      *reinterpret_cast<uint2*>(&hs[1][r][d]) = make_uint2(lo2[0] | ((uint32_t)lo2[1] << 16), lo2[2] | ((uint32_t)lo2[3] << 16));
+      uint32_t hi2[2], lo2[2];
+      split_bf16x2(f[0], f[1], hi2[0], lo2[0]);
+      split_bf16x2(f[2], f[3], hi2[1], lo2[1]);
+      *reinterpret_cast<uint2*>(&hs[0][r][d]) = make_uint2(hi2[0], hi2[1]);
+      *reinterpret_cast<uint2*>(&hs[1][r][d]) = make_uint2(lo2[0], lo2[1]);
     }
     __syncthreads();
 
