@@ -145,11 +145,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float mn = fmaxf(mrun[hh], readlane_f(mx, hh));
-      alpha[hh] = (mrun[hh] == -INFINITY) ? 0.f : exp2f(mrun[hh] - mn);
+      alpha[hh] = (mrun[hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[hh] - mn);
       mrun[hh] = mn;
       mhl = (hl == hh) ? mn : mhl;
     }
-    const float p = (jl < nk) ? exp2f(s - mhl) : 0.f;
+    const float p = (jl < nk) ? __builtin_amdgcn_exp2f(s - mhl) : 0.f;
     float ps = p;
 #pragma unroll
     for (int of = G; of < 64; of <<= 1) ps += __shfl_xor(ps, of, 64);
@@ -282,11 +282,12 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
   mt = fmaxf(mt, xr_partner<16>(mt));
   mt = fmaxf(mt, xr_partner<32>(mt));
   const float mn = fmaxf(mrun, mt);
-  const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
+  // 2^x on the hardware instruction: weights below 2^-126 flush to zero, far below what a weight contributes
+  const float alpha = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
   float pv[4], ps = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    pv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
+    pv[r] = (sv[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[r] - mn);
     ps += pv[r];
   }
   ps += xr_partner<16>(ps);

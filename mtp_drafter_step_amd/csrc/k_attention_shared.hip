@@ -208,11 +208,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       mt = fmaxf(mt, xr_partner<16>(mt));
       mt = fmaxf(mt, xr_partner<32>(mt));
       const float mn = fmaxf(mrun, mt);
-      const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mn);
+      // 2^x on the hardware instruction: weights below 2^-126 flush to zero, far below what a weight contributes
+      const float alpha = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
       float pv[8], ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pv[i] = (sv[i] == -INFINITY) ? 0.f : exp2f(sv[i] - mn);
+        pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - mn);
         ps += pv[i];
       }
       ps += xr_partner<16>(ps);
