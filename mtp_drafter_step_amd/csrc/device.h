@@ -38,6 +38,7 @@ constexpr int kRG = kRowGroup;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -87,6 +88,17 @@ __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a >
 __device__ __forceinline__ uint4 ld_global16(const void* p) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(p));
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Each lane names 4 consecutive 16-bit values (an 8-byte aligned LDS
+// address); within each group of 16 lanes, take the 64 values the group names in lane order, and lane i of the group
+// receives values i, 16 + i, 32 + i and 48 + i of that list. So when lane j of a group names row R + j / 4, columns
+// C + 4 (j % 4) .. +4 of a row-major tile, lane i receives column C + i of rows R .. R + 3: a 4 x 16 block read
+// column-wise, the B operand layout of a 16-deep matrix-core step. (Mapping established on gfx950 by reading an
+// index-filled tile.)
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(__attribute__((address_space(3))) void*)(p));
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {

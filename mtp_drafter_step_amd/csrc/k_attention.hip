@@ -228,7 +228,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
 //     terms q = q_hi + q_lo (relative error <= 2^-16) so the product keeps fp32-level accuracy;
 //   online softmax on the S layout (lane l holds keys 4*(l/16)+r of head l%16);
 //   O[16 heads][256] += P . V with v_mfma_f32_16x16x16_bf16: P (split into bf16 hi + lo) is already in the A layout,
-//     V comes from the wave's LDS copy of the key tile read column-wise (4 keys of one dim per lane).
+//     V comes from the wave's LDS copy of the key tile, read column-wise by transposing LDS reads (4 keys of one dim
+//     per lane).
 
 
 // One batch of 16 keys for one wave of k_attn_mfma: scores of the keys in ka against the G heads, online softmax
@@ -313,11 +314,11 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[t][r] *= al[r];
   }
+  // V operand: keys 4 kq + r of dim 16 t + hq, one transposing read of the 4 x 16 block at row 4 kq
+  const uint16_t* vrow = tile + (4 * kq + (hq >> 2)) * LROW + 4 * (hq & 3);
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
-    i16x4 vb;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vb[r] = (short)tile[(4 * kq + r) * LROW + 16 * t + hq];
+    const i16x4 vb = lds_read_tr16(vrow + 16 * t);
     f32x4 a = acc[t];
     a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
     a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);

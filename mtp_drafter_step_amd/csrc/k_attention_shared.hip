@@ -17,10 +17,9 @@ namespace {
 // Multi-query matrix-core attention over a cache shared by the batch's rows (rows of one sequence scored together):
 // every row reads the same keys, so the query rows meet each key tile once. A block holds 128 queries (8 waves x 16
 // queries: 16 / G rows x the G query heads of kv head blockIdx.z) and one key range: split blockIdx.x of the union
-// [u0, u1) of the rows' windows. Key tiles of 64 rows are staged in LDS for all waves (double-buffered, one barrier
-// per tile), twice: row-major (K rows for the scores) and transposed (each dim's keys contiguous, so a lane's keys
-// of one dim, the P.V operand, are 8-byte reads). Each thread loads 4 x 4 (key x dim) blocks so that it can
-// write both layouts with 8-byte stores. Per wave and 32-key batch (two 16-key score tiles):
+// [u0, u1) of the rows' windows. Key tiles of 64 rows are staged row-major in LDS for all waves (double-buffered,
+// one barrier per tile): the scores read key rows, the P.V operand reads the same tile column-wise with transposing
+// LDS reads. Per wave and 32-key batch (two 16-key score tiles):
 //   S^T[16 keys][16 queries] = K_tile . Q^T with v_mfma_f32_16x16x32_bf16, the keys as A rows from LDS and the
 //     queries as B columns held in registers as bf16 hi + lo (q after q_norm and rotation, fp32-level accuracy);
 //   online softmax per query (lane column), each key masked by the query row's own window;
@@ -37,11 +36,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
                                                     float* __restrict__ pacc, float* __restrict__ pml,
                                                     float* __restrict__ o) {
   constexpr int HD = 256, KSTEPS = HD / 32, TILES = HD / 16, NW = 8, KT = 64, LROW = HD + 8, half = HD / 2;
-  constexpr int VROW = KT + 4;  // transposed rows: 136 B, so 16 dims at one key offset fall in distinct banks
   constexpr int RPW = 16 / G, RPB = NW * RPW;  // rows per wave, per block
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "16 queries per wave are whole rows");
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][KT][LROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][HD][VROW];
   const int sp = blockIdx.x, g = blockIdx.z;
   const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
   const int hq = lane & 15, kq = lane >> 4;
@@ -79,16 +76,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(&kt[bf][4 * kg + j][4 * dg]) = st[x][j];
-      // dim 4 dg + e of the 4 keys
-      const uint32_t w[4][2] = {{st[x][0].x, st[x][0].y}, {st[x][1].x, st[x][1].y}, {st[x][2].x, st[x][2].y},
-                                {st[x][3].x, st[x][3].y}};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int wi = e >> 1, sh = (e & 1) * 16;
-        const uint32_t k0v = (w[0][wi] >> sh) & 0xFFFFu, k1v = (w[1][wi] >> sh) & 0xFFFFu;
-        const uint32_t k2v = (w[2][wi] >> sh) & 0xFFFFu, k3v = (w[3][wi] >> sh) & 0xFFFFu;
-        *reinterpret_cast<uint2*>(&vt[bf][4 * dg + e][4 * kg]) = make_uint2(k0v | (k1v << 16), k2v | (k3v << 16));
-      }
     }
   };
   const bool any = k0 < k1;
@@ -242,11 +229,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[t][r] *= al[r];
       }
+      // V operand: keys 32 j + 4 kq + r and 32 j + 16 + 4 kq + r of dim 16 t + hq, two transposing reads of the
+      // 4 x 16 blocks at those key rows
+      const uint16_t* vrow = &kt[buf][32 * j + 4 * kq + (hq >> 2)][4 * (hq & 3)];
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
-        const uint2 v0 = *reinterpret_cast<const uint2*>(&vt[buf][16 * t + hq][32 * j + 4 * kq]);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(&vt[buf][16 * t + hq][32 * j + 16 + 4 * kq]);
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        const i16x4 v0 = lds_read_tr16(vrow + 16 * t);
+        const i16x4 v1 = lds_read_tr16(vrow + 16 * LROW + 16 * t);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, (i16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
         f32x4 a = acc[t];
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi), vb, a, 0, 0, 0);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo), vb, a, 0, 0, 0);
