@@ -17,7 +17,7 @@ namespace {
 // Multi-query matrix-core attention over a cache shared by the batch's rows (rows of one sequence scored together):
 // every row reads the same keys, so the query rows meet each key tile once. A block holds 128 queries (8 waves x 16
 // queries: 16 / G rows x the G query heads of kv head blockIdx.z) and one key range: split blockIdx.x of the union
-// [u0, u1) of the rows' windows. Key tiles of 64 rows are staged row-major in LDS for all waves (double-buffered,
+// [u0, u1) of the rows' windows. Key tiles of 128 rows are staged row-major in LDS for all waves (double-buffered,
 // one barrier per tile): the scores read key rows, the P.V operand reads the same tile column-wise with transposing
 // LDS reads. Per wave and 32-key batch (two 16-key score tiles):
 //   S^T[16 keys][16 queries] = K_tile . Q^T with v_mfma_f32_16x16x32_bf16, the keys as A rows from LDS and the
@@ -27,6 +27,26 @@ namespace {
 // Each wave's queries are its own, so the outputs need no combine: (max, sum) and the unnormalised sums go to the
 // split partials that the o_proj kernel merges (or, with one split, straight to o).
 // grid (nsplit, ceil(B / (128 / G)), n_kv), 512 threads.
+constexpr int kMqRow = 256 + 8;  // LDS row of a staged key (elements): 528 B
+
+// Part x of a key tile starting at key tb (keys 32 x .. +32, clamped into the range ending at k1): thread tid
+// loads dims 8 (tid % 32) .. +8 of keys 32 x + tid / 32 and 32 x + 16 + tid / 32, so a wave reads two whole keys
+// per load; mq_store_part writes them to the same places of a row-major LDS tile.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mq_load_part(const uint16_t* Kb, int cap, int k1, int tb, int x, int tid,
+                                             u32x4 (&r)[2]) {
+  const int kr = tid >> 5, dc = tid & 31;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    r[j] = *reinterpret_cast<const u32x4*>(Kb + (size_t)slot_of(min(tb + 32 * x + 16 * j + kr, k1 - 1), cap) * 256 +
+                                           8 * dc);
+}
+__device__ __forceinline__ void mq_store_part(uint16_t* tile, int x, int tid, const u32x4 (&r)[2]) {
+  const int kr = tid >> 5, dc = tid & 31;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(tile + (32 * x + 16 * j + kr) * kMqRow + 8 * dc) = r[j];
+}
+
 template <int G>
 __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, const float* __restrict__ q,
                                                     const uint16_t* __restrict__ qnorm, float eps,
@@ -35,7 +55,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
                                                     int nsplit, int u0, int u1, float scale_log2,
                                                     float* __restrict__ pacc, float* __restrict__ pml,
                                                     float* __restrict__ o) {
-  constexpr int HD = 256, KSTEPS = HD / 32, TILES = HD / 16, NW = 8, KT = 64, LROW = HD + 8, half = HD / 2;
+  constexpr int HD = 256, KSTEPS = HD / 32, TILES = HD / 16, NW = 8, KT = 128, LROW = kMqRow, half = HD / 2;
   constexpr int RPW = 16 / G, RPB = NW * RPW;  // rows per wave, per block
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "16 queries per wave are whole rows");
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][KT][LROW];
@@ -61,27 +81,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
   const int k0 = u0 + sp * chunk, k1 = min(u1, k0 + chunk);
   const uint16_t* Kb = K + (size_t)g * cap * HD;  // the shared cache (row 0)
 
-  // first key tile in flight before the q prologue: thread t loads the 4 x 4 blocks (keys 4 kg .. +4, dims 4 dg ..
-  // +4) with kg = i / 64, dg = i % 64 for i = t and t + 512 (a wave reads 512 contiguous bytes of one key per load)
-  uint2 st[2][4];
-  // half x of a tile (keys 32 x .. +32): loads into st[x], stores into LDS buffer bf
-  auto gload = [&](int tb, int x) {
-    const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      st[x][j] = *reinterpret_cast<const uint2*>(Kb + (size_t)slot_of(min(tb + 4 * kg + j, k1 - 1), cap) * HD + 4 * dg);
-  };
-  auto lstore = [&](int bf, int x) {
-    {
-      const int bi = tid + 512 * x, kg = bi >> 6, dg = bi & 63;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(&kt[bf][4 * kg + j][4 * dg]) = st[x][j];
-    }
-  };
+  // first key tile in flight before the q prologue (both parts: registers st0, st1)
+  u32x4 st0[2], st1[2];
   const bool any = k0 < k1;
   if (any) {
-    gload(k0, 0);
-    gload(k0, 1);
+    mq_load_part(Kb, cap, k1, k0, 0, tid, st0);
+    mq_load_part(Kb, cap, k1, k0, 1, tid, st1);
   }
 
   // q_norm + rotation of the lane's query: the lane holds dims 32 s + 8 kq + e (s < 8, e < 8); the rotation partner
@@ -148,16 +153,23 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (any) {
-    lstore(0, 0);
-    lstore(0, 1);
+    mq_store_part(&kt[0][0][0], 0, tid, st0);
+    mq_store_part(&kt[0][0][0], 1, tid, st1);
+#pragma unroll
+    for (int p = 2; p < KT / 32; p += 2) {  // the rest of a longer first tile
+      mq_load_part(Kb, cap, k1, k0, p, tid, st0);
+      mq_load_part(Kb, cap, k1, k0, p + 1, tid, st1);
+      mq_store_part(&kt[0][0][0], p, tid, st0);
+      mq_store_part(&kt[0][0][0], p + 1, tid, st1);
+    }
   }
   __syncthreads();
   int buf = 0;
   for (int tb = k0; tb < k1; tb += KT) {  // block-uniform
     const bool more = tb + KT < k1;
-    // the next tile, in halves, into the other buffer (free since the last barrier): each half's loads are in
-    // flight during one 32-key batch, and only one half's registers are live at a time
-    if (more) gload(tb + KT, 0);
+    // the next tile, in 32-key parts, into the other buffer (free since the last barrier): each part's loads are in
+    // flight during one 32-key batch, and at most two parts' registers are live at a time
+    if (more) mq_load_part(Kb, cap, k1, tb + KT, 0, tid, st0);
 #pragma unroll
     for (int j = 0; j < KT / 32; ++j) {  // 32-key batches: two score tiles, one softmax update
       const int kb = tb + 32 * j;
@@ -243,9 +255,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
         acc[t] = a;
       }
       }
-      if (more) {
-        lstore(buf ^ 1, j);
-        if (j == 0) gload(tb + KT, 1);
+      if (more) {  // part j of the next tile to LDS, part j + 1 into the freed registers
+        if ((j & 1) == 0) {
+          mq_store_part(&kt[buf ^ 1][0][0], j, tid, st0);
+          if (j + 1 < KT / 32) mq_load_part(Kb, cap, k1, tb + KT, j + 1, tid, st1);
+        } else {
+          mq_store_part(&kt[buf ^ 1][0][0], j, tid, st1);
+          if (j + 1 < KT / 32) mq_load_part(Kb, cap, k1, tb + KT, j + 1, tid, st0);
+        }
       }
     }
     __syncthreads();
