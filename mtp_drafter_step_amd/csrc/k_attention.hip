@@ -202,7 +202,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float mw = wml[w][hh][0];
-        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
         L = fmaf(wml[w][hh][1], f, L);
         A = fmaf(wacc[w][hh][d], f, A);
       }
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float mw = ml[w][hh].x;
-        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
         L = fmaf(ml[w][hh].y, f, L);
         A = fmaf(av[w][hh >> 2][hh & 3], f, A);
       }
