@@ -111,10 +111,16 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// GELU, tanh form: 0.5 a (1 + tanh(u)) with u = sqrt(2/pi) (a + 0.044715 a^3), evaluated as the equal a / (1 + e^-2u)
+// on the hardware 2^x and reciprocal (a few ulp at every a; no cancellation in 1 + tanh(u) for negative a)
 __device__ __forceinline__ float gelu_tanh(float a) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * a * (1.0f + tanhf(c * (a + 0.044715f * a * a * a)));
+  const float u = c * (a + 0.044715f * a * a * a);
+  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * u));  // 2 log2(e)
 }
+
+// 1 / sqrt(x) on the hardware instruction (1 ulp): the RMSNorm scale, x >= eps > 0
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
 
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));

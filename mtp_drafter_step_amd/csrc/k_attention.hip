@@ -89,7 +89,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
       ss = fmaf(v[e], v[e], ss);
     }
     ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+    const float r = rsqrt_hw(ss / (float)HD + eps);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) v[e] = v[e] * r * wq[e];
 #pragma unroll
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss = fmaf(v[e], v[e], ss);
     ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+    const float r = rsqrt_hw(ss / (float)HD + eps);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = v[e] * r * wq[e];
 #pragma unroll

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
     }
     ss += xr_partner<16>(ss);
     ss += xr_partner<32>(ss);
-    const float rn = 1.0f / sqrtf(ss / (float)HD + eps);
+    const float rn = rsqrt_hw(ss / (float)HD + eps);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float c8[8] = {co[s][0].x, co[s][0].y, co[s][0].z, co[s][0].w, co[s][1].x, co[s][1].y, co[s][1].z, co[s][1].w};

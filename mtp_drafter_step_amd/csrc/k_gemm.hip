@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
       d[i] = s;
       ss = fmaf(s, s, ss);
     }
-    const float r = 1.0f / sqrtf(block_sum<HPT>(ss, red) / (float)H + eps);
+    const float r = rsqrt_hw(block_sum<HPT>(ss, red) / (float)H + eps);
 #pragma unroll
     for (int i = 0; i < HPT; ++i) x[i] = (x[i] + d[i] * r * bf2f(w_delta[tid + 256 * i])) * scale;
   }
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
     if (x_new) x_new[(size_t)b * H + tid + 256 * i] = x[i];
     ss = fmaf(x[i], x[i], ss);
   }
-  const float r = 1.0f / sqrtf(block_sum<HPT>(ss, red) / (float)H + eps);
+  const float r = rsqrt_hw(block_sum<HPT>(ss, red) / (float)H + eps);
 #pragma unroll
   for (int i = 0; i < HPT; ++i) u[(size_t)b * H + tid + 256 * i] = x[i] * r * bf2f(w_norm[tid + 256 * i]);
   if (keys_zero && tid == 0) keys_zero[b] = 0ull;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void k_merge(int nsplit, int hd, const float* 
   if (M != -INFINITY) {
     for (int s = 0; s < nsplit; ++s) {
       const float mw = pml[(base + s) * 2];
-      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L = fmaf(pml[(base + s) * 2 + 1], f, L);
       A = fmaf(pacc[(base + s) * hd + d], f, A);
     }

@@ -110,14 +110,14 @@ __device__ __forceinline__ void prologue_norm(const Residual& res, const uint16_
 #pragma unroll
   for (int j = 0; j < NPL; ++j) ss = fmaf(dv[j], dv[j], ss);
   ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  const float r = rsqrt_hw(ss / (float)H + eps);
 #pragma unroll
   for (int j = 0; j < NPL; ++j) xv[j] = hasd ? (xv[j] + dv[j] * r * bf2f(wd[j])) * res.scale : xv[j];
   float s2 = 0.f;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) s2 = fmaf(xv[j], xv[j], s2);
   s2 = wave_sum(s2);
-  const float r2 = 1.0f / sqrtf(s2 / (float)H + eps);
+  const float r2 = rsqrt_hw(s2 / (float)H + eps);
   const bool valid = row < B;
   if (res.x_new && blockIdx.x == 0 && valid) {
 #pragma unroll
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void k_oproj(int N, int QD, int hd, int nh, in
     M = fmaxf(M, xr_partner<4>(M));
     M = fmaxf(M, xr_partner<2>(M));
     M = fmaxf(M, xr_partner<1>(M));
-    const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - M);
+    const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
     const float L = wave_sum(ml.y * f);
     float A = 0.f;
 #pragma unroll
