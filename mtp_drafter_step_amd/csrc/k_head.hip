@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
   constexpr int H = HCH * 128;
   constexpr int HPT = (H + 255) / 256;  // hidden elements per thread
   __shared__ uint32_t hist[2][4][256];  // per wave (fewer same-address atomics), double-buffered
-  __shared__ uint32_t sh_digit, sh_before, sh_n;
+  __shared__ uint32_t sh_n;
   __shared__ uint64_t cand[kMaxCentroids];
   __shared__ int sh_c;
   __shared__ float hs[H];
@@ -53,13 +53,14 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
   // Slot j holds the (j+1)-th element in descending (score, then ascending index) order. Radix select on the order
   // keys, 8 bits at a time from the top, narrows the search to the digit bin that holds that rank; once the bin
   // holds a single element, that element is the answer. Only elements tied with the exact key (bin still larger
-  // than one after all four passes) need ordering by index, below. Histograms are double-buffered so that a pass
-  // takes two barriers: the scan wave reads one buffer while the others clear the next.
+  // than one after all four passes) need ordering by index, below. Each wave counts into its own histogram and
+  // every wave scans all four after the pass's one barrier (so the chosen digit never goes through LDS); a wave
+  // then clears its own histogram of the other buffer, last read before this pass's barrier, for the next pass.
   uint32_t prefix = 0, pmask = 0;
   uint32_t need = (uint32_t)j + 1u;
   uint32_t inbin = 0;
-  hist[0][0][tid] = hist[0][1][tid] = hist[0][2][tid] = hist[0][3][tid] = 0u;
-  __syncthreads();
+#pragma unroll
+  for (int q2 = 0; q2 < 4; ++q2) hist[0][wave][lane + 64 * q2] = hist[1][wave][lane + 64 * q2] = 0u;
   int buf = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
@@ -67,40 +68,42 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
       if (tid + 256 * i < C && (ok[i] & pmask) == prefix)
         atomicAdd(&hist[buf][wave][(ok[i] >> shift) & 255u], 1u);
     __syncthreads();
-    if (wave == 0) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      uint32_t cnt[4], sum = 0;
+    // lane l owns digits 255-4l .. 252-4l (descending)
+    uint32_t cnt[4], sum = 0;
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const int dg = 255 - 4 * lane - q2;
-        cnt[q2] = hist[buf][0][dg] + hist[buf][1][dg] + hist[buf][2][dg] + hist[buf][3][dg];
-        sum += cnt[q2];
-      }
-      uint32_t incl = sum;  // inclusive prefix over lanes (higher digits first)
-#pragma unroll
-      for (int of = 1; of < 64; of <<= 1) {
-        const uint32_t t = __shfl_up(incl, of, 64);
-        if (lane >= of) incl += t;
-      }
-      uint32_t before = incl - sum;
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        if (before < need && before + cnt[q2] >= need) {
-          sh_digit = 255u - 4u * lane - q2;
-          sh_before = before;
-          sh_n = cnt[q2];
-        }
-        before += cnt[q2];
-      }
-    } else {
-      const int ow = wave - 1;  // waves 1-3 clear the other buffer (all four wave histograms)
-      for (int i = ow * 64 + lane; i < 4 * 256; i += 3 * 64) (&hist[buf ^ 1][0][0])[i] = 0u;
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const int dg = 255 - 4 * lane - q2;
+      cnt[q2] = hist[buf][0][dg] + hist[buf][1][dg] + hist[buf][2][dg] + hist[buf][3][dg];
+      sum += cnt[q2];
     }
-    __syncthreads();
-    prefix |= sh_digit << shift;
+    uint32_t incl = sum;  // inclusive prefix over lanes (higher digits first)
+#pragma unroll
+    for (int of = 1; of < 64; of <<= 1) {
+      const uint32_t t = __shfl_up(incl, of, 64);
+      if (lane >= of) incl += t;
+    }
+    uint32_t before = incl - sum, dsel = 0u, bsel = 0u, nsel = 0u;
+    bool hit = false;
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      if (before < need && before + cnt[q2] >= need) {
+        hit = true;
+        dsel = 255u - 4u * lane - q2;
+        bsel = before;
+        nsel = cnt[q2];
+      }
+      before += cnt[q2];
+    }
+    const uint64_t hm = __ballot(hit);  // exactly one lane: the bins partition the ranks 1 .. (bin size)
+    const int src = hm ? __ffsll((unsigned long long)hm) - 1 : 0;
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane((int)dsel, src);
+    const uint32_t nbefore = (uint32_t)__builtin_amdgcn_readlane((int)bsel, src);
+    inbin = (uint32_t)__builtin_amdgcn_readlane((int)nsel, src);
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) hist[buf ^ 1][wave][lane + 64 * q2] = 0u;
+    prefix |= digit << shift;
     pmask |= 255u << shift;
-    need -= sh_before;
-    inbin = sh_n;
+    need -= nbefore;
     buf ^= 1;
     if (inbin == 1u) break;
   }
@@ -111,7 +114,6 @@ __global__ __launch_bounds__(256) void k_head(int C, int k, int vsc, const float
     __syncthreads();
   } else {
   // the bin's members as (key, ~index) composites: descending composite order is the slot order
-  __syncthreads();  // every wave has read the last bin count
   if (tid == 0) sh_n = 0u;
   __syncthreads();
 #pragma unroll
