@@ -27,7 +27,12 @@ namespace {
 // Each wave's queries are its own, so the outputs need no combine: (max, sum) and the unnormalised sums go to the
 // split partials that the o_proj kernel merges (or, with one split, straight to o).
 // grid (nsplit, ceil(B / (128 / G)), n_kv), 512 threads.
-constexpr int kMqRow = 256 + 8;  // LDS row of a staged key (elements): 528 B
+// LDS row of a staged key: 544 B (256 elements and 32 B of padding), with the 16-byte columns of rows 8 .. 15 of
+// every 16 swapped in pairs (column c at c ^ 1). With 64 four-byte banks a row starts two 16-byte bank groups after
+// the previous one, so the 16 rows of a key read (one column each), the 8 rows of half a transposing V read (one
+// column pair each) and the 16 columns of a row store all fall in distinct banks.
+constexpr int kMqRow = 256 + 16;
+__device__ __forceinline__ int mq_swz(int row) { return (row >> 3) & 1; }
 
 // Part x of a key tile starting at key tb (keys 32 x .. +32, clamped into the range ending at k1): thread tid
 // loads dims 8 (tid % 32) .. +8 of keys 32 x + tid / 32 and 32 x + 16 + tid / 32, so a wave reads two whole keys
@@ -44,7 +49,8 @@ __device__ __forceinline__ void mq_load_part(const uint16_t* Kb, int cap, int k1
 __device__ __forceinline__ void mq_store_part(uint16_t* tile, int x, int tid, const u32x4 (&r)[2]) {
   const int kr = tid >> 5, dc = tid & 31;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(tile + (32 * x + 16 * j + kr) * kMqRow + 8 * dc) = r[j];
+  for (int j = 0; j < 2; ++j)
+    *reinterpret_cast<u32x4*>(tile + (32 * x + 16 * j + kr) * kMqRow + 8 * (dc ^ mq_swz(kr))) = r[j];
 }
 
 template <int G>
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         // K operands read two steps ahead of the products
-        const uint16_t* krow = &kt[buf][32 * j + 16 * h2 + hq][8 * kq];
+        const uint16_t* krow = &kt[buf][32 * j + 16 * h2 + hq][8 * (kq ^ mq_swz(hq))];
         uint4 kcur = *reinterpret_cast<const uint4*>(krow);
         uint4 knx = *reinterpret_cast<const uint4*>(krow + 32);
         sacc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -243,7 +249,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       }
       // V operand: keys 32 j + 4 kq + r and 32 j + 16 + 4 kq + r of dim 16 t + hq, two transposing reads of the
       // 4 x 16 blocks at those key rows
-      const uint16_t* vrow = &kt[buf][32 * j + 4 * kq + (hq >> 2)][4 * (hq & 3)];
+      const uint16_t* vrow =
+          &kt[buf][32 * j + 4 * kq + (hq >> 2)][8 * (((hq & 3) >> 1) ^ mq_swz(4 * kq)) + 4 * (hq & 1)];
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         const i16x4 v0 = lds_read_tr16(vrow + 16 * t);
