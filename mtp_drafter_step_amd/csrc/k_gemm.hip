@@ -71,29 +71,47 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
 
   // stage the X chunk: 16 rows x KC, rows past B are zero
   constexpr int NV4 = NC * KC / 4 / 256;  // float4 (or 4 bf16) per thread
+  float xf[NV4][4];
+  if constexpr (SRC == SRC_F32) {
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int e = (tid + i * 256) * 4, r = e / KC, k = e % KC;
+      const float4 v = *reinterpret_cast<const float4*>(src.x + (size_t)min(c0 + r, B - 1) * K + kbase + k);
+      xf[i][0] = v.x; xf[i][1] = v.y; xf[i][2] = v.z; xf[i][3] = v.w;
+    }
+  } else {
+    // the rows' tokens first, then every row load unconditionally (a select picks the table), so that the loads
+    // issue together instead of one branch, load and wait per element
+    int tk[NV4];
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) tk[i] = src.tok[min(c0 + ((tid + i * 256) * 4) / KC, B - 1)];
+    uint2 w[NV4];
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int e = (tid + i * 256) * 4, r = e / KC, k = e % KC;
+      const int kk = kbase + k;  // Bb % 256 == 0: 4 dims lie in one half
+      const bool hid = kk < src.Bb;
+      const size_t oh = (size_t)min(c0 + r, B - 1) * src.Bb + kk;
+      const size_t oe = (size_t)tk[i] * src.Bb + (kk - src.Bb);
+      const uint16_t* ptr = hid ? src.th + oh : src.emb + oe;
+      w[i] = *reinterpret_cast<const uint2*>(ptr);
+    }
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int kk = kbase + ((tid + i * 256) * 4) % KC;
+      const float sc = kk < src.Bb ? 1.0f : src.escale;
+      unpack4(w[i], xf[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[i][j] *= sc;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NV4; ++i) {
     const int e = (tid + i * 256) * 4, r = e / KC, k = e % KC;
-    const int b = min(c0 + r, B - 1);
-    float f[4];
-    if constexpr (SRC == SRC_F32) {
-      const float4 v = *reinterpret_cast<const float4*>(src.x + (size_t)b * K + kbase + k);
-      f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
-    } else {
-      const int kk = kbase + k;  // Bb % 256 == 0: 4 dims lie in one half
-      const bool hid = kk < src.Bb;
-      const uint16_t* p = hid ? src.th + (size_t)b * src.Bb + kk : src.emb + (size_t)src.tok[b] * src.Bb + (kk - src.Bb);
-      const uint2 w = *reinterpret_cast<const uint2*>(p);
-      unpack4(w, f);
-      if (!hid) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f[j] *= src.escale;
-      }
-    }
     const bool live = c0 + r < B;
     uint32_t hi[2], lo[2];
-    split_bf16x2(live ? f[0] : 0.f, live ? f[1] : 0.f, hi[0], lo[0]);
-    split_bf16x2(live ? f[2] : 0.f, live ? f[3] : 0.f, hi[1], lo[1]);
+    split_bf16x2(live ? xf[i][0] : 0.f, live ? xf[i][1] : 0.f, hi[0], lo[0]);
+    split_bf16x2(live ? xf[i][2] : 0.f, live ? xf[i][3] : 0.f, hi[1], lo[1]);
     *reinterpret_cast<uint2*>(&xs[0][r][k]) = make_uint2(hi[0], hi[1]);
     *reinterpret_cast<uint2*>(&xs[1][r][k]) = make_uint2(lo[0], lo[1]);
   }
@@ -234,20 +252,31 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
 // ------------------------------------------------------------------------------------------------------------
 // Merge of the key-range split partials of the attention: o[b][h][d] = sum_s f_s A_s[d] / sum_s f_s L_s with
 // f_s = 2^(M_s - max M). grid B * nh, hd threads.
+template <int NS>
 __global__ __launch_bounds__(256) void k_merge(int nsplit, int hd, const float* pacc, const float* pml, float* o) {
-  const int bh = blockIdx.x, d = threadIdx.x;
+  static_assert(NS >= 1 && NS <= 64, "one (max, sum) pair per lane");
+  const int bh = blockIdx.x, d = threadIdx.x, lane = lane_id();
   const size_t base = (size_t)bh * kMaxSplit;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml[(base + s) * 2]);
-  float L = 0.f, A = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float mw = pml[(base + s) * 2];
-      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L = fmaf(pml[(base + s) * 2 + 1], f, L);
-      A = fmaf(pacc[(base + s) * hd + d], f, A);
-    }
-  }
+  // every load first: the thread's dim of each split, and split `lane`'s (max, sum) pair in lane `lane`
+  float a[NS];
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) a[s2] = pacc[(base + (size_t)min(s2, nsplit - 1)) * hd + d];
+  const float2 ml = *reinterpret_cast<const float2*>(pml + (base + (size_t)min(lane, nsplit - 1)) * 2);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  const float mv = lane < nsplit ? ml.x : -INFINITY;
+  float M = mv;
+  M = fmaxf(M, xr_partner<32>(M));
+  M = fmaxf(M, xr_partner<16>(M));
+  M = fmaxf(M, xr_partner<8>(M));
+  M = fmaxf(M, xr_partner<4>(M));
+  M = fmaxf(M, xr_partner<2>(M));
+  M = fmaxf(M, xr_partner<1>(M));
+  const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);  // 0 for splits past nsplit
+  const float L = wave_sum(ml.y * f);
+  float A = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) A = fmaf(a[s2], readlane_f(f, s2), A);
   o[(size_t)bh * hd + d] = (L > 0.f) ? A / L : 0.f;
 }
 
@@ -342,7 +371,13 @@ hipError_t launch_rownorm(hipStream_t s, int B, int H, const float* xp, int nx, 
 
 hipError_t launch_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml,
                         float* o) {
-  return go(k_merge, B * nh, hd, 0, s, nsplit, hd, pacc, pml, o);
+#define MTPD_MERGE(NS_) return go(k_merge<NS_>, B * nh, hd, 0, s, nsplit, hd, pacc, pml, o)
+  if (nsplit <= 2) MTPD_MERGE(2);
+  if (nsplit <= 4) MTPD_MERGE(4);
+  if (nsplit <= 8) MTPD_MERGE(8);
+  if (nsplit <= 16) MTPD_MERGE(16);
+  MTPD_MERGE(32);
+#undef MTPD_MERGE
 }
 
 hipError_t launch_token(hipStream_t s, int B, int V, TokenSource ts, int32_t* tok_out) {
