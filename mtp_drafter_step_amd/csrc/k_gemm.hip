@@ -205,7 +205,14 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
   constexpr int H = HPT * 256;
   __shared__ float red[4];
   const int b = blockIdx.x, tid = threadIdx.x;
-  float xv[NX][HPT], dv[ND][HPT];
+  // every load first and unconditionally, so that none waits behind a branch: without a delta the delta slots read
+  // the x partials (valid memory; the values are not used) and the delta weights read w_norm
+  const bool hasd = delta != nullptr;
+  const float* dsrc = hasd ? delta : xp;
+  const size_t dstr = hasd ? ds : xs;
+  const int ndl = hasd ? nd : nx;
+  const uint16_t* wdsrc = hasd ? w_delta : w_norm;
+  float xv[NX][HPT], dv[ND][HPT], wd[HPT], wn[HPT];
 #pragma unroll
   for (int p = 0; p < NX; ++p)
 #pragma unroll
@@ -213,8 +220,14 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
 #pragma unroll
   for (int p = 0; p < ND; ++p)
 #pragma unroll
-    for (int i = 0; i < HPT; ++i)
-      dv[p][i] = delta ? delta[(size_t)min(p, nd - 1) * ds + (size_t)b * H + tid + 256 * i] : 0.f;
+    for (int i = 0; i < HPT; ++i) dv[p][i] = dsrc[(size_t)min(p, ndl - 1) * dstr + (size_t)b * H + tid + 256 * i];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    wd[i] = bf2f(wdsrc[tid + 256 * i]);
+    wn[i] = bf2f(w_norm[tid + 256 * i]);
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   float x[HPT];
 #pragma unroll
   for (int i = 0; i < HPT; ++i) {
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
     for (int p = 0; p < NX; ++p) s += p < nx ? xv[p][i] : 0.f;
     x[i] = s;
   }
-  if (delta) {
+  if (hasd) {
     float d[HPT], ss = 0.f;
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
     }
     const float r = rsqrt_hw(block_sum<HPT>(ss, red) / (float)H + eps);
 #pragma unroll
-    for (int i = 0; i < HPT; ++i) x[i] = (x[i] + d[i] * r * bf2f(w_delta[tid + 256 * i])) * scale;
+    for (int i = 0; i < HPT; ++i) x[i] = (x[i] + d[i] * r * wd[i]) * scale;
   }
   float ss = 0.f;
 #pragma unroll
@@ -245,7 +258,7 @@ __global__ __launch_bounds__(256) void k_rownorm(int B, const float* xp, int nx,
   }
   const float r = rsqrt_hw(block_sum<HPT>(ss, red) / (float)H + eps);
 #pragma unroll
-  for (int i = 0; i < HPT; ++i) u[(size_t)b * H + tid + 256 * i] = x[i] * r * bf2f(w_norm[tid + 256 * i]);
+  for (int i = 0; i < HPT; ++i) u[(size_t)b * H + tid + 256 * i] = x[i] * r * wn[i];
   if (keys_zero && tid == 0) keys_zero[b] = 0ull;
 }
 

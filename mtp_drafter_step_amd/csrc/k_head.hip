@@ -514,12 +514,14 @@ __global__ __launch_bounds__(1024) void k_group(int n, int C, int T, const int32
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   for (int c = tid; c < kMaxCentroids; c += 1024) cnt[c] = 0u;
   __syncthreads();
+  // every selection loaded first (clamped index, unconditionally) so the loads issue together, then counted
   int cv[EPT];
   uint32_t pos[EPT];
 #pragma unroll
+  for (int i = 0; i < EPT; ++i) cv[i] = sel[min(tid + 1024 * i, n - 1)];
+#pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int e = tid + 1024 * i;
-    cv[i] = e < n ? sel[e] : -1;
+    if (tid + 1024 * i >= n) cv[i] = -1;
     pos[i] = cv[i] >= 0 ? atomicAdd(&cnt[cv[i]], 1u) : 0u;
   }
   __syncthreads();
