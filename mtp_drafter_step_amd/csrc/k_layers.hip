@@ -46,6 +46,8 @@ struct WaveW {
     for (int r = 0; r < kRG; ++r)
 #pragma unroll
       for (int i = 0; i < IT; ++i) xr[r][i] = *reinterpret_cast<const float4*>(xrow[r] + i * 256 + lane * 4);
+    asm volatile("" ::: "memory");  // all activation loads issued together (the scheduler would spread them out)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kRG * OPW; ++i) acc[i] = 0.f;
 #pragma unroll
@@ -98,6 +100,10 @@ __device__ __forceinline__ void prologue_norm(const Residual& res, const uint16_
   for (int p = 0; p < ND; ++p)
 #pragma unroll
     for (int j = 0; j < NPL; ++j) dp[p][j] = dr[(size_t)min(p, nd - 1) * dst + lane + 64 * j];
+  // every load above issued here: otherwise the compiler sinks the delta-weight load into a branch on hasd and
+  // waits for it there, one more dependent round trip
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   float dv[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
