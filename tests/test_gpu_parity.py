@@ -331,6 +331,9 @@ GEMM_PATH_CASES = {
     "e2b_h768_b33_ragged900": dict(shape=dataclasses.replace(synth.E2B, hidden=768), batch=33, context=900, ragged=True),
     # and the matrix-core path forced on a small batch (one 16-row pass with ragged columns)
     "e4b_b5_forced": dict(shape=synth.E4B, batch=5, context=900, ragged=True),
+    # one long row among short ones: the full layer takes the most key-range splits (32), so both split merges
+    # (k_merge on the large-batch path, k_oproj's prologue on the small one) run their widest form
+    "e4b_b32_one_long_row": dict(shape=synth.E4B, batch=32, context=4096, lens=[4096] + [40] * 31),
 }
 
 
