@@ -40,7 +40,7 @@ struct GemmSrc {
 
 template <int KC, int WPT, int SRC, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, const uint16_t* W, const uint16_t* W2,
-                                              float* Y, uint16_t* Yb) {
+                                              float* Y, uint16_t* Yb, FillRange fill) {
   constexpr int NC = 16, KSTEPS = KC / 32, LROW = KC + 8;
   constexpr int WSTEPS = KSTEPS / WPT;  // steps per wave (WPT waves per 16-row tile)
   constexpr int NW2 = EPI == EPI_GEGLU ? 2 : 1;
@@ -68,6 +68,23 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
       for (int p = 0; p < P; ++p) a[bf][m][p] = ld_global16(wrow[m] + (ch * P + p) * 32);
   };
   load(0, 0);
+
+  // the block's share of the logits fill ([Inventory] "Centroid / ordered embeddings LM head", step 5: the -1e30 base
+  // row), written while the weight loads are in flight (streaming stores: nothing reads the row before the head)
+  if (fill.logits) {
+    const size_t nblk = (size_t)gridDim.x * gridDim.y * gridDim.z;
+    const size_t bid = ((size_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const size_t total = fill.end - fill.begin;
+    const size_t per = ((total + nblk - 1) / nblk + 3) & ~(size_t)3;
+    const size_t a = fill.begin + bid * per;
+    const size_t e = a + per < fill.end ? a + per : fill.end;
+    if (a < e) {
+      const f32x4 v = f32x4{-1e30f, -1e30f, -1e30f, -1e30f};
+      size_t i = a + tid * 4;
+      for (; i + 4 <= e; i += 1024) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(fill.logits + i));
+      for (; i < e; ++i) __builtin_nontemporal_store(-1e30f, fill.logits + i);
+    }
+  }
 
   // stage the X chunk: 16 rows x KC, rows past B are zero
   constexpr int NV4 = NC * KC / 4 / 256;  // float4 (or 4 bf16) per thread
@@ -332,7 +349,7 @@ int gemm_chunks(int B, int N, int K, bool one_chunk) {
 
 hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float* X, const uint16_t* th,
                        const uint16_t* emb, const int32_t* tok, int Bb, float escale, const uint16_t* W,
-                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks) {
+                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks, FillRange fill) {
   if (K % 256 || N % 16 || K > 4096 * 2 || (K / 256) % nchunks) return hipErrorInvalidValue;
   const int KC = K / nchunks;
   // waves per 16-row tile: more only while the grid is below about 256 blocks (each block stages its X chunk, so
@@ -343,7 +360,7 @@ hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float
   const dim3 grid((N + 64 / wpt - 1) / (64 / wpt), nchunks, (B + 15) / 16);
   GemmSrc src{X, th, emb, tok, Bb, escale};
 #define MTPD_GEMM_W(KC_, WPT_, SRC_, EPI_) \
-  if (KC == KC_ && wpt == WPT_) return go(k_gemm<KC_, WPT_, SRC_, EPI_>, grid, 256, 0, s, B, N, K, src, W, W2, Y, Yb);
+  if (KC == KC_ && wpt == WPT_) return go(k_gemm<KC_, WPT_, SRC_, EPI_>, grid, 256, 0, s, B, N, K, src, W, W2, Y, Yb, fill);
 #define MTPD_GEMM(KC_, SRC_, EPI_) MTPD_GEMM_W(KC_, 1, SRC_, EPI_) MTPD_GEMM_W(KC_, 2, SRC_, EPI_) MTPD_GEMM_W(KC_, 4, SRC_, EPI_)
   if (kind == 0) {  // fp32 partials from fp32 rows
     MTPD_GEMM(256, SRC_F32, EPI_F32) MTPD_GEMM(512, SRC_F32, EPI_F32) MTPD_GEMM(768, SRC_F32, EPI_F32)

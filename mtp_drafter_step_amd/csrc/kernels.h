@@ -160,10 +160,11 @@ int gemm_chunks(int B, int N, int K, bool one_chunk);
 
 // Matrix-core GEMM Y = W X^T, W bf16 [N][K], over nchunks K chunks (K % 256 == 0, N % 16 == 0). kind 0: X fp32
 // [B][K] -> fp32 partials Y [nchunks][B][N]; 1: -> bf16 Yb [B][N]; 2: GeGLU gelu_tanh(W X) * (W2 X) -> fp32 Y [B][N];
-// 3: X = [th ; escale * emb[tok]] (bf16 tables, K = 2 Bb) -> fp32 partials. Kinds 1 and 2 need nchunks == 1.
+// 3: X = [th ; escale * emb[tok]] (bf16 tables, K = 2 Bb) -> fp32 partials. Kinds 1 and 2 need nchunks == 1. The
+// blocks also fill a slice of the logits with -1e30 (fill.logits null: none).
 hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float* X, const uint16_t* th,
                        const uint16_t* emb, const int32_t* tok, int Bb, float escale, const uint16_t* W,
-                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks);
+                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks, FillRange fill = FillRange{nullptr, 0, 0});
 
 // Per row: x = sum of nx partials of xp (stride xs); with delta (nd partials, stride ds) x = (x + RMSNorm(delta;
 // w_delta)) * scale; x_new = x (when set); u = RMSNorm(x; w_norm); keys_zero[b] = 0 (when set). H % 256 == 0.

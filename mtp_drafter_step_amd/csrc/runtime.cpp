@@ -392,6 +392,16 @@ int run_step_gemm(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p
   const uint16_t* wd = nullptr;
   float sc = 1.0f;
   const int no = mtpd::gemm_chunks(B, H, QD, false), nf = mtpd::gemm_chunks(B, H, F, false);
+  // the masked head's -1e30 base row, written in 4 nL slices by the blocks of the layers' four GEMMs (the dense head
+  // writes every logit itself)
+  const size_t BV = (size_t)B * c.vocab;
+  const int nslice = 4 * nL;
+  auto fill_slice = [&](int i) {
+    if (!logits || dense) return mtpd::FillRange{nullptr, 0, 0};
+    const size_t a = (BV * (size_t)i / nslice) & ~size_t(3);
+    const size_t e = i + 1 == nslice ? BV : (BV * (size_t)(i + 1) / nslice) & ~size_t(3);
+    return mtpd::FillRange{logits, a, e};
+  };
   for (int l = 0; l < nL; ++l) {
     const mtpd_layer& L = h->layers[l];
     const int type = ((c.full_attn_layers >> l) & 1u) ? 1 : 0;
@@ -399,7 +409,7 @@ int run_step_gemm(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p
     KLAUNCH(h, "rownorm", mtpd::launch_rownorm(s, B, H, xin, nx, BH, din, nd, BH, wd, sc, L.attn_norm, c.rms_eps, x, u,
                                                nullptr));
     KLAUNCH(h, "qproj_gemm", mtpd::launch_gemm(s, 0, B, QD, H, u, nullptr, nullptr, nullptr, 0, 0.f, L.attn_q, nullptr,
-                                               q, nullptr, 1));
+                                               q, nullptr, 1, fill_slice(4 * l)));
     KLAUNCH(h, type ? "attn_full" : "attn_sliding",
             mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
                               cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale, at<float>(ws, p.pacc),
@@ -408,13 +418,13 @@ int run_step_gemm(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p
       KLAUNCH(h, "attn_merge", mtpd::launch_merge(s, B, c.n_head, c.head_dim, nsplit[type], at<float>(ws, p.pacc),
                                                   at<float>(ws, p.pml), o));
     KLAUNCH(h, "o_proj_gemm", mtpd::launch_gemm(s, 0, B, H, QD, o, nullptr, nullptr, nullptr, 0, 0.f, L.attn_output,
-                                                nullptr, t, nullptr, no));
+                                                nullptr, t, nullptr, no, fill_slice(4 * l + 1)));
     KLAUNCH(h, "rownorm", mtpd::launch_rownorm(s, B, H, x, 1, 0, t, no, BH, L.post_attention_norm, 1.0f, L.ffn_norm,
                                                c.rms_eps, x, u, nullptr));
     KLAUNCH(h, "ffn_gemm", mtpd::launch_gemm(s, 2, B, F, H, u, nullptr, nullptr, nullptr, 0, 0.f, L.ffn_gate, L.ffn_up,
-                                             m, nullptr, 1));
+                                             m, nullptr, 1, fill_slice(4 * l + 2)));
     KLAUNCH(h, "down_gemm", mtpd::launch_gemm(s, 0, B, H, F, m, nullptr, nullptr, nullptr, 0, 0.f, L.ffn_down, nullptr,
-                                              dp, nullptr, nf));
+                                              dp, nullptr, nf, fill_slice(4 * l + 3)));
     xin = x;
     nx = 1;
     din = dp;
@@ -430,11 +440,9 @@ int run_step_gemm(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p
   if (!dense && c.n_centroids % 16 != 0) {
     KLAUNCH(h, "scores", mtpd::launch_scores(s, B, H, c.n_centroids, at<float>(ws, p.h), h->w.centroids,
                                              at<float>(ws, p.scores)));
-    if (logits) KLAUNCH(h, "fill", mtpd::launch_fill(s, logits, (size_t)B * c.vocab));
   } else if (!dense) {
     KLAUNCH(h, "scores_gemm", mtpd::launch_gemm(s, 0, B, c.n_centroids, H, at<float>(ws, p.h), nullptr, nullptr, nullptr,
                                                 0, 0.f, h->w.centroids, nullptr, at<float>(ws, p.scores), nullptr, 1));
-    if (logits) KLAUNCH(h, "fill", mtpd::launch_fill(s, logits, (size_t)B * c.vocab));
   }
   return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, sel_out, ids_out, z_out);
 }
