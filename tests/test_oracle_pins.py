@@ -311,29 +311,30 @@ def test_layer_scalar_zero_branch_closed_form():
     assert np.allclose(x, want, rtol=1e-13, atol=0)
 
 
-def test_gqa_head_mapping():
-    """n_kv = 2, n_head = 4: heads 0-1 read kv head 0 and heads 2-3 kv head 1. Make kv head 1 a single repeated key:
-    every head reading it returns that key (K = V), heads reading kv head 0 do not."""
+def test_gqa_head_mapping_through_the_layer():
+    """n_kv = 2, n_head = 4: query heads 0-1 read kv head 0 and heads 2-3 kv head 1. Kv head 1 holds one repeated key
+    (K = V), so heads 2 and 3 return that key whatever their query, while kv head 0 keeps random keys. With the
+    columns of attn_output that read heads 0-1 set to zero and the FFN branch zeroed, decoder_layer must equal the
+    closed form (x + RMSNorm(W_o [.. ; c ; c], post_attention_norm)) * s for every layer and row; a head mapping
+    that sent head 2 or 3 to kv head 0 would read random keys there."""
     m, w, shape = _tiny_model(n_kv_head=2)
     wl, d, kv = _tiny_inputs(shape)
-    const = kv.k[1][0, 1, 0].copy()
-    kv.k[1][:, 1] = const
-    kv.v = kv.k
     cfg = m.cfg
-    b, l = 0, 3  # layer 3 is the full-attention layer
-    L = m.layers[l]
+    for t in range(2):
+        kv.k[t][:, 1] = kv.k[t][:, 1, :1]
+    kv.v = kv.k
+    hd = cfg.head_dim
     x = rng(10).standard_normal(cfg.hidden)
-    u = O.round_bf16(O.rmsnorm(x, L["attn_norm"], cfg.rms_eps))
-    q = (L["q"] @ u).reshape(cfg.n_head, cfg.head_dim)
-    a0, a1 = O.key_window(kv.lens[1][b], cfg.swa_window, True)
-    for h in range(cfg.n_head):
-        qh = O.round_bf16(O.rope_rotate(O.rmsnorm(q[h], L["q_norm"], cfg.rms_eps), kv.rope[b, 1, 0], kv.rope[b, 1, 1]))
-        g = h * cfg.n_kv_head // cfg.n_head
-        o = O.attend(qh, O.bf16_to_f64(kv.k[1][b, g, a0:a1]), O.bf16_to_f64(kv.k[1][b, g, a0:a1]), cfg.attn_scale)
-        if h >= 2:
-            assert np.allclose(o, O.bf16_to_f64(const))
-        else:
-            assert not np.allclose(o, O.bf16_to_f64(const))
+    for l in range(cfg.n_layer):
+        L = m.layers[l]
+        L["down"][:] = 0.0
+        L["o"][:, :2 * hd] = 0.0
+        t = 1 if cfg.is_full(l) else 0
+        for b in range(3):
+            c = O.bf16_to_f64(kv.k[t][b, 1, 0])
+            o = np.concatenate([np.zeros(2 * hd), c, c])
+            want = (x + O.rmsnorm(L["o"] @ o, L["post_attn_norm"], cfg.rms_eps)) * L["scale"]
+            assert np.allclose(O.decoder_layer(m, l, x, b, kv), want, rtol=1e-12, atol=1e-12), (l, b)
 
 
 def test_window_one_returns_last_key():
@@ -599,3 +600,198 @@ def test_attention_branch_closed_form_with_identical_keys():
         want = (x + O.rmsnorm(L["o"] @ o, L["post_attn_norm"], cfg.rms_eps)) * L["scale"]
         got = O.decoder_layer(m, l, x, b, kv)
         assert np.allclose(got, want, rtol=1e-12, atol=1e-12), l
+
+
+# ---------------------------------------------------------------- the query path, the softmax scale and the norm roles
+# Metamorphic relations through decoder_layer / drafter_step: each transforms an input in a way the method's
+# definition says must (or must not) change the result, with factors of 2 and quarter turns that are exact in bf16
+# and fp64, so that equalities are exact.
+
+
+def _distinct_v_inputs(shape, batch=3, context=40, seed=0):
+    """Tiny inputs whose caches carry a V distinct from K (the attention output then shows what was read as V)."""
+    wl = synth.Workload("tiny", shape, batch=batch, context=context, n_steps=1, ragged=True, seed=seed)
+    d = synth.make_inputs(wl, distinct_v=True)
+    u16 = lambda t: t.numpy().view(np.uint16).copy()  # noqa: E731
+    kv = O.SharedKV(k=[u16(d["k_sliding"]), u16(d["k_full"])], v=[u16(d["v_sliding"]), u16(d["v_full"])],
+                    lens=[d["len_sliding"], d["len_full"]], rope=d["rope"].numpy().copy())
+    return d, kv
+
+
+def _quarter_turn_tables(B, half, seed):
+    """Per-row, per-type rotary tables whose angles are multiples of pi/2 (cos, sin in {0, +1, -1}, so a rotation of
+    bf16 values is exact), different for the sliding and the full type."""
+    r = rng(seed)
+    k = r.integers(0, 4, size=(B, 2, half))
+    while np.array_equal(k[:, 0], k[:, 1]) or np.all(k % 2 == 0):
+        k = r.integers(0, 4, size=(B, 2, half))
+    tab = np.zeros((B, 2, 2, half), np.float32)
+    tab[:, :, 0] = np.array([1, 0, -1, 0], np.float32)[k]  # cos(k pi/2)
+    tab[:, :, 1] = np.array([0, 1, 0, -1], np.float32)[k]  # sin(k pi/2)
+    return tab
+
+
+def _rotate_back_bits(bits, cos, sin):
+    """bf16 keys rotated by minus the angle of (cos, sin) on the half-split pairs (i, i + d/2): (a, b) ->
+    (a cos + b sin, b cos - a sin). With cos, sin in {0, +-1} every output is +-a or +-b, so the result is exact."""
+    v = O.bf16_to_f64(bits)
+    d2 = v.shape[-1] // 2
+    a, b = v[..., :d2], v[..., d2:]
+    c, s = cos.astype(np.float64), sin.astype(np.float64)
+    out = np.concatenate([a * c + b * s, b * c - a * s], axis=-1)
+    res = O.bf16_bits(out)
+    assert np.array_equal(O.bf16_to_f64(res), out)
+    return res
+
+
+def test_rope_rotates_the_normed_query_with_its_type_table():
+    """The score of a query rotated by R(theta) against key k equals the unrotated query against R(-theta) k. So a
+    layer whose rotary tables hold angles theta (one table per attention type, per row) must equal the same layer
+    with identity tables (cos 1, sin 0) over keys rotated by -theta of their type, V unchanged. This pins that RoPE is
+    applied (to q only), after q_norm (the q_norm weight is not symmetric between the two halves of a pair, so norming
+    the rotated query differs), and with the table of the layer's own type (the two types' angles differ)."""
+    m, w, shape = _tiny_model()
+    d, kv = _distinct_v_inputs(shape)
+    cfg = m.cfg
+    B, half = 3, cfg.head_dim // 2
+    for L in m.layers:
+        assert not np.allclose(L["q_norm"][:half], L["q_norm"][half:])
+    kv.rope = _quarter_turn_tables(B, half, seed=31)
+    ident = np.zeros_like(kv.rope)
+    ident[:, :, 0] = 1.0
+    rot = []
+    for t in range(2):
+        kt = kv.k[t].copy()
+        for b in range(B):
+            kt[b] = _rotate_back_bits(kv.k[t][b], kv.rope[b, t, 0], kv.rope[b, t, 1])
+        rot.append(kt)
+    kv_b = O.SharedKV(k=rot, v=kv.v, lens=kv.lens, rope=ident)
+    kv_c = O.SharedKV(k=kv.k, v=kv.v, lens=kv.lens, rope=ident)
+    x = rng(32).standard_normal(cfg.hidden)
+    for l in range(cfg.n_layer):
+        for b in range(B):
+            a_ = O.decoder_layer(m, l, x, b, kv)
+            b_ = O.decoder_layer(m, l, x, b, kv_b)
+            assert np.allclose(a_, b_, rtol=1e-12, atol=1e-12), (l, b)
+            # control: the rotation does change the layer (the relation is not vacuous) wherever the window holds
+            # more than one key (a single key is returned whatever the query)
+            if kv.lens[1 if cfg.is_full(l) else 0][b] > 1:
+                assert not np.allclose(a_, O.decoder_layer(m, l, x, b, kv_c), rtol=1e-6), (l, b)
+
+
+def test_softmax_scale_multiplies_the_scores():
+    """Doubling every key (exact in bf16) and halving attn_scale leaves each score, and so the layer, bit for bit
+    unchanged (V distinct from K, so V is not doubled); changing attn_scale alone changes the layer."""
+    m, w, shape = _tiny_model()
+    d, kv = _distinct_v_inputs(shape)
+    cfg = m.cfg
+    k2 = [O.bf16_bits(2.0 * O.bf16_to_f64(kv.k[t])) for t in range(2)]
+    kv2 = O.SharedKV(k=k2, v=kv.v, lens=kv.lens, rope=kv.rope)
+    import dataclasses
+    m_half = O.Model(dataclasses.replace(cfg, attn_scale=cfg.attn_scale / 2), w)
+    m_dbl = O.Model(dataclasses.replace(cfg, attn_scale=cfg.attn_scale * 2), w)
+    x = rng(33).standard_normal(cfg.hidden)
+    for l in range(cfg.n_layer):
+        for b in range(3):
+            ref = O.decoder_layer(m, l, x, b, kv)
+            assert np.array_equal(O.decoder_layer(m_half, l, x, b, kv2), ref), (l, b)
+            if kv.lens[1 if cfg.is_full(l) else 0][b] > 1:  # one key: the scale cannot matter
+                assert not np.allclose(O.decoder_layer(m_dbl, l, x, b, kv), ref, rtol=1e-6), (l, b)
+
+
+def test_sandwich_norm_weight_roles():
+    """Which norm weight feeds which branch. With eps = 0: doubling attn_norm's weight doubles q, which q_norm
+    removes exactly, so the layer is bit-identical; doubling ffn_norm's weight doubles the GeGLU inputs (gelu is not
+    homogeneous), so the layer changes; doubling post_attention_norm or post_ffw_norm doubles that branch's
+    contribution. Permuting attn_norm's weight (not a scalar multiple) changes q, so the layer changes."""
+    m, w, shape = _tiny_model(rms_eps=0.0)
+    d, kv = _distinct_v_inputs(shape)
+    x = rng(34).standard_normal(shape.hidden)
+    for l in range(shape.n_layer):
+        L = m.layers[l]
+        for b in range(3):
+            ref = O.decoder_layer(m, l, x, b, kv)
+            for key, same in (("attn_norm", True), ("ffn_norm", False), ("post_attn_norm", False),
+                              ("post_ffw_norm", False)):
+                saved = L[key].copy()
+                L[key] = saved * 2.0
+                got = O.decoder_layer(m, l, x, b, kv)
+                L[key] = saved
+                if same:
+                    assert np.array_equal(got, ref), (l, b, key)
+                else:
+                    assert not np.allclose(got, ref, rtol=1e-6), (l, b, key)
+            if kv.lens[1 if shape.is_full(l) else 0][b] > 1:  # one key: q cannot matter
+                saved = L["attn_norm"].copy()
+                L["attn_norm"] = saved[::-1].copy()
+                assert not np.allclose(O.decoder_layer(m, l, x, b, kv), ref, rtol=1e-6), (l, b)
+                L["attn_norm"] = saved
+
+
+def _step_inputs(shape, batch=3):
+    wl, d, kv = _tiny_inputs(shape, batch=batch)
+    return (d["target_hidden"].numpy().view(np.uint16), d["last_token"].numpy(),
+            d["target_embd"].numpy().view(np.uint16), kv)
+
+
+def test_output_norm_feeds_post_projection_and_the_head():
+    """h = RMSNorm(x, output_norm) feeds both post_projection and the head. With eps = 0, doubling the last layer's
+    scalar doubles x, which the output norm removes exactly: hidden_out, the selected clusters, the ids, the sparse
+    logits and the token are bit-identical. Doubling output_norm's weight doubles h: hidden_out and the sparse
+    logits double exactly (bf16 and fp32 scale exactly by 2), selections and token are unchanged."""
+    m, w, shape = _tiny_model(rms_eps=0.0)
+    th, tok, emb, kv = _step_inputs(shape)
+    ref = O.drafter_step(m, th, tok, emb, kv)
+    m.layers[-1]["scale"] *= 2.0
+    got = O.drafter_step(m, th, tok, emb, kv)
+    m.layers[-1]["scale"] /= 2.0
+    assert np.array_equal(got["hidden_out"], ref["hidden_out"])
+    for b in range(3):
+        for key in ("sel", "ids", "z"):
+            assert np.array_equal(got[key][b], ref[key][b]), (b, key)
+    assert np.array_equal(got["next"], ref["next"])
+    m.out_norm = m.out_norm * 2.0
+    got = O.drafter_step(m, th, tok, emb, kv)
+    assert np.array_equal(O.bf16_to_f64(got["hidden_out"]), 2.0 * O.bf16_to_f64(ref["hidden_out"]))
+    for b in range(3):
+        assert np.array_equal(got["sel"][b], ref["sel"][b]) and np.array_equal(got["ids"][b], ref["ids"][b])
+        assert np.array_equal(got["z"][b], np.float32(2.0) * ref["z"][b])
+    assert np.array_equal(got["next"], ref["next"])
+
+
+def test_embed_scale_multiplies_the_embedded_token():
+    """embed_scale = 2 over the target table E gives the same step, bit for bit, as embed_scale = 1 over the table
+    2E (exact in bf16); embed_scale = 2 alone changes the step."""
+    m, w, shape = _tiny_model()
+    th, tok, emb, kv = _step_inputs(shape)
+    import dataclasses
+    m2 = O.Model(dataclasses.replace(m.cfg, embed_scale=2.0), w)
+    emb2 = O.bf16_bits(2.0 * O.bf16_to_f64(emb))
+    a = O.drafter_step(m2, th, tok, emb, kv)
+    b = O.drafter_step(m, th, tok, emb2, kv)
+    assert np.array_equal(a["hidden_out"], b["hidden_out"]) and np.array_equal(a["next"], b["next"])
+    ref = O.drafter_step(m, th, tok, emb, kv)
+    assert not np.array_equal(a["hidden_out"], ref["hidden_out"])
+
+
+def test_distinct_values_are_read_as_v():
+    """With every key of a row equal (uniform softmax weights) and a distinct V, each head returns the mean of V
+    over the row's key window (np.mean over the window's rows: the window of the layer's type); with the FFN branch
+    zeroed the layer is (x + RMSNorm(W_o [o_0; ..], post_attention_norm)) * s."""
+    m, w, shape = _tiny_model()
+    d, kv = _distinct_v_inputs(shape)
+    cfg = m.cfg
+    for t in range(2):
+        kv.k[t][:] = kv.k[t][:, :, :1]
+    x = rng(35).standard_normal(cfg.hidden)
+    for l in range(cfg.n_layer):
+        L = m.layers[l]
+        L["down"][:] = 0.0
+        t = 1 if cfg.is_full(l) else 0
+        for b in range(3):
+            n = int(kv.lens[t][b])
+            a0 = 0 if t == 1 else n - min(cfg.swa_window, n)
+            mean_v = O.bf16_to_f64(kv.v[t][b, 0, a0:n]).mean(axis=0)
+            o = np.tile(mean_v, cfg.n_head)
+            want = (x + O.rmsnorm(L["o"] @ o, L["post_attn_norm"], cfg.rms_eps)) * L["scale"]
+            assert np.allclose(O.decoder_layer(m, l, x, b, kv), want, rtol=1e-12, atol=1e-12), (l, b)
