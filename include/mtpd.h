@@ -158,6 +158,22 @@ MTPD_API int mtpd_drafter_step(mtpd_handle h, void *stream, void *workspace, int
                       float *logits, int32_t *next_token, uint16_t *hidden_out, int32_t *sel_centroids,
                       int32_t *sparse_ids, float *sparse_logits);
 
+/* mtpd_drafter_step without a workspace argument and without any allocation during the call, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc. Arguments, outputs and results are those of mtpd_drafter_step. The intermediates live in a
+ * file-scope device array of the library (MTPD_NOALLOC_SCRATCH_BYTES, one copy per device, resolved by the first
+ * mtpd_create on that device and held until the process ends). Batches whose workspace (mtpd_workspace_bytes)
+ * exceeds that size are rejected with MTPD_ESHAPE before anything is enqueued; MTPD_EINVAL if no handle was ever
+ * created on the current device. The kernels are launched directly on `stream` (no graph is instantiated) and no
+ * timing records are taken. Every call on one device shares that array and it keeps the last call's contents: calls
+ * that overlap on one device (different streams, or different threads without ordering) race and must not be
+ * issued. */
+#define MTPD_NOALLOC_SCRATCH_BYTES (8u << 20)
+MTPD_API int mtpd_drafter_step_noalloc(mtpd_handle h, void *stream, int32_t batch, const uint16_t *target_hidden,
+                      const int32_t *last_token, const uint16_t *target_embd, const mtpd_shared_kv *kv,
+                      float *logits, int32_t *next_token, uint16_t *hidden_out, int32_t *sel_centroids,
+                      int32_t *sparse_ids, float *sparse_logits);
+
 /* n >= 1 chained drafter steps at the constant position over the same caches ([Guide] section 2(3): within a
  * draft round the last-seen token is the drafter's own; [Explained] "Target Activations": later rounds take the
  * drafter's own post-projected activations). Step i+1 reads step i's hidden_out and next token on the device.
@@ -215,7 +231,7 @@ MTPD_API int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char **names
 /* Message for the last non-OK return on the calling thread ("" if none). */
 MTPD_API const char *mtpd_last_error(void);
 
-/* ABI version: 3 (mtpd_kv gained `first` in 2 and `shared` in 3). */
+/* ABI version: 4 (mtpd_kv gained `first` in 2 and `shared` in 3; mtpd_drafter_step_noalloc in 4). */
 MTPD_API int32_t mtpd_abi_version(void);
 
 #ifdef __cplusplus

@@ -17,7 +17,8 @@ MTPD_MAX_BATCH = 256
 MTPD_MAX_TIMED = 4096
 SYMBOLS = ("mtpd_create", "mtpd_destroy", "mtpd_workspace_bytes", "mtpd_drafter_step", "mtpd_draft_block",
            "mtpd_masked_head", "mtpd_last_error", "mtpd_abi_version", "mtpd_timing_enable", "mtpd_timing_read",
-           "mtpd_draft_block_sampled", "mtpd_sample_head")
+           "mtpd_draft_block_sampled", "mtpd_sample_head", "mtpd_drafter_step_noalloc")
+MTPD_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 u16p = C.POINTER(C.c_uint16)
 i32p = C.POINTER(C.c_int32)
@@ -75,6 +76,9 @@ def lib() -> C.CDLL:
     L.mtpd_drafter_step.argtypes = [vp, vp, vp, C.c_int32, vp, vp, vp, C.POINTER(mtpd_shared_kv), vp, vp, vp, vp, vp,
                                     vp]
     L.mtpd_drafter_step.restype = C.c_int
+    L.mtpd_drafter_step_noalloc.argtypes = [vp, vp, C.c_int32, vp, vp, vp, C.POINTER(mtpd_shared_kv), vp, vp, vp, vp,
+                                            vp, vp]
+    L.mtpd_drafter_step_noalloc.restype = C.c_int
     L.mtpd_draft_block.argtypes = [vp, vp, vp, C.c_int32, C.c_int32, vp, vp, vp, C.POINTER(mtpd_shared_kv), vp, vp,
                                    vp]
     L.mtpd_draft_block.restype = C.c_int

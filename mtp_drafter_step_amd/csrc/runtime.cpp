@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -38,7 +39,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+// Scratch memory of the allocation-free entry point (mtpd_drafter_step_noalloc): a file-scope device array, one copy
+// per device, held until the process ends. In host code the name `scratch` is a host-side stand-in, never a device
+// address: host code uses only the per-device address resolved by scratch_setup().
+constexpr size_t kScratchBytes = MTPD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// While set on this thread, the call in progress launches its kernels directly on the caller's stream (no graph is
+// captured or instantiated, both of which allocate) and takes no timing records (their events are created lazily).
+thread_local bool t_direct = false;
 
 constexpr int kGraphCache = 32;
 constexpr int kChains = 4;  // maximum sub-batches (make_chains currently uses one: graph replays on separate streams
@@ -202,7 +217,7 @@ int check_ptr(const void* p, const char* name) {
 // Take the next timing record for a launch labelled `name` (no-op unless timing is on; launches beyond
 // MTPD_MAX_TIMED records are not recorded).
 int timing_mark(const mtpd_handle_s* h, const char* name) {
-  if (!h->timing || h->n_timed >= MTPD_MAX_TIMED) return MTPD_OK;
+  if (t_direct || !h->timing || h->n_timed >= MTPD_MAX_TIMED) return MTPD_OK;
   const size_t i = (size_t)h->n_timed;
   if (h->timing_ev.size() < 2 * (i + 1)) {
     for (int j = 0; j < 2; ++j) {
@@ -627,7 +642,7 @@ template <typename Body>
 int run_call(mtpd_handle_s* h, hipStream_t s, const CallKey& key, const Chains& ch, Body body) {
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &st) != hipSuccess) st = hipStreamCaptureStatusActive;
-  if (!h->use_graphs || h->timing || st != hipStreamCaptureStatusNone) return run_chains(h, s, ch, body);
+  if (t_direct || !h->use_graphs || h->timing || st != hipStreamCaptureStatusNone) return run_chains(h, s, ch, body);
   hipGraphExec_t exec[kChains];
   for (int c = 0; c < ch.n; ++c) CHECK(chain_graph(h, key, c, body, &exec[c]));
   if (ch.n == 1) {
@@ -638,6 +653,28 @@ int run_call(mtpd_handle_s* h, hipStream_t s, const CallKey& key, const Chains& 
     LAUNCH(hipGraphLaunch(exec[c], cs));
     return MTPD_OK;
   });
+}
+
+// Resolve the current device's copy of `scratch` (once per device; called by mtpd_create with the device current).
+int scratch_setup() {
+  int dev = -1;
+  LAUNCH(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MTPD_EUNSUP, "device %d: at most %d devices are supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_dev[dev]) return MTPD_OK;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) return fail(MTPD_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  g_scratch_dev[dev] = ptr;
+  return MTPD_OK;
+}
+
+// The current device's scratch address, or nullptr if no handle was created on this device.
+void* scratch_lookup() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  return g_scratch_dev[dev];
 }
 
 CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs, const mtpd::RowWindows* win,
@@ -668,7 +705,7 @@ CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs
 
 extern "C" {
 
-int32_t mtpd_abi_version(void) { return 3; }
+int32_t mtpd_abi_version(void) { return 4; }
 
 const char* mtpd_last_error(void) { return g_last_error.c_str(); }
 
@@ -701,6 +738,7 @@ int mtpd_create(const mtpd_config* cfg, const mtpd_weights* w, int32_t max_batch
       CHECK(check_ptr(ps[i], nm));
     }
   }
+  CHECK(scratch_setup());  // the allocation-free entry point's scratch on this device (after all host-side checks)
   if (!dense) {
     // token_ordering must list every token once ([Inventory] "GGUF / converter layout", verification)
     std::vector<int32_t> ord((size_t)cfg->vocab);
@@ -800,6 +838,27 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
       KLAUNCH(h, "final", mtpd::launch_final(cs, Bc, key_slots(c), at<uint64_t>(wsc, p.keys), next_token + b0, nullptr, 0));
       return MTPD_OK;
   });
+}
+
+int mtpd_drafter_step_noalloc(mtpd_handle h, void* stream, int32_t batch, const uint16_t* target_hidden,
+                              const int32_t* last_token, const uint16_t* target_embd, const mtpd_shared_kv* kv,
+                              float* logits, int32_t* next_token, uint16_t* hidden_out, int32_t* sel_centroids,
+                              int32_t* sparse_ids, float* sparse_logits) {
+  g_last_error.clear();
+  if (!h) return fail(MTPD_EINVAL, "handle is NULL");
+  void* ws = scratch_lookup();
+  if (!ws) return fail(MTPD_EINVAL, "no handle was created on the current device, so its scratch is not set up");
+  const size_t need = mtpd_workspace_bytes(h, batch);
+  if (need == 0) return fail(MTPD_ESHAPE, "batch %d outside [1, max_batch=%d]", batch, h->max_batch);
+  if (need > kScratchBytes)
+    return fail(MTPD_ESHAPE, "batch %d needs %zu bytes of scratch; the allocation-free entry point holds %zu", batch,
+                need, kScratchBytes);
+  struct Direct {
+    Direct() { t_direct = true; }
+    ~Direct() { t_direct = false; }
+  } direct;
+  return mtpd_drafter_step(h, stream, ws, batch, target_hidden, last_token, target_embd, kv, logits, next_token,
+                           hidden_out, sel_centroids, sparse_ids, sparse_logits);
 }
 
 int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch, int32_t n,

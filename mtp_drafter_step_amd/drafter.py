@@ -150,6 +150,18 @@ class Drafter:
             _ptr(o.get("ids")), _ptr(o.get("z"))))
         return o
 
+    def drafter_step_noalloc(self, target_hidden, last_token, target_embd, kv: SharedKV,
+                             out: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+        """mtpd_drafter_step_noalloc into caller-allocated outputs `out` (the keys drafter_step returns: next,
+        hidden_out, optionally logits, sel, ids, z); allocates nothing."""
+        B = int(target_hidden.shape[0])
+        s, keep = kv.struct()
+        abi.check(abi.lib().mtpd_drafter_step_noalloc(
+            self.handle, _stream(), B, _ptr(target_hidden), _ptr(last_token), _ptr(target_embd), C.byref(s),
+            _ptr(out.get("logits")), _ptr(out["next"]), _ptr(out["hidden_out"]), _ptr(out.get("sel")),
+            _ptr(out.get("ids")), _ptr(out.get("z"))))
+        return out
+
     def draft_block(self, n: int, target_hidden, last_token, target_embd, kv: SharedKV, want_logits: bool = False,
                     out: Optional[Dict[str, torch.Tensor]] = None,
                     workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
