@@ -41,7 +41,7 @@ KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k
                "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip",
                "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip", "k_gemm": "k_gemm.hip",
                "k_group": "k_head.hip", "k_head_grouped": "k_head.hip", "k_topk_rows": "k_head.hip",
-               "k_rownorm": "k_gemm.hip", "k_merge": "k_gemm.hip", "k_token": "k_gemm.hip"}
+               "k_rownorm": "k_gemm.hip", "k_merge": "k_gemm.hip", "k_token": "k_gemm.hip", "k_team": "k_team.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 512 << 20
 
@@ -55,7 +55,9 @@ SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma"
                "token": "k_token", "rownorm": "k_rownorm", "post_norm": "k_rownorm", "attn_merge": "k_merge",
                "pre_gemm": "k_gemm", "qproj_gemm": "k_gemm", "o_proj_gemm": "k_gemm", "ffn_gemm": "k_gemm",
                "down_gemm": "k_gemm", "post_gemm": "k_gemm", "scores_gemm": "k_gemm",
-               "head_select": "k_topk_rows", "head_group": "k_group", "head_grouped": "k_head_grouped"}
+               "head_select": "k_topk_rows", "head_group": "k_group", "head_grouped": "k_head_grouped",
+               # the persistent kernel: every step of a call in one launch
+               "team": "k_team"}
 
 
 def site_kernel(site, shape, shared=False):
@@ -72,7 +74,8 @@ def site_kernel(site, shape, shared=False):
 def source_digest(kernel: str) -> str:
     """sha256[:16] of the sources that define `kernel` (its file plus device.h and kernels.h)."""
     h = hashlib.sha256()
-    for name in ("device.h", "kernels.h", KERNEL_FILE.get(kernel, "k_layers.hip")):
+    extra = ("attn_mfma.h",) if kernel in ("k_team", "k_attn_mfma") else ()
+    for name in ("device.h", "kernels.h", *extra, KERNEL_FILE.get(kernel, "k_layers.hip")):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -325,7 +328,8 @@ def run_bench(args):
         e = per_kernel.setdefault(k, {"launches": 0, "total_ms": 0.0, "bytes": 0.0, "sites": []})
         e["launches"] += len(v)
         e["total_ms"] += float(np.sum(v))
-        e["bytes"] += len(v) * site_bytes(site, shape, B, lens, u_mean, shared=wl.shared_kv)
+        e["bytes"] += len(v) * (sbytes * n if site == "team" else site_bytes(site, shape, B, lens, u_mean,
+                                                                              shared=wl.shared_kv))
         fl = site_flops(site, shape, lens, wl.shared_kv)
         if fl is not None:
             e["flops"] = e.get("flops", 0.0) + len(v) * fl

@@ -213,6 +213,27 @@ MTPD_API int mtpd_draft_block_sampled(mtpd_handle h, void *stream, void *workspa
 MTPD_API int mtpd_sample_head(mtpd_handle h, void *stream, void *workspace, int32_t m, const float *hidden,
                      float temperature, const float *uniforms, int32_t *token, float *prob, float *logits);
 
+/* Handle options (set after mtpd_create; each change discards the handle's captured graphs). Values:
+ *   MTPD_OPT_GRAPHS      1 (default): replay each call from a captured HIP graph; 0: launch every kernel directly.
+ *   MTPD_OPT_PERSISTENT  1 (default): calls of at most 16 rows on per-row K = V caches of the E2B / E4B shapes
+ *                        (hidden 256, 4 heads of 256 over one kv head, FFN 1024, 2048 clusters of 128, top 32, <= 4
+ *                        layers) on a 256-CU gfx950 run as one launch of the persistent drafter kernel, whose blocks
+ *                        hand values to each other inside each XCD; it needs every CU free for the launch (a wait
+ *                        that cannot finish gives up after a bounded time and is reported by mtpd_fault_status).
+ *                        0: the per-stage kernels.
+ *   MTPD_OPT_DENSE_PATH  0 (default): dense stages by batch size (fused small-batch kernels below 32 rows, matrix-core
+ *                        GEMMs from 32 rows); 1: always the small-batch kernels; 2: always the GEMMs.
+ *   MTPD_OPT_ATTN_VALU   0 (default); 1: the vector-ALU attention kernel for every shape.
+ * Returns MTPD_OK or MTPD_EINVAL (unknown option or value). */
+enum { MTPD_OPT_GRAPHS = 1, MTPD_OPT_PERSISTENT = 2, MTPD_OPT_DENSE_PATH = 3, MTPD_OPT_ATTN_VALU = 4 };
+MTPD_API int mtpd_set_option(mtpd_handle h, int32_t option, int32_t value);
+
+/* Status of the persistent drafter kernel's launches on this handle and on the allocation-free entry point's scratch
+ * of the current device: 0 if every launch so far finished its waits normally, else bit 0 (a wait gave up, the
+ * launch's outputs are undefined), bit 1 (a block ran on another XCD than its team's) and in bits 8-15 one plus the
+ * stage id of the first wait that gave up. Waits for the device (a blocking copy); clear != 0 resets the status. */
+MTPD_API int32_t mtpd_fault_status(mtpd_handle h, int32_t clear);
+
 /* Kernel timing, a measurement aid outside the method. While enabled on a handle, drafter_step, draft_block and
  * masked_head launch their kernels directly on the caller's stream (captured graphs are not replayed) and attach
  * to each launch a pair of HIP events that the runtime records at the kernel's start and end. Enabling clears
@@ -231,7 +252,8 @@ MTPD_API int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char **names
 /* Message for the last non-OK return on the calling thread ("" if none). */
 MTPD_API const char *mtpd_last_error(void);
 
-/* ABI version: 4 (mtpd_kv gained `first` in 2 and `shared` in 3; mtpd_drafter_step_noalloc in 4). */
+/* ABI version: 5 (mtpd_kv gained `first` in 2 and `shared` in 3; mtpd_drafter_step_noalloc in 4; options and
+ * the persistent kernel's status in 5). */
 MTPD_API int32_t mtpd_abi_version(void);
 
 #ifdef __cplusplus

@@ -2,7 +2,8 @@
 // stream; every launcher returns the hipError_t of its launch.
 //
 // Activations are fp32 throughout; stored tensors (weights, caches, embeddings, target hidden) are bf16.
-// Kernels never synchronise with each other inside a launch: every cross-block dependency is a kernel boundary.
+// Kernels never synchronise with each other inside a launch (every cross-block dependency is a kernel boundary),
+// except the persistent drafter kernel at the end of this file.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -72,7 +73,8 @@ hipError_t launch_qproj(hipStream_t s, int B, int H, int QD, Residual res, const
 // nsplit > 1: unnormalised partials (pacc, pml) for launch_attn_merge.
 // Whether launch_attn takes the multi-query kernel (a cache shared by the rows, head_dim 256, V = K): its key
 // splits then cover the union of the rows' windows.
-bool attn_uses_multi_query(bool shared, int hd, bool same_v);
+// valu: the vector-ALU kernel for every shape (the handle option MTPD_OPT_ATTN_VALU).
+bool attn_uses_multi_query(bool valu, bool shared, int hd, bool same_v);
 
 // Multi-query attention of rows sharing one cache (head_dim 256, V = K): same inputs and outputs as launch_attn
 // with scale_log2 = scale * log2(e).
@@ -80,7 +82,7 @@ hipError_t launch_attn_shared(hipStream_t s, int B, int nh, int nkv, const float
                               const float* rope, int type, const uint16_t* K, int cap, const RowWindows& win,
                               int nsplit, float scale_log2, float* pacc, float* pml, float* o);
 
-hipError_t launch_attn(hipStream_t s, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
+hipError_t launch_attn(hipStream_t s, bool valu, int B, int nh, int nkv, int hd, const float* q, const uint16_t* qnorm,
                        float eps, const float* rope, int type, const uint16_t* K, const uint16_t* V, int cap,
                        const RowWindows& win, int nsplit, float scale, float* pacc, float* pml, float* o);
 
@@ -177,5 +179,74 @@ hipError_t launch_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const 
 
 // tok_out[b] = the step's input token of row b from the token source (recorded where it asks), clamped to [0, V).
 hipError_t launch_token(hipStream_t s, int B, int V, TokenSource ts, int32_t* tok_out);
+
+// ---- persistent drafter kernel (k_team.hip)
+//
+// One launch runs n whole drafter steps for up to kTeamMaxBatch rows. The grid is one block per CU of the 8 XCDs
+// (256 blocks of 256 threads); the 32 blocks of XCD t form team t and compute rows t and t + 8. Inside a team,
+// every value one block hands to another is a 64-bit word (fp32 or packed bits, 32-bit tag) stored into the XCD's
+// L2 and polled with device-coherent loads; tags are unique per (launch, step, stage), so the exchange buffers never
+// need clearing. Every wait is bounded: a wait that runs out sets `status` and the launch finishes with undefined
+// outputs instead of hanging.
+
+constexpr int kTeamMaxBatch = 16;
+constexpr int kTeamMaxLayers = 4;
+constexpr int kTeamBlocks = 256;
+// status bits
+constexpr uint32_t kTeamTimeout = 1u;    // a wait ran out (the first stage id that did is in status[1] + 1)
+constexpr uint32_t kTeamMisplaced = 2u;  // a block found itself on another XCD than its team's
+
+struct TeamLayer {
+  const uint16_t *q, *q_norm, *o, *attn_norm, *post_attn_norm, *ffn_norm, *post_ffw_norm, *gate, *up, *down;
+  float scale;
+};
+
+struct TeamArgs {
+  const uint16_t* wpk;  // the dense weights packed by team_pack_weights (one base pointer: compile-time offsets)
+  float scale[kTeamMaxLayers];  // layer_output_scale
+  const uint16_t* head_sorted;
+  const int32_t* ordering;
+  const uint16_t* th;    // [B][Bb] step-0 hidden input
+  const int32_t* tok;    // [B] step-0 token
+  const uint16_t* temb;  // [V][Bb]
+  const uint16_t* kc[2];  // per-row caches [B][1][cap][256], K = V (0 sliding, 1 full)
+  int32_t cap[2];
+  int32_t win_start[2][kTeamMaxBatch], win_count[2][kTeamMaxBatch];
+  const float* rope;  // [B][2][2][128]
+  float* logits;      // [n][B][V] or null
+  int32_t* tokens;    // tokens[b * tok_stride + i] = step i's token (null: not stored)
+  int32_t tok_stride;
+  int32_t* next;          // [B] the last step's token (null: not stored)
+  uint16_t* hidden_out;   // [B][Bb] of the last step
+  int32_t* sel;           // [B][32] (null: not stored)
+  int32_t* ids;           // [B][32][128] (null: not stored)
+  float* z;               // [B][32][128] (null: not stored)
+  int32_t B, n_steps, n_layer, Bb, V;
+  uint32_t full_mask;
+  float eps, scale_log2, escale;
+  uint64_t* xch;     // exchange words, team_arena_words() per team
+  uint32_t* epoch;   // [kTeamBlocks] per-block launch counters (zero at creation)
+  uint32_t* status;  // [2]
+};
+
+// The persistent kernel reads the dense weights (every layer's q / norms / o / gate / up / down, pre_proj,
+// post_proj, output_norm, centroids) from one buffer of team_weights_bytes(Bb); team_pack_weights fills it with
+// device-to-device copies on stream s.
+size_t team_weights_bytes(int Bb);
+hipError_t team_pack_weights(hipStream_t s, uint16_t* dst, const TeamLayer* L, int n_layer, const uint16_t* pre,
+                             const uint16_t* post, const uint16_t* out_norm, const uint16_t* cen, int Bb);
+// Bytes of the arena (exchange words, epochs, status) the persistent kernel needs; must be zeroed once before the
+// first launch and then only used by this kernel.
+size_t team_arena_bytes();
+// Point a's exchange words, epochs and status into an arena of team_arena_bytes(); the status words sit at byte
+// team_status_offset() of it.
+void team_bind_arena(TeamArgs& a, void* arena);
+size_t team_status_offset();
+// Whether a backbone width has a persistent-kernel instance.
+bool team_backbone_ok(int Bb);
+hipError_t launch_team(hipStream_t s, const TeamArgs& a);
+#ifdef MTPD_TEAM_TRACE
+hipError_t team_trace_read(uint64_t* host);  // measurement builds: the last launch's stage timeline
+#endif
 
 }  // namespace mtpd

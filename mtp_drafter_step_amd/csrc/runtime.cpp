@@ -87,6 +87,14 @@ struct mtpd_handle_s {
   int32_t vsc;
   uint16_t* head_sorted = nullptr;  // token_embd rows in cluster order (owned; built by mtpd_create)
   bool use_graphs = true;
+  // the persistent drafter kernel (k_team.hip): whether the configuration has an instance, whether it is enabled,
+  // and its arena (exchange words, per-block epochs, status), zeroed at creation
+  bool team_shape = false;
+  bool team_enabled = true;  // MTPD_OPT_PERSISTENT
+  int dense_path = 0;        // MTPD_OPT_DENSE_PATH: 0 by batch size, 1 fused small-batch kernels, 2 matrix-core GEMMs
+  bool attn_valu = false;    // MTPD_OPT_ATTN_VALU
+  uint8_t* team_arena = nullptr;
+  uint16_t* team_weights = nullptr;  // the dense weights packed in the persistent kernel's layout (owned)
   hipStream_t cap_stream = nullptr;
   GraphEntry graphs[kGraphCache];
   uint64_t tick = 0;
@@ -342,7 +350,7 @@ int run_step_small(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& 
       cur ^= 1;
     }
     KLAUNCH(h, "qproj", mtpd::launch_qproj(s, B, H, QD, rq, L.attn_norm, c.rms_eps, L.attn_q, q));
-    KLAUNCH(h, type ? "attn_full" : "attn_sliding", mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
+    KLAUNCH(h, type ? "attn_full" : "attn_sliding", mtpd::launch_attn(s, h->attn_valu, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
                              cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale,
                              at<float>(ws, p.pacc), at<float>(ws, p.pml), o));
     // o_proj in QD / 256 partials, merging the split attention partials on the way in
@@ -365,14 +373,13 @@ int run_step_small(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& 
   return run_head(h, s, ws, p, B, at<float>(ws, p.h), logits, sel_out, ids_out, z_out);
 }
 
-// Batches of at least this many rows take the matrix-core path for the dense stages (MTPD_GEMM_PATH=1 / 0 forces
-// it on / off, read at each call).
+// Batches of at least this many rows take the matrix-core path for the dense stages (the handle option
+// MTPD_OPT_DENSE_PATH forces either path).
 constexpr int kGemmRows = 32;
 
-bool use_gemm_path(int B) {
-  const char* e = getenv("MTPD_GEMM_PATH");
-  if (e && e[0] == '1') return true;
-  if (e && e[0] == '0') return false;
+bool use_gemm_path(const mtpd_handle_s* h, int B) {
+  if (h->dense_path == 1) return false;
+  if (h->dense_path == 2) return true;
   return B >= kGemmRows;
 }
 
@@ -426,7 +433,7 @@ int run_step_gemm(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p
     KLAUNCH(h, "qproj_gemm", mtpd::launch_gemm(s, 0, B, QD, H, u, nullptr, nullptr, nullptr, 0, 0.f, L.attn_q, nullptr,
                                                q, nullptr, 1, fill_slice(4 * l)));
     KLAUNCH(h, type ? "attn_full" : "attn_sliding",
-            mtpd::launch_attn(s, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
+            mtpd::launch_attn(s, h->attn_valu, B, c.n_head, c.n_kv_head, c.head_dim, q, L.attn_q_norm, c.rms_eps, kv->rope, type,
                               cache.k, cache.v, cache.cap, win[type], nsplit[type], c.attn_scale, at<float>(ws, p.pacc),
                               at<float>(ws, p.pml), o));
     if (nsplit[type] > 1)
@@ -466,7 +473,7 @@ int run_step(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p, int
              mtpd::TokenSource ts, const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win,
              const int* nsplit, float* logits, uint16_t* hidden_out, int32_t* sel_out, int32_t* ids_out,
              float* z_out) {
-  if (use_gemm_path(B))
+  if (use_gemm_path(h, B))
     return run_step_gemm(h, s, ws, p, B, th, ts, temb, kv, win, nsplit, logits, hidden_out, sel_out, ids_out, z_out);
   return run_step_small(h, s, ws, p, B, th, ts, temb, kv, win, nsplit, logits, hidden_out, sel_out, ids_out, z_out);
 }
@@ -501,7 +508,7 @@ int nsplit_multi_query(const mtpd::RowWindows& win, int B, int G, int nkv) {
 
 int split_count(const mtpd_handle_s* h, const mtpd_kv& kv, const mtpd::RowWindows& win, int B) {
   const mtpd_config& c = h->cfg;
-  if (mtpd::attn_uses_multi_query(kv.shared != 0, c.head_dim, kv.v == kv.k))
+  if (mtpd::attn_uses_multi_query(h->attn_valu, kv.shared != 0, c.head_dim, kv.v == kv.k))
     return nsplit_multi_query(win, B, c.n_head / c.n_kv_head, c.n_kv_head);
   return nsplit_for(win, B, c.n_kv_head);
 }
@@ -655,6 +662,10 @@ int run_call(mtpd_handle_s* h, hipStream_t s, const CallKey& key, const Chains& 
   });
 }
 
+// Bytes reserved for the persistent kernel's arena (at the start of the allocation-free entry point's scratch and of
+// each handle's own arena allocation).
+size_t team_arena_span() { return align_up(mtpd::team_arena_bytes()); }
+
 // Resolve the current device's copy of `scratch` (once per device; called by mtpd_create with the device current).
 int scratch_setup() {
   int dev = -1;
@@ -663,8 +674,12 @@ int scratch_setup() {
   std::lock_guard<std::mutex> g(g_scratch_mu);
   if (g_scratch_dev[dev]) return MTPD_OK;
   void* ptr = nullptr;
-  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
   if (e != hipSuccess || !ptr) return fail(MTPD_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  // the persistent kernel's arena at the start of the array must start out zero (epochs, tags, status)
+  e = hipMemset(ptr, 0, team_arena_span());
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(MTPD_EHIP, "clearing the scratch arena: %s", hipGetErrorString(e));
   g_scratch_dev[dev] = ptr;
   return MTPD_OK;
 }
@@ -675,6 +690,76 @@ void* scratch_lookup() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> g(g_scratch_mu);
   return g_scratch_dev[dev];
+}
+
+// The persistent kernel's shapes: the E2B / E4B drafters (hidden 256, 4 heads of 256 over one K = V head, FFN 1024,
+// 2048 clusters of 128 tokens, top 32, at most 4 layers) on a gfx950 with 256 CUs (8 XCDs of 32).
+bool team_config_ok(const mtpd_config& c) {
+  return c.hidden == 256 && c.n_head == 4 && c.n_kv_head == 1 && c.head_dim == 256 && c.ffn == 1024 &&
+         c.n_layer >= 1 && c.n_layer <= mtpd::kTeamMaxLayers && c.n_centroids == 2048 && c.top_k == 32 &&
+         c.vocab == 2048 * 128 && mtpd::team_backbone_ok(c.backbone);
+}
+
+bool team_device_ok() {
+  int dev = -1;
+  hipDeviceProp_t p;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess) return false;
+  return p.multiProcessorCount == mtpd::kTeamBlocks && std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+}
+
+// The arena the persistent kernel uses on this call: the allocation-free entry point's, else the handle's.
+thread_local uint8_t* t_arena = nullptr;
+
+bool team_call_ok(const mtpd_handle_s* h, int B, const mtpd_shared_kv* kv) {
+  return h->team_shape && h->team_enabled && B <= mtpd::kTeamMaxBatch && !kv->sliding.shared && !kv->full.shared &&
+         kv->sliding.v == kv->sliding.k && kv->full.v == kv->full.k;
+}
+
+// n drafter steps of B rows in one launch of the persistent kernel. Step i's token goes to tokens[b * n + i] and the
+// last step's to next[b] (each when set); logits [n][B][V]; sel / ids / z of the last step.
+int run_team(const mtpd_handle_s* h, hipStream_t s, int B, int n, const uint16_t* th, const int32_t* tok,
+             const uint16_t* temb, const mtpd_shared_kv* kv, const mtpd::RowWindows* win, float* logits,
+             int32_t* tokens, int32_t* next, uint16_t* hidden_out, int32_t* sel, int32_t* ids, float* z) {
+  const mtpd_config& c = h->cfg;
+  mtpd::TeamArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int l = 0; l < c.n_layer; ++l) a.scale[l] = h->layers[l].layer_output_scale;
+  a.wpk = h->team_weights;
+  a.head_sorted = h->head_sorted;
+  a.ordering = h->w.token_ordering;
+  a.th = th;
+  a.tok = tok;
+  a.temb = temb;
+  a.kc[0] = kv->sliding.k;
+  a.kc[1] = kv->full.k;
+  a.cap[0] = kv->sliding.cap;
+  a.cap[1] = kv->full.cap;
+  for (int t = 0; t < 2; ++t)
+    for (int b = 0; b < B; ++b) {
+      a.win_start[t][b] = win[t].start[b];
+      a.win_count[t][b] = win[t].count[b];
+    }
+  a.rope = kv->rope;
+  a.logits = logits;
+  a.tokens = tokens;
+  a.tok_stride = n;
+  a.next = next;
+  a.hidden_out = hidden_out;
+  a.sel = sel;
+  a.ids = ids;
+  a.z = z;
+  a.B = B;
+  a.n_steps = n;
+  a.n_layer = c.n_layer;
+  a.Bb = c.backbone;
+  a.V = c.vocab;
+  a.full_mask = c.full_attn_layers;
+  a.eps = c.rms_eps;
+  a.scale_log2 = c.attn_scale * 1.4426950408889634f;
+  a.escale = c.embed_scale;
+  mtpd::team_bind_arena(a, t_arena ? t_arena : h->team_arena);
+  KLAUNCH(h, "team", mtpd::launch_team(s, a));
+  return MTPD_OK;
 }
 
 CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs, const mtpd::RowWindows* win,
@@ -705,7 +790,7 @@ CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs
 
 extern "C" {
 
-int32_t mtpd_abi_version(void) { return 4; }
+int32_t mtpd_abi_version(void) { return 5; }
 
 const char* mtpd_last_error(void) { return g_last_error.c_str(); }
 
@@ -777,8 +862,32 @@ int mtpd_create(const mtpd_config* cfg, const mtpd_weights* w, int32_t max_batch
   hh->w.layers = nullptr;
   hh->max_batch = max_batch;
   hh->vsc = dense ? 0 : cfg->vocab / cfg->n_centroids;
-  const char* g = getenv("MTPD_GRAPHS");
-  hh->use_graphs = !(g && g[0] == '0');
+  hh->team_shape = team_config_ok(*cfg) && team_device_ok();
+  if (hh->team_shape) {
+    if (hipMalloc(&hh->team_arena, team_arena_span()) != hipSuccess) {
+      mtpd_destroy(hh);
+      return fail(MTPD_ENOMEM, "no device memory for the persistent kernel's arena (%zu bytes)", team_arena_span());
+    }
+    if (hipMalloc(&hh->team_weights, mtpd::team_weights_bytes(cfg->backbone)) != hipSuccess) {
+      mtpd_destroy(hh);
+      return fail(MTPD_ENOMEM, "no device memory for the persistent kernel's packed weights (%zu bytes)",
+                  mtpd::team_weights_bytes(cfg->backbone));
+    }
+    mtpd::TeamLayer tl[mtpd::kTeamMaxLayers];
+    for (int l = 0; l < cfg->n_layer; ++l) {
+      const mtpd_layer& L = hh->layers[l];
+      tl[l] = mtpd::TeamLayer{L.attn_q, L.attn_q_norm, L.attn_output, L.attn_norm, L.post_attention_norm,
+                              L.ffn_norm, L.post_ffw_norm, L.ffn_gate, L.ffn_up, L.ffn_down, L.layer_output_scale};
+    }
+    hipError_t e = mtpd::team_pack_weights(nullptr, hh->team_weights, tl, cfg->n_layer, w->pre_proj, w->post_proj,
+                                           w->output_norm, w->centroids, cfg->backbone);
+    if (e == hipSuccess) e = hipMemset(hh->team_arena, 0, team_arena_span());
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      mtpd_destroy(hh);
+      return fail(MTPD_EHIP, "clearing the persistent kernel's arena: %s", hipGetErrorString(e));
+    }
+  }
   *out = hh;
   return MTPD_OK;
 }
@@ -795,6 +904,8 @@ void mtpd_destroy(mtpd_handle h) {
   if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
   for (hipEvent_t e : h->timing_ev) (void)hipEventDestroy(e);
   if (h->head_sorted) (void)hipFree(h->head_sorted);
+  if (h->team_arena) (void)hipFree(h->team_arena);
+  if (h->team_weights) (void)hipFree(h->team_weights);
   delete h;
 }
 
@@ -817,6 +928,9 @@ int mtpd_drafter_step(mtpd_handle h, void* stream, void* workspace, int32_t batc
   CHECK(check_ptr(hidden_out, "hidden_out"));
   if (logits) CHECK(check_ptr(logits, "logits"));
   CHECK(check_head_outputs(h, sel_centroids, sparse_ids, sparse_logits));
+  if (team_call_ok(h, batch, kv))
+    return run_team(h, static_cast<hipStream_t>(stream), batch, 1, target_hidden, last_token, target_embd, kv, win,
+                    logits, nullptr, next_token, hidden_out, sel_centroids, sparse_ids, sparse_logits);
   const Chains ch = make_chains(batch);
   const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
   const CallKey key = make_key(1, batch, 1,
@@ -846,17 +960,27 @@ int mtpd_drafter_step_noalloc(mtpd_handle h, void* stream, int32_t batch, const 
                               int32_t* sparse_ids, float* sparse_logits) {
   g_last_error.clear();
   if (!h) return fail(MTPD_EINVAL, "handle is NULL");
-  void* ws = scratch_lookup();
-  if (!ws) return fail(MTPD_EINVAL, "no handle was created on the current device, so its scratch is not set up");
+  uint8_t* sc = static_cast<uint8_t*>(scratch_lookup());
+  if (!sc) return fail(MTPD_EINVAL, "no handle was created on the current device, so its scratch is not set up");
+  // the persistent kernel's arena first, then the workspace of the other paths
+  void* ws = sc + team_arena_span();
+  const size_t room = kScratchBytes - team_arena_span();
   const size_t need = mtpd_workspace_bytes(h, batch);
   if (need == 0) return fail(MTPD_ESHAPE, "batch %d outside [1, max_batch=%d]", batch, h->max_batch);
-  if (need > kScratchBytes)
+  if (need > room)
     return fail(MTPD_ESHAPE, "batch %d needs %zu bytes of scratch; the allocation-free entry point holds %zu", batch,
-                need, kScratchBytes);
+                need, room);
   struct Direct {
-    Direct() { t_direct = true; }
-    ~Direct() { t_direct = false; }
-  } direct;
+    uint8_t* saved;
+    explicit Direct(uint8_t* arena) : saved(t_arena) {
+      t_direct = true;
+      t_arena = arena;
+    }
+    ~Direct() {
+      t_direct = false;
+      t_arena = saved;
+    }
+  } direct(sc);
   return mtpd_drafter_step(h, stream, ws, batch, target_hidden, last_token, target_embd, kv, logits, next_token,
                            hidden_out, sel_centroids, sparse_ids, sparse_logits);
 }
@@ -873,6 +997,9 @@ int mtpd_draft_block(mtpd_handle h, void* stream, void* workspace, int32_t batch
   if (!tokens) return fail(MTPD_EINVAL, "tokens is NULL");
   CHECK(check_ptr(hidden_out, "hidden_out"));
   if (logits) CHECK(check_ptr(logits, "logits"));
+  if (team_call_ok(h, batch, kv))
+    return run_team(h, static_cast<hipStream_t>(stream), batch, n, target_hidden, last_token, target_embd, kv, win,
+                    logits, tokens, nullptr, hidden_out, nullptr, nullptr, nullptr);
   const Chains ch = make_chains(batch);
   const Plan p = make_plan(h->cfg, ch.bmax, h->vsc);
   const mtpd_config& c = h->cfg;
@@ -1052,6 +1179,63 @@ int mtpd_sample_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
       return run_sample(h, cs, wsc, p, Bc, lc, temperature, uniforms + b0, token + b0, prob ? prob + b0 : nullptr, 1);
   });
 }
+
+int mtpd_set_option(mtpd_handle h, int32_t option, int32_t value) {
+  g_last_error.clear();
+  if (!h) return fail(MTPD_EINVAL, "handle is NULL");
+  switch (option) {
+    case MTPD_OPT_GRAPHS:
+      if (value != 0 && value != 1) return fail(MTPD_EINVAL, "MTPD_OPT_GRAPHS takes 0 or 1");
+      h->use_graphs = value != 0;
+      break;
+    case MTPD_OPT_PERSISTENT:
+      if (value != 0 && value != 1) return fail(MTPD_EINVAL, "MTPD_OPT_PERSISTENT takes 0 or 1");
+      h->team_enabled = value != 0;
+      break;
+    case MTPD_OPT_DENSE_PATH:
+      if (value < 0 || value > 2) return fail(MTPD_EINVAL, "MTPD_OPT_DENSE_PATH takes 0, 1 or 2");
+      h->dense_path = value;
+      break;
+    case MTPD_OPT_ATTN_VALU:
+      if (value != 0 && value != 1) return fail(MTPD_EINVAL, "MTPD_OPT_ATTN_VALU takes 0 or 1");
+      h->attn_valu = value != 0;
+      break;
+    default:
+      return fail(MTPD_EINVAL, "unknown option %d", option);
+  }
+  // captured graphs baked in the previous choice
+  for (auto& e : h->graphs)
+    if (e.exec) {
+      (void)hipGraphExecDestroy(e.exec);
+      e.exec = nullptr;
+    }
+  return MTPD_OK;
+}
+
+int32_t mtpd_fault_status(mtpd_handle h, int32_t clear) {
+  g_last_error.clear();
+  if (!h) return fail(MTPD_EINVAL, "handle is NULL");
+  uint32_t st = 0;
+  uint8_t* arenas[2] = {h->team_arena, static_cast<uint8_t*>(scratch_lookup())};
+  for (uint8_t* ar : arenas) {
+    if (!ar) continue;
+    uint32_t w[2] = {0, 0};
+    uint32_t* dev = reinterpret_cast<uint32_t*>(ar + mtpd::team_status_offset());
+    LAUNCH(hipMemcpy(w, dev, sizeof(w), hipMemcpyDeviceToHost));
+    st |= (w[0] & 0xFFu) | ((w[1] & 0xFFu) << 8);
+    if (clear) LAUNCH(hipMemset(dev, 0, sizeof(w)));
+  }
+  return (int32_t)st;
+}
+
+#ifdef MTPD_TEAM_TRACE
+// Measurement builds only: the persistent kernel's stage timeline of the last launch, [256 blocks][128] wall-clock
+// ticks (100 MHz).
+MTPD_API int mtpd_debug_team_trace(uint64_t* host) {
+  LAUNCH(mtpd::team_trace_read(host));
+  return MTPD_OK;
+}
+#endif
 
 int mtpd_timing_enable(mtpd_handle h, int32_t enable) {
   g_last_error.clear();

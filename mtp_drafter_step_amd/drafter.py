@@ -57,7 +57,9 @@ class SharedKV:
 class Drafter:
     """A handle over borrowed device weights (dict as produced by fixtures.synth.make_weights, on the device)."""
 
-    def __init__(self, shape, weights: Dict[str, object], max_batch: int = abi.MTPD_MAX_BATCH):
+    def __init__(self, shape, weights: Dict[str, object], max_batch: int = abi.MTPD_MAX_BATCH,
+                 options: Optional[Dict[int, int]] = None):
+        """options: {abi.MTPD_OPT_*: value} applied right after creation (see include/mtpd.h)."""
         L = abi.lib()
         self.shape = shape
         self.weights = weights  # keep the tensors alive: the handle borrows them
@@ -83,6 +85,18 @@ class Drafter:
         self.handle = h
         self.max_batch = max_batch
         self._ws: Dict[int, torch.Tensor] = {}
+        for k, v in (options or {}).items():
+            self.set_option(k, v)
+
+    def set_option(self, option: int, value: int) -> None:
+        abi.check(abi.lib().mtpd_set_option(self.handle, int(option), int(value)))
+
+    def fault_status(self, clear: bool = False) -> int:
+        """0 if every persistent-kernel launch finished its waits normally (see mtpd_fault_status)."""
+        st = int(abi.lib().mtpd_fault_status(self.handle, 1 if clear else 0))
+        if st < 0:
+            abi.check(st)
+        return st
 
     def close(self):
         if getattr(self, "handle", None):

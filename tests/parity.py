@@ -40,7 +40,8 @@ class Case:
 
     def __init__(self, shape, batch: int, context: int, ragged: bool = False, seed: int = 0,
                  distinct_v: bool = False, lens: Optional[Sequence[int]] = None, max_batch: Optional[int] = None,
-                 gen_device: str = "cpu", shared_kv: bool = False, swa_window: Optional[int] = None):
+                 gen_device: str = "cpu", shared_kv: bool = False, swa_window: Optional[int] = None,
+                 options: Optional[Dict[int, int]] = None):
         """gen_device "cuda" runs the (bit-identical) generators on the GPU and copies the results to the host, for
         shapes whose tables take the CPU generator too long."""
         from mtp_drafter_step_amd import Drafter, SharedKV
@@ -74,7 +75,7 @@ class Case:
         vd = [None, None] if not distinct_v else [inp["v_sliding"].cuda(), inp["v_full"].cuda()]
         self.kv = SharedKV(kd[0], kd[1], inp["len_sliding"], inp["len_full"], inp["rope"].cuda(), vd[0], vd[1],
                            shared=shared_kv)
-        self.drafter = Drafter(shape, self.wg, max_batch=max_batch or max(batch, 1))
+        self.drafter = Drafter(shape, self.wg, max_batch=max_batch or max(batch, 1), options=options)
 
     def oracle_step(self, rows=None, want_rows=False, th=None, tok=None):
         th = self.inp["target_hidden"].numpy().view(np.uint16) if th is None else th

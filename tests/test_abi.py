@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mtpd_\w+)", out))
     assert exported == set(declared_functions())
-    assert L.mtpd_abi_version() == 4
+    assert L.mtpd_abi_version() == 5
 
 
 def test_struct_layout_matches_c(tmp_path):

@@ -191,21 +191,16 @@ def test_drafter_step_parity(name):
 
 
 def test_vector_alu_attention_at_head_dim_256():
-    """The vector-ALU attention (selected per launch by MTPD_ATTN_VALU=1, else used only for head_dim 64 / 128)
+    """The vector-ALU attention (selected by the handle option MTPD_OPT_ATTN_VALU, else used only for head_dim 64 / 128)
     on head_dim 256 with 4 and 8 query heads per kv head, split over several key ranges."""
-    import os
-    from mtp_drafter_step_amd import Drafter
+    from mtp_drafter_step_amd import Drafter, abi
     for shape in (synth.E4B, synth.E26B):
         say(f"valu attention {shape.n_head}/{shape.n_kv_head} heads")
         case = Case(shape, batch=3, context=2500, ragged=True, gen_device="cuda")
-        os.environ["MTPD_ATTN_VALU"] = "1"
-        try:
-            d = Drafter(shape, case.wg, max_batch=3)
-            want_sparse = shape.n_centroids > 0
-            out = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=want_sparse)
-            torch.cuda.synchronize()
-        finally:
-            del os.environ["MTPD_ATTN_VALU"]
+        d = Drafter(shape, case.wg, max_batch=3, options={abi.MTPD_OPT_ATTN_VALU: 1, abi.MTPD_OPT_PERSISTENT: 0})
+        want_sparse = shape.n_centroids > 0
+        out = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=want_sparse)
+        torch.cuda.synchronize()
         rows = [0, 1, 2]
         ref = case.oracle_step(rows=rows, want_rows=not want_sparse)
         tally = compare_step(case, out, ref, rows, where=f"valu {shape.n_head}")
@@ -341,23 +336,19 @@ GEMM_PATH_CASES = {
 def test_dense_stage_paths(name):
     """The large-batch path (residual + norm kernels, matrix-core GEMMs with K-split partials, separate attention
     merge) and the small-batch path (fused prologues), each forced on a fresh handle, both against the oracle."""
-    import os
-    from mtp_drafter_step_amd import Drafter
+    from mtp_drafter_step_amd import Drafter, abi
     kw = GEMM_PATH_CASES[name]
     case = Case(**kw)
     dense = case.shape.n_centroids == 0
     B = kw["batch"]
     rows = list(range(B)) if B <= 8 else list(range(0, B, 6)) + [B - 1]
     ref = case.oracle_step(rows=rows, want_rows=dense)
-    for flag in ("1", "0"):
-        say(f"dense stages {name} MTPD_GEMM_PATH={flag}")
-        os.environ["MTPD_GEMM_PATH"] = flag
-        try:
-            d = Drafter(case.shape, case.wg, max_batch=B)
-            out = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=not dense)
-            torch.cuda.synchronize()
-        finally:
-            del os.environ["MTPD_GEMM_PATH"]
+    for flag in (2, 1):
+        say(f"dense stages {name} MTPD_OPT_DENSE_PATH={flag}")
+        d = Drafter(case.shape, case.wg, max_batch=B,
+                    options={abi.MTPD_OPT_DENSE_PATH: flag, abi.MTPD_OPT_PERSISTENT: 0})
+        out = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=not dense)
+        torch.cuda.synchronize()
         tally = compare_step(case, out, ref, rows, where=f"{name} path {flag}")
         say(tally.summary())
         assert tally.tok_checked >= len(rows) // 2
@@ -432,14 +423,10 @@ def test_draft_block_equals_chained_steps():
 def test_graph_replays_match_direct_launches():
     """The same call replayed from a captured graph, interleaved with other work and synchronisations, gives
     bit-identical results to direct launches (graphs disabled) every time."""
-    import os
-    from mtp_drafter_step_amd import Drafter
-    case = Case(synth.E4B, batch=4, context=1200, ragged=True)
-    os.environ["MTPD_GRAPHS"] = "0"
-    try:
-        direct = Drafter(case.shape, case.wg, max_batch=4)
-    finally:
-        del os.environ["MTPD_GRAPHS"]
+    from mtp_drafter_step_amd import Drafter, abi
+    case = Case(synth.E4B, batch=4, context=1200, ragged=True, options={abi.MTPD_OPT_PERSISTENT: 0})
+    direct = Drafter(case.shape, case.wg, max_batch=4,
+                     options={abi.MTPD_OPT_GRAPHS: 0, abi.MTPD_OPT_PERSISTENT: 0})
     ref = direct.draft_block(3, case.th, case.tok, case.temb, case.kv, want_logits=True)
     ref = {k: v.clone() for k, v in ref.items()}
     for rep in range(4):

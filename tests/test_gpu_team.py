@@ -1,0 +1,87 @@
+"""GPU parity of the persistent drafter kernel (one launch per drafter_step / draft_block for at most 16 rows of the
+E2B / E4B shapes) through the C ABI: against the oracle, against the per-stage kernels, block against chained steps,
+and its fault status."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from fixtures import synth
+from parity import Case, compare_step
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mtp_drafter_step_amd import abi
+    abi.lib()
+
+
+def _check_status(d):
+    st = d.fault_status(clear=True)
+    assert st == 0, f"persistent kernel status {st:#x}"
+
+
+@pytest.mark.parametrize("shape_name,batch,context", [("E4B", 16, 2048), ("E4B", 1, 700), ("E2B", 5, 1300),
+                                                      ("E4B", 11, 3000), ("E2B", 16, 600)])
+def test_team_step_matches_oracle(shape_name, batch, context):
+    shape = getattr(synth, shape_name)
+    say(f"team step {shape_name} B={batch} ctx={context}")
+    case = Case(shape, batch=batch, context=context, ragged=True)
+    out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    _check_status(case.drafter)
+    rows = list(range(batch))
+    ref = case.oracle_step(rows=rows)
+    tally = compare_step(case, out, ref, rows, where=f"team {shape_name} B={batch}")
+    say(tally.summary())
+    assert tally.sel_checked >= len(rows) // 2
+
+
+def test_team_block_equals_chained_team_steps():
+    """draft_block(4) in one launch reproduces four chained one-step launches bit for bit (tokens, logits, hidden)."""
+    case = Case(synth.E4B, batch=16, context=1500, ragged=True)
+    d = case.drafter
+    blk = d.draft_block(4, case.th, case.tok, case.temb, case.kv, want_logits=True)
+    blk = {k: v.clone() for k, v in blk.items()}
+    th, tok = case.th, case.tok
+    for i in range(4):
+        s = d.drafter_step(th, tok, case.temb, case.kv, want_logits=True)
+        torch.cuda.synchronize()
+        assert torch.equal(s["next"], blk["tokens"][:, i].contiguous()), i
+        assert torch.equal(s["logits"], blk["logits"][i]), i
+        th, tok = s["hidden_out"].clone(), s["next"].clone()
+    assert torch.equal(th, blk["hidden_out"])
+    _check_status(d)
+    say(f"block tokens row 0: {blk['tokens'][0].tolist()}")
+
+
+def test_team_against_per_stage_kernels():
+    """The persistent kernel and the per-stage kernels on the same inputs agree on the tokens where the oracle's
+    margins are clear, and on hidden_out within the float rule."""
+    from mtp_drafter_step_amd import Drafter, abi
+    from parity import rel_ok
+    case = Case(synth.E4B, batch=16, context=4000, ragged=True)
+    a = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_sparse=True)
+    d2 = Drafter(case.shape, case.wg, max_batch=16, options={abi.MTPD_OPT_PERSISTENT: 0})
+    b = d2.drafter_step(case.th, case.tok, case.temb, case.kv, want_sparse=True)
+    torch.cuda.synchronize()
+    _check_status(case.drafter)
+    ha = a["hidden_out"].cpu().numpy().view(np.uint16)
+    hb = b["hidden_out"].cpu().numpy().view(np.uint16)
+    import oracle as O
+    for r in range(16):
+        assert rel_ok(O.bf16_to_f64(ha[r]), O.bf16_to_f64(hb[r])), r
+    same = int((a["next"] == b["next"]).sum())
+    say(f"tokens equal on {same} of 16 rows")
+    assert same >= 14
