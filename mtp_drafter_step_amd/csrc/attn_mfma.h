@@ -14,8 +14,8 @@
 namespace mtpd {
 namespace {
 
-// One batch of 16 keys for one wave of k_attn_mfma: scores of the keys in ka against the G heads, online softmax
-// update, and P V into acc. PF: the next batch's key loads (into kn) are issued first, to arrive during this batch's
+// One batch of 16 keys for one wave of k_attn_mfma: scores of the keys in ka against the G <= 8 heads, online
+// softmax update, and P V into acc (hi and lo parts of P in separate rows until attn_fold_rows). PF: the next batch's key loads (into kn) are issued first, to arrive during this batch's
 // arithmetic, and become ka at the end; the last batch of a wave issues none, since copying them into ka would wait
 // for loads nobody uses. The two forms are separate instances, so that the loads of the first are unconditional
 // (loads under a run-time branch make every later wait count assume the branch was not taken).
@@ -24,7 +24,7 @@ namespace {
 template <int G, bool PF, bool STAGED = false>
 __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, const uint16_t* Vb, int cap,
                                            bool same_v, float scale_log2, uint16_t* tile,
-                                           const uint16_t (*qop)[2][G][4][8], uint4 (&ka)[8], uint4 (&kn)[8],
+                                           const uint16_t (*qop)[2][8][4][8], uint4 (&ka)[8], uint4 (&kn)[8],
                                            f32x4 (&acc)[16], float& mrun, float& lrun) {
   constexpr int HD = 256, KSTEPS = 8, TILES = 16, LROW = HD + 8, S = 64;
   constexpr int GQ = (G + 3) / 4;
@@ -50,24 +50,31 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) *reinterpret_cast<uint4*>(tile + hq * LROW + 32 * c + 8 * kq) = vv[c];
   }
-  // scores S[key 4kq + r][head hq]
+  // scores: column n < G of the tile takes q_hi of head n, column 8 + n takes q_lo of head n (qop holds zeros for
+  // the other columns), so one product covers both terms; lane hq < G adds its column 8 + hq partner, 8 lanes away
+  // in its row of 16. All eight B operands are read before the products, so the reads overlap.
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    uint4 qb[KSTEPS];
 #pragma unroll
-  for (int c = 0; c < KSTEPS; ++c) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, ka[c]);
-    uint4 hi = *reinterpret_cast<const uint4*>(&qop[c][0][hsel][kq][0]);
-    uint4 lo = *reinterpret_cast<const uint4*>(&qop[c][1][hsel][kq][0]);
-    if (hq >= G) hi = lo = make_uint4(0u, 0u, 0u, 0u);
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), sacc, 0, 0, 0);
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), sacc, 0, 0, 0);
+    for (int c = 0; c < KSTEPS; ++c) qb[c] = *reinterpret_cast<const uint4*>(&qop[c][hq >> 3][hq & 7][kq][0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[c]), __builtin_bit_cast(bf16x8, qb[c]),
+                                                     sacc, 0, 0, 0);
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sacc[r] += xr_partner<8>(sacc[r]);
   float sv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) sv[r] = (4 * kq + r < nk && hq < G) ? sacc[r] * scale_log2 : -INFINITY;
   float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mt = fmaxf(mt, xr_partner<16>(mt));
   mt = fmaxf(mt, xr_partner<32>(mt));
-  const float mn = fmaxf(mrun, mt);
+  // the reference maximum moves only when a score exceeds it by more than 2^8: below that the weights stay under
+  // 256, far inside fp32 and exact in the bf16 hi + lo split, and most batches skip the rescale
+  const float mn = (mt > mrun + 8.0f) ? mt : mrun;
   // 2^x on the hardware instruction: weights below 2^-126 flush to zero, far below what a weight contributes
   const float alpha = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
   float pv[4], ps = 0.f;
@@ -80,19 +87,26 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
   ps += xr_partner<32>(ps);
   lrun = lrun * alpha + ps;
   mrun = mn;
+  // P operand: row h < G holds the bf16 hi part of head h's weights, row 8 + h the lo part (taken from lane h, 8
+  // lanes away); the output rows 8 + h therefore collect the lo products, folded in by attn_fold_rows
   uint32_t ph2[2], pl2[2];
   split_bf16x2(pv[0], pv[1], ph2[0], pl2[0]);
   split_bf16x2(pv[2], pv[3], ph2[1], pl2[1]);
-  const i16x4 phi = __builtin_bit_cast(i16x4, make_uint2(ph2[0], ph2[1]));
-  const i16x4 plo = __builtin_bit_cast(i16x4, make_uint2(pl2[0], pl2[1]));
-  // rescale the accumulators only when some head's maximum moved (alpha is exactly 1 otherwise): D rows are heads
-  // 4kq + r, whose alpha lives in lane 4kq + r (rows of heads >= G are padding)
-  if (__any(alpha != 1.0f)) {
+  uint32_t pa[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t lo8 = __float_as_uint(xr_partner<8>(__uint_as_float(pl2[i])));
+    pa[i] = (hq < 8) ? ph2[i] : lo8;
+  }
+  const i16x4 pop = __builtin_bit_cast(i16x4, make_uint2(pa[0], pa[1]));
+  // rescale the accumulators only when some head's maximum moved (alpha is exactly 1 otherwise): D row 4kq + r
+  // belongs to head (4kq + r) mod 8, whose alpha lives in that lane (rows of no head are zero)
+  if (__any(hq < G && alpha != 1.0f)) {
     float al[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       al[r] = readlane_f(alpha, r);
-      if constexpr (GQ > 1) al[r] = (kq == 1) ? readlane_f(alpha, 4 + r) : al[r];
+      if constexpr (GQ > 1) al[r] = (kq & 1) ? readlane_f(alpha, 4 + r) : al[r];
     }
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -101,18 +115,26 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
   }
   // V operand: keys 4 kq + r of dim 16 t + hq, one transposing read of the 4 x 16 block at row 4 kq
   const uint16_t* vrow = tile + (4 * kq + (hq >> 2)) * LROW + 4 * (hq & 3);
+  i16x4 vb[TILES];
 #pragma unroll
-  for (int t = 0; t < TILES; ++t) {
-    const i16x4 vb = lds_read_tr16(vrow + 16 * t);
-    f32x4 a = acc[t];
-    a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, a, 0, 0, 0);
-    a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, a, 0, 0, 0);
-    acc[t] = a;
-  }
+  for (int t = 0; t < TILES; ++t) vb[t] = lds_read_tr16(vrow + 16 * t);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, vb[t], acc[t], 0, 0, 0);
   if constexpr (PF) {
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) ka[c] = kn[c];
   }
+}
+
+// After the last batch: output rows 8 .. 15 hold the lo-part products of the heads in rows 0 .. 7; rows 4kq + r of
+// lane (hq, kq) and (hq, kq ^ 2) are 8 rows apart, so one exchange over lanes 32 apart leaves every head's full
+// accumulator in the lanes of kq = 0, 1 (and a copy in kq = 2, 3).
+__device__ __forceinline__ void attn_fold_rows(f32x4 (&acc)[16]) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] += xr_partner<32>(acc[t][r]);
 }
 
 }  // namespace

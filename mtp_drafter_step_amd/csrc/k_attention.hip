@@ -221,16 +221,15 @@ __global__ __launch_bounds__(NW * 64) void k_attn(int B, int nh, int nkv, const 
   }
 }
 
-// Matrix-core variant for head_dim 256 and up to 8 query heads per kv head (heads padded to the 16 rows of an
-// MFMA tile). Per wave and batch of 16 keys:
-//   S[16 keys][16 heads] = K_tile . q^T with v_mfma_f32_16x16x32_bf16: the key rows load straight into the A
-//     operand (lane l: key l%16, 8 dims at 8*(l/16) of each 32-dim step); the fp32 query is split into two bf16
-//     terms q = q_hi + q_lo (relative error <= 2^-16) so the product keeps fp32-level accuracy;
+// Matrix-core variant for head_dim 256 and up to 8 query heads per kv head. Per wave and batch of 16 keys:
+//   S[16 keys][16 columns] = K_tile . [q_hi | q_lo]^T with v_mfma_f32_16x16x32_bf16: the key rows load straight into
+//     the A operand (lane l: key l%16, 8 dims at 8*(l/16) of each 32-dim step); the fp32 query is split into two
+//     bf16 terms q = q_hi + q_lo (relative error <= 2^-16) so the product keeps fp32-level accuracy: column h holds
+//     q_hi of head h, column 8 + h its q_lo, and one exchange 8 lanes apart sums the two;
 //   online softmax on the S layout (lane l holds keys 4*(l/16)+r of head l%16);
-//   O[16 heads][256] += P . V with v_mfma_f32_16x16x16_bf16: P (split into bf16 hi + lo) is already in the A layout,
-//     V comes from the wave's LDS copy of the key tile, read column-wise by transposing LDS reads (4 keys of one dim
-//     per lane).
-
+//   O[16 rows][256] += P . V with v_mfma_f32_16x16x16_bf16: P split into bf16 hi (row h) + lo (row 8 + h) is already
+//     in the A layout, V comes from the wave's LDS copy of the key tile, read column-wise by transposing LDS reads (4
+//     keys of one dim per lane); the lo rows are folded into the hi rows once, after the last batch.
 
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv, const float* __restrict__ q,
@@ -249,7 +248,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   __shared__ __attribute__((aligned(16))) float qs_wacc[QS_FLOATS > WACC_FLOATS ? QS_FLOATS : WACC_FLOATS];
   float (*qs)[HD] = reinterpret_cast<float (*)[HD]>(qs_wacc);                  // [head][dim]
   float (*wacc)[HD][4 * GQ] = reinterpret_cast<float (*)[HD][4 * GQ]>(qs_wacc);  // [wave][dim][head]
-  __shared__ __attribute__((aligned(16))) uint16_t qop[KSTEPS][2][G][4][8];  // [step][hi/lo][head][kq][8 dims]
+  // [step][hi/lo][head slot][kq][8 dims]; slots G .. 7 stay zero (the unused columns of the score tile)
+  __shared__ __attribute__((aligned(16))) uint16_t qop[KSTEPS][2][8][4][8];
   __shared__ __attribute__((aligned(16))) uint16_t vt[NW][16][LROW];
   __shared__ __attribute__((aligned(16))) float wml[NW][G][2];
   static_assert(NW * 64 == HD, "one thread per dim in the combine");
@@ -316,9 +316,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   }
   __syncthreads();
   // q = q_hi + q_lo in bf16, stored in the MFMA B-operand order
-  for (int i = threadIdx.x; i < KSTEPS * G * 4 * 8; i += NW * 64) {
-    const int e = i & 7, kk = (i >> 3) & 3, hh = (i >> 5) % G, c = i / (32 * G);
-    const float v = qs[hh][32 * c + 8 * kk + e];
+  for (int i = threadIdx.x; i < KSTEPS * 8 * 4 * 8; i += NW * 64) {
+    const int e = i & 7, kk = (i >> 3) & 3, hh = (i >> 5) & 7, c = i >> 8;
+    const float v = hh < G ? qs[hh][32 * c + 8 * kk + e] : 0.f;
     const uint16_t hb = f2bf(v);
     qop[c][0][hh][kk][e] = hb;
     qop[c][1][hh][kk][e] = f2bf(v - bf2f(hb));
@@ -335,6 +335,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(int B, int nh, int nkv
   for (; t0 + S < k1; t0 += S)
     mfma_batch<G, true>(t0, k1, Kb, Vb, cap, same_v, scale_log2, tile, qop, ka, kn, acc, mrun, lrun);
   if (t0 < k1) mfma_batch<G, false>(t0, k1, Kb, Vb, cap, same_v, scale_log2, tile, qop, ka, kn, acc, mrun, lrun);
+  attn_fold_rows(acc);
   // combine the waves of this block: head h's softmax state is in lane h; output row group kq (heads 4kq .. +3)
   // sits in lanes 16kq .. +15: dim 16t + hq, heads in the four registers of acc[t], stored as one float4 per dim
   if (lane < G) {

@@ -167,7 +167,8 @@ struct Smem {
   float mrgl[4];
   int tok[2];
   // attention
-  __attribute__((aligned(16))) uint16_t qop[8][2][4][4][8];  // [step][hi/lo][head][kq][8 dims]
+  // [step][hi/lo][head slot][kq][8 dims]; slots 4 .. 7 stay zero (unused columns of the score tile)
+  __attribute__((aligned(16))) uint16_t qop[8][2][8][4][8];
   __attribute__((aligned(16))) float qs_wacc[4 * 256 * 4];   // q staging, then the waves' combine tiles
   __attribute__((aligned(16))) uint16_t vt[4][16][264];
   __attribute__((aligned(16))) float wml[4][4][2];
@@ -243,12 +244,90 @@ __device__ __forceinline__ float dot4(uint2 w, float4 u) {
 }
 
 // ------------------------------------------------------------------------------------------------------------
+// Each stage's weight slices are requested one stage ahead: a stage issues the next stage's loads as soon as its
+// own inputs have arrived, so their latency overlaps its arithmetic and the next exchange instead of gating the
+// next poll (a wait covers every load issued before the one it needs).
+
+template <int NBB>
+struct WPre {
+  uint2 w[8][NBB / 2];
+};
+struct WQ {
+  uint2 w[8];
+  uint16_t an[4], pfn[4];  // attn_norm of the layer, post_ffw_norm of the previous layer
+};
+struct WK {
+  uint2 w[8];  // o_proj or down: 8 outputs over this wave's quarter of K = 1024
+};
+struct WF {
+  uint2 g[8], u[8];
+  uint16_t fn[4], pan[4];  // ffn_norm, post_attention_norm
+};
+template <int NBB>
+struct WPost {
+  uint2 p[((NBB * 2 + 7) / 8) * 8], c[16];
+  uint16_t on[4], pfn[4];  // output_norm, the last layer's post_ffw_norm
+};
+
+template <int NBB>
+__device__ __forceinline__ void issue_pre(const TeamArgs& a, const Team& T, WPre<NBB>& W) {
+  constexpr int Bb = NBB * 256, CPL = NBB / 2;
+  const int w = wave_id(), lane = lane_id(), n0 = 8 * T.m, kb = w * (Bb / 2);
+#pragma unroll
+  for (int o = 0; o < 8; ++o)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      W.w[o][c] = *reinterpret_cast<const uint2*>(a.wpk + W_PRE + (size_t)(n0 + o) * (2 * Bb) + kb + 256 * c + 4 * lane);
+}
+
+__device__ __forceinline__ void issue_q(const TeamArgs& a, const Team& T, int l, WQ& W) {
+  const int w = wave_id(), lane = lane_id(), n0 = 32 * T.m + 8 * w;
+#pragma unroll
+  for (int o = 0; o < 8; ++o) W.w[o] = *reinterpret_cast<const uint2*>(lw(a, l, W_Q) + (size_t)(n0 + o) * TH + 4 * lane);
+  load_w4(lw(a, l, W_AN), W.an);
+  load_w4(lw(a, l > 0 ? l - 1 : 0, W_PFN), W.pfn);
+}
+
+__device__ __forceinline__ void issue_k1024(const uint16_t* Wm, const Team& T, WK& W) {
+  const int w = wave_id(), lane = lane_id(), n0 = 8 * T.m, k = 256 * w + 4 * lane;
+#pragma unroll
+  for (int o = 0; o < 8; ++o) W.w[o] = *reinterpret_cast<const uint2*>(Wm + (size_t)(n0 + o) * 1024 + k);
+}
+
+__device__ __forceinline__ void issue_ffn(const TeamArgs& a, const Team& T, int l, WF& W) {
+  const int w = wave_id(), lane = lane_id(), f0 = 32 * T.m + 8 * w;
+#pragma unroll
+  for (int o = 0; o < 8; ++o) {
+    W.g[o] = *reinterpret_cast<const uint2*>(lw(a, l, W_G) + (size_t)(f0 + o) * TH + 4 * lane);
+    W.u[o] = *reinterpret_cast<const uint2*>(lw(a, l, W_U) + (size_t)(f0 + o) * TH + 4 * lane);
+  }
+  load_w4(lw(a, l, W_FN), W.fn);
+  load_w4(lw(a, l, W_PAN), W.pan);
+}
+
+template <int NBB>
+__device__ __forceinline__ void issue_post(const TeamArgs& a, const Team& T, WPost<NBB>& W) {
+  constexpr int Bb = NBB * 256, NPB = Bb / 32, NPW = NPB / 4, NPG = (NPW + 7) / 8;
+  const int w = wave_id(), lane = lane_id();
+  const int p0 = NPB * T.m + NPW * w, c0 = 64 * T.m + 16 * w;
+#pragma unroll
+  for (int o = 0; o < NPG * 8; ++o)
+    W.p[o] = *reinterpret_cast<const uint2*>(a.wpk + w_post(Bb) + (size_t)(p0 + min(o, NPW - 1)) * TH + 4 * lane);
+#pragma unroll
+  for (int o = 0; o < 16; ++o) W.c[o] = *reinterpret_cast<const uint2*>(a.wpk + w_cen(Bb) + (size_t)(c0 + o) * TH + 4 * lane);
+  load_w4(a.wpk + w_onorm(Bb), W.on);
+  load_w4(lw(a, a.n_layer - 1, W_PFN), W.pfn);
+}
+
+// ------------------------------------------------------------------------------------------------------------
 // pre_projection of [hidden ; escale E[token]] ([MTP doc] "What it is": 2x backbone input; [Guide] section 2(3);
 // [Explained] "Target Activations"). Member m: outputs 8m .. 8m + 7. Wave w covers K quarter w: waves 0-1 the
 // hidden half, waves 2-3 the embedding half (Bb % 512 == 0: NBB / 2 chunks of 4 elements per lane).
 
 template <int R, int NBB>
-__device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, int step) {
+__device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, int step, WQ& Wq) {
+  WPre<NBB> W;
+  issue_pre<NBB>(a, T, W);
   constexpr int Bb = NBB * 256, CPL = NBB / 2;
   const int w = wave_id(), lane = lane_id();
   const int n0 = 8 * T.m;
@@ -271,12 +350,6 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
       kres[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)slot_of(t, cap) * 256 + (threadIdx.x & 31) * 8);
     }
   }
-  uint2 wr[8][CPL];
-#pragma unroll
-  for (int o = 0; o < 8; ++o)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      wr[o][c] = *reinterpret_cast<const uint2*>(a.wpk + W_PRE + (size_t)(n0 + o) * (2 * Bb) + kb + 256 * c + 4 * lane);
   uint2 xr[R][CPL];
   const bool emb = w >= 2;
   if (!emb) {
@@ -303,6 +376,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
 #pragma unroll
         for (int c = 0; c < CPL; ++c) xr[r][c] = make_uint2(raw[(r * CPL + c) * 2], raw[(r * CPL + c) * 2 + 1]);
     }
+    issue_q(a, T, 0, Wq);
   } else {
     // the row's token: the caller's at step 0, else the best of the previous step's 32 slot keys
     int tk[R];
@@ -330,6 +404,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
       for (int c = 0; c < CPL; ++c)
         xr[r][c] = *reinterpret_cast<const uint2*>(a.temb + (size_t)t * Bb + (kb - Bb) + 256 * c + 4 * lane);
     }
+    issue_q(a, T, 0, Wq);
     // this member's 1/32 of the step's -1e30 base rows ([Inventory] "Centroid / ordered embeddings LM head", step 5),
     // streaming stores that drain while the embedding rows arrive; every wave passes a full wait before it
     // publishes the centroid scores the head waits for, so the fill precedes every scatter
@@ -363,7 +438,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
 #pragma unroll
       for (int o = 0; o < 8; ++o) {
         float wf[4];
-        unpack4(wr[o][c], wf);
+        unpack4(W.w[o][c], wf);
         float s = acc[r * 8 + o];
 #pragma unroll
         for (int e = 0; e < 4; ++e) s = fmaf(xf[e], wf[e], s);
@@ -392,33 +467,60 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
 // residual stream; later layers first finish the previous layer's FFN residual:
 // x = (x + RMSNorm(W_d m; post_ffw_norm)) * layer_output_scale ([MTP doc] "What it is": per-layer scalar).
 
+// This member's split of a row's key window in the attention stage of layer l (stage_att's layout).
+struct KeySplit {
+  const uint16_t* Kb;  // the row's cache + 8 kq
+  int k0, k1, start, cap;
+};
+
 template <int R>
-__device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int step, int l) {
+__device__ __forceinline__ KeySplit key_split(const TeamArgs& a, const Team& T, int type) {
+  constexpr int NS = TM / R;
+  const int kq = lane_id() >> 4;
+  const int r = (R == 2) ? (T.m >> 4) : 0, s = (R == 2) ? (T.m & 15) : T.m;
+  const int row = T.row(r);
+  KeySplit k;
+  const int cnt = a.win_count[type][row];
+  k.start = a.win_start[type][row];
+  k.cap = a.cap[type];
+  const int chunk = (cnt + NS - 1) / NS;
+  k.k0 = k.start + s * chunk;
+  k.k1 = min(k.start + cnt, k.k0 + chunk);
+  k.Kb = a.kc[type] + (size_t)row * k.cap * 256 + 8 * kq;
+  return k;
+}
+
+// Batch j of this wave in a streamed split: keys k0 + 64 j + 16 w .. +16 (rows past the split clamped to its last
+// key: cache hits, masked in the scores).
+__device__ __forceinline__ void load_key_batch(const KeySplit& k, int j, uint4 (&dst)[8]) {
+  const int tt = k.k0 + 64 * j + 16 * wave_id() + (lane_id() & 15);
+  const uint16_t* rp = k.Kb + (size_t)slot_of(max(min(tt, k.k1 - 1), k.start), k.cap) * 256;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dst[c] = *reinterpret_cast<const uint4*>(rp + 32 * c);
+}
+
+template <int R>
+__device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int step, int l, const WQ& W, WK& Wo) {
   const int w = wave_id(), lane = lane_id();
   const int n0 = 32 * T.m + 8 * w;
-  uint2 wq[8];
-#pragma unroll
-  for (int o = 0; o < 8; ++o) wq[o] = *reinterpret_cast<const uint2*>(lw(a, l, W_Q) + (size_t)(n0 + o) * TH + 4 * lane);
+  const int lp = l > 0 ? l - 1 : 0;
   if (w < R) {
-    uint16_t wn[4], wd[4];
-    load_w4(lw(a, l, W_AN), wn);
-    const int lp = l > 0 ? l - 1 : 0;
-    load_w4(lw(a, lp, W_PFN), wd);
     float d[4];
     if (l == 0)
       poll_row(T, A_XB + w * TH, T.tag(step, S_PRE), S_PRE, d);
     else
       poll_row(T, A_D + w * TH, T.tag(step, s_dn(l - 1)), s_dn(l - 1), d);
     if (l == 1) TEAM_TRACE(step, 32);
-    row_update(S, w, l == 0 ? 0 : 1, d, wd, a.scale[lp], wn, a.eps);
+    row_update(S, w, l == 0 ? 0 : 1, d, W.pfn, a.scale[lp], W.an, a.eps);
   }
+  issue_k1024(lw(a, l, W_O), T, Wo);  // the o_proj slice, used two stages on
   __syncthreads();
   float acc[R * 8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float4 u = *reinterpret_cast<const float4*>(&S.us[r][4 * lane]);
 #pragma unroll
-    for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(wq[o], u);
+    for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(W.w[o], u);
   }
   XR<R * 8, 32>::run(acc, lane);
   constexpr int RL = kRedLanes<R>;
@@ -454,19 +556,13 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
   const int i0 = (lane * 4) & (half - 1);
   const float4 co4 = *reinterpret_cast<const float4*>(tab + i0);
   const float4 si4 = *reinterpret_cast<const float4*>(tab + half + i0);
-  // three 16-key batches of this wave in flight: batch j of the wave holds keys k0 + 64 j + 16 w .. +16; rows past
-  // the split are clamped to its last key (cache hits, masked in the scores)
-  uint4 kA[KSTEPS], kB[KSTEPS], kC[KSTEPS];  // (the prefetch argument of mfma_batch is unused here)
-  auto load_batch = [&](uint4 (&dst)[KSTEPS], int j) {
-    const int tt = k0 + 64 * j + 16 * w + hq;
-    const uint16_t* rp = Kb + (size_t)slot_of(max(min(tt, k1 - 1), start), cap) * HD;
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) dst[c] = *reinterpret_cast<const uint4*>(rp + 32 * c);
-  };
+  // streamed splits keep three 16-key batches of this wave in flight
+  const KeySplit ksp = key_split<R>(a, T, type);
+  uint4 kA[KSTEPS], kB[KSTEPS], kC[KSTEPS];
   if (!resident) {
-    load_batch(kA, 0);
-    load_batch(kB, 1);
-    load_batch(kC, 2);
+    load_key_batch(ksp, 0, kA);
+    load_key_batch(ksp, 1, kB);
+    load_key_batch(ksp, 2, kC);
   }
   // q of head w (dims 4 lane .. +3), whose rotation partners (d <-> d + 128) sit in lane ^ 32
   float v[4];
@@ -529,16 +625,17 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
     if (k0 + 64 * j + 16 * w < k1)
       mfma_batch<4, false>(k0 + 64 * j + 16 * w, k1, Kb, Kb, cap, true, a.scale_log2, tile, S.qop, kA, kA, acc,
                            mrun, lrun);
-    load_batch(kA, j + 3);
+    load_key_batch(ksp, j + 3, kA);
     if (k0 + 64 * (j + 1) + 16 * w < k1)
       mfma_batch<4, false>(k0 + 64 * (j + 1) + 16 * w, k1, Kb, Kb, cap, true, a.scale_log2, tile, S.qop, kB, kB,
                            acc, mrun, lrun);
-    load_batch(kB, j + 4);
+    load_key_batch(ksp, j + 4, kB);
     if (k0 + 64 * (j + 2) + 16 * w < k1)
       mfma_batch<4, false>(k0 + 64 * (j + 2) + 16 * w, k1, Kb, Kb, cap, true, a.scale_log2, tile, S.qop, kC, kC,
                            acc, mrun, lrun);
-    load_batch(kC, j + 5);
+    load_key_batch(ksp, j + 5, kC);
   }
+  attn_fold_rows(acc);
   if (type) TEAM_TRACE(step, 30);
   // combine the waves: head h's state in lane h; output rows (heads) 0..3 of the tile in lanes 0..15
   float (*wacc)[HD][4] = reinterpret_cast<float (*)[HD][4]>(S.qs_wacc);
@@ -637,14 +734,11 @@ __device__ __forceinline__ void stage_mrg(const TeamArgs& a, Team& T, Smem& S, i
 // 1024 -> 256 products (o_proj over the merged attention output, [MTP doc] "Tensor schema": attn_output; the
 // down projection, ffn_down): member m computes outputs 8m .. 8m + 7, wave w the partial over K quarter w.
 
-template <int R>
-__device__ __forceinline__ void stage_k1024(Team& T, Smem& S, const uint16_t* W, int src, uint32_t tag_in, int sid_in, int dst,
-                            uint32_t tag_out) {
+template <int R, typename After>
+__device__ __forceinline__ void stage_k1024(Team& T, Smem& S, const WK& W, int src, uint32_t tag_in, int sid_in,
+                                            int dst, uint32_t tag_out, After after_poll) {
   const int w = wave_id(), lane = lane_id();
   const int n0 = 8 * T.m, k = 256 * w + 4 * lane;
-  uint2 wv[8];
-#pragma unroll
-  for (int o = 0; o < 8; ++o) wv[o] = *reinterpret_cast<const uint2*>(W + (size_t)(n0 + o) * 1024 + k);
   int idx[R * 4];
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -654,13 +748,14 @@ __device__ __forceinline__ void stage_k1024(Team& T, Smem& S, const uint16_t* W,
   wait_words<R * 4>(T, idx, tag_in, sid_in, raw);
   if (sid_in == s_mrg(1)) TEAM_TRACE((int)(tag_in / NSID - T.E - 1), 35);
   if (sid_in == s_ffn(1)) TEAM_TRACE((int)(tag_in / NSID - T.E - 1), 37);
+  after_poll();
   float acc[R * 8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float4 u = make_float4(__uint_as_float(raw[r * 4]), __uint_as_float(raw[r * 4 + 1]),
                                  __uint_as_float(raw[r * 4 + 2]), __uint_as_float(raw[r * 4 + 3]));
 #pragma unroll
-    for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(wv[o], u);
+    for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(W.w[o], u);
   }
   XR<R * 8, 32>::run(acc, lane);
   constexpr int RL = kRedLanes<R>;
@@ -679,24 +774,17 @@ __device__ __forceinline__ void stage_k1024(Team& T, Smem& S, const uint16_t* W,
 // indices 32m .. 32m + 31.
 
 template <int R>
-__device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, int step, int l) {
+__device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, int step, int l, const WF& W,
+                                          WK& Wd) {
   const int w = wave_id(), lane = lane_id();
   const int f0 = 32 * T.m + 8 * w;
-  uint2 wg[8], wu[8];
-#pragma unroll
-  for (int o = 0; o < 8; ++o) {
-    wg[o] = *reinterpret_cast<const uint2*>(lw(a, l, W_G) + (size_t)(f0 + o) * TH + 4 * lane);
-    wu[o] = *reinterpret_cast<const uint2*>(lw(a, l, W_U) + (size_t)(f0 + o) * TH + 4 * lane);
-  }
   if (w < R) {
-    uint16_t wn[4], wd[4];
-    load_w4(lw(a, l, W_FN), wn);
-    load_w4(lw(a, l, W_PAN), wd);
     float d[4];
     poll_row(T, A_T + w * TH, T.tag(step, s_op(l)), s_op(l), d);
     if (l == 1) TEAM_TRACE(step, 36);
-    row_update(S, w, 2, d, wd, 1.0f, wn, a.eps);
+    row_update(S, w, 2, d, W.pan, 1.0f, W.fn, a.eps);
   }
+  issue_k1024(lw(a, l, W_D), T, Wd);  // the down slice, used next stage
   __syncthreads();
   float ag[R * 8], au[R * 8];
 #pragma unroll
@@ -704,8 +792,8 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
     const float4 u = *reinterpret_cast<const float4*>(&S.us[r][4 * lane]);
 #pragma unroll
     for (int o = 0; o < 8; ++o) {
-      ag[r * 8 + o] = dot4(wg[o], u);
-      au[r * 8 + o] = dot4(wu[o], u);
+      ag[r * 8 + o] = dot4(W.g[o], u);
+      au[r * 8 + o] = dot4(W.u[o], u);
     }
   }
   XR<R * 8, 32>::run(ag, lane);
@@ -725,26 +813,20 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
 
 template <int R, int NBB>
 __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, int step) {
+  WPost<NBB> W;
+  issue_post<NBB>(a, T, W);
   constexpr int Bb = NBB * 256, NPB = Bb / 32, NPW = NPB / 4, NPG = (NPW + 7) / 8;
   const int w = wave_id(), lane = lane_id();
   const int last_l = a.n_layer - 1;
   const int p0 = NPB * T.m + NPW * w;  // this wave's first post output
   const int c0 = 64 * T.m + 16 * w;    // this wave's first centroid
-  uint2 wp[NPG * 8], wc[16];
-#pragma unroll
-  for (int o = 0; o < NPG * 8; ++o)
-    wp[o] = *reinterpret_cast<const uint2*>(a.wpk + w_post(Bb) + (size_t)(p0 + min(o, NPW - 1)) * TH + 4 * lane);
-#pragma unroll
-  for (int o = 0; o < 16; ++o) wc[o] = *reinterpret_cast<const uint2*>(a.wpk + w_cen(Bb) + (size_t)(c0 + o) * TH + 4 * lane);
   if (w < R) {
-    uint16_t wn[4], wd[4];
-    load_w4(a.wpk + w_onorm(Bb), wn);
-    load_w4(lw(a, last_l, W_PFN), wd);
     float d[4];
     poll_row(T, A_D + w * TH, T.tag(step, s_dn(last_l)), s_dn(last_l), d);
     TEAM_TRACE(step, 38);
-    row_update(S, w, 1, d, wd, a.scale[last_l], wn, a.eps);
+    row_update(S, w, 1, d, W.pfn, a.scale[last_l], W.on, a.eps);
   }
+
   // this member's -1e30 stores are complete before it publishes anything the head waits for
   if (a.logits) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -759,7 +841,7 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(wp[g * 8 + o], u[r]);
+      for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(W.p[g * 8 + o], u[r]);
     XR<R * 8, 32>::run(acc, lane);
     const float nxt = __shfl_down(acc[0], RL, 64);  // output o + 1 of the same row
     const int i = lane / RL, r = i >> 3, o = i & 7;
@@ -776,7 +858,7 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(wc[g * 8 + o], u[r]);
+      for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(W.c[g * 8 + o], u[r]);
     XR<R * 8, 32>::run(acc, lane);
     if (lane % RL == 0) {
       const int i = lane / RL;
@@ -962,22 +1044,29 @@ __device__ __forceinline__ void stage_final(const TeamArgs& a, Team& T, int step
 
 template <int R, int NBB>
 __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
+  WQ wq;
+  WK wo, wd;
+  WF wf;
   for (int step = 0; step < a.n_steps; ++step) {
     TEAM_TRACE(step, S_PRE);
-    stage_pre<R, NBB>(a, T, S, step);
+    stage_pre<R, NBB>(a, T, S, step, wq);
     for (int l = 0; l < a.n_layer; ++l) {
+      const bool last = l + 1 == a.n_layer;
       TEAM_TRACE(step, s_q(l));
-      stage_q<R>(a, T, S, step, l);
+      stage_q<R>(a, T, S, step, l, wq, wo);
       TEAM_TRACE(step, s_att(l));
       stage_att<R>(a, T, S, step, l);
       TEAM_TRACE(step, s_mrg(l));
       stage_mrg<R>(a, T, S, step, l);
       TEAM_TRACE(step, s_op(l));
-      stage_k1024<R>(T, S, lw(a, l, W_O), A_O, T.tag(step, s_mrg(l)), s_mrg(l), A_T, T.tag(step, s_op(l)));
+      stage_k1024<R>(T, S, wo, A_O, T.tag(step, s_mrg(l)), s_mrg(l), A_T, T.tag(step, s_op(l)),
+                     [&] { issue_ffn(a, T, l, wf); });
       TEAM_TRACE(step, s_ffn(l));
-      stage_ffn<R>(a, T, S, step, l);
+      stage_ffn<R>(a, T, S, step, l, wf, wd);
       TEAM_TRACE(step, s_dn(l));
-      stage_k1024<R>(T, S, lw(a, l, W_D), A_M, T.tag(step, s_ffn(l)), s_ffn(l), A_D, T.tag(step, s_dn(l)));
+      stage_k1024<R>(T, S, wd, A_M, T.tag(step, s_ffn(l)), s_ffn(l), A_D, T.tag(step, s_dn(l)), [&] {
+        if (!last) issue_q(a, T, l + 1, wq);
+      });
     }
     TEAM_TRACE(step, S_POST);
     stage_post<R, NBB>(a, T, S, step);
@@ -1006,6 +1095,10 @@ __global__ __launch_bounds__(256, 1) void k_team(TeamArgs a) {
   const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;  // XCC_ID
   if (xcc != (uint32_t)T.t && threadIdx.x == 0)
     __hip_atomic_fetch_or(a.status, kTeamMisplaced, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {  // the score tile's unused q columns (head slots 4 .. 7) stay zero for the whole launch
+    uint32_t* q = reinterpret_cast<uint32_t*>(&S.qop[0][0][0][0][0]);
+    for (int i = threadIdx.x; i < (int)(sizeof(S.qop) / 4); i += 256) q[i] = 0u;
+  }
   if (T.t < a.B) {
     T.R = (T.t + NT < a.B) ? 2 : 1;
     T.row0 = T.t;

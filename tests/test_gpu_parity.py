@@ -476,10 +476,12 @@ def test_caller_graph_capture_replays(name, shape, batch):
         assert other["next"].shape[0] == batch
 
 
-def test_kernel_timing_records_every_launch_and_keeps_results():
+@pytest.mark.parametrize("persistent", [0, 1])
+def test_kernel_timing_records_every_launch_and_keeps_results(persistent):
     """Timing records: one per kernel launch of the call, in launch order, with positive durations; the results
-    equal those of the graph-replayed call."""
-    case = Case(synth.E4B, batch=4, context=1200, ragged=True)
+    equal those of the graph-replayed (per-stage kernels) or plain (persistent kernel) call."""
+    from mtp_drafter_step_amd import abi
+    case = Case(synth.E4B, batch=4, context=1200, ragged=True, options={abi.MTPD_OPT_PERSISTENT: persistent})
     d = case.drafter
     ref = d.draft_block(2, case.th, case.tok, case.temb, case.kv, want_logits=True)
     ref = {k: v.clone() for k, v in ref.items()}
@@ -491,6 +493,10 @@ def test_kernel_timing_records_every_launch_and_keeps_results():
     for k in ref:
         assert torch.equal(out[k], ref[k]), k
     names = [r[0] for r in recs]
+    if persistent:  # every step of the call in one launch
+        assert names == ["team"], names
+        assert recs[0][1] > 0.0
+        return
     L = case.shape.n_layer
     per_step = ["pre"] + ["qproj", "attn", "o_proj", "ffn", "down"] * L + ["post", "head"]
     got = [("attn" if n.startswith("attn_") and "merge" not in n else n) for n in names if "merge" not in n]
