@@ -9,8 +9,11 @@ synthetic (seeded counter-based generator) and resident in HBM before the timed 
 heads over one kv head, batch 32, context 32768, window 1024) with the dense tied head over the full table.
 
 Prints one JSON line: draft tokens/s (value), µs per drafter step, the roofline of the dominant kernel (its
-algorithmic bytes per launch over its HIP-event launch duration, against 8 TB/s), and the CPU oracle timed on a
-bounded sample on this host.
+algorithmic bytes per launch over its HIP-event launch duration, against 8 TB/s; at batch <= 16 that kernel is the
+persistent one, whose launch is the whole draft block), warm (back to back) and cold (after a 1 GiB streaming read
+that evicts L2 and the memory-side cache), per launch site of the per-stage kernels as well, and the CPU oracle
+timed on a bounded sample on this host with all BLAS threads and with one.
+--cold-only runs only calls that each follow a sweep (for counter collection; prints no JSON line).
 
 Host-only helper modes (no GPU) turn rocprofv3 output of this script into the text summaries kept in profiles/:
   --summarize-stats DIR   kernel-trace statistics of a bench run
@@ -36,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 CSRC = os.path.join(ROOT, "mtp_drafter_step_amd", "csrc")
 # the source file of each kernel; a kernel's digest covers that file and the shared headers
-KERNEL_FILE = {"k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_attn_mq": "k_attention_shared.hip", "k_head": "k_head.hip",
+KERNEL_FILE = {"k_stream_read": "k_stream.hip", "k_attn_mfma": "k_attention.hip", "k_attn": "k_attention.hip", "k_attn_mq": "k_attention_shared.hip", "k_head": "k_head.hip",
                "k_head_dense": "k_head.hip", "k_final": "k_head.hip", "k_fill": "k_head.hip",
                "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip",
                "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip", "k_gemm": "k_gemm.hip",
@@ -173,11 +176,29 @@ def site_flops(site, shape, lens, shared):
     return 4.0 * shape.n_head * keys * shape.head_dim
 
 
+def host_cpu():
+    """(model name, usable cores) of this host, from /proc/cpuinfo and the process's CPU affinity."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
 def cpu_baseline(wl, seconds, w_dev=None, inp_dev=None):
-    """The oracle as it stands, on single-row drafter steps of the same workload, for about `seconds`. The weights
-    and inputs are the GPU-generated ones copied to the host when given (the generator is bit-identical on both
-    devices), else generated on the host."""
-    from threadpoolctl import threadpool_info
+    """The oracle as it stands, on single-row drafter steps of the same workload, for about `seconds` twice: with the
+    BLAS thread pools at their default size, then limited to one thread. The weights and inputs are the
+    GPU-generated ones copied to the host when given (the generator is bit-identical on both devices), else
+    generated on the host."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import torch
 
@@ -209,18 +230,31 @@ def cpu_baseline(wl, seconds, w_dev=None, inp_dev=None):
     rows_emb = synth.LazyRows(wl.seed, shape)
     for b in range(wl.batch):
         rows_emb[int(tok[b])]  # generate the embedding rows outside the timed loop
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        O.drafter_step(m, th, tok, rows_emb, kv, rows=[done % wl.batch])
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+
+    def timed():
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            O.drafter_step(m, th, tok, rows_emb, kv, rows=[done % wl.batch])
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        return done, time.perf_counter() - t0
+
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    done, dt = timed()
+    with threadpool_limits(limits=1):
+        done1, dt1 = timed()
+    model, cores = host_cpu()
     return {"value": done / dt, "unit": "draft tokens/s", "cores": int(threads), "kind": "oracle",
+            "us_per_drafter_step_per_row": dt / done * 1e6,
+            "host": {"cpu_model": model, "nproc": cores},
+            "one_thread": {"value": done1 / dt1, "unit": "draft tokens/s", "cores": 1,
+                           "us_per_drafter_step_per_row": dt1 / done1 * 1e6,
+                           "sample": f"{done1} single-row drafter steps, {dt1:.1f} s"},
             "sample": f"{done} single-row drafter steps of the {wl.name} workload (rows 0..{min(done, wl.batch) - 1},"
-                      f" first step of the block), fp64 NumPy oracle, {dt:.1f} s"}
+                      f" first step of the block), fp64 NumPy oracle with {threads} BLAS threads, {dt:.1f} s; then "
+                      f"the same with one thread"}
 
 
 def traffic_file(kernel, workload):
@@ -274,6 +308,29 @@ def run_bench(args):
                                          workspace=ws)
         return d.draft_block(n, th, tok, temb, kv, want_logits=True, out=out, workspace=ws)
 
+    def copy_probe():
+        # calibration copy of known size for the HBM byte counters (a plain device-to-device copy)
+        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if args.cold_only:  # profiling mode: every call after a sweep that evicts L2 and the memory-side cache
+        from mtp_drafter_step_amd import stream_read
+        sweep = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        for i in range(args.cold_steps):
+            stream_read(sweep, sink)
+            run()
+            torch.cuda.synchronize()
+            print(f"cold call {i + 1} of {args.cold_steps} done", flush=True)
+        del sweep
+        if args.copy_probe:
+            copy_probe()
+        return
+
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -311,30 +368,62 @@ def run_bench(args):
     value = B * n * args.steps / wall
     us_drafter_step = float(np.median(launch_ms)) * 1e3 / n
 
+    # the library's streaming read (one pass over 1 GiB) gives the measured read rate of this device and, run
+    # before a call, evicts L2 and the 256 MB memory-side cache with clean lines
+    from mtp_drafter_step_amd import stream_read
+    sweep = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    read_ms = []
+    for _ in range(8):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        stream_read(sweep, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        read_ms.append(e0.elapsed_time(e1))
+    read_gbs = sweep.numel() * 4 / (min(read_ms) * 1e-3) / 1e9
+
+    def flush():
+        stream_read(sweep, sink)
+
+    def timed_records(drafter, call, calls, cold):
+        """Per-launch (site, ms) records of `calls` calls in timing mode; with cold, a sweep before each call (the
+        sweep is not a recorded launch)."""
+        drafter.timing(True)
+        for _ in range(calls):
+            if cold:
+                flush()
+            call()
+        torch.cuda.synchronize()
+        drafter.timing(False)
+        return drafter.timing_records()
+
+    def tally(recs, calls, drafter_shape):
+        per_site = {}
+        for name, ms in recs:
+            per_site.setdefault(name, []).append(ms)
+        per_kernel = {}
+        for site, v in per_site.items():
+            k = site_kernel(site, drafter_shape, wl.shared_kv)
+            e = per_kernel.setdefault(k, {"launches": 0, "total_ms": 0.0, "bytes": 0.0, "sites": []})
+            e["launches"] += len(v)
+            e["total_ms"] += float(np.sum(v))
+            e["bytes"] += len(v) * site_launch_bytes(site)
+            fl = site_flops(site, shape, lens, wl.shared_kv)
+            if fl is not None:
+                e["flops"] = e.get("flops", 0.0) + len(v) * fl
+            e["sites"].append(site)
+        return per_site, per_kernel
+
+    def site_launch_bytes(site):
+        return sbytes * n if site == "team" else site_bytes(site, shape, B, lens, u_mean, shared=wl.shared_kv)
+
     # per-kernel durations: the same calls with every launch bracketed by HIP events that the runtime records at
-    # the kernel's start and end (on the library's launch stream, which is torch's current stream)
-    d.timing(True)
-    for _ in range(args.timing_steps):
-        run()
-    torch.cuda.synchronize()
-    d.timing(False)
-    recs = d.timing_records()
-    per_site = {}
-    for name, ms in recs:
-        per_site.setdefault(name, []).append(ms)
-    per_kernel = {}
-    for site, v in per_site.items():
-        k = site_kernel(site, shape, wl.shared_kv)
-        e = per_kernel.setdefault(k, {"launches": 0, "total_ms": 0.0, "bytes": 0.0, "sites": []})
-        e["launches"] += len(v)
-        e["total_ms"] += float(np.sum(v))
-        e["bytes"] += len(v) * (sbytes * n if site == "team" else site_bytes(site, shape, B, lens, u_mean,
-                                                                              shared=wl.shared_kv))
-        fl = site_flops(site, shape, lens, wl.shared_kv)
-        if fl is not None:
-            e["flops"] = e.get("flops", 0.0) + len(v) * fl
-        e["sites"].append(site)
+    # the kernel's start and end (on the library's launch stream, which is torch's current stream), warm (back to
+    # back) and cold (a sweep before each call)
     calls = args.timing_steps
+    per_site, per_kernel = tally(timed_records(d, run, calls, False), calls, shape)
+    cold_site, cold_kernel = tally(timed_records(d, run, args.cold_steps, True), args.cold_steps, shape)
     dom = max(per_kernel, key=lambda k: per_kernel[k]["total_ms"])
     dk = per_kernel[dom]
     avg_launch_s = dk["total_ms"] / dk["launches"] * 1e-3
@@ -342,63 +431,113 @@ def run_bench(args):
     achieved = bytes_per_launch / avg_launch_s / 1e9
     tr = load_traffic(dom, wl.name)
     traffic = None if tr is None else tr["hbm_bytes_per_launch"]
+    ck = cold_kernel.get(dom)
+    cold_launch_s = ck["total_ms"] / ck["launches"] * 1e-3 if ck else None
     if "flops" in dk:  # a dense contraction (attention over a cache shared by the rows): priced on the matrix cores
         tfl = dk["flops"] / dk["launches"] / avg_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": tfl, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tfl / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                 "algorithmic_flops_per_launch": dk["flops"] / dk["launches"], "algorithmic_GBs": achieved}
+        if cold_launch_s:
+            ctf = dk["flops"] / dk["launches"] / cold_launch_s / 1e12
+            roof["cold"] = {"avg_launch_us": cold_launch_s * 1e6, "achieved": ctf,
+                            "frac": ctf / MFMA_BF16_PEAK_TFLOPS}
     else:
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+        if cold_launch_s:
+            cga = bytes_per_launch / cold_launch_s / 1e9
+            roof["cold"] = {"avg_launch_us": cold_launch_s * 1e6, "achieved": cga, "frac": cga / HBM_PEAK_GBS,
+                            "frac_of_measured_read_peak": cga / read_gbs}
+        roof["frac_of_measured_read_peak"] = achieved / read_gbs
     roof.update({"kernel": dom, "launch_sites": sorted(set(dk["sites"])),
+                 "scope": ("the whole drafter step: one launch runs every step of a draft block" if dom == "k_team"
+                           else "the dominant kernel (step_roofline has the whole step)"),
                  "launches_per_drafter_step": dk["launches"] / (calls * n),
                  "avg_launch_us": avg_launch_s * 1e6, "algorithmic_bytes_per_launch": bytes_per_launch,
                  "traffic_source": None if tr is None else os.path.relpath(traffic_file(dom, wl.name), ROOT)})
-    kernels_table = {k: {"launches_per_drafter_step": v["launches"] / (calls * n),
-                         "avg_launch_us": v["total_ms"] / v["launches"] * 1e3,
-                         "us_per_drafter_step": v["total_ms"] * 1e3 / (calls * n),
-                         "algorithmic_GBs": v["bytes"] / (v["total_ms"] * 1e-3) / 1e9,
-                         "algorithmic_TFLOPs": (v["flops"] / (v["total_ms"] * 1e-3) / 1e12) if "flops" in v else None,
-                         "sites": sorted(set(v["sites"]))}
-                     for k, v in sorted(per_kernel.items(), key=lambda kv_: -kv_[1]["total_ms"])}
 
-    # cold regime: before each timed call a 1 GiB read sweep evicts L2 and the memory-side cache (the first drafter
-    # step of the block starts cold; the next three run on what it brought in)
-    sweep = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-    # the measured streaming-read rate of this device: the best of a few row-wise reductions over the resident
-    # 1 GiB tensor (rows of 4096 floats, and 4096 rows), whose output is negligible next to the bytes read
-    read_ms = []
-    for rows in ((-1, 4096), (4096, -1)):
-        for _ in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            sweep.view(*rows).sum(dim=1)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            read_ms.append(e0.elapsed_time(e1))
-    read_gbs = sweep.numel() * 4 / (min(read_ms) * 1e-3) / 1e9
-    if roof["bound"] == "hbm":
-        roof["frac_of_measured_read_peak"] = roof["achieved"] / read_gbs
-    cold_ms = []
+    def kernels_of(pk, ncalls):
+        return {k: {"launches_per_drafter_step": v["launches"] / (ncalls * n),
+                    "avg_launch_us": v["total_ms"] / v["launches"] * 1e3,
+                    "us_per_drafter_step": v["total_ms"] * 1e3 / (ncalls * n),
+                    "algorithmic_GBs": v["bytes"] / (v["total_ms"] * 1e-3) / 1e9,
+                    "algorithmic_TFLOPs": (v["flops"] / (v["total_ms"] * 1e-3) / 1e12) if "flops" in v else None,
+                    "sites": sorted(set(v["sites"]))}
+                for k, v in sorted(pk.items(), key=lambda kv_: -kv_[1]["total_ms"])}
+
+    def sites_of(warm, cold, ncalls):
+        out_ = {}
+        for site, v in sorted(warm.items(), key=lambda kv_: -sum(kv_[1])):
+            b = site_launch_bytes(site)
+            wu = float(np.mean(v)) * 1e3
+            e = {"launches_per_drafter_step": len(v) / (ncalls * n), "avg_launch_us": wu,
+                 "algorithmic_bytes_per_launch": b, "GBs": b / (wu * 1e-6) / 1e9,
+                 "frac": b / (wu * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            if site in cold:
+                cu = float(np.mean(cold[site])) * 1e3
+                e.update({"cold_avg_launch_us": cu, "cold_GBs": b / (cu * 1e-6) / 1e9,
+                          "cold_frac": b / (cu * 1e-6) / 1e9 / HBM_PEAK_GBS})
+            out_[site] = e
+        return out_
+
+    kernels_table = kernels_of(per_kernel, calls)
+    sites_table = sites_of(per_site, cold_site, calls)
+
+    # the per-stage kernels on the same inputs (the path taken when the persistent kernel does not apply): warm and
+    # cold per launch site, e.g. the full and the sliding attention separately
+    per_stage = None
+    if dom == "k_team" and not args.no_per_stage:
+        from mtp_drafter_step_amd import abi as _abi
+        d2 = Drafter(shape, w, max_batch=B, options={_abi.MTPD_OPT_PERSISTENT: 0})
+        out2 = {}
+        ws2 = d2.workspace(B)
+
+        def run2():
+            return d2.draft_block(n, th, tok, temb, kv, want_logits=True, out=out2, workspace=ws2)
+
+        for _ in range(3):
+            run2()
+        torch.cuda.synchronize()
+        ps_warm, _ = tally(timed_records(d2, run2, calls, False), calls, shape)
+        ps_cold, _ = tally(timed_records(d2, run2, args.cold_steps, True), args.cold_steps, shape)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            run2()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_stage = {"us_per_drafter_step": e0.elapsed_time(e1) * 1e3 / (calls * n),
+                     "sites": sites_of(ps_warm, ps_cold, calls)}
+        d2.close()
+        del d2, ws2, out2
+
+    # cold regime for the whole call: a sweep before each timed call (the first drafter step of the block starts
+    # cold; the next ones run on what it brought in), and single drafter steps after a sweep each
+    cold_ms, cold_step_ms = [], []
     for _ in range(args.cold_steps):
-        sweep.sum()
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         run()
         e1.record(stream)
         torch.cuda.synchronize()
         cold_ms.append(e0.elapsed_time(e1))
+    out1 = {}
+    for _ in range(args.cold_steps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        d.drafter_step(th, tok, temb, kv, want_logits=True, out=out1, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_step_ms.append(e0.elapsed_time(e1))
     del sweep
     us_cold = float(np.median(cold_ms)) * 1e3 / n if cold_ms else None
+    us_cold_step = float(np.median(cold_step_ms)) * 1e3 if cold_step_ms else None
 
     if args.copy_probe:
-        # calibration copy of known size for the HBM byte counters (a plain device-to-device copy)
-        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe()
 
     res = {
         "metric": "draft tokens/sec and µs per drafter step; achieved HBM GB/s vs roofline",
@@ -419,15 +558,19 @@ def run_bench(args):
                           "distinct_clusters_per_step": U,
                           "achieved_GBs": sbytes / (us_drafter_step * 1e-6) / 1e9,
                           "frac": sbytes / (us_drafter_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                          "cold_us_per_drafter_step": us_cold,
-                          "cold_achieved_GBs": sbytes / (us_cold * 1e-6) / 1e9 if us_cold else None,
-                          "measured_read_peak_GBs": read_gbs,
-                          "frac_of_measured_read_peak": sbytes / (us_drafter_step * 1e-6) / 1e9 / read_gbs},
-        "measured_read_peak": {"GBs": read_gbs, "how": "best of 8 row-wise torch sums over a resident 1 GiB fp32 "
-                                                       "tensor (4096-wide rows and 4096 rows), timed with HIP events"},
+                          "frac_of_measured_read_peak": sbytes / (us_drafter_step * 1e-6) / 1e9 / read_gbs,
+                          "cold_block_us_per_drafter_step": us_cold,
+                          "cold_block_frac": sbytes / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS if us_cold else None,
+                          "cold_single_step_us": us_cold_step,
+                          "cold_single_step_frac": (sbytes / (us_cold_step * 1e-6) / 1e9 / HBM_PEAK_GBS
+                                                    if us_cold_step else None),
+                          "us_per_drafter_step_for_60pct": sbytes / (0.6 * HBM_PEAK_GBS * 1e9) * 1e6},
+        "measured_read_peak": {"GBs": read_gbs, "how": "best of 8 passes of the library's streaming read "
+                                                       "(mtpd_stream_read) over a resident 1 GiB buffer, timed "
+                                                       "with HIP events"},
         "kernels": kernels_table,
-        "sites": {site: {"launches_per_drafter_step": len(v) / (calls * n), "avg_launch_us": float(np.mean(v)) * 1e3}
-                  for site, v in sorted(per_site.items(), key=lambda kv_: -sum(kv_[1]))},
+        "sites": sites_table,
+        "per_stage_kernels": per_stage,
         "kernel_source_sha256_16": source_digest(dom),
     }
     if not args.no_cpu_baseline:
@@ -537,8 +680,12 @@ def main():
     ap.add_argument("--workload", default="e4b_b16_ctx8192_block4")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="time draft_block_sampled at this temperature instead of the argmax draft_block")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle seconds per thread setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-stage", action="store_true", help="skip timing the per-stage kernels beside the "
+                                                                 "persistent kernel")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="profiling mode: only calls after a cache-evicting sweep each (no JSON line)")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter calibration copy after timing")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))

@@ -58,7 +58,8 @@ typedef struct mtpd_handle_s *mtpd_handle;
  * centroid_intermediate_top_k), "Variants supported" (4 layers, hidden 256, KV heads); [Inventory]
  * "HF config highlights" (three sliding + one full layer, attention_k_eq_v, vocab 262144).
  * Rules checked by mtpd_create: all sizes > 0 except n_centroids; n_head / n_kv_head in {1,2,4,8}; head_dim in
- * {64,128,256}; hidden, backbone, ffn, n_head*head_dim multiples of 256 (hidden <= 1024); n_layer <= 32.
+ * {64,128,256}; hidden, backbone, ffn, n_head*head_dim multiples of 256 (hidden <= 1024, backbone <= 8192, ffn and
+ * n_head*head_dim <= 4096); n_layer <= 32.
  * Masked head (n_centroids > 0): vocab % n_centroids == 0; top_k <= min(n_centroids, 64); vocab / n_centroids a
  * multiple of 16, <= 1024; n_centroids <= 4096.
  * Dense tied head (n_centroids == 0: the use_ordered_embeddings=false form, [Guide] section 5; [MTP doc]
@@ -222,7 +223,8 @@ MTPD_API int mtpd_sample_head(mtpd_handle h, void *stream, void *workspace, int3
  *                        that cannot finish gives up after a bounded time and is reported by mtpd_fault_status).
  *                        0: the per-stage kernels.
  *   MTPD_OPT_DENSE_PATH  0 (default): dense stages by batch size (fused small-batch kernels below 32 rows, matrix-core
- *                        GEMMs from 32 rows); 1: always the small-batch kernels; 2: always the GEMMs.
+ *                        GEMMs from 32 rows); 1: always the small-batch kernels; 2: always the GEMMs. A backbone
+ *                        above 4096 always runs the small-batch kernels (the GEMMs reduce over at most 8192).
  *   MTPD_OPT_ATTN_VALU   0 (default); 1: the vector-ALU attention kernel for every shape.
  * Returns MTPD_OK or MTPD_EINVAL (unknown option or value). */
 enum { MTPD_OPT_GRAPHS = 1, MTPD_OPT_PERSISTENT = 2, MTPD_OPT_DENSE_PATH = 3, MTPD_OPT_ATTN_VALU = 4 };
@@ -249,11 +251,19 @@ MTPD_API int mtpd_timing_enable(mtpd_handle h, int32_t enable);
  * or a negative error code. */
 MTPD_API int32_t mtpd_timing_read(mtpd_handle h, int32_t cap, const char **names, float *ms);
 
+/* Streaming read, a measurement aid outside the method: reads `bytes` at buf (device memory, 16-byte aligned,
+ * bytes a multiple of 16) with 16-byte vector loads spread over every CU, enqueued on `stream`, and writes nothing
+ * but possibly sink[0] (a caller-owned device word, written only if the xor of every word read equals `key`). One
+ * call over a buffer much larger than the last-level caches (1 GiB against 8 x 4 MB L2 and the 256 MB memory-side
+ * cache) measures the sustained read rate and leaves the caches holding that buffer's clean lines.
+ * Returns MTPD_OK, MTPD_EINVAL (NULL or misaligned pointer, bytes not a multiple of 16) or MTPD_EHIP. */
+MTPD_API int mtpd_stream_read(const void *buf, uint64_t bytes, uint32_t key, uint32_t *sink, void *stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 MTPD_API const char *mtpd_last_error(void);
 
-/* ABI version: 5 (mtpd_kv gained `first` in 2 and `shared` in 3; mtpd_drafter_step_noalloc in 4; options and
- * the persistent kernel's status in 5). */
+/* ABI version: 6 (mtpd_kv gained `first` in 2 and `shared` in 3; mtpd_drafter_step_noalloc in 4; options and
+ * the persistent kernel's status in 5; mtpd_stream_read in 6). */
 MTPD_API int32_t mtpd_abi_version(void);
 
 #ifdef __cplusplus

@@ -18,7 +18,7 @@ MTPD_MAX_TIMED = 4096
 SYMBOLS = ("mtpd_create", "mtpd_destroy", "mtpd_workspace_bytes", "mtpd_drafter_step", "mtpd_draft_block",
            "mtpd_masked_head", "mtpd_last_error", "mtpd_abi_version", "mtpd_timing_enable", "mtpd_timing_read",
            "mtpd_draft_block_sampled", "mtpd_sample_head", "mtpd_drafter_step_noalloc", "mtpd_set_option",
-           "mtpd_fault_status")
+           "mtpd_fault_status", "mtpd_stream_read")
 # handle options (include/mtpd.h)
 MTPD_OPT_GRAPHS, MTPD_OPT_PERSISTENT, MTPD_OPT_DENSE_PATH, MTPD_OPT_ATTN_VALU = 1, 2, 3, 4
 MTPD_NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -100,6 +100,8 @@ def lib() -> C.CDLL:
     L.mtpd_set_option.restype = C.c_int
     L.mtpd_fault_status.argtypes = [vp, C.c_int32]
     L.mtpd_fault_status.restype = C.c_int32
+    L.mtpd_stream_read.argtypes = [vp, C.c_uint64, C.c_uint32, vp, vp]
+    L.mtpd_stream_read.restype = C.c_int
     L.mtpd_timing_enable.argtypes = [vp, C.c_int32]
     L.mtpd_timing_enable.restype = C.c_int
     L.mtpd_timing_read.argtypes = [vp, C.c_int32, C.POINTER(C.c_char_p), f32p]

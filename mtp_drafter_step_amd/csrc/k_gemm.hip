@@ -350,7 +350,7 @@ int gemm_chunks(int B, int N, int K, bool one_chunk) {
 hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float* X, const uint16_t* th,
                        const uint16_t* emb, const int32_t* tok, int Bb, float escale, const uint16_t* W,
                        const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks, FillRange fill) {
-  if (K % 256 || N % 16 || K > 4096 * 2 || (K / 256) % nchunks) return hipErrorInvalidValue;
+  if (K % 256 || N % 16 || K > kGemmMaxK || (K / 256) % nchunks) return hipErrorInvalidValue;
   const int KC = K / nchunks;
   // waves per 16-row tile: more only while the grid is below about 256 blocks (each block stages its X chunk, so
   // more blocks cost L2 reads), and at most KC / 256

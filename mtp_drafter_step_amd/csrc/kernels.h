@@ -16,6 +16,7 @@ constexpr int kRowGroup = 4;   // batch rows handled together by the dense kerne
 constexpr int kMaxTopK = 64;   // clusters kept per row
 constexpr int kMaxCentroids = 4096;
 constexpr int kMaxSampleTiles = 256;  // sampled rows hold at most 256 * 4096 scored tokens
+constexpr int kGemmMaxK = 8192;      // reduction length of the streaming matrix-core GEMM
 
 // Per-row key window [start, start + count) of one cache, passed by value; start < cap, count <= cap, and indices
 // from cap on wrap to slot index - cap.
@@ -248,5 +249,9 @@ hipError_t launch_team(hipStream_t s, const TeamArgs& a);
 #ifdef MTPD_TEAM_TRACE
 hipError_t team_trace_read(uint64_t* host);  // measurement builds: the last launch's stage timeline
 #endif
+
+// Measurement helper (k_stream.hip): read `bytes` (a multiple of 16, 16-byte aligned buffer) with streaming vector
+// loads; sink[0] is written only if the xor of all words equals key.
+hipError_t launch_stream_read(hipStream_t s, const void* buf, uint64_t bytes, uint32_t key, uint32_t* sink);
 
 }  // namespace mtpd

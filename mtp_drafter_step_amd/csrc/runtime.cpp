@@ -378,6 +378,8 @@ int run_step_small(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& 
 constexpr int kGemmRows = 32;
 
 bool use_gemm_path(const mtpd_handle_s* h, int B) {
+  // the pre_projection GEMM takes K = 2 * backbone <= 8192; wider backbones keep the small-batch kernels
+  if (2 * h->cfg.backbone > mtpd::kGemmMaxK) return false;
   if (h->dense_path == 1) return false;
   if (h->dense_path == 2) return true;
   return B >= kGemmRows;
@@ -790,7 +792,7 @@ CallKey make_key(int kind, int B, int n, std::initializer_list<const void*> ptrs
 
 extern "C" {
 
-int32_t mtpd_abi_version(void) { return 5; }
+int32_t mtpd_abi_version(void) { return 6; }
 
 const char* mtpd_last_error(void) { return g_last_error.c_str(); }
 
@@ -1178,6 +1180,16 @@ int mtpd_sample_head(mtpd_handle h, void* stream, void* workspace, int32_t m, co
       }
       return run_sample(h, cs, wsc, p, Bc, lc, temperature, uniforms + b0, token + b0, prob ? prob + b0 : nullptr, 1);
   });
+}
+
+int mtpd_stream_read(const void* buf, uint64_t bytes, uint32_t key, uint32_t* sink, void* stream) {
+  g_last_error.clear();
+  if (!buf || (reinterpret_cast<uintptr_t>(buf) & 15)) return fail(MTPD_EINVAL, "buf is NULL or not 16-byte aligned");
+  if (!sink || (reinterpret_cast<uintptr_t>(sink) & 3)) return fail(MTPD_EINVAL, "sink is NULL or misaligned");
+  if (bytes % 16) return fail(MTPD_EINVAL, "bytes must be a multiple of 16");
+  const hipError_t e = mtpd::launch_stream_read(static_cast<hipStream_t>(stream), buf, bytes, key, sink);
+  if (e != hipSuccess) return fail(MTPD_EHIP, "stream_read: %s", hipGetErrorString(e));
+  return MTPD_OK;
 }
 
 int mtpd_set_option(mtpd_handle h, int32_t option, int32_t value) {

@@ -27,6 +27,16 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, key: int = 0x5EED5EED) -> None:
+    """Measurement aid (mtpd_stream_read): one streaming read of the whole contiguous device tensor `buf` on torch's
+    current stream; `sink` is a device int32/uint32 tensor of at least one element."""
+    if not (buf.is_cuda and buf.is_contiguous() and sink.is_cuda and sink.numel() >= 1):
+        raise ValueError("stream_read needs a contiguous device buffer and a device sink")
+    nbytes = buf.numel() * buf.element_size()
+    abi.check(abi.lib().mtpd_stream_read(buf.data_ptr(), nbytes - nbytes % 16, key & 0xFFFFFFFF, sink.data_ptr(),
+                                         _stream()))
+
+
 class SharedKV:
     """The two target caches ([batch][n_kv][cap][head_dim] bf16 device tensors, v may be k), HOST per-row lengths,
     optional HOST per-row first slots (left padding, ring buffers), and the rotary table [batch][2][2][head_dim/2]

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mtpd_\w+)", out))
     assert exported == set(declared_functions())
-    assert L.mtpd_abi_version() == 5
+    assert L.mtpd_abi_version() == 6
 
 
 def test_struct_layout_matches_c(tmp_path):
@@ -88,6 +88,27 @@ def create_rc(cfg, weights=None, max_batch=16):
 def test_create_rejects_bad_config(over, code, msg):
     rc, err = create_rc(good_config(**over))
     assert rc == code and msg in err
+
+
+def test_backbone_limit():
+    """backbone up to 8192 passes the config checks (the first error is then the NULL weights); above, ESHAPE."""
+    rc, err = create_rc(good_config(backbone=8448))
+    assert rc == abi.MTPD_ESHAPE and "backbone" in err
+    for bb in (4096, 4352, 8192):
+        rc, err = create_rc(good_config(backbone=bb))
+        assert rc == abi.MTPD_EINVAL and "weights" in err, (bb, err)
+
+
+def test_stream_read_rejects_bad_arguments():
+    """The measurement read checks its pointers and size on the host, before any device work."""
+    L = abi.lib()
+    sink = 0x2000
+    assert L.mtpd_stream_read(None, 16, 0, sink, None) == abi.MTPD_EINVAL
+    assert L.mtpd_stream_read(0x1008, 16, 0, sink, None) == abi.MTPD_EINVAL
+    assert "aligned" in L.mtpd_last_error().decode()
+    assert L.mtpd_stream_read(0x1000, 24, 0, sink, None) == abi.MTPD_EINVAL
+    assert "multiple of 16" in L.mtpd_last_error().decode()
+    assert L.mtpd_stream_read(0x1000, 16, 0, None, None) == abi.MTPD_EINVAL
 
 
 def test_create_rejects_null_and_misaligned_weights():
