@@ -292,7 +292,8 @@ def run_bench(args):
     inp = synth.make_inputs(wl, device=dev, with_target_embd=True)
     kv = SharedKV(inp["k_sliding"], inp["k_full"], inp["len_sliding"], inp["len_full"], inp["rope"],
                   shared=wl.shared_kv)
-    d = Drafter(shape, w, max_batch=B)
+    from mtp_drafter_step_amd import abi as _abi
+    d = Drafter(shape, w, max_batch=B, options={_abi.MTPD_OPT_PERSISTENT: args.persistent})
     out = {}
     ws = d.workspace(B)
     th, tok, temb = inp["target_hidden"], inp["last_token"], inp["target_embd"]
@@ -488,7 +489,6 @@ def run_bench(args):
     # cold per launch site, e.g. the full and the sliding attention separately
     per_stage = None
     if dom == "k_team" and not args.no_per_stage:
-        from mtp_drafter_step_amd import abi as _abi
         d2 = Drafter(shape, w, max_batch=B, options={_abi.MTPD_OPT_PERSISTENT: 0})
         out2 = {}
         ws2 = d2.workspace(B)
@@ -603,7 +603,9 @@ def summarize_stats(args):
              "Kernel source sha256[:16]: " + ", ".join(
                  f"{f} `{source_digest(k)}`" for f, k in (("k_layers.hip", "k_ffn"), ("k_attention.hip", "k_attn_mfma"),
                                                           ("k_attention_shared.hip", "k_attn_mq"),
-                                                          ("k_head.hip", "k_head"), ("k_gemm.hip", "k_gemm"))), "",
+                                                          ("k_head.hip", "k_head"), ("k_gemm.hip", "k_gemm"),
+                                                          ("k_team.hip", "k_team"),
+                                                          ("k_stream.hip", "k_stream_read"))), "",
              "Only the library's kernels are listed (the run also holds the input generator's and torch's own "
              "kernels, which are outside the timed calls).", "",
              "| kernel | calls | avg µs | min µs | max µs | total µs | share of library time |", "|---|---|---|---|---|---|---|"]
@@ -612,6 +614,20 @@ def summarize_stats(args):
         lines.append(f"| `{_stem(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / tot:.1f}% |")
+    # the persistent kernel runs whole draft blocks and single drafter steps: its dispatches split by duration
+    trace = glob.glob(os.path.join(args.summarize_stats, "**", "*kernel_trace.csv"), recursive=True)
+    if trace:
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(open(trace[0]))
+                if _stem(r["Kernel_Name"]).startswith("k_team")]
+        if durs:
+            cut = 0.6 * max(durs)
+            lines += ["", "Persistent kernel dispatches by kind (from the kernel trace; a draft_block(4) launch runs four "
+                          "steps, so the two kinds separate by duration):", "",
+                      "| kind | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+            for kind, v in (("draft_block(4)", [x for x in durs if x >= cut]),
+                            ("drafter_step", [x for x in durs if x < cut])):
+                if v:
+                    lines.append(f"| {kind} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, f"drafter_kernels__{args.workload}.stats.md")
     open(out, "w").write("\n".join(lines) + "\n")
@@ -646,6 +662,15 @@ def summarize_pmc(args):
         out[counter] = {"kernel_kib_per_dispatch": sum(kv) / len(kv), "dispatches": len(kv),
                         "copy_kib": copy_kib, "copy_known_kib": COPY_PROBE_BYTES / 1024.0, "factor": factor,
                         "bytes_per_launch": sum(kv) / len(kv) * 1024.0 * factor}
+        if counter == "FETCH_SIZE" and max(kv) > 4 * max(min(kv), 1e-9):
+            # launches of very different size (the full layer's attention against the sliding layers'): the two
+            # groups separately, split at a quarter of the largest
+            big_ = [x for x in kv if x >= max(kv) / 4]
+            small_ = [x for x in kv if x < max(kv) / 4]
+            out[counter]["groups"] = {"large": {"dispatches": len(big_),
+                                                "bytes_per_launch": sum(big_) / len(big_) * 1024.0 * factor},
+                                      "small": {"dispatches": len(small_),
+                                                "bytes_per_launch": sum(small_) / len(small_) * 1024.0 * factor}}
     total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
     t = {"kernel": args.kernel, "workload": args.workload, "hbm_bytes_per_launch": total,
          "fetch_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"],
@@ -663,6 +688,13 @@ def summarize_pmc(args):
         o = out[c]
         lines.append(f"| {c} | {o['kernel_kib_per_dispatch']:.1f} | {o['dispatches']} | {o['copy_kib']:.1f} | "
                      f"{o['copy_known_kib']:.1f} | {o['factor']:.4f} | {o['bytes_per_launch']:.0f} |")
+    g = out["FETCH_SIZE"].get("groups")
+    if g:
+        t["fetch_groups"] = g
+        lines += ["", "FETCH_SIZE by launch size (split at a quarter of the largest dispatch):", "",
+                  "| group | dispatches | fetch bytes / launch |", "|---|---|---|"]
+        for k in ("large", "small"):
+            lines.append(f"| {k} | {g[k]['dispatches']} | {g[k]['bytes_per_launch']:.0f} |")
     lines += ["", f"HBM bytes per launch (fetch + write): {total:.0f}", "", f"<!-- traffic-json: {json.dumps(t)} -->"]
     os.makedirs(PROFILES, exist_ok=True)
     p = traffic_file(args.kernel, args.workload)
@@ -684,6 +716,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-stage", action="store_true", help="skip timing the per-stage kernels beside the "
                                                                  "persistent kernel")
+    ap.add_argument("--persistent", type=int, choices=(0, 1), default=1,
+                    help="0: time the per-stage kernels only (the persistent kernel switched off)")
     ap.add_argument("--cold-only", action="store_true",
                     help="profiling mode: only calls after a cache-evicting sweep each (no JSON line)")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter calibration copy after timing")
