@@ -1085,21 +1085,26 @@ __global__ __launch_bounds__(256, 1) void k_team(TeamArgs a) {
   __shared__ Smem S;
   __shared__ uint8_t pad[kLdsPad > 0 ? kLdsPad : 1];
   if (threadIdx.x == 0) pad[0] = 0;
+  // The dispatcher deals the blocks out to the XCDs in turn, starting where the previous launch left off: block b
+  // runs on XCD (b + k) mod 8 for some k of the launch. The team is the XCD the block runs on (read from the
+  // hardware), so a team's 32 blocks share that XCD's L2 and each XCD always uses the same exchange words; b / 8 is
+  // then a distinct member index within every team.
+  const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;  // XCC_ID
   Team T;
-  T.t = blockIdx.x & (NT - 1);
+  T.t = (int)(xcc & (NT - 1));
   T.m = blockIdx.x >> 3;
   T.status = a.status;
   T.dead = false;
   T.X = a.xch + (size_t)T.t * TEAM_WORDS;
   T.E = __hip_atomic_load(a.epoch + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;  // XCC_ID
-  if (xcc != (uint32_t)T.t && threadIdx.x == 0)
+  const bool placed = xcc < (uint32_t)NT;  // else not the 8-XCD layout this kernel is built for: no team work
+  if (!placed && threadIdx.x == 0)
     __hip_atomic_fetch_or(a.status, kTeamMisplaced, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   {  // the score tile's unused q columns (head slots 4 .. 7) stay zero for the whole launch
     uint32_t* q = reinterpret_cast<uint32_t*>(&S.qop[0][0][0][0][0]);
     for (int i = threadIdx.x; i < (int)(sizeof(S.qop) / 4); i += 256) q[i] = 0u;
   }
-  if (T.t < a.B) {
+  if (placed && T.t < a.B) {
     T.R = (T.t + NT < a.B) ? 2 : 1;
     T.row0 = T.t;
     T.row1 = T.t + NT;

@@ -195,7 +195,7 @@ constexpr int kTeamMaxLayers = 4;
 constexpr int kTeamBlocks = 256;
 // status bits
 constexpr uint32_t kTeamTimeout = 1u;    // a wait ran out (the first stage id that did is in status[1] + 1)
-constexpr uint32_t kTeamMisplaced = 2u;  // a block found itself on another XCD than its team's
+constexpr uint32_t kTeamMisplaced = 2u;  // a block ran on an XCD outside the 8 the teams are built for
 
 struct TeamLayer {
   const uint16_t *q, *q_norm, *o, *attn_norm, *post_attn_norm, *ffn_norm, *post_ffw_norm, *gate, *up, *down;

@@ -103,15 +103,16 @@ def test_masked_head_shapes(name, m):
     assert tally.sel_checked >= m // 2
 
 
-@pytest.mark.parametrize("batch", [1, 64])
+@pytest.mark.parametrize("batch", [1, 64, 65, 256])
 @pytest.mark.parametrize("ntie", [20, 40, 100])
 def test_masked_head_exact_ties(ntie, batch):
     """Centroid rows 0 .. ntie-1 are copies of row ntie and h points along that row, so those ntie + 1 scores tie
     exactly (identical terms in the same order) and lie far above every other score. Ties go to the lower index, so
     the first slots must be centroids 0, 1, 2, ... in order. With 20 ties the rest of the slots come from the
     untied scores; 40 tied members are ordered by the small in-wave sort of the one-row-per-block head, 100 by its
-    rank-by-index path. At batch 64 every row is the same and the head takes its per-row selection and per-cluster
-    scoring, each cluster then serving all 64 rows."""
+    rank-by-index path. From batch 64 every row is the same and the head takes its per-row selection and per-cluster
+    scoring, each cluster then serving every row: one 64-entry tile per cluster at 64 rows, two (64 + 1) at 65 and
+    four at 256. Every row is compared."""
     from mtp_drafter_step_amd import Drafter
     say(f"masked_head ties={ntie} batch={batch}")
     case = Case(synth.E4B, batch=1, context=16, max_batch=batch)
@@ -142,6 +143,7 @@ def test_masked_head_exact_ties(ntie, batch):
             assert rel_ok(out["z"][r].cpu().numpy(), ref["z"])
         compare_head_row(tally, case.model.cfg, refl, 0, sel, out["ids"][r].cpu().numpy(), out["z"][r].cpu().numpy(),
                          int(out["argmax"][r]), out["logits"][r].cpu().numpy(), where=f"ties row {r}")
+    say(tally.summary())
 
 
 STEP_CASES = {
@@ -307,15 +309,51 @@ def test_shared_cache_rows(name):
 
 def test_verify_width_step():
     """The verify-width workload: 256 rows of one sequence sharing one cache of 131072 keys (window 1024), the
-    largest batch the ABI takes; sampled rows against the oracle."""
+    largest batch the ABI takes. Rows 0 .. 63 repeat row 0's target hidden state and token, so each of their clusters
+    is chosen by 64 rows (one full tile of the grouped head per cluster); 16 rows against the oracle: four of the
+    repeated group and twelve spread over the rest, and the repeated rows equal to each other bit for bit."""
     say("verify width: 256 rows, shared 131072-key cache")
     case = Case(synth.E4B, batch=256, context=131072, gen_device="cuda", shared_kv=True, swa_window=1024)
-    out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+    th = case.th.clone()
+    tok = case.tok.clone()
+    th[1:64] = th[0]
+    tok[1:64] = tok[0]
+    out = case.drafter.drafter_step(th, tok, case.temb, case.kv, want_logits=True, want_sparse=True)
     torch.cuda.synchronize()
-    rows = [0, 97, 255]
-    tally = compare_step(case, out, case.oracle_step(rows=rows), rows, where="verify")
+    for k in ("next", "hidden_out", "sel", "ids", "z", "logits"):
+        assert torch.equal(out[k][1:64], out[k][0:1].expand_as(out[k][1:64])), k
+    rows = [0, 1, 31, 63] + list(range(64, 256, 17))[:11] + [255]
+    thn = th.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = case.oracle_step(rows=rows, th=thn, tok=tok.cpu().numpy())
+    tally = compare_step(case, out, ref, rows, where="verify")
     say(tally.summary())
-    assert tally.sel_checked >= 2
+    assert tally.rows == 16 and tally.sel_checked >= 12
+
+
+def test_verify_width_head_shared_clusters():
+    """The grouped head at verify width on rows that share most of their clusters: 8 distinct fp32 states, each
+    repeated over 32 rows with a small per-row perturbation; all 256 rows against the oracle's head on the same
+    input."""
+    say("verify width head: 256 rows in 8 groups of near-identical states")
+    case = Case(synth.E4B, batch=1, context=16, max_batch=256)
+    g = torch.Generator().manual_seed(7)
+    base = torch.randn(8, case.shape.hidden, generator=g, dtype=torch.float32) * 3.0
+    h = base.repeat_interleave(32, dim=0) + 0.01 * torch.randn(256, case.shape.hidden, generator=g)
+    out = case.drafter.masked_head(h.cuda(), want_logits=True, want_sparse=True)
+    torch.cuda.synchronize()
+    tally = Tally()
+    shared = 0
+    for r in range(256):
+        ref = O.masked_head_row(case.model, h[r].numpy().astype(np.float64))
+        refl = {key: [ref[key]] for key in ("sel", "ids", "z", "cgap", "margin", "next")}
+        sel = out["sel"][r].cpu().numpy()
+        if r % 32:
+            shared += len(set(sel.tolist()) & set(out["sel"][r - r % 32].cpu().numpy().tolist()))
+        compare_head_row(tally, case.model.cfg, refl, 0, sel, out["ids"][r].cpu().numpy(), out["z"][r].cpu().numpy(),
+                         int(out["argmax"][r]), out["logits"][r].cpu().numpy(), where=f"shared row {r}")
+    frac = shared / (248 * case.shape.top_k)
+    say(tally.summary() + f" clusters shared with the group's first row: {frac:.2f}")
+    assert frac > 0.7 and tally.sel_checked >= 128
 
 
 GEMM_PATH_CASES = {

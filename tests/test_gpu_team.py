@@ -85,3 +85,28 @@ def test_team_against_per_stage_kernels():
     same = int((a["next"] == b["next"]).sum())
     say(f"tokens equal on {same} of 16 rows")
     assert same >= 14
+
+
+def test_team_after_launches_of_every_size_mod_8():
+    """The dispatcher hands blocks to the XCDs in turn from where the previous launch stopped, so the persistent
+    kernel's block b can land on any XCD. Before each call, a streaming read of k 32 KB chunks (k blocks, k = 0..7)
+    shifts that start; every call must finish its waits and give the same outputs bit for bit."""
+    from mtp_drafter_step_amd import stream_read
+    case = Case(synth.E4B, batch=16, context=1200, ragged=True)
+    d = case.drafter
+    buf = torch.ones(8 * 8192, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ref = None
+    for k in range(8):
+        if k:
+            stream_read(buf[: k * 8192], sink)
+        out = d.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
+        torch.cuda.synchronize()
+        _check_status(d)
+        got = {key: v.clone() for key, v in out.items()}
+        if ref is None:
+            ref = got
+            continue
+        for key in ref:
+            assert torch.equal(got[key], ref[key]), (k, key)
+    say("outputs identical after launches of 1..7 blocks")
