@@ -11,9 +11,10 @@
 // Shapes: hidden 256, 4 query heads of 256 over one K = V head, FFN 1024, 2048 centroids of 128 tokens, top 32, up
 // to 4 layers, backbone a multiple of 512 (the E2B and E4B drafters of [MTP doc] "Variants supported").
 //
-// Layout of the work. Block b runs on XCD b % 8 (the dispatcher deals workgroups to the XCDs in turn; each block
-// checks this against the hardware XCC_ID register) and is member m = b / 8 of team t = b % 8. Team t computes rows
-// t and t + 8 (R = 2 rows) or row t alone. Every block keeps the residual stream of its team's rows in LDS; a stage
+// Layout of the work. The dispatcher deals workgroups to the XCDs in turn, continuing from where the previous launch
+// stopped, so block b runs on XCD (b + k) % 8 for some k of the launch. A block reads its XCD from the hardware
+// XCC_ID register: it is member m = b / 8 of team t = that XCD. Team t computes rows t and t + 8 (R = 2 rows) or
+// row t alone. Every block keeps the residual stream of its team's rows in LDS; a stage
 // splits its outputs over the 32 members and publishes them, and the next stage polls what it needs:
 //   pre     x = W_pre [hidden ; escale E[token]]      8 outputs per member, K split over the 4 waves
 //   q       q = W_q RMSNorm(x; attn_norm)             32 outputs per member
