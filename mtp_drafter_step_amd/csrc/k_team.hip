@@ -306,18 +306,27 @@ __device__ __forceinline__ void issue_ffn(const TeamArgs& a, const Team& T, int 
   load_w4(lw(a, l, W_PAN), W.pan);
 }
 
+// the centroid rows and norms of the post stage (before its poll: the head waits for the scores)
 template <int NBB>
-__device__ __forceinline__ void issue_post(const TeamArgs& a, const Team& T, WPost<NBB>& W) {
-  constexpr int Bb = NBB * 256, NPB = Bb / 32, NPW = NPB / 4, NPG = (NPW + 7) / 8;
+__device__ __forceinline__ void issue_post_cen(const TeamArgs& a, const Team& T, WPost<NBB>& W) {
+  constexpr int Bb = NBB * 256;
   const int w = wave_id(), lane = lane_id();
-  const int p0 = NPB * T.m + NPW * w, c0 = 64 * T.m + 16 * w;
-#pragma unroll
-  for (int o = 0; o < NPG * 8; ++o)
-    W.p[o] = *reinterpret_cast<const uint2*>(a.wpk + w_post(Bb) + (size_t)(p0 + min(o, NPW - 1)) * TH + 4 * lane);
+  const int c0 = 64 * T.m + 16 * w;
 #pragma unroll
   for (int o = 0; o < 16; ++o) W.c[o] = *reinterpret_cast<const uint2*>(a.wpk + w_cen(Bb) + (size_t)(c0 + o) * TH + 4 * lane);
   load_w4(a.wpk + w_onorm(Bb), W.on);
   load_w4(lw(a, a.n_layer - 1, W_PFN), W.pfn);
+}
+
+// the post_projection rows (after the poll: only the next step's pre reads their outputs)
+template <int NBB>
+__device__ __forceinline__ void issue_post_proj(const TeamArgs& a, const Team& T, WPost<NBB>& W) {
+  constexpr int Bb = NBB * 256, NPB = Bb / 32, NPW = NPB / 4, NPG = (NPW + 7) / 8;
+  const int w = wave_id(), lane = lane_id();
+  const int p0 = NPB * T.m + NPW * w;
+#pragma unroll
+  for (int o = 0; o < NPG * 8; ++o)
+    W.p[o] = *reinterpret_cast<const uint2*>(a.wpk + w_post(Bb) + (size_t)(p0 + min(o, NPW - 1)) * TH + 4 * lane);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -326,7 +335,8 @@ __device__ __forceinline__ void issue_post(const TeamArgs& a, const Team& T, WPo
 // hidden half, waves 2-3 the embedding half (Bb % 512 == 0: NBB / 2 chunks of 4 elements per lane).
 
 template <int R, int NBB>
-__device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, int step, WQ& Wq) {
+__device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, int step, WQ& Wq,
+                                          const uint32_t (&pf)[2]) {
   WPre<NBB> W;
   issue_pre<NBB>(a, T, W);
   constexpr int Bb = NBB * 256, CPL = NBB / 2;
@@ -377,6 +387,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
 #pragma unroll
         for (int c = 0; c < CPL; ++c) xr[r][c] = make_uint2(raw[(r * CPL + c) * 2], raw[(r * CPL + c) * 2 + 1]);
     }
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]));  // the previous head's row touches end here
     issue_q(a, T, 0, Wq);
   } else {
     // the row's token: the caller's at step 0, else the best of the previous step's 32 slot keys
@@ -815,7 +826,7 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
 template <int R, int NBB>
 __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, int step) {
   WPost<NBB> W;
-  issue_post<NBB>(a, T, W);
+  issue_post_cen<NBB>(a, T, W);
   constexpr int Bb = NBB * 256, NPB = Bb / 32, NPW = NPB / 4, NPG = (NPW + 7) / 8;
   const int w = wave_id(), lane = lane_id();
   const int last_l = a.n_layer - 1;
@@ -830,12 +841,27 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
 
   // this member's -1e30 stores are complete before it publishes anything the head waits for
   if (a.logits) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  issue_post_proj<NBB>(a, T, W);
   __syncthreads();
   constexpr int RL = kRedLanes<R>;
   const bool lastep = step + 1 == a.n_steps;
   float4 u[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) u[r] = *reinterpret_cast<const float4*>(&S.us[r][4 * lane]);
+  // the centroid scores first: the head waits for them, while the post_projection rows are still arriving
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float acc[R * 8];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(W.c[g * 8 + o], u[r]);
+    XR<R * 8, 32>::run(acc, lane);
+    if (lane % RL == 0) {
+      const int i = lane / RL;
+      putf(T.X + A_SC + (i >> 3) * TC + c0 + 8 * g + (i & 7), T.tag(step, S_POST), acc[0]);
+    }
+  }
 #pragma unroll
   for (int g = 0; g < NPG; ++g) {
     float acc[R * 8];
@@ -853,19 +879,6 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
       if (lastep) *reinterpret_cast<uint32_t*>(a.hidden_out + (size_t)T.row(r) * Bb + n) = pair;
     }
   }
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    float acc[R * 8];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(W.c[g * 8 + o], u[r]);
-    XR<R * 8, 32>::run(acc, lane);
-    if (lane % RL == 0) {
-      const int i = lane / RL;
-      putf(T.X + A_SC + (i >> 3) * TC + c0 + 8 * g + (i & 7), T.tag(step, S_POST), acc[0]);
-    }
-  }
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -880,7 +893,7 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
 // tau of the 4 waves' values therefore has at least 32 keys at or above it, so the 32 largest keys all have high
 // half >= tau. Those candidates (typically a few dozen) are ranked by counting the candidates above each.
 
-__device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], const int (&ci)[8]) {
+__device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], const int (&ci)[8], int step) {
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   uint32_t mx = ok[0];
 #pragma unroll
@@ -894,6 +907,7 @@ __device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], c
   if (lane == 0) S.wtot[w] = tw;
   if (tid == 0) S.ncand = 0u;
   __syncthreads();
+  TEAM_TRACE(step, 42);
   const uint32_t tau = min(min(S.wtot[0], S.wtot[1]), min(S.wtot[2], S.wtot[3]));
   // append the candidates: per-lane counts, a wave prefix sum, one LDS atomic per wave for the base
   uint32_t c = 0;
@@ -920,11 +934,12 @@ __device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], c
     for (uint32_t f = 0; f < nc; ++f) rank += (S.cand[f] > me) ? 1u : 0u;
     if (rank < (uint32_t)TKS) S.sel[rank] = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
   }
+  TEAM_TRACE(step, 43);
   __syncthreads();
 }
 
 template <int R>
-__device__ __forceinline__ void stage_head(const TeamArgs& a, Team& T, Smem& S, int step) {
+__device__ __forceinline__ void stage_head(const TeamArgs& a, Team& T, Smem& S, int step, uint32_t (&pf)[2]) {
   constexpr int NSL = R;  // slots per member: 2 (R = 2: 16 members per row) or 1 (32 members)
   constexpr int HCH = 2;          // 128-dim chunks of a 256-wide row
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
@@ -947,7 +962,7 @@ __device__ __forceinline__ void stage_head(const TeamArgs& a, Team& T, Smem& S, 
     for (int q = 0; q < 8; ++q) ok[q] = f32_order(__uint_as_float(raw[q]));
   }
   TEAM_TRACE(step, 39);
-  select_top32(S, ok, ci);
+  select_top32(S, ok, ci, step);
   TEAM_TRACE(step, 40);
   // the slots' clusters: group grp (16 lanes) scores ids grp + 16 u, u < 8
   const int grp = tid >> 4, l16 = tid & 15;
@@ -1019,6 +1034,19 @@ __device__ __forceinline__ void stage_head(const TeamArgs& a, Team& T, Smem& S, 
     put(T.X + A_KEY + r * (2 * TKS) + 2 * (slot0 + q) + half, T.tag(step, S_KEY),
         half ? (uint32_t)(k >> 32) : (uint32_t)k);
   }
+  // The next step's pre reads the target embedding row of the row's token, the best of the 32 slot tokens. Each of
+  // this member's slot tokens is a candidate, so wave q touches every 64-byte segment of slot q's row: the row is in
+  // the XCD's L2 when the pre stage gathers it. The two words are kept until the next pre stage's waves 0 and 1 have
+  // passed their own wait (which covers these loads), so holding them costs no wait.
+  if (step + 1 < a.n_steps && w < NSL) {
+    const uint64_t k = u64_max(u64_max(S.bestw[w][0], S.bestw[w][1]), u64_max(S.bestw[w][2], S.bestw[w][3]));
+    const int t0 = key_id(k);
+    const int t = t0 < 0 ? 0 : (t0 >= a.V ? a.V - 1 : t0);
+    const uint32_t* er = reinterpret_cast<const uint32_t*>(a.temb + (size_t)t * a.Bb);
+    const int nseg = a.Bb / 32;  // 64-byte segments of the row (at most 128)
+    pf[0] = er[16 * min(lane, nseg - 1)];
+    pf[1] = er[16 * min(64 + lane, nseg - 1)];
+  }
   __syncthreads();
 }
 
@@ -1048,9 +1076,10 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
   WQ wq;
   WK wo, wd;
   WF wf;
+  uint32_t pf[2] = {0u, 0u};
   for (int step = 0; step < a.n_steps; ++step) {
     TEAM_TRACE(step, S_PRE);
-    stage_pre<R, NBB>(a, T, S, step, wq);
+    stage_pre<R, NBB>(a, T, S, step, wq, pf);
     for (int l = 0; l < a.n_layer; ++l) {
       const bool last = l + 1 == a.n_layer;
       TEAM_TRACE(step, s_q(l));
@@ -1072,7 +1101,7 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
     TEAM_TRACE(step, S_POST);
     stage_post<R, NBB>(a, T, S, step);
     TEAM_TRACE(step, S_KEY);
-    stage_head<R>(a, T, S, step);
+    stage_head<R>(a, T, S, step, pf);
     TEAM_TRACE(step, 27);
   }
   stage_final<R>(a, T, a.n_steps - 1);
