@@ -233,8 +233,8 @@ MTPD_API int mtpd_set_option(mtpd_handle h, int32_t option, int32_t value);
 /* Status of the persistent drafter kernel's launches on this handle and on the allocation-free entry point's scratch
  * of the current device: 0 if every launch so far finished its waits normally, else bit 0 (a wait gave up, the
  * launch's outputs are undefined), bit 1 (a block ran on an XCD outside the 8 the kernel expects) and in bits 8-15
- * one plus the stage id of the first wait that gave up. Waits for the device (a blocking copy); clear != 0 resets
- * the status. */
+ * one plus the largest stage id among the waits that gave up. Waits for the device (a blocking copy); clear != 0
+ * resets the status. */
 MTPD_API int32_t mtpd_fault_status(mtpd_handle h, int32_t clear);
 
 /* Kernel timing, a measurement aid outside the method. While enabled on a handle, drafter_step, draft_block and

@@ -29,7 +29,6 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
   constexpr int HD = 256, KSTEPS = 8, TILES = 16, LROW = HD + 8, S = 64;
   constexpr int GQ = (G + 3) / 4;
   const int lane = lane_id(), hq = lane & 15, kq = lane >> 4;
-  const int hsel = hq < G ? hq : 0;
   const int tb = t0;
   if constexpr (PF) {
     const uint16_t* r = Kb + (size_t)slot_of(min(t0 + S + hq, k1 - 1), cap) * HD;

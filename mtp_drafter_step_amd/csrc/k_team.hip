@@ -107,7 +107,14 @@ __device__ uint64_t g_team_trace[256 * 256];
   do {                                                                                                   \
     if (threadIdx.x == 0 && (step) < 4) g_team_trace[blockIdx.x * 256 + (step) * 64 + (sid)] = wall_clock64(); \
   } while (0)
+#define TEAM_TRACE_AT(step, sid, thread)                                                                 \
+  do {                                                                                                   \
+    if (threadIdx.x == (thread) && (step) < 4) g_team_trace[blockIdx.x * 256 + (step) * 64 + (sid)] = wall_clock64(); \
+  } while (0)
 #else
+#define TEAM_TRACE_AT(step, sid, thread) \
+  do {                                   \
+  } while (0)
 #define TEAM_TRACE(step, sid) \
   do {                        \
   } while (0)
@@ -150,9 +157,11 @@ __device__ __forceinline__ void wait_words(Team& T, const int (&idx)[N], uint32_
       T.dead = true;
       if (lane_id() == 0) {
         __hip_atomic_fetch_or(T.status, kTeamTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t z = 0;
-        __hip_atomic_compare_exchange_strong(T.status + 1, &z, (uint32_t)sid + 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+        // one plus the stage id, made opaque here so that the compiler does not keep the constant in a register
+        // across the whole launch for this rarely taken path
+        uint32_t st = (uint32_t)sid + 1u;
+        asm volatile("" : "+v"(st));
+        __hip_atomic_fetch_max(T.status + 1, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       break;
     }
@@ -401,6 +410,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
       for (int r = 0; r < R; ++r) idx[r] = A_KEY + r * (2 * TKS) + lane;  // lane = 2 slot + half
       uint32_t raw[R];
       wait_words<R>(T, idx, T.tag(step - 1, S_KEY), S_KEY, raw);
+      TEAM_TRACE_AT(step, 44, 128);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t lo = (uint32_t)__shfl(raw[r], lane & ~1, 64), hi = (uint32_t)__shfl(raw[r], lane | 1, 64);
@@ -457,6 +467,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
         acc[r * 8 + o] = s;
       }
     }
+  TEAM_TRACE_AT(step, 45, 128);
   XR<R * 8, 32>::run(acc, lane);
   constexpr int RL = kRedLanes<R>;
   if (lane % RL == 0) S.red[w][lane / RL] = acc[0];
@@ -466,6 +477,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
       *reinterpret_cast<uint4*>(&S.ks[(threadIdx.x >> 5) + 8 * i][(threadIdx.x & 31) * 8]) = kres[i];
   }
   __syncthreads();
+  TEAM_TRACE(step, 46);
   if (threadIdx.x < R * 8) {
     const int i = threadIdx.x;
     const float v = S.red[0][i] + S.red[1][i] + S.red[2][i] + S.red[3][i];
@@ -891,7 +903,8 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
 // are distinct and descending key order is descending score with ties to the lower index. Each wave takes the
 // 8th largest of its lanes' maximal high halves (at least 8 of its lanes hold a key at or above it); the minimum
 // tau of the 4 waves' values therefore has at least 32 keys at or above it, so the 32 largest keys all have high
-// half >= tau. Those candidates (typically a few dozen) are ranked by counting the candidates above each.
+// half >= tau. Those candidates (typically a few dozen) are ranked by counting the candidates above each (all
+// 256 threads at once when there are at most 64).
 
 __device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], const int (&ci)[8], int step) {
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
@@ -906,6 +919,7 @@ __device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], c
   }
   if (lane == 0) S.wtot[w] = tw;
   if (tid == 0) S.ncand = 0u;
+  if (tid < 64) S.cand[tid] = 0ull;  // below every key: the padding of the 64-entry ranking
   __syncthreads();
   TEAM_TRACE(step, 42);
   const uint32_t tau = min(min(S.wtot[0], S.wtot[1]), min(S.wtot[2], S.wtot[3]));
@@ -928,11 +942,31 @@ __device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], c
     if (ok[i] >= tau) S.cand[pos++] = ((uint64_t)ok[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)ci[i]);
   __syncthreads();
   const uint32_t nc = S.ncand;
-  for (uint32_t e = tid; e < nc; e += 256) {
+  if (nc <= 64) {
+    // up to 64 candidates (zero-padded): wave w ranks candidates 16 w + (lane % 16), each lane group of 16 counting
+    // the larger ones among 16 of the 64 (reads issued 8 at a time), the 4 groups' counts summed across lanes
+    const int e = 16 * w + (lane & 15), fq = lane >> 4;
     const uint64_t me = S.cand[e];
     uint32_t rank = 0;
-    for (uint32_t f = 0; f < nc; ++f) rank += (S.cand[f] > me) ? 1u : 0u;
-    if (rank < (uint32_t)TKS) S.sel[rank] = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint64_t o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = S.cand[16 * fq + 8 * h + j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rank += (o[j] > me) ? 1u : 0u;
+    }
+    rank += __float_as_uint(xr_partner<16>(__uint_as_float(rank)));
+    rank += __float_as_uint(xr_partner<32>(__uint_as_float(rank)));
+    if (fq == 0 && (uint32_t)e < nc && rank < (uint32_t)TKS)
+      S.sel[rank] = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
+  } else {
+    for (uint32_t e = tid; e < nc; e += 256) {
+      const uint64_t me = S.cand[e];
+      uint32_t rank = 0;
+      for (uint32_t f = 0; f < nc; ++f) rank += (S.cand[f] > me) ? 1u : 0u;
+      if (rank < (uint32_t)TKS) S.sel[rank] = (int)(0xFFFFFFFFu - (uint32_t)(me & 0xFFFFFFFFull));
+    }
   }
   TEAM_TRACE(step, 43);
   __syncthreads();
