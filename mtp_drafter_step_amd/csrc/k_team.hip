@@ -338,6 +338,30 @@ __device__ __forceinline__ void issue_post_proj(const TeamArgs& a, const Team& T
     W.p[o] = *reinterpret_cast<const uint2*>(a.wpk + w_post(Bb) + (size_t)(p0 + min(o, NPW - 1)) * TH + 4 * lane);
 }
 
+// Part p of np of this member's 1/32 of the step's -1e30 base rows ([Inventory] "Centroid / ordered embeddings LM
+// head", step 5), as streaming stores of waves 2 and 3. The q and ffn stages call it while waves 0 and 1 poll, so
+// the 16 MB of each step's fill spreads over the layers instead of loading one stage; every wave passes a full wait
+// before it publishes the centroid scores the head waits for, so the fill precedes every scatter.
+template <int R>
+__device__ __forceinline__ void fill_part(const TeamArgs& a, const Team& T, int step, int p, int np) {
+  if (!a.logits || wave_id() < 2) return;
+  const size_t V = (size_t)a.V;
+  const size_t per = ((V + TM - 1) / TM + 3) & ~(size_t)3;
+  const size_t b0 = (size_t)T.m * per;
+  const size_t e0 = b0 + per < V ? b0 + per : V;
+  const size_t q = ((per + np - 1) / np + 3) & ~(size_t)3;
+  const size_t s0 = b0 + (size_t)p * q;
+  const size_t s1 = (p == np - 1) ? e0 : (s0 + q < e0 ? s0 + q : e0);
+  const f32x4 neg = f32x4{-1e30f, -1e30f, -1e30f, -1e30f};
+  const int tt = threadIdx.x - 128;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float* rowp = a.logits + ((size_t)step * a.B + T.row(r)) * V;
+    for (size_t i = s0 + 4 * (size_t)tt; i + 4 <= s1; i += 512)
+      __builtin_nontemporal_store(neg, reinterpret_cast<f32x4*>(rowp + i));
+  }
+}
+
 // ------------------------------------------------------------------------------------------------------------
 // pre_projection of [hidden ; escale E[token]] ([MTP doc] "What it is": 2x backbone input; [Guide] section 2(3);
 // [Explained] "Target Activations"). Member m: outputs 8m .. 8m + 7. Wave w covers K quarter w: waves 0-1 the
@@ -427,23 +451,6 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
         xr[r][c] = *reinterpret_cast<const uint2*>(a.temb + (size_t)t * Bb + (kb - Bb) + 256 * c + 4 * lane);
     }
     issue_q(a, T, 0, Wq);
-    // this member's 1/32 of the step's -1e30 base rows ([Inventory] "Centroid / ordered embeddings LM head", step 5),
-    // streaming stores that drain while the embedding rows arrive; every wave passes a full wait before it
-    // publishes the centroid scores the head waits for, so the fill precedes every scatter
-    if (a.logits) {
-      const size_t V = (size_t)a.V;
-      const size_t per = ((V + TM - 1) / TM + 3) & ~(size_t)3;
-      const size_t b0 = (size_t)T.m * per;
-      const size_t e0 = b0 + per < V ? b0 + per : V;
-      const f32x4 neg = f32x4{-1e30f, -1e30f, -1e30f, -1e30f};
-      const int tt = threadIdx.x - 128;  // waves 2 and 3
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float* rowp = a.logits + ((size_t)step * a.B + T.row(r)) * V;
-        for (size_t i = b0 + 4 * (size_t)tt; i + 4 <= e0; i += 512)
-          __builtin_nontemporal_store(neg, reinterpret_cast<f32x4*>(rowp + i));
-      }
-    }
   }
   const float sc = emb ? a.escale : 1.0f;
   float acc[R * 8];
@@ -538,6 +545,7 @@ __device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int
     row_update(S, w, l == 0 ? 0 : 1, d, W.pfn, a.scale[lp], W.an, a.eps);
   }
   issue_k1024(lw(a, l, W_O), T, Wo);  // the o_proj slice, used two stages on
+  fill_part<R>(a, T, step, 2 * l, 2 * a.n_layer);
   __syncthreads();
   float acc[R * 8];
 #pragma unroll
@@ -809,6 +817,7 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
     row_update(S, w, 2, d, W.pan, 1.0f, W.fn, a.eps);
   }
   issue_k1024(lw(a, l, W_D), T, Wd);  // the down slice, used next stage
+  fill_part<R>(a, T, step, 2 * l + 1, 2 * a.n_layer);
   __syncthreads();
   float ag[R * 8], au[R * 8];
 #pragma unroll
