@@ -179,7 +179,8 @@ struct Smem {
   // attention
   // [step][hi/lo][head slot][kq][8 dims]; slots 4 .. 7 stay zero (unused columns of the score tile)
   __attribute__((aligned(16))) uint16_t qop[8][2][8][4][8];
-  __attribute__((aligned(16))) float qs_wacc[4 * 256 * 4];   // q staging, then the waves' combine tiles
+  // q staging, then the waves' combine tiles: [wave][dim][hi rows of heads 0..3 | lo rows of heads 0..3]
+  __attribute__((aligned(16))) float qs_wacc[4 * 256 * 8];
   __attribute__((aligned(16))) uint16_t vt[4][16][264];
   __attribute__((aligned(16))) float wml[4][4][2];
   // this member's split of its row's sliding window, resident for the whole launch (every sliding layer of every
@@ -627,7 +628,9 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
       qs[w][lane * 4 + e] = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
     }
   }
+  if (l == 1) TEAM_TRACE(step, 47);
   __syncthreads();
+  if (l == 1) TEAM_TRACE(step, 48);
   {
     float (*qs)[HD] = reinterpret_cast<float (*)[HD]>(S.qs_wacc);
     for (int i = threadIdx.x; i < KSTEPS * 4 * 4 * 8; i += 256) {
@@ -640,6 +643,7 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
   }
   __syncthreads();
   if (type) TEAM_TRACE(step, 29);
+  if (l == 1) TEAM_TRACE(step, 49);
   float mrun = -INFINITY, lrun = 0.f;
   f32x4 acc[TILES];
 #pragma unroll
@@ -667,26 +671,31 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
                            acc, mrun, lrun);
     load_key_batch(ksp, j + 5, kC);
   }
-  attn_fold_rows(acc);
+  if (l == 1) TEAM_TRACE(step, 50);
   if (type) TEAM_TRACE(step, 30);
-  // combine the waves: head h's state in lane h; output rows (heads) 0..3 of the tile in lanes 0..15
-  float (*wacc)[HD][4] = reinterpret_cast<float (*)[HD][4]>(S.qs_wacc);
+  if (l == 1) TEAM_TRACE(step, 51);
+  // combine the waves: head h's state in lane h; output rows 0..3 (the hi products of heads 0..3) of the tile in
+  // lanes 0..15, rows 8..11 (their lo products) in lanes 32..47: both go to LDS and the combine adds them, which
+  // costs less than folding the rows across lanes in registers
+  float (*wacc)[HD][8] = reinterpret_cast<float (*)[HD][8]>(S.qs_wacc);
   if (lane < 4) {
     S.wml[w][lane][0] = mrun;
     S.wml[w][lane][1] = lrun;
   }
-  if (kq == 0) {
+  if (kq == 0 || kq == 2) {
+    const int half = kq >> 1;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) *reinterpret_cast<f32x4*>(&wacc[w][16 * t + hq][0]) = acc[t];
+    for (int t = 0; t < TILES; ++t) *reinterpret_cast<f32x4*>(&wacc[w][16 * t + hq][4 * half]) = acc[t];
   }
   __syncthreads();
+  if (l == 1) TEAM_TRACE(step, 52);
   {
     const int d = threadIdx.x;
     f32x4 av[4];
     float2 ml[4][4];
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      av[ww] = *reinterpret_cast<const f32x4*>(&wacc[ww][d][0]);
+      av[ww] = *reinterpret_cast<const f32x4*>(&wacc[ww][d][0]) + *reinterpret_cast<const f32x4*>(&wacc[ww][d][4]);
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) ml[ww][hh] = *reinterpret_cast<const float2*>(&S.wml[ww][hh][0]);
     }
