@@ -621,27 +621,29 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
     const float rr = rsqrt_hw(ss / (float)HD + a.eps);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = v[e] * rr * wq[e];
-    float (*qs)[HD] = reinterpret_cast<float (*)[HD]>(S.qs_wacc);
+    // the rotated q goes straight into the score operand: dims 4 lane .. +3 of head w are step c = lane / 8,
+    // kq = (lane % 8) / 2, elements 4 (lane % 2) .. +3, as a bf16 hi part and the bf16 rest
+    float qv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float partner = xr_partner<32>(v[e]);
-      qs[w][lane * 4 + e] = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
+      qv[e] = (lane < 32) ? (v[e] * co[e] - partner * si[e]) : (v[e] * co[e] + partner * si[e]);
     }
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hb[e] = f2bf(qv[e]);
+      lb[e] = f2bf(qv[e] - bf2f(hb[e]));
+    }
+    const int c = lane >> 3, kk = (lane & 7) >> 1, e0 = 4 * (lane & 1);
+    *reinterpret_cast<uint2*>(&S.qop[c][0][w][kk][e0]) =
+        make_uint2((uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16));
+    *reinterpret_cast<uint2*>(&S.qop[c][1][w][kk][e0]) =
+        make_uint2((uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16));
   }
   if (l == 1) TEAM_TRACE(step, 47);
   __syncthreads();
   if (l == 1) TEAM_TRACE(step, 48);
-  {
-    float (*qs)[HD] = reinterpret_cast<float (*)[HD]>(S.qs_wacc);
-    for (int i = threadIdx.x; i < KSTEPS * 4 * 4 * 8; i += 256) {
-      const int e = i & 7, kk = (i >> 3) & 3, hh = (i >> 5) & 3, c = i >> 7;
-      const float q = qs[hh][32 * c + 8 * kk + e];
-      const uint16_t hb = f2bf(q);
-      S.qop[c][0][hh][kk][e] = hb;
-      S.qop[c][1][hh][kk][e] = f2bf(q - bf2f(hb));
-    }
-  }
-  __syncthreads();
   if (type) TEAM_TRACE(step, 29);
   if (l == 1) TEAM_TRACE(step, 49);
   float mrun = -INFINITY, lrun = 0.f;
