@@ -101,16 +101,6 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
       (__attribute__((address_space(3))) i16x4*)(__attribute__((address_space(3))) void*)(p));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    v = u64_max(v, ((uint64_t)hi << 32) | lo);
-  }
-  return v;
-}
-
 // GELU, tanh form: 0.5 a (1 + tanh(u)) with u = sqrt(2/pi) (a + 0.044715 a^3), evaluated as the equal a / (1 + e^-2u)
 // on the hardware 2^x and reciprocal (a few ulp at every a; no cancellation in 1 + tanh(u) for negative a)
 __device__ __forceinline__ float gelu_tanh(float a) {
@@ -202,6 +192,44 @@ struct XR {
 __device__ __forceinline__ float wave_sum(float v) {
   XR<1, 32>::run(&v, 0);
   return v;
+}
+
+// Maximum over the wave, left in every lane: the partners of XR's steps (lanes 32 and 16 apart, then within rows of
+// 16 a rotation by 8, the half-row mirror and two quad permutations), all in the vector ALU; the halves of each
+// 64-bit value move as exact bit patterns.
+template <int O>
+__device__ __forceinline__ uint32_t xr_partner_u32(uint32_t v) {
+  return __float_as_uint(xr_partner<O>(__uint_as_float(v)));
+}
+template <int O>
+__device__ __forceinline__ void max_step_u64(uint32_t& lo, uint32_t& hi) {
+  const uint32_t plo = xr_partner_u32<O>(lo), phi = xr_partner_u32<O>(hi);
+  const bool take = phi > hi || (phi == hi && plo > lo);
+  lo = take ? plo : lo;
+  hi = take ? phi : hi;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  max_step_u64<32>(lo, hi);
+  max_step_u64<16>(lo, hi);
+  max_step_u64<8>(lo, hi);
+  max_step_u64<4>(lo, hi);
+  max_step_u64<2>(lo, hi);
+  max_step_u64<1>(lo, hi);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xr_partner<32>(v));
+  v = fmaxf(v, xr_partner<16>(v));
+  v = fmaxf(v, xr_partner<8>(v));
+  v = fmaxf(v, xr_partner<4>(v));
+  v = fmaxf(v, xr_partner<2>(v));
+  return fmaxf(v, xr_partner<1>(v));
+}
+// The value of the even (ODD = 0) or odd (ODD = 1) lane of each lane pair, by a quad permutation.
+template <int ODD>
+__device__ __forceinline__ uint32_t pair_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ODD ? 0xF5 : 0xA0, 0xf, 0xf, false);  // [1,1,3,3] / [0,0,2,2]
 }
 
 __device__ __forceinline__ void unpack4(uint2 w, float* f) {

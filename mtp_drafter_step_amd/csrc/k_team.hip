@@ -438,7 +438,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
       TEAM_TRACE_AT(step, 44, 128);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const uint32_t lo = (uint32_t)__shfl(raw[r], lane & ~1, 64), hi = (uint32_t)__shfl(raw[r], lane | 1, 64);
+        const uint32_t lo = pair_lane<0>(raw[r]), hi = pair_lane<1>(raw[r]);
         tk[r] = key_id(wave_max_u64(((uint64_t)hi << 32) | lo));
         if (w == 2 && lane == 0 && T.m == 0 && a.tokens)
           a.tokens[(size_t)T.row(r) * a.tok_stride + (step - 1)] = tk[r];
@@ -750,9 +750,7 @@ __device__ __forceinline__ void stage_mrg(const TeamArgs& a, Team& T, Smem& S, i
   wait_words<SPW + 2>(T, idx, T.tag(step, s_att(l)), s_att(l), raw);
   if (l == 1) TEAM_TRACE(step, 34);
   const float Ml = __uint_as_float(raw[SPW]), Ll = __uint_as_float(raw[SPW + 1]);
-  float M = lane < NS ? Ml : -INFINITY;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float M = wave_max(lane < NS ? Ml : -INFINITY);
   float A = 0.f, Lw = 0.f;
 #pragma unroll
   for (int q = 0; q < SPW; ++q) {
@@ -943,23 +941,26 @@ __device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], c
   __syncthreads();
   TEAM_TRACE(step, 42);
   const uint32_t tau = min(min(S.wtot[0], S.wtot[1]), min(S.wtot[2], S.wtot[3]));
-  // append the candidates: per-lane counts, a wave prefix sum, one LDS atomic per wave for the base
-  uint32_t c = 0;
+  // append the candidates (their order does not matter): for each of the lane's 8 keys a ballot, the key's place
+  // among the wave's set lanes by a count of the lower ones, and one LDS atomic per wave for the base
+  uint64_t bal[8];
+  uint32_t tot = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c += ok[i] >= tau ? 1u : 0u;
-  uint32_t incl = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = (uint32_t)__shfl_up((int)incl, o, 64);
-    if (lane >= o) incl += t;
+  for (int i = 0; i < 8; ++i) {
+    bal[i] = __ballot(ok[i] >= tau);
+    tot += (uint32_t)__popcll(bal[i]);
   }
   uint32_t base = 0;
-  if (lane == 63) base = atomicAdd(&S.ncand, incl);
-  base = (uint32_t)__shfl((int)base, 63, 64);
-  uint32_t pos = base + incl - c;
+  if (lane == 0) base = atomicAdd(&S.ncand, tot);
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes under this one
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (ok[i] >= tau) S.cand[pos++] = ((uint64_t)ok[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)ci[i]);
+  for (int i = 0; i < 8; ++i) {
+    if (ok[i] >= tau)
+      S.cand[base + (uint32_t)__popcll(bal[i] & below)] = ((uint64_t)ok[i] << 32) |
+                                                         (uint64_t)(0xFFFFFFFFu - (uint32_t)ci[i]);
+    base += (uint32_t)__popcll(bal[i]);
+  }
   __syncthreads();
   const uint32_t nc = S.ncand;
   if (nc <= 64) {
@@ -1116,7 +1117,7 @@ __device__ __forceinline__ void stage_final(const TeamArgs& a, Team& T, int step
   wait_words<R>(T, idx, T.tag(step, S_KEY), S_KEY, raw);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t lo = (uint32_t)__shfl(raw[r], lane & ~1, 64), hi = (uint32_t)__shfl(raw[r], lane | 1, 64);
+    const uint32_t lo = pair_lane<0>(raw[r]), hi = pair_lane<1>(raw[r]);
     const int tk = key_id(wave_max_u64(((uint64_t)hi << 32) | lo));
     if (lane == 0) {
       if (a.next) a.next[T.row(r)] = tk;
