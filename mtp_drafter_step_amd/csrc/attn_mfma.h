@@ -1,5 +1,6 @@
 // One 16-key batch of the matrix-core single-query attention, shared by the per-launch attention kernel
-// (k_attention.hip) and the persistent drafter kernel (k_team.hip).
+// (k_attention.hip) and the persistent drafter kernel (k_team.hip), and the persistent kernel's variant for keys
+// held in LDS that splits the output dims over the waves (mfma_tiles2_dims).
 //
 // Pages cited (by title; sections as headed on each page):
 //   [MTP doc]    "Gemma 4 Multi-Token Prediction (MTP) drafter" (llama.cpp fork, gemma4-assistant.md)
@@ -124,6 +125,93 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) ka[c] = kn[c];
   }
+}
+
+// Two 16-key tiles (32 keys from tb) of a split whose keys sit in LDS (`tile`: the first tile's row, rows of 264
+// elements; ka[i] holds tile i's rows as read from there), scored against the 4 heads whose q operand is in qop, with
+// P V taken for dims 64 dq .. 64 dq + 63 only (acc[t] covers dims 64 dq + 16 t + hq). The two tiles' score products
+// are independent chains, one softmax update covers all 32 keys, and P V runs as v_mfma_f32_16x16x32_bf16 over the
+// 32 keys. Every wave of a block runs the same scores and softmax on the same keys, so the waves' (max, sum) states
+// are identical and a wave's 64 dims need no combine with the other waves. Row layout of acc as in mfma_batch: rows
+// 0 .. 3 the hi products of heads 0 .. 3, rows 8 .. 11 their lo products.
+__device__ __forceinline__ void mfma_tiles2_dims(int tb, int k1, float scale_log2, const uint16_t* tile,
+                                                 const uint16_t (*qop)[2][8][4][8], const uint4 (&ka)[2][8], int dq,
+                                                 f32x4 (&acc)[4], float& mrun, float& lrun) {
+  constexpr int KSTEPS = 8, LROW = 264;
+  const int lane = lane_id(), hq = lane & 15, kq = lane >> 4;
+  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  {
+    uint4 qb[KSTEPS];
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) qb[c] = *reinterpret_cast<const uint4*>(&qop[c][hq >> 3][hq & 7][kq][0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[i][c]),
+                                                          __builtin_bit_cast(bf16x8, qb[c]), sacc[i], 0, 0, 0);
+  }
+  // scores of keys tb + 16 i + 4 kq + r in sv[4 i + r] (column hq: head hq once the lo column is added)
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sacc[i][r] + xr_partner<8>(sacc[i][r]);
+      sv[4 * i + r] = (tb + 16 * i + 4 * kq + r < k1 && hq < 4) ? s * scale_log2 : -INFINITY;
+    }
+  float mt = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+  mt = fmaxf(mt, xr_partner<16>(mt));
+  mt = fmaxf(mt, xr_partner<32>(mt));
+  // lazy maximum as in mfma_batch: it moves only when a score exceeds it by more than 2^8
+  const float mn = (mt > mrun + 8.0f) ? mt : mrun;
+  const float alpha = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+  float pv[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - mn);
+    ps += pv[i];
+  }
+  ps += xr_partner<16>(ps);
+  ps += xr_partner<32>(ps);
+  lrun = lrun * alpha + ps;
+  mrun = mn;
+  // P as the A operand over the 32 keys: lane (hq, kq) supplies k = 8 kq + i, standing for key 4 kq + i (i < 4) and
+  // key 16 + 4 kq + i - 4; row hq < 8 the hi parts of head hq, row 8 + h the lo parts of head h (from lane h)
+  uint32_t ph[4], pl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split_bf16x2(pv[2 * i], pv[2 * i + 1], ph[i], pl[i]);
+  uint32_t pa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo8 = __float_as_uint(xr_partner<8>(__uint_as_float(pl[i])));
+    pa[i] = (hq < 8) ? ph[i] : lo8;
+  }
+  const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
+  if (__any(hq < 4 && alpha != 1.0f)) {
+    float al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) al[r] = readlane_f(alpha, r);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] *= al[r];
+  }
+  // V operand in the same key order: two transposing reads, at key rows 4 kq and 16 + 4 kq
+  const uint16_t* vrow = tile + (4 * kq + (hq >> 2)) * LROW + 4 * (hq & 3) + 64 * dq;
+  bf16x8 vb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const i16x4 v0 = lds_read_tr16(vrow + 16 * t);
+    const i16x4 v1 = lds_read_tr16(vrow + 16 * LROW + 16 * t);
+    vb[t] = __builtin_bit_cast(bf16x8, (i16x8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, vb[t], acc[t], 0, 0, 0);
 }
 
 // After the last batch: output rows 8 .. 15 hold the lo-part products of the heads in rows 0 .. 7; rows 4kq + r of

@@ -232,6 +232,12 @@ __device__ __forceinline__ uint32_t pair_lane(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ODD ? 0xF5 : 0xA0, 0xf, 0xf, false);  // [1,1,3,3] / [0,0,2,2]
 }
 
+// a.lo * b.lo + a.hi * b.hi + c for two packed bf16 pairs, on the packed dot instruction (fp32 accumulation)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ void unpack4(uint2 w, float* f) {
   f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
 }

@@ -111,7 +111,25 @@ __device__ uint64_t g_team_trace[256 * 256];
   do {                                                                                                   \
     if (threadIdx.x == (thread) && (step) < 4) g_team_trace[blockIdx.x * 256 + (step) * 64 + (sid)] = wall_clock64(); \
   } while (0)
+// the shader cycle counter instead of the wall clock (the two give the shader clock rate)
+#define TEAM_TRACE_CYCLES(step, sid)                                                                         \
+  do {                                                                                                       \
+    if (threadIdx.x == 0 && (step) < 4) g_team_trace[blockIdx.x * 256 + (step) * 64 + (sid)] = clock64(); \
+  } while (0)
+// the same after the value v is computed (an empty asm that consumes it keeps the clock read behind it)
+#define TEAM_TRACE_DEP(step, sid, v)              \
+  do {                                            \
+    const float tdv_ = (v);                       \
+    asm volatile("" ::"v"(tdv_) : "memory");      \
+    TEAM_TRACE(step, sid);                        \
+  } while (0)
 #else
+#define TEAM_TRACE_CYCLES(step, sid) \
+  do {                               \
+  } while (0)
+#define TEAM_TRACE_DEP(step, sid, v) \
+  do {                               \
+  } while (0)
 #define TEAM_TRACE_AT(step, sid, thread) \
   do {                                   \
   } while (0)
@@ -453,6 +471,8 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
     }
     issue_q(a, T, 0, Wq);
   }
+  // both operands are bf16 (weights, the hidden state or embedding row), so pairs go through the packed bf16 dot
+  // with fp32 accumulation; the embedding scale multiplies the wave's sums
   const float sc = emb ? a.escale : 1.0f;
   float acc[R * 8];
 #pragma unroll
@@ -460,21 +480,16 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      float xf[4];
-      unpack4(xr[r][c], xf);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xf[e] *= sc;
+    for (int c = 0; c < CPL; ++c)
 #pragma unroll
       for (int o = 0; o < 8; ++o) {
-        float wf[4];
-        unpack4(W.w[o][c], wf);
         float s = acc[r * 8 + o];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s = fmaf(xf[e], wf[e], s);
+        s = dot2_bf16(xr[r][c].x, W.w[o][c].x, s);
+        s = dot2_bf16(xr[r][c].y, W.w[o][c].y, s);
         acc[r * 8 + o] = s;
       }
-    }
+#pragma unroll
+  for (int i = 0; i < R * 8; ++i) acc[i] *= sc;
   TEAM_TRACE_AT(step, 45, 128);
   XR<R * 8, 32>::run(acc, lane);
   constexpr int RL = kRedLanes<R>;
@@ -647,17 +662,53 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
   if (type) TEAM_TRACE(step, 29);
   if (l == 1) TEAM_TRACE(step, 49);
   float mrun = -INFINITY, lrun = 0.f;
+  if (resident) {
+    // every wave scores all of the split's keys and accumulates P.V for dims 64 w .. 64 w + 63, so the member's
+    // partial is complete in each wave's quarter of the dims and goes out without a combine
+    f32x4 acc4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      if (k0 + 16 * j < k1) {  // block-uniform
+        uint4 kk[2][KSTEPS];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int c = 0; c < KSTEPS; ++c)
+            kk[i][c] = *reinterpret_cast<const uint4*>(&S.ks[16 * (j + i) + hq][32 * c + 8 * kq]);
+        mfma_tiles2_dims(k0 + 16 * j, k1, a.scale_log2, &S.ks[16 * j][0], S.qop, kk, w, acc4, mrun, lrun);
+      }
+    }
+    if (l == 1) TEAM_TRACE(step, 50);
+    // rows 8 .. 11 (lo products) join rows 0 .. 3 (hi) in lanes 32 apart; lanes of kq 0 then publish tiles 0 and 1,
+    // lanes of kq 2 tiles 2 and 3
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc4[t][r] += xr_partner<32>(acc4[t][r]);
+    const uint32_t tg = T.tag(step, s_att(l));
+    uint64_t* ap = T.X + A_AP + T.m * AP_STRIDE;
+    if (kq == 0 || kq == 2) {
+      const int tp = kq >> 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int d = 64 * w + 16 * (2 * tp + i) + hq;
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) putf(ap + hh * 258 + d, tg, tp ? acc4[2 + i][hh] : acc4[i][hh]);
+      }
+    }
+    if (w == 0 && lane < 4) {  // head `lane`: its running maximum and sum (the same in every wave)
+      putf(ap + lane * 258 + 256, tg, mrun);
+      putf(ap + lane * 258 + 257, tg, lrun);
+    }
+    return;
+  }
   f32x4 acc[TILES];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* tile = &S.vt[w][0][0];
-  const int nb = resident ? 0 : (k1 - k0 + 63) / 64;  // 64-key rounds of the block (one 16-key batch per wave each)
-  if (resident && k0 + 16 * w < k1) {  // wave w: resident keys 16 w .. 16 w + 15 of the split
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) kA[c] = *reinterpret_cast<const uint4*>(&S.ks[16 * w + hq][32 * c + 8 * kq]);
-    mfma_batch<4, false, true>(k0 + 16 * w, k1, Kb, Kb, cap, true, a.scale_log2, &S.ks[16 * w][0], S.qop, kA, kA,
-                               acc, mrun, lrun);
-  }
+  const int nb = (k1 - k0 + 63) / 64;  // 64-key rounds of the block (one 16-key batch per wave each)
   for (int j = 0; j < nb; j += 3) {
     // compute batch j from A while B and C are in flight, then refill A with batch j + 3, and so on
     if (k0 + 64 * j + 16 * w < k1)
@@ -798,10 +849,14 @@ __device__ __forceinline__ void stage_k1024(Team& T, Smem& S, const WK& W, int s
 #pragma unroll
     for (int o = 0; o < 8; ++o) acc[r * 8 + o] = dot4(W.w[o], u);
   }
+  const int tstep = (int)(tag_in / NSID - T.E - 1);
+  if (sid_in == s_mrg(1)) TEAM_TRACE_DEP(tstep, 53, acc[R * 8 - 1]);
   XR<R * 8, 32>::run(acc, lane);
+  if (sid_in == s_mrg(1)) TEAM_TRACE_DEP(tstep, 54, acc[0]);
   constexpr int RL = kRedLanes<R>;
   if (lane % RL == 0) S.red[w][lane / RL] = acc[0];
   __syncthreads();
+  if (sid_in == s_mrg(1)) TEAM_TRACE(tstep, 55);
   if (threadIdx.x < R * 8) {
     const int i = threadIdx.x;
     putf(T.X + dst + (i >> 3) * TH + n0 + (i & 7), tag_out, S.red[0][i] + S.red[1][i] + S.red[2][i] + S.red[3][i]);
@@ -824,10 +879,12 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
     poll_row(T, A_T + w * TH, T.tag(step, s_op(l)), s_op(l), d);
     if (l == 1) TEAM_TRACE(step, 36);
     row_update(S, w, 2, d, W.pan, 1.0f, W.fn, a.eps);
+    if (l == 1) TEAM_TRACE_DEP(step, 56, S.us[w][lane]);
   }
   issue_k1024(lw(a, l, W_D), T, Wd);  // the down slice, used next stage
   fill_part<R>(a, T, step, 2 * l + 1, 2 * a.n_layer);
   __syncthreads();
+  if (l == 1) TEAM_TRACE(step, 57);
   float ag[R * 8], au[R * 8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -838,13 +895,16 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
       au[r * 8 + o] = dot4(W.u[o], u);
     }
   }
+  if (l == 1) TEAM_TRACE_DEP(step, 58, ag[R * 8 - 1] + au[R * 8 - 1]);
   XR<R * 8, 32>::run(ag, lane);
   XR<R * 8, 32>::run(au, lane);
+  if (l == 1) TEAM_TRACE_DEP(step, 59, ag[0] + au[0]);
   constexpr int RL = kRedLanes<R>;
   if (lane % RL == 0) {
     const int i = lane / RL;
     putf(T.X + A_M + (i >> 3) * TF + f0 + (i & 7), T.tag(step, s_ffn(l)), gelu_tanh(ag[0]) * au[0]);
   }
+  if (l == 1) TEAM_TRACE(step, 60);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1134,6 +1194,7 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
   uint32_t pf[2] = {0u, 0u};
   for (int step = 0; step < a.n_steps; ++step) {
     TEAM_TRACE(step, S_PRE);
+    TEAM_TRACE_CYCLES(step, 61);
     stage_pre<R, NBB>(a, T, S, step, wq, pf);
     for (int l = 0; l < a.n_layer; ++l) {
       const bool last = l + 1 == a.n_layer;
@@ -1158,6 +1219,7 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
     TEAM_TRACE(step, S_KEY);
     stage_head<R>(a, T, S, step, pf);
     TEAM_TRACE(step, 27);
+    TEAM_TRACE_CYCLES(step, 62);
   }
   stage_final<R>(a, T, a.n_steps - 1);
 }
