@@ -978,20 +978,21 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
 // sparse logits E[id] . h from the cluster-ordered table, the scatter into the row, the slot's best (value, id).
 //
 // Selection, exact: every key is the composite (order-preserving score bits, complement of the index), so the keys
-// are distinct and descending key order is descending score with ties to the lower index. Each wave takes the
-// 8th largest of its lanes' maximal high halves (at least 8 of its lanes hold a key at or above it); the minimum
-// tau of the 4 waves' values therefore has at least 32 keys at or above it, so the 32 largest keys all have high
-// half >= tau. Those candidates (typically a few dozen) are ranked by counting the candidates above each (all
-// 256 threads at once when there are at most 64).
+// are distinct and descending key order is descending score with ties to the lower index. Each wave takes a lower
+// bound of the 8th largest of its lanes' maximal high halves (at least 8 of its lanes hold a key at or above it);
+// the minimum tau of the 4 waves' values therefore has at least 32 keys at or above it, so the 32 largest keys all
+// have high half >= tau. Those candidates (typically a few dozen) are ranked by counting the candidates above each
+// (all 256 threads at once when there are at most 64).
 
 __device__ __forceinline__ void select_top32(Smem& S, const uint32_t (&ok)[8], const int (&ci)[8], int step) {
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   uint32_t mx = ok[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = max(mx, ok[i]);
-  // the wave's 8th largest lane maximum, bit by bit: the largest value that at least 8 lane maxima reach
+  // the wave's 8th largest lane maximum with its low 12 bits cleared, bit by bit from the top: the largest multiple
+  // of 2^12 that at least 8 lane maxima reach (the cleared bits only admit a few more candidates)
   uint32_t tw = 0;
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= 12; --b) {
     const uint32_t cand = tw | (1u << b);
     if (__popcll(__ballot(mx >= cand)) >= 8) tw = cand;
   }
