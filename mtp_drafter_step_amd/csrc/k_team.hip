@@ -34,6 +34,10 @@
 // expected tag. Tags never repeat, so stale words from earlier stages, steps or launches are simply not accepted,
 // and no buffer is ever cleared. A word's slot is rewritten only after every consumer of its previous value has
 // published something the writer waited for, so no value is overwritten before it is read.
+// The two widest hand-offs (the merged attention output, 2048 values of which every member reads 2048, and the
+// centroid scores) go out as untagged fp32 values instead: the producing wave waits until its stores have reached L2
+// (vmcnt(0)) and then stores one tagged flag word; a consumer spins on the few flags of the producers it needs and
+// then reads the values once. Re-reading 2048 tagged words on every spin costs more than the extra round trip.
 #include "attn_mfma.h"
 
 namespace mtpd {
@@ -65,14 +69,16 @@ constexpr int AP_STRIDE = 4 * 258;  // per member: 4 heads x (256 partial sums, 
 constexpr int A_XB = 0;
 constexpr int A_Q = A_XB + 2 * TH;
 constexpr int A_AP = A_Q + 2 * TQ;
-constexpr int A_O = A_AP + TM * AP_STRIDE;
+constexpr int A_O = A_AP + TM * AP_STRIDE;  // untagged fp32 pairs, announced by the A_OFL flags
 constexpr int A_T = A_O + 2 * TQ;
 constexpr int A_M = A_T + 2 * TH;
 constexpr int A_D = A_M + 2 * TF;
 constexpr int A_HID = A_D + 2 * TH;        // 2 rows x up to 2048 words (bf16 pairs of a 4096-wide hidden)
-constexpr int A_SC = A_HID + 2 * 2048;
+constexpr int A_SC = A_HID + 2 * 2048;    // untagged fp32 centroid scores, announced by the A_SFL flags
 constexpr int A_KEY = A_SC + 2 * TC;       // 2 rows x 32 slots x (low, high) halves of the (value, id) key
-constexpr int A_END = A_KEY + 2 * TKS * 2;
+constexpr int A_OFL = A_KEY + 2 * TKS * 2;  // flags of the merged attention output (one per member)
+constexpr int A_SFL = A_OFL + TM;           // flags of the centroid scores (one per wave of every member)
+constexpr int A_END = A_SFL + 4 * TM;
 constexpr int TEAM_WORDS = (A_END + 511) & ~511;
 
 // packed dense weights (bf16 elements): kTeamMaxLayers layers of [q | q_norm | o | attn_norm | post_attn_norm |
@@ -814,10 +820,16 @@ __device__ __forceinline__ void stage_mrg(const TeamArgs& a, Team& T, Smem& S, i
   S.red[w][lane] = A;
   if (lane == 0) S.mrgl[w] = Lw;
   __syncthreads();
-  if (w == 0 && lane < DPB) {
-    const float As = S.red[0][lane] + S.red[1][lane] + S.red[2][lane] + S.red[3][lane];
-    const float Ls = S.mrgl[0] + S.mrgl[1] + S.mrgl[2] + S.mrgl[3];
-    putf(T.X + A_O + r * TQ + d0 + lane, T.tag(step, s_mrg(l)), Ls > 0.f ? As / Ls : 0.f);
+  if (w == 0) {
+    // the 2048-value output goes out untagged; once wave 0's stores have reached L2, one tagged flag announces them
+    // (the consumers then spin on 8 flags instead of re-reading 2048 tagged words)
+    if (lane < DPB) {
+      const float As = S.red[0][lane] + S.red[1][lane] + S.red[2][lane] + S.red[3][lane];
+      const float Ls = S.mrgl[0] + S.mrgl[1] + S.mrgl[2] + S.mrgl[3];
+      reinterpret_cast<float*>(T.X + A_O)[r * TQ + d0 + lane] = Ls > 0.f ? As / Ls : 0.f;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) put(T.X + A_OFL + T.m, T.tag(step, s_mrg(l)), 1u);
   }
   __syncthreads();
 }
@@ -826,18 +838,42 @@ __device__ __forceinline__ void stage_mrg(const TeamArgs& a, Team& T, Smem& S, i
 // 1024 -> 256 products (o_proj over the merged attention output, [MTP doc] "Tensor schema": attn_output; the
 // down projection, ffn_down): member m computes outputs 8m .. 8m + 7, wave w the partial over K quarter w.
 
-template <int R, typename After>
-__device__ __forceinline__ void stage_k1024(Team& T, Smem& S, const WK& W, int src, uint32_t tag_in, int sid_in,
-                                            int dst, uint32_t tag_out, After after_poll) {
+// The flag a lane of wave w polls before reading quarter w of the merged attention output (dims 256 w .. 256 w + 255
+// of each row): member m wrote dims 64 (m mod 16) .. +63 of row m / 16 (R = 2) or dims 32 m .. +31 (R = 1), so the
+// quarter's 8 producers are picked by lane mod 8.
+template <int R>
+__device__ __forceinline__ int mrg_flag() {
+  const int w = wave_id(), j = lane_id() & 7;
+  if constexpr (R == 2) return (j < 4) ? 4 * w + j : 16 + 4 * w + (j - 4);
+  return 8 * w + j;
+}
+
+template <int R, bool FLAGGED, typename After>
+__device__ __forceinline__ void stage_k1024(Team& T, Smem& S, const WK& W, int src, int flag, uint32_t tag_in,
+                                            int sid_in, int dst, uint32_t tag_out, After after_poll) {
   const int w = wave_id(), lane = lane_id();
   const int n0 = 8 * T.m, k = 256 * w + 4 * lane;
-  int idx[R * 4];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) idx[r * 4 + e] = src + r * 1024 + k + e;
   uint32_t raw[R * 4];
-  wait_words<R * 4>(T, idx, tag_in, sid_in, raw);
+  if constexpr (!FLAGGED) {  // tagged input words, polled until every one carries tag_in
+    int idx[R * 4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) idx[r * 4 + e] = src + r * 1024 + k + e;
+    wait_words<R * 4>(T, idx, tag_in, sid_in, raw);
+  } else {  // untagged fp32 pairs: the flags of this wave's quarter's producers, then the quarter, read once from L2
+    int fi[1] = {flag};
+    uint32_t fr[1];
+    wait_words<1>(T, fi, tag_in, sid_in, fr);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint64_t p0 = peek(T.X + src + (r * 1024 + k) / 2), p1 = peek(T.X + src + (r * 1024 + k) / 2 + 1);
+      raw[r * 4 + 0] = (uint32_t)p0;
+      raw[r * 4 + 1] = (uint32_t)(p0 >> 32);
+      raw[r * 4 + 2] = (uint32_t)p1;
+      raw[r * 4 + 3] = (uint32_t)(p1 >> 32);
+    }
+  }
   if (sid_in == s_mrg(1)) TEAM_TRACE((int)(tag_in / NSID - T.E - 1), 35);
   if (sid_in == s_ffn(1)) TEAM_TRACE((int)(tag_in / NSID - T.E - 1), 37);
   after_poll();
@@ -949,9 +985,13 @@ __device__ __forceinline__ void stage_post(const TeamArgs& a, Team& T, Smem& S, 
     XR<R * 8, 32>::run(acc, lane);
     if (lane % RL == 0) {
       const int i = lane / RL;
-      putf(T.X + A_SC + (i >> 3) * TC + c0 + 8 * g + (i & 7), T.tag(step, S_POST), acc[0]);
+      reinterpret_cast<float*>(T.X + A_SC)[(i >> 3) * TC + c0 + 8 * g + (i & 7)] = acc[0];
     }
   }
+  // the scores go out untagged; once this wave's stores have reached L2, its flag announces them (the head then
+  // spins on 32 flags instead of re-reading 2048 tagged words)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane == 0) put(T.X + A_SFL + 4 * T.m + w, T.tag(step, S_POST), 1u);
 #pragma unroll
   for (int g = 0; g < NPG; ++g) {
     float acc[R * 8];
@@ -1070,10 +1110,19 @@ __device__ __forceinline__ void stage_head(const TeamArgs& a, Team& T, Smem& S, 
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       ci[q] = 512 * w + 64 * q + lane;
-      idx[q] = A_SC + r * TC + ci[q];
+      idx[q] = r * TC + ci[q];  // fp32 index into the score region
     }
     uint32_t raw[8];
-    wait_words<8>(T, idx, T.tag(step, S_POST), S_POST, raw);
+    {
+      // this wave's centroids 512 w .. 512 w + 511 come from members 8 w .. 8 w + 7 (all four waves of each): their
+      // flags, then the untagged scores, read once from L2
+      int fi[1] = {A_SFL + 4 * (8 * w + ((lane >> 2) & 7)) + (lane & 3)};
+      uint32_t fr[1];
+      wait_words<1>(T, fi, T.tag(step, S_POST), S_POST, fr);
+      uint32_t* sc = reinterpret_cast<uint32_t*>(T.X + A_SC);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) raw[q] = __hip_atomic_load(sc + idx[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) ok[q] = f32_order(__uint_as_float(raw[q]));
   }
@@ -1206,12 +1255,12 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
       TEAM_TRACE(step, s_mrg(l));
       stage_mrg<R>(a, T, S, step, l);
       TEAM_TRACE(step, s_op(l));
-      stage_k1024<R>(T, S, wo, A_O, T.tag(step, s_mrg(l)), s_mrg(l), A_T, T.tag(step, s_op(l)),
+      stage_k1024<R, true>(T, S, wo, A_O, A_OFL + mrg_flag<R>(), T.tag(step, s_mrg(l)), s_mrg(l), A_T, T.tag(step, s_op(l)),
                      [&] { issue_ffn(a, T, l, wf); });
       TEAM_TRACE(step, s_ffn(l));
       stage_ffn<R>(a, T, S, step, l, wf, wd);
       TEAM_TRACE(step, s_dn(l));
-      stage_k1024<R>(T, S, wd, A_M, T.tag(step, s_ffn(l)), s_ffn(l), A_D, T.tag(step, s_dn(l)), [&] {
+      stage_k1024<R, false>(T, S, wd, A_M, 0, T.tag(step, s_ffn(l)), s_ffn(l), A_D, T.tag(step, s_dn(l)), [&] {
         if (!last) issue_q(a, T, l + 1, wq);
       });
     }
