@@ -364,9 +364,10 @@ __device__ __forceinline__ void issue_post_proj(const TeamArgs& a, const Team& T
 }
 
 // Part p of np of this member's 1/32 of the step's -1e30 base rows ([Inventory] "Centroid / ordered embeddings LM
-// head", step 5), as streaming stores of waves 2 and 3. The q and ffn stages call it while waves 0 and 1 poll, so
-// the 16 MB of each step's fill spreads over the layers instead of loading one stage; every wave passes a full wait
-// before it publishes the centroid scores the head waits for, so the fill precedes every scatter.
+// head", step 5), as streaming stores of waves 2 and 3. The q and ffn stages issue it right after their own
+// publishes (stores issued before a publish hold the published words back), so the 16 MB of each step's fill spreads
+// over the layers and drains while the next stage waits; every wave passes a full wait before it publishes the
+// centroid scores the head waits for, so the fill precedes every scatter.
 template <int R>
 __device__ __forceinline__ void fill_part(const TeamArgs& a, const Team& T, int step, int p, int np) {
   if (!a.logits || wave_id() < 2) return;
@@ -567,7 +568,6 @@ __device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int
     row_update(S, w, l == 0 ? 0 : 1, d, W.pfn, a.scale[lp], W.an, a.eps);
   }
   issue_k1024(lw(a, l, W_O), T, Wo);  // the o_proj slice, used two stages on
-  fill_part<R>(a, T, step, 2 * l, 2 * a.n_layer);
   __syncthreads();
   float acc[R * 8];
 #pragma unroll
@@ -582,6 +582,7 @@ __device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int
     const int i = lane / RL;
     putf(T.X + A_Q + (i >> 3) * TQ + n0 + (i & 7), T.tag(step, s_q(l)), acc[0]);
   }
+  fill_part<R>(a, T, step, 2 * l, 2 * a.n_layer);  // behind the publish, so it does not delay the q words
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -918,7 +919,6 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
     if (l == 1) TEAM_TRACE_DEP(step, 56, S.us[w][lane]);
   }
   issue_k1024(lw(a, l, W_D), T, Wd);  // the down slice, used next stage
-  fill_part<R>(a, T, step, 2 * l + 1, 2 * a.n_layer);
   __syncthreads();
   if (l == 1) TEAM_TRACE(step, 57);
   float ag[R * 8], au[R * 8];
@@ -940,6 +940,7 @@ __device__ __forceinline__ void stage_ffn(const TeamArgs& a, Team& T, Smem& S, i
     const int i = lane / RL;
     putf(T.X + A_M + (i >> 3) * TF + f0 + (i & 7), T.tag(step, s_ffn(l)), gelu_tanh(ag[0]) * au[0]);
   }
+  fill_part<R>(a, T, step, 2 * l + 1, 2 * a.n_layer);  // behind the publish, as in the q stage
   if (l == 1) TEAM_TRACE(step, 60);
 }
 
