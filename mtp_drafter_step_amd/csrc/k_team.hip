@@ -554,7 +554,7 @@ __device__ __forceinline__ void load_key_batch(const KeySplit& k, int j, uint4 (
 }
 
 template <int R>
-__device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int step, int l, const WQ& W, WK& Wo) {
+__device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int step, int l, const WQ& W) {
   const int w = wave_id(), lane = lane_id();
   const int n0 = 32 * T.m + 8 * w;
   const int lp = l > 0 ? l - 1 : 0;
@@ -567,7 +567,6 @@ __device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int
     if (l == 1) TEAM_TRACE(step, 32);
     row_update(S, w, l == 0 ? 0 : 1, d, W.pfn, a.scale[lp], W.an, a.eps);
   }
-  issue_k1024(lw(a, l, W_O), T, Wo);  // the o_proj slice, used two stages on
   __syncthreads();
   float acc[R * 8];
 #pragma unroll
@@ -592,7 +591,7 @@ __device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int
 // section 2(2)). Member m takes split s of its row's key window; wave w normalises and rotates head w.
 
 template <int R>
-__device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, int step, int l) {
+__device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, int step, int l, WK& Wo) {
   constexpr int HD = 256, KSTEPS = 8, TILES = 16, NS = TM / R, half = HD / 2;
   const int w = wave_id(), lane = lane_id();
   const int hq = lane & 15, kq = lane >> 4;
@@ -630,6 +629,8 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(raw[e]);
   }
+  // the o_proj slice, used two stages on: requested only now, so that the q poll above does not wait for it
+  issue_k1024(lw(a, l, W_O), T, Wo);
   if (type) TEAM_TRACE(step, 28);
   if (l == 1) TEAM_TRACE(step, 33);
   {
@@ -1250,9 +1251,9 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
     for (int l = 0; l < a.n_layer; ++l) {
       const bool last = l + 1 == a.n_layer;
       TEAM_TRACE(step, s_q(l));
-      stage_q<R>(a, T, S, step, l, wq, wo);
+      stage_q<R>(a, T, S, step, l, wq);
       TEAM_TRACE(step, s_att(l));
-      stage_att<R>(a, T, S, step, l);
+      stage_att<R>(a, T, S, step, l, wo);
       TEAM_TRACE(step, s_mrg(l));
       stage_mrg<R>(a, T, S, step, l);
       TEAM_TRACE(step, s_op(l));
