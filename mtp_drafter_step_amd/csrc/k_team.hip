@@ -397,7 +397,9 @@ template <int R, int NBB>
 __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, int step, WQ& Wq,
                                           const uint32_t (&pf)[2]) {
   WPre<NBB> W;
-  issue_pre<NBB>(a, T, W);
+  // the hidden half's slices now; the embedding half's after the key wait below, so that the wait does not also
+  // cover these loads (loads complete in order)
+  if (wave_id() < 2) issue_pre<NBB>(a, T, W);
   constexpr int Bb = NBB * 256, CPL = NBB / 2;
   const int w = wave_id(), lane = lane_id();
   const int n0 = 8 * T.m;
@@ -469,6 +471,7 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
           a.tokens[(size_t)T.row(r) * a.tok_stride + (step - 1)] = tk[r];
       }
     }
+    issue_pre<NBB>(a, T, W);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int t = tk[r] < 0 ? 0 : (tk[r] >= a.V ? a.V - 1 : tk[r]);  // out-of-range ids are clamped
