@@ -217,8 +217,8 @@ MTPD_API int mtpd_sample_head(mtpd_handle h, void *stream, void *workspace, int3
 /* Handle options (set after mtpd_create; each change discards the handle's captured graphs). Values:
  *   MTPD_OPT_GRAPHS      1 (default): replay each call from a captured HIP graph; 0: launch every kernel directly.
  *   MTPD_OPT_PERSISTENT  1 (default): calls of at most 16 rows on per-row K = V caches of the E2B / E4B shapes
- *                        (hidden 256, 4 heads of 256 over one kv head, FFN 1024, 2048 clusters of 128, top 32, <= 4
- *                        layers) on a 256-CU gfx950 run as one launch of the persistent drafter kernel, whose blocks
+ *                        (hidden 256, 4 heads of 256 over one or two kv heads, FFN 1024, 2048 clusters of 128, top
+ *                        32, <= 4 layers) on a 256-CU gfx950 run as one launch of the persistent drafter kernel, whose blocks
  *                        hand values to each other inside each XCD; it needs every CU free for the launch (a wait
  *                        that cannot finish gives up after a bounded time and is reported by mtpd_fault_status).
  *                        0: the per-stage kernels.

@@ -26,7 +26,7 @@ template <int G, bool PF, bool STAGED = false>
 __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, const uint16_t* Vb, int cap,
                                            bool same_v, float scale_log2, uint16_t* tile,
                                            const uint16_t (*qop)[2][8][4][8], uint4 (&ka)[8], uint4 (&kn)[8],
-                                           f32x4 (&acc)[16], float& mrun, float& lrun) {
+                                           f32x4 (&acc)[16], float& mrun, float& lrun, int h0 = 0, int h1 = G) {
   constexpr int HD = 256, KSTEPS = 8, TILES = 16, LROW = HD + 8, S = 64;
   constexpr int GQ = (G + 3) / 4;
   const int lane = lane_id(), hq = lane & 15, kq = lane >> 4;
@@ -68,7 +68,8 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
   for (int r = 0; r < 4; ++r) sacc[r] += xr_partner<8>(sacc[r]);
   float sv[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sv[r] = (4 * kq + r < nk && hq < G) ? sacc[r] * scale_log2 : -INFINITY;
+  // columns h0 .. h1 - 1 only: the query heads that read this batch's kv head (the others see no key here)
+  for (int r = 0; r < 4; ++r) sv[r] = (4 * kq + r < nk && hq >= h0 && hq < h1) ? sacc[r] * scale_log2 : -INFINITY;
   float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mt = fmaxf(mt, xr_partner<16>(mt));
   mt = fmaxf(mt, xr_partner<32>(mt));
@@ -133,10 +134,11 @@ __device__ __forceinline__ void mfma_batch(int t0, int k1, const uint16_t* Kb, c
 // are independent chains, one softmax update covers all 32 keys, and P V runs as v_mfma_f32_16x16x32_bf16 over the
 // 32 keys. Every wave of a block runs the same scores and softmax on the same keys, so the waves' (max, sum) states
 // are identical and a wave's 64 dims need no combine with the other waves. Row layout of acc as in mfma_batch: rows
-// 0 .. 3 the hi products of heads 0 .. 3, rows 8 .. 11 their lo products.
+// 0 .. 3 the hi products of heads 0 .. 3, rows 8 .. 11 their lo products. Only heads h0 .. h1 - 1 read these keys
+// (the query heads of the tile's kv head); the others get no weight from them.
 __device__ __forceinline__ void mfma_tiles2_dims(int tb, int k1, float scale_log2, const uint16_t* tile,
                                                  const uint16_t (*qop)[2][8][4][8], const uint4 (&ka)[2][8], int dq,
-                                                 f32x4 (&acc)[4], float& mrun, float& lrun) {
+                                                 f32x4 (&acc)[4], float& mrun, float& lrun, int h0 = 0, int h1 = 4) {
   constexpr int KSTEPS = 8, LROW = 264;
   const int lane = lane_id(), hq = lane & 15, kq = lane >> 4;
   f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -159,7 +161,7 @@ __device__ __forceinline__ void mfma_tiles2_dims(int tb, int k1, float scale_log
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = sacc[i][r] + xr_partner<8>(sacc[i][r]);
-      sv[4 * i + r] = (tb + 16 * i + 4 * kq + r < k1 && hq < 4) ? s * scale_log2 : -INFINITY;
+      sv[4 * i + r] = (tb + 16 * i + 4 * kq + r < k1 && hq >= h0 && hq < h1) ? s * scale_log2 : -INFINITY;
     }
   float mt = sv[0];
 #pragma unroll

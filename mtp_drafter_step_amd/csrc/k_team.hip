@@ -393,7 +393,7 @@ __device__ __forceinline__ void fill_part(const TeamArgs& a, const Team& T, int 
 // [Explained] "Target Activations"). Member m: outputs 8m .. 8m + 7. Wave w covers K quarter w: waves 0-1 the
 // hidden half, waves 2-3 the embedding half (Bb % 512 == 0: NBB / 2 chunks of 4 elements per lane).
 
-template <int R, int NBB>
+template <int R, int NBB, int NKV>
 __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, int step, WQ& Wq,
                                           const uint32_t (&pf)[2]) {
   WPre<NBB> W;
@@ -405,7 +405,8 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
   const int n0 = 8 * T.m;
   const int kb = w * (Bb / 2);  // first element of this wave's quarter of K = 2 Bb
   // step 0 also brings in this member's split of the sliding window (the split of stage_att), which stays in S.ks
-  // for the whole launch: every sliding layer of every step reads the same keys. 8 rows of 512 bytes per pass.
+  // for the whole launch: every sliding layer of every step reads the same keys. 8 rows of 512 bytes per pass; with
+  // two kv heads, rows 0 .. 31 hold kv head 0's keys of the split and rows 32 .. 63 kv head 1's.
   uint4 kres[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) kres[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -415,11 +416,16 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
     const int cnt = a.win_count[0][row], start = a.win_start[0][row], cap = a.cap[0];
     const int chunk = (cnt + NS - 1) / NS;
     const int k0 = start + sp * chunk, k1 = min(start + cnt, k0 + chunk);
-    const uint16_t* Kb = a.kc[0] + (size_t)row * cap * 256;
+    constexpr bool two = NKV == 2;
+    const uint16_t* Kb = a.kc[0] + (size_t)row * NKV * cap * 256;
+    const uint16_t* Kb1 = two ? Kb + (size_t)cap * 256 : Kb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int t = max(min(k0 + (threadIdx.x >> 5) + 8 * i, k1 - 1), start);
-      kres[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)slot_of(t, cap) * 256 + (threadIdx.x & 31) * 8);
+      // passes 4 .. 7 (rows 32 .. 63) take kv head 1's keys from the split's start when there are two
+      const bool g1 = i >= 4 && two;
+      const int t = max(min(k0 + (threadIdx.x >> 5) + 8 * (g1 ? i - 4 : i), k1 - 1), start);
+      kres[i] = *reinterpret_cast<const uint4*>((g1 ? Kb1 : Kb) + (size_t)slot_of(t, cap) * 256 +
+                                                (threadIdx.x & 31) * 8);
     }
   }
   uint2 xr[R][CPL];
@@ -526,11 +532,12 @@ __device__ __forceinline__ void stage_pre(const TeamArgs& a, Team& T, Smem& S, i
 
 // This member's split of a row's key window in the attention stage of layer l (stage_att's layout).
 struct KeySplit {
-  const uint16_t* Kb;  // the row's cache + 8 kq
+  const uint16_t* Kb;  // the row's cache of kv head 0, + 8 kq
   int k0, k1, start, cap;
+  int nbg;  // 64-key rounds per kv head (two kv heads: batches nbg .. 2 nbg - 1 read kv head 1)
 };
 
-template <int R>
+template <int R, int NKV>
 __device__ __forceinline__ KeySplit key_split(const TeamArgs& a, const Team& T, int type) {
   constexpr int NS = TM / R;
   const int kq = lane_id() >> 4;
@@ -543,15 +550,18 @@ __device__ __forceinline__ KeySplit key_split(const TeamArgs& a, const Team& T, 
   const int chunk = (cnt + NS - 1) / NS;
   k.k0 = k.start + s * chunk;
   k.k1 = min(k.start + cnt, k.k0 + chunk);
-  k.Kb = a.kc[type] + (size_t)row * k.cap * 256 + 8 * kq;
+  k.Kb = a.kc[type] + (size_t)row * NKV * k.cap * 256 + 8 * kq;
+  k.nbg = (k.k1 - k.k0 + 63) / 64;
   return k;
 }
 
-// Batch j of this wave in a streamed split: keys k0 + 64 j + 16 w .. +16 (rows past the split clamped to its last
-// key: cache hits, masked in the scores).
+// Batch j of this wave in a streamed split: keys k0 + 64 j' + 16 w .. +16 of kv head g, where j = g nbg + j' (rows
+// past the split clamped to its last key: cache hits, masked in the scores).
+template <int NKV>
 __device__ __forceinline__ void load_key_batch(const KeySplit& k, int j, uint4 (&dst)[8]) {
-  const int tt = k.k0 + 64 * j + 16 * wave_id() + (lane_id() & 15);
-  const uint16_t* rp = k.Kb + (size_t)slot_of(max(min(tt, k.k1 - 1), k.start), k.cap) * 256;
+  const int g = (NKV == 2 && j >= k.nbg) ? 1 : 0;
+  const int tt = k.k0 + 64 * (j - g * k.nbg) + 16 * wave_id() + (lane_id() & 15);
+  const uint16_t* rp = k.Kb + ((size_t)g * k.cap + slot_of(max(min(tt, k.k1 - 1), k.start), k.cap)) * 256;
 #pragma unroll
   for (int c = 0; c < 8; ++c) dst[c] = *reinterpret_cast<const uint4*>(rp + 32 * c);
 }
@@ -593,7 +603,7 @@ __device__ __forceinline__ void stage_q(const TeamArgs& a, Team& T, Smem& S, int
 // [Inventory] "Notes for llama.cpp port" 2: V = K). q_norm + rotation at the row's constant position ([Guide]
 // section 2(2)). Member m takes split s of its row's key window; wave w normalises and rotates head w.
 
-template <int R>
+template <int R, int NKV>
 __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, int step, int l, WK& Wo) {
   constexpr int HD = 256, KSTEPS = 8, TILES = 16, NS = TM / R, half = HD / 2;
   const int w = wave_id(), lane = lane_id();
@@ -605,8 +615,10 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
   const int chunk = (cnt + NS - 1) / NS;
   const int k0 = start + s * chunk;
   const int k1 = min(start + cnt, k0 + chunk);
-  const uint16_t* Kb = a.kc[type] + (size_t)row * cap * HD + 8 * kq;
-  const bool resident = type == 0 && chunk <= 64;  // the split sits in S.ks (loaded at the start of the launch)
+  const uint16_t* Kb = a.kc[type] + (size_t)row * NKV * cap * HD + 8 * kq;
+  constexpr bool two = NKV == 2;
+  // the split sits in S.ks (loaded at the start of the launch)
+  const bool resident = type == 0 && chunk <= (two ? 32 : 64);
   // inputs of q_norm + rotation, then the first key batch: none of them waits on the q projection
   const float* tab = a.rope + ((size_t)row * 2 + type) * 2 * half;
   const uint2 qw = *reinterpret_cast<const uint2*>(lw(a, l, W_QN) + lane * 4);
@@ -614,12 +626,12 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
   const float4 co4 = *reinterpret_cast<const float4*>(tab + i0);
   const float4 si4 = *reinterpret_cast<const float4*>(tab + half + i0);
   // streamed splits keep three 16-key batches of this wave in flight
-  const KeySplit ksp = key_split<R>(a, T, type);
+  const KeySplit ksp = key_split<R, NKV>(a, T, type);
   uint4 kA[KSTEPS], kB[KSTEPS], kC[KSTEPS];
   if (!resident) {
-    load_key_batch(ksp, 0, kA);
-    load_key_batch(ksp, 1, kB);
-    load_key_batch(ksp, 2, kC);
+    load_key_batch<NKV>(ksp, 0, kA);
+    load_key_batch<NKV>(ksp, 1, kB);
+    load_key_batch<NKV>(ksp, 2, kC);
   }
   // q of head w (dims 4 lane .. +3), whose rotation partners (d <-> d + 128) sit in lane ^ 32
   float v[4];
@@ -679,16 +691,20 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
     f32x4 acc4[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // rows 16 j .. 16 j + 31 of S.ks: keys k0 + 16 j .. of the one kv head, or (two kv heads) keys k0 .. k0 + 31
+    // of kv head j / 2, which only its query heads j .. j + 1 read
 #pragma unroll
     for (int j = 0; j < 4; j += 2) {
-      if (k0 + 16 * j < k1) {  // block-uniform
+      const int tb = two ? k0 : k0 + 16 * j;
+      if (tb < k1) {  // block-uniform
         uint4 kk[2][KSTEPS];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int c = 0; c < KSTEPS; ++c)
             kk[i][c] = *reinterpret_cast<const uint4*>(&S.ks[16 * (j + i) + hq][32 * c + 8 * kq]);
-        mfma_tiles2_dims(k0 + 16 * j, k1, a.scale_log2, &S.ks[16 * j][0], S.qop, kk, w, acc4, mrun, lrun);
+        mfma_tiles2_dims(tb, k1, a.scale_log2, &S.ks[16 * j][0], S.qop, kk, w, acc4, mrun, lrun, two ? j : 0,
+                         two ? j + 2 : 4);
       }
     }
     if (l == 1) TEAM_TRACE(step, 50);
@@ -719,21 +735,26 @@ __device__ __forceinline__ void stage_att(const TeamArgs& a, Team& T, Smem& S, i
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* tile = &S.vt[w][0][0];
-  const int nb = (k1 - k0 + 63) / 64;  // 64-key rounds of the block (one 16-key batch per wave each)
-  for (int j = 0; j < nb; j += 3) {
+  // 64-key rounds of the block (one 16-key batch per wave each); with two kv heads, rounds nb .. 2 nb - 1 take kv
+  // head 1's keys of the same split, which only query heads 2 and 3 read
+  const int nb = (k1 - k0 + 63) / 64;
+  const int nbt = two ? 2 * nb : nb;
+  for (int j = 0; j < nbt; j += 3) {
     // compute batch j from A while B and C are in flight, then refill A with batch j + 3, and so on
-    if (k0 + 64 * j + 16 * w < k1)
-      mfma_batch<4, false>(k0 + 64 * j + 16 * w, k1, Kb, Kb, cap, true, a.scale_log2, tile, S.qop, kA, kA, acc,
-                           mrun, lrun);
-    load_key_batch(ksp, j + 3, kA);
-    if (k0 + 64 * (j + 1) + 16 * w < k1)
-      mfma_batch<4, false>(k0 + 64 * (j + 1) + 16 * w, k1, Kb, Kb, cap, true, a.scale_log2, tile, S.qop, kB, kB,
-                           acc, mrun, lrun);
-    load_key_batch(ksp, j + 4, kB);
-    if (k0 + 64 * (j + 2) + 16 * w < k1)
-      mfma_batch<4, false>(k0 + 64 * (j + 2) + 16 * w, k1, Kb, Kb, cap, true, a.scale_log2, tile, S.qop, kC, kC,
-                           acc, mrun, lrun);
-    load_key_batch(ksp, j + 5, kC);
+#define MTPD_TEAM_BATCH(J, KR)                                                                                   \
+  {                                                                                                              \
+    const int g_ = (two && (J) >= nb) ? 1 : 0, t_ = k0 + 64 * ((J) - g_ * nb) + 16 * w;                          \
+    if (t_ < k1)                                                                                                 \
+      mfma_batch<4, false>(t_, k1, Kb, Kb, cap, true, a.scale_log2, tile, S.qop, KR, KR, acc, mrun, lrun,       \
+                           two ? 2 * g_ : 0, two ? 2 * g_ + 2 : 4);                                            \
+  }
+    MTPD_TEAM_BATCH(j, kA)
+    load_key_batch<NKV>(ksp, j + 3, kA);
+    MTPD_TEAM_BATCH(j + 1, kB)
+    load_key_batch<NKV>(ksp, j + 4, kB);
+    MTPD_TEAM_BATCH(j + 2, kC)
+    load_key_batch<NKV>(ksp, j + 5, kC);
+#undef MTPD_TEAM_BATCH
   }
   if (l == 1) TEAM_TRACE(step, 50);
   if (type) TEAM_TRACE(step, 30);
@@ -1241,7 +1262,7 @@ __device__ __forceinline__ void stage_final(const TeamArgs& a, Team& T, int step
   }
 }
 
-template <int R, int NBB>
+template <int R, int NBB, int NKV>
 __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
   WQ wq;
   WK wo, wd;
@@ -1250,13 +1271,13 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
   for (int step = 0; step < a.n_steps; ++step) {
     TEAM_TRACE(step, S_PRE);
     TEAM_TRACE_CYCLES(step, 61);
-    stage_pre<R, NBB>(a, T, S, step, wq, pf);
+    stage_pre<R, NBB, NKV>(a, T, S, step, wq, pf);
     for (int l = 0; l < a.n_layer; ++l) {
       const bool last = l + 1 == a.n_layer;
       TEAM_TRACE(step, s_q(l));
       stage_q<R>(a, T, S, step, l, wq);
       TEAM_TRACE(step, s_att(l));
-      stage_att<R>(a, T, S, step, l, wo);
+      stage_att<R, NKV>(a, T, S, step, l, wo);
       TEAM_TRACE(step, s_mrg(l));
       stage_mrg<R>(a, T, S, step, l);
       TEAM_TRACE(step, s_op(l));
@@ -1282,7 +1303,9 @@ __device__ __forceinline__ void run_team(const TeamArgs& a, Team& T, Smem& S) {
 // At least 96 KB of LDS per block keeps one block per CU, so the 256 blocks cover all 256 CUs.
 constexpr int kLdsPad = (96 * 1024 > (int)sizeof(Smem)) ? 96 * 1024 - (int)sizeof(Smem) : 0;
 
-template <int NBB>
+// NKV: kv heads (1 or 2), a compile-time constant so that the one-kv-head instance carries none of the second
+// head's selects
+template <int NBB, int NKV>
 __global__ __launch_bounds__(256, 1) void k_team(TeamArgs a) {
   __shared__ Smem S;
   __shared__ uint8_t pad[kLdsPad > 0 ? kLdsPad : 1];
@@ -1311,9 +1334,9 @@ __global__ __launch_bounds__(256, 1) void k_team(TeamArgs a) {
     T.row0 = T.t;
     T.row1 = T.t + NT;
     if (T.R == 2)
-      run_team<2, NBB>(a, T, S);
+      run_team<2, NBB, NKV>(a, T, S);
     else
-      run_team<1, NBB>(a, T, S);
+      run_team<1, NBB, NKV>(a, T, S);
   }
   __syncthreads();
   if (threadIdx.x == 0) a.epoch[blockIdx.x] = T.E + (uint32_t)a.n_steps;
@@ -1367,14 +1390,21 @@ hipError_t team_trace_read(uint64_t* host) {
 
 bool team_backbone_ok(int Bb) { return Bb == 1536 || Bb == 2048 || Bb == 2560 || Bb == 3072 || Bb == 4096; }
 
-hipError_t launch_team(hipStream_t s, const TeamArgs& a) {
+template <int NKV>
+hipError_t launch_team_nkv(hipStream_t s, const TeamArgs& a) {
   switch (a.Bb) {
-    case 1536: return go(k_team<6>, dim3(kTeamBlocks), dim3(256), 0, s, a);
-    case 2048: return go(k_team<8>, dim3(kTeamBlocks), dim3(256), 0, s, a);
-    case 2560: return go(k_team<10>, dim3(kTeamBlocks), dim3(256), 0, s, a);
-    case 3072: return go(k_team<12>, dim3(kTeamBlocks), dim3(256), 0, s, a);
-    case 4096: return go(k_team<16>, dim3(kTeamBlocks), dim3(256), 0, s, a);
+    case 1536: return go(k_team<6, NKV>, dim3(kTeamBlocks), dim3(256), 0, s, a);
+    case 2048: return go(k_team<8, NKV>, dim3(kTeamBlocks), dim3(256), 0, s, a);
+    case 2560: return go(k_team<10, NKV>, dim3(kTeamBlocks), dim3(256), 0, s, a);
+    case 3072: return go(k_team<12, NKV>, dim3(kTeamBlocks), dim3(256), 0, s, a);
+    case 4096: return go(k_team<16, NKV>, dim3(kTeamBlocks), dim3(256), 0, s, a);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_team(hipStream_t s, const TeamArgs& a) {
+  if (a.nkv == 1) return launch_team_nkv<1>(s, a);
+  if (a.nkv == 2) return launch_team_nkv<2>(s, a);
   return hipErrorInvalidValue;
 }
 

@@ -210,7 +210,7 @@ struct TeamArgs {
   const uint16_t* th;    // [B][Bb] step-0 hidden input
   const int32_t* tok;    // [B] step-0 token
   const uint16_t* temb;  // [V][Bb]
-  const uint16_t* kc[2];  // per-row caches [B][1][cap][256], K = V (0 sliding, 1 full)
+  const uint16_t* kc[2];  // per-row caches [B][nkv][cap][256], K = V (0 sliding, 1 full)
   int32_t cap[2];
   int32_t win_start[2][kTeamMaxBatch], win_count[2][kTeamMaxBatch];
   const float* rope;  // [B][2][2][128]
@@ -223,6 +223,7 @@ struct TeamArgs {
   int32_t* ids;           // [B][32][128] (null: not stored)
   float* z;               // [B][32][128] (null: not stored)
   int32_t B, n_steps, n_layer, Bb, V;
+  int32_t nkv;  // kv heads: 1 (4 query heads per kv head) or 2 (query heads 2 g, 2 g + 1 read kv head g)
   uint32_t full_mask;
   float eps, scale_log2, escale;
   uint64_t* xch;     // exchange words, team_arena_words() per team

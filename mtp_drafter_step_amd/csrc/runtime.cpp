@@ -694,10 +694,11 @@ void* scratch_lookup() {
   return g_scratch_dev[dev];
 }
 
-// The persistent kernel's shapes: the E2B / E4B drafters (hidden 256, 4 heads of 256 over one K = V head, FFN 1024,
-// 2048 clusters of 128 tokens, top 32, at most 4 layers) on a gfx950 with 256 CUs (8 XCDs of 32).
+// The persistent kernel's shapes: the E2B / E4B drafters (hidden 256, 4 heads of 256 over one or two K = V heads,
+// FFN 1024, 2048 clusters of 128 tokens, top 32, at most 4 layers) on a gfx950 with 256 CUs (8 XCDs of 32).
 bool team_config_ok(const mtpd_config& c) {
-  return c.hidden == 256 && c.n_head == 4 && c.n_kv_head == 1 && c.head_dim == 256 && c.ffn == 1024 &&
+  return c.hidden == 256 && c.n_head == 4 && (c.n_kv_head == 1 || c.n_kv_head == 2) && c.head_dim == 256 &&
+         c.ffn == 1024 &&
          c.n_layer >= 1 && c.n_layer <= mtpd::kTeamMaxLayers && c.n_centroids == 2048 && c.top_k == 32 &&
          c.vocab == 2048 * 128 && mtpd::team_backbone_ok(c.backbone);
 }
@@ -755,6 +756,7 @@ int run_team(const mtpd_handle_s* h, hipStream_t s, int B, int n, const uint16_t
   a.n_layer = c.n_layer;
   a.Bb = c.backbone;
   a.V = c.vocab;
+  a.nkv = c.n_kv_head;
   a.full_mask = c.full_attn_layers;
   a.eps = c.rms_eps;
   a.scale_log2 = c.attn_scale * 1.4426950408889634f;

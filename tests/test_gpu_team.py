@@ -32,14 +32,26 @@ def _check_status(d):
     assert st == 0, f"persistent kernel status {st:#x}"
 
 
+# two kv heads (query heads 0-1 read kv head 0, 2-3 kv head 1); a 1024-key window makes the sliding split of 16
+# members 64 keys, too many to hold in LDS for two kv heads, so the sliding layers stream their keys too
+SHAPES = {"E4B": synth.E4B, "E2B": synth.E2B, "E4B_NKV2": dataclasses.replace(synth.E4B, n_kv_head=2),
+          "E4B_NKV2_W1024": dataclasses.replace(synth.E4B, n_kv_head=2, swa_window=1024)}
+
+
 @pytest.mark.parametrize("shape_name,batch,context", [("E4B", 16, 2048), ("E4B", 1, 700), ("E2B", 5, 1300),
-                                                      ("E4B", 11, 3000), ("E2B", 16, 600)])
+                                                      ("E4B", 11, 3000), ("E2B", 16, 600),
+                                                      ("E4B_NKV2", 16, 2048), ("E4B_NKV2", 3, 900),
+                                                      ("E4B_NKV2_W1024", 16, 1700)])
 def test_team_step_matches_oracle(shape_name, batch, context):
-    shape = getattr(synth, shape_name)
+    shape = SHAPES[shape_name]
     say(f"team step {shape_name} B={batch} ctx={context}")
     case = Case(shape, batch=batch, context=context, ragged=True)
+    case.drafter.timing(True)
     out = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_logits=True, want_sparse=True)
     torch.cuda.synchronize()
+    names = [n for n, _ in case.drafter.timing_records()]
+    case.drafter.timing(False)
+    assert "team" in names and not any(n.startswith("attn") for n in names), names  # the persistent kernel ran
     _check_status(case.drafter)
     rows = list(range(batch))
     ref = case.oracle_step(rows=rows)
@@ -66,12 +78,14 @@ def test_team_block_equals_chained_team_steps():
     say(f"block tokens row 0: {blk['tokens'][0].tolist()}")
 
 
-def test_team_against_per_stage_kernels():
+@pytest.mark.parametrize("shape_name", ["E4B", "E4B_NKV2"])
+def test_team_against_per_stage_kernels(shape_name):
     """The persistent kernel and the per-stage kernels on the same inputs agree on the tokens where the oracle's
     margins are clear, and on hidden_out within the float rule."""
     from mtp_drafter_step_amd import Drafter, abi
     from parity import rel_ok
-    case = Case(synth.E4B, batch=16, context=4000, ragged=True)
+    say(f"team against per-stage kernels {shape_name}")
+    case = Case(SHAPES[shape_name], batch=16, context=4000, ragged=True)
     a = case.drafter.drafter_step(case.th, case.tok, case.temb, case.kv, want_sparse=True)
     d2 = Drafter(case.shape, case.wg, max_batch=16, options={abi.MTPD_OPT_PERSISTENT: 0})
     b = d2.drafter_step(case.th, case.tok, case.temb, case.kv, want_sparse=True)

@@ -27,5 +27,5 @@ def test_persistent_kernel_uses_no_scratch(tmp_path):
     scratch = [int(x) for x in re.findall(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", r.stderr)]
     assert len(names) == len(scratch) and names
     team = [(n, s) for n, s in zip(names, scratch) if "k_team" in n]
-    assert len(team) == 5, team  # one instance per supported backbone width
+    assert len(team) == 10, team  # one instance per supported backbone width and kv head count (1, 2)
     assert all(s == 0 for _, s in team), team
