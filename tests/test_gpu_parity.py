@@ -405,6 +405,9 @@ def test_drafter_step_is_deterministic():
 BLOCK_CASES = {
     "e2b_b1_ctx4096_block4": dict(shape=synth.E2B, batch=1, context=4096, n=4),
     "e4b_b16_ctx8192_block4": dict(shape=synth.E4B, batch=16, context=8192, n=4),
+    # the two-kv-head workload at its full size
+    "e4b_nkv2_b16_ctx8192_block4": dict(shape=dataclasses.replace(synth.E4B, n_kv_head=2), batch=16, context=8192,
+                                        n=4),
 }
 
 

@@ -60,9 +60,12 @@ def test_team_step_matches_oracle(shape_name, batch, context):
     assert tally.sel_checked >= len(rows) // 2
 
 
-def test_team_block_equals_chained_team_steps():
-    """draft_block(4) in one launch reproduces four chained one-step launches bit for bit (tokens, logits, hidden)."""
-    case = Case(synth.E4B, batch=16, context=1500, ragged=True)
+@pytest.mark.parametrize("shape_name", ["E4B", "E4B_NKV2"])
+def test_team_block_equals_chained_team_steps(shape_name):
+    """draft_block(4) in one launch reproduces four chained one-step launches bit for bit (tokens, logits, hidden):
+    the sliding keys loaded into LDS at the block's first step serve its later steps."""
+    say(f"team block against chained steps {shape_name}")
+    case = Case(SHAPES[shape_name], batch=16, context=1500, ragged=True)
     d = case.drafter
     blk = d.draft_block(4, case.th, case.tok, case.temb, case.kv, want_logits=True)
     blk = {k: v.clone() for k, v in blk.items()}
