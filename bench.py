@@ -353,20 +353,29 @@ def run_bench(args):
     lens = [int(x) for x in inp["len_full"]]
     sbytes, parts = step_bytes(shape, B, lens, u_mean, shared=wl.shared_kv)
 
-    # timed region: graph-replayed draft_block calls on torch's current stream
+    # timed region: the K draft_block calls back to back on torch's current stream, nothing else in between
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = B * n * args.steps / wall
+    # then the same number of calls, each between two events, for the per-call distribution (outside the timed
+    # region: event records between the calls add a few microseconds per call)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:  # create the events before the loop
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
     for i in range(args.steps):
         ev[i][0].record(stream)
         run()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    ms_per_step = wall * 1e3 / args.steps
-    value = B * n * args.steps / wall
     us_drafter_step = float(np.median(launch_ms)) * 1e3 / n
 
     # the library's streaming read (one pass over 1 GiB) gives the measured read rate of this device and, run
