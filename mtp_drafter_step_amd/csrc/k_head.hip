@@ -353,7 +353,9 @@ __global__ __launch_bounds__(1024) void k_head_dense(int B, int V, const uint16_
           const int col = c0 + t * 16 + n;
           const f32x4 v = acc[r][t];
           if (logits && col < B)
-            *reinterpret_cast<float4*>(logits + (size_t)col * V + row0) = make_float4(v[0], v[1], v[2], v[3]);
+            // streaming stores: the row is not read again here, and dirty lines left in L2 would be written back
+            // during the next kernels
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(logits + (size_t)col * V + row0));
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (v[i] > best[t]) {
