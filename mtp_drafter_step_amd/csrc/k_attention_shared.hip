@@ -212,7 +212,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
       mt = fmaxf(mt, xr_partner<16>(mt));
       mt = fmaxf(mt, xr_partner<32>(mt));
-      const float mn = fmaxf(mrun, mt);
+      // the reference maximum moves only when a score exceeds it by more than 2^8: below that the weights stay under
+      // 256, far inside fp32 and kept to fp32-level accuracy by the bf16 hi + lo split, and most batches skip the
+      // rescale of the 64 output sums
+      const float mn = (mt > mrun + 8.0f) ? mt : mrun;
       // 2^x on the hardware instruction: weights below 2^-126 flush to zero, far below what a weight contributes
       const float alpha = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
       float pv[8], ps = 0.f;
