@@ -83,6 +83,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       wen = en;
     }
   }
+  // the keys inside every query window of the wave: batches wholly in [wlo, whi) need no per-key mask
+  int wlo = wst, whi = wen;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    wlo = max(wlo, __shfl_xor(wlo, o, 64));
+    whi = min(whi, __shfl_xor(whi, o, 64));
+  }
   const int chunk = (u1 - u0 + nsplit - 1) / nsplit;
   const int k0 = u0 + sp * chunk, k1 = min(u1, k0 + chunk);
   const uint16_t* Kb = K + (size_t)g * cap * HD;  // the shared cache (row 0)
@@ -144,11 +151,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
         v[s + 4][e] = hi * c8[e] + lo * s8[e];
       }
     }
+    // the softmax scale (with log2 e) goes into q before the split, so the products are the exponents' arguments
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       uint32_t h32[4], l32[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) split_bf16x2(v[s][2 * e], v[s][2 * e + 1], h32[e], l32[e]);
+      for (int e = 0; e < 4; ++e)
+        split_bf16x2(v[s][2 * e] * scale_log2, v[s][2 * e + 1] * scale_log2, h32[e], l32[e]);
       qhi[s] = make_uint4(h32[0], h32[1], h32[2], h32[3]);
       qlo[s] = make_uint4(l32[0], l32[1], l32[2], l32[3]);
     }
@@ -200,13 +209,21 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       }
       // scores S[query hq][key kb + 16 h2 + 4 kq + r], masked to the query row's window
       float sv[8];
+      const bool inside = kb >= wlo && kb + 32 <= whi && kb + 32 <= k1;  // wave-uniform: no key of the batch masked
+      if (inside) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = kb + 16 * h2 + 4 * kq + r;
-          sv[4 * h2 + r] = (t < k1 && t >= wst && t < wen) ? sacc[h2][r] * scale_log2 : -INFINITY;
-        }
+          for (int r = 0; r < 4; ++r) sv[4 * h2 + r] = sacc[h2][r];
+      } else {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = kb + 16 * h2 + 4 * kq + r;
+            sv[4 * h2 + r] = (t < k1 && t >= wst && t < wen) ? sacc[h2][r] : -INFINITY;
+          }
+      }
       float mt = sv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
@@ -216,12 +233,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
       // 256, far inside fp32 and kept to fp32-level accuracy by the bf16 hi + lo split, and most batches skip the
       // rescale of the 64 output sums
       const float mn = (mt > mrun + 8.0f) ? mt : mrun;
-      // 2^x on the hardware instruction: weights below 2^-126 flush to zero, far below what a weight contributes
-      const float alpha = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+      // 2^x on the hardware instruction: weights below 2^-126 flush to zero, far below what a weight contributes, and
+      // 2^-inf is 0, so masked keys and a first maximum need no select: only a query with no key yet (mn = -inf)
+      // takes 0 as its reference, which leaves its weights and alpha at 0
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mref);
       float pv[8], ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - mn);
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - mref);
         ps += pv[i];
       }
       ps += xr_partner<16>(ps);
