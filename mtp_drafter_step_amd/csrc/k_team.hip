@@ -8,8 +8,9 @@
 //   [Guide]      "Gemma 4 Assistant 使用指南：用 MTP 投机解码与 KV Sharing 加速 Gemma 4 推理" (gitcode blog)
 //   [Explained]  "Gemma 4 drafter explained" (techtwitter)
 //
-// Shapes: hidden 256, 4 query heads of 256 over one K = V head, FFN 1024, 2048 centroids of 128 tokens, top 32, up
-// to 4 layers, backbone a multiple of 512 (the E2B and E4B drafters of [MTP doc] "Variants supported").
+// Shapes: hidden 256, 4 query heads of 256 over one K = V head (or two, each read by two query heads), FFN 1024,
+// 2048 centroids of 128 tokens, top 32, up to 4 layers, backbone a multiple of 512 (the E2B and E4B drafters of
+// [MTP doc] "Variants supported").
 //
 // Layout of the work. The dispatcher deals workgroups to the XCDs in turn, continuing from where the previous launch
 // stopped, so block b runs on XCD (b + k) % 8 for some k of the launch. A block reads its XCD from the hardware
