@@ -1315,6 +1315,17 @@ __global__ __launch_bounds__(256, 1) void k_team(TeamArgs a) {
   // runs on XCD (b + k) mod 8 for some k of the launch. The team is the XCD the block runs on (read from the
   // hardware), so a team's 32 blocks share that XCD's L2 and each XCD always uses the same exchange words; b / 8 is
   // then a distinct member index within every team.
+  // touch every 64-byte line of the argument block at once: the compiler fetches the arguments lazily, near each
+  // use, and at the start of the kernel those fetches would otherwise miss one after another
+  {
+    constexpr int kLines = (int)((sizeof(TeamArgs) + 63) / 64);
+    const uint32_t* kp = (const uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t t[kLines];
+#pragma unroll
+    for (int i = 0; i < kLines; ++i) t[i] = kp[16 * i];
+#pragma unroll
+    for (int i = 0; i < kLines; ++i) asm volatile("" ::"s"(t[i]));
+  }
   const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u;  // XCC_ID
   Team T;
   T.t = (int)(xcc & (NT - 1));
