@@ -74,14 +74,21 @@ __global__ __launch_bounds__(512, 1) void k_attn_mq(int B, int nh, int nkv, cons
   const bool qlive = rbase + hq / G < B;
   const int head = g * G + hq % G;
   int wst = 0, wen = 0;  // the query row's window (virtual indices), from wave-uniform reads of the row table
+  {
+    // all of the wave's table reads first, so that they go out together instead of one after another
+    int st[RPW], ct[RPW];
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int r = min(rbase + j, B - 1);
-    const int st = win.start[r], en = st + win.count[r];
-    if (hq / G == j) {
-      wst = st;
-      wen = en;
+    for (int j = 0; j < RPW; ++j) {
+      const int r = min(rbase + j, B - 1);
+      st[j] = win.start[r];
+      ct[j] = win.count[r];
     }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+      if (hq / G == j) {
+        wst = st[j];
+        wen = st[j] + ct[j];
+      }
   }
   // the keys inside every query window of the wave: batches wholly in [wlo, whi) need no per-key mask
   int wlo = wst, whi = wen;
