@@ -44,7 +44,7 @@ KERNEL_FILE = {"k_stream_read": "k_stream.hip", "k_attn_mfma": "k_attention.hip"
                "k_zero_u64": "k_head.hip", "k_gather_rows": "k_head.hip",
                "k_sample_tiles": "k_head.hip", "k_sample_pick": "k_head.hip", "k_gemm": "k_gemm.hip",
                "k_group": "k_head.hip", "k_head_grouped": "k_head.hip", "k_topk_rows": "k_head.hip",
-               "k_rownorm": "k_gemm.hip", "k_merge": "k_gemm.hip", "k_token": "k_gemm.hip", "k_team": "k_team.hip"}
+               "k_rownorm": "k_gemm.hip", "k_merge": "k_gemm.hip", "k_team": "k_team.hip"}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 512 << 20
 
@@ -55,7 +55,7 @@ SITE_KERNEL = {"pre": "k_pre", "qproj": "k_qproj", "attn_sliding": "k_attn_mfma"
                "scores": "k_dense", "fill": "k_fill", "head_dense": "k_head_dense", "zero_keys": "k_zero_u64",
                "sample_tiles": "k_sample_tiles", "sample_pick": "k_sample_pick",
                # the large-batch path
-               "token": "k_token", "rownorm": "k_rownorm", "post_norm": "k_rownorm", "attn_merge": "k_merge",
+               "rownorm": "k_rownorm", "post_norm": "k_rownorm", "attn_merge": "k_merge",
                "pre_gemm": "k_gemm", "qproj_gemm": "k_gemm", "o_proj_gemm": "k_gemm", "ffn_gemm": "k_gemm",
                "down_gemm": "k_gemm", "post_gemm": "k_gemm", "scores_gemm": "k_gemm",
                "head_select": "k_topk_rows", "head_group": "k_group", "head_grouped": "k_head_grouped",
@@ -125,8 +125,6 @@ def site_bytes(site, shape, batch, lens, distinct_clusters, shared=False):
         return act(QD) * 2
     if site == "fill":  # the -1e30 logits rows
         return 4 * shape.vocab * B
-    if site == "token":
-        return 8 * max(shape.top_k, 1) * B + 8 * B
     W = shape.swa_window
     if site == "pre":
         return 2 * H * 2 * Bb + 2 * 2 * B * Bb + act(H)

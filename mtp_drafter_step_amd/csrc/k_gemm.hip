@@ -33,7 +33,8 @@ struct GemmSrc {
   const float* x;          // SRC_F32: [B][K]
   const uint16_t* th;      // SRC_PRE: target hidden [B][Bb]
   const uint16_t* emb;     // SRC_PRE: embedding table [V][Bb]
-  const int32_t* tok;      // SRC_PRE: resolved tokens [B]
+  TokenSource ts;          // SRC_PRE: the rows' tokens (the caller's, or the previous step's argmax from its keys)
+  int V;                   // SRC_PRE: vocabulary (tokens are clamped into [0, V))
   int Bb;                  // SRC_PRE: backbone width (K = 2 Bb)
   float escale;            // SRC_PRE: factor on the embedding half
 };
@@ -97,11 +98,32 @@ __global__ __launch_bounds__(256) void k_gemm(int B, int N, int K, GemmSrc src, 
       xf[i][0] = v.x; xf[i][1] = v.y; xf[i][2] = v.z; xf[i][3] = v.w;
     }
   } else {
-    // the rows' tokens first, then every row load unconditionally (a select picks the table), so that the loads
-    // issue together instead of one branch, load and wait per element
+    // the tile's 16 tokens, one row per wave at a time: the caller's, or the argmax of the row's keys from the
+    // previous step (recorded by the blocks of the first output tile and chunk), clamped into [0, V)
+    __shared__ int tks[NC];
+    {
+      const TokenSource& ts = src.ts;
+#pragma unroll
+      for (int q = 0; q < NC / 4; ++q) {
+        const int r = (tid >> 6) * (NC / 4) + q, b = min(c0 + r, B - 1);
+        const uint64_t kraw = ts.keys[(size_t)b * ts.k + min(lane, ts.k - 1)];
+        int t = ts.tok[b];
+        if (ts.use_keys) {
+          t = key_id(wave_max_u64(lane < ts.k ? kraw : 0ull));
+          if (lane == 0 && blockIdx.x == 0 && blockIdx.y == 0 && c0 + r < B) {
+            if (ts.out) ts.out[(size_t)b * ts.out_stride] = t;
+            if (ts.next) ts.next[b] = t;
+          }
+        }
+        if (lane == 0) tks[r] = t < 0 ? 0 : (t >= src.V ? src.V - 1 : t);
+      }
+      __syncthreads();
+    }
+    // then every row load unconditionally (a select picks the table), so that the loads issue together instead of
+    // one branch, load and wait per element
     int tk[NV4];
 #pragma unroll
-    for (int i = 0; i < NV4; ++i) tk[i] = src.tok[min(c0 + ((tid + i * 256) * 4) / KC, B - 1)];
+    for (int i = 0; i < NV4; ++i) tk[i] = tks[((tid + i * 256) * 4) / KC];
     uint2 w[NV4];
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
@@ -311,23 +333,6 @@ __global__ __launch_bounds__(256) void k_merge(int nsplit, int hd, const float* 
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// The step's input token of each row (the caller's, or the previous step's argmax from its keys), clamped into
-// [0, V), recorded where the token source asks. grid B, 64 threads.
-__global__ void k_token(int V, TokenSource ts, int32_t* tok_out) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const uint64_t kraw = ts.keys[(size_t)b * ts.k + min(lane, ts.k - 1)];
-  int t = ts.tok[b];
-  if (ts.use_keys) {
-    t = key_id(wave_max_u64(lane < ts.k ? kraw : 0ull));
-    if (lane == 0) {
-      if (ts.out) ts.out[(size_t)b * ts.out_stride] = t;
-      if (ts.next) ts.next[b] = t;
-    }
-  }
-  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  if (lane == 0) tok_out[b] = t;
-}
-
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------------------
@@ -348,8 +353,9 @@ int gemm_chunks(int B, int N, int K, bool one_chunk) {
 }
 
 hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float* X, const uint16_t* th,
-                       const uint16_t* emb, const int32_t* tok, int Bb, float escale, const uint16_t* W,
-                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks, FillRange fill) {
+                       const uint16_t* emb, const TokenSource* ts, int Bb, float escale, const uint16_t* W,
+                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks, FillRange fill, int V) {
+  if (kind == 3 && (!ts || ts->k < 1 || ts->k > 64 || V < 1)) return hipErrorInvalidValue;
   if (K % 256 || N % 16 || K > kGemmMaxK || (K / 256) % nchunks) return hipErrorInvalidValue;
   const int KC = K / nchunks;
   // waves per 16-row tile: more only while the grid is below about 256 blocks (each block stages its X chunk, so
@@ -358,7 +364,7 @@ hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float
   auto blocks = [&](int w) { return ((N + 64 / w - 1) / (64 / w)) * nchunks * ((B + 15) / 16); };
   while (wpt < 4 && wpt * 2 <= KC / 256 && blocks(wpt) < 256) wpt *= 2;
   const dim3 grid((N + 64 / wpt - 1) / (64 / wpt), nchunks, (B + 15) / 16);
-  GemmSrc src{X, th, emb, tok, Bb, escale};
+  GemmSrc src{X, th, emb, ts ? *ts : TokenSource{}, V, Bb, escale};
 #define MTPD_GEMM_W(KC_, WPT_, SRC_, EPI_) \
   if (KC == KC_ && wpt == WPT_) return go(k_gemm<KC_, WPT_, SRC_, EPI_>, grid, 256, 0, s, B, N, K, src, W, W2, Y, Yb, fill);
 #define MTPD_GEMM(KC_, SRC_, EPI_) MTPD_GEMM_W(KC_, 1, SRC_, EPI_) MTPD_GEMM_W(KC_, 2, SRC_, EPI_) MTPD_GEMM_W(KC_, 4, SRC_, EPI_)
@@ -410,8 +416,5 @@ hipError_t launch_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const 
 #undef MTPD_MERGE
 }
 
-hipError_t launch_token(hipStream_t s, int B, int V, TokenSource ts, int32_t* tok_out) {
-  return go(k_token, B, 64, 0, s, V, ts, tok_out);
-}
 
 }  // namespace mtpd

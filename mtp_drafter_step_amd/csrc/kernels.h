@@ -163,11 +163,13 @@ int gemm_chunks(int B, int N, int K, bool one_chunk);
 
 // Matrix-core GEMM Y = W X^T, W bf16 [N][K], over nchunks K chunks (K % 256 == 0, N % 16 == 0). kind 0: X fp32
 // [B][K] -> fp32 partials Y [nchunks][B][N]; 1: -> bf16 Yb [B][N]; 2: GeGLU gelu_tanh(W X) * (W2 X) -> fp32 Y [B][N];
-// 3: X = [th ; escale * emb[tok]] (bf16 tables, K = 2 Bb) -> fp32 partials. Kinds 1 and 2 need nchunks == 1. The
-// blocks also fill a slice of the logits with -1e30 (fill.logits null: none).
+// 3: X = [th ; escale * emb[tok]] (bf16 tables, K = 2 Bb) -> fp32 partials, each row's token taken from ts (the
+// caller's or the previous step's argmax, recorded where ts asks; 1 <= ts->k <= 64) and clamped into [0, V). Kinds 1
+// and 2 need nchunks == 1. The blocks also fill a slice of the logits with -1e30 (fill.logits null: none).
 hipError_t launch_gemm(hipStream_t s, int kind, int B, int N, int K, const float* X, const uint16_t* th,
-                       const uint16_t* emb, const int32_t* tok, int Bb, float escale, const uint16_t* W,
-                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks, FillRange fill = FillRange{nullptr, 0, 0});
+                       const uint16_t* emb, const TokenSource* ts, int Bb, float escale, const uint16_t* W,
+                       const uint16_t* W2, float* Y, uint16_t* Yb, int nchunks, FillRange fill = FillRange{nullptr, 0, 0},
+                       int V = 0);
 
 // Per row: x = sum of nx partials of xp (stride xs); with delta (nd partials, stride ds) x = (x + RMSNorm(delta;
 // w_delta)) * scale; x_new = x (when set); u = RMSNorm(x; w_norm); keys_zero[b] = 0 (when set). H % 256 == 0.
@@ -177,9 +179,6 @@ hipError_t launch_rownorm(hipStream_t s, int B, int H, const float* xp, int nx, 
 
 // o[b][h] = merge of the nsplit key-range partials (pacc, pml) of the attention.
 hipError_t launch_merge(hipStream_t s, int B, int nh, int hd, int nsplit, const float* pacc, const float* pml, float* o);
-
-// tok_out[b] = the step's input token of row b from the token source (recorded where it asks), clamped to [0, V).
-hipError_t launch_token(hipStream_t s, int B, int V, TokenSource ts, int32_t* tok_out);
 
 // ---- persistent drafter kernel (k_team.hip)
 //

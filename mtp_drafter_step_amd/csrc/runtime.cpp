@@ -115,7 +115,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Offsets of every intermediate in the caller's workspace for a given batch.
 struct Plan {
-  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, stok, tsum, row, u, xp, dp, rtok,
+  size_t x[2], q, pacc, pml, o, t, m, d, h, hid, tok, scores, sel, ids, z, keys, stok, tsum, row, u, xp, dp,
       grp, total;
 };
 
@@ -155,7 +155,6 @@ Plan make_plan(const mtpd_config& c, int B, int vsc) {
   p.u = take((size_t)B * H * 4);
   p.xp = take((size_t)(2 * Bb / 256) * B * H * 4);
   p.dp = take((size_t)(F / 256) * B * H * 4);
-  p.rtok = take((size_t)B * 4);
   // cluster grouping of the head: a 16-byte record per (cluster, entry tile), then the grouped entries
   p.grp = take((size_t)(4 * (c.n_centroids + B * std::max(c.top_k, 1)) + B * std::max(c.top_k, 1)) * 4);
   p.total = off;
@@ -403,12 +402,11 @@ int run_step_gemm(const mtpd_handle_s* h, hipStream_t s, void* ws, const Plan& p
   float* m = at<float>(ws, p.m);
   float* xp = at<float>(ws, p.xp);
   float* dp = at<float>(ws, p.dp);
-  int32_t* rtok = at<int32_t>(ws, p.rtok);
-  // input assembly + pre_projection ([MTP doc] "What it is"; [Guide] section 2(3))
-  KLAUNCH(h, "token", mtpd::launch_token(s, B, c.vocab, ts, rtok));
+  // input assembly + pre_projection ([MTP doc] "What it is"; [Guide] section 2(3)); the GEMM's blocks resolve the
+  // rows' tokens themselves
   const int npre = mtpd::gemm_chunks(B, H, 2 * Bb, false);
-  KLAUNCH(h, "pre_gemm", mtpd::launch_gemm(s, 3, B, H, 2 * Bb, nullptr, th, temb, rtok, Bb, c.embed_scale, h->w.pre_proj,
-                                           nullptr, xp, nullptr, npre));
+  KLAUNCH(h, "pre_gemm", mtpd::launch_gemm(s, 3, B, H, 2 * Bb, nullptr, th, temb, &ts, Bb, c.embed_scale, h->w.pre_proj,
+                                           nullptr, xp, nullptr, npre, mtpd::FillRange{nullptr, 0, 0}, c.vocab));
   const float* xin = xp;  // the residual stream entering the next norm, as partials
   int nx = npre;
   const float* din = nullptr;
